@@ -1,0 +1,69 @@
+"""Pin the float64 oracle to explicit enumeration of every segmentation.
+
+The enumerator (oracle/bruteforce.py) sums scores straight from the
+emissions and weights every segmentation by its probability; it shares no
+recursion with the oracle's dynamic programme.  Grid: T <= 8, C <= 3, K <= 4,
+ragged lengths, centring on and off, several seeds, non-unit grad weights.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import bruteforce
+from semi_markov_crf_zero_amd.workloads import make_random
+
+CASES = []
+for C, K in itertools.product([1, 2, 3], [1, 2, 3, 4]):
+    for seed in range(2):
+        CASES.append((C, K, seed))
+
+
+@pytest.mark.parametrize("center", [True, False])
+@pytest.mark.parametrize("C,K,seed", CASES)
+def test_oracle_matches_enumeration(oracle_mod, C, K, seed, center):
+    T = 7 if C == 3 else 8
+    rng = np.random.default_rng(100 + seed)
+    lengths = [T, int(rng.integers(1, T + 1)), 1]
+    inp = make_random(3, T, C, K, seed=seed, lengths=lengths, sigma=1.0, tsd=0.5, dsd=0.5)
+    w = np.array([1.0, -0.5, 2.0])
+    bf = bruteforce.brute_force(inp, center=center, grad_logz=w)
+    orc = oracle_mod.fwd_bwd(inp, center=center, grad_logz=w)
+    np.testing.assert_allclose(orc["logz"], bf["logz"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(orc["logz_bwd"], bf["logz"], rtol=1e-12, atol=1e-12)
+    for key in ("marginals", "grad_emissions", "grad_trans", "grad_dur"):
+        np.testing.assert_allclose(orc[key], bf[key], rtol=0, atol=1e-11, err_msg=key)
+    vit = oracle_mod.viterbi(inp, center=center)
+    for b in range(3):
+        segs = [(int(vit["seg_start"][b, j]), int(vit["seg_len"][b, j]), int(vit["seg_label"][b, j]))
+                for j in range(vit["num_segs"][b])]
+        best, _ = bf["viterbi"][b]
+        assert abs(vit["best_score"][b] - best) < 1e-12
+        # the returned path is one of the enumerated maximisers
+        assert segs in bf["viterbi_ties"][b]
+        assert np.all(vit["seg_start"][b, vit["num_segs"][b]:] == -1)
+
+
+def test_enumeration_counts_match_closed_form():
+    # sanity of the enumerator itself: number of labelled segmentations
+    from oracle import closed_form
+    for L, C, K in [(5, 2, 3), (6, 3, 2), (4, 3, 4)]:
+        x = np.zeros((L, C))
+        n = sum(1 for _ in bruteforce.enumerate_sequence(x, L, np.zeros((C, C)), np.zeros((K, C))))
+        assert np.isclose(np.log(n), closed_form.log_count(L, C, K))
+
+
+def test_viterbi_tie_break_rule_on_enumeration(oracle_mod):
+    """Zero potentials: every segmentation ties; the stated rule (smallest k,
+    then smallest previous label, smallest final label) yields L unit
+    segments of label 0."""
+    for (C, K, L) in [(2, 3, 6), (3, 4, 7), (1, 2, 5)]:
+        inp = dict(emissions=np.zeros((1, L, C), np.float32), lengths=np.array([L], np.int32),
+                   trans=np.zeros((C, C), np.float32), dur=np.zeros((K, C), np.float32))
+        vit = oracle_mod.viterbi(inp)
+        n = vit["num_segs"][0]
+        assert n == L
+        assert np.all(vit["seg_len"][0, :n] == 1)
+        assert np.all(vit["seg_label"][0, :n] == 0)
+        assert np.all(vit["seg_start"][0, :n] == np.arange(L))
+        assert vit["min_margin"][0] == 0.0
