@@ -68,8 +68,8 @@ def brute_force(inp, center=True, grad_logz=None):
     """Exact log Z, coverage marginals, parameter gradients and the MAP
     segmentation by enumeration.  Returns a dict like oracle.fwd_bwd plus
     'viterbi' = list of (best_score, segments) per sequence, where among
-    equal scores the first in enumeration order is kept (ties are reported
-    separately via 'viterbi_ties')."""
+    maximisers the first in enumeration order is kept; 'viterbi_ties' lists
+    every segmentation within rounding (1e-9 relative) of the maximum."""
     x = np.asarray(inp["emissions"], dtype=np.float64)
     lengths = np.asarray(inp["lengths"])
     trans = np.asarray(inp["trans"], dtype=np.float64)
@@ -104,7 +104,9 @@ def brute_force(inp, center=True, grad_logz=None):
         else:
             gx[b, :L] = w[b] * mu[b, :L]
         best = scores.max()
-        idx = [i for i in range(len(items)) if scores[i] == best]
+        # maximisers up to rounding: reordering segment lengths inside a run of
+        # one label gives exactly equal scores in real arithmetic
+        idx = [i for i in range(len(items)) if scores[i] >= best - 1e-9 * (abs(best) + 1.0)]
         vit.append((float(best), items[idx[0]][0]))
         ties.append([items[i][0] for i in idx])
     return dict(logz=logz, marginals=mu, grad_emissions=gx, grad_trans=gt, grad_dur=gd,

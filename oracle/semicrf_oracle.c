@@ -43,9 +43,14 @@
  *   dF/d trans[c',c]   = sum_b w_b sum_t P(t,c'->c)
  *   dF/d x[b,i,c]      = w_b (mu[i,c] - (1/L) sum_j mu[j,c])   (centred: nu depends on x)
  *                      = w_b mu[i,c]                          (centring off)
- * Viterbi is the same programme in the (max,+) semiring; ties are broken
- * towards the smallest duration k, then the smallest previous label c', and
- * at the end towards the smallest final label c.
+ * Viterbi is the same programme in the (max,+) semiring.  Segmentations that
+ * differ only in the order of segment lengths inside a run of one label score
+ * exactly the same in real arithmetic, so ties are structural; in floating
+ * point such tied candidates differ by rounding only.  A candidate therefore
+ * ties with the maximum when it lies within eps = 1e-11 * (|max| + 1) of it;
+ * among tied candidates the smallest duration k wins, then the smallest
+ * previous label c', and at the end the smallest final label c.  The stored
+ * programme value is the maximum itself.
  *
  * Parity pins for every function here live in tests/test_oracle_*.py
  * (brute-force enumeration, K=1 linear-chain reduction, closed forms,
@@ -73,6 +78,12 @@ static double lse_array(const double *v, int n)
     double s = 0.0;
     for (int i = 0; i < n; ++i) s += exp(v[i] - m);
     return m + log(s);
+}
+
+/* tie tolerance of the Viterbi decisions (see the file header) */
+static double tie_eps(double best)
+{
+    return 1e-11 * (fabs(best) + 1.0);
 }
 
 static int pick_threads(int nthreads)
@@ -345,8 +356,9 @@ int oracle_fwd_bwd(int B, int T, int C, int K, const float *x, const int32_t *le
 
 /* Viterbi (max,+) decoding.  Segments of sequence b are written at
  * [b*T + j] for j < num_segs[b]; remaining slots are set to -1.
- * min_margin (optional): smallest gap between the winning and the best
- * losing candidate over the decisions on the returned path (0 on a tie). */
+ * min_margin (optional): over the decisions on the returned path, the
+ * smallest gap between the maximum and the best candidate outside its tie
+ * set (+inf when every candidate tied). */
 int oracle_viterbi(int B, int T, int C, int K, const float *x, const int32_t *lengths,
                    const float *trans, const float *dur, int center, double *best_score,
                    int32_t *seg_start, int32_t *seg_len, int32_t *seg_label,
@@ -387,43 +399,57 @@ int oracle_viterbi(int B, int T, int C, int K, const float *x, const int32_t *le
         for (int t = 1; t <= L; ++t) {
             int kmax = t < K ? t : K;
             for (int c = 0; c < C; ++c) {
-                double best = ORACLE_NEG_INF, second = ORACLE_NEG_INF;
+                double best = ORACLE_NEG_INF;
+                for (int k = 1; k <= kmax; ++k) {
+                    double val = ((S[(size_t)t * C + c] - S[(size_t)(t - k) * C + c])
+                                  + (double)dur[(size_t)(k - 1) * C + c])
+                               + uh[(size_t)(t - k) * C + c];
+                    if (val > best) best = val;
+                }
+                double eps = tie_eps(best), outside = ORACLE_NEG_INF;
                 int arg = 0;
                 for (int k = 1; k <= kmax; ++k) {
                     double val = ((S[(size_t)t * C + c] - S[(size_t)(t - k) * C + c])
                                   + (double)dur[(size_t)(k - 1) * C + c])
                                + uh[(size_t)(t - k) * C + c];
-                    if (val > best) { second = best; best = val; arg = k; }
-                    else if (val > second) second = val;
+                    if (val >= best - eps) { if (arg == 0) arg = k; }
+                    else if (val > outside) outside = val;
                 }
                 ah[(size_t)t * C + c] = best;
                 bk[(size_t)t * C + c] = arg;
-                mk[(size_t)t * C + c] = best - second;
+                mk[(size_t)t * C + c] = best - outside;
             }
             if (t < L) {
                 for (int c = 0; c < C; ++c) {
-                    double best = ORACLE_NEG_INF, second = ORACLE_NEG_INF;
-                    int arg = 0;
+                    double best = ORACLE_NEG_INF;
                     for (int cp = 0; cp < C; ++cp) {
                         double val = ah[(size_t)t * C + cp] + (double)trans[(size_t)cp * C + c];
-                        if (val > best) { second = best; best = val; arg = cp; }
-                        else if (val > second) second = val;
+                        if (val > best) best = val;
+                    }
+                    double eps = tie_eps(best), outside = ORACLE_NEG_INF;
+                    int arg = -1;
+                    for (int cp = 0; cp < C; ++cp) {
+                        double val = ah[(size_t)t * C + cp] + (double)trans[(size_t)cp * C + c];
+                        if (val >= best - eps) { if (arg < 0) arg = cp; }
+                        else if (val > outside) outside = val;
                     }
                     uh[(size_t)t * C + c] = best;
                     bc[(size_t)t * C + c] = arg;
-                    mc[(size_t)t * C + c] = best - second;
+                    mc[(size_t)t * C + c] = best - outside;
                 }
             }
         }
-        double best = ORACLE_NEG_INF, second = ORACLE_NEG_INF;
-        int cbest = 0;
+        double best = ORACLE_NEG_INF, outside = ORACLE_NEG_INF;
+        for (int c = 0; c < C; ++c)
+            if (ah[(size_t)L * C + c] > best) best = ah[(size_t)L * C + c];
+        int cbest = -1;
         for (int c = 0; c < C; ++c) {
             double val = ah[(size_t)L * C + c];
-            if (val > best) { second = best; best = val; cbest = c; }
-            else if (val > second) second = val;
+            if (val >= best - tie_eps(best)) { if (cbest < 0) cbest = c; }
+            else if (val > outside) outside = val;
         }
         best_score[b] = best;
-        double margin = best - second;
+        double margin = best - outside;
         /* backtrack, then reverse into the output slots */
         int nseg = 0;
         int t = L, c = cbest;
@@ -432,6 +458,7 @@ int oracle_viterbi(int B, int T, int C, int K, const float *x, const int32_t *le
         int32_t *tmp_c = malloc((size_t)L * sizeof(int32_t));
         while (t > 0) {
             int k = bk[(size_t)t * C + c];
+            if (k < 1 || k > t) k = t; /* only with non-finite scores */
             double m1 = mk[(size_t)t * C + c];
             if (m1 < margin) margin = m1;
             tmp_s[nseg] = t - k; tmp_k[nseg] = k; tmp_c[nseg] = c;
@@ -441,6 +468,7 @@ int oracle_viterbi(int B, int T, int C, int K, const float *x, const int32_t *le
                 double m2 = mc[(size_t)s * C + c];
                 if (m2 < margin) margin = m2;
                 c = bc[(size_t)s * C + c];
+                if (c < 0) c = 0; /* only with non-finite scores */
             }
             t = s;
         }

@@ -53,6 +53,27 @@ def test_enumeration_counts_match_closed_form():
         assert np.isclose(np.log(n), closed_form.log_count(L, C, K))
 
 
+def test_viterbi_structural_ties(oracle_mod):
+    """Two segments of one label in either order score the same: the
+    smallest-k rule picks the shorter segment first at the later end point,
+    i.e. the longer segment is placed first."""
+    C, K, L = 2, 4, 6
+    x = np.zeros((1, L, C), np.float32)
+    x[0, :, 0] = 1.0  # label 0 everywhere is best
+    dur = np.full((K, C), -5.0, np.float32)
+    dur[1, 0] = 0.25   # length 2
+    dur[3, 0] = 0.6    # length 4: {2,4} in either order beats {2,2,2}
+    trans = np.zeros((C, C), np.float32)
+    inp = dict(emissions=x, lengths=np.array([L], np.int32), trans=trans, dur=dur)
+    vit = oracle_mod.viterbi(inp, center=False)
+    n = vit["num_segs"][0]
+    segs = [(int(vit["seg_start"][0, j]), int(vit["seg_len"][0, j]), int(vit["seg_label"][0, j]))
+            for j in range(n)]
+    assert segs == [(0, 4, 0), (4, 2, 0)]
+    bf = bruteforce.brute_force(inp, center=False)
+    assert segs in bf["viterbi_ties"][0] and len(bf["viterbi_ties"][0]) == 2
+
+
 def test_viterbi_tie_break_rule_on_enumeration(oracle_mod):
     """Zero potentials: every segmentation ties; the stated rule (smallest k,
     then smallest previous label, smallest final label) yields L unit
@@ -66,4 +87,4 @@ def test_viterbi_tie_break_rule_on_enumeration(oracle_mod):
         assert np.all(vit["seg_len"][0, :n] == 1)
         assert np.all(vit["seg_label"][0, :n] == 0)
         assert np.all(vit["seg_start"][0, :n] == np.arange(L))
-        assert vit["min_margin"][0] == 0.0
+        assert vit["min_margin"][0] == np.inf  # every candidate is in the tie set
