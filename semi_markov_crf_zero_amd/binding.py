@@ -1,0 +1,243 @@
+"""ctypes binding of libsemicrf.so (the C ABI in include/semicrf.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels of the library.  Functions carry the C names; tensors must be CUDA
+(HIP) tensors, contiguous, float32 (emissions, trans, dur, grad_logz) and
+int32 (lengths).  Outputs and the workspace are allocated with torch on the
+input's device and the work is enqueued on torch's current stream.
+
+If the library has not been built this module raises at the first call;
+there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsemicrf.so")
+
+OP_SCAN, OP_LOGZ, OP_FWD_BWD, OP_VITERBI = 0, 1, 2, 3
+NO_CENTER = 1
+
+STATUS = {
+    0: "SEMICRF_OK", 1: "SEMICRF_ERR_NULL", 2: "SEMICRF_ERR_SHAPE",
+    3: "SEMICRF_ERR_UNSUPPORTED", 4: "SEMICRF_ERR_WORKSPACE", 5: "SEMICRF_ERR_HIP",
+    6: "SEMICRF_ERR_ARG",
+}
+
+EXPORTS = (
+    "semicrf_status_string", "semicrf_default_checkpoint_interval", "semicrf_workspace_size",
+    "semicrf_cumulative_scores", "semicrf_logz_fwd", "semicrf_fwd_bwd", "semicrf_fwd_bwd_timed",
+    "semicrf_viterbi",
+)
+FWD_BWD_PHASES = ("cumulative_scores", "k_sweep", "k_chunk", "reductions")
+
+
+class SemiCRFError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__("%s failed: %s (%s)" % (what, STATUS.get(code, code), status_string(code)))
+
+
+_lib = None
+
+
+def load():
+    """Load libsemicrf.so and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libsemicrf.so is not built (run: python -m semi_markov_crf_zero_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, U, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+    lib.semicrf_status_string.argtypes = [I]
+    lib.semicrf_status_string.restype = ctypes.c_char_p
+    lib.semicrf_default_checkpoint_interval.argtypes = [I, I]
+    lib.semicrf_default_checkpoint_interval.restype = I
+    lib.semicrf_workspace_size.argtypes = [I, I, I, I, I, U, I, ctypes.POINTER(Z)]
+    lib.semicrf_workspace_size.restype = I
+    lib.semicrf_cumulative_scores.argtypes = [P, P, I, I, I, U, P, P, P, Z, P]
+    lib.semicrf_cumulative_scores.restype = I
+    lib.semicrf_logz_fwd.argtypes = [P, P, P, P, I, I, I, I, U, P, P, Z, P]
+    lib.semicrf_logz_fwd.restype = I
+    lib.semicrf_fwd_bwd.argtypes = [P, P, P, P, I, I, I, I, U, I, P, P, P, P, P, P, P, Z, P]
+    lib.semicrf_fwd_bwd.restype = I
+    lib.semicrf_fwd_bwd_timed.argtypes = [P, P, P, P, I, I, I, I, U, I, P, P, P, P, P, P, P, Z, P,
+                                          P]
+    lib.semicrf_fwd_bwd_timed.restype = I
+    lib.semicrf_viterbi.argtypes = [P, P, P, P, I, I, I, I, U, P, P, P, P, P, P, Z, P]
+    lib.semicrf_viterbi.restype = I
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().semicrf_status_string(int(code)).decode()
+
+
+def semicrf_default_checkpoint_interval(T: int, K: int) -> int:
+    return int(load().semicrf_default_checkpoint_interval(int(T), int(K)))
+
+
+def semicrf_workspace_size(op: int, B: int, T: int, C: int, K: int, flags: int = 0,
+                           checkpoint_interval: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().semicrf_workspace_size(op, B, T, C, K, flags, checkpoint_interval, ctypes.byref(n))
+    if rc:
+        raise SemiCRFError(rc, "semicrf_workspace_size")
+    return int(n.value)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check_inputs(emissions, lengths, trans=None, dur=None):
+    if emissions.dim() != 3:
+        raise ValueError("emissions must be [B, T, C]")
+    B, T, C = emissions.shape
+    dev = emissions.device
+    if dev.type != "cuda":
+        raise ValueError("semicrf runs on the GPU only; got a %s tensor" % dev.type)
+    for name, t, dt in (("emissions", emissions, torch.float32), ("lengths", lengths, torch.int32),
+                        ("trans", trans, torch.float32), ("dur", dur, torch.float32)):
+        if t is None:
+            continue
+        if t.device != dev or t.dtype != dt or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous %s tensor on %s" % (name, dt, dev))
+    if lengths.shape != (B,):
+        raise ValueError("lengths must be [B]")
+    K = None
+    if trans is not None and trans.shape != (C, C):
+        raise ValueError("trans must be [C, C]")
+    if dur is not None:
+        if dur.dim() != 2 or dur.shape[1] != C:
+            raise ValueError("dur must be [K, C]")
+        K = dur.shape[0]
+    return B, T, C, K, dev
+
+
+def _workspace(op, B, T, C, K, flags, ckpt, dev):
+    n = semicrf_workspace_size(op, B, T, C, K, flags, ckpt)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=dev), n
+
+
+def semicrf_cumulative_scores(emissions, lengths, center: bool = True):
+    """Row (a): returns (nu [B,C] float64, S [B,T+1,C] float64)."""
+    B, T, C, _, dev = _check_inputs(emissions, lengths)
+    flags = 0 if center else NO_CENTER
+    ws, n = _workspace(OP_SCAN, B, T, C, 1, flags, 0, dev)
+    nu = torch.empty((B, C), dtype=torch.float64, device=dev)
+    S = torch.empty((B, T + 1, C), dtype=torch.float64, device=dev)
+    rc = load().semicrf_cumulative_scores(_ptr(emissions), _ptr(lengths), B, T, C, flags, _ptr(nu),
+                                          _ptr(S), _ptr(ws), n, _stream(dev))
+    if rc:
+        raise SemiCRFError(rc, "semicrf_cumulative_scores")
+    return nu, S
+
+
+def semicrf_logz_fwd(emissions, lengths, trans, dur, center: bool = True):
+    """log Z [B] float32."""
+    B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
+    flags = 0 if center else NO_CENTER
+    ws, n = _workspace(OP_LOGZ, B, T, C, K, flags, 0, dev)
+    out = torch.empty(B, dtype=torch.float32, device=dev)
+    rc = load().semicrf_logz_fwd(_ptr(emissions), _ptr(lengths), _ptr(trans), _ptr(dur), B, T, C,
+                                 K, flags, _ptr(out), _ptr(ws), n, _stream(dev))
+    if rc:
+        raise SemiCRFError(rc, "semicrf_logz_fwd")
+    return out
+
+
+class FwdBwdPlan:
+    """Preallocated outputs + workspace for repeated semicrf_fwd_bwd calls on
+    one shape (the benchmark times `run()` alone)."""
+
+    def __init__(self, emissions, lengths, trans, dur, center=True, grad_logz=None,
+                 checkpoint_interval=0, want_marginals=False):
+        B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
+        if grad_logz is not None and (grad_logz.shape != (B,) or grad_logz.dtype != torch.float32
+                                      or grad_logz.device != dev):
+            raise ValueError("grad_logz must be a float32 [B] tensor on %s" % dev)
+        self.args = (emissions, lengths, trans, dur)
+        self.B, self.T, self.C, self.K = B, T, C, K
+        self.flags = 0 if center else NO_CENTER
+        self.ckpt = int(checkpoint_interval)
+        self.grad_logz = grad_logz
+        self.dev = dev
+        self.ws, self.ws_bytes = _workspace(OP_FWD_BWD, B, T, C, K, self.flags, self.ckpt, dev)
+        self.logz = torch.empty(B, dtype=torch.float32, device=dev)
+        self.grad_emissions = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+        self.grad_trans = torch.empty((C, C), dtype=torch.float32, device=dev)
+        self.grad_dur = torch.empty((K, C), dtype=torch.float32, device=dev)
+        self.marginals = (torch.empty((B, T, C), dtype=torch.float32, device=dev)
+                          if want_marginals else None)
+
+    def run(self, stream=None, phase_events=None):
+        """Enqueue one fwd+bwd.  phase_events: optional list of
+        len(FWD_BWD_PHASES)+1 recorded torch.cuda.Event(enable_timing=True)
+        objects; the library re-records them around its phases."""
+        e, l, t, d = self.args
+        st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(self.dev)
+        evs = None
+        if phase_events is not None:
+            if len(phase_events) != len(FWD_BWD_PHASES) + 1:
+                raise ValueError("need %d events" % (len(FWD_BWD_PHASES) + 1))
+            evs = (ctypes.c_void_p * len(phase_events))(*[ev.cuda_event for ev in phase_events])
+        rc = load().semicrf_fwd_bwd_timed(
+            _ptr(e), _ptr(l), _ptr(t), _ptr(d), self.B, self.T, self.C, self.K, self.flags,
+            self.ckpt, _ptr(self.grad_logz), _ptr(self.logz), _ptr(self.grad_emissions),
+            _ptr(self.grad_trans), _ptr(self.grad_dur), _ptr(self.marginals), _ptr(self.ws),
+            self.ws_bytes, st, evs)
+        if rc:
+            raise SemiCRFError(rc, "semicrf_fwd_bwd")
+        return self
+
+    def outputs(self):
+        out = dict(logz=self.logz, grad_emissions=self.grad_emissions,
+                   grad_trans=self.grad_trans, grad_dur=self.grad_dur)
+        if self.marginals is not None:
+            out["marginals"] = self.marginals
+        return out
+
+
+def semicrf_fwd_bwd(emissions, lengths, trans, dur, center: bool = True, grad_logz=None,
+                    checkpoint_interval: int = 0, want_marginals: bool = False):
+    """Returns dict(logz, grad_emissions, grad_trans, grad_dur[, marginals])."""
+    plan = FwdBwdPlan(emissions, lengths, trans, dur, center, grad_logz, checkpoint_interval,
+                      want_marginals)
+    return plan.run().outputs()
+
+
+def semicrf_viterbi(emissions, lengths, trans, dur, center: bool = True):
+    """Returns dict(best_score [B] f32, seg_start/seg_len/seg_label [B,T] i32, num_segs [B] i32)."""
+    B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
+    flags = 0 if center else NO_CENTER
+    ws, n = _workspace(OP_VITERBI, B, T, C, K, flags, 0, dev)
+    best = torch.empty(B, dtype=torch.float32, device=dev)
+    ss = torch.empty((B, T), dtype=torch.int32, device=dev)
+    sl = torch.empty((B, T), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, T), dtype=torch.int32, device=dev)
+    ns = torch.empty(B, dtype=torch.int32, device=dev)
+    rc = load().semicrf_viterbi(_ptr(emissions), _ptr(lengths), _ptr(trans), _ptr(dur), B, T, C, K,
+                                flags, _ptr(best), _ptr(ss), _ptr(sl), _ptr(sc), _ptr(ns), _ptr(ws),
+                                n, _stream(dev))
+    if rc:
+        raise SemiCRFError(rc, "semicrf_viterbi")
+    return dict(best_score=best, seg_start=ss, seg_len=sl, seg_label=sc, num_segs=ns)
+
+
+# short aliases
+cumulative_scores = semicrf_cumulative_scores
+logz = semicrf_logz_fwd
+fwd_bwd = semicrf_fwd_bwd
+viterbi = semicrf_viterbi
+workspace_size = semicrf_workspace_size

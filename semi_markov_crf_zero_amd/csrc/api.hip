@@ -1,0 +1,313 @@
+// api.hip -- the extern "C" entry points declared in include/semicrf.h.
+//
+// Host side only: argument validation (before any launch), launch
+// configuration, workspace carve-up and launch sequencing on the caller's
+// stream.  No allocation, no synchronisation, no state between calls.
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/semicrf.h"
+#include "internal.h"
+
+using namespace semicrf;
+
+namespace {
+
+// Pick the chain workgroup shape for (C, K): the smallest workgroup whose
+// per-thread duration count fits the register arrays (32 at 256/512 threads,
+// 16 at 1024), whose contraction slices fit, and whose LDS fits 160 KB.
+bool chain_config(int C, int K, ChainShape &sh) {
+  if (C < 1 || C > kMaxC || K < 1 || (long long)K * C > kMaxKC) return false;
+  const int nts[3] = {256, 512, 1024};
+  const int amax[3] = {32, 32, 16};
+  const int Q = (C + 63) / 64;
+  for (int i = 0; i < 3; ++i) {
+    const int NT = nts[i];
+    const int P = NT / C;
+    if (P < 1 || Q * C > NT) continue;
+    const int A = (K + P - 1) / P;
+    if (A > amax[i]) continue;
+    if (chain_lds_bytes(C, K, P, Q) > kMaxLds) continue;
+    if (viterbi_lds_bytes(C, K, P, Q) > kMaxLds) continue;
+    sh.NT = NT;
+    sh.P = P;
+    sh.A = A;
+    sh.Q = Q;
+    return true;
+  }
+  return false;
+}
+
+semicrf_status_t check_sizes(int B, int T, int C, int K) {
+  if (B < 1 || T < 1 || C < 1 || K < 1) return SEMICRF_ERR_SHAPE;
+  if ((long long)B * (T + 1) * C >= (1LL << 31)) return SEMICRF_ERR_SHAPE;
+  return SEMICRF_OK;
+}
+
+int default_delta(int T, int K) {
+  double d = ceil(sqrt((double)T * (double)K));
+  if (d < 1) d = 1;
+  if (d > T) d = T;
+  return (int)d;
+}
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  }
+};
+
+// Workspace layout for an op.  Returns false for an invalid op.
+bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layout &lay) {
+  Carver cv;
+  lay = Layout{};
+  lay.ntile = (T + scan_tile(C) - 1) / scan_tile(C);
+  const size_t nS = (size_t)B * (T + 1) * C;
+  if (op != SEMICRF_OP_SCAN) {
+    lay.S = cv.take(nS * 8);
+    lay.nu = cv.take((size_t)B * C * 8);
+  }
+  lay.tile_sum = cv.take((size_t)B * lay.ntile * C * 8);
+  lay.anchor = cv.take((size_t)B * lay.ntile * C * 8);
+  switch (op) {
+    case SEMICRF_OP_SCAN:
+      break;
+    case SEMICRF_OP_LOGZ:
+      lay.logz = cv.take((size_t)B * 8);
+      break;
+    case SEMICRF_OP_FWD_BWD: {
+      const size_t nck = (size_t)B * sh->nchunk;
+      const size_t rows = (size_t)sh->delta + 1;
+      lay.logz = cv.take((size_t)B * 8);
+      lay.logz_bwd = cv.take((size_t)B * 8);
+      lay.ck_fwd = cv.take(nck * (size_t)(K + 3) * C * 8);
+      lay.ck_bwd = cv.take(nck * (size_t)(K + 3) * C * 8);
+      lay.scr_a = cv.take(nck * rows * C * 8);
+      lay.scr_u = cv.take(nck * rows * C * 8);
+      lay.scr_ea = cv.take(nck * rows * C * 4);
+      lay.scr_ev = cv.take(nck * rows * C * 4);
+      lay.part_x = cv.take(nck * (size_t)C * C * 8);
+      lay.part_gd = cv.take(nck * (size_t)K * C * 8);
+      lay.part_tot = cv.take(nck * C * 8);
+      lay.part_ssum = cv.take(nck * C * 8);
+      lay.carry = cv.take(nck * C * 8);
+      lay.mean = cv.take((size_t)B * C * 8);
+      break;
+    }
+    case SEMICRF_OP_VITERBI:
+      lay.bp = cv.take(nS * 4);
+      lay.vbest = cv.take((size_t)B * 8);
+      lay.vcbest = cv.take((size_t)B * 4);
+      break;
+    default:
+      return false;
+  }
+  lay.total = cv.off;
+  return true;
+}
+
+// Validate sizes/flags and fill the shape + layout.  No launches.
+semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int ckpt,
+                         ChainShape &sh, Layout &lay) {
+  if (op < SEMICRF_OP_SCAN || op > SEMICRF_OP_VITERBI) return SEMICRF_ERR_ARG;
+  if (flags & ~(unsigned)SEMICRF_NO_CENTER) return SEMICRF_ERR_ARG;
+  if (ckpt < 0) return SEMICRF_ERR_ARG;
+  const semicrf_status_t s = check_sizes(B, T, C, op == SEMICRF_OP_SCAN ? 1 : K);
+  if (s != SEMICRF_OK) return s;
+  if (C > kMaxC) return SEMICRF_ERR_UNSUPPORTED;
+  sh = ChainShape{};
+  sh.B = B;
+  sh.T = T;
+  sh.C = C;
+  sh.K = K;
+  sh.center = (flags & SEMICRF_NO_CENTER) ? 0 : 1;
+  if (op != SEMICRF_OP_SCAN) {
+    if (!chain_config(C, K, sh)) return SEMICRF_ERR_UNSUPPORTED;
+    sh.delta = ckpt > 0 ? (ckpt < T ? ckpt : T) : default_delta(T, K);
+    sh.nchunk = (T + sh.delta - 1) / sh.delta;
+  }
+  if (!make_layout(op, B, T, C, K, &sh, lay)) return SEMICRF_ERR_ARG;
+  return SEMICRF_OK;
+}
+
+template <typename P>
+P *at(void *ws, size_t off) {
+  return reinterpret_cast<P *>(static_cast<unsigned char *>(ws) + off);
+}
+
+// With SEMICRF_DEBUG set in the environment, name the HIP error on stderr.
+semicrf_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return SEMICRF_OK;
+  if (getenv("SEMICRF_DEBUG")) fprintf(stderr, "semicrf: HIP error %d: %s\n", (int)e, hipGetErrorString(e));
+  return SEMICRF_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *semicrf_status_string(semicrf_status_t status) {
+  switch (status) {
+    case SEMICRF_OK: return "ok";
+    case SEMICRF_ERR_NULL: return "a required pointer is NULL";
+    case SEMICRF_ERR_SHAPE: return "invalid sizes (B, T, C, K must be >= 1; B*(T+1)*C < 2^31)";
+    case SEMICRF_ERR_UNSUPPORTED: return "unsupported C or K (see semicrf.h)";
+    case SEMICRF_ERR_WORKSPACE: return "workspace NULL or smaller than semicrf_workspace_size";
+    case SEMICRF_ERR_HIP: return "HIP launch failed";
+    case SEMICRF_ERR_ARG: return "invalid op, flags or checkpoint interval";
+  }
+  return "unknown status";
+}
+
+int semicrf_default_checkpoint_interval(int T, int K) {
+  if (T < 1 || K < 1) return 0;
+  return default_delta(T, K);
+}
+
+semicrf_status_t semicrf_workspace_size(int op, int B, int T, int C, int K, unsigned flags,
+                                        int checkpoint_interval, size_t *bytes) {
+  if (!bytes) return SEMICRF_ERR_NULL;
+  ChainShape sh;
+  Layout lay;
+  const semicrf_status_t s =
+      prepare(op, B, T, C, K, flags, op == SEMICRF_OP_FWD_BWD ? checkpoint_interval : 0, sh, lay);
+  if (s != SEMICRF_OK) return s;
+  *bytes = lay.total;
+  return SEMICRF_OK;
+}
+
+semicrf_status_t semicrf_cumulative_scores(const float *emissions, const int32_t *lengths, int B,
+                                           int T, int C, unsigned flags, double *nu, double *S,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *stream) {
+  if (!emissions || !lengths || !nu || !S) return SEMICRF_ERR_NULL;
+  ChainShape sh;
+  Layout lay;
+  const semicrf_status_t s = prepare(SEMICRF_OP_SCAN, B, T, C, 1, flags, 0, sh, lay);
+  if (s != SEMICRF_OK) return s;
+  if (!workspace || workspace_bytes < lay.total) return SEMICRF_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  return hip_status(launch_scan(emissions, lengths, B, T, C, sh.center, nu, S,
+                                at<double>(workspace, lay.tile_sum),
+                                at<double>(workspace, lay.anchor), lay.ntile, st));
+}
+
+semicrf_status_t semicrf_logz_fwd(const float *emissions, const int32_t *lengths,
+                                  const float *trans, const float *dur, int B, int T, int C, int K,
+                                  unsigned flags, float *logz, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  if (!emissions || !lengths || !trans || !dur || !logz) return SEMICRF_ERR_NULL;
+  ChainShape sh;
+  Layout lay;
+  const semicrf_status_t s = prepare(SEMICRF_OP_LOGZ, B, T, C, K, flags, 0, sh, lay);
+  if (s != SEMICRF_OK) return s;
+  if (!workspace || workspace_bytes < lay.total) return SEMICRF_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  double *S = at<double>(workspace, lay.S);
+  hipError_t e = launch_scan(emissions, lengths, B, T, C, sh.center, at<double>(workspace, lay.nu),
+                             S, at<double>(workspace, lay.tile_sum),
+                             at<double>(workspace, lay.anchor), lay.ntile, st);
+  if (e != hipSuccess) return hip_status(e);
+  e = launch_sweep(sh, trans, dur, S, lengths, nullptr, nullptr, at<double>(workspace, lay.logz),
+                   nullptr, logz, 0, 0, st);
+  return hip_status(e);
+}
+
+semicrf_status_t semicrf_fwd_bwd_timed(const float *emissions, const int32_t *lengths,
+                                       const float *trans, const float *dur, int B, int T, int C,
+                                       int K, unsigned flags, int checkpoint_interval,
+                                       const float *grad_logz, float *logz,
+                                       float *grad_emissions, float *grad_trans, float *grad_dur,
+                                       float *marginals, void *workspace, size_t workspace_bytes,
+                                       void *stream, void *const *phase_events) {
+  if (!emissions || !lengths || !trans || !dur || !logz || !grad_emissions || !grad_trans ||
+      !grad_dur)
+    return SEMICRF_ERR_NULL;
+  ChainShape sh;
+  Layout lay;
+  const semicrf_status_t s =
+      prepare(SEMICRF_OP_FWD_BWD, B, T, C, K, flags, checkpoint_interval, sh, lay);
+  if (s != SEMICRF_OK) return s;
+  if (!workspace || workspace_bytes < lay.total) return SEMICRF_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  auto mark = [&](int i) {
+    if (phase_events) (void)hipEventRecord(static_cast<hipEvent_t>(phase_events[i]), st);
+  };
+  void *ws = workspace;
+  double *S = at<double>(ws, lay.S);
+  mark(0);
+  hipError_t e = launch_scan(emissions, lengths, B, T, C, sh.center, at<double>(ws, lay.nu), S,
+                             at<double>(ws, lay.tile_sum), at<double>(ws, lay.anchor), lay.ntile,
+                             st);
+  if (e != hipSuccess) return hip_status(e);
+  mark(1);
+  e = launch_sweep(sh, trans, dur, S, lengths, at<double>(ws, lay.ck_fwd),
+                   at<double>(ws, lay.ck_bwd), at<double>(ws, lay.logz),
+                   at<double>(ws, lay.logz_bwd), logz, 1, 1, st);
+  if (e != hipSuccess) return hip_status(e);
+  mark(2);
+  e = launch_chunks(sh, trans, dur, S, lengths, at<double>(ws, lay.ck_fwd),
+                    at<double>(ws, lay.ck_bwd), at<double>(ws, lay.logz),
+                    at<double>(ws, lay.scr_a), at<double>(ws, lay.scr_u),
+                    at<float>(ws, lay.scr_ea), at<float>(ws, lay.scr_ev),
+                    at<double>(ws, lay.part_x), at<double>(ws, lay.part_gd),
+                    at<double>(ws, lay.part_tot), at<double>(ws, lay.part_ssum), grad_emissions,
+                    st);
+  if (e != hipSuccess) return hip_status(e);
+  mark(3);
+  e = launch_finish(sh, trans, lengths, grad_logz, at<double>(ws, lay.part_x),
+                    at<double>(ws, lay.part_gd), at<double>(ws, lay.part_tot),
+                    at<double>(ws, lay.part_ssum), at<double>(ws, lay.carry),
+                    at<double>(ws, lay.mean), grad_trans, grad_dur, grad_emissions, marginals, st);
+  if (e != hipSuccess) return hip_status(e);
+  mark(SEMICRF_FWD_BWD_PHASES);
+  return SEMICRF_OK;
+}
+
+semicrf_status_t semicrf_fwd_bwd(const float *emissions, const int32_t *lengths,
+                                 const float *trans, const float *dur, int B, int T, int C, int K,
+                                 unsigned flags, int checkpoint_interval, const float *grad_logz,
+                                 float *logz, float *grad_emissions, float *grad_trans,
+                                 float *grad_dur, float *marginals, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+  return semicrf_fwd_bwd_timed(emissions, lengths, trans, dur, B, T, C, K, flags,
+                               checkpoint_interval, grad_logz, logz, grad_emissions, grad_trans,
+                               grad_dur, marginals, workspace, workspace_bytes, stream, nullptr);
+}
+
+semicrf_status_t semicrf_viterbi(const float *emissions, const int32_t *lengths,
+                                 const float *trans, const float *dur, int B, int T, int C, int K,
+                                 unsigned flags, float *best_score, int32_t *seg_start,
+                                 int32_t *seg_len, int32_t *seg_label, int32_t *num_segs,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+  if (!emissions || !lengths || !trans || !dur || !best_score || !seg_start || !seg_len ||
+      !seg_label || !num_segs)
+    return SEMICRF_ERR_NULL;
+  ChainShape sh;
+  Layout lay;
+  const semicrf_status_t s = prepare(SEMICRF_OP_VITERBI, B, T, C, K, flags, 0, sh, lay);
+  if (s != SEMICRF_OK) return s;
+  if (K > 65535 || C > 65535) return SEMICRF_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < lay.total) return SEMICRF_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  void *ws = workspace;
+  double *S = at<double>(ws, lay.S);
+  hipError_t e = launch_scan(emissions, lengths, B, T, C, sh.center, at<double>(ws, lay.nu), S,
+                             at<double>(ws, lay.tile_sum), at<double>(ws, lay.anchor), lay.ntile,
+                             st);
+  if (e != hipSuccess) return hip_status(e);
+  e = launch_viterbi(sh, trans, dur, S, lengths, at<uint32_t>(ws, lay.bp),
+                     at<double>(ws, lay.vbest), at<int32_t>(ws, lay.vcbest), best_score,
+                     seg_start, seg_len, seg_label, num_segs, st);
+  return hip_status(e);
+}
+
+}  // extern "C"

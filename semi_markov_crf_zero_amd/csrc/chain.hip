@@ -1,0 +1,744 @@
+// chain.hip -- streaming semi-CRF forward-backward on gfx950.
+//
+// Method ("Streaming Structured Inference with Flash-SemiCRF"; abstract and
+// technical summary at gist.science, sections 2.A-2.C):
+//   * segment scores are read on the fly from the cumulative scores S
+//     (scan.hip); no edge tensor exists anywhere;
+//   * the forward and backward messages stream through a ring buffer of the
+//     K most recent rows (section 2.B);
+//   * the forward state is stored every `delta` ~ sqrt(T*K) positions
+//     together with its running log normaliser, and the backward pass
+//     recomputes the forward messages between those checkpoints (2.C).
+//
+// Recurrences (0-based, per sequence of length L; sigma = +1 forward, -1
+// backward; "entry" is what a position contributes to the ring):
+//   forward   o[t,c] = alpha[t,c] = S[t,c] + LSE_{k<=min(K,t)} (dur[k-1,c] + g[t-k,c])
+//             m[t,c] = u[t,c]     = LSE_{c'} (alpha[t,c'] + trans[c',c]);  u[0,.] = 0
+//             entry  g[t,c]       = u[t,c] - S[t,c]
+//   backward  o[t,c] = v[t,c]     = -S[t,c] + LSE_{k<=min(K,L-t)} (dur[k-1,c] + h[t+k,c])
+//             m[t,c] = beta[t,c]  = LSE_{c'} (trans[c,c'] + v[t,c']);    beta[L,.] = 0
+//             entry  h[t,c]       = beta[t,c] + S[t,c]
+// This is the plain semi-CRF dynamic programme (score of a segment [s,s+k)
+// with label c = S[s+k,c] - S[s,c] + dur[k-1,c]) written in the ring's
+// variables.
+//
+// MI355X design:
+//   * exp-space ring in LDS: ring[slot][c] = exp(entry - ref[c]) in float64,
+//     ref[c] a per-label float64 log reference.  The K-way log-sum-exp becomes
+//     a K-term float64 dot product with D[k][c] = exp(dur[k-1][c]) (no
+//     transcendental per segment cell).  Whenever a new entry leaves
+//     [2^-260, 2^260] relative to ref[c], the label's column is rescaled by
+//     an exact power of two (v_ldexp_f64) and ref[c] moves by n*ln2.  The
+//     recurrence guarantees g[t] >= g[t-k] + trans[c,c] + dur[k-1,c] (and the
+//     mirror for h), so older ring entries never exceed the newest by more
+//     than a parameter-bounded factor, and the rescale keeps every entry in
+//     float64 range.
+//   * the transition contraction is an exp-space matrix-vector product with
+//     exp(trans) held in registers (fp32), max-shifted per row.
+//   * one workgroup per chain; the forward and the backward chain of every
+//     sequence run concurrently (they are independent).  The marginal pass is
+//     chunk-parallel: one workgroup per (sequence, checkpoint interval)
+//     recomputes alpha from the forward checkpoint and beta from the backward
+//     checkpoint and accumulates the posteriors.
+//   * parameter-gradient partials are per chunk and reduced in a fixed order
+//     in float64 (deterministic; no floating-point atomics).
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "device_math.h"
+#include "internal.h"
+
+namespace semicrf {
+
+constexpr double kRebaseNats = 180.0;  // ~2^260
+
+struct Smem {
+  double *ring, *part, *orow, *refs, *scal;
+  float *erow, *dotp;
+  int *shiftn;
+};
+
+__device__ __forceinline__ Smem carve(unsigned char *base, const ChainShape &s) {
+  Smem m;
+  size_t off = 0;
+  m.ring = reinterpret_cast<double *>(base + off); off += (size_t)s.K * s.C * 8;
+  m.part = reinterpret_cast<double *>(base + off); off += (size_t)s.P * s.C * 8;
+  m.orow = reinterpret_cast<double *>(base + off); off += (size_t)s.C * 8;
+  m.refs = reinterpret_cast<double *>(base + off); off += (size_t)s.C * 8;
+  m.scal = reinterpret_cast<double *>(base + off); off += 8 * 8;
+  m.erow = reinterpret_cast<float *>(base + off); off += (size_t)s.C * 4;
+  m.dotp = reinterpret_cast<float *>(base + off); off += (size_t)s.Q * s.C * 4;
+  m.shiftn = reinterpret_cast<int *>(base + off);
+  return m;
+}
+
+// Per-thread constants of one chain direction.
+template <int AMAX, int TRMAX, typename DT>
+struct Regs {
+  DT D[AMAX];       // exp(dur[k-1][c]) for the thread's durations
+  float Tr[TRMAX];  // exp(trans) slice for the contraction role
+  int kc, kp, age0, nage;
+  int cc, cq, cp0, ncp;
+};
+
+template <int AMAX, int TRMAX, typename DT>
+__device__ __forceinline__ void init_regs(Regs<AMAX, TRMAX, DT> &r, const ChainShape &sh,
+                                          const float *__restrict__ dur) {
+  const int tid = threadIdx.x, C = sh.C;
+  r.kc = tid % C;
+  r.kp = tid / C;
+  r.age0 = r.kp * sh.A + 1;
+  int n = (r.kp < sh.P) ? sh.K - r.age0 + 1 : 0;
+  n = n < 0 ? 0 : (n > sh.A ? sh.A : n);
+  r.nage = n;
+#pragma unroll
+  for (int j = 0; j < AMAX; ++j)
+    r.D[j] = (j < r.nage) ? (DT)exp((double)dur[(size_t)(r.age0 + j - 1) * C + r.kc]) : (DT)0;
+  r.cc = tid % C;
+  r.cq = tid / C;
+  r.cp0 = r.cq * 64;
+  int m = (r.cq < sh.Q) ? C - r.cp0 : 0;
+  r.ncp = m < 0 ? 0 : (m > 64 ? 64 : m);
+}
+
+// Contraction weights for direction `fwd`: forward sums over the previous
+// label c' (rows of trans), backward over the next label (columns).
+template <int AMAX, int TRMAX, typename DT>
+__device__ __forceinline__ void load_trans(Regs<AMAX, TRMAX, DT> &r, const ChainShape &sh,
+                                           const float *__restrict__ trans, bool fwd) {
+  const int C = sh.C;
+#pragma unroll
+  for (int j = 0; j < TRMAX; ++j) {
+    float w = 0.f;
+    if (j < r.ncp) {
+      const int cp = r.cp0 + j;
+      w = __expf(fwd ? trans[(size_t)cp * C + r.cc] : trans[(size_t)r.cc * C + cp]);
+    }
+    r.Tr[j] = w;
+  }
+}
+
+__device__ __forceinline__ int slot_of(int tm, int k, int K, bool fwd) {
+  int s = fwd ? tm - k : tm + k;
+  s += (s < 0) ? K : 0;
+  s -= (s >= K) ? K : 0;
+  return s;
+}
+
+// K-sum over the thread's durations: sum_k D[k] * ring[slot(t,k)].  With
+// WITH_GD (backward marginal pass) also accumulates the segment posteriors
+// gd[j] += q * D[k] * ring[slot].
+template <bool WITH_GD, int AMAX, int TRMAX, typename DT, typename GT>
+__device__ __forceinline__ double ksum(const Regs<AMAX, TRMAX, DT> &r, const Smem &sm,
+                                       const ChainShape &sh, int t, bool fwd, GT (&gd)[AMAX],
+                                       double q) {
+  double s = 0.0;
+  const int K = sh.K, C = sh.C;
+  const int tm = t % K;
+#pragma unroll
+  for (int j = 0; j < AMAX; ++j) {
+    if (j < r.nage) {
+      const int sl = slot_of(tm, r.age0 + j, K, fwd);
+      const double w = (double)r.D[j] * sm.ring[sl * C + r.kc];
+      s += w;
+      if (WITH_GD) gd[j] += (GT)(q * w);
+    }
+  }
+  return s;
+}
+
+// Max over the C row values (row threads hold `v`).  All threads call.
+__device__ __forceinline__ double row_max(double v, bool is_row, const ChainShape &sh,
+                                          const Smem &sm) {
+  double x = is_row ? v : -__builtin_huge_val();
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmax(x, __shfl_xor(x, off));
+  if (sh.C <= 64) return x;  // all row threads are in wave 0
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0 && w < sh.Q) sm.scal[w] = x;
+  __syncthreads();
+  double m = sm.scal[0];
+  for (int i = 1; i < sh.Q; ++i) m = fmax(m, sm.scal[i]);
+  return m;
+}
+
+// Contraction: row thread c receives M + log(sum_{c'} e[c'] * W[c'][c]).
+// Requires sm.erow written and a barrier before the call.  All threads call.
+template <int AMAX, int TRMAX, typename DT>
+__device__ __forceinline__ double contract(const Regs<AMAX, TRMAX, DT> &r, const Smem &sm,
+                                           const ChainShape &sh, double M) {
+  float dp = 0.f;
+#pragma unroll
+  for (int j = 0; j < TRMAX; ++j)
+    if (j < r.ncp) dp = fmaf(sm.erow[r.cp0 + j], r.Tr[j], dp);
+  if (sh.Q > 1) {
+    if (r.cq < sh.Q) sm.dotp[r.cq * sh.C + r.cc] = dp;
+    __syncthreads();
+    if ((int)threadIdx.x < sh.C) {
+      dp = 0.f;
+      for (int q = 0; q < sh.Q; ++q) dp += sm.dotp[q * sh.C + threadIdx.x];
+    }
+  }
+  return M + (double)__builtin_amdgcn_logf(dp) * kLn2;
+}
+
+// Row thread c inserts the entry for position t (log value `entry`) and
+// decides an exact power-of-two rebase of its column.  Returns true if the
+// column must be rescaled by 2^-n (n in sm.shiftn[c]).
+__device__ __forceinline__ bool insert_entry(const Smem &sm, const ChainShape &sh, int t,
+                                             double entry, double &ref) {
+  const int c = threadIdx.x;
+  double d = entry - ref;
+  int n = 0;
+  if (fabs(d) > kRebaseNats) {
+    n = (int)rint(d * kLog2e);
+    ref += (double)n * kLn2;
+    d = entry - ref;
+  }
+  sm.shiftn[c] = n;
+  sm.refs[c] = ref;
+  sm.ring[(t % sh.K) * sh.C + c] = exp_wide(d);
+  return n != 0;
+}
+
+// Apply pending column rescales: every ring slot except the newest (position
+// t) is multiplied by 2^-shiftn[c].  Slots are owned through the durations
+// of the next step, so each is touched by exactly one thread.
+template <int AMAX, int TRMAX, typename DT>
+__device__ __forceinline__ void apply_rebase(const Regs<AMAX, TRMAX, DT> &r, const Smem &sm,
+                                             const ChainShape &sh, int t, bool fwd) {
+  if (r.nage > 0) {
+    const int n = sm.shiftn[r.kc];
+    if (n != 0) {
+      const int tn = fwd ? t + 1 : t - 1;
+      const int tm = tn % sh.K;
+      for (int j = 0; j < r.nage; ++j) {
+        const int k = r.age0 + j;
+        if (k < 2) continue;
+        const int sl = slot_of(tm, k, sh.K, fwd);
+        sm.ring[sl * sh.C + r.kc] = ldexp(sm.ring[sl * sh.C + r.kc], -n);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Checkpoint record: [K*C ring][C ref][C o][C m] (float64).
+__host__ __device__ inline size_t ck_stride(int C, int K) { return (size_t)(K + 3) * C; }
+
+__device__ __forceinline__ void save_ckpt(double *__restrict__ dst, const Smem &sm,
+                                          const ChainShape &sh, double ref, double o, double m) {
+  const int n = sh.K * sh.C;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = sm.ring[i];
+  if ((int)threadIdx.x < sh.C) {
+    dst[n + threadIdx.x] = ref;
+    dst[n + sh.C + threadIdx.x] = o;
+    dst[n + 2 * sh.C + threadIdx.x] = m;
+  }
+}
+
+__device__ __forceinline__ void load_ckpt(const double *__restrict__ src, const Smem &sm,
+                                          const ChainShape &sh, double &ref, double &o,
+                                          double &m) {
+  const int n = sh.K * sh.C;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) sm.ring[i] = src[i];
+  if ((int)threadIdx.x < sh.C) {
+    ref = src[n + threadIdx.x];
+    o = src[n + sh.C + threadIdx.x];
+    m = src[n + 2 * sh.C + threadIdx.x];
+    sm.refs[threadIdx.x] = ref;
+  }
+  __syncthreads();
+}
+
+// Sum over labels of exp(o - M) for the log normaliser at a sequence end.
+__device__ __forceinline__ double row_lse(double o, bool is_row, const ChainShape &sh,
+                                          const Smem &sm) {
+  const double M = row_max(o, is_row, sh, sm);
+  if (is_row) sm.orow[threadIdx.x] = exp_wide(o - M);
+  __syncthreads();
+  double s = 0.0;
+  for (int c = 0; c < sh.C; ++c) s += sm.orow[c];
+  return M + log_wide(s);
+}
+
+// ---------------------------------------------------------------- sweeps
+// blockIdx.x < B: forward chain of sequence b; else backward chain.
+template <int NT, int AMAX, int TRMAX, typename DT>
+__global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__restrict__ trans,
+                                              const float *__restrict__ dur,
+                                              const double *__restrict__ S,
+                                              const int32_t *__restrict__ lengths,
+                                              double *__restrict__ ck_fwd,
+                                              double *__restrict__ ck_bwd,
+                                              double *__restrict__ logz_ws,
+                                              double *__restrict__ logz_bwd_ws,
+                                              float *__restrict__ logz_out, int write_ckpt) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const bool fwd = (int)blockIdx.x < sh.B;
+  const int b = fwd ? blockIdx.x : blockIdx.x - sh.B;
+  const int L = lengths[b];
+  const int tid = threadIdx.x, C = sh.C, K = sh.K;
+  const bool is_row = tid < C;
+  if (L < 1 || L > sh.T) {
+    if (tid == 0) {
+      if (fwd) {
+        logz_ws[b] = __builtin_nan("");
+        logz_out[b] = __builtin_nanf("");
+      } else if (logz_bwd_ws) {
+        logz_bwd_ws[b] = __builtin_nan("");
+      }
+    }
+    return;
+  }
+  Smem sm = carve(lds, sh);
+  Regs<AMAX, TRMAX, DT> r;
+  init_regs(r, sh, dur);
+  load_trans(r, sh, trans, fwd);
+  const double *Sb = S + (size_t)b * (sh.T + 1) * C;
+  const size_t cks = ck_stride(C, K);
+  double *ckb = (fwd ? ck_fwd : ck_bwd) + (size_t)b * sh.nchunk * cks;
+  const double sigma = fwd ? 1.0 : -1.0;
+
+  for (int i = tid; i < K * C; i += NT) sm.ring[i] = 0.0;
+  __syncthreads();
+  // initial entry: forward position 0 (u = 0), backward position L (beta = 0)
+  const int tstart = fwd ? 0 : L;
+  double ref = 0.0;
+  if (is_row) {
+    const double entry = fwd ? 0.0 : Sb[(size_t)L * C + tid];
+    ref = entry;
+    sm.refs[tid] = ref;
+    sm.ring[(tstart % K) * C + tid] = 1.0;
+  }
+  __syncthreads();
+  if (write_ckpt) {
+    // forward checkpoint 0 holds p0 = 0 (u[0] = 0); the backward checkpoint
+    // of the last chunk holds p1 = L (beta[L] = 0).  o is undefined there.
+    const int j = fwd ? 0 : (L - 1) / sh.delta;
+    save_ckpt(ckb + (size_t)j * cks, sm, sh, ref, -__builtin_huge_val(), 0.0);
+  }
+
+  const int nsteps = L;  // forward t = 1..L, backward t = L-1..0
+  for (int step = 1; step <= nsteps; ++step) {
+    const int t = fwd ? step : L - step;
+    double nogd[AMAX];
+    const double s = r.kp < sh.P ? ksum<false>(r, sm, sh, t, fwd, nogd, 0.0) : 0.0;
+    if (r.kp < sh.P) sm.part[r.kp * C + r.kc] = s;
+    __syncthreads();
+    double o = 0.0;
+    if (is_row) {
+      double sum = 0.0;
+      for (int p = 0; p < sh.P; ++p) sum += sm.part[p * C + tid];
+      o = sigma * Sb[(size_t)t * C + tid] + ref + log_wide(sum);
+    }
+    const bool last = fwd ? (t == L) : (t == 0);
+    if (last) {
+      const double lz = row_lse(o, is_row, sh, sm);
+      if (tid == 0) {
+        if (fwd) {
+          logz_ws[b] = lz;
+          logz_out[b] = (float)lz;
+        } else if (logz_bwd_ws) {
+          logz_bwd_ws[b] = lz;
+        }
+      }
+      break;
+    }
+    const double M = row_max(o, is_row, sh, sm);
+    if (is_row) sm.erow[tid] = (float)exp_wide(o - M);
+    __syncthreads();
+    const double m = contract(r, sm, sh, M);
+    bool need = false;
+    if (is_row) need = insert_entry(sm, sh, t, m - sigma * Sb[(size_t)t * C + tid], ref);
+    if (__syncthreads_or(need)) apply_rebase(r, sm, sh, t, fwd);
+    if (write_ckpt && (t % sh.delta) == 0) {
+      // forward: checkpoint j = t/delta holds position p0 = t;
+      // backward: checkpoint j = t/delta - 1 holds position p1 = t.
+      const int j = fwd ? t / sh.delta : t / sh.delta - 1;
+      save_ckpt(ckb + (size_t)j * cks, sm, sh, ref, o, m);
+    }
+  }
+}
+
+// -------------------------------------------------------- marginal pass
+// One workgroup per (sequence b, chunk j) with chunk = [p0, p1),
+// p0 = j*delta, p1 = min(p0 + delta, L).
+//   phase A: forward from checkpoint j; alpha[t] for t in (p0, p1] and
+//            u[t] for t in [p0, p1) go to the chunk scratch;
+//   phase B: backward from the checkpoint at p1; per position
+//            E_start[t,c] = exp(u + v - logZ), E_end[t,c] = exp(alpha + beta - logZ),
+//            segment posteriors P(t,k,c) = Q[t,c] * D[k][c] * ring (accumulated
+//            per duration into grad_dur partials), the coverage suffix sums,
+//            and the exp-space factors of the transition posteriors;
+//   phase C: grad_trans partial = sum_t ea[t,c'] * ev[t,c] (float64),
+//            multiplied by exp(trans) in the reduction.
+template <int NT, int AMAX, int TRMAX, typename DT, typename GT>
+__global__ __launch_bounds__(NT) void k_chunk(
+    ChainShape sh, const float *__restrict__ trans, const float *__restrict__ dur,
+    const double *__restrict__ S, const int32_t *__restrict__ lengths,
+    const double *__restrict__ ck_fwd, const double *__restrict__ ck_bwd,
+    const double *__restrict__ logz_ws, double *__restrict__ scr_a, double *__restrict__ scr_u,
+    float *__restrict__ scr_ea, float *__restrict__ scr_ev, double *__restrict__ part_x,
+    double *__restrict__ part_gd, double *__restrict__ part_tot, double *__restrict__ part_ssum,
+    float *__restrict__ suffix_out) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int b = blockIdx.x / sh.nchunk, jc = blockIdx.x % sh.nchunk;
+  const int tid = threadIdx.x, C = sh.C, K = sh.K;
+  const bool is_row = tid < C;
+  const int L = lengths[b];
+  const int p0 = jc * sh.delta;
+  const size_t cid = (size_t)b * sh.nchunk + jc;
+  double *px = part_x + cid * C * C;
+  double *pg = part_gd + cid * K * C;
+  if (L < 1 || L > sh.T || p0 >= L) {
+    for (int i = tid; i < C * C; i += NT) px[i] = 0.0;
+    for (int i = tid; i < K * C; i += NT) pg[i] = 0.0;
+    if (is_row) {
+      part_tot[cid * C + tid] = 0.0;
+      part_ssum[cid * C + tid] = 0.0;
+    }
+    return;
+  }
+  const int p1 = min(p0 + sh.delta, L);
+  const double logZ = logz_ws[b];
+  Smem sm = carve(lds, sh);
+  Regs<AMAX, TRMAX, DT> r;
+  init_regs(r, sh, dur);
+  const double *Sb = S + (size_t)b * (sh.T + 1) * C;
+  const size_t cks = ck_stride(C, K);
+  const size_t rows = (size_t)sh.delta + 1;
+  double *sa = scr_a + cid * rows * C;  // alpha[p0 + i]
+  double *su = scr_u + cid * rows * C;  // u[p0 + i]
+  float *sea = scr_ea + cid * rows * C;
+  float *sev = scr_ev + cid * rows * C;
+
+  // ---- phase A: forward recompute
+  load_trans(r, sh, trans, true);
+  double ref = 0.0, o = 0.0, m = 0.0;
+  load_ckpt(ck_fwd + cid * cks, sm, sh, ref, o, m);
+  if (is_row) {
+    sa[tid] = o;
+    su[tid] = m;
+  }
+  for (int t = p0 + 1; t <= p1; ++t) {
+    double nogd[AMAX];
+    const double s = r.kp < sh.P ? ksum<false>(r, sm, sh, t, true, nogd, 0.0) : 0.0;
+    if (r.kp < sh.P) sm.part[r.kp * C + r.kc] = s;
+    __syncthreads();
+    if (is_row) {
+      double sum = 0.0;
+      for (int p = 0; p < sh.P; ++p) sum += sm.part[p * C + tid];
+      o = Sb[(size_t)t * C + tid] + ref + log_wide(sum);
+      sa[(size_t)(t - p0) * C + tid] = o;
+    }
+    if (t == p1) break;
+    const double M = row_max(o, is_row, sh, sm);
+    if (is_row) sm.erow[tid] = (float)exp_wide(o - M);
+    __syncthreads();
+    m = contract(r, sm, sh, M);
+    bool need = false;
+    if (is_row) {
+      su[(size_t)(t - p0) * C + tid] = m;
+      need = insert_entry(sm, sh, t, m - Sb[(size_t)t * C + tid], ref);
+    }
+    if (__syncthreads_or(need)) apply_rebase(r, sm, sh, t, true);
+  }
+  __syncthreads();
+
+  // ---- phase B: backward over the chunk with posteriors
+  load_trans(r, sh, trans, false);
+  load_ckpt(ck_bwd + cid * cks, sm, sh, ref, o, m);  // state at p1, m = beta[p1]
+  GT gd[AMAX];
+#pragma unroll
+  for (int j = 0; j < AMAX; ++j) gd[j] = (GT)0;
+  double suffix = 0.0, ssum = 0.0;
+  float *suf = suffix_out + (size_t)b * sh.T * C;
+  if (is_row) {
+    const double eend = exp_wide(sa[(size_t)(p1 - p0) * C + tid] + m - logZ);
+    suffix = -eend;
+  }
+  for (int t = p1 - 1; t >= p0; --t) {
+    double s = 0.0;
+    if (r.kp < sh.P) {
+      // Q[t,c] = exp(u[t,c] - S[t,c] + ref[c] - logZ): P(t,k,c) = Q * D * ring
+      const double ut = su[(size_t)(t - p0) * C + r.kc];
+      const double q = exp_wide(ut - Sb[(size_t)t * C + r.kc] + sm.refs[r.kc] - logZ);
+      s = ksum<true>(r, sm, sh, t, false, gd, q);
+      sm.part[r.kp * C + r.kc] = s;
+    }
+    __syncthreads();
+    double at = 0.0;
+    if (is_row) {
+      double sum = 0.0;
+      for (int p = 0; p < sh.P; ++p) sum += sm.part[p * C + tid];
+      o = -Sb[(size_t)t * C + tid] + ref + log_wide(sum);  // v[t]
+      const double ut = su[(size_t)(t - p0) * C + tid];
+      const double estart = exp_wide(ut + o - logZ);
+      suf[(size_t)t * C + tid] = (float)suffix;
+      ssum += suffix;
+      suffix += estart;
+      at = sa[(size_t)(t - p0) * C + tid];
+    }
+    if (t == 0) break;
+    const double M = row_max(o, is_row, sh, sm);
+    if (is_row) {
+      const float e = (float)exp_wide(o - M);
+      sm.erow[tid] = e;
+      sev[(size_t)(t - p0) * C + tid] = e;
+      sea[(size_t)(t - p0) * C + tid] = (float)exp_wide(at + M - logZ);
+    }
+    __syncthreads();
+    m = contract(r, sm, sh, M);  // beta[t]
+    bool need = false;
+    if (is_row) {
+      need = insert_entry(sm, sh, t, m + Sb[(size_t)t * C + tid], ref);
+      if (t > p0) suffix -= exp_wide(at + m - logZ);  // E_end[t]
+    }
+    if (__syncthreads_or(need)) apply_rebase(r, sm, sh, t, false);
+  }
+  if (is_row) {
+    part_tot[cid * C + tid] = suffix;
+    part_ssum[cid * C + tid] = ssum;
+  }
+  // P*A >= K, so every duration is owned by exactly one thread
+#pragma unroll
+  for (int j = 0; j < AMAX; ++j)
+    if (j < r.nage) pg[(size_t)(r.age0 + j - 1) * C + r.kc] = (double)gd[j];
+  __syncthreads();
+
+  // ---- phase C: transition posteriors, X[c',c] = sum_t ea[t,c'] * ev[t,c]
+  const int tlo = p0 < 1 ? 1 : p0;
+  const int nrow = p1 - tlo;
+  const int npair = C * C;
+  // the ring area (K*C doubles) now holds K rows of ea and K rows of ev
+  float *tile_a = reinterpret_cast<float *>(sm.ring);
+  const int tile_rows = K;
+  float *tile_v = tile_a + (size_t)tile_rows * C;
+  constexpr int kPairs = 16;
+  for (int pbase = 0; pbase < npair; pbase += NT * kPairs) {
+    double acc[kPairs];
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) acc[i] = 0.0;
+    for (int r0 = 0; r0 < nrow; r0 += tile_rows) {
+      const int nr = min(tile_rows, nrow - r0);
+      __syncthreads();
+      for (int i = tid; i < nr * C; i += NT) {
+        const size_t src = (size_t)(tlo - p0 + r0) * C + i;
+        tile_a[i] = sea[src];
+        tile_v[i] = sev[src];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kPairs; ++i) {
+        const int pi = pbase + i * NT + tid;
+        if (pi < npair) {
+          const int cp = pi / C, c = pi % C;
+          double a = acc[i];
+          for (int rr = 0; rr < nr; ++rr)
+            a += (double)tile_a[rr * C + cp] * (double)tile_v[rr * C + c];
+          acc[i] = a;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      const int pi = pbase + i * NT + tid;
+      if (pi < npair) px[pi] = acc[i];
+    }
+  }
+}
+
+// ------------------------------------------------------------ reductions
+// grad_trans[c',c] = exp(trans[c',c]) * sum_{b,j} w_b X[b,j][c',c];
+// grad_dur[k,c]    = sum_{b,j} w_b gd[b,j][k,c]; fixed order, float64.
+__global__ void k_reduce_params(ChainShape sh, const float *__restrict__ trans,
+                                const int32_t *__restrict__ lengths,
+                                const float *__restrict__ grad_logz,
+                                const double *__restrict__ part_x,
+                                const double *__restrict__ part_gd,
+                                float *__restrict__ grad_trans, float *__restrict__ grad_dur) {
+  const int C = sh.C, K = sh.K;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nx = C * C, ng = K * C;
+  if (e >= nx + ng) return;
+  double acc = 0.0;
+  for (int b = 0; b < sh.B; ++b) {
+    const int L = lengths[b];
+    if (L < 1 || L > sh.T) continue;
+    const double w = grad_logz ? (double)grad_logz[b] : 1.0;
+    double sb = 0.0;
+    for (int j = 0; j < sh.nchunk; ++j) {
+      const size_t cid = (size_t)b * sh.nchunk + j;
+      sb += e < nx ? part_x[cid * nx + e] : part_gd[cid * ng + (e - nx)];
+    }
+    acc += w * sb;
+  }
+  if (e < nx)
+    grad_trans[e] = (float)(acc * exp((double)trans[e]));
+  else
+    grad_dur[e - nx] = (float)acc;
+}
+
+// Coverage carries: Ctot_{j+1}[c] = sum_{j'<=j} tot[j'][c] (the probability
+// that a label-c segment started before p1 and ends after it), and the
+// per-label mean coverage used by the centring correction.
+__global__ void k_carry(ChainShape sh, const int32_t *__restrict__ lengths,
+                        const double *__restrict__ part_tot, const double *__restrict__ part_ssum,
+                        double *__restrict__ carry, double *__restrict__ mean) {
+  const int b = blockIdx.x;
+  const int L = lengths[b];
+  for (int c = threadIdx.x; c < sh.C; c += blockDim.x) {
+    double ct = 0.0, sum = 0.0;
+    for (int j = 0; j < sh.nchunk; ++j) {
+      const size_t cid = (size_t)b * sh.nchunk + j;
+      const int p0 = j * sh.delta;
+      if (L >= 1 && L <= sh.T && p0 < L) {
+        const int n = min(p0 + sh.delta, L) - p0;
+        ct += part_tot[cid * sh.C + c];
+        sum += (double)n * ct - part_ssum[cid * sh.C + c];
+      }
+      carry[cid * sh.C + c] = ct;
+    }
+    mean[(size_t)b * sh.C + c] = (L >= 1 && L <= sh.T) ? sum / (double)L : 0.0;
+  }
+}
+
+// mu[b,t,c] = carry[b, t/delta, c] - suffix[b,t,c];
+// grad_x = w_b (mu - mean_c) (centred) or w_b mu.  In place on grad_emissions.
+__global__ void k_finalize(ChainShape sh, const int32_t *__restrict__ lengths,
+                           const float *__restrict__ grad_logz, const double *__restrict__ carry,
+                           const double *__restrict__ mean, float *__restrict__ grad_emissions,
+                           float *__restrict__ marginals) {
+  const int b = blockIdx.y;
+  const int C = sh.C;
+  const int L = lengths[b];
+  const bool ok = L >= 1 && L <= sh.T;
+  const double w = grad_logz ? (double)grad_logz[b] : 1.0;
+  const size_t n = (size_t)sh.T * C;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int t = (int)(i / C), c = (int)(i % C);
+    float mu_out = 0.f, g_out = 0.f;
+    if (ok && t < L) {
+      const size_t cid = (size_t)b * sh.nchunk + t / sh.delta;
+      const double mu = carry[cid * C + c] - (double)grad_emissions[(size_t)b * n + i];
+      const double g = sh.center ? w * (mu - mean[(size_t)b * C + c]) : w * mu;
+      mu_out = (float)mu;
+      g_out = (float)g;
+    }
+    grad_emissions[(size_t)b * n + i] = g_out;
+    if (marginals) marginals[(size_t)b * n + i] = mu_out;
+  }
+}
+
+// ------------------------------------------------------------- dispatch
+// With SEMICRF_DEBUG set, name a failed launch and its configuration.
+static hipError_t report(hipError_t e, const char *what, const ChainShape &sh, size_t lds) {
+  if (e != hipSuccess && getenv("SEMICRF_DEBUG"))
+    fprintf(stderr, "semicrf: %s (NT=%d C=%d K=%d lds=%zu) failed: %s\n", what, sh.NT, sh.C, sh.K,
+            lds, hipGetErrorString(e));
+  return e;
+}
+
+template <int NT, int AMAX, int TRMAX, typename DT, typename GT>
+struct ChainKernels {
+  // Raise the dynamic-LDS limit once per instance (the ring can exceed 64 KB);
+  // clear the error state so a refusal cannot masquerade as a launch error.
+  static void set_attrs() {
+    static bool done = false;
+    if (!done) {
+      (void)hipFuncSetAttribute((const void *)k_sweep<NT, AMAX, TRMAX, DT>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+      (void)hipFuncSetAttribute((const void *)k_chunk<NT, AMAX, TRMAX, DT, GT>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+      (void)hipGetLastError();
+      done = true;
+    }
+  }
+  static hipError_t sweep(const ChainShape &sh, const float *trans, const float *dur,
+                          const double *S, const int32_t *lengths, double *ck_fwd,
+                          double *ck_bwd, double *logz_ws, double *logz_bwd_ws,
+                          float *logz_out, int with_bwd, int write_ckpt, hipStream_t st) {
+    const size_t lds = chain_lds_bytes(sh.C, sh.K, sh.P, sh.Q);
+    set_attrs();
+    hipLaunchKernelGGL((k_sweep<NT, AMAX, TRMAX, DT>), dim3(with_bwd ? 2 * sh.B : sh.B),
+                       dim3(NT), lds, st, sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws,
+                       logz_bwd_ws, logz_out, write_ckpt);
+    return report(hipGetLastError(), "k_sweep", sh, lds);
+  }
+  static hipError_t chunks(const ChainShape &sh, const float *trans, const float *dur,
+                           const double *S, const int32_t *lengths, const double *ck_fwd,
+                           const double *ck_bwd, const double *logz_ws, double *scr_a,
+                           double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
+                           double *part_gd, double *part_tot, double *part_ssum,
+                           float *suffix_out, hipStream_t st) {
+    const size_t lds = chain_lds_bytes(sh.C, sh.K, sh.P, sh.Q);
+    set_attrs();
+    hipLaunchKernelGGL((k_chunk<NT, AMAX, TRMAX, DT, GT>), dim3(sh.B * sh.nchunk), dim3(NT),
+                       lds, st, sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, scr_a,
+                       scr_u, scr_ea, scr_ev, part_x, part_gd, part_tot, part_ssum, suffix_out);
+    return report(hipGetLastError(), "k_chunk", sh, lds);
+  }
+};
+
+#define SEMICRF_CHAIN_DISPATCH(SH, CALL)                                                   \
+  do {                                                                                     \
+    const int trmax_ = (SH).C <= 8 ? 8 : ((SH).C <= 32 ? 32 : 64);                        \
+    if ((SH).NT == 256) {                                                                  \
+      if (trmax_ == 8) return ChainKernels<256, 32, 8, double, double>::CALL;              \
+      if (trmax_ == 32) return ChainKernels<256, 32, 32, double, double>::CALL;            \
+      return ChainKernels<256, 32, 64, double, double>::CALL;                              \
+    } else if ((SH).NT == 512) {                                                           \
+      if (trmax_ == 8) return ChainKernels<512, 32, 8, double, double>::CALL;              \
+      if (trmax_ == 32) return ChainKernels<512, 32, 32, double, double>::CALL;            \
+      return ChainKernels<512, 32, 64, double, double>::CALL;                              \
+    } else {                                                                               \
+      if (trmax_ == 8) return ChainKernels<1024, 16, 8, float, float>::CALL;               \
+      if (trmax_ == 32) return ChainKernels<1024, 16, 32, float, float>::CALL;             \
+      return ChainKernels<1024, 16, 64, float, float>::CALL;                               \
+    }                                                                                      \
+  } while (0)
+
+hipError_t launch_sweep(const ChainShape &sh, const float *trans, const float *dur,
+                        const double *S, const int32_t *lengths, double *ck_fwd,
+                        double *ck_bwd, double *logz_ws, double *logz_bwd_ws, float *logz_out,
+                        int with_bwd, int write_ckpt, hipStream_t st) {
+  SEMICRF_CHAIN_DISPATCH(sh, sweep(sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws,
+                                   logz_bwd_ws, logz_out, with_bwd, write_ckpt, st));
+}
+
+hipError_t launch_chunks(const ChainShape &sh, const float *trans, const float *dur,
+                         const double *S, const int32_t *lengths, const double *ck_fwd,
+                         const double *ck_bwd, const double *logz_ws, double *scr_a,
+                         double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
+                         double *part_gd, double *part_tot, double *part_ssum,
+                         float *suffix_out, hipStream_t st) {
+  SEMICRF_CHAIN_DISPATCH(sh, chunks(sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, scr_a,
+                                    scr_u, scr_ea, scr_ev, part_x, part_gd, part_tot, part_ssum,
+                                    suffix_out, st));
+}
+
+hipError_t launch_finish(const ChainShape &sh, const float *trans, const int32_t *lengths,
+                         const float *grad_logz, const double *part_x, const double *part_gd,
+                         const double *part_tot, const double *part_ssum, double *carry,
+                         double *mean, float *grad_trans, float *grad_dur,
+                         float *grad_emissions, float *marginals, hipStream_t st) {
+  const int ne = sh.C * sh.C + sh.K * sh.C;
+  hipLaunchKernelGGL(k_reduce_params, dim3((ne + 255) / 256), dim3(256), 0, st, sh, trans,
+                     lengths, grad_logz, part_x, part_gd, grad_trans, grad_dur);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_carry, dim3(sh.B), dim3(256), 0, st, sh, lengths, part_tot, part_ssum,
+                     carry, mean);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t n = (size_t)sh.T * sh.C;
+  int gx = (int)((n + 255) / 256);
+  if (gx > 4096) gx = 4096;
+  hipLaunchKernelGGL(k_finalize, dim3(gx, sh.B), dim3(256), 0, st, sh, lengths, grad_logz,
+                     carry, mean, grad_emissions, marginals);
+  return hipGetLastError();
+}
+
+}  // namespace semicrf

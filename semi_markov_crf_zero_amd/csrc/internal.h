@@ -1,0 +1,111 @@
+// internal.h -- shapes, launch configuration and workspace layout shared by
+// the host entry points (api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace semicrf {
+
+// Thread roles of one chain workgroup (see chain.hip):
+//   K-sum role   thread (c = tid % C, p = tid / C), p < P, owns the A
+//                consecutive durations k = p*A+1 .. p*A+A of label c;
+//   row role     thread tid < C owns label c (its log reference, outputs);
+//   contraction  thread (c = tid % C, q = tid / C), q < Q, sums over the
+//                previous labels c' in [64q, 64q+64).
+struct ChainShape {
+  int B, T, C, K;
+  int NT;      // threads per workgroup (256, 512 or 1024)
+  int P;       // K-sum threads per label = NT / C
+  int A;       // durations per K-sum thread = ceil(K / P)
+  int Q;       // contraction slices = ceil(C / 64)
+  int delta;   // checkpoint interval (positions)
+  int nchunk;  // ceil(T / delta) chunks per sequence
+  int center;  // 1 = subtract the per-label baseline nu
+};
+
+constexpr int kMaxC = 256;
+constexpr int kMaxKC = 16384;
+constexpr size_t kMaxLds = 163840;  // gfx950: 160 KB per workgroup
+
+// Scan tiles: NT_SCAN threads as R = NT_SCAN / C rows x C labels, each row
+// thread owning J consecutive positions; a tile covers R*J positions.
+constexpr int kScanThreads = 256;
+constexpr int kScanJ = 32;
+
+inline int scan_rows(int C) { return kScanThreads / C; }
+inline int scan_tile(int C) { return scan_rows(C) * kScanJ; }
+
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Dynamic LDS bytes of one chain workgroup; the carve-up in chain.hip
+// follows the same order.
+__host__ __device__ inline size_t chain_lds_bytes(int C, int K, int P, int Q) {
+  size_t off = 0;
+  off += (size_t)K * C * 8;  // ring
+  off += (size_t)P * C * 8;  // K-sum partials
+  off += (size_t)C * 8;      // o row
+  off += (size_t)C * 8;      // per-label log references
+  off += 8 * 8;              // scalars
+  off += (size_t)C * 4;      // e row
+  off += (size_t)Q * C * 4;  // contraction partials
+  off += (size_t)C * 4;      // rebase shifts
+  return align_up(off, 16);
+}
+
+// Viterbi LDS: ring (double), partial maxima (double), partial argmax (int),
+// alpha-hat row (double), contraction partial max/arg.
+__host__ __device__ inline size_t viterbi_lds_bytes(int C, int K, int P, int Q) {
+  size_t off = 0;
+  off += (size_t)K * C * 8;
+  off += (size_t)P * C * 8;
+  off += (size_t)P * C * 4;
+  off += (size_t)C * 8;
+  off += (size_t)Q * C * 8;
+  off += (size_t)Q * C * 4;
+  off += 8 * 8;
+  return align_up(off, 16);
+}
+
+// Workspace layout (byte offsets, 256-aligned).
+struct Layout {
+  size_t S, nu, tile_sum, anchor, logz, logz_bwd;
+  size_t ck_fwd, ck_bwd, scr_a, scr_u, scr_ea, scr_ev;
+  size_t part_x, part_gd, part_tot, part_ssum, carry, mean;
+  size_t bp, vbest, vcbest;
+  size_t total;
+  int ntile;
+};
+
+// ---- launchers (defined in scan.hip / chain.hip / viterbi.hip) ----------
+
+hipError_t launch_scan(const float *x, const int32_t *lengths, int B, int T, int C, int center,
+                       double *nu, double *S, double *tile_sum, double *anchor, int ntile,
+                       hipStream_t st);
+
+hipError_t launch_sweep(const ChainShape &sh, const float *trans, const float *dur,
+                        const double *S, const int32_t *lengths, double *ck_fwd,
+                        double *ck_bwd, double *logz_ws, double *logz_bwd_ws, float *logz_out,
+                        int with_bwd, int write_ckpt, hipStream_t st);
+
+hipError_t launch_chunks(const ChainShape &sh, const float *trans, const float *dur,
+                         const double *S, const int32_t *lengths, const double *ck_fwd,
+                         const double *ck_bwd, const double *logz_ws, double *scr_a,
+                         double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
+                         double *part_gd, double *part_tot, double *part_ssum,
+                         float *suffix_out, hipStream_t st);
+
+hipError_t launch_finish(const ChainShape &sh, const float *trans, const int32_t *lengths,
+                         const float *grad_logz, const double *part_x, const double *part_gd,
+                         const double *part_tot, const double *part_ssum, double *carry,
+                         double *mean, float *grad_trans, float *grad_dur,
+                         float *grad_emissions, float *marginals, hipStream_t st);
+
+hipError_t launch_viterbi(const ChainShape &sh, const float *trans, const float *dur,
+                          const double *S, const int32_t *lengths, uint32_t *bp, double *vbest,
+                          int32_t *vcbest, float *best_out, int32_t *seg_start,
+                          int32_t *seg_len, int32_t *seg_label, int32_t *num_segs,
+                          hipStream_t st);
+
+}  // namespace semicrf

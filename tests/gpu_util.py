@@ -1,0 +1,82 @@
+"""Helpers shared by the GPU parity tests: move seeded numpy inputs to the
+device, run the HIP path through the C ABI, compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from semi_markov_crf_zero_amd import binding as bd
+
+# Tolerances of the hot path (log Z relative; gradients, marginals absolute).
+TOL_LOGZ = 1e-5
+TOL_GRAD = 1e-4
+
+DEV = "cuda:0"
+
+
+def to_dev(inp):
+    return {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(DEV)
+            for k in ("emissions", "lengths", "trans", "dur")}
+
+
+def gpu_fwd_bwd(inp, center=True, w=None, ckpt=0):
+    t = to_dev(inp)
+    gl = None if w is None else torch.tensor(np.asarray(w), dtype=torch.float32, device=DEV)
+    out = bd.semicrf_fwd_bwd(t["emissions"], t["lengths"], t["trans"], t["dur"], center=center,
+                             grad_logz=gl, checkpoint_interval=ckpt, want_marginals=True)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+
+
+def gpu_logz(inp, center=True):
+    t = to_dev(inp)
+    out = bd.semicrf_logz_fwd(t["emissions"], t["lengths"], t["trans"], t["dur"], center=center)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def gpu_viterbi(inp, center=True):
+    t = to_dev(inp)
+    out = bd.semicrf_viterbi(t["emissions"], t["lengths"], t["trans"], t["dur"], center=center)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def gpu_scan(inp, center=True):
+    t = to_dev(inp)
+    nu, S = bd.semicrf_cumulative_scores(t["emissions"], t["lengths"], center=center)
+    torch.cuda.synchronize()
+    return nu.cpu().numpy(), S.cpu().numpy()
+
+
+def logz_rel_err(g, o):
+    ok = np.isfinite(o)
+    return np.abs(g[ok] - o[ok]) / np.maximum(1.0, np.abs(o[ok]))
+
+
+def assert_fwd_bwd_close(g, o, tol_logz=TOL_LOGZ, tol=TOL_GRAD, label=""):
+    assert np.array_equal(np.isnan(g["logz"]), np.isnan(o["logz"])), label
+    rel = logz_rel_err(g["logz"], o["logz"])
+    assert rel.size == 0 or rel.max() <= tol_logz, (label, "logz", rel.max())
+    errs = {}
+    for k in ("grad_emissions", "grad_trans", "grad_dur", "marginals"):
+        if k in g and k in o:
+            e = float(np.abs(g[k] - o[k]).max()) if g[k].size else 0.0
+            errs[k] = e
+            assert e <= tol, (label, k, e)
+    return errs
+
+
+def assert_viterbi_equal(g, o, label=""):
+    B = o["num_segs"].shape[0]
+    for b in range(B):
+        if np.isnan(o["best_score"][b]):
+            assert np.isnan(g["best_score"][b]), (label, b)
+            assert g["num_segs"][b] == 0
+            continue
+        n = int(o["num_segs"][b])
+        assert int(g["num_segs"][b]) == n, (label, b, "num_segs", g["num_segs"][b], n,
+                                            o["min_margin"][b])
+        for k in ("seg_start", "seg_len", "seg_label"):
+            assert np.array_equal(g[k][b], o[k][b]), (label, b, k, o["min_margin"][b])
+        assert abs(float(g["best_score"][b]) - o["best_score"][b]) <= 1e-5 * max(1.0, abs(o["best_score"][b]))

@@ -1,0 +1,189 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs, element by element.
+
+Bars: log Z relative 1e-5; gradients and marginals absolute 1e-4;
+Viterbi segmentations identical (smallest-k / smallest-label tie-break).
+Shapes cover every workgroup configuration of the library (256/512/1024
+threads; C <= 8, <= 32, <= 64, > 64 with 1-4 contraction slices), several
+checkpoint intervals and ragged tails, plus the edge cases: K > T, L = 1,
+C = 1, K = 1, NaN padding, invalid lengths, non-unit grad weights,
+centring off, large emission scales.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from semi_markov_crf_zero_amd.workloads import make_random
+from tests.gpu_util import (assert_fwd_bwd_close, assert_viterbi_equal, gpu_fwd_bwd, gpu_logz,
+                            gpu_scan, gpu_viterbi, logz_rel_err)
+
+pytestmark = pytest.mark.gpu
+
+# (B, T, C, K, lengths): one per workgroup configuration, ragged tails
+SHAPES = [
+    (3, 300, 8, 16, [300, 211, 5]),      # 256 threads, C <= 8
+    (3, 400, 24, 32, [400, 257, 33]),    # 256 threads, C = 24 (not a power of 2)
+    (2, 500, 16, 40, [500, 123]),        # 256 threads, C = 16
+    (2, 333, 64, 100, [333, 300]),       # 256 threads, C = 64
+    (2, 600, 64, 200, [600, 444]),       # 512 threads
+    (2, 300, 100, 70, [300, 151]),       # 512 threads, 2 contraction slices
+    (2, 200, 256, 20, [200, 199]),       # 1024 threads, 4 slices
+    (2, 150, 200, 50, [150, 77]),        # 1024 threads, C = 200
+    (3, 50, 5, 80, [50, 10, 1]),         # K > T, L = 1
+    (2, 64, 1, 8, [64, 63]),             # C = 1
+    (2, 90, 6, 1, [90, 40]),             # K = 1 (linear chain)
+]
+
+
+def _case(B, T, C, K, lengths, seed=0, **kw):
+    return make_random(B, T, C, K, seed=seed, lengths=lengths, **kw)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dT%dC%dK%d" % s[:4])
+def test_fwd_bwd_shapes(shape):
+    B, T, C, K, lengths = shape
+    inp = _case(B, T, C, K, lengths, seed=T + C + K, tsd=0.3, dsd=0.3)
+    o = oracle.fwd_bwd(inp)
+    g = gpu_fwd_bwd(inp)
+    errs = assert_fwd_bwd_close(g, o, label=str(shape[:4]))
+    print(shape[:4], errs, "logz rel", logz_rel_err(g["logz"], o["logz"]).max())
+
+
+@pytest.mark.parametrize("C,K", list(itertools.product([1, 2, 3], [1, 2, 3, 4])))
+def test_fwd_bwd_enumeration_grid(C, K):
+    """The oracle is pinned to explicit enumeration on exactly this grid."""
+    T = 7 if C == 3 else 8
+    for center in (True, False):
+        inp = _case(3, T, C, K, [T, 4, 1], seed=C * 10 + K, tsd=0.5, dsd=0.5)
+        o = oracle.fwd_bwd(inp, center=center, grad_logz=np.array([1.0, -0.5, 2.0]))
+        g = gpu_fwd_bwd(inp, center=center, w=[1.0, -0.5, 2.0])
+        assert_fwd_bwd_close(g, o, tol_logz=1e-6, tol=1e-5, label=(C, K, center))
+
+
+@pytest.mark.parametrize("ckpt", [1, 3, 16, 0, 97, 400])
+def test_checkpoint_interval_invariance(ckpt):
+    inp = _case(3, 400, 12, 16, [400, 399, 130], seed=5, tsd=0.3, dsd=0.3)
+    o = oracle.fwd_bwd(inp)
+    g = gpu_fwd_bwd(inp, ckpt=ckpt)
+    assert_fwd_bwd_close(g, o, label=ckpt)
+    ref = gpu_fwd_bwd(inp, ckpt=0)
+    for k in ("grad_emissions", "grad_trans", "grad_dur", "marginals"):
+        assert np.abs(g[k] - ref[k]).max() < 1e-5
+    assert np.abs(g["logz"] - ref["logz"]).max() <= 1e-6 * np.abs(ref["logz"]).max()
+
+
+def test_weights_and_no_center():
+    inp = _case(3, 257, 10, 24, [257, 256, 100], seed=7)
+    w = np.array([0.5, -1.25, 3.0])
+    for center in (True, False):
+        o = oracle.fwd_bwd(inp, center=center, grad_logz=w)
+        g = gpu_fwd_bwd(inp, center=center, w=w)
+        assert_fwd_bwd_close(g, o, label=center)
+
+
+def test_nan_padding_is_never_read():
+    clean = _case(3, 200, 8, 16, [200, 77, 9], seed=9)
+    padded = _case(3, 200, 8, 16, [200, 77, 9], seed=9, pad_value=np.nan)
+    a = gpu_fwd_bwd(clean)
+    b = gpu_fwd_bwd(padded)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    va, vb = gpu_viterbi(clean), gpu_viterbi(padded)
+    for k in va:
+        assert np.array_equal(va[k], vb[k]), k
+
+
+def test_invalid_lengths():
+    """lengths outside [1, T]: NaN log Z, zero gradient rows, excluded from
+    the parameter gradients (compared with the valid sequence alone)."""
+    base = _case(3, 60, 4, 8, [60, 60, 23], seed=11)
+    bad = dict(base)
+    bad["lengths"] = np.array([0, 61, 23], np.int32)
+    g = gpu_fwd_bwd(bad)
+    assert np.isnan(g["logz"][0]) and np.isnan(g["logz"][1])
+    assert np.all(g["grad_emissions"][:2] == 0) and np.all(g["marginals"][:2] == 0)
+    only = dict(base)
+    for k in ("emissions",):
+        only[k] = base[k][2:3]
+    only["lengths"] = np.array([23], np.int32)
+    o = oracle.fwd_bwd(only)
+    assert abs(g["logz"][2] - o["logz"][0]) <= 1e-5 * abs(o["logz"][0])
+    assert np.abs(g["grad_trans"] - o["grad_trans"]).max() <= 1e-4
+    assert np.abs(g["grad_dur"] - o["grad_dur"]).max() <= 1e-4
+    assert np.abs(g["grad_emissions"][2] - o["grad_emissions"][0]).max() <= 1e-4
+    lz = gpu_logz(bad)
+    assert np.isnan(lz[0]) and np.isnan(lz[1])
+    v = gpu_viterbi(bad)
+    assert np.isnan(v["best_score"][0]) and v["num_segs"][0] == 0 and np.all(v["seg_start"][0] == -1)
+
+
+@pytest.mark.parametrize("sigma", [10.0, 100.0])
+def test_large_emission_scales(sigma):
+    inp = _case(2, 300, 8, 24, [300, 181], seed=13, sigma=sigma, tsd=1.0, dsd=1.0)
+    o = oracle.fwd_bwd(inp)
+    g = gpu_fwd_bwd(inp)
+    assert_fwd_bwd_close(g, o, label=sigma)
+    assert_viterbi_equal(gpu_viterbi(inp), oracle.viterbi(inp), label=sigma)
+
+
+def test_deterministic_bitwise():
+    inp = _case(3, 500, 16, 40, [500, 300, 77], seed=17)
+    a = gpu_fwd_bwd(inp)
+    b = gpu_fwd_bwd(inp)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("shape", SHAPES[:8], ids=lambda s: "B%dT%dC%dK%d" % s[:4])
+def test_logz_fwd(shape):
+    B, T, C, K, lengths = shape
+    inp = _case(B, T, C, K, lengths, seed=1 + T)
+    o = oracle.logz(inp)
+    g = gpu_logz(inp)
+    assert logz_rel_err(g, o).max() <= 1e-5
+
+
+@pytest.mark.parametrize("C,T", [(1, 50), (3, 1000), (16, 4097), (24, 777), (64, 3000), (256, 300)])
+def test_cumulative_scores(C, T):
+    inp = _case(3, T, C, 4, [T, T // 2 + 1, 1], seed=C, sigma=2.0)
+    for center in (True, False):
+        nu_o, S_o = oracle.prefix(inp, center=center)
+        nu_g, S_g = gpu_scan(inp, center=center)
+        np.testing.assert_allclose(nu_g, nu_o, rtol=1e-12, atol=1e-12)
+        # S rows beyond L repeat row L on both sides
+        np.testing.assert_allclose(S_g, S_o, rtol=1e-11, atol=1e-9)
+        if center:
+            L = inp["lengths"]
+            for b in range(3):
+                assert np.abs(S_g[b, L[b]]).max() < 1e-9 * max(1, L[b])
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dT%dC%dK%d" % s[:4])
+def test_viterbi_shapes(shape):
+    B, T, C, K, lengths = shape
+    inp = _case(B, T, C, K, lengths, seed=2 * T + C, tsd=0.3, dsd=0.3)
+    assert_viterbi_equal(gpu_viterbi(inp), oracle.viterbi(inp), label=shape[:4])
+
+
+def test_viterbi_tie_break_zero_potentials():
+    """Every segmentation ties: the rule yields L unit segments of label 0."""
+    for (C, K, T) in [(3, 5, 40), (16, 32, 100), (64, 8, 33)]:
+        inp = dict(emissions=np.zeros((2, T, C), np.float32),
+                   lengths=np.array([T, T - 7], np.int32),
+                   trans=np.zeros((C, C), np.float32), dur=np.zeros((K, C), np.float32))
+        g = gpu_viterbi(inp)
+        for b, L in enumerate([T, T - 7]):
+            assert g["num_segs"][b] == L
+            assert np.all(g["seg_len"][b, :L] == 1) and np.all(g["seg_label"][b, :L] == 0)
+            assert np.all(g["seg_start"][b, :L] == np.arange(L)) and np.all(g["seg_start"][b, L:] == -1)
+        assert_viterbi_equal(g, oracle.viterbi(inp))
+
+
+@pytest.mark.parametrize("C,K", list(itertools.product([1, 2, 3], [1, 2, 3, 4])))
+def test_viterbi_enumeration_grid(C, K):
+    T = 7 if C == 3 else 8
+    for center in (True, False):
+        inp = _case(3, T, C, K, [T, 4, 1], seed=100 + C * 10 + K, tsd=0.5, dsd=0.5)
+        assert_viterbi_equal(gpu_viterbi(inp, center), oracle.viterbi(inp, center), label=(C, K))
