@@ -1,0 +1,197 @@
+"""Benchmark of the semi-CRF hot path (one fwd+bwd = one step) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload nlp]
+
+A step is one semicrf_fwd_bwd call (cumulative scores, forward and backward
+sweeps with checkpoints, chunk-parallel recompute + posteriors, reductions)
+over one batch of seeded synthetic input already resident in HBM.  The
+default workload is the NLP-scale configuration (B=32, T=512, C=24, K=32).
+
+Prints ONE JSON line on stdout:
+  value      = B*T*K*C segment cells per second (whole job, 1 GPU)
+  roofline   = the dominant kernel's algorithmic float64 FMA work per launch
+               divided by its average duration (HIP events recorded by the
+               library on the launch stream during the timed steps), against
+               the MI355X float64 vector peak (78.6 TFLOP/s); `traffic` is
+               the HBM bytes per launch from rocprofv3 counters stored under
+               profiles/ (null when absent or when the kernel source changed)
+  cpu_baseline = the float64 oracle timed on this host on the same workload
+Diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "semi-CRF fwd+bwd segment-cells/s (B*T*K*C) and % of roofline, 1 MI355X"
+FP64_PEAK_TFLOPS = 78.6   # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "semi_markov_crf_zero_amd", "csrc", "chain.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def positions_and_kterms(lengths, K):
+    """Sum over sequences of L_b and of sum_{t=1}^{L_b} min(K, t)."""
+    npos = 0
+    kterms = 0
+    for L in lengths:
+        L = int(L)
+        npos += L
+        if L >= K:
+            kterms += K * (K + 1) // 2 + (L - K) * K
+        else:
+            kterms += L * (L + 1) // 2
+    return npos, kterms
+
+
+def algorithmic_flops(lengths, C, K):
+    """Float64 flops the method itself needs, per kernel (FMA = 2 flops):
+    k_sweep  forward K-term sums (2 per segment cell) + forward contraction
+             (2 C^2 per position); its backward chain only produces
+             checkpoints and is overhead of the chunk-parallel design;
+    k_chunk  backward K-term sums + duration posteriors (4 per segment cell)
+             + backward contraction + transition posteriors (4 C^2 per
+             position); its forward recompute is overhead."""
+    npos, kterms = positions_and_kterms(lengths, K)
+    return {
+        "k_sweep": 2.0 * kterms * C + 2.0 * C * C * npos,
+        "k_chunk": 4.0 * kterms * C + 4.0 * C * C * npos,
+    }
+
+
+def source_digest(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.json, or
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != source_digest(KERNEL_SOURCE):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    import oracle
+
+    oracle.core.build(force=False)
+    cells = inp["B"] * inp["T"] * inp["K"] * inp["C"]
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.fwd_bwd(inp, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / reps * (reps + 1) > 3 * budget_s:
+            break
+    per = el / reps
+    return {"value": cells / per, "unit": "segment-cells/s", "cores": threads, "kind": "oracle",
+            "sample": "the full %s workload (B=%d T=%d C=%d K=%d), %d repetition(s) in %.1f s, "
+                      "float64 C with OpenMP" % (inp["name"], inp["B"], inp["T"], inp["C"], inp["K"],
+                                                 reps, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="nlp",
+                    choices=["tiny", "nlp", "speech", "genome", "extreme"])
+    ap.add_argument("--checkpoint-interval", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the batch would shard across GPUs with one all-reduce of the parameter "
+              "gradients; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from semi_markov_crf_zero_amd import binding as bd
+    from semi_markov_crf_zero_amd.workloads import make_inputs
+
+    inp = make_inputs(args.workload)
+    inp["name"] = args.workload
+    B, T, C, K = inp["B"], inp["T"], inp["C"], inp["K"]
+    dev = torch.device("cuda:0")
+    t = {k: torch.from_numpy(inp[k]).to(dev) for k in ("emissions", "lengths", "trans", "dur")}
+    plan = bd.FwdBwdPlan(t["emissions"], t["lengths"], t["trans"], t["dur"],
+                         checkpoint_interval=args.checkpoint_interval)
+    ckpt = args.checkpoint_interval or bd.semicrf_default_checkpoint_interval(T, K)
+    nph = len(bd.FWD_BWD_PHASES)
+    for _ in range(args.warmup):
+        plan.run()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)]
+              for _ in range(args.steps)]
+    for evs in events:  # create the handles; the library re-records them
+        for ev in evs:
+            ev.record()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plan.run(phase_events=events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    phase_ms = np.zeros(nph)
+    for evs in events:
+        for p in range(nph):
+            phase_ms[p] += evs[p].elapsed_time(evs[p + 1])
+    phase_ms /= args.steps
+    ms_step = wall * 1e3 / args.steps
+    cells = float(B) * T * K * C
+    value = cells / (ms_step * 1e-3)
+    for name, ms in zip(bd.FWD_BWD_PHASES, phase_ms):
+        log("phase %-18s %9.3f ms" % (name, ms))
+    log("step %.3f ms (wall), %.3e segment-cells/s, workspace %.1f MB"
+        % (ms_step, value, plan.ws_bytes / 1e6))
+
+    flops = algorithmic_flops(inp["lengths"], C, K)
+    kernels = {"k_sweep": phase_ms[1], "k_chunk": phase_ms[2]}
+    dom = max(kernels, key=kernels.get)
+    achieved = flops[dom] / (kernels[dom] * 1e-3) / 1e12
+    roofline = {"bound": "alu", "kernel": dom, "achieved": achieved, "peak": FP64_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / FP64_PEAK_TFLOPS,
+                "traffic": stored_traffic(dom, args.workload),
+                "launch_ms": float(kernels[dom]),
+                "algorithmic_flops_per_launch": flops[dom]}
+    out = {
+        "metric": METRIC, "value": value, "unit": "segment-cells/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic (seeded numpy PCG64, shapes of the pages' workloads)",
+        "config": {"workload": args.workload, "B": B, "T": T, "C": C, "K": K,
+                   "checkpoint_interval": ckpt, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "phase_ms": {n: float(m) for n, m in zip(bd.FWD_BWD_PHASES, phase_ms)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
