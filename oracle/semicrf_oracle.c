@@ -26,13 +26,22 @@
  *
  * log Z is evaluated by the textbook dynamic programme over segment end
  * points, kept as full (T+1) x C float64 tables -- no ring buffer, no
- * checkpointing, no normalisation tricks:
+ * checkpointing:
  *   u[0,c] = 0;  alpha[t,c] = LSE_{k=1..min(K,t)} (u[t-k,c] + S[t,c]-S[t-k,c] + dur[k-1,c])
  *   u[t,c] = LSE_{c'} (alpha[t,c'] + trans[c',c])          1 <= t < L
  *   log Z = LSE_c alpha[L,c]
  * and its mirror image from the right:
  *   beta[L,c] = 0;  v[t,c] = LSE_{k=1..min(K,L-t)} (S[t+k,c]-S[t,c] + dur[k-1,c] + beta[t+k,c])
  *   beta[t,c'] = LSE_c (trans[c',c] + v[t,c])               1 <= t < L
+ * The log values grow roughly linearly with t (log Z reaches ~5e6 at a
+ * million positions), and a float64 number that large carries only ~1e-9
+ * absolute precision, which every step of the recursion would add to.  So
+ * each table row t stores its values minus an exact integer offset (zf[t]
+ * forward, zb[t] backward: the previous row's offset plus the floor of the
+ * new row's maximum), and the integers are combined exactly before the small
+ * parts are added: log Z = zf[L] + LSE_c (alpha[L,c] - zf[L]), and every
+ * posterior exponent below is (zf[s] + zb[e] - zf[L]) plus small terms.  In
+ * exact arithmetic this is the same programme.
  * Posteriors follow from the definition of a marginal:
  *   P(segment s,k,c) = exp(u[s,c] + S[s+k,c]-S[s,c] + dur[k-1,c] + beta[s+k,c] - log Z)
  *   P(transition c'->c at boundary t) = exp(alpha[t,c'] + trans[c',c] + v[t,c] - log Z)
@@ -119,7 +128,7 @@ static void prefix_one(int T, int C, int L, const float *x, int center,
 /* ------------------------------------------------------ per-sequence tables */
 
 typedef struct {
-    double *S, *alpha, *u, *v, *beta, *tmp;
+    double *S, *alpha, *u, *v, *beta, *zf, *zb, *tmp;
 } tables_t;
 
 static int tables_alloc(tables_t *tb, int T, int C, int K, int nth)
@@ -131,20 +140,36 @@ static int tables_alloc(tables_t *tb, int T, int C, int K, int nth)
     tb->u = malloc(n * sizeof(double));
     tb->v = malloc(n * sizeof(double));
     tb->beta = malloc(n * sizeof(double));
+    tb->zf = malloc((size_t)(T + 1) * sizeof(double));
+    tb->zb = malloc((size_t)(T + 1) * sizeof(double));
     tb->tmp = malloc(ntmp * sizeof(double));
-    return tb->S && tb->alpha && tb->u && tb->v && tb->beta && tb->tmp;
+    return tb->S && tb->alpha && tb->u && tb->v && tb->beta && tb->zf && tb->zb && tb->tmp;
 }
 
 static void tables_free(tables_t *tb)
 {
-    free(tb->S); free(tb->alpha); free(tb->u); free(tb->v); free(tb->beta); free(tb->tmp);
+    free(tb->S); free(tb->alpha); free(tb->u); free(tb->v); free(tb->beta);
+    free(tb->zf); free(tb->zb); free(tb->tmp);
 }
 
-/* Forward table: alpha[t,c] for t=1..L, u[t,c] for t=0..L-1.  Returns log Z. */
+/* Largest value of a row (-inf when all are -inf). */
+static double row_max(const double *v, int n)
+{
+    double m = ORACLE_NEG_INF;
+    for (int i = 0; i < n; ++i)
+        if (v[i] > m) m = v[i];
+    return m;
+}
+
+/* Forward table: alpha[t,c] for t=1..L, u[t,c] for t=0..L-1, each stored
+ * minus the integer offset zf[t].  Returns LSE_c (alpha[L,c] - zf[L]); log Z
+ * is zf[L] plus that. */
 static double forward_one(int L, int C, int K, const double *S, const double *tr,
-                          const double *du, double *alpha, double *u, double *tmp, int nth)
+                          const double *du, double *alpha, double *u, double *zf, double *tmp,
+                          int nth)
 {
     for (int c = 0; c < C; ++c) { u[c] = 0.0; alpha[c] = ORACLE_NEG_INF; }
+    zf[0] = 0.0;
 #pragma omp parallel num_threads(nth) if (nth > 1)
     {
         int tid = 0;
@@ -154,13 +179,20 @@ static double forward_one(int L, int C, int K, const double *S, const double *tr
         double *buf = tmp + (size_t)tid * (size_t)(K > C ? K : C);
         for (int t = 1; t <= L; ++t) {
             int kmax = t < K ? t : K;
+            /* alpha[t,c] relative to zf[t-1] */
 #pragma omp for schedule(static)
             for (int c = 0; c < C; ++c) {
                 for (int k = 1; k <= kmax; ++k)
-                    buf[k - 1] = u[(size_t)(t - k) * C + c]
+                    buf[k - 1] = u[(size_t)(t - k) * C + c] + (zf[t - k] - zf[t - 1])
                                + (S[(size_t)t * C + c] - S[(size_t)(t - k) * C + c])
                                + du[(size_t)(k - 1) * C + c];
                 alpha[(size_t)t * C + c] = lse_array(buf, kmax);
+            }
+#pragma omp single
+            {
+                double n = floor(row_max(alpha + (size_t)t * C, C));
+                zf[t] = zf[t - 1] + n;
+                for (int c = 0; c < C; ++c) alpha[(size_t)t * C + c] -= n;
             }
             if (t < L) {
 #pragma omp for schedule(static)
@@ -175,12 +207,15 @@ static double forward_one(int L, int C, int K, const double *S, const double *tr
     return lse_array(alpha + (size_t)L * C, C);
 }
 
-/* Backward table: v[t,c] for t=0..L-1, beta[t,c] for t=1..L.  Returns the
- * right-to-left log Z, LSE_c v[0,c]. */
+/* Backward table: v[t,c] for t=0..L-1, beta[t,c] for t=1..L, each stored
+ * minus the integer offset zb[t].  Returns LSE_c (v[0,c] - zb[0]); the
+ * right-to-left log Z is zb[0] plus that. */
 static double backward_one(int L, int C, int K, const double *S, const double *tr,
-                           const double *du, double *v, double *beta, double *tmp, int nth)
+                           const double *du, double *v, double *beta, double *zb, double *tmp,
+                           int nth)
 {
     for (int c = 0; c < C; ++c) beta[(size_t)L * C + c] = 0.0;
+    zb[L] = 0.0;
 #pragma omp parallel num_threads(nth) if (nth > 1)
     {
         int tid = 0;
@@ -190,13 +225,20 @@ static double backward_one(int L, int C, int K, const double *S, const double *t
         double *buf = tmp + (size_t)tid * (size_t)(K > C ? K : C);
         for (int t = L - 1; t >= 0; --t) {
             int kmax = (L - t) < K ? (L - t) : K;
+            /* v[t,c] relative to zb[t+1] */
 #pragma omp for schedule(static)
             for (int c = 0; c < C; ++c) {
                 for (int k = 1; k <= kmax; ++k)
                     buf[k - 1] = (S[(size_t)(t + k) * C + c] - S[(size_t)t * C + c])
                                + du[(size_t)(k - 1) * C + c]
-                               + beta[(size_t)(t + k) * C + c];
+                               + beta[(size_t)(t + k) * C + c] + (zb[t + k] - zb[t + 1]);
                 v[(size_t)t * C + c] = lse_array(buf, kmax);
+            }
+#pragma omp single
+            {
+                double n = floor(row_max(v + (size_t)t * C, C));
+                zb[t] = zb[t + 1] + n;
+                for (int c = 0; c < C; ++c) v[(size_t)t * C + c] -= n;
             }
             if (t >= 1) {
 #pragma omp for schedule(static)
@@ -214,11 +256,12 @@ static double backward_one(int L, int C, int K, const double *S, const double *t
 /* Posteriors of one sequence.  Adds w * (its contribution) into gtrans/gdur
  * (local per-sequence buffers supplied by the caller) and writes mu / grad_x
  * rows [0,T) (zeros at t >= L). */
-static void posteriors_one(int T, int L, int C, int K, int center, double w, double logz,
+static void posteriors_one(int T, int L, int C, int K, int center, double w, double lzs,
                            const double *S, const double *tr, const double *du,
                            const double *alpha, const double *u, const double *v,
-                           const double *beta, double *gtrans, double *gdur,
-                           double *mu_out, double *gx_out, int nth)
+                           const double *beta, const double *zf, const double *zb,
+                           double *gtrans, double *gdur, double *mu_out, double *gx_out,
+                           int nth)
 {
     double *diff = calloc((size_t)(T + 1) * C, sizeof(double));
     double *mu = calloc((size_t)T * C, sizeof(double));
@@ -231,7 +274,8 @@ static void posteriors_one(int T, int L, int C, int K, int center, double w, dou
                 double lp = u[(size_t)s * C + c]
                           + (S[(size_t)(s + k) * C + c] - S[(size_t)s * C + c])
                           + du[(size_t)(k - 1) * C + c]
-                          + beta[(size_t)(s + k) * C + c] - logz;
+                          + beta[(size_t)(s + k) * C + c]
+                          + ((zf[s] + zb[s + k] - zf[L]) - lzs);
                 double p = exp(lp);
                 if (gdur) gdur[(size_t)(k - 1) * C + c] += w * p;
                 diff[(size_t)s * C + c] += p;
@@ -248,7 +292,7 @@ static void posteriors_one(int T, int L, int C, int K, int center, double w, dou
             for (int t = 1; t < L; ++t)
                 for (int cp = 0; cp < C; ++cp) {
                     double lp = alpha[(size_t)t * C + cp] + tr[(size_t)cp * C + c]
-                              + v[(size_t)t * C + c] - logz;
+                              + v[(size_t)t * C + c] + ((zf[t] + zb[t] - zf[L]) - lzs);
                     gtrans[(size_t)cp * C + c] += w * exp(lp);
                 }
         }
@@ -324,15 +368,16 @@ int oracle_fwd_bwd(int B, int T, int C, int K, const float *x, const int32_t *le
         }
         double *nu = malloc((size_t)C * sizeof(double));
         prefix_one(T, C, L, xb, center, nu, tb.S);
-        double lz = forward_one(L, C, K, tb.S, tr, du, tb.alpha, tb.u, tb.tmp, inner);
-        logz[b] = lz;
+        double lzs = forward_one(L, C, K, tb.S, tr, du, tb.alpha, tb.u, tb.zf, tb.tmp, inner);
+        logz[b] = tb.zf[L] + lzs;
         if (want_post || logz_bwd) {
-            double lzb = backward_one(L, C, K, tb.S, tr, du, tb.v, tb.beta, tb.tmp, inner);
-            if (logz_bwd) logz_bwd[b] = lzb;
+            double lzb = backward_one(L, C, K, tb.S, tr, du, tb.v, tb.beta, tb.zb, tb.tmp, inner);
+            if (logz_bwd) logz_bwd[b] = tb.zb[0] + lzb;
         }
         if (want_post)
-            posteriors_one(T, L, C, K, center, wb, lz, tb.S, tr, du, tb.alpha, tb.u, tb.v,
-                           tb.beta, gt_all + (size_t)b * C * C, gd_all + (size_t)b * K * C,
+            posteriors_one(T, L, C, K, center, wb, lzs, tb.S, tr, du, tb.alpha, tb.u, tb.v,
+                           tb.beta, tb.zf, tb.zb, gt_all + (size_t)b * C * C,
+                           gd_all + (size_t)b * K * C,
                            marginals ? marginals + (size_t)b * T * C : NULL,
                            grad_x ? grad_x + (size_t)b * T * C : NULL, inner);
         free(nu);
