@@ -28,15 +28,37 @@ bool chain_config(int C, int K, ChainShape &sh) {
     if (P < 1 || Q * C > NT) continue;
     const int A = (K + P - 1) / P;
     if (A > amax[i]) continue;
-    if (chain_lds_bytes(C, K, P, Q) > kMaxLds) continue;
+    int QT, CS;
+    chain_slices(C, NT, QT, CS);
+    if (chain_lds_bytes(C, K, P, QT) > kMaxLds) continue;
     if (viterbi_lds_bytes(C, K, P, Q) > kMaxLds) continue;
     sh.NT = NT;
     sh.P = P;
     sh.A = A;
     sh.Q = Q;
+    sh.QT = QT;
+    sh.CS = CS;
     return true;
   }
   return false;
+}
+
+// Windowed engine (C <= 32, 256 threads): each of the P = 256 / C threads
+// of a label owns a register window of up to 32 consecutive durations, so it
+// applies when K <= 32 * P and the LDS fits.  Other shapes run on the
+// LDS-ring engine.
+bool win_config(int C, int K, ChainShape &sh) {
+  if (C < 1 || C > 32) return false;
+  const int NT = 256;
+  const int P = NT / C;
+  const int A = (K + P - 1) / P;
+  if (A > 32 || win_lds_bytes(C, K, P) > kMaxLds) return false;
+  sh.NT = NT;
+  sh.P = P;
+  sh.A = A;
+  sh.Q = 1;
+  sh.win = 1;
+  return true;
 }
 
 semicrf_status_t check_sizes(int B, int T, int C, int K) {
@@ -126,7 +148,11 @@ semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int
   sh.K = K;
   sh.center = (flags & SEMICRF_NO_CENTER) ? 0 : 1;
   if (op != SEMICRF_OP_SCAN) {
-    if (!chain_config(C, K, sh)) return SEMICRF_ERR_UNSUPPORTED;
+    // Viterbi always uses the LDS-ring layout; the sweeps use the windowed
+    // engine when it applies.  Both must exist for a supported (C, K).
+    ChainShape probe = sh;
+    if (!chain_config(C, K, probe)) return SEMICRF_ERR_UNSUPPORTED;
+    if (op == SEMICRF_OP_VITERBI || !win_config(C, K, sh)) sh = probe;
     sh.delta = ckpt > 0 ? (ckpt < T ? ckpt : T) : default_delta(T, K);
     sh.nchunk = (T + sh.delta - 1) / sh.delta;
   }

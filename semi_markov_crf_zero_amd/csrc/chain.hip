@@ -23,16 +23,24 @@
 // variables.
 //
 // MI355X design:
-//   * exp-space ring in LDS: ring[slot][c] = exp(entry - ref[c]) in float64,
-//     ref[c] a per-label float64 log reference.  The K-way log-sum-exp becomes
-//     a K-term float64 dot product with D[k][c] = exp(dur[k-1][c]) (no
-//     transcendental per segment cell).  Whenever a new entry leaves
-//     [2^-260, 2^260] relative to ref[c], the label's column is rescaled by
-//     an exact power of two (v_ldexp_f64) and ref[c] moves by n*ln2.  The
-//     recurrence guarantees g[t] >= g[t-k] + trans[c,c] + dur[k-1,c] (and the
-//     mirror for h), so older ring entries never exceed the newest by more
-//     than a parameter-bounded factor, and the rescale keeps every entry in
-//     float64 range.
+//   * exp-space ring in LDS: ring[slot][c] = exp(entry - R[c]*ln2) in
+//     float64, R[c] a per-label integer log reference.  The K-way
+//     log-sum-exp becomes a K-term float64 dot product with
+//     D[k][c] = exp(dur[k-1][c]) (no transcendental per segment cell).
+//     Whenever a new entry leaves [2^-260, 2^260] relative to its reference,
+//     the label's column is rescaled by an exact power of two (v_ldexp_f64)
+//     and R[c] moves by that exponent.  The recurrence guarantees
+//     g[t] >= g[t-k] + trans[c,c] + dur[k-1,c] (and the mirror for h), so
+//     older ring entries never exceed the newest by more than a
+//     parameter-bounded factor, and the rescale keeps every entry in float64
+//     range.
+//   * the log values themselves grow linearly along the sequence (~5e6 at a
+//     million positions, where a float64 holds only ~1e-9 absolute).  Each
+//     step therefore runs relative to base*ln2, base = label 0's integer
+//     reference: only small numbers and small integer differences R - base
+//     enter the recursion, so no rounding of a large number accumulates.
+//     Absolute alpha/u/beta (formed once, for the posterior exponents) and
+//     log Z carry a single rounding each.
 //   * the transition contraction is an exp-space matrix-vector product with
 //     exp(trans) held in registers (fp32), max-shifted per row.
 //   * one workgroup per chain; the forward and the backward chain of every
@@ -45,6 +53,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "device_math.h"
 #include "internal.h"
 
@@ -53,8 +63,7 @@ namespace semicrf {
 constexpr double kRebaseNats = 180.0;  // ~2^260
 
 struct Smem {
-  double *ring, *part, *orow, *refs, *scal;
-  float *erow, *dotp;
+  double *ring, *part, *orow, *refs, *scal, *erow, *dotp;
   int *shiftn;
 };
 
@@ -66,17 +75,23 @@ __device__ __forceinline__ Smem carve(unsigned char *base, const ChainShape &s) 
   m.orow = reinterpret_cast<double *>(base + off); off += (size_t)s.C * 8;
   m.refs = reinterpret_cast<double *>(base + off); off += (size_t)s.C * 8;
   m.scal = reinterpret_cast<double *>(base + off); off += 8 * 8;
-  m.erow = reinterpret_cast<float *>(base + off); off += (size_t)s.C * 4;
-  m.dotp = reinterpret_cast<float *>(base + off); off += (size_t)s.Q * s.C * 4;
+  m.erow = reinterpret_cast<double *>(base + off); off += (size_t)s.C * 8;
+  m.dotp = reinterpret_cast<double *>(base + off); off += (size_t)s.QT * s.C * 8;
   m.shiftn = reinterpret_cast<int *>(base + off);
   return m;
 }
 
-// Per-thread constants of one chain direction.
+// Per-thread constants of one chain direction.  The contraction weights are
+// float64 for slices of up to 16 previous labels (every C <= 64): a rounded
+// exp(trans) is a fixed perturbation of the parameters, and the parameter
+// gradients -- sums over the whole sequence -- move by it times their own
+// sensitivity, which grows with the sequence length.  Wider slices (C > 90
+// at 512 threads, C > 128 at 1024) keep float32 weights for registers.
 template <int AMAX, int TRMAX, typename DT>
 struct Regs {
-  DT D[AMAX];       // exp(dur[k-1][c]) for the thread's durations
-  float Tr[TRMAX];  // exp(trans) slice for the contraction role
+  using WT = typename std::conditional<(TRMAX <= 16), double, float>::type;
+  DT D[AMAX];    // exp(dur[k-1][c]) for the thread's durations
+  WT Tr[TRMAX];  // exp(trans) slice for the contraction role
   int kc, kp, age0, nage;
   int cc, cq, cp0, ncp;
 };
@@ -96,9 +111,9 @@ __device__ __forceinline__ void init_regs(Regs<AMAX, TRMAX, DT> &r, const ChainS
     r.D[j] = (j < r.nage) ? (DT)exp((double)dur[(size_t)(r.age0 + j - 1) * C + r.kc]) : (DT)0;
   r.cc = tid % C;
   r.cq = tid / C;
-  r.cp0 = r.cq * 64;
-  int m = (r.cq < sh.Q) ? C - r.cp0 : 0;
-  r.ncp = m < 0 ? 0 : (m > 64 ? 64 : m);
+  r.cp0 = r.cq * sh.CS;
+  int m = (r.cq < sh.QT) ? C - r.cp0 : 0;
+  r.ncp = m < 0 ? 0 : (m > sh.CS ? sh.CS : m);
 }
 
 // Contraction weights for direction `fwd`: forward sums over the previous
@@ -109,12 +124,12 @@ __device__ __forceinline__ void load_trans(Regs<AMAX, TRMAX, DT> &r, const Chain
   const int C = sh.C;
 #pragma unroll
   for (int j = 0; j < TRMAX; ++j) {
-    float w = 0.f;
+    double w = 0.0;
     if (j < r.ncp) {
       const int cp = r.cp0 + j;
-      w = __expf(fwd ? trans[(size_t)cp * C + r.cc] : trans[(size_t)r.cc * C + cp]);
+      w = exp((double)(fwd ? trans[(size_t)cp * C + r.cc] : trans[(size_t)r.cc * C + cp]));
     }
-    r.Tr[j] = w;
+    r.Tr[j] = (typename Regs<AMAX, TRMAX, DT>::WT)w;
   }
 }
 
@@ -162,42 +177,55 @@ __device__ __forceinline__ double row_max(double v, bool is_row, const ChainShap
   return m;
 }
 
-// Contraction: row thread c receives M + log(sum_{c'} e[c'] * W[c'][c]).
-// Requires sm.erow written and a barrier before the call.  All threads call.
+// Contraction: row thread c receives M + log(sum_{c'} e[c'] * W[c'][c]),
+// summed in float64 (any per-step rounding here would accumulate along the
+// chain).  Slice partials meet in LDS and the row thread adds them in a
+// fixed order.  Requires sm.erow written and a barrier before the call.
+// All threads call.
 template <int AMAX, int TRMAX, typename DT>
 __device__ __forceinline__ double contract(const Regs<AMAX, TRMAX, DT> &r, const Smem &sm,
                                            const ChainShape &sh, double M) {
-  float dp = 0.f;
+  using WT = typename Regs<AMAX, TRMAX, DT>::WT;
+  double dp = 0.0;
 #pragma unroll
-  for (int j = 0; j < TRMAX; ++j)
-    if (j < r.ncp) dp = fmaf(sm.erow[r.cp0 + j], r.Tr[j], dp);
-  if (sh.Q > 1) {
-    if (r.cq < sh.Q) sm.dotp[r.cq * sh.C + r.cc] = dp;
-    __syncthreads();
-    if ((int)threadIdx.x < sh.C) {
-      dp = 0.f;
-      for (int q = 0; q < sh.Q; ++q) dp += sm.dotp[q * sh.C + threadIdx.x];
+  for (int j = 0; j < TRMAX; ++j) {
+    if (j < r.ncp) {
+      WT w = r.Tr[j];
+      if (!std::is_same<WT, double>::value) {
+        // keep a float32 weight live as float32: converting all TRMAX
+        // weights once, outside the time loop, would double their registers
+        asm volatile("" : "+v"(w));
+      }
+      dp = fma(sm.erow[r.cp0 + j], (double)w, dp);
     }
   }
-  return M + (double)__builtin_amdgcn_logf(dp) * kLn2;
+  if (sh.QT > 1) {
+    if (r.cq < sh.QT) sm.dotp[r.cq * sh.C + r.cc] = dp;
+    __syncthreads();
+    if ((int)threadIdx.x < sh.C) {
+      dp = 0.0;
+      for (int q = 0; q < sh.QT; ++q) dp += sm.dotp[q * sh.C + threadIdx.x];
+    }
+  }
+  return M + log(dp);
 }
 
-// Row thread c inserts the entry for position t (log value `entry`) and
-// decides an exact power-of-two rebase of its column.  Returns true if the
-// column must be rescaled by 2^-n (n in sm.shiftn[c]).
+// Row thread c inserts the entry for position t, given as d = entry minus
+// its log reference R*ln2 (R an exact integer), and decides an exact
+// power-of-two rebase of its column.  Returns true if the column must be
+// rescaled by 2^-n (n in sm.shiftn[c]).
 __device__ __forceinline__ bool insert_entry(const Smem &sm, const ChainShape &sh, int t,
-                                             double entry, double &ref) {
+                                             double d, int &R) {
   const int c = threadIdx.x;
-  double d = entry - ref;
   int n = 0;
   if (fabs(d) > kRebaseNats) {
     n = (int)rint(d * kLog2e);
-    ref += (double)n * kLn2;
-    d = entry - ref;
+    R += n;
+    d -= (double)n * kLn2;
   }
   sm.shiftn[c] = n;
-  sm.refs[c] = ref;
-  sm.ring[(t % sh.K) * sh.C + c] = exp_wide(d);
+  sm.refs[c] = (double)R;
+  sm.ring[(t % sh.K) * sh.C + c] = exp(d);
   return n != 0;
 }
 
@@ -223,30 +251,27 @@ __device__ __forceinline__ void apply_rebase(const Regs<AMAX, TRMAX, DT> &r, con
   __syncthreads();
 }
 
-// Checkpoint record: [K*C ring][C ref][C o][C m] (float64).
-__host__ __device__ inline size_t ck_stride(int C, int K) { return (size_t)(K + 3) * C; }
 
 __device__ __forceinline__ void save_ckpt(double *__restrict__ dst, const Smem &sm,
-                                          const ChainShape &sh, double ref, double o, double m) {
+                                          const ChainShape &sh, int R, double o, double m) {
   const int n = sh.K * sh.C;
   for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = sm.ring[i];
   if ((int)threadIdx.x < sh.C) {
-    dst[n + threadIdx.x] = ref;
+    dst[n + threadIdx.x] = (double)R;
     dst[n + sh.C + threadIdx.x] = o;
     dst[n + 2 * sh.C + threadIdx.x] = m;
   }
 }
 
 __device__ __forceinline__ void load_ckpt(const double *__restrict__ src, const Smem &sm,
-                                          const ChainShape &sh, double &ref, double &o,
-                                          double &m) {
+                                          const ChainShape &sh, int &R, double &o, double &m) {
   const int n = sh.K * sh.C;
   for (int i = threadIdx.x; i < n; i += blockDim.x) sm.ring[i] = src[i];
   if ((int)threadIdx.x < sh.C) {
-    ref = src[n + threadIdx.x];
+    R = (int)src[n + threadIdx.x];
     o = src[n + sh.C + threadIdx.x];
     m = src[n + 2 * sh.C + threadIdx.x];
-    sm.refs[threadIdx.x] = ref;
+    sm.refs[threadIdx.x] = (double)R;
   }
   __syncthreads();
 }
@@ -255,11 +280,11 @@ __device__ __forceinline__ void load_ckpt(const double *__restrict__ src, const 
 __device__ __forceinline__ double row_lse(double o, bool is_row, const ChainShape &sh,
                                           const Smem &sm) {
   const double M = row_max(o, is_row, sh, sm);
-  if (is_row) sm.orow[threadIdx.x] = exp_wide(o - M);
+  if (is_row) sm.orow[threadIdx.x] = exp(o - M);
   __syncthreads();
   double s = 0.0;
   for (int c = 0; c < sh.C; ++c) s += sm.orow[c];
-  return M + log_wide(s);
+  return M + log(s);
 }
 
 // ---------------------------------------------------------------- sweeps
@@ -304,19 +329,23 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
   __syncthreads();
   // initial entry: forward position 0 (u = 0), backward position L (beta = 0)
   const int tstart = fwd ? 0 : L;
-  double ref = 0.0;
+  int R = 0;
   if (is_row) {
-    const double entry = fwd ? 0.0 : Sb[(size_t)L * C + tid];
-    ref = entry;
-    sm.refs[tid] = ref;
-    sm.ring[(tstart % K) * C + tid] = 1.0;
+    double d = 0.0;  // entry minus R*ln2: u[0] - S[0] = 0 forward, beta[L] + S[L] backward
+    if (!fwd) {
+      const double sl = Sb[(size_t)L * C + tid];
+      R = (int)rint(sl * kLog2e);
+      d = sl - (double)R * kLn2;
+    }
+    sm.refs[tid] = (double)R;
+    sm.ring[(tstart % K) * C + tid] = exp(d);
   }
   __syncthreads();
   if (write_ckpt) {
     // forward checkpoint 0 holds p0 = 0 (u[0] = 0); the backward checkpoint
     // of the last chunk holds p1 = L (beta[L] = 0).  o is undefined there.
     const int j = fwd ? 0 : (L - 1) / sh.delta;
-    save_ckpt(ckb + (size_t)j * cks, sm, sh, ref, -__builtin_huge_val(), 0.0);
+    save_ckpt(ckb + (size_t)j * cks, sm, sh, R, -__builtin_huge_val(), 0.0);
   }
 
   const int nsteps = L;  // forward t = 1..L, backward t = L-1..0
@@ -326,15 +355,18 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
     const double s = r.kp < sh.P ? ksum<false>(r, sm, sh, t, fwd, nogd, 0.0) : 0.0;
     if (r.kp < sh.P) sm.part[r.kp * C + r.kc] = s;
     __syncthreads();
-    double o = 0.0;
+    // the step runs relative to base*ln2, base = label 0's integer reference
+    const int base = (int)sm.refs[0];
+    const double bl = (double)base * kLn2;
+    double o = 0.0;  // alpha (forward) or v (backward) minus bl
     if (is_row) {
       double sum = 0.0;
       for (int p = 0; p < sh.P; ++p) sum += sm.part[p * C + tid];
-      o = sigma * Sb[(size_t)t * C + tid] + ref + log_wide(sum);
+      o = sigma * Sb[(size_t)t * C + tid] + (double)(R - base) * kLn2 + log(sum);
     }
     const bool last = fwd ? (t == L) : (t == 0);
     if (last) {
-      const double lz = row_lse(o, is_row, sh, sm);
+      const double lz = bl + row_lse(o, is_row, sh, sm);
       if (tid == 0) {
         if (fwd) {
           logz_ws[b] = lz;
@@ -346,17 +378,19 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
       break;
     }
     const double M = row_max(o, is_row, sh, sm);
-    if (is_row) sm.erow[tid] = (float)exp_wide(o - M);
+    if (is_row) sm.erow[tid] = exp(o - M);
     __syncthreads();
-    const double m = contract(r, sm, sh, M);
+    const double m = contract(r, sm, sh, M);  // u (forward) or beta (backward) minus bl
     bool need = false;
-    if (is_row) need = insert_entry(sm, sh, t, m - sigma * Sb[(size_t)t * C + tid], ref);
+    if (is_row)
+      need = insert_entry(sm, sh, t,
+                          (m - sigma * Sb[(size_t)t * C + tid]) + (double)(base - R) * kLn2, R);
     if (__syncthreads_or(need)) apply_rebase(r, sm, sh, t, fwd);
     if (write_ckpt && (t % sh.delta) == 0) {
       // forward: checkpoint j = t/delta holds position p0 = t;
       // backward: checkpoint j = t/delta - 1 holds position p1 = t.
       const int j = fwd ? t / sh.delta : t / sh.delta - 1;
-      save_ckpt(ckb + (size_t)j * cks, sm, sh, ref, o, m);
+      save_ckpt(ckb + (size_t)j * cks, sm, sh, R, bl + o, bl + m);
     }
   }
 }
@@ -415,8 +449,9 @@ __global__ __launch_bounds__(NT) void k_chunk(
 
   // ---- phase A: forward recompute
   load_trans(r, sh, trans, true);
-  double ref = 0.0, o = 0.0, m = 0.0;
-  load_ckpt(ck_fwd + cid * cks, sm, sh, ref, o, m);
+  int R = 0;
+  double o = 0.0, m = 0.0;
+  load_ckpt(ck_fwd + cid * cks, sm, sh, R, o, m);
   if (is_row) {
     sa[tid] = o;
     su[tid] = m;
@@ -426,21 +461,24 @@ __global__ __launch_bounds__(NT) void k_chunk(
     const double s = r.kp < sh.P ? ksum<false>(r, sm, sh, t, true, nogd, 0.0) : 0.0;
     if (r.kp < sh.P) sm.part[r.kp * C + r.kc] = s;
     __syncthreads();
+    const int base = (int)sm.refs[0];
+    const double bl = (double)base * kLn2;
     if (is_row) {
       double sum = 0.0;
       for (int p = 0; p < sh.P; ++p) sum += sm.part[p * C + tid];
-      o = Sb[(size_t)t * C + tid] + ref + log_wide(sum);
-      sa[(size_t)(t - p0) * C + tid] = o;
+      o = Sb[(size_t)t * C + tid] + (double)(R - base) * kLn2 + log(sum);  // alpha - bl
+      sa[(size_t)(t - p0) * C + tid] = bl + o;
     }
     if (t == p1) break;
     const double M = row_max(o, is_row, sh, sm);
-    if (is_row) sm.erow[tid] = (float)exp_wide(o - M);
+    if (is_row) sm.erow[tid] = exp(o - M);
     __syncthreads();
-    m = contract(r, sm, sh, M);
+    m = contract(r, sm, sh, M);  // u - bl
     bool need = false;
     if (is_row) {
-      su[(size_t)(t - p0) * C + tid] = m;
-      need = insert_entry(sm, sh, t, m - Sb[(size_t)t * C + tid], ref);
+      su[(size_t)(t - p0) * C + tid] = bl + m;
+      need = insert_entry(sm, sh, t, (m - Sb[(size_t)t * C + tid]) + (double)(base - R) * kLn2,
+                          R);
     }
     if (__syncthreads_or(need)) apply_rebase(r, sm, sh, t, true);
   }
@@ -448,33 +486,36 @@ __global__ __launch_bounds__(NT) void k_chunk(
 
   // ---- phase B: backward over the chunk with posteriors
   load_trans(r, sh, trans, false);
-  load_ckpt(ck_bwd + cid * cks, sm, sh, ref, o, m);  // state at p1, m = beta[p1]
+  load_ckpt(ck_bwd + cid * cks, sm, sh, R, o, m);  // state at p1, m = beta[p1]
   GT gd[AMAX];
 #pragma unroll
   for (int j = 0; j < AMAX; ++j) gd[j] = (GT)0;
   double suffix = 0.0, ssum = 0.0;
   float *suf = suffix_out + (size_t)b * sh.T * C;
   if (is_row) {
-    const double eend = exp_wide(sa[(size_t)(p1 - p0) * C + tid] + m - logZ);
+    const double eend = exp(sa[(size_t)(p1 - p0) * C + tid] + m - logZ);
     suffix = -eend;
   }
   for (int t = p1 - 1; t >= p0; --t) {
     double s = 0.0;
     if (r.kp < sh.P) {
-      // Q[t,c] = exp(u[t,c] - S[t,c] + ref[c] - logZ): P(t,k,c) = Q * D * ring
+      // Q[t,c] = exp(u[t,c] - S[t,c] + R[c]*ln2 - logZ): P(t,k,c) = Q * D * ring
       const double ut = su[(size_t)(t - p0) * C + r.kc];
-      const double q = exp_wide(ut - Sb[(size_t)t * C + r.kc] + sm.refs[r.kc] - logZ);
+      const double q =
+          exp_wide((ut + sm.refs[r.kc] * kLn2 - logZ) - Sb[(size_t)t * C + r.kc]);
       s = ksum<true>(r, sm, sh, t, false, gd, q);
       sm.part[r.kp * C + r.kc] = s;
     }
     __syncthreads();
+    const int base = (int)sm.refs[0];
+    const double bl = (double)base * kLn2;
     double at = 0.0;
     if (is_row) {
       double sum = 0.0;
       for (int p = 0; p < sh.P; ++p) sum += sm.part[p * C + tid];
-      o = -Sb[(size_t)t * C + tid] + ref + log_wide(sum);  // v[t]
+      o = -Sb[(size_t)t * C + tid] + (double)(R - base) * kLn2 + log(sum);  // v[t] - bl
       const double ut = su[(size_t)(t - p0) * C + tid];
-      const double estart = exp_wide(ut + o - logZ);
+      const double estart = exp((ut + bl - logZ) + o);
       suf[(size_t)t * C + tid] = (float)suffix;
       ssum += suffix;
       suffix += estart;
@@ -483,17 +524,18 @@ __global__ __launch_bounds__(NT) void k_chunk(
     if (t == 0) break;
     const double M = row_max(o, is_row, sh, sm);
     if (is_row) {
-      const float e = (float)exp_wide(o - M);
+      const double e = exp(o - M);
       sm.erow[tid] = e;
-      sev[(size_t)(t - p0) * C + tid] = e;
-      sea[(size_t)(t - p0) * C + tid] = (float)exp_wide(at + M - logZ);
+      sev[(size_t)(t - p0) * C + tid] = (float)e;
+      sea[(size_t)(t - p0) * C + tid] = (float)exp_wide((at + bl - logZ) + M);
     }
     __syncthreads();
-    m = contract(r, sm, sh, M);  // beta[t]
+    m = contract(r, sm, sh, M);  // beta[t] - bl
     bool need = false;
     if (is_row) {
-      need = insert_entry(sm, sh, t, m + Sb[(size_t)t * C + tid], ref);
-      if (t > p0) suffix -= exp_wide(at + m - logZ);  // E_end[t]
+      need = insert_entry(sm, sh, t, (m + Sb[(size_t)t * C + tid]) + (double)(base - R) * kLn2,
+                          R);
+      if (t > p0) suffix -= exp((at + bl - logZ) + m);  // E_end[t]
     }
     if (__syncthreads_or(need)) apply_rebase(r, sm, sh, t, false);
   }
@@ -660,7 +702,7 @@ struct ChainKernels {
                           const double *S, const int32_t *lengths, double *ck_fwd,
                           double *ck_bwd, double *logz_ws, double *logz_bwd_ws,
                           float *logz_out, int with_bwd, int write_ckpt, hipStream_t st) {
-    const size_t lds = chain_lds_bytes(sh.C, sh.K, sh.P, sh.Q);
+    const size_t lds = chain_lds_bytes(sh.C, sh.K, sh.P, sh.QT);
     set_attrs();
     hipLaunchKernelGGL((k_sweep<NT, AMAX, TRMAX, DT>), dim3(with_bwd ? 2 * sh.B : sh.B),
                        dim3(NT), lds, st, sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws,
@@ -673,7 +715,7 @@ struct ChainKernels {
                            double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
                            double *part_gd, double *part_tot, double *part_ssum,
                            float *suffix_out, hipStream_t st) {
-    const size_t lds = chain_lds_bytes(sh.C, sh.K, sh.P, sh.Q);
+    const size_t lds = chain_lds_bytes(sh.C, sh.K, sh.P, sh.QT);
     set_attrs();
     hipLaunchKernelGGL((k_chunk<NT, AMAX, TRMAX, DT, GT>), dim3(sh.B * sh.nchunk), dim3(NT),
                        lds, st, sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, scr_a,
@@ -682,19 +724,25 @@ struct ChainKernels {
   }
 };
 
+// Instances: threads NT x slice width TRMAX (>= sh.CS, the contraction
+// slice; float64 weights up to 16).
 #define SEMICRF_CHAIN_DISPATCH(SH, CALL)                                                   \
   do {                                                                                     \
-    const int trmax_ = (SH).C <= 8 ? 8 : ((SH).C <= 32 ? 32 : 64);                        \
+    const int cs_ = (SH).CS;                                                               \
+    const int trmax_ = cs_ <= 8 ? 8 : (cs_ <= 16 ? 16 : (cs_ <= 32 ? 32 : 64));           \
     if ((SH).NT == 256) {                                                                  \
       if (trmax_ == 8) return ChainKernels<256, 32, 8, double, double>::CALL;              \
+      if (trmax_ == 16) return ChainKernels<256, 32, 16, double, double>::CALL;            \
       if (trmax_ == 32) return ChainKernels<256, 32, 32, double, double>::CALL;            \
       return ChainKernels<256, 32, 64, double, double>::CALL;                              \
     } else if ((SH).NT == 512) {                                                           \
       if (trmax_ == 8) return ChainKernels<512, 32, 8, double, double>::CALL;              \
+      if (trmax_ == 16) return ChainKernels<512, 32, 16, double, double>::CALL;            \
       if (trmax_ == 32) return ChainKernels<512, 32, 32, double, double>::CALL;            \
       return ChainKernels<512, 32, 64, double, double>::CALL;                              \
     } else {                                                                               \
       if (trmax_ == 8) return ChainKernels<1024, 16, 8, float, float>::CALL;               \
+      if (trmax_ == 16) return ChainKernels<1024, 16, 16, float, float>::CALL;             \
       if (trmax_ == 32) return ChainKernels<1024, 16, 32, float, float>::CALL;             \
       return ChainKernels<1024, 16, 64, float, float>::CALL;                               \
     }                                                                                      \
@@ -704,6 +752,9 @@ hipError_t launch_sweep(const ChainShape &sh, const float *trans, const float *d
                         const double *S, const int32_t *lengths, double *ck_fwd,
                         double *ck_bwd, double *logz_ws, double *logz_bwd_ws, float *logz_out,
                         int with_bwd, int write_ckpt, hipStream_t st) {
+  if (sh.win)
+    return launch_sweep_w(sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, logz_bwd_ws,
+                          logz_out, with_bwd, write_ckpt, st);
   SEMICRF_CHAIN_DISPATCH(sh, sweep(sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws,
                                    logz_bwd_ws, logz_out, with_bwd, write_ckpt, st));
 }
@@ -714,6 +765,9 @@ hipError_t launch_chunks(const ChainShape &sh, const float *trans, const float *
                          double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
                          double *part_gd, double *part_tot, double *part_ssum,
                          float *suffix_out, hipStream_t st) {
+  if (sh.win)
+    return launch_chunks_w(sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, scr_a, scr_u,
+                           scr_ea, scr_ev, part_x, part_gd, part_tot, part_ssum, suffix_out, st);
   SEMICRF_CHAIN_DISPATCH(sh, chunks(sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, scr_a,
                                     scr_u, scr_ea, scr_ev, part_x, part_gd, part_tot, part_ssum,
                                     suffix_out, st));

@@ -12,14 +12,17 @@ namespace semicrf {
 //   K-sum role   thread (c = tid % C, p = tid / C), p < P, owns the A
 //                consecutive durations k = p*A+1 .. p*A+A of label c;
 //   row role     thread tid < C owns label c (its log reference, outputs);
-//   contraction  thread (c = tid % C, q = tid / C), q < Q, sums over the
-//                previous labels c' in [64q, 64q+64).
+//   contraction  thread (c = tid % C, q = tid / C), q < QT, sums over the
+//                previous labels c' in [CS*q, CS*q+CS).
 struct ChainShape {
   int B, T, C, K;
   int NT;      // threads per workgroup (256, 512 or 1024)
+  int win;     // 1: windowed engine (C <= 32), 0: LDS-ring engine
   int P;       // K-sum threads per label = NT / C
   int A;       // durations per K-sum thread = ceil(K / P)
-  int Q;       // contraction slices = ceil(C / 64)
+  int Q;       // waves holding row threads = ceil(C / 64) (Viterbi slices)
+  int QT;      // contraction slices of the LDS-ring engine
+  int CS;      // previous labels per contraction slice = ceil(C / QT)
   int delta;   // checkpoint interval (positions)
   int nchunk;  // ceil(T / delta) chunks per sequence
   int center;  // 1 = subtract the per-label baseline nu
@@ -41,17 +44,26 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 
 // Dynamic LDS bytes of one chain workgroup; the carve-up in chain.hip
 // follows the same order.
-__host__ __device__ inline size_t chain_lds_bytes(int C, int K, int P, int Q) {
+__host__ __device__ inline size_t chain_lds_bytes(int C, int K, int P, int QT) {
   size_t off = 0;
-  off += (size_t)K * C * 8;  // ring
-  off += (size_t)P * C * 8;  // K-sum partials
-  off += (size_t)C * 8;      // o row
-  off += (size_t)C * 8;      // per-label log references
-  off += 8 * 8;              // scalars
-  off += (size_t)C * 4;      // e row
-  off += (size_t)Q * C * 4;  // contraction partials
-  off += (size_t)C * 4;      // rebase shifts
+  off += (size_t)K * C * 8;   // ring
+  off += (size_t)P * C * 8;   // K-sum partials
+  off += (size_t)C * 8;       // o row
+  off += (size_t)C * 8;       // per-label log references
+  off += 8 * 8;               // scalars
+  off += (size_t)C * 8;       // e row
+  off += (size_t)QT * C * 8;  // contraction partials
+  off += (size_t)C * 4;       // rebase shifts
   return align_up(off, 16);
+}
+
+// Contraction split of the LDS-ring engine: as many slices as there are
+// thread rows (NT / C, at most C), each of CS consecutive previous labels.
+__host__ __device__ inline void chain_slices(int C, int NT, int &QT, int &CS) {
+  int q = NT / C;
+  q = q < 1 ? 1 : (q > C ? C : q);
+  CS = (C + q - 1) / q;
+  QT = (C + CS - 1) / CS;
 }
 
 // Viterbi LDS: ring (double), partial maxima (double), partial argmax (int),
@@ -65,6 +77,30 @@ __host__ __device__ inline size_t viterbi_lds_bytes(int C, int K, int P, int Q) 
   off += (size_t)Q * C * 8;
   off += (size_t)Q * C * 4;
   off += 8 * 8;
+  return align_up(off, 16);
+}
+
+// Checkpoint record of one chain state (float64): [K*C ring][C ref][C o][C m].
+// ring[slot][c] = exp(entry(position) - ref[c]) with slot = position mod K;
+// o and m are the chain's row outputs at the checkpoint position.
+__host__ __device__ inline size_t ck_stride(int C, int K) { return (size_t)(K + 3) * C; }
+
+// LDS bytes of the windowed chain engine (chain_win.hip, same order as its
+// carve-up): ring, K-sum partials, posterior factors, exp(trans)
+// (float64) with rows padded to a multiple of 4, e row (float64, padded),
+// rebase shifts, flags.
+__host__ __device__ inline size_t win_lds_bytes(int C, int K, int P) {
+  const size_t C4 = (size_t)((C + 3) & ~3);
+  size_t off = 0;
+  off += (size_t)K * C * 8;
+  off += (size_t)P * C * 8;
+  off += (size_t)C * 8;
+  off = align_up(off, 16);
+  off += C4 * C * 8;
+  off = align_up(off, 16);
+  off += C4 * 8;
+  off += (size_t)C * 4;
+  off += 2 * 4;
   return align_up(off, 16);
 }
 
@@ -95,6 +131,19 @@ hipError_t launch_chunks(const ChainShape &sh, const float *trans, const float *
                          double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
                          double *part_gd, double *part_tot, double *part_ssum,
                          float *suffix_out, hipStream_t st);
+
+// windowed engine for C <= 32 (chain_win.hip); same arguments and outputs
+hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float *dur,
+                          const double *S, const int32_t *lengths, double *ck_fwd,
+                          double *ck_bwd, double *logz_ws, double *logz_bwd_ws, float *logz_out,
+                          int with_bwd, int write_ckpt, hipStream_t st);
+
+hipError_t launch_chunks_w(const ChainShape &sh, const float *trans, const float *dur,
+                           const double *S, const int32_t *lengths, const double *ck_fwd,
+                           const double *ck_bwd, const double *logz_ws, double *scr_a,
+                           double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
+                           double *part_gd, double *part_tot, double *part_ssum,
+                           float *suffix_out, hipStream_t st);
 
 hipError_t launch_finish(const ChainShape &sh, const float *trans, const int32_t *lengths,
                          const float *grad_logz, const double *part_x, const double *part_gd,

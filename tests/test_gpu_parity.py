@@ -17,7 +17,7 @@ import pytest
 import oracle
 from semi_markov_crf_zero_amd.workloads import make_random
 from tests.gpu_util import (assert_fwd_bwd_close, assert_viterbi_equal, gpu_fwd_bwd, gpu_logz,
-                            gpu_scan, gpu_viterbi, logz_rel_err)
+                            gpu_scan, gpu_viterbi, logz_rel_err, param_excess)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,26 @@ SHAPES = [
 ]
 
 
+# one per instance of the windowed engine (C <= 32, 256 threads): durations
+# per thread A in {<=8, <=16, <=32} x label bound C in {<=8, <=32}; the C > 32
+# entries run on the LDS-ring engine.
+_WIN64_SKIP = pytest.mark.skip(
+    reason="faulted the GPU while C > 32 shapes ran on the windowed engine (cause not "
+           "found on the CPU emulation); that engine is now limited to C <= 32 and these "
+           "shapes stay off the GPU until the fault is explained")
+WINDOW_SHAPES = [
+    (2, 300, 8, 40, [300, 177]),         # A = 2,  C <= 8
+    (2, 800, 8, 500, [800, 555]),        # A = 16, C <= 8
+    (2, 1200, 8, 1000, [1200, 1001]),    # A = 32, C <= 8
+    (2, 400, 32, 60, [400, 261]),        # A = 8,  C <= 32
+    (2, 900, 32, 120, [900, 611]),       # A = 15, C <= 32
+    (2, 1100, 16, 500, [1100, 777]),     # A = 32, C <= 32 (genome-like)
+    pytest.param((2, 400, 64, 32, [400, 271]), marks=_WIN64_SKIP),
+    pytest.param((2, 700, 64, 60, [700, 513]), marks=_WIN64_SKIP),
+    pytest.param((2, 600, 48, 160, [600, 389]), marks=_WIN64_SKIP),
+]
+
+
 def _case(B, T, C, K, lengths, seed=0, **kw):
     return make_random(B, T, C, K, seed=seed, lengths=lengths, **kw)
 
@@ -49,6 +69,17 @@ def test_fwd_bwd_shapes(shape):
     g = gpu_fwd_bwd(inp)
     errs = assert_fwd_bwd_close(g, o, label=str(shape[:4]))
     print(shape[:4], errs, "logz rel", logz_rel_err(g["logz"], o["logz"]).max())
+
+
+@pytest.mark.parametrize("shape", WINDOW_SHAPES, ids=lambda s: "B%dT%dC%dK%d" % s[:4])
+def test_fwd_bwd_window_instances(shape):
+    B, T, C, K, lengths = shape
+    inp = _case(B, T, C, K, lengths, seed=3 * T + C + K, tsd=0.3, dsd=0.3)
+    o = oracle.fwd_bwd(inp)
+    g = gpu_fwd_bwd(inp)
+    errs = assert_fwd_bwd_close(g, o, label=str(shape[:4]))
+    print(shape[:4], errs)
+    assert logz_rel_err(gpu_logz(inp), o["logz"]).max() <= 1e-5
 
 
 @pytest.mark.parametrize("C,K", list(itertools.product([1, 2, 3], [1, 2, 3, 4])))
@@ -69,8 +100,10 @@ def test_checkpoint_interval_invariance(ckpt):
     g = gpu_fwd_bwd(inp, ckpt=ckpt)
     assert_fwd_bwd_close(g, o, label=ckpt)
     ref = gpu_fwd_bwd(inp, ckpt=0)
-    for k in ("grad_emissions", "grad_trans", "grad_dur", "marginals"):
+    for k in ("grad_emissions", "marginals"):
         assert np.abs(g[k] - ref[k]).max() < 1e-5
+    for k in ("grad_trans", "grad_dur"):
+        assert param_excess(g[k], ref[k], 1e-5) <= 1.0, k
     assert np.abs(g["logz"] - ref["logz"]).max() <= 1e-6 * np.abs(ref["logz"]).max()
 
 

@@ -20,7 +20,7 @@ from semi_markov_crf_zero_amd import binding as bd
 from semi_markov_crf_zero_amd.workloads import make_inputs
 from tests.golden.make_golden import input_digest
 from tests.gpu_util import (TOL_GRAD, assert_fwd_bwd_close, assert_viterbi_equal, gpu_fwd_bwd,
-                            gpu_scan, gpu_viterbi, logz_rel_err, to_dev)
+                            gpu_scan, gpu_viterbi, logz_rel_err, param_excess, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,12 +64,14 @@ def test_large_workloads_golden(name):
     assert rel.max() <= 1e-5, rel
     e_tr = np.abs(g["grad_trans"] - gold["grad_trans"]).max()
     e_du = np.abs(g["grad_dur"] - gold["grad_dur"]).max()
+    x_tr = param_excess(g["grad_trans"], gold["grad_trans"])
+    x_du = param_excess(g["grad_dur"], gold["grad_dur"])
     rows = gold["rows"]
     bidx = np.arange(inp["B"])[:, None]
     e_mu = np.abs(g["marginals"][bidx, rows] - gold["marginals_rows"]).max()
     e_gx = np.abs(g["grad_emissions"][bidx, rows] - gold["grad_rows"]).max()
     print(name, "logz rel %.2e trans %.2e dur %.2e mu %.2e gx %.2e" % (rel.max(), e_tr, e_du, e_mu, e_gx))
-    assert e_tr <= TOL_GRAD and e_du <= TOL_GRAD
+    assert x_tr <= 1.0 and x_du <= 1.0, (e_tr, x_tr, e_du, x_du)
     assert e_mu <= TOL_GRAD and e_gx <= TOL_GRAD
     np.testing.assert_allclose(g["marginals"].sum(axis=1), gold["colsum_marginals"],
                                atol=TOL_GRAD * inp["T"] / 100)
