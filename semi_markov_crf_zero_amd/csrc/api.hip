@@ -99,15 +99,23 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
     case SEMICRF_OP_SCAN:
       break;
     case SEMICRF_OP_LOGZ:
-      lay.logz = cv.take((size_t)B * 8);
-      break;
     case SEMICRF_OP_FWD_BWD: {
       const size_t nck = (size_t)B * sh->nchunk;
-      const size_t rows = (size_t)sh->delta + 1;
+      const size_t rec = nck * (size_t)(K + 3) * C * 8;
+      const bool bwd = op == SEMICRF_OP_FWD_BWD;
       lay.logz = cv.take((size_t)B * 8);
       lay.logz_bwd = cv.take((size_t)B * 8);
-      lay.ck_fwd = cv.take(nck * (size_t)(K + 3) * C * 8);
-      lay.ck_bwd = cv.take(nck * (size_t)(K + 3) * C * 8);
+      lay.ck_fwd = cv.take(rec);
+      lay.end_fwd = cv.take(rec);
+      lay.ck_bwd = bwd ? cv.take(rec) : 0;
+      lay.end_bwd = bwd ? cv.take(rec) : 0;
+      lay.redo = cv.take(2 * nck * 4);
+      lay.corr_i = cv.take(2 * nck * 8);
+      lay.corr_f = cv.take(2 * nck * 8);
+      lay.nbad = cv.take((size_t)sh->nchunk * 4);
+      lay.lz_part = cv.take((size_t)2 * B * 8);
+      if (!bwd) break;
+      const size_t rows = (size_t)sh->delta + 1;
       lay.scr_a = cv.take(nck * rows * C * 8);
       lay.scr_u = cv.take(nck * rows * C * 8);
       lay.scr_ea = cv.take(nck * rows * C * 4);
@@ -163,6 +171,20 @@ semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int
 template <typename P>
 P *at(void *ws, size_t off) {
   return reinterpret_cast<P *>(static_cast<unsigned char *>(ws) + off);
+}
+
+PitBufs pit_bufs(void *ws, const Layout &lay, bool bwd) {
+  PitBufs pb;
+  pb.ck_fwd = at<double>(ws, lay.ck_fwd);
+  pb.end_fwd = at<double>(ws, lay.end_fwd);
+  pb.ck_bwd = bwd ? at<double>(ws, lay.ck_bwd) : nullptr;
+  pb.end_bwd = bwd ? at<double>(ws, lay.end_bwd) : nullptr;
+  pb.redo = at<int>(ws, lay.redo);
+  pb.corr_i = at<long long>(ws, lay.corr_i);
+  pb.corr_f = at<double>(ws, lay.corr_f);
+  pb.nbad = at<int>(ws, lay.nbad);
+  pb.lz_part = at<double>(ws, lay.lz_part);
+  return pb;
 }
 
 // With SEMICRF_DEBUG set in the environment, name the HIP error on stderr.
@@ -240,8 +262,8 @@ semicrf_status_t semicrf_logz_fwd(const float *emissions, const int32_t *lengths
                              S, at<double>(workspace, lay.tile_sum),
                              at<double>(workspace, lay.anchor), lay.ntile, st);
   if (e != hipSuccess) return hip_status(e);
-  e = launch_sweep(sh, trans, dur, S, lengths, nullptr, nullptr, at<double>(workspace, lay.logz),
-                   nullptr, logz, 0, 0, st);
+  e = run_sweeps(sh, trans, dur, S, lengths, pit_bufs(workspace, lay, false),
+                 at<double>(workspace, lay.logz), nullptr, logz, 0, st);
   return hip_status(e);
 }
 
@@ -274,9 +296,8 @@ semicrf_status_t semicrf_fwd_bwd_timed(const float *emissions, const int32_t *le
                              st);
   if (e != hipSuccess) return hip_status(e);
   mark(1);
-  e = launch_sweep(sh, trans, dur, S, lengths, at<double>(ws, lay.ck_fwd),
-                   at<double>(ws, lay.ck_bwd), at<double>(ws, lay.logz),
-                   at<double>(ws, lay.logz_bwd), logz, 1, 1, st);
+  e = run_sweeps(sh, trans, dur, S, lengths, pit_bufs(ws, lay, true), at<double>(ws, lay.logz),
+                 at<double>(ws, lay.logz_bwd), logz, 1, st);
   if (e != hipSuccess) return hip_status(e);
   mark(2);
   e = launch_chunks(sh, trans, dur, S, lengths, at<double>(ws, lay.ck_fwd),

@@ -288,69 +288,84 @@ __device__ __forceinline__ double row_lse(double o, bool is_row, const ChainShap
 }
 
 // ---------------------------------------------------------------- sweeps
-// blockIdx.x < B: forward chain of sequence b; else backward chain.
+// One workgroup per (direction, sequence b, chunk j), chunk = [p0, p1): the
+// forward chain runs t = p0+1 .. p1 from the state at p0, the backward chain
+// t = p1-1 .. p0 from the state at p1 (parallel-in-time; pit.hip verifies and
+// normalises).  The start state is the chunk's checkpoint record: built at
+// iteration 0 (exact at the sequence end the chain starts from, neutral
+// elsewhere), re-read afterwards.  The chunk that ends its chain yields log Z
+// in its own frame; every other chunk writes its end state.
 template <int NT, int AMAX, int TRMAX, typename DT>
 __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__restrict__ trans,
                                               const float *__restrict__ dur,
                                               const double *__restrict__ S,
-                                              const int32_t *__restrict__ lengths,
-                                              double *__restrict__ ck_fwd,
-                                              double *__restrict__ ck_bwd,
-                                              double *__restrict__ logz_ws,
-                                              double *__restrict__ logz_bwd_ws,
-                                              float *__restrict__ logz_out, int write_ckpt) {
+                                              const int32_t *__restrict__ lengths, PitBufs pb,
+                                              int iter) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const bool fwd = (int)blockIdx.x < sh.B;
-  const int b = fwd ? blockIdx.x : blockIdx.x - sh.B;
+  const int nck = sh.B * sh.nchunk;
+  const bool fwd = (int)blockIdx.x < nck;
+  const int rem = fwd ? blockIdx.x : blockIdx.x - nck;
+  const int b = rem / sh.nchunk, jc = rem % sh.nchunk;
   const int L = lengths[b];
   const int tid = threadIdx.x, C = sh.C, K = sh.K;
   const bool is_row = tid < C;
-  if (L < 1 || L > sh.T) {
-    if (tid == 0) {
-      if (fwd) {
-        logz_ws[b] = __builtin_nan("");
-        logz_out[b] = __builtin_nanf("");
-      } else if (logz_bwd_ws) {
-        logz_bwd_ws[b] = __builtin_nan("");
-      }
-    }
-    return;
-  }
+  if (L < 1 || L > sh.T) return;
+  const int p0 = jc * sh.delta;
+  if (p0 >= L) return;
+  const int p1 = min(p0 + sh.delta, L);
+  const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + jc;
+  if (iter > 0 && (pb.nbad[iter - 1] == 0 || pb.redo[idx] == 0)) return;
   Smem sm = carve(lds, sh);
   Regs<AMAX, TRMAX, DT> r;
   init_regs(r, sh, dur);
   load_trans(r, sh, trans, fwd);
   const double *Sb = S + (size_t)b * (sh.T + 1) * C;
   const size_t cks = ck_stride(C, K);
-  double *ckb = (fwd ? ck_fwd : ck_bwd) + (size_t)b * sh.nchunk * cks;
+  double *rec_start = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
+  double *rec_end = (fwd ? pb.end_fwd : pb.end_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
   const double sigma = fwd ? 1.0 : -1.0;
+  const int isig = fwd ? 1 : -1;
+  const int tstart = fwd ? p0 : p1;
+  const bool tail = fwd ? (p1 == L) : (p0 == 0);  // this chunk ends the chain
 
-  for (int i = tid; i < K * C; i += NT) sm.ring[i] = 0.0;
-  __syncthreads();
-  // initial entry: forward position 0 (u = 0), backward position L (beta = 0)
-  const int tstart = fwd ? 0 : L;
   int R = 0;
-  if (is_row) {
-    double d = 0.0;  // entry minus R*ln2: u[0] - S[0] = 0 forward, beta[L] + S[L] backward
-    if (!fwd) {
-      const double sl = Sb[(size_t)L * C + tid];
-      R = (int)rint(sl * kLog2e);
-      d = sl - (double)R * kLn2;
+  double o = 0.0, m = 0.0;
+  if (iter == 0) {
+    for (int i = tid; i < K * C; i += NT) sm.ring[i] = 0.0;
+    __syncthreads();
+    const bool exact = fwd ? (jc == 0) : (p1 == L);
+    if (exact) {
+      // forward position 0 (u = 0), backward position L (beta = 0)
+      if (is_row) {
+        double d = 0.0;  // entry minus R*ln2
+        if (!fwd) {
+          const double sl = Sb[(size_t)L * C + tid];
+          R = (int)rint(sl * kLog2e);
+          d = sl - (double)R * kLn2;
+        }
+        sm.ring[(tstart % K) * C + tid] = exp(d);
+      }
+    } else {
+      // neutral start: every entry of the window (positions inside [0, L]) is 1
+      for (int i = tid; i < K * C; i += NT) {
+        const int dq = i / C, c = i % C;
+        const int q = tstart - isig * dq;
+        if (q >= 0 && q <= L) sm.ring[(q % K) * C + c] = 1.0;
+      }
     }
-    sm.refs[tid] = (double)R;
-    sm.ring[(tstart % K) * C + tid] = exp(d);
-  }
-  __syncthreads();
-  if (write_ckpt) {
-    // forward checkpoint 0 holds p0 = 0 (u[0] = 0); the backward checkpoint
-    // of the last chunk holds p1 = L (beta[L] = 0).  o is undefined there.
-    const int j = fwd ? 0 : (L - 1) / sh.delta;
-    save_ckpt(ckb + (size_t)j * cks, sm, sh, R, -__builtin_huge_val(), 0.0);
+    if (is_row) sm.refs[tid] = (double)R;
+    __syncthreads();
+    // o = NaN marks a neutral start (never accepted by the verification)
+    save_ckpt(rec_start, sm, sh, R, exact ? -__builtin_huge_val() : __builtin_nan(""),
+              exact ? 0.0 : __builtin_nan(""));
+    __syncthreads();
+  } else {
+    load_ckpt(rec_start, sm, sh, R, o, m);
   }
 
-  const int nsteps = L;  // forward t = 1..L, backward t = L-1..0
+  const int nsteps = p1 - p0;  // forward t = p0+1..p1, backward t = p1-1..p0
   for (int step = 1; step <= nsteps; ++step) {
-    const int t = fwd ? step : L - step;
+    const int t = fwd ? p0 + step : p1 - step;
     double nogd[AMAX];
     const double s = r.kp < sh.P ? ksum<false>(r, sm, sh, t, fwd, nogd, 0.0) : 0.0;
     if (r.kp < sh.P) sm.part[r.kp * C + r.kc] = s;
@@ -358,40 +373,28 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
     // the step runs relative to base*ln2, base = label 0's integer reference
     const int base = (int)sm.refs[0];
     const double bl = (double)base * kLn2;
-    double o = 0.0;  // alpha (forward) or v (backward) minus bl
+    o = 0.0;  // alpha (forward) or v (backward) minus bl
     if (is_row) {
       double sum = 0.0;
       for (int p = 0; p < sh.P; ++p) sum += sm.part[p * C + tid];
       o = sigma * Sb[(size_t)t * C + tid] + (double)(R - base) * kLn2 + log(sum);
     }
-    const bool last = fwd ? (t == L) : (t == 0);
-    if (last) {
+    const bool last = step == nsteps;
+    if (last && tail) {
       const double lz = bl + row_lse(o, is_row, sh, sm);
-      if (tid == 0) {
-        if (fwd) {
-          logz_ws[b] = lz;
-          logz_out[b] = (float)lz;
-        } else if (logz_bwd_ws) {
-          logz_bwd_ws[b] = lz;
-        }
-      }
+      if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
       break;
     }
     const double M = row_max(o, is_row, sh, sm);
     if (is_row) sm.erow[tid] = exp(o - M);
     __syncthreads();
-    const double m = contract(r, sm, sh, M);  // u (forward) or beta (backward) minus bl
+    m = contract(r, sm, sh, M);  // u (forward) or beta (backward) minus bl
     bool need = false;
     if (is_row)
       need = insert_entry(sm, sh, t,
                           (m - sigma * Sb[(size_t)t * C + tid]) + (double)(base - R) * kLn2, R);
     if (__syncthreads_or(need)) apply_rebase(r, sm, sh, t, fwd);
-    if (write_ckpt && (t % sh.delta) == 0) {
-      // forward: checkpoint j = t/delta holds position p0 = t;
-      // backward: checkpoint j = t/delta - 1 holds position p1 = t.
-      const int j = fwd ? t / sh.delta : t / sh.delta - 1;
-      save_ckpt(ckb + (size_t)j * cks, sm, sh, R, bl + o, bl + m);
-    }
+    if (last) save_ckpt(rec_end, sm, sh, R, bl + o, bl + m);
   }
 }
 
@@ -699,14 +702,12 @@ struct ChainKernels {
     }
   }
   static hipError_t sweep(const ChainShape &sh, const float *trans, const float *dur,
-                          const double *S, const int32_t *lengths, double *ck_fwd,
-                          double *ck_bwd, double *logz_ws, double *logz_bwd_ws,
-                          float *logz_out, int with_bwd, int write_ckpt, hipStream_t st) {
+                          const double *S, const int32_t *lengths, const PitBufs &pb,
+                          int with_bwd, int iter, hipStream_t st) {
     const size_t lds = chain_lds_bytes(sh.C, sh.K, sh.P, sh.QT);
     set_attrs();
-    hipLaunchKernelGGL((k_sweep<NT, AMAX, TRMAX, DT>), dim3(with_bwd ? 2 * sh.B : sh.B),
-                       dim3(NT), lds, st, sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws,
-                       logz_bwd_ws, logz_out, write_ckpt);
+    hipLaunchKernelGGL((k_sweep<NT, AMAX, TRMAX, DT>), dim3((with_bwd ? 2 : 1) * sh.B * sh.nchunk),
+                       dim3(NT), lds, st, sh, trans, dur, S, lengths, pb, iter);
     return report(hipGetLastError(), "k_sweep", sh, lds);
   }
   static hipError_t chunks(const ChainShape &sh, const float *trans, const float *dur,
@@ -749,14 +750,10 @@ struct ChainKernels {
   } while (0)
 
 hipError_t launch_sweep(const ChainShape &sh, const float *trans, const float *dur,
-                        const double *S, const int32_t *lengths, double *ck_fwd,
-                        double *ck_bwd, double *logz_ws, double *logz_bwd_ws, float *logz_out,
-                        int with_bwd, int write_ckpt, hipStream_t st) {
-  if (sh.win)
-    return launch_sweep_w(sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, logz_bwd_ws,
-                          logz_out, with_bwd, write_ckpt, st);
-  SEMICRF_CHAIN_DISPATCH(sh, sweep(sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws,
-                                   logz_bwd_ws, logz_out, with_bwd, write_ckpt, st));
+                        const double *S, const int32_t *lengths, const PitBufs &pb,
+                        int with_bwd, int iter, hipStream_t st) {
+  if (sh.win) return launch_sweep_w(sh, trans, dur, S, lengths, pb, with_bwd, iter, st);
+  SEMICRF_CHAIN_DISPATCH(sh, sweep(sh, trans, dur, S, lengths, pb, with_bwd, iter, st));
 }
 
 hipError_t launch_chunks(const ChainShape &sh, const float *trans, const float *dur,

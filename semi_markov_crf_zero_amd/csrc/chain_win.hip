@@ -317,70 +317,85 @@ __device__ __forceinline__ double ld_or(const double *p, bool ok) { return ok ? 
 }  // namespace
 
 // ------------------------------------------------------------------ sweeps
-// blockIdx.x < B: forward chain of sequence b (checkpoint j holds p0 = j*delta);
-// otherwise backward chain (checkpoint j holds p1 = min((j+1)*delta, L)).
+// One workgroup per (direction, sequence b, chunk j), chunk = [p0, p1): the
+// forward chain runs t = p0+1 .. p1 from the state at p0, the backward chain
+// t = p1-1 .. p0 from the state at p1 (parallel-in-time; pit.hip verifies and
+// normalises).  The start state is the chunk's checkpoint record: built at
+// iteration 0 (exact at the sequence end the chain starts from, neutral
+// elsewhere), re-read afterwards.  The chunk that ends its chain yields log Z
+// in its own frame; every other chunk writes its end state.
 // Per step: K-sum by every thread (one new ring value each), barrier, the
 // chain wave's serial part, barrier; plus the rare rebase mini-phase.
 template <int NT, int AMAX, int U, int CMAX>
 __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__restrict__ trans,
                                                 const float *__restrict__ dur,
                                                 const double *__restrict__ S,
-                                                const int32_t *__restrict__ lengths,
-                                                double *__restrict__ ck_fwd,
-                                                double *__restrict__ ck_bwd,
-                                                double *__restrict__ logz_ws,
-                                                double *__restrict__ logz_bwd_ws,
-                                                float *__restrict__ logz_out, int write_ckpt) {
+                                                const int32_t *__restrict__ lengths, PitBufs pb,
+                                                int iter) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const bool fwd = (int)blockIdx.x < sh.B;
-  const int b = fwd ? blockIdx.x : blockIdx.x - sh.B;
+  const int nck = sh.B * sh.nchunk;
+  const bool fwd = (int)blockIdx.x < nck;
+  const int rem = fwd ? blockIdx.x : blockIdx.x - nck;
+  const int b = rem / sh.nchunk, jc = rem % sh.nchunk;
   const int L = lengths[b];
   const int tid = threadIdx.x, C = sh.C, K = sh.K, T = sh.T;
   const int lane = tid & 63;
   const bool chain = tid < C;  // lanes of wave 0
   const bool wave0 = tid < 64;
-  if (L < 1 || L > T) {
-    if (tid == 0) {
-      if (fwd) {
-        logz_ws[b] = __builtin_nan("");
-        logz_out[b] = __builtin_nanf("");
-      } else if (logz_bwd_ws) {
-        logz_bwd_ws[b] = __builtin_nan("");
-      }
-    }
-    return;
-  }
+  if (L < 1 || L > T) return;
+  const int p0 = jc * sh.delta;
+  if (p0 >= L) return;
+  const int p1 = min(p0 + sh.delta, L);
+  const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + jc;
+  if (iter > 0 && (pb.nbad[iter - 1] == 0 || pb.redo[idx] == 0)) return;
   const WSmem sm = wcarve(lds, sh);
   Win<AMAX, U> win;
   win.init(sh, dur);
   stage_trans(sm, sh, trans, fwd, NT);
   const double *Sb = S + (size_t)b * (T + 1) * C;
   const size_t cks = ck_stride(C, K);
-  double *ckb = (fwd ? ck_fwd : ck_bwd) + (size_t)b * sh.nchunk * cks;
+  double *rec_start = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
+  double *rec_end = (fwd ? pb.end_fwd : pb.end_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
   const int sigma = fwd ? 1 : -1;
   const double sg = (double)sigma;
+  const int tstart = fwd ? p0 : p1;
+  const bool tail = fwd ? (p1 == L) : (p0 == 0);  // this chunk ends the chain
 
-  for (int i = tid; i < K * C; i += NT) sm.ring[i] = 0.0;
-  __syncthreads();
-  const int tstart = fwd ? 0 : L;
   int R = 0;  // integer log reference of label `lane` (units of ln2)
-  if (chain) {
-    double d = 0.0;  // entry minus R*ln2: u[0] - S[0] = 0 forward, beta[L] + S[L] backward
-    if (!fwd) {
-      const double sl = Sb[(size_t)L * C + lane];
-      R = (int)rint(sl * kLog2e);
-      d = sl - (double)R * kLn2;
+  if (iter == 0) {
+    for (int i = tid; i < K * C; i += NT) sm.ring[i] = 0.0;
+    __syncthreads();
+    const bool exact = fwd ? (jc == 0) : (p1 == L);
+    if (exact) {
+      if (chain) {
+        double d = 0.0;  // entry minus R*ln2: u[0] - S[0] = 0 forward, beta[L] + S[L] backward
+        if (!fwd) {
+          const double sl = Sb[(size_t)L * C + lane];
+          R = (int)rint(sl * kLog2e);
+          d = sl - (double)R * kLn2;
+        }
+        sm.ring[pos_slot(tstart, K) * C + lane] = exp(d);
+      }
+    } else {
+      // neutral start: every entry of the window (positions inside [0, L]) is 1
+      for (int i = tid; i < K * C; i += NT) {
+        const int dq = i / C, c = i % C;
+        const int q = tstart - sigma * dq;
+        if (q >= 0 && q <= L) sm.ring[pos_slot(q, K) * C + c] = 1.0;
+      }
     }
-    sm.ring[pos_slot(tstart, K) * C + lane] = exp(d);
+    __syncthreads();
+    // o = NaN marks a neutral start (never accepted by the verification)
+    wsave(rec_start, sm, sh, chain, lane, R,
+          exact ? -__builtin_huge_val() : __builtin_nan(""), exact ? 0.0 : __builtin_nan(""), NT);
+  } else {
+    double o0, m0;
+    wload(rec_start, sm, sh, chain, lane, R, o0, m0, NT);
   }
   __syncthreads();
-  if (write_ckpt)
-    wsave(ckb + (size_t)(fwd ? 0 : (L - 1) / sh.delta) * cks, sm, sh, chain, lane, R,
-          -__builtin_huge_val(), 0.0, NT);
 
-  // steps: forward t = 1..L, backward t = L-1..0; the last one only yields o
-  const int first = fwd ? 1 : L - 1;
-  const int nsteps = L;
+  const int first = fwd ? p0 + 1 : p1 - 1;
+  const int nsteps = p1 - p0;
   double Sq[U];
 #pragma unroll
   for (int i = 0; i < U; ++i) {
@@ -401,6 +416,7 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
         win.publish(sm, sh, ks);
         __syncthreads();
         const bool last = step == nsteps - 1;
+        const bool lz_step = last && tail;
         double o = 0.0, m = 0.0;  // relative to bl
         double bl = 0.0;
         if (wave0) {
@@ -408,18 +424,11 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
           const int base = chain_base(R);
           bl = (double)base * kLn2;
           o = chain ? sg * st + (double)(R - base) * kLn2 + log(chain_sum<NT>(sm, sh, lane)) : 0.0;
-          if (last) {
+          if (lz_step) {
             const float M = wave_max(chain ? (float)o : -__builtin_huge_valf());
             const double ex = chain ? exp(o - (double)M) : 0.0;
             const double lz = bl + ((double)M + log(wave_sum(ex)));
-            if (tid == 0) {
-              if (fwd) {
-                logz_ws[b] = lz;
-                logz_out[b] = (float)lz;
-              } else if (logz_bwd_ws) {
-                logz_bwd_ws[b] = lz;
-              }
-            }
+            if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
           } else {
             double e, M;
             m = chain_contract<CMAX>(sm, sh, lane, o, e, M);
@@ -433,18 +442,16 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
             Sq[i] = ld_or(Sb + (size_t)tp * C + lane, tp >= 0 && tp <= T);
           }
         }
-        if (last) {
-          done = true;
-        } else {
+        if (!lz_step) {
           __syncthreads();
           if (sm.flag[t & 1]) {
             win.rebase(sm, sh, t, sigma);
             __syncthreads();
           }
-          if (write_ckpt && (t % sh.delta) == 0) {
-            const int j = fwd ? t / sh.delta : t / sh.delta - 1;
-            wsave(ckb + (size_t)j * cks, sm, sh, chain, lane, R, bl + o, bl + m, NT);
-          }
+        }
+        if (last) {
+          done = true;
+          if (!lz_step) wsave(rec_end, sm, sh, chain, lane, R, bl + o, bl + m, NT);
         }
       }
     }
@@ -732,14 +739,12 @@ struct WinKernels {
     }
   }
   static hipError_t sweep(const ChainShape &sh, const float *trans, const float *dur,
-                          const double *S, const int32_t *lengths, double *ck_fwd,
-                          double *ck_bwd, double *logz_ws, double *logz_bwd_ws,
-                          float *logz_out, int with_bwd, int write_ckpt, hipStream_t st) {
+                          const double *S, const int32_t *lengths, const PitBufs &pb,
+                          int with_bwd, int iter, hipStream_t st) {
     attrs();
     const size_t lds = win_lds_bytes(sh.C, sh.K, sh.P);
-    hipLaunchKernelGGL((k_sweep_w<NT, AMAX, U, CMAX>), dim3(with_bwd ? 2 * sh.B : sh.B),
-                       dim3(NT), lds, st, sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws,
-                       logz_bwd_ws, logz_out, write_ckpt);
+    hipLaunchKernelGGL((k_sweep_w<NT, AMAX, U, CMAX>), dim3((with_bwd ? 2 : 1) * sh.B * sh.nchunk),
+                       dim3(NT), lds, st, sh, trans, dur, S, lengths, pb, iter);
     return wreport(hipGetLastError(), "k_sweep_w", sh, lds);
   }
   static hipError_t chunks(const ChainShape &sh, const float *trans, const float *dur,
@@ -779,12 +784,10 @@ static hipError_t win_dispatch(const ChainShape &sh, F &&f) {
 }
 
 hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float *dur,
-                          const double *S, const int32_t *lengths, double *ck_fwd,
-                          double *ck_bwd, double *logz_ws, double *logz_bwd_ws, float *logz_out,
-                          int with_bwd, int write_ckpt, hipStream_t st) {
+                          const double *S, const int32_t *lengths, const PitBufs &pb,
+                          int with_bwd, int iter, hipStream_t st) {
   return win_dispatch(sh, [&](auto k) {
-    return decltype(k)::sweep(sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, logz_bwd_ws,
-                              logz_out, with_bwd, write_ckpt, st);
+    return decltype(k)::sweep(sh, trans, dur, S, lengths, pb, with_bwd, iter, st);
   });
 }
 

@@ -107,11 +107,24 @@ __host__ __device__ inline size_t win_lds_bytes(int C, int K, int P) {
 // Workspace layout (byte offsets, 256-aligned).
 struct Layout {
   size_t S, nu, tile_sum, anchor, logz, logz_bwd;
-  size_t ck_fwd, ck_bwd, scr_a, scr_u, scr_ea, scr_ev;
+  size_t ck_fwd, ck_bwd, end_fwd, end_bwd, redo, corr_i, corr_f, nbad, lz_part;
+  size_t scr_a, scr_u, scr_ea, scr_ev;
   size_t part_x, part_gd, part_tot, part_ssum, carry, mean;
   size_t bp, vbest, vcbest;
   size_t total;
   int ntile;
+};
+
+// Buffers of the parallel-in-time sweeps (pit.hip).  Records have the
+// checkpoint layout [K*C ring][C integer refs][C o][C m] (float64).
+struct PitBufs {
+  double *ck_fwd, *ck_bwd;    // chunk start records = checkpoint records [B][nchunk]
+  double *end_fwd, *end_bwd;  // chunk end records [B][nchunk]
+  int *redo;                  // [2][B][nchunk]: sweep the chunk in the next iteration
+  long long *corr_i;          // [2][B][nchunk]: log2 scalar to the predecessor, integer part
+  double *corr_f;             // [2][B][nchunk]: its fraction
+  int *nbad;                  // [nchunk]: start states replaced by each verification
+  double *lz_part;            // [2][B]: log Z in the frame of the chain's last chunk
 };
 
 // ---- launchers (defined in scan.hip / chain.hip / viterbi.hip) ----------
@@ -120,10 +133,24 @@ hipError_t launch_scan(const float *x, const int32_t *lengths, int B, int T, int
                        double *nu, double *S, double *tile_sum, double *anchor, int ntile,
                        hipStream_t st);
 
+// One iteration of the chunk-parallel sweeps (every chunk of every sequence,
+// both directions when with_bwd); iteration 0 builds the start states.
 hipError_t launch_sweep(const ChainShape &sh, const float *trans, const float *dur,
-                        const double *S, const int32_t *lengths, double *ck_fwd,
-                        double *ck_bwd, double *logz_ws, double *logz_bwd_ws, float *logz_out,
-                        int with_bwd, int write_ckpt, hipStream_t st);
+                        const double *S, const int32_t *lengths, const PitBufs &pb,
+                        int with_bwd, int iter, hipStream_t st);
+
+// The whole parallel-in-time sweep: init, nchunk x (sweep, verify), fix-up.
+hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur,
+                      const double *S, const int32_t *lengths, const PitBufs &pb,
+                      double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
+                      hipStream_t st);
+
+hipError_t launch_pit_init(const ChainShape &sh, const PitBufs &pb, int niter, hipStream_t st);
+hipError_t launch_pit_verify(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
+                             int iter, int with_bwd, hipStream_t st);
+hipError_t launch_pit_fixup(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
+                            double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
+                            hipStream_t st);
 
 hipError_t launch_chunks(const ChainShape &sh, const float *trans, const float *dur,
                          const double *S, const int32_t *lengths, const double *ck_fwd,
@@ -134,9 +161,8 @@ hipError_t launch_chunks(const ChainShape &sh, const float *trans, const float *
 
 // windowed engine for C <= 32 (chain_win.hip); same arguments and outputs
 hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float *dur,
-                          const double *S, const int32_t *lengths, double *ck_fwd,
-                          double *ck_bwd, double *logz_ws, double *logz_bwd_ws, float *logz_out,
-                          int with_bwd, int write_ckpt, hipStream_t st);
+                          const double *S, const int32_t *lengths, const PitBufs &pb,
+                          int with_bwd, int iter, hipStream_t st);
 
 hipError_t launch_chunks_w(const ChainShape &sh, const float *trans, const float *dur,
                            const double *S, const int32_t *lengths, const double *ck_fwd,

@@ -1,0 +1,270 @@
+// pit.hip -- parallel-in-time sweeps: verification and normaliser fix-up.
+//
+// The streamed forward (and backward) state at a checkpoint boundary is the
+// ring of the K newest entries of every label, in exp space relative to an
+// integer log reference per label (the record layout of chain.hip /
+// chain_win.hip: [K*C ring][C refs][C o][C m], float64).  The recursion is
+// linear in that state, and it forgets where it started: run from two start
+// states that differ, the states it reaches agree in direction (up to one
+// scalar) after enough positions.  So every checkpoint interval ("chunk") is
+// swept concurrently:
+//   iteration 0: the chunk at the sequence end a direction starts from (the
+//     first chunk forward, the last backward) starts from its exact state,
+//     every other chunk from a neutral state;
+//   after each iteration, k_pit_verify compares each chunk's start with the
+//     end state its predecessor produced.  Equal in direction: the chunk is
+//     consistent, and the scalar between the two (log2 units, kept as an
+//     exact integer plus a fraction) is recorded.  Different: the
+//     predecessor's end becomes the chunk's new start and the chunk is swept
+//     again in the next iteration;
+//   the iterations stop once one verification finds no difference.  After
+//     n iterations the first n chunks have exact starts, so nchunk
+//     iterations always suffice; every kernel of an iteration after
+//     convergence returns at once;
+//   k_pit_fixup adds the prefix sums of the recorded scalars to the
+//     checkpoint records and to log Z, which makes every record the exact
+//     state with its exact log normaliser -- the checkpoint-boundary
+//     normalisation of "Streaming Structured Inference with Flash-SemiCRF"
+//     (abstract; technical summary, section 2.C) computed chunk-parallel.
+#include "device_math.h"
+#include "internal.h"
+
+namespace semicrf {
+
+namespace {
+
+constexpr int kPitThreads = 256;
+constexpr double kPitTol = 1e-12;  // direction mismatch accepted, relative to the largest entry
+
+struct MaxArg {
+  double v;
+  int i;
+};
+
+__device__ __forceinline__ MaxArg max_arg(MaxArg a, MaxArg b) {
+  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+  return a;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kPitThreads) void k_pit_init(ChainShape sh, PitBufs pb, int niter) {
+  const int n = 2 * sh.B * sh.nchunk;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    pb.redo[i] = 1;
+    pb.corr_i[i] = 0;
+    pb.corr_f[i] = 0.0;
+  }
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < niter; i += gridDim.x * blockDim.x)
+    pb.nbad[i] = 0;
+}
+
+// One workgroup per (direction, sequence, chunk).  Forward chunk j >= 1
+// compares its start (state at p0_j) with the end of forward chunk j-1;
+// backward chunk j compares its start (state at p1_j) with the end of
+// backward chunk j+1.
+__global__ __launch_bounds__(kPitThreads) void k_pit_verify(ChainShape sh,
+                                                            const int32_t *__restrict__ lengths,
+                                                            PitBufs pb, int iter) {
+  if (iter > 0 && pb.nbad[iter - 1] == 0) return;
+  __shared__ MaxArg red[kPitThreads / 64];
+  __shared__ double redd[kPitThreads / 64];
+  const int nck = sh.B * sh.nchunk;
+  const bool fwd = (int)blockIdx.x < nck;
+  const int rem = fwd ? blockIdx.x : blockIdx.x - nck;
+  const int b = rem / sh.nchunk, j = rem % sh.nchunk;
+  const int L = lengths[b];
+  if (L < 1 || L > sh.T) return;
+  const int nvalid = (L + sh.delta - 1) / sh.delta;
+  int jp;  // chunk whose end must equal this chunk's start
+  if (fwd) {
+    if (j == 0 || j >= nvalid) return;
+    jp = j - 1;
+  } else {
+    if (j + 1 >= nvalid) return;
+    jp = j + 1;
+  }
+  const int C = sh.C, K = sh.K;
+  const size_t cks = ck_stride(C, K);
+  double *A = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + j) * cks;
+  const double *E = (fwd ? pb.end_fwd : pb.end_bwd) + ((size_t)b * sh.nchunk + jp) * cks;
+  const double *RA = A + (size_t)K * C, *RE = E + (size_t)K * C;
+  const int n = K * C;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const long long re0 = (long long)RE[0];
+
+  // largest entry of E in log2, relative to E's label-0 reference
+  MaxArg best = {-__builtin_huge_val(), 0x7fffffff};
+  for (int i = tid; i < n; i += kPitThreads) {
+    const double e = E[i];
+    if (e > 0.0) {
+      const double le = (double)((long long)RE[i % C] - re0) + log2(e);
+      best = max_arg(best, MaxArg{le, i});
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    MaxArg o;
+    o.v = __shfl_xor(best.v, off);
+    o.i = __shfl_xor(best.i, off);
+    best = max_arg(best, o);
+  }
+  if (lane == 0) red[w] = best;
+  __syncthreads();
+  best = red[0];
+  for (int q = 1; q < kPitThreads / 64; ++q) best = max_arg(best, red[q]);
+  const bool neutral = A[(size_t)K * C + C] != A[(size_t)K * C + C];  // o is NaN on a neutral start
+  bool ok = best.i != 0x7fffffff && !neutral && A[best.i] > 0.0;
+  long long di = 0;
+  double df = 0.0;
+  double mism = 0.0;
+  if (ok) {
+    // scalar between the states: A ~ 2^delta E, delta = di + df
+    const int cs = best.i % C;
+    const double l = log2(A[best.i]) - log2(E[best.i]);
+    const double fl = floor(l);
+    di = (long long)RA[cs] - (long long)RE[cs] + (long long)fl;
+    df = l - fl;
+    for (int i = tid; i < n; i += kPitThreads) {
+      const double a = A[i], e = E[i];
+      if (a == 0.0 && e == 0.0) continue;
+      const int c = i % C;
+      const double we =
+          e > 0.0 ? exp2((double)((long long)RE[c] - re0) + log2(e) - best.v) : 0.0;
+      const double wa =
+          a > 0.0 ? exp2((double)((long long)RA[c] - re0 - di) + (log2(a) - df) - best.v) : 0.0;
+      mism = fmax(mism, fabs(wa - we));
+    }
+    for (int off = 32; off > 0; off >>= 1) mism = fmax(mism, __shfl_xor(mism, off));
+    __syncthreads();
+    if (lane == 0) redd[w] = mism;
+    __syncthreads();
+    mism = redd[0];
+    for (int q = 1; q < kPitThreads / 64; ++q) mism = fmax(mism, redd[q]);
+    ok = mism <= kPitTol;
+  }
+  const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + j;
+  __syncthreads();  // every read of A above precedes the copy below
+  if (ok) {
+    if (tid == 0) {
+      pb.corr_i[idx] = di;
+      pb.corr_f[idx] = df;
+      pb.redo[idx] = 0;
+    }
+  } else {
+    for (size_t i = tid; i < cks; i += kPitThreads) A[i] = E[i];
+    if (tid == 0) {
+      pb.redo[idx] = 1;
+      atomicAdd(&pb.nbad[iter], 1);
+    }
+  }
+}
+
+// One workgroup per (direction, sequence): prefix sums of the recorded
+// scalars along the direction of the chain, applied to every checkpoint
+// record (integer part to the references, fraction to the ring, both to the
+// absolute o / m rows) and to the chain's log Z.
+__global__ __launch_bounds__(kPitThreads) void k_pit_fixup(ChainShape sh,
+                                                           const int32_t *__restrict__ lengths,
+                                                           PitBufs pb, double *logz_ws,
+                                                           double *logz_bwd_ws, float *logz_out,
+                                                           int with_bwd) {
+  const bool fwd = (int)blockIdx.x < sh.B;
+  const int b = fwd ? blockIdx.x : blockIdx.x - sh.B;
+  if (!fwd && !with_bwd) return;
+  const int L = lengths[b];
+  const int C = sh.C, K = sh.K, tid = threadIdx.x;
+  if (L < 1 || L > sh.T) {
+    if (tid == 0) {
+      if (fwd) {
+        logz_ws[b] = __builtin_nan("");
+        logz_out[b] = __builtin_nanf("");
+      } else if (logz_bwd_ws) {
+        logz_bwd_ws[b] = __builtin_nan("");
+      }
+    }
+    return;
+  }
+  const int nvalid = (L + sh.delta - 1) / sh.delta;
+  const size_t cks = ck_stride(C, K);
+  const size_t base = (fwd ? 0 : (size_t)sh.B * sh.nchunk) + (size_t)b * sh.nchunk;
+  double *rec0 = (fwd ? pb.ck_fwd : pb.ck_bwd) + (size_t)b * sh.nchunk * cks;
+  long long oi = 0;  // accumulated offset of the current chunk, log2 units
+  double of = 0.0;
+  for (int s = 1; s < nvalid; ++s) {
+    const int j = fwd ? s : nvalid - 1 - s;
+    oi += pb.corr_i[base + j];
+    of += pb.corr_f[base + j];
+    const double fo = floor(of);
+    oi += (long long)fo;
+    of -= fo;
+    // correction = -(oi + of) = ni + nf, nf in [0, 1)
+    long long ni = -oi;
+    double nf = -of;
+    if (nf < 0.0) {
+      nf += 1.0;
+      ni -= 1;
+    }
+    double *rec = rec0 + (size_t)j * cks;
+    const double scale = exp2(nf);
+    const double shift = ((double)ni + nf) * kLn2;
+    for (int i = tid; i < K * C; i += kPitThreads) rec[i] *= scale;
+    for (int c = tid; c < C; c += kPitThreads) {
+      rec[(size_t)K * C + c] = (double)((long long)rec[(size_t)K * C + c] + ni);
+      rec[(size_t)K * C + C + c] += shift;
+      rec[(size_t)K * C + 2 * C + c] += shift;
+    }
+  }
+  if (tid == 0) {
+    // the chain's log Z was computed in the frame of its last chunk
+    const double lz = pb.lz_part[fwd ? b : sh.B + b] - ((double)oi + of) * kLn2;
+    if (fwd) {
+      logz_ws[b] = lz;
+      logz_out[b] = (float)lz;
+    } else if (logz_bwd_ws) {
+      logz_bwd_ws[b] = lz;
+    }
+  }
+}
+
+// nchunk iterations always suffice (after n of them the first n chunks of
+// every chain have exact starts); the ones after convergence return at once.
+hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur,
+                      const double *S, const int32_t *lengths, const PitBufs &pb,
+                      double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
+                      hipStream_t st) {
+  const int niter = sh.nchunk;
+  hipError_t e = launch_pit_init(sh, pb, niter, st);
+  if (e != hipSuccess) return e;
+  for (int it = 0; it < niter; ++it) {
+    e = launch_sweep(sh, trans, dur, S, lengths, pb, with_bwd, it, st);
+    if (e != hipSuccess) return e;
+    e = launch_pit_verify(sh, lengths, pb, it, with_bwd, st);
+    if (e != hipSuccess) return e;
+  }
+  return launch_pit_fixup(sh, lengths, pb, logz_ws, logz_bwd_ws, logz_out, with_bwd, st);
+}
+
+hipError_t launch_pit_init(const ChainShape &sh, const PitBufs &pb, int niter, hipStream_t st) {
+  const int n = 2 * sh.B * sh.nchunk;
+  const int grid = (n + kPitThreads - 1) / kPitThreads;
+  hipLaunchKernelGGL(k_pit_init, dim3(grid > 0 ? grid : 1), dim3(kPitThreads), 0, st, sh, pb,
+                     niter);
+  return hipGetLastError();
+}
+
+hipError_t launch_pit_verify(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
+                             int iter, int with_bwd, hipStream_t st) {
+  const int grid = (with_bwd ? 2 : 1) * sh.B * sh.nchunk;
+  hipLaunchKernelGGL(k_pit_verify, dim3(grid), dim3(kPitThreads), 0, st, sh, lengths, pb, iter);
+  return hipGetLastError();
+}
+
+hipError_t launch_pit_fixup(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
+                            double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_pit_fixup, dim3(2 * sh.B), dim3(kPitThreads), 0, st, sh, lengths, pb,
+                     logz_ws, logz_bwd_ws, logz_out, with_bwd);
+  return hipGetLastError();
+}
+
+}  // namespace semicrf
