@@ -9,15 +9,14 @@ default workload is the NLP-scale configuration (B=32, T=512, C=24, K=32).
 
 Prints ONE JSON line on stdout:
   value      = B*T*K*C segment cells per second (whole job, 1 GPU)
-  roofline   = the dominant kernel -- the chunk-parallel marginal pass
-               (k_chunk_w for C <= 32, k_chunk otherwise), one launch per
-               step -- as algorithmic float64 FMA work per launch divided by
-               its average duration (HIP events the library records on the
-               launch stream around that launch during the timed steps),
-               against the MI355X float64 vector peak (78.6 TFLOP/s);
-               `traffic` is its HBM bytes per launch from rocprofv3 counters
-               stored under profiles/ (null when absent or when the kernel
-               sources changed since)
+  roofline   = the dominant kernel -- the parallel-in-time sweep (k_sweep_w
+               for C <= 32, k_sweep otherwise; one launch per iteration) --
+               as its algorithmic float64 FMA work divided by its time (HIP
+               events the library records on the launch stream around the
+               sweep phase during the timed steps), against the MI355X
+               float64 vector peak (78.6 TFLOP/s); `traffic` is its HBM bytes
+               per step from rocprofv3 counters stored under profiles/ (null
+               when absent or when the kernel sources changed since)
   cpu_baseline = the float64 oracle timed on this host on the same workload
 Diagnostics go to stderr.  --copy-calibration MB runs one device copy of MB
 megabytes after the timed steps (outside them), the reference kernel for
@@ -60,17 +59,17 @@ def positions_and_kterms(lengths, K):
 
 
 def algorithmic_flops(lengths, C, K):
-    """Float64 flops the method itself needs, per kernel (FMA = 2 flops):
-    k_sweep  forward K-term sums (2 per segment cell) + forward contraction
-             (2 C^2 per position); its backward chain only produces
-             checkpoints and is overhead of the chunk-parallel design;
-    k_chunk  backward K-term sums + duration posteriors (4 per segment cell)
-             + backward contraction + transition posteriors (4 C^2 per
-             position); its forward recompute is overhead."""
+    """Float64 flops the method itself needs per step (FMA = 2 flops):
+    sweeps      forward and backward K-term sums (2 + 2 per segment cell) and
+                the forward and backward C x C contractions (2 C^2 + 2 C^2 per
+                position); the repeated parallel-in-time iterations and the
+                verification are overhead of the design and not counted;
+    posteriors  the duration posteriors (2 per segment cell) and the
+                transition-posterior GEMM (2 C^2 per position)."""
     npos, kterms = positions_and_kterms(lengths, K)
     return {
-        "k_sweep": 2.0 * kterms * C + 2.0 * C * C * npos,
-        "k_chunk": 4.0 * kterms * C + 4.0 * C * C * npos,
+        "sweeps": 4.0 * kterms * C + 4.0 * C * C * npos,
+        "posteriors": 2.0 * kterms * C + 2.0 * C * C * npos,
     }
 
 
@@ -190,16 +189,21 @@ def main():
         del src, dst
 
     flops = algorithmic_flops(inp["lengths"], C, K)
-    # the marginal pass is one launch per step; the sweep phase is several
-    # (one per parallel-in-time iteration plus verification kernels)
-    dom = "k_chunk_w" if C <= 32 else "k_chunk"
-    launch_ms = float(phase_ms[2])
-    achieved = flops["k_chunk"] / (launch_ms * 1e-3) / 1e12
+    # The dominant kernel is the sweep: one launch per parallel-in-time
+    # iteration (at most one per checkpoint interval; those after convergence
+    # return at once), so per launch the algorithmic work is the step's sweep
+    # work over the launch count, and the average launch time is the phase
+    # time over the same count -- the ratio is the phase rate.  The phase also
+    # holds the small verification / fix-up kernels, so this is a lower bound.
+    dom = "k_sweep_w" if C <= 32 else "k_sweep"
+    nchunk = -(-T // ckpt)
+    phase = float(phase_ms[1])
+    achieved = flops["sweeps"] / (phase * 1e-3) / 1e12
     roofline = {"bound": "alu", "kernel": dom, "achieved": achieved, "peak": FP64_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / FP64_PEAK_TFLOPS,
                 "traffic": stored_traffic(dom, args.workload),
-                "launch_ms": launch_ms,
-                "algorithmic_flops_per_launch": flops["k_chunk"]}
+                "launches_per_step": nchunk, "phase_ms": phase,
+                "algorithmic_flops_per_step": flops["sweeps"]}
     out = {
         "metric": METRIC, "value": value, "unit": "segment-cells/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,

@@ -130,10 +130,13 @@ semicrf_status_t semicrf_fwd_bwd(const float *emissions, const int32_t *lengths,
 /* semicrf_fwd_bwd with phase timing: `phase_events` (may be NULL) points to
  * SEMICRF_FWD_BWD_PHASES + 1 hipEvent_t handles created by the caller; event
  * i is recorded on `stream` when phase i is enqueued and the last one after
- * the final phase.  Phases: 0 cumulative scores (3 kernels), 1 forward and
- * backward sweeps (k_sweep, one launch), 2 chunk-parallel recompute and
- * posteriors (k_chunk, one launch), 3 reductions (3 kernels).  Everything
- * else is identical to semicrf_fwd_bwd. */
+ * the final phase.  Phases: 0 cumulative scores (3 kernels); 1 the
+ * parallel-in-time forward and backward sweeps (one sweep launch per
+ * iteration, at most one iteration per checkpoint interval, with their
+ * verification, normaliser fix-up and row correction); 2 the posteriors
+ * (coverage scan, transition and duration sums: 5 kernels); 3 the
+ * parameter-gradient reduction (1 kernel).  Everything else is identical to
+ * semicrf_fwd_bwd. */
 enum { SEMICRF_FWD_BWD_PHASES = 4 };
 semicrf_status_t semicrf_fwd_bwd_timed(const float *emissions, const int32_t *lengths,
                                        const float *trans, const float *dur,

@@ -33,7 +33,7 @@ EXPORTS = (
     "semicrf_cumulative_scores", "semicrf_logz_fwd", "semicrf_fwd_bwd", "semicrf_fwd_bwd_timed",
     "semicrf_viterbi",
 )
-FWD_BWD_PHASES = ("cumulative_scores", "k_sweep", "k_chunk", "reductions")
+FWD_BWD_PHASES = ("cumulative_scores", "sweeps", "posteriors", "reductions")
 
 
 class SemiCRFError(RuntimeError):

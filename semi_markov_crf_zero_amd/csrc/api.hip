@@ -114,18 +114,20 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
       lay.corr_f = cv.take(2 * nck * 8);
       lay.nbad = cv.take((size_t)sh->nchunk * 4);
       lay.lz_part = cv.take((size_t)2 * B * 8);
+      lay.shift = cv.take(2 * nck * 8);
       if (!bwd) break;
-      const size_t rows = (size_t)sh->delta + 1;
-      lay.scr_a = cv.take(nck * rows * C * 8);
-      lay.scr_u = cv.take(nck * rows * C * 8);
-      lay.scr_ea = cv.take(nck * rows * C * 4);
-      lay.scr_ev = cv.take(nck * rows * C * 4);
-      lay.part_x = cv.take(nck * (size_t)C * C * 8);
-      lay.part_gd = cv.take(nck * (size_t)K * C * 8);
-      lay.part_tot = cv.take(nck * C * 8);
-      lay.part_ssum = cv.take(nck * C * 8);
-      lay.carry = cv.take(nck * C * 8);
-      lay.mean = cv.take((size_t)B * C * 8);
+      lay.row_a = cv.take(nS * 8);
+      lay.row_u = cv.take(nS * 8);
+      lay.row_v = cv.take(nS * 8);
+      lay.row_b = cv.take(nS * 8);
+      PostGeom g;
+      post_geometry(*sh, g);
+      lay.cov_part = cv.take((size_t)B * g.cov_ntile * C * 8);
+      lay.cov_part2 = cv.take((size_t)B * g.cov_ntile * C * 8);
+      lay.cov_anchor = cv.take((size_t)B * g.cov_ntile * C * 8);
+      lay.cov_mean = cv.take((size_t)B * C * 8);
+      lay.tx_part = cv.take((size_t)B * g.tx_nseg * C * C * 8);
+      lay.dur_part = cv.take((size_t)B * g.dur_nspan * K * C * 8);
       break;
     }
     case SEMICRF_OP_VITERBI:
@@ -184,6 +186,11 @@ PitBufs pit_bufs(void *ws, const Layout &lay, bool bwd) {
   pb.corr_f = at<double>(ws, lay.corr_f);
   pb.nbad = at<int>(ws, lay.nbad);
   pb.lz_part = at<double>(ws, lay.lz_part);
+  pb.shift = at<double>(ws, lay.shift);
+  pb.row_a = bwd ? at<double>(ws, lay.row_a) : nullptr;
+  pb.row_u = bwd ? at<double>(ws, lay.row_u) : nullptr;
+  pb.row_v = bwd ? at<double>(ws, lay.row_v) : nullptr;
+  pb.row_b = bwd ? at<double>(ws, lay.row_b) : nullptr;
   return pb;
 }
 
@@ -300,19 +307,31 @@ semicrf_status_t semicrf_fwd_bwd_timed(const float *emissions, const int32_t *le
                  at<double>(ws, lay.logz_bwd), logz, 1, st);
   if (e != hipSuccess) return hip_status(e);
   mark(2);
-  e = launch_chunks(sh, trans, dur, S, lengths, at<double>(ws, lay.ck_fwd),
-                    at<double>(ws, lay.ck_bwd), at<double>(ws, lay.logz),
-                    at<double>(ws, lay.scr_a), at<double>(ws, lay.scr_u),
-                    at<float>(ws, lay.scr_ea), at<float>(ws, lay.scr_ev),
-                    at<double>(ws, lay.part_x), at<double>(ws, lay.part_gd),
-                    at<double>(ws, lay.part_tot), at<double>(ws, lay.part_ssum), grad_emissions,
-                    st);
+  PostArgs pa;
+  pa.lengths = lengths;
+  pa.trans = trans;
+  pa.dur = dur;
+  pa.grad_logz = grad_logz;
+  pa.S = S;
+  pa.logz = at<double>(ws, lay.logz);
+  pa.row_a = at<double>(ws, lay.row_a);
+  pa.row_u = at<double>(ws, lay.row_u);
+  pa.row_v = at<double>(ws, lay.row_v);
+  pa.row_b = at<double>(ws, lay.row_b);
+  pa.cov_part = at<double>(ws, lay.cov_part);
+  pa.cov_part2 = at<double>(ws, lay.cov_part2);
+  pa.cov_anchor = at<double>(ws, lay.cov_anchor);
+  pa.cov_mean = at<double>(ws, lay.cov_mean);
+  pa.tx_part = at<double>(ws, lay.tx_part);
+  pa.dur_part = at<double>(ws, lay.dur_part);
+  pa.grad_emissions = grad_emissions;
+  pa.marginals = marginals;
+  pa.grad_trans = grad_trans;
+  pa.grad_dur = grad_dur;
+  e = launch_posteriors(sh, pa, st);
   if (e != hipSuccess) return hip_status(e);
   mark(3);
-  e = launch_finish(sh, trans, lengths, grad_logz, at<double>(ws, lay.part_x),
-                    at<double>(ws, lay.part_gd), at<double>(ws, lay.part_tot),
-                    at<double>(ws, lay.part_ssum), at<double>(ws, lay.carry),
-                    at<double>(ws, lay.mean), grad_trans, grad_dur, grad_emissions, marginals, st);
+  e = launch_post_reduce(sh, pa, st);
   if (e != hipSuccess) return hip_status(e);
   mark(SEMICRF_FWD_BWD_PHASES);
   return SEMICRF_OK;

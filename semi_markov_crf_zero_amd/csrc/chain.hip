@@ -358,6 +358,8 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
     // o = NaN marks a neutral start (never accepted by the verification)
     save_ckpt(rec_start, sm, sh, R, exact ? -__builtin_huge_val() : __builtin_nan(""),
               exact ? 0.0 : __builtin_nan(""));
+    if (exact && is_row && pb.row_a)  // u[0] = 0 forward, beta[L] = 0 backward
+      (fwd ? pb.row_u : pb.row_b)[((size_t)b * (sh.T + 1) + tstart) * C + tid] = 0.0;
     __syncthreads();
   } else {
     load_ckpt(rec_start, sm, sh, R, o, m);
@@ -380,6 +382,8 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
       o = sigma * Sb[(size_t)t * C + tid] + (double)(R - base) * kLn2 + log(sum);
     }
     const bool last = step == nsteps;
+    if (is_row && pb.row_a)  // per-position rows, in this chunk's frame
+      (fwd ? pb.row_a : pb.row_v)[((size_t)b * (sh.T + 1) + t) * C + tid] = bl + o;
     if (last && tail) {
       const double lz = bl + row_lse(o, is_row, sh, sm);
       if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
@@ -389,291 +393,14 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
     if (is_row) sm.erow[tid] = exp(o - M);
     __syncthreads();
     m = contract(r, sm, sh, M);  // u (forward) or beta (backward) minus bl
+    if (is_row && pb.row_a)
+      (fwd ? pb.row_u : pb.row_b)[((size_t)b * (sh.T + 1) + t) * C + tid] = bl + m;
     bool need = false;
     if (is_row)
       need = insert_entry(sm, sh, t,
                           (m - sigma * Sb[(size_t)t * C + tid]) + (double)(base - R) * kLn2, R);
     if (__syncthreads_or(need)) apply_rebase(r, sm, sh, t, fwd);
     if (last) save_ckpt(rec_end, sm, sh, R, bl + o, bl + m);
-  }
-}
-
-// -------------------------------------------------------- marginal pass
-// One workgroup per (sequence b, chunk j) with chunk = [p0, p1),
-// p0 = j*delta, p1 = min(p0 + delta, L).
-//   phase A: forward from checkpoint j; alpha[t] for t in (p0, p1] and
-//            u[t] for t in [p0, p1) go to the chunk scratch;
-//   phase B: backward from the checkpoint at p1; per position
-//            E_start[t,c] = exp(u + v - logZ), E_end[t,c] = exp(alpha + beta - logZ),
-//            segment posteriors P(t,k,c) = Q[t,c] * D[k][c] * ring (accumulated
-//            per duration into grad_dur partials), the coverage suffix sums,
-//            and the exp-space factors of the transition posteriors;
-//   phase C: grad_trans partial = sum_t ea[t,c'] * ev[t,c] (float64),
-//            multiplied by exp(trans) in the reduction.
-template <int NT, int AMAX, int TRMAX, typename DT, typename GT>
-__global__ __launch_bounds__(NT) void k_chunk(
-    ChainShape sh, const float *__restrict__ trans, const float *__restrict__ dur,
-    const double *__restrict__ S, const int32_t *__restrict__ lengths,
-    const double *__restrict__ ck_fwd, const double *__restrict__ ck_bwd,
-    const double *__restrict__ logz_ws, double *__restrict__ scr_a, double *__restrict__ scr_u,
-    float *__restrict__ scr_ea, float *__restrict__ scr_ev, double *__restrict__ part_x,
-    double *__restrict__ part_gd, double *__restrict__ part_tot, double *__restrict__ part_ssum,
-    float *__restrict__ suffix_out) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  const int b = blockIdx.x / sh.nchunk, jc = blockIdx.x % sh.nchunk;
-  const int tid = threadIdx.x, C = sh.C, K = sh.K;
-  const bool is_row = tid < C;
-  const int L = lengths[b];
-  const int p0 = jc * sh.delta;
-  const size_t cid = (size_t)b * sh.nchunk + jc;
-  double *px = part_x + cid * C * C;
-  double *pg = part_gd + cid * K * C;
-  if (L < 1 || L > sh.T || p0 >= L) {
-    for (int i = tid; i < C * C; i += NT) px[i] = 0.0;
-    for (int i = tid; i < K * C; i += NT) pg[i] = 0.0;
-    if (is_row) {
-      part_tot[cid * C + tid] = 0.0;
-      part_ssum[cid * C + tid] = 0.0;
-    }
-    return;
-  }
-  const int p1 = min(p0 + sh.delta, L);
-  const double logZ = logz_ws[b];
-  Smem sm = carve(lds, sh);
-  Regs<AMAX, TRMAX, DT> r;
-  init_regs(r, sh, dur);
-  const double *Sb = S + (size_t)b * (sh.T + 1) * C;
-  const size_t cks = ck_stride(C, K);
-  const size_t rows = (size_t)sh.delta + 1;
-  double *sa = scr_a + cid * rows * C;  // alpha[p0 + i]
-  double *su = scr_u + cid * rows * C;  // u[p0 + i]
-  float *sea = scr_ea + cid * rows * C;
-  float *sev = scr_ev + cid * rows * C;
-
-  // ---- phase A: forward recompute
-  load_trans(r, sh, trans, true);
-  int R = 0;
-  double o = 0.0, m = 0.0;
-  load_ckpt(ck_fwd + cid * cks, sm, sh, R, o, m);
-  if (is_row) {
-    sa[tid] = o;
-    su[tid] = m;
-  }
-  for (int t = p0 + 1; t <= p1; ++t) {
-    double nogd[AMAX];
-    const double s = r.kp < sh.P ? ksum<false>(r, sm, sh, t, true, nogd, 0.0) : 0.0;
-    if (r.kp < sh.P) sm.part[r.kp * C + r.kc] = s;
-    __syncthreads();
-    const int base = (int)sm.refs[0];
-    const double bl = (double)base * kLn2;
-    if (is_row) {
-      double sum = 0.0;
-      for (int p = 0; p < sh.P; ++p) sum += sm.part[p * C + tid];
-      o = Sb[(size_t)t * C + tid] + (double)(R - base) * kLn2 + log(sum);  // alpha - bl
-      sa[(size_t)(t - p0) * C + tid] = bl + o;
-    }
-    if (t == p1) break;
-    const double M = row_max(o, is_row, sh, sm);
-    if (is_row) sm.erow[tid] = exp(o - M);
-    __syncthreads();
-    m = contract(r, sm, sh, M);  // u - bl
-    bool need = false;
-    if (is_row) {
-      su[(size_t)(t - p0) * C + tid] = bl + m;
-      need = insert_entry(sm, sh, t, (m - Sb[(size_t)t * C + tid]) + (double)(base - R) * kLn2,
-                          R);
-    }
-    if (__syncthreads_or(need)) apply_rebase(r, sm, sh, t, true);
-  }
-  __syncthreads();
-
-  // ---- phase B: backward over the chunk with posteriors
-  load_trans(r, sh, trans, false);
-  load_ckpt(ck_bwd + cid * cks, sm, sh, R, o, m);  // state at p1, m = beta[p1]
-  GT gd[AMAX];
-#pragma unroll
-  for (int j = 0; j < AMAX; ++j) gd[j] = (GT)0;
-  double suffix = 0.0, ssum = 0.0;
-  float *suf = suffix_out + (size_t)b * sh.T * C;
-  if (is_row) {
-    const double eend = exp(sa[(size_t)(p1 - p0) * C + tid] + m - logZ);
-    suffix = -eend;
-  }
-  for (int t = p1 - 1; t >= p0; --t) {
-    double s = 0.0;
-    if (r.kp < sh.P) {
-      // Q[t,c] = exp(u[t,c] - S[t,c] + R[c]*ln2 - logZ): P(t,k,c) = Q * D * ring
-      const double ut = su[(size_t)(t - p0) * C + r.kc];
-      const double q =
-          exp_wide((ut + sm.refs[r.kc] * kLn2 - logZ) - Sb[(size_t)t * C + r.kc]);
-      s = ksum<true>(r, sm, sh, t, false, gd, q);
-      sm.part[r.kp * C + r.kc] = s;
-    }
-    __syncthreads();
-    const int base = (int)sm.refs[0];
-    const double bl = (double)base * kLn2;
-    double at = 0.0;
-    if (is_row) {
-      double sum = 0.0;
-      for (int p = 0; p < sh.P; ++p) sum += sm.part[p * C + tid];
-      o = -Sb[(size_t)t * C + tid] + (double)(R - base) * kLn2 + log(sum);  // v[t] - bl
-      const double ut = su[(size_t)(t - p0) * C + tid];
-      const double estart = exp((ut + bl - logZ) + o);
-      suf[(size_t)t * C + tid] = (float)suffix;
-      ssum += suffix;
-      suffix += estart;
-      at = sa[(size_t)(t - p0) * C + tid];
-    }
-    if (t == 0) break;
-    const double M = row_max(o, is_row, sh, sm);
-    if (is_row) {
-      const double e = exp(o - M);
-      sm.erow[tid] = e;
-      sev[(size_t)(t - p0) * C + tid] = (float)e;
-      sea[(size_t)(t - p0) * C + tid] = (float)exp_wide((at + bl - logZ) + M);
-    }
-    __syncthreads();
-    m = contract(r, sm, sh, M);  // beta[t] - bl
-    bool need = false;
-    if (is_row) {
-      need = insert_entry(sm, sh, t, (m + Sb[(size_t)t * C + tid]) + (double)(base - R) * kLn2,
-                          R);
-      if (t > p0) suffix -= exp((at + bl - logZ) + m);  // E_end[t]
-    }
-    if (__syncthreads_or(need)) apply_rebase(r, sm, sh, t, false);
-  }
-  if (is_row) {
-    part_tot[cid * C + tid] = suffix;
-    part_ssum[cid * C + tid] = ssum;
-  }
-  // P*A >= K, so every duration is owned by exactly one thread
-#pragma unroll
-  for (int j = 0; j < AMAX; ++j)
-    if (j < r.nage) pg[(size_t)(r.age0 + j - 1) * C + r.kc] = (double)gd[j];
-  __syncthreads();
-
-  // ---- phase C: transition posteriors, X[c',c] = sum_t ea[t,c'] * ev[t,c]
-  const int tlo = p0 < 1 ? 1 : p0;
-  const int nrow = p1 - tlo;
-  const int npair = C * C;
-  // the ring area (K*C doubles) now holds K rows of ea and K rows of ev
-  float *tile_a = reinterpret_cast<float *>(sm.ring);
-  const int tile_rows = K;
-  float *tile_v = tile_a + (size_t)tile_rows * C;
-  constexpr int kPairs = 16;
-  for (int pbase = 0; pbase < npair; pbase += NT * kPairs) {
-    double acc[kPairs];
-#pragma unroll
-    for (int i = 0; i < kPairs; ++i) acc[i] = 0.0;
-    for (int r0 = 0; r0 < nrow; r0 += tile_rows) {
-      const int nr = min(tile_rows, nrow - r0);
-      __syncthreads();
-      for (int i = tid; i < nr * C; i += NT) {
-        const size_t src = (size_t)(tlo - p0 + r0) * C + i;
-        tile_a[i] = sea[src];
-        tile_v[i] = sev[src];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < kPairs; ++i) {
-        const int pi = pbase + i * NT + tid;
-        if (pi < npair) {
-          const int cp = pi / C, c = pi % C;
-          double a = acc[i];
-          for (int rr = 0; rr < nr; ++rr)
-            a += (double)tile_a[rr * C + cp] * (double)tile_v[rr * C + c];
-          acc[i] = a;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kPairs; ++i) {
-      const int pi = pbase + i * NT + tid;
-      if (pi < npair) px[pi] = acc[i];
-    }
-  }
-}
-
-// ------------------------------------------------------------ reductions
-// grad_trans[c',c] = exp(trans[c',c]) * sum_{b,j} w_b X[b,j][c',c];
-// grad_dur[k,c]    = sum_{b,j} w_b gd[b,j][k,c]; fixed order, float64.
-__global__ void k_reduce_params(ChainShape sh, const float *__restrict__ trans,
-                                const int32_t *__restrict__ lengths,
-                                const float *__restrict__ grad_logz,
-                                const double *__restrict__ part_x,
-                                const double *__restrict__ part_gd,
-                                float *__restrict__ grad_trans, float *__restrict__ grad_dur) {
-  const int C = sh.C, K = sh.K;
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  const int nx = C * C, ng = K * C;
-  if (e >= nx + ng) return;
-  double acc = 0.0;
-  for (int b = 0; b < sh.B; ++b) {
-    const int L = lengths[b];
-    if (L < 1 || L > sh.T) continue;
-    const double w = grad_logz ? (double)grad_logz[b] : 1.0;
-    double sb = 0.0;
-    for (int j = 0; j < sh.nchunk; ++j) {
-      const size_t cid = (size_t)b * sh.nchunk + j;
-      sb += e < nx ? part_x[cid * nx + e] : part_gd[cid * ng + (e - nx)];
-    }
-    acc += w * sb;
-  }
-  if (e < nx)
-    grad_trans[e] = (float)(acc * exp((double)trans[e]));
-  else
-    grad_dur[e - nx] = (float)acc;
-}
-
-// Coverage carries: Ctot_{j+1}[c] = sum_{j'<=j} tot[j'][c] (the probability
-// that a label-c segment started before p1 and ends after it), and the
-// per-label mean coverage used by the centring correction.
-__global__ void k_carry(ChainShape sh, const int32_t *__restrict__ lengths,
-                        const double *__restrict__ part_tot, const double *__restrict__ part_ssum,
-                        double *__restrict__ carry, double *__restrict__ mean) {
-  const int b = blockIdx.x;
-  const int L = lengths[b];
-  for (int c = threadIdx.x; c < sh.C; c += blockDim.x) {
-    double ct = 0.0, sum = 0.0;
-    for (int j = 0; j < sh.nchunk; ++j) {
-      const size_t cid = (size_t)b * sh.nchunk + j;
-      const int p0 = j * sh.delta;
-      if (L >= 1 && L <= sh.T && p0 < L) {
-        const int n = min(p0 + sh.delta, L) - p0;
-        ct += part_tot[cid * sh.C + c];
-        sum += (double)n * ct - part_ssum[cid * sh.C + c];
-      }
-      carry[cid * sh.C + c] = ct;
-    }
-    mean[(size_t)b * sh.C + c] = (L >= 1 && L <= sh.T) ? sum / (double)L : 0.0;
-  }
-}
-
-// mu[b,t,c] = carry[b, t/delta, c] - suffix[b,t,c];
-// grad_x = w_b (mu - mean_c) (centred) or w_b mu.  In place on grad_emissions.
-__global__ void k_finalize(ChainShape sh, const int32_t *__restrict__ lengths,
-                           const float *__restrict__ grad_logz, const double *__restrict__ carry,
-                           const double *__restrict__ mean, float *__restrict__ grad_emissions,
-                           float *__restrict__ marginals) {
-  const int b = blockIdx.y;
-  const int C = sh.C;
-  const int L = lengths[b];
-  const bool ok = L >= 1 && L <= sh.T;
-  const double w = grad_logz ? (double)grad_logz[b] : 1.0;
-  const size_t n = (size_t)sh.T * C;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x) {
-    const int t = (int)(i / C), c = (int)(i % C);
-    float mu_out = 0.f, g_out = 0.f;
-    if (ok && t < L) {
-      const size_t cid = (size_t)b * sh.nchunk + t / sh.delta;
-      const double mu = carry[cid * C + c] - (double)grad_emissions[(size_t)b * n + i];
-      const double g = sh.center ? w * (mu - mean[(size_t)b * C + c]) : w * mu;
-      mu_out = (float)mu;
-      g_out = (float)g;
-    }
-    grad_emissions[(size_t)b * n + i] = g_out;
-    if (marginals) marginals[(size_t)b * n + i] = mu_out;
   }
 }
 
@@ -695,8 +422,6 @@ struct ChainKernels {
     if (!done) {
       (void)hipFuncSetAttribute((const void *)k_sweep<NT, AMAX, TRMAX, DT>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
-      (void)hipFuncSetAttribute((const void *)k_chunk<NT, AMAX, TRMAX, DT, GT>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
       (void)hipGetLastError();
       done = true;
     }
@@ -709,19 +434,6 @@ struct ChainKernels {
     hipLaunchKernelGGL((k_sweep<NT, AMAX, TRMAX, DT>), dim3((with_bwd ? 2 : 1) * sh.B * sh.nchunk),
                        dim3(NT), lds, st, sh, trans, dur, S, lengths, pb, iter);
     return report(hipGetLastError(), "k_sweep", sh, lds);
-  }
-  static hipError_t chunks(const ChainShape &sh, const float *trans, const float *dur,
-                           const double *S, const int32_t *lengths, const double *ck_fwd,
-                           const double *ck_bwd, const double *logz_ws, double *scr_a,
-                           double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
-                           double *part_gd, double *part_tot, double *part_ssum,
-                           float *suffix_out, hipStream_t st) {
-    const size_t lds = chain_lds_bytes(sh.C, sh.K, sh.P, sh.QT);
-    set_attrs();
-    hipLaunchKernelGGL((k_chunk<NT, AMAX, TRMAX, DT, GT>), dim3(sh.B * sh.nchunk), dim3(NT),
-                       lds, st, sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, scr_a,
-                       scr_u, scr_ea, scr_ev, part_x, part_gd, part_tot, part_ssum, suffix_out);
-    return report(hipGetLastError(), "k_chunk", sh, lds);
   }
 };
 
@@ -754,42 +466,6 @@ hipError_t launch_sweep(const ChainShape &sh, const float *trans, const float *d
                         int with_bwd, int iter, hipStream_t st) {
   if (sh.win) return launch_sweep_w(sh, trans, dur, S, lengths, pb, with_bwd, iter, st);
   SEMICRF_CHAIN_DISPATCH(sh, sweep(sh, trans, dur, S, lengths, pb, with_bwd, iter, st));
-}
-
-hipError_t launch_chunks(const ChainShape &sh, const float *trans, const float *dur,
-                         const double *S, const int32_t *lengths, const double *ck_fwd,
-                         const double *ck_bwd, const double *logz_ws, double *scr_a,
-                         double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
-                         double *part_gd, double *part_tot, double *part_ssum,
-                         float *suffix_out, hipStream_t st) {
-  if (sh.win)
-    return launch_chunks_w(sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, scr_a, scr_u,
-                           scr_ea, scr_ev, part_x, part_gd, part_tot, part_ssum, suffix_out, st);
-  SEMICRF_CHAIN_DISPATCH(sh, chunks(sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, scr_a,
-                                    scr_u, scr_ea, scr_ev, part_x, part_gd, part_tot, part_ssum,
-                                    suffix_out, st));
-}
-
-hipError_t launch_finish(const ChainShape &sh, const float *trans, const int32_t *lengths,
-                         const float *grad_logz, const double *part_x, const double *part_gd,
-                         const double *part_tot, const double *part_ssum, double *carry,
-                         double *mean, float *grad_trans, float *grad_dur,
-                         float *grad_emissions, float *marginals, hipStream_t st) {
-  const int ne = sh.C * sh.C + sh.K * sh.C;
-  hipLaunchKernelGGL(k_reduce_params, dim3((ne + 255) / 256), dim3(256), 0, st, sh, trans,
-                     lengths, grad_logz, part_x, part_gd, grad_trans, grad_dur);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_carry, dim3(sh.B), dim3(256), 0, st, sh, lengths, part_tot, part_ssum,
-                     carry, mean);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t n = (size_t)sh.T * sh.C;
-  int gx = (int)((n + 255) / 256);
-  if (gx > 4096) gx = 4096;
-  hipLaunchKernelGGL(k_finalize, dim3(gx, sh.B), dim3(256), 0, st, sh, lengths, grad_logz,
-                     carry, mean, grad_emissions, marginals);
-  return hipGetLastError();
 }
 
 }  // namespace semicrf

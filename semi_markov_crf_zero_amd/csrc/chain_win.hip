@@ -388,6 +388,8 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
     // o = NaN marks a neutral start (never accepted by the verification)
     wsave(rec_start, sm, sh, chain, lane, R,
           exact ? -__builtin_huge_val() : __builtin_nan(""), exact ? 0.0 : __builtin_nan(""), NT);
+    if (exact && chain && pb.row_a)  // u[0] = 0 forward, beta[L] = 0 backward
+      (fwd ? pb.row_u : pb.row_b)[((size_t)b * (T + 1) + tstart) * C + lane] = 0.0;
   } else {
     double o0, m0;
     wload(rec_start, sm, sh, chain, lane, R, o0, m0, NT);
@@ -437,6 +439,11 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
               rb = chain_insert(sm, sh, lane, t, (m - sg * st) + (double)(base - R) * kLn2, R);
             chain_flag(sm, t, rb);
           }
+          if (chain && pb.row_a) {  // per-position rows, in this chunk's frame
+            const size_t ri = ((size_t)b * (T + 1) + t) * C + lane;
+            (fwd ? pb.row_a : pb.row_v)[ri] = bl + o;
+            if (!lz_step) (fwd ? pb.row_u : pb.row_b)[ri] = bl + m;
+          }
           if (chain) {  // prefetch S for the same block offset of the next block
             const int tp = t + sigma * U;
             Sq[i] = ld_or(Sb + (size_t)tp * C + lane, tp >= 0 && tp <= T);
@@ -458,265 +465,6 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   }
 }
 
-// -------------------------------------------------------- marginal pass
-// One workgroup per (sequence b, chunk j), chunk = [p0, p1).  Phases as in
-// chain.hip's k_chunk: A forward recompute into the chunk scratch, B backward
-// with posteriors, C transition-posterior GEMM.
-template <int NT, int AMAX, int U, int CMAX>
-__global__ __launch_bounds__(NT) void k_chunk_w(
-    ChainShape sh, const float *__restrict__ trans, const float *__restrict__ dur,
-    const double *__restrict__ S, const int32_t *__restrict__ lengths,
-    const double *__restrict__ ck_fwd, const double *__restrict__ ck_bwd,
-    const double *__restrict__ logz_ws, double *__restrict__ scr_a, double *__restrict__ scr_u,
-    float *__restrict__ scr_ea, float *__restrict__ scr_ev, double *__restrict__ part_x,
-    double *__restrict__ part_gd, double *__restrict__ part_tot, double *__restrict__ part_ssum,
-    float *__restrict__ suffix_out) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  const int b = blockIdx.x / sh.nchunk, jc = blockIdx.x % sh.nchunk;
-  const int tid = threadIdx.x, C = sh.C, K = sh.K, T = sh.T;
-  const int lane = tid & 63;
-  const bool chain = tid < C;
-  const bool wave0 = tid < 64;
-  const int L = lengths[b];
-  const int p0 = jc * sh.delta;
-  const size_t cid = (size_t)b * sh.nchunk + jc;
-  double *px = part_x + cid * C * C;
-  double *pg = part_gd + cid * K * C;
-  if (L < 1 || L > T || p0 >= L) {
-    for (int i = tid; i < C * C; i += NT) px[i] = 0.0;
-    for (int i = tid; i < K * C; i += NT) pg[i] = 0.0;
-    if (chain) {
-      part_tot[cid * C + lane] = 0.0;
-      part_ssum[cid * C + lane] = 0.0;
-    }
-    return;
-  }
-  const int p1 = min(p0 + sh.delta, L);
-  const double logZ = logz_ws[b];
-  const WSmem sm = wcarve(lds, sh);
-  Win<AMAX, U> win;
-  win.init(sh, dur);
-  const double *Sb = S + (size_t)b * (T + 1) * C;
-  const size_t cks = ck_stride(C, K);
-  const size_t rows = (size_t)sh.delta + 1;
-  double *sa = scr_a + cid * rows * C;  // alpha[p0 + r]
-  double *su = scr_u + cid * rows * C;  // u[p0 + r]
-  float *sea = scr_ea + cid * rows * C;
-  float *sev = scr_ev + cid * rows * C;
-  double nogd[AMAX];
-
-  // ---- phase A: forward recompute, steps t = p0+1 .. p1
-  stage_trans(sm, sh, trans, true, NT);
-  int R = 0;
-  double o = 0.0, m = 0.0;
-  wload(ck_fwd + cid * cks, sm, sh, chain, lane, R, o, m, NT);
-  __syncthreads();
-  if (chain) {
-    sa[lane] = o;
-    su[lane] = m;
-  }
-  {
-    const int first = p0 + 1, nsteps = p1 - p0;
-    double Sq[U];
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const int t = first + i;
-      Sq[i] = chain ? ld_or(Sb + (size_t)t * C + lane, t <= T) : 0.0;
-    }
-    bool done = false;
-    for (int s0 = 0; !done; s0 += U) {
-      const int t0 = first + s0;
-      win.fill(sm, sh, t0, 1);
-#pragma unroll
-      for (int i = 0; i < U; ++i) {
-        if (!done) {
-          const int step = s0 + i;
-          const int t = t0 + i;
-          const double ks = win.on ? win.template step<false>(i, sm, sh, 1, nogd, 0.0) : 0.0;
-          win.publish(sm, sh, ks);
-          __syncthreads();
-          const bool last = step == nsteps - 1;
-          if (wave0) {
-            const double st = Sq[i];
-            const int base = chain_base(R);
-            const double bl = (double)base * kLn2;
-            const double ov =  // alpha - bl
-                chain ? st + (double)(R - base) * kLn2 + log(chain_sum<NT>(sm, sh, lane)) : 0.0;
-            if (chain) sa[(size_t)(t - p0) * C + lane] = bl + ov;
-            if (!last) {
-              double e, M;
-              const double mv = chain_contract<CMAX>(sm, sh, lane, ov, e, M);  // u - bl
-              bool rb = false;
-              if (chain) {
-                su[(size_t)(t - p0) * C + lane] = bl + mv;
-                rb = chain_insert(sm, sh, lane, t, (mv - st) + (double)(base - R) * kLn2, R);
-              }
-              chain_flag(sm, t, rb);
-            }
-            if (chain) {
-              const int tp = t + U;
-              Sq[i] = ld_or(Sb + (size_t)tp * C + lane, tp <= T);
-            }
-          }
-          if (last) {
-            done = true;
-          } else {
-            __syncthreads();
-            if (sm.flag[t & 1]) {
-              win.rebase(sm, sh, t, 1);
-              __syncthreads();
-            }
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- phase B: backward over the chunk with posteriors, steps t = p1-1 .. p0
-  stage_trans(sm, sh, trans, false, NT);
-  wload(ck_bwd + cid * cks, sm, sh, chain, lane, R, o, m, NT);  // m = beta[p1]
-  double gd[AMAX];
-#pragma unroll
-  for (int j = 0; j < AMAX; ++j) gd[j] = 0.0;
-  double suffix = 0.0, ssum = 0.0;
-  float *suf = suffix_out + (size_t)b * T * C;
-  const int first = p1 - 1, nsteps = p1 - p0;
-  double Sq[U], uq[U], aq[U];
-#pragma unroll
-  for (int i = 0; i < U; ++i) {
-    const int t = first - i;
-    const bool ok = chain && t >= p0;
-    Sq[i] = ok ? Sb[(size_t)t * C + lane] : 0.0;
-    uq[i] = ok ? su[(size_t)(t - p0) * C + lane] : 0.0;
-    aq[i] = ok ? sa[(size_t)(t - p0) * C + lane] : 0.0;
-  }
-  if (chain) {
-    suffix = -exp(sa[(size_t)(p1 - p0) * C + lane] + m - logZ);  // -E_end[p1]
-    // factor of position p1-1
-    sm.qrow[lane] = exp_wide((uq[0] + (double)R * kLn2 - logZ) - Sq[0]);
-  }
-  __syncthreads();
-  bool done = false;
-  for (int s0 = 0; !done; s0 += U) {
-    const int t0 = first - s0;
-    win.fill(sm, sh, t0, -1);
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      if (!done) {
-        const int step = s0 + i;
-        const int t = t0 - i;
-        double ks = 0.0;
-        if (win.on) ks = win.template step<true>(i, sm, sh, -1, gd, sm.qrow[win.kc]);
-        win.publish(sm, sh, ks);
-        __syncthreads();
-        const bool last = step == nsteps - 1;  // t == p0
-        if (wave0) {
-          const double st = Sq[i], ut = uq[i], at = aq[i];
-          const int base = chain_base(R);
-          const double bl = (double)base * kLn2;
-          const double v =  // v[t] - bl
-              chain ? -st + (double)(R - base) * kLn2 + log(chain_sum<NT>(sm, sh, lane)) : 0.0;
-          if (chain) {
-            const double estart = exp((ut + bl - logZ) + v);
-            suf[(size_t)t * C + lane] = (float)suffix;
-            ssum += suffix;
-            suffix += estart;
-          }
-          if (!last) {
-            double e, M;
-            const double beta = chain_contract<CMAX>(sm, sh, lane, v, e, M);  // beta - bl
-            bool rb = false;
-            if (chain) {
-              sev[(size_t)(t - p0) * C + lane] = (float)e;
-              sea[(size_t)(t - p0) * C + lane] = (float)exp_wide((at + bl - logZ) + M);
-              rb = chain_insert(sm, sh, lane, t, (beta + st) + (double)(base - R) * kLn2, R);
-              suffix -= exp((at + bl - logZ) + beta);  // E_end[t], t > p0
-              // posterior factor of the next position t-1 with the new reference
-              const int nx = (i + 1) % U;
-              sm.qrow[lane] = exp_wide((uq[nx] + (double)R * kLn2 - logZ) - Sq[nx]);
-            }
-            chain_flag(sm, t, rb);
-          } else if (t > 0) {
-            // transition posteriors at t = p0 > 0 need ea/ev with this row's max
-            const float M = wave_max(chain ? (float)v : -__builtin_huge_valf());
-            if (chain) {
-              sev[lane] = exp_f32(v - (double)M);
-              sea[lane] = (float)exp_wide((at + bl - logZ) + (double)M);
-            }
-          }
-          if (chain) {
-            const int tp = t - U;
-            const bool ok = tp >= p0;
-            Sq[i] = ok ? Sb[(size_t)tp * C + lane] : 0.0;
-            uq[i] = ok ? su[(size_t)(tp - p0) * C + lane] : 0.0;
-            aq[i] = ok ? sa[(size_t)(tp - p0) * C + lane] : 0.0;
-          }
-        }
-        if (last) {
-          done = true;
-        } else {
-          __syncthreads();
-          if (sm.flag[t & 1]) {
-            win.rebase(sm, sh, t, -1);
-            __syncthreads();
-          }
-        }
-      }
-    }
-  }
-  if (chain) {
-    part_tot[cid * C + lane] = suffix;
-    part_ssum[cid * C + lane] = ssum;
-  }
-  if (win.on) {
-#pragma unroll
-    for (int j = 0; j < AMAX; ++j)
-      if (j < win.nage) pg[(size_t)(win.a0 + j - 1) * C + win.kc] = gd[j];
-  }
-  __syncthreads();
-
-  // ---- phase C: X[c',c] = sum_t ea[t,c'] * ev[t,c] over t in [max(p0,1), p1)
-  const int tlo = p0 < 1 ? 1 : p0;
-  const int nrow = p1 - tlo;
-  const int npair = C * C;
-  float *tile_a = reinterpret_cast<float *>(sm.ring);
-  const int tile_rows = K;
-  float *tile_v = tile_a + (size_t)tile_rows * C;
-  constexpr int kPairs = 16;
-  for (int pbase = 0; pbase < npair; pbase += NT * kPairs) {
-    double acc[kPairs];
-#pragma unroll
-    for (int i = 0; i < kPairs; ++i) acc[i] = 0.0;
-    for (int r0 = 0; r0 < nrow; r0 += tile_rows) {
-      const int nr = min(tile_rows, nrow - r0);
-      __syncthreads();
-      for (int i = tid; i < nr * C; i += NT) {
-        const size_t src = (size_t)(tlo - p0 + r0) * C + i;
-        tile_a[i] = sea[src];
-        tile_v[i] = sev[src];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < kPairs; ++i) {
-        const int pi = pbase + i * NT + tid;
-        if (pi < npair) {
-          const int cp = pi / C, c = pi % C;
-          double a = acc[i];
-          for (int rr = 0; rr < nr; ++rr)
-            a += (double)tile_a[rr * C + cp] * (double)tile_v[rr * C + c];
-          acc[i] = a;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kPairs; ++i) {
-      const int pi = pbase + i * NT + tid;
-      if (pi < npair) px[pi] = acc[i];
-    }
-  }
-}
-
 // ------------------------------------------------------------- dispatch
 static hipError_t wreport(hipError_t e, const char *what, const ChainShape &sh, size_t lds) {
   if (e != hipSuccess && getenv("SEMICRF_DEBUG"))
@@ -732,8 +480,6 @@ struct WinKernels {
     if (!done) {
       (void)hipFuncSetAttribute((const void *)k_sweep_w<NT, AMAX, U, CMAX>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
-      (void)hipFuncSetAttribute((const void *)k_chunk_w<NT, AMAX, UC, CMAX>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
       (void)hipGetLastError();
       done = true;
     }
@@ -746,19 +492,6 @@ struct WinKernels {
     hipLaunchKernelGGL((k_sweep_w<NT, AMAX, U, CMAX>), dim3((with_bwd ? 2 : 1) * sh.B * sh.nchunk),
                        dim3(NT), lds, st, sh, trans, dur, S, lengths, pb, iter);
     return wreport(hipGetLastError(), "k_sweep_w", sh, lds);
-  }
-  static hipError_t chunks(const ChainShape &sh, const float *trans, const float *dur,
-                           const double *S, const int32_t *lengths, const double *ck_fwd,
-                           const double *ck_bwd, const double *logz_ws, double *scr_a,
-                           double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
-                           double *part_gd, double *part_tot, double *part_ssum,
-                           float *suffix_out, hipStream_t st) {
-    attrs();
-    const size_t lds = win_lds_bytes(sh.C, sh.K, sh.P);
-    hipLaunchKernelGGL((k_chunk_w<NT, AMAX, UC, CMAX>), dim3(sh.B * sh.nchunk), dim3(NT), lds,
-                       st, sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, scr_a, scr_u,
-                       scr_ea, scr_ev, part_x, part_gd, part_tot, part_ssum, suffix_out);
-    return wreport(hipGetLastError(), "k_chunk_w", sh, lds);
   }
 };
 
@@ -788,19 +521,6 @@ hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float 
                           int with_bwd, int iter, hipStream_t st) {
   return win_dispatch(sh, [&](auto k) {
     return decltype(k)::sweep(sh, trans, dur, S, lengths, pb, with_bwd, iter, st);
-  });
-}
-
-hipError_t launch_chunks_w(const ChainShape &sh, const float *trans, const float *dur,
-                           const double *S, const int32_t *lengths, const double *ck_fwd,
-                           const double *ck_bwd, const double *logz_ws, double *scr_a,
-                           double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
-                           double *part_gd, double *part_tot, double *part_ssum,
-                           float *suffix_out, hipStream_t st) {
-  return win_dispatch(sh, [&](auto k) {
-    return decltype(k)::chunks(sh, trans, dur, S, lengths, ck_fwd, ck_bwd, logz_ws, scr_a, scr_u,
-                               scr_ea, scr_ev, part_x, part_gd, part_tot, part_ssum, suffix_out,
-                               st);
   });
 }
 

@@ -107,12 +107,30 @@ __host__ __device__ inline size_t win_lds_bytes(int C, int K, int P) {
 // Workspace layout (byte offsets, 256-aligned).
 struct Layout {
   size_t S, nu, tile_sum, anchor, logz, logz_bwd;
-  size_t ck_fwd, ck_bwd, end_fwd, end_bwd, redo, corr_i, corr_f, nbad, lz_part;
-  size_t scr_a, scr_u, scr_ea, scr_ev;
-  size_t part_x, part_gd, part_tot, part_ssum, carry, mean;
+  size_t ck_fwd, ck_bwd, end_fwd, end_bwd, redo, corr_i, corr_f, nbad, lz_part, shift;
+  size_t row_a, row_u, row_v, row_b;
+  size_t cov_part, cov_part2, cov_anchor, cov_mean, tx_part, dur_part;
   size_t bp, vbest, vcbest;
   size_t total;
   int ntile;
+};
+
+// Arguments of the posterior pass (post.hip).
+struct PostArgs {
+  const int32_t *lengths;
+  const float *trans, *dur, *grad_logz;
+  const double *S, *logz;
+  const double *row_a, *row_u, *row_v, *row_b;
+  double *cov_part, *cov_part2, *cov_anchor, *cov_mean;  // [B][ntile][C], [B][C]
+  double *tx_part;                                       // [B][tx_nseg][C][C]
+  double *dur_part;                                      // [B][dur_nspan][K][C]
+  float *grad_emissions, *marginals, *grad_trans, *grad_dur;
+};
+
+// Launch geometry of the posterior pass (also sizes its workspace).
+struct PostGeom {
+  int cov_ntile, tx_seg, tx_nseg, dur_span, dur_nspan, dur_kb, dur_npg;
+  size_t dur_lds;
 };
 
 // Buffers of the parallel-in-time sweeps (pit.hip).  Records have the
@@ -125,9 +143,15 @@ struct PitBufs {
   double *corr_f;             // [2][B][nchunk]: its fraction
   int *nbad;                  // [nchunk]: start states replaced by each verification
   double *lz_part;            // [2][B]: log Z in the frame of the chain's last chunk
+  double *shift;              // [2][B][nchunk]: log correction of each chunk (fix-up)
+  // Per-position rows [B][T+1][C] (float64, NULL when not wanted): forward
+  // alpha (t = 1..L) and u (t = 0..L-1), backward v (t = 0..L-1) and beta
+  // (t = 1..L); written in each chunk's frame, corrected by k_pit_rows.
+  double *row_a, *row_u, *row_v, *row_b;
 };
 
-// ---- launchers (defined in scan.hip / chain.hip / viterbi.hip) ----------
+// ---- launchers (scan.hip, chain.hip, chain_win.hip, pit.hip, post.hip,
+// viterbi.hip) ------------------------------------------------------------
 
 hipError_t launch_scan(const float *x, const int32_t *lengths, int B, int T, int C, int center,
                        double *nu, double *S, double *tile_sum, double *anchor, int ntile,
@@ -139,7 +163,13 @@ hipError_t launch_sweep(const ChainShape &sh, const float *trans, const float *d
                         const double *S, const int32_t *lengths, const PitBufs &pb,
                         int with_bwd, int iter, hipStream_t st);
 
-// The whole parallel-in-time sweep: init, nchunk x (sweep, verify), fix-up.
+// windowed engine for C <= 32 (chain_win.hip); same arguments
+hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float *dur,
+                          const double *S, const int32_t *lengths, const PitBufs &pb,
+                          int with_bwd, int iter, hipStream_t st);
+
+// The whole parallel-in-time sweep: init, nchunk x (sweep, verify), fix-up
+// of the records, log Z and (when wanted) the per-position rows.
 hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur,
                       const double *S, const int32_t *lengths, const PitBufs &pb,
                       double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
@@ -151,31 +181,16 @@ hipError_t launch_pit_verify(const ChainShape &sh, const int32_t *lengths, const
 hipError_t launch_pit_fixup(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
                             double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
                             hipStream_t st);
+hipError_t launch_pit_rows(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
+                           hipStream_t st);
 
-hipError_t launch_chunks(const ChainShape &sh, const float *trans, const float *dur,
-                         const double *S, const int32_t *lengths, const double *ck_fwd,
-                         const double *ck_bwd, const double *logz_ws, double *scr_a,
-                         double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
-                         double *part_gd, double *part_tot, double *part_ssum,
-                         float *suffix_out, hipStream_t st);
+void post_geometry(const ChainShape &sh, PostGeom &g);
 
-// windowed engine for C <= 32 (chain_win.hip); same arguments and outputs
-hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float *dur,
-                          const double *S, const int32_t *lengths, const PitBufs &pb,
-                          int with_bwd, int iter, hipStream_t st);
-
-hipError_t launch_chunks_w(const ChainShape &sh, const float *trans, const float *dur,
-                           const double *S, const int32_t *lengths, const double *ck_fwd,
-                           const double *ck_bwd, const double *logz_ws, double *scr_a,
-                           double *scr_u, float *scr_ea, float *scr_ev, double *part_x,
-                           double *part_gd, double *part_tot, double *part_ssum,
-                           float *suffix_out, hipStream_t st);
-
-hipError_t launch_finish(const ChainShape &sh, const float *trans, const int32_t *lengths,
-                         const float *grad_logz, const double *part_x, const double *part_gd,
-                         const double *part_tot, const double *part_ssum, double *carry,
-                         double *mean, float *grad_trans, float *grad_dur,
-                         float *grad_emissions, float *marginals, hipStream_t st);
+// Coverage, emission gradients and marginals; transition and duration
+// posterior sums (per-block partials) ...
+hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream_t st);
+// ... and their fixed-order reduction into grad_trans / grad_dur.
+hipError_t launch_post_reduce(const ChainShape &sh, const PostArgs &pa, hipStream_t st);
 
 hipError_t launch_viterbi(const ChainShape &sh, const float *trans, const float *dur,
                           const double *S, const int32_t *lengths, uint32_t *bp, double *vbest,

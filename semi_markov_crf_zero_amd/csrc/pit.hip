@@ -190,6 +190,7 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_fixup(ChainShape sh,
   double *rec0 = (fwd ? pb.ck_fwd : pb.ck_bwd) + (size_t)b * sh.nchunk * cks;
   long long oi = 0;  // accumulated offset of the current chunk, log2 units
   double of = 0.0;
+  if (tid == 0) pb.shift[base + (fwd ? 0 : nvalid - 1)] = 0.0;  // the chain's exact chunk
   for (int s = 1; s < nvalid; ++s) {
     const int j = fwd ? s : nvalid - 1 - s;
     oi += pb.corr_i[base + j];
@@ -207,6 +208,7 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_fixup(ChainShape sh,
     double *rec = rec0 + (size_t)j * cks;
     const double scale = exp2(nf);
     const double shift = ((double)ni + nf) * kLn2;
+    if (tid == 0) pb.shift[base + j] = shift;
     for (int i = tid; i < K * C; i += kPitThreads) rec[i] *= scale;
     for (int c = tid; c < C; c += kPitThreads) {
       rec[(size_t)K * C + c] = (double)((long long)rec[(size_t)K * C + c] + ni);
@@ -241,7 +243,48 @@ hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur
     e = launch_pit_verify(sh, lengths, pb, it, with_bwd, st);
     if (e != hipSuccess) return e;
   }
-  return launch_pit_fixup(sh, lengths, pb, logz_ws, logz_bwd_ws, logz_out, with_bwd, st);
+  e = launch_pit_fixup(sh, lengths, pb, logz_ws, logz_bwd_ws, logz_out, with_bwd, st);
+  if (e != hipSuccess || !pb.row_a) return e;
+  return launch_pit_rows(sh, lengths, pb, st);
+}
+
+// Add each chunk's log correction to the rows it wrote: forward chunk j
+// owns alpha and u at t in (p0, p1]; backward chunk j owns v and beta at t
+// in [p0, p1).  Grid: (direction, sequence, chunk) x row blocks.
+__global__ __launch_bounds__(kPitThreads) void k_pit_rows(ChainShape sh,
+                                                          const int32_t *__restrict__ lengths,
+                                                          PitBufs pb) {
+  const int nck = sh.B * sh.nchunk;
+  const bool fwd = (int)blockIdx.y < nck;
+  const int rem = fwd ? blockIdx.y : blockIdx.y - nck;
+  const int b = rem / sh.nchunk, j = rem % sh.nchunk;
+  const int L = lengths[b];
+  if (L < 1 || L > sh.T) return;
+  const int p0 = j * sh.delta;
+  if (p0 >= L) return;
+  const int p1 = min(p0 + sh.delta, L);
+  const double sh_j = pb.shift[(fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + j];
+  if (sh_j == 0.0) return;
+  const int C = sh.C;
+  const int t0 = fwd ? p0 + 1 : p0;  // rows [t0, t0 + p1 - p0)
+  const size_t n = (size_t)(p1 - p0) * C;
+  double *r1 = (fwd ? pb.row_a : pb.row_v) + ((size_t)b * (sh.T + 1) + t0) * C;
+  double *r2 = (fwd ? pb.row_u : pb.row_b) + ((size_t)b * (sh.T + 1) + t0) * C;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    r1[i] += sh_j;
+    r2[i] += sh_j;
+  }
+}
+
+hipError_t launch_pit_rows(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
+                           hipStream_t st) {
+  const size_t per = (size_t)sh.delta * sh.C;
+  int gx = (int)((per + kPitThreads - 1) / kPitThreads);
+  gx = gx < 1 ? 1 : (gx > 64 ? 64 : gx);
+  hipLaunchKernelGGL(k_pit_rows, dim3(gx, 2 * sh.B * sh.nchunk), dim3(kPitThreads), 0, st, sh,
+                     lengths, pb);
+  return hipGetLastError();
 }
 
 hipError_t launch_pit_init(const ChainShape &sh, const PitBufs &pb, int niter, hipStream_t st) {

@@ -1,0 +1,398 @@
+// post.hip -- posteriors and gradients from the per-position rows.
+//
+// With the forward rows alpha[t,c], u[t,c] and the backward rows v[t,c],
+// beta[t,c] of every position (written by the parallel-in-time sweeps, see
+// pit.hip), every marginal of the semi-CRF has a closed form, so this whole
+// pass is data-parallel -- no recursion, no dependent chain:
+//   segment     P(s,k,c)    = exp(u[s,c] + S[s+k,c] - S[s,c] + dur[k-1,c] + beta[s+k,c] - logZ)
+//   transition  P(t,c'->c)  = exp(alpha[t,c'] + trans[c',c] + v[t,c] - logZ),   1 <= t < L
+//   boundaries  E_start[t,c] = exp(u + v - logZ),  E_end[t,c] = exp(alpha + beta - logZ)
+//   coverage    mu[i,c]     = sum_{t <= i} (E_start[t,c] - E_end[t,c])
+// and with F = sum_b w_b log Z_b (technical summary of "Streaming Structured
+// Inference with Flash-SemiCRF", section 2.C: exact gradients):
+//   dF/d dur[k-1,c]  = sum_b w_b sum_s P(s,k,c)
+//   dF/d trans[c',c] = sum_b w_b sum_t P(t,c'->c)
+//   dF/d x[b,i,c]    = w_b (mu[i,c] - mean_j mu[j,c])   (centred; w_b mu[i,c] otherwise)
+// Every reduction goes through per-block partials summed in a fixed order in
+// float64 (deterministic; no floating-point atomics).
+#include "device_math.h"
+#include "internal.h"
+
+namespace semicrf {
+
+namespace {
+
+constexpr int kCovThreads = 256;
+constexpr int kCovJ = 16;  // consecutive positions per coverage thread
+constexpr int kTxThreads = 256;
+constexpr int kTxTile = 64;   // output tile of the transition GEMM (64 x 64)
+constexpr int kTxRows = 32;   // positions staged in LDS per batch
+constexpr int kDurThreads = 256;
+constexpr int kDurW = 64;     // positions per duration tile
+
+__device__ __forceinline__ size_t rix(const ChainShape &sh, int b, int t) {
+  return ((size_t)b * (sh.T + 1) + t) * sh.C;
+}
+
+__device__ __forceinline__ bool valid_len(const ChainShape &sh, int L) { return L >= 1 && L <= sh.T; }
+
+}  // namespace
+
+// ------------------------------------------------------------ coverage
+// Tiles of R x J positions (R = kCovThreads / C rows of threads, thread
+// (r, c) owns J consecutive positions of label c), as in the score scan.
+// delta[t,c] = E_start[t,c] - E_end[t,c] (E_end[0] = 0), float64-accurate:
+// the coverage is their running sum over the whole sequence.
+__device__ __forceinline__ double cov_delta(const PostArgs &pa, const ChainShape &sh, int b,
+                                            int t, int c, double logZ) {
+  const size_t i = rix(sh, b, t) + c;
+  double d = exp(pa.row_u[i] + pa.row_v[i] - logZ);
+  if (t >= 1) d -= exp(pa.row_a[i] + pa.row_b[i] - logZ);
+  return d;
+}
+
+__global__ __launch_bounds__(kCovThreads) void k_cov_partial(ChainShape sh, PostArgs pa,
+                                                             int ntile) {
+  __shared__ double red1[kCovThreads], red2[kCovThreads];
+  const int tile = blockIdx.x, b = blockIdx.y;
+  const int C = sh.C, R = kCovThreads / C, tid = threadIdx.x;
+  const int c = tid % C, r = tid / C;
+  const int L = pa.lengths[b];
+  double s1 = 0.0, s2 = 0.0;
+  if (r < R && valid_len(sh, L)) {
+    const double logZ = pa.logz[b];
+    const int t0 = tile * R * kCovJ + r * kCovJ;
+    for (int j = 0; j < kCovJ; ++j) {
+      const int t = t0 + j;
+      if (t >= L) break;
+      const double d = cov_delta(pa, sh, b, t, c, logZ);
+      s1 += d;
+      s2 += d * (double)(L - t);  // sum_{i<L} mu[i] = sum_t delta[t] (L - t)
+    }
+  }
+  red1[tid] = s1;
+  red2[tid] = s2;
+  __syncthreads();
+  if (tid < C) {
+    double a1 = 0.0, a2 = 0.0;
+    for (int q = 0; q < R; ++q) {
+      a1 += red1[q * C + tid];
+      a2 += red2[q * C + tid];
+    }
+    const size_t o = ((size_t)b * ntile + tile) * C + tid;
+    pa.cov_part[o] = a1;
+    pa.cov_part2[o] = a2;
+  }
+}
+
+// Exclusive prefix over tiles per (b, c) and the mean coverage.
+__global__ void k_cov_anchor(ChainShape sh, PostArgs pa, int ntile) {
+  const int b = blockIdx.x;
+  const int L = pa.lengths[b];
+  for (int c = threadIdx.x; c < sh.C; c += blockDim.x) {
+    double run = 0.0, tot2 = 0.0;
+    for (int i = 0; i < ntile; ++i) {
+      const size_t o = ((size_t)b * ntile + i) * sh.C + c;
+      pa.cov_anchor[o] = run;
+      run += pa.cov_part[o];
+      tot2 += pa.cov_part2[o];
+    }
+    pa.cov_mean[(size_t)b * sh.C + c] = valid_len(sh, L) ? tot2 / (double)L : 0.0;
+  }
+}
+
+__global__ __launch_bounds__(kCovThreads) void k_cov_write(ChainShape sh, PostArgs pa, int ntile) {
+  __shared__ double runs[kCovThreads];
+  const int tile = blockIdx.x, b = blockIdx.y;
+  const int C = sh.C, R = kCovThreads / C, tid = threadIdx.x;
+  const int c = tid % C, r = tid / C;
+  const int L = pa.lengths[b];
+  const bool ok = valid_len(sh, L);
+  const double logZ = ok ? pa.logz[b] : 0.0;
+  const int t0 = tile * R * kCovJ + r * kCovJ;
+  double own = 0.0;
+  if (r < R && ok) {
+    for (int j = 0; j < kCovJ; ++j) {
+      const int t = t0 + j;
+      if (t >= L) break;
+      own += cov_delta(pa, sh, b, t, c, logZ);
+    }
+  }
+  runs[tid] = own;
+  __syncthreads();
+  if (r >= R) return;
+  double mu = 0.0, mean = 0.0, w = 1.0;
+  if (ok) {
+    mu = pa.cov_anchor[((size_t)b * ntile + tile) * C + c];
+    for (int q = 0; q < r; ++q) mu += runs[q * C + c];
+    mean = sh.center ? pa.cov_mean[(size_t)b * C + c] : 0.0;
+    w = pa.grad_logz ? (double)pa.grad_logz[b] : 1.0;
+  }
+  for (int j = 0; j < kCovJ; ++j) {
+    const int t = t0 + j;
+    if (t >= sh.T) break;
+    float m_out = 0.f, g_out = 0.f;
+    if (ok && t < L) {
+      mu += cov_delta(pa, sh, b, t, c, logZ);
+      m_out = (float)mu;
+      g_out = (float)(w * (mu - mean));
+    }
+    const size_t o = ((size_t)b * sh.T + t) * C + c;
+    pa.grad_emissions[o] = g_out;
+    if (pa.marginals) pa.marginals[o] = m_out;
+  }
+}
+
+// ---------------------------------------------------------- transitions
+// X[c',c] = sum_{t=1}^{L-1} exp(alpha[t,c'] + v[t,c] - logZ) as an exp-space
+// GEMM over positions: a[t,c'] = exp(alpha[t,c'] - m_t) and
+// g[t,c] = exp(v[t,c] + m_t - logZ), m_t the largest alpha of the block's
+// rows (a <= 1, and g <= exp(-min trans): no overflow).  One workgroup per
+// (64 x 64 output tile, sequence, position segment); each thread owns a
+// 4 x 4 block of the tile.
+__global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs pa, int tseg,
+                                                        int nseg) {
+  __shared__ double ta[kTxRows][kTxTile];
+  __shared__ double tg[kTxRows][kTxTile];
+  __shared__ double tm[kTxRows];
+  const int ntc = (sh.C + kTxTile - 1) / kTxTile;
+  const int ti = blockIdx.x / ntc, tj = blockIdx.x % ntc;  // rows c' / columns c
+  const int b = blockIdx.y / nseg, seg = blockIdx.y % nseg;
+  const int C = sh.C, tid = threadIdx.x;
+  const int L = pa.lengths[b];
+  const int ci0 = ti * kTxTile, cj0 = tj * kTxTile;
+  const int bi = tid / (kTxTile / 4), bj = tid % (kTxTile / 4);  // 16 x 16 thread grid
+  double acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+  int tbeg = 1 + seg * tseg, tend = tbeg + tseg;
+  if (!valid_len(sh, L)) tend = tbeg;
+  if (tend > L) tend = L;  // transitions at 1 <= t < L
+  const double logZ = valid_len(sh, L) ? pa.logz[b] : 0.0;
+  for (int r0 = tbeg; r0 < tend; r0 += kTxRows) {
+    const int nr = min(kTxRows, tend - r0);
+    __syncthreads();
+    for (int i = tid; i < kTxRows * kTxTile; i += kTxThreads) {
+      const int rr = i / kTxTile, cc = i % kTxTile;
+      const bool in = rr < nr && ci0 + cc < C;
+      ta[rr][cc] = in ? pa.row_a[rix(sh, b, r0 + rr) + ci0 + cc] : -__builtin_huge_val();
+    }
+    __syncthreads();
+    if (tid < kTxRows) {
+      double m = -__builtin_huge_val();
+      for (int cc = 0; cc < kTxTile; ++cc) m = fmax(m, ta[tid][cc]);
+      tm[tid] = m;
+    }
+    __syncthreads();
+    for (int i = tid; i < kTxRows * kTxTile; i += kTxThreads) {
+      const int rr = i / kTxTile, cc = i % kTxTile;
+      const bool ina = rr < nr && ci0 + cc < C;
+      const bool ing = rr < nr && cj0 + cc < C;
+      const double m = tm[rr];
+      ta[rr][cc] = ina ? exp_wide(ta[rr][cc] - m) : 0.0;
+      tg[rr][cc] = ing ? exp_wide(pa.row_v[rix(sh, b, r0 + rr) + cj0 + cc] + m - logZ) : 0.0;
+    }
+    __syncthreads();
+    for (int rr = 0; rr < nr; ++rr) {
+      double a[4], g[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        a[x] = ta[rr][4 * bi + x];
+        g[x] = tg[rr][4 * bj + x];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], g[y], acc[x][y]);
+    }
+  }
+  double *out = pa.tx_part + ((size_t)b * nseg + seg) * C * C;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int cp = ci0 + 4 * bi + x, c = cj0 + 4 * bj + y;
+      if (cp < C && c < C) out[(size_t)cp * C + c] = acc[x][y];
+    }
+}
+
+// ------------------------------------------------------------ durations
+// D[k,c] = sum_s exp(a[s,c] + b[s+k,c] + dur[k-1,c]) with
+// a[s,c] = u[s,c] - S[s,c] and b[e,c] = S[e,c] + beta[e,c] - logZ, for
+// s + k <= L.  One workgroup per (label group of up to 16, lag group of up
+// to kDurLags lags, sequence, span of position tiles); thread (label cl, lag
+// block kb) owns KB consecutive lags and keeps b[s+k0 .. s+k0+KB-1] in a
+// sliding register window, so each position costs one LDS read of a and one
+// of b.  LDS: a for the tile's positions, b for the ends its lags reach.
+constexpr int kDurLags = 512;
+
+template <int KB>
+__global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs pa, int span,
+                                                       int nspan, int npg) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int C = sh.C, K = sh.K, tid = threadIdx.x;
+  const int cg = blockIdx.x / npg, pg = blockIdx.x % npg;
+  const int b = blockIdx.y / nspan, sp = blockIdx.y % nspan;
+  const int c0 = cg * 16, CG = min(16, C - c0);
+  const int klo = 1 + pg * kDurLags, khi = min(K, (pg + 1) * kDurLags);  // lags [klo, khi]
+  const int cl = tid % CG, kb = tid / CG;
+  const int k0 = klo + kb * KB;
+  const bool act = tid < CG * (kDurThreads / CG) && k0 <= khi;
+  const int c = c0 + cl;
+  const int L = pa.lengths[b];
+  double *sa = reinterpret_cast<double *>(lds);  // [kDurW][16]
+  double *sb = sa + (size_t)kDurW * 16;          // [kDurW + kDurLags][16], index e - s0 - klo
+  double acc[KB], dk[KB];
+#pragma unroll
+  for (int j = 0; j < KB; ++j) {
+    acc[j] = 0.0;
+    const int k = k0 + j;
+    dk[j] = (act && k <= khi) ? (double)pa.dur[(size_t)(k - 1) * C + c] : 0.0;
+  }
+  if (valid_len(sh, L)) {
+    const double logZ = pa.logz[b];
+    const double *Sb = pa.S + (size_t)b * (sh.T + 1) * C;
+    const int sbeg = sp * span * kDurW;
+    const int send = min(sbeg + span * kDurW, L);  // segment starts s < L
+    for (int s0 = sbeg; s0 < send; s0 += kDurW) {
+      const int ns = min(kDurW, send - s0);
+      // ends e in [s0 + klo, min(s0 + ns - 1 + khi, L)]
+      const int ne = min(ns - 1 + khi - klo + 1, L - s0 - klo + 1);
+      __syncthreads();
+      for (int i = tid; i < ns * CG; i += kDurThreads) {
+        const int ss = i / CG, cc = i % CG;
+        const size_t ri = rix(sh, b, s0 + ss) + c0 + cc;
+        sa[ss * 16 + cc] = pa.row_u[ri] - Sb[(size_t)(s0 + ss) * C + c0 + cc];
+      }
+      for (int i = tid; i < ne * CG; i += kDurThreads) {
+        const int ee = i / CG, cc = i % CG;
+        const int e = s0 + klo + ee;
+        const size_t ri = rix(sh, b, e) + c0 + cc;
+        sb[ee * 16 + cc] = (Sb[(size_t)e * C + c0 + cc] + pa.row_b[ri]) - logZ;
+      }
+      __syncthreads();
+      if (act) {
+        // window w[j] = b[s + k0 + j], index (s - s0) + (k0 - klo) + j
+        const int kofs = k0 - klo;
+        double w[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          const int ee = kofs + j;
+          w[j] = ee < ne ? sb[ee * 16 + cl] : -__builtin_huge_val();
+        }
+        for (int ss = 0; ss < ns; ++ss) {
+          const double av = sa[ss * 16 + cl];
+#pragma unroll
+          for (int j = 0; j < KB; ++j) acc[j] += exp_wide(av + w[j] + dk[j]);
+#pragma unroll
+          for (int j = 0; j < KB - 1; ++j) w[j] = w[j + 1];
+          const int ee = ss + 1 + kofs + KB - 1;
+          w[KB - 1] = ee < ne ? sb[ee * 16 + cl] : -__builtin_huge_val();
+        }
+      }
+    }
+  }
+  if (act) {
+    double *out = pa.dur_part + ((size_t)b * nspan + sp) * K * C;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int k = k0 + j;
+      if (k <= khi) out[(size_t)(k - 1) * C + c] = acc[j];
+    }
+  }
+}
+
+// ------------------------------------------------------------ reductions
+// grad_trans = exp(trans) * sum_b w_b sum_seg X;  grad_dur = sum_b w_b sum_span D.
+__global__ void k_post_reduce(ChainShape sh, PostArgs pa, int nseg, int nspan) {
+  const int C = sh.C, K = sh.K;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nx = C * C, ng = K * C;
+  if (e >= nx + ng) return;
+  double acc = 0.0;
+  for (int b = 0; b < sh.B; ++b) {
+    const int L = pa.lengths[b];
+    if (!valid_len(sh, L)) continue;
+    const double w = pa.grad_logz ? (double)pa.grad_logz[b] : 1.0;
+    double sb = 0.0;
+    if (e < nx) {
+      for (int j = 0; j < nseg; ++j) sb += pa.tx_part[((size_t)b * nseg + j) * nx + e];
+    } else {
+      for (int j = 0; j < nspan; ++j) sb += pa.dur_part[((size_t)b * nspan + j) * ng + (e - nx)];
+    }
+    acc += w * sb;
+  }
+  if (e < nx)
+    pa.grad_trans[e] = (float)(acc * exp((double)pa.trans[e]));
+  else
+    pa.grad_dur[e - nx] = (float)acc;
+}
+
+// ------------------------------------------------------------ launch
+void post_geometry(const ChainShape &sh, PostGeom &g) {
+  const int R = kCovThreads / sh.C;
+  g.cov_ntile = (sh.T + R * kCovJ - 1) / (R * kCovJ);
+  g.tx_seg = 512;
+  g.tx_nseg = (sh.T + g.tx_seg - 1) / g.tx_seg;
+  g.dur_span = 8;  // tiles of kDurW positions per workgroup
+  g.dur_nspan = (sh.T + g.dur_span * kDurW - 1) / (g.dur_span * kDurW);
+  // lag blocks of KB: the smallest power of two >= 4 with CG x ceil(lags / KB) <= threads
+  const int cg = sh.C < 16 ? sh.C : 16;
+  const int lags = sh.K < kDurLags ? sh.K : kDurLags;
+  g.dur_kb = 4;
+  while (g.dur_kb < 32 && cg * ((lags + g.dur_kb - 1) / g.dur_kb) > kDurThreads) g.dur_kb *= 2;
+  g.dur_npg = (sh.K + kDurLags - 1) / kDurLags;
+  g.dur_lds = (size_t)(kDurW + kDurW + lags) * 16 * 8;
+}
+
+hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream_t st) {
+  PostGeom g;
+  post_geometry(sh, g);
+  hipLaunchKernelGGL(k_cov_partial, dim3(g.cov_ntile, sh.B), dim3(kCovThreads), 0, st, sh, pa,
+                     g.cov_ntile);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_cov_anchor, dim3(sh.B), dim3(256), 0, st, sh, pa, g.cov_ntile);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_cov_write, dim3(g.cov_ntile, sh.B), dim3(kCovThreads), 0, st, sh, pa,
+                     g.cov_ntile);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ntc = (sh.C + kTxTile - 1) / kTxTile;
+  hipLaunchKernelGGL(k_trans_x, dim3(ntc * ntc, sh.B * g.tx_nseg), dim3(kTxThreads), 0, st, sh,
+                     pa, g.tx_seg, g.tx_nseg);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ncg = (sh.C + 15) / 16;
+  const dim3 gd(ncg * g.dur_npg, sh.B * g.dur_nspan);
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void *)k_dur_x<4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    (void)hipFuncSetAttribute((const void *)k_dur_x<8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    (void)hipFuncSetAttribute((const void *)k_dur_x<16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    (void)hipFuncSetAttribute((const void *)k_dur_x<32>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    (void)hipGetLastError();
+    attr = true;
+  }
+  switch (g.dur_kb) {
+    case 4: hipLaunchKernelGGL(k_dur_x<4>, gd, dim3(kDurThreads), g.dur_lds, st, sh, pa, g.dur_span, g.dur_nspan, g.dur_npg); break;
+    case 8: hipLaunchKernelGGL(k_dur_x<8>, gd, dim3(kDurThreads), g.dur_lds, st, sh, pa, g.dur_span, g.dur_nspan, g.dur_npg); break;
+    case 16: hipLaunchKernelGGL(k_dur_x<16>, gd, dim3(kDurThreads), g.dur_lds, st, sh, pa, g.dur_span, g.dur_nspan, g.dur_npg); break;
+    default: hipLaunchKernelGGL(k_dur_x<32>, gd, dim3(kDurThreads), g.dur_lds, st, sh, pa, g.dur_span, g.dur_nspan, g.dur_npg); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_post_reduce(const ChainShape &sh, const PostArgs &pa, hipStream_t st) {
+  PostGeom g;
+  post_geometry(sh, g);
+  const int ne = sh.C * sh.C + sh.K * sh.C;
+  hipLaunchKernelGGL(k_post_reduce, dim3((ne + 255) / 256), dim3(256), 0, st, sh, pa, g.tx_nseg,
+                     g.dur_nspan);
+  return hipGetLastError();
+}
+
+}  // namespace semicrf
