@@ -25,19 +25,35 @@ bool chain_config(int C, int K, ChainShape &sh) {
   for (int i = 0; i < 3; ++i) {
     const int NT = nts[i];
     const int P = NT / C;
-    if (P < 1 || Q * C > NT) continue;
+    // Q * C <= NT: contraction slices never straddle; (Q + 2) * 64 <= NT: at
+    // least two waves hold no row thread (score loader and row writer roles)
+    if (P < 1 || Q * C > NT || (Q + 2) * 64 > NT) continue;
     const int A = (K + P - 1) / P;
     if (A > amax[i]) continue;
     int QT, CS;
     chain_slices(C, NT, QT, CS);
-    if (chain_lds_bytes(C, K, P, QT) > kMaxLds) continue;
-    if (viterbi_lds_bytes(C, K, P, Q) > kMaxLds) continue;
+    if (chain_lds_bytes(C, K, P, QT, 0) > kMaxDynLds) continue;
+    if (viterbi_lds_bytes(C, K, P, Q) > kMaxDynLds) continue;
+    // helper waves: enough row writers for the 2C logs of a step (two per
+    // lane), the rest load scores; a prefetch block of up to 8 positions,
+    // at most kMaxPairs (position, label) pairs per loader lane, in the LDS
+    // left over (below 2 positions the rows load their scores themselves)
+    const int helpers = NT / 64 - Q;
+    int writers = (C + 63) / 64;
+    writers = writers < 1 ? 1 : (writers > helpers - 1 ? helpers - 1 : writers);
+    const int loaders = helpers - writers;
+    int pf = kMaxPairs * 64 * loaders / C;
+    pf = pf > 8 ? 8 : pf;
+    while (pf > 0 && chain_lds_bytes(C, K, P, QT, pf) > kMaxDynLds) --pf;
+    if (pf < 2) pf = 0;
     sh.NT = NT;
     sh.P = P;
     sh.A = A;
     sh.Q = Q;
     sh.QT = QT;
     sh.CS = CS;
+    sh.pf = pf;
+    sh.nload = loaders;
     return true;
   }
   return false;
@@ -52,7 +68,7 @@ bool win_config(int C, int K, ChainShape &sh) {
   const int NT = 256;
   const int P = NT / C;
   const int A = (K + P - 1) / P;
-  if (A > 32 || win_lds_bytes(C, K, P) > kMaxLds) return false;
+  if (A > 32 || win_lds_bytes(C, K, P) > kMaxDynLds) return false;
   sh.NT = NT;
   sh.P = P;
   sh.A = A;
@@ -92,6 +108,11 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
   if (op != SEMICRF_OP_SCAN) {
     lay.S = cv.take(nS * 8);
     lay.nu = cv.take((size_t)B * C * 8);
+  }
+  if (op == SEMICRF_OP_LOGZ || op == SEMICRF_OP_FWD_BWD) {
+    lay.es_p = cv.take(nS * 8);
+    lay.es_m = cv.take(nS * 8);
+    lay.es_n = cv.take(nS * 4);
   }
   lay.tile_sum = cv.take((size_t)B * lay.ntile * C * 8);
   lay.anchor = cv.take((size_t)B * lay.ntile * C * 8);
@@ -175,6 +196,14 @@ P *at(void *ws, size_t off) {
   return reinterpret_cast<P *>(static_cast<unsigned char *>(ws) + off);
 }
 
+Escaled escaled(void *ws, const Layout &lay) {
+  Escaled es;
+  es.ep = at<double>(ws, lay.es_p);
+  es.em = at<double>(ws, lay.es_m);
+  es.n = at<int32_t>(ws, lay.es_n);
+  return es;
+}
+
 PitBufs pit_bufs(void *ws, const Layout &lay, bool bwd) {
   PitBufs pb;
   pb.ck_fwd = at<double>(ws, lay.ck_fwd);
@@ -247,8 +276,8 @@ semicrf_status_t semicrf_cumulative_scores(const float *emissions, const int32_t
   if (!workspace || workspace_bytes < lay.total) return SEMICRF_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  return hip_status(launch_scan(emissions, lengths, B, T, C, sh.center, nu, S,
-                                at<double>(workspace, lay.tile_sum),
+  return hip_status(launch_scan(emissions, lengths, B, T, C, sh.center, nu, S, nullptr,
+                                nullptr, nullptr, at<double>(workspace, lay.tile_sum),
                                 at<double>(workspace, lay.anchor), lay.ntile, st));
 }
 
@@ -265,11 +294,13 @@ semicrf_status_t semicrf_logz_fwd(const float *emissions, const int32_t *lengths
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   double *S = at<double>(workspace, lay.S);
+  const Escaled es = escaled(workspace, lay);
   hipError_t e = launch_scan(emissions, lengths, B, T, C, sh.center, at<double>(workspace, lay.nu),
-                             S, at<double>(workspace, lay.tile_sum),
+                             S, at<double>(workspace, lay.es_p), at<double>(workspace, lay.es_m),
+                             at<int32_t>(workspace, lay.es_n), at<double>(workspace, lay.tile_sum),
                              at<double>(workspace, lay.anchor), lay.ntile, st);
   if (e != hipSuccess) return hip_status(e);
-  e = run_sweeps(sh, trans, dur, S, lengths, pit_bufs(workspace, lay, false),
+  e = run_sweeps(sh, trans, dur, es, lengths, pit_bufs(workspace, lay, false),
                  at<double>(workspace, lay.logz), nullptr, logz, 0, st);
   return hip_status(e);
 }
@@ -299,11 +330,13 @@ semicrf_status_t semicrf_fwd_bwd_timed(const float *emissions, const int32_t *le
   double *S = at<double>(ws, lay.S);
   mark(0);
   hipError_t e = launch_scan(emissions, lengths, B, T, C, sh.center, at<double>(ws, lay.nu), S,
-                             at<double>(ws, lay.tile_sum), at<double>(ws, lay.anchor), lay.ntile,
-                             st);
+                             at<double>(ws, lay.es_p), at<double>(ws, lay.es_m),
+                             at<int32_t>(ws, lay.es_n), at<double>(ws, lay.tile_sum),
+                             at<double>(ws, lay.anchor), lay.ntile, st);
   if (e != hipSuccess) return hip_status(e);
   mark(1);
-  e = run_sweeps(sh, trans, dur, S, lengths, pit_bufs(ws, lay, true), at<double>(ws, lay.logz),
+  e = run_sweeps(sh, trans, dur, escaled(ws, lay), lengths, pit_bufs(ws, lay, true),
+                 at<double>(ws, lay.logz),
                  at<double>(ws, lay.logz_bwd), logz, 1, st);
   if (e != hipSuccess) return hip_status(e);
   mark(2);
@@ -367,8 +400,8 @@ semicrf_status_t semicrf_viterbi(const float *emissions, const int32_t *lengths,
   void *ws = workspace;
   double *S = at<double>(ws, lay.S);
   hipError_t e = launch_scan(emissions, lengths, B, T, C, sh.center, at<double>(ws, lay.nu), S,
-                             at<double>(ws, lay.tile_sum), at<double>(ws, lay.anchor), lay.ntile,
-                             st);
+                             nullptr, nullptr, nullptr, at<double>(ws, lay.tile_sum),
+                             at<double>(ws, lay.anchor), lay.ntile, st);
   if (e != hipSuccess) return hip_status(e);
   e = launch_viterbi(sh, trans, dur, S, lengths, at<uint32_t>(ws, lay.bp),
                      at<double>(ws, lay.vbest), at<int32_t>(ws, lay.vcbest), best_score,

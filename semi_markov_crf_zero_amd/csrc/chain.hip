@@ -27,29 +27,38 @@
 //     float64, R[c] a per-label integer log reference.  The K-way
 //     log-sum-exp becomes a K-term float64 dot product with
 //     D[k][c] = exp(dur[k-1][c]) (no transcendental per segment cell).
-//     Whenever a new entry leaves [2^-260, 2^260] relative to its reference,
+//   * the whole step stays in exp space, so no transcendental function sits
+//     on the serial path at all.  The score scan supplies exp(+-S[t,c]) split
+//     as a float64 mantissa in [2^-1/2, 2^1/2] times 2^(+-n[t,c]); with the
+//     K-sum ks[c] (relative to 2^R[c])
+//       exp(o[t,c]) = x[c] * 2^E[c],  x = ks * exp(+-S) mantissa, E = R +- n
+//     (an exact integer E); the step's scale 2^B is the largest float64
+//     exponent of these (an integer maximum over the labels), the
+//     contraction input a[c] = x[c] * 2^(E[c] - B) <= 1 is an exact ldexp,
+//       exp(m[t,c]) = d[c] * 2^B,  d = sum_{c'} a[c'] * exp(trans)
+//     and the new entry is d * exp(-+S) mantissa * 2^(B -+ n - R), again an
+//     exact power-of-two scaling.  Every operation on the path is a float64
+//     multiply-add or an exact scaling, so the recursion carries no error
+//     beyond float64 rounding of products and sums, whatever the length.
+//   * whenever a new entry leaves [2^-260, 2^260] relative to its reference,
 //     the label's column is rescaled by an exact power of two (v_ldexp_f64)
 //     and R[c] moves by that exponent.  The recurrence guarantees
 //     g[t] >= g[t-k] + trans[c,c] + dur[k-1,c] (and the mirror for h), so
 //     older ring entries never exceed the newest by more than a
 //     parameter-bounded factor, and the rescale keeps every entry in float64
 //     range.
-//   * the log values themselves grow linearly along the sequence (~5e6 at a
-//     million positions, where a float64 holds only ~1e-9 absolute).  Each
-//     step therefore runs relative to base*ln2, base = label 0's integer
-//     reference: only small numbers and small integer differences R - base
-//     enter the recursion, so no rounding of a large number accumulates.
-//     Absolute alpha/u/beta (formed once, for the posterior exponents) and
-//     log Z carry a single rounding each.
+//   * the waves specialise, each running its own copy of the step loop with
+//     the same barriers: the row waves do the recursion; loader waves
+//     prefetch the split scores of the next block of positions into LDS
+//     (their loop issues only loads, consumed a block later); writer waves
+//     take the per-position log rows (alpha, u / v, beta: log x + E ln2 and
+//     log d + B ln2, a single rounding each) one step behind from values
+//     staged in LDS (their loop issues only stores).  So neither a
+//     global-memory access nor a logarithm sits on the serial path.
 //   * the transition contraction is an exp-space matrix-vector product with
-//     exp(trans) held in registers (fp32), max-shifted per row.
-//   * one workgroup per chain; the forward and the backward chain of every
-//     sequence run concurrently (they are independent).  The marginal pass is
-//     chunk-parallel: one workgroup per (sequence, checkpoint interval)
-//     recomputes alpha from the forward checkpoint and beta from the backward
-//     checkpoint and accumulates the posteriors.
-//   * parameter-gradient partials are per chunk and reduced in a fixed order
-//     in float64 (deterministic; no floating-point atomics).
+//     exp(trans) held in registers, split over the thread rows.
+//   * one workgroup per (direction, sequence, checkpoint interval); the
+//     intervals are swept concurrently and stitched by pit.hip.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -60,11 +69,12 @@
 
 namespace semicrf {
 
-constexpr double kRebaseNats = 180.0;  // ~2^260
+constexpr int kRebaseExp = 260;  // rebase bound, log2 units
 
 struct Smem {
-  double *ring, *part, *orow, *refs, *scal, *erow, *dotp;
-  int *shiftn;
+  double *ring, *part, *erow, *scal, *dotp, *stg;
+  double *efx, *efy;  // split scores of two prefetch blocks [2][pf][C]
+  int *en, *shiftn;
 };
 
 __device__ __forceinline__ Smem carve(unsigned char *base, const ChainShape &s) {
@@ -72,11 +82,13 @@ __device__ __forceinline__ Smem carve(unsigned char *base, const ChainShape &s) 
   size_t off = 0;
   m.ring = reinterpret_cast<double *>(base + off); off += (size_t)s.K * s.C * 8;
   m.part = reinterpret_cast<double *>(base + off); off += (size_t)s.P * s.C * 8;
-  m.orow = reinterpret_cast<double *>(base + off); off += (size_t)s.C * 8;
-  m.refs = reinterpret_cast<double *>(base + off); off += (size_t)s.C * 8;
-  m.scal = reinterpret_cast<double *>(base + off); off += 8 * 8;
   m.erow = reinterpret_cast<double *>(base + off); off += (size_t)s.C * 8;
+  m.scal = reinterpret_cast<double *>(base + off); off += 8 * 8;
   m.dotp = reinterpret_cast<double *>(base + off); off += (size_t)s.QT * s.C * 8;
+  m.stg = reinterpret_cast<double *>(base + off); off += (size_t)2 * (3 * s.C + 1) * 8;
+  m.efx = reinterpret_cast<double *>(base + off); off += (size_t)2 * s.pf * s.C * 8;
+  m.efy = reinterpret_cast<double *>(base + off); off += (size_t)2 * s.pf * s.C * 8;
+  m.en = reinterpret_cast<int *>(base + off); off += (size_t)2 * s.pf * s.C * 4;
   m.shiftn = reinterpret_cast<int *>(base + off);
   return m;
 }
@@ -162,29 +174,27 @@ __device__ __forceinline__ double ksum(const Regs<AMAX, TRMAX, DT> &r, const Sme
   return s;
 }
 
-// Max over the C row values (row threads hold `v`).  All threads call.
-__device__ __forceinline__ double row_max(double v, bool is_row, const ChainShape &sh,
-                                          const Smem &sm) {
-  double x = is_row ? v : -__builtin_huge_val();
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmax(x, __shfl_xor(x, off));
-  if (sh.C <= 64) return x;  // all row threads are in wave 0
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0 && w < sh.Q) sm.scal[w] = x;
+// Maximum over the row threads of an int (others pass kNoExp).  All threads
+// call; the result is meaningful on the row waves.
+__device__ __forceinline__ int rows_max_i(int v, const ChainShape &sh, const Smem &sm) {
+  const int w = threadIdx.x >> 6;
+  const int x = w < sh.Q ? wave_max_i(v) : kNoExp;
+  if (sh.Q == 1) return x;  // all row threads are in wave 0
+  int *si = reinterpret_cast<int *>(sm.scal);
+  if ((threadIdx.x & 63) == 0 && w < sh.Q) si[w] = x;
   __syncthreads();
-  double m = sm.scal[0];
-  for (int i = 1; i < sh.Q; ++i) m = fmax(m, sm.scal[i]);
+  int m = si[0];
+  for (int i = 1; i < sh.Q; ++i) m = max(m, si[i]);
   return m;
 }
 
-// Contraction: row thread c receives M + log(sum_{c'} e[c'] * W[c'][c]),
-// summed in float64 (any per-step rounding here would accumulate along the
-// chain).  Slice partials meet in LDS and the row thread adds them in a
-// fixed order.  Requires sm.erow written and a barrier before the call.
-// All threads call.
+// Contraction: row thread c receives sum_{c'} e[c'] * W[c'][c] in float64
+// (any per-step rounding here would accumulate along the chain).  Slice
+// partials meet in LDS and the row thread adds them in a fixed order.
+// Requires sm.erow written and a barrier before the call.  All threads call.
 template <int AMAX, int TRMAX, typename DT>
 __device__ __forceinline__ double contract(const Regs<AMAX, TRMAX, DT> &r, const Smem &sm,
-                                           const ChainShape &sh, double M) {
+                                           const ChainShape &sh) {
   using WT = typename Regs<AMAX, TRMAX, DT>::WT;
   double dp = 0.0;
 #pragma unroll
@@ -207,25 +217,22 @@ __device__ __forceinline__ double contract(const Regs<AMAX, TRMAX, DT> &r, const
       for (int q = 0; q < sh.QT; ++q) dp += sm.dotp[q * sh.C + threadIdx.x];
     }
   }
-  return M + log(dp);
+  return dp;
 }
 
-// Row thread c inserts the entry for position t, given as d = entry minus
-// its log reference R*ln2 (R an exact integer), and decides an exact
-// power-of-two rebase of its column.  Returns true if the column must be
-// rescaled by 2^-n (n in sm.shiftn[c]).
+// Row thread c inserts the entry for position t, y * 2^s relative to its
+// reference 2^R (y > 0, s an exact integer), and decides an exact
+// power-of-two rebase of its column: an entry outside
+// [2^-kRebaseExp, 2^kRebaseExp] moves R by its exponent.  Returns true if
+// the column must be rescaled by 2^-n (n in sm.shiftn[c]).
 __device__ __forceinline__ bool insert_entry(const Smem &sm, const ChainShape &sh, int t,
-                                             double d, int &R) {
+                                             double y, int s, int &R) {
   const int c = threadIdx.x;
-  int n = 0;
-  if (fabs(d) > kRebaseNats) {
-    n = (int)rint(d * kLog2e);
-    R += n;
-    d -= (double)n * kLn2;
-  }
+  const int ey = exponent_of(y) + s;
+  const int n = (ey > kRebaseExp || ey < -kRebaseExp) ? ey : 0;
+  R += n;
   sm.shiftn[c] = n;
-  sm.refs[c] = (double)R;
-  sm.ring[(t % sh.K) * sh.C + c] = exp(d);
+  sm.ring[(t % sh.K) * sh.C + c] = ldexp(y, s - n);
   return n != 0;
 }
 
@@ -271,20 +278,37 @@ __device__ __forceinline__ void load_ckpt(const double *__restrict__ src, const 
     R = (int)src[n + threadIdx.x];
     o = src[n + sh.C + threadIdx.x];
     m = src[n + 2 * sh.C + threadIdx.x];
-    sm.refs[threadIdx.x] = (double)R;
   }
   __syncthreads();
 }
 
-// Sum over labels of exp(o - M) for the log normaliser at a sequence end.
-__device__ __forceinline__ double row_lse(double o, bool is_row, const ChainShape &sh,
-                                          const Smem &sm) {
-  const double M = row_max(o, is_row, sh, sm);
-  if (is_row) sm.orow[threadIdx.x] = exp(o - M);
-  __syncthreads();
-  double s = 0.0;
-  for (int c = 0; c < sh.C; ++c) s += sm.orow[c];
-  return M + log(s);
+// Split scores of position t for label c (row / chain lanes; other lanes
+// read label 0), in the order the direction uses them: fx multiplies the
+// K-sum (exp(S) forward, exp(-S) backward), fy the contraction (the other
+// one), n is the exponent (its sign is applied where it is used).  t is
+// clamped into [0, T], so every lane loads from a valid address and no
+// select touches the loaded values: the loads stay in flight until their
+// first use several positions later (a prefetch).
+__device__ __forceinline__ void es_get(const Escaled &es, size_t ob, int t, int T, int C, int c,
+                                       bool fwd, double &fx, double &fy, int &n) {
+  const int tc = t < 0 ? 0 : (t > T ? T : t);
+  const size_t i = ob + (size_t)tc * C + (c < C ? c : 0);
+  fx = (fwd ? es.ep : es.em)[i];
+  fy = (fwd ? es.em : es.ep)[i];
+  n = es.n[i];
+}
+
+// Log rows from a step's staged values (stg: x[C], E[C], d[C], B), rows
+// [lo, hi) of the 2C (alpha / v first, then u / beta), shared by threads
+// [first, first + nthr).
+__device__ __forceinline__ void stage_rows(const double *stg, int C, double *r1, double *r2,
+                                           int lo, int hi, int first, int nthr) {
+  for (int i = lo + (int)threadIdx.x - first; i < hi; i += nthr) {
+    if (i < C)
+      r1[i] = log(stg[i]) + stg[C + i] * kLn2;
+    else
+      r2[i - C] = log(stg[C + i]) + stg[3 * C] * kLn2;
+  }
 }
 
 // ---------------------------------------------------------------- sweeps
@@ -295,10 +319,147 @@ __device__ __forceinline__ double row_lse(double o, bool is_row, const ChainShap
 // iteration 0 (exact at the sequence end the chain starts from, neutral
 // elsewhere), re-read afterwards.  The chunk that ends its chain yields log Z
 // in its own frame; every other chunk writes its end state.
+// Wave roles of the LDS-ring engine: row waves (w < Q), loader waves
+// (Q <= w < Q + nload), writer waves (the rest).
+enum ChainRole { kRowRole = 0, kLoadRole = 1, kWriteRole = 2 };
+
+// Loader: the split scores of the prefetch block starting at step s (steps
+// s .. s+pf-1, positions tstart + isig*step) for every label, pf*C pairs
+// over the loader lanes, at most kMaxPairs each.
+struct PfLoad {
+  double fx[kMaxPairs], fy[kMaxPairs];
+  int n[kMaxPairs];
+
+  __device__ __forceinline__ void issue(const Escaled &es, size_t ob, const ChainShape &sh,
+                                        int tstart, int isig, int s, int lid, bool fwd) {
+#pragma unroll
+    for (int k = 0; k < kMaxPairs; ++k) {
+      const int q = lid + 64 * sh.nload * k;  // pair (i, c) = (q / C, q % C)
+      const bool in = q < sh.pf * sh.C;
+      const int i = in ? q / sh.C : 0, c = in ? q % sh.C : 0;
+      es_get(es, ob, tstart + isig * (s + i), sh.T, sh.C, c, fwd, fx[k], fy[k], n[k]);
+    }
+  }
+
+  __device__ __forceinline__ void put(const Smem &sm, const ChainShape &sh, int buf, int lid) const {
+#pragma unroll
+    for (int k = 0; k < kMaxPairs; ++k) {
+      const int q = lid + 64 * sh.nload * k;
+      if (q < sh.pf * sh.C) {
+        const int o = buf * sh.pf * sh.C + q;  // [buf][i][c], q = i*C + c
+        sm.efx[o] = fx[k];
+        sm.efy[o] = fy[k];
+        sm.en[o] = n[k];
+      }
+    }
+  }
+};
+
+// The step loop of one role.  Per step: K-sum share, barrier, row phase
+// (label maximum, with a barrier when the rows span several waves),
+// barrier, contraction (a barrier when it is split), insertion, barrier
+// (with the rebase vote).  The row threads leave log Z (tail chunk) or the
+// end-state o / m in lz / o_end / m_end.
+template <int ROLE, int NT, int AMAX, int TRMAX, typename DT>
+__device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
+                                           const Regs<AMAX, TRMAX, DT> &r, const Escaled &es,
+                                           size_t ob, int p0, int p1, int tstart, bool fwd,
+                                           bool tail, bool rows, double *row1, double *row2,
+                                           int &R, double &o_end, double &m_end, double &lz) {
+  const int tid = threadIdx.x, C = sh.C;
+  const bool is_row = tid < C;
+  const int isig = fwd ? 1 : -1;
+  const int pf = sh.pf;
+  const int lid = tid - 64 * sh.Q;  // loader lane
+  const int wfirst = 64 * (sh.Q + sh.nload), wn = NT - wfirst;  // writer threads
+  const int nsteps = p1 - p0;  // forward t = p0+1..p1, backward t = p1-1..p0
+  PfLoad ld;
+  for (int step = 1; step <= nsteps; ++step) {
+    const int t = fwd ? p0 + step : p1 - step;
+    const int i = pf > 0 ? (step - 1) % pf : 0;  // position in the prefetch block
+    const int buf = pf > 0 ? ((step - 1) / pf) & 1 : 0;
+    double fx = 0.0, fy = 0.0;
+    int nq = 0;
+    if (ROLE == kRowRole && is_row) {
+      if (pf > 0) {
+        const int o = (buf * pf + i) * C + tid;
+        fx = sm.efx[o];
+        fy = sm.efy[o];
+        nq = isig * sm.en[o];
+      } else {
+        int n;
+        es_get(es, ob, t, sh.T, C, tid, fwd, fx, fy, n);
+        nq = isig * n;
+      }
+    }
+    const bool next_blk = pf > 0 && step - 1 - i + pf < nsteps;  // a block follows this one
+    if (ROLE == kLoadRole && i == 0 && next_blk)
+      ld.issue(es, ob, sh, tstart, isig, step + pf, lid, fwd);
+    double nogd[AMAX];
+    const double s = r.kp < sh.P ? ksum<false>(r, sm, sh, t, fwd, nogd, 0.0) : 0.0;
+    if (r.kp < sh.P) sm.part[r.kp * C + r.kc] = s;
+    __syncthreads();
+    const bool last = step == nsteps;
+    const bool lz_step = last && tail;
+    const double *sprev = sm.stg + ((step - 1) & 1) * (3 * C + 1);
+    const size_t tprev = (size_t)(t - isig) * C;
+    // exp(o) = x * 2^E, o = alpha (forward) or v (backward)
+    double x = 0.0;
+    int E = 0;
+    if (ROLE == kRowRole && is_row) {
+      double sum = 0.0;
+      for (int p = 0; p < sh.P; ++p) sum += sm.part[p * C + tid];
+      x = sum * fx;
+      E = R + nq;
+    }
+    if (ROLE == kWriteRole && rows && step > 1)
+      stage_rows(sprev, C, row1 + tprev, row2 + tprev, 0, C, wfirst, wn);
+    const int Bm = rows_max_i((is_row && x > 0.0) ? E + exponent_of(x) : kNoExp, sh, sm);
+    double *stg = sm.stg + (step & 1) * (3 * C + 1);
+    if (ROLE == kRowRole && is_row) {
+      stg[tid] = x;
+      stg[C + tid] = (double)E;
+      sm.erow[tid] = ldexp(x, E - Bm);  // exp(o) / 2^Bm
+    }
+    __syncthreads();
+    if (lz_step) {
+      if (ROLE == kRowRole && tid == 0) {
+        double z = 0.0;
+        for (int c = 0; c < C; ++c) z += sm.erow[c];
+        lz = (double)Bm * kLn2 + log(z);
+      }
+      if (ROLE == kWriteRole && rows && step > 1)
+        stage_rows(sprev, C, row1 + tprev, row2 + tprev, C, 2 * C, wfirst, wn);
+      break;  // the chain's last step (uniform)
+    }
+    const double d = contract(r, sm, sh);  // exp(m) / 2^Bm, m = u or beta
+    if (ROLE == kWriteRole && rows && step > 1)
+      stage_rows(sprev, C, row1 + tprev, row2 + tprev, C, 2 * C, wfirst, wn);
+    int *vote = reinterpret_cast<int *>(sm.scal) + 8;  // rebase votes of two steps
+    bool need = false;
+    if (ROLE == kRowRole && is_row) {
+      if (tid == 0) vote[(step + 1) & 1] = 0;  // every thread has read it (last step)
+      stg[2 * C + tid] = d;
+      if (tid == 0) stg[3 * C] = (double)Bm;
+      // entry exp(m -+ S) / 2^R = d * fy * 2^(Bm -+ n - R)
+      need = insert_entry(sm, sh, t, d * fy, Bm - nq - R, R);
+      if (need) vote[step & 1] = 1;
+      if (last) {
+        o_end = log(x) + (double)E * kLn2;
+        m_end = log(d) + (double)Bm * kLn2;
+      }
+    }
+    // the next block's scores land in the other buffer before the barrier
+    // that ends this block
+    if (ROLE == kLoadRole && i == pf - 1 && next_blk) ld.put(sm, sh, buf ^ 1, lid);
+    __syncthreads();
+    if (vote[step & 1]) apply_rebase(r, sm, sh, t, fwd);
+  }
+}
+
 template <int NT, int AMAX, int TRMAX, typename DT>
 __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__restrict__ trans,
-                                              const float *__restrict__ dur,
-                                              const double *__restrict__ S,
+                                              const float *__restrict__ dur, Escaled es,
                                               const int32_t *__restrict__ lengths, PitBufs pb,
                                               int iter) {
   extern __shared__ __align__(16) unsigned char lds[];
@@ -319,31 +480,32 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
   Regs<AMAX, TRMAX, DT> r;
   init_regs(r, sh, dur);
   load_trans(r, sh, trans, fwd);
-  const double *Sb = S + (size_t)b * (sh.T + 1) * C;
+  const size_t ob = (size_t)b * (sh.T + 1) * C;
   const size_t cks = ck_stride(C, K);
   double *rec_start = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
   double *rec_end = (fwd ? pb.end_fwd : pb.end_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
-  const double sigma = fwd ? 1.0 : -1.0;
   const int isig = fwd ? 1 : -1;
   const int tstart = fwd ? p0 : p1;
   const bool tail = fwd ? (p1 == L) : (p0 == 0);  // this chunk ends the chain
+  const bool rows = pb.row_a != nullptr;
+  double *row1 = (fwd ? pb.row_a : pb.row_v) + ob;  // alpha / v
+  double *row2 = (fwd ? pb.row_u : pb.row_b) + ob;  // u / beta
 
   int R = 0;
-  double o = 0.0, m = 0.0;
   if (iter == 0) {
     for (int i = tid; i < K * C; i += NT) sm.ring[i] = 0.0;
     __syncthreads();
     const bool exact = fwd ? (jc == 0) : (p1 == L);
     if (exact) {
-      // forward position 0 (u = 0), backward position L (beta = 0)
+      // entry u[0] - S[0] = 0 forward; beta[L] + S[L] = S[L] backward
       if (is_row) {
-        double d = 0.0;  // entry minus R*ln2
+        double v = 1.0;
         if (!fwd) {
-          const double sl = Sb[(size_t)L * C + tid];
-          R = (int)rint(sl * kLog2e);
-          d = sl - (double)R * kLn2;
+          const size_t i = ob + (size_t)L * C + tid;
+          v = es.ep[i];
+          R = es.n[i];
         }
-        sm.ring[(tstart % K) * C + tid] = exp(d);
+        sm.ring[(tstart % K) * C + tid] = v;
       }
     } else {
       // neutral start: every entry of the window (positions inside [0, L]) is 1
@@ -353,54 +515,57 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
         if (q >= 0 && q <= L) sm.ring[(q % K) * C + c] = 1.0;
       }
     }
-    if (is_row) sm.refs[tid] = (double)R;
     __syncthreads();
     // o = NaN marks a neutral start (never accepted by the verification)
     save_ckpt(rec_start, sm, sh, R, exact ? -__builtin_huge_val() : __builtin_nan(""),
               exact ? 0.0 : __builtin_nan(""));
-    if (exact && is_row && pb.row_a)  // u[0] = 0 forward, beta[L] = 0 backward
-      (fwd ? pb.row_u : pb.row_b)[((size_t)b * (sh.T + 1) + tstart) * C + tid] = 0.0;
+    if (exact && is_row && rows)  // u[0] = 0 forward, beta[L] = 0 backward
+      row2[(size_t)tstart * C + tid] = 0.0;
     __syncthreads();
   } else {
-    load_ckpt(rec_start, sm, sh, R, o, m);
+    double o0, m0;
+    load_ckpt(rec_start, sm, sh, R, o0, m0);
   }
+  if (sh.pf > 0) {  // the first block's scores (later blocks: the loader waves)
+    const int npair = min(sh.pf, p1 - p0) * C;
+    for (int q = tid; q < npair; q += NT) {
+      double fx, fy;
+      int n;
+      es_get(es, ob, tstart + isig * (1 + q / C), sh.T, C, q % C, fwd, fx, fy, n);
+      sm.efx[q] = fx;
+      sm.efy[q] = fy;
+      sm.en[q] = n;
+    }
+  }
+  if (tid == 0) {  // rebase votes of the first two steps
+    reinterpret_cast<int *>(sm.scal)[8] = 0;
+    reinterpret_cast<int *>(sm.scal)[9] = 0;
+  }
+  vm_drain();
+  __syncthreads();
 
-  const int nsteps = p1 - p0;  // forward t = p0+1..p1, backward t = p1-1..p0
-  for (int step = 1; step <= nsteps; ++step) {
-    const int t = fwd ? p0 + step : p1 - step;
-    double nogd[AMAX];
-    const double s = r.kp < sh.P ? ksum<false>(r, sm, sh, t, fwd, nogd, 0.0) : 0.0;
-    if (r.kp < sh.P) sm.part[r.kp * C + r.kc] = s;
+  double o_end = 0.0, m_end = 0.0, lz = 0.0;
+  const int w = tid >> 6;
+  if (w < sh.Q)
+    sweep_loop<kRowRole, NT>(sh, sm, r, es, ob, p0, p1, tstart, fwd, tail, rows, row1, row2, R,
+                             o_end, m_end, lz);
+  else if (w < sh.Q + sh.nload)
+    sweep_loop<kLoadRole, NT>(sh, sm, r, es, ob, p0, p1, tstart, fwd, tail, rows, row1, row2, R,
+                              o_end, m_end, lz);
+  else
+    sweep_loop<kWriteRole, NT>(sh, sm, r, es, ob, p0, p1, tstart, fwd, tail, rows, row1, row2, R,
+                               o_end, m_end, lz);
+  if (tail) {
+    if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
+  } else {
+    save_ckpt(rec_end, sm, sh, R, o_end, m_end);
+  }
+  if (rows) {  // rows of the last step (t = p1 forward, p0 backward)
     __syncthreads();
-    // the step runs relative to base*ln2, base = label 0's integer reference
-    const int base = (int)sm.refs[0];
-    const double bl = (double)base * kLn2;
-    o = 0.0;  // alpha (forward) or v (backward) minus bl
-    if (is_row) {
-      double sum = 0.0;
-      for (int p = 0; p < sh.P; ++p) sum += sm.part[p * C + tid];
-      o = sigma * Sb[(size_t)t * C + tid] + (double)(R - base) * kLn2 + log(sum);
-    }
-    const bool last = step == nsteps;
-    if (is_row && pb.row_a)  // per-position rows, in this chunk's frame
-      (fwd ? pb.row_a : pb.row_v)[((size_t)b * (sh.T + 1) + t) * C + tid] = bl + o;
-    if (last && tail) {
-      const double lz = bl + row_lse(o, is_row, sh, sm);
-      if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
-      break;
-    }
-    const double M = row_max(o, is_row, sh, sm);
-    if (is_row) sm.erow[tid] = exp(o - M);
-    __syncthreads();
-    m = contract(r, sm, sh, M);  // u (forward) or beta (backward) minus bl
-    if (is_row && pb.row_a)
-      (fwd ? pb.row_u : pb.row_b)[((size_t)b * (sh.T + 1) + t) * C + tid] = bl + m;
-    bool need = false;
-    if (is_row)
-      need = insert_entry(sm, sh, t,
-                          (m - sigma * Sb[(size_t)t * C + tid]) + (double)(base - R) * kLn2, R);
-    if (__syncthreads_or(need)) apply_rebase(r, sm, sh, t, fwd);
-    if (last) save_ckpt(rec_end, sm, sh, R, bl + o, bl + m);
+    const int nsteps = p1 - p0;
+    const size_t tl = (size_t)(fwd ? p1 : p0) * C;
+    stage_rows(sm.stg + (nsteps & 1) * (3 * C + 1), C, row1 + tl, row2 + tl, 0,
+               tail ? C : 2 * C, 0, NT);
   }
 }
 
@@ -427,12 +592,14 @@ struct ChainKernels {
     }
   }
   static hipError_t sweep(const ChainShape &sh, const float *trans, const float *dur,
-                          const double *S, const int32_t *lengths, const PitBufs &pb,
+                          const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                           int with_bwd, int iter, hipStream_t st) {
-    const size_t lds = chain_lds_bytes(sh.C, sh.K, sh.P, sh.QT);
+    const size_t lds = chain_lds_bytes(sh.C, sh.K, sh.P, sh.QT, sh.pf);
     set_attrs();
+    if (!lds_fits((const void *)k_sweep<NT, AMAX, TRMAX, DT>, lds))
+      return report(hipErrorInvalidConfiguration, "k_sweep (LDS)", sh, lds);
     hipLaunchKernelGGL((k_sweep<NT, AMAX, TRMAX, DT>), dim3((with_bwd ? 2 : 1) * sh.B * sh.nchunk),
-                       dim3(NT), lds, st, sh, trans, dur, S, lengths, pb, iter);
+                       dim3(NT), lds, st, sh, trans, dur, es, lengths, pb, iter);
     return report(hipGetLastError(), "k_sweep", sh, lds);
   }
 };
@@ -462,10 +629,10 @@ struct ChainKernels {
   } while (0)
 
 hipError_t launch_sweep(const ChainShape &sh, const float *trans, const float *dur,
-                        const double *S, const int32_t *lengths, const PitBufs &pb,
+                        const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                         int with_bwd, int iter, hipStream_t st) {
-  if (sh.win) return launch_sweep_w(sh, trans, dur, S, lengths, pb, with_bwd, iter, st);
-  SEMICRF_CHAIN_DISPATCH(sh, sweep(sh, trans, dur, S, lengths, pb, with_bwd, iter, st));
+  if (sh.win) return launch_sweep_w(sh, trans, dur, es, lengths, pb, with_bwd, iter, st);
+  SEMICRF_CHAIN_DISPATCH(sh, sweep(sh, trans, dur, es, lengths, pb, with_bwd, iter, st));
 }
 
 }  // namespace semicrf

@@ -12,13 +12,19 @@
 //     constant, and the window is refilled from the ring once per U steps.
 //     LDS traffic per step drops from K*C*8 bytes to about P*C*8*(1+AMAX/U).
 //   * one "chain wave" (wave 0, lane c = label c) does the per-position
-//     serial part -- log of the K-sum, max, exp, the C x C contraction
-//     (exp(trans) staged in LDS), the new ring entry and the rebase decision
-//     -- with wave-local synchronisation only: two workgroup barriers per
-//     step in total.
-//   * S rows (and, in the backward marginal pass, the alpha/u rows of the
-//     chunk) are prefetched U steps ahead into per-lane register queues, so
-//     no global-memory latency sits on the per-step critical path.
+//     serial part -- the K-sum times exp(+-S), an integer maximum of the
+//     float64 exponents, the C x C contraction (exp(trans) staged in LDS), the
+//     new ring entry and the rebase decision -- with wave-local
+//     synchronisation only: two workgroup barriers per step in total.  No
+//     transcendental function sits on this path (see chain.hip: exp(+-S) come
+//     split from the score scan, every rescaling is an exact power of two).
+//   * the waves specialise (each runs its own copy of the step loop, with
+//     the same barriers): wave 1 prefetches the split scores of the next
+//     block of U positions into LDS (its loop issues only loads, so nothing
+//     waits on them before the block ends), waves 2-3 turn the previous
+//     step's staged values into the per-position log rows (their loop issues
+//     only stores), and the chain wave reads its scores from LDS -- no
+//     global-memory access sits on the per-step critical path.
 //   * an exact power-of-two column rebase (rare) runs as its own barrier-
 //     separated mini-phase that rescales the register windows and the LDS
 //     ring together.
@@ -34,11 +40,13 @@ namespace semicrf {
 
 namespace {
 
-constexpr double kRebaseNatsW = 180.0;  // ~2^260
+constexpr int kRebaseExp = 260;  // rebase bound, log2 units
+constexpr int kWinPB = 8;        // largest unroll block (positions); sizes the score buffers
 
 struct WSmem {
-  double *ring, *part, *qrow, *tr, *erow;
-  int *shiftn, *flag;
+  double *ring, *part, *stg, *tr, *erow;
+  double *efx, *efy;  // split scores of two blocks [2][kWinPB][C]
+  int *shiftn, *flag, *en;
 };
 
 __device__ __forceinline__ int round4(int c) { return (c + 3) & ~3; }
@@ -50,13 +58,17 @@ __device__ __forceinline__ WSmem wcarve(unsigned char *base, const ChainShape &s
   const int C4 = round4(s.C);
   m.ring = reinterpret_cast<double *>(base + off); off += (size_t)s.K * s.C * 8;
   m.part = reinterpret_cast<double *>(base + off); off += (size_t)s.P * s.C * 8;
-  m.qrow = reinterpret_cast<double *>(base + off); off += (size_t)s.C * 8;
+  m.stg = reinterpret_cast<double *>(base + off); off += (size_t)2 * (3 * s.C + 1) * 8;
   off = (off + 15) & ~(size_t)15;
   m.tr = reinterpret_cast<double *>(base + off); off += (size_t)C4 * s.C * 8;
   off = (off + 15) & ~(size_t)15;
   m.erow = reinterpret_cast<double *>(base + off); off += (size_t)C4 * 8;
   m.shiftn = reinterpret_cast<int *>(base + off); off += (size_t)s.C * 4;
-  m.flag = reinterpret_cast<int *>(base + off);
+  m.flag = reinterpret_cast<int *>(base + off); off += 2 * 4;
+  off = (off + 15) & ~(size_t)15;
+  m.efx = reinterpret_cast<double *>(base + off); off += (size_t)2 * kWinPB * s.C * 8;
+  m.efy = reinterpret_cast<double *>(base + off); off += (size_t)2 * kWinPB * s.C * 8;
+  m.en = reinterpret_cast<int *>(base + off);
   return m;
 }
 
@@ -187,35 +199,6 @@ __device__ __forceinline__ double chain_sum(const WSmem &sm, const ChainShape &s
   return sum;
 }
 
-// Row rotation by DPP; lanes whose source would be invalid keep their own
-// value (update_dpp with old = src), so no register is ever left undefined.
-__device__ __forceinline__ float dpp_ror(float v, int ctrl_sel) {
-  const int iv = __builtin_bit_cast(int, v);
-  int r;
-  switch (ctrl_sel) {
-    case 8: r = __builtin_amdgcn_update_dpp(iv, iv, 0x128, 0xf, 0xf, false); break;
-    case 4: r = __builtin_amdgcn_update_dpp(iv, iv, 0x124, 0xf, 0xf, false); break;
-    case 2: r = __builtin_amdgcn_update_dpp(iv, iv, 0x122, 0xf, 0xf, false); break;
-    default: r = __builtin_amdgcn_update_dpp(iv, iv, 0x121, 0xf, 0xf, false); break;
-  }
-  return __builtin_bit_cast(float, r);
-}
-
-// Wave-wide max of a float (all 64 lanes call): row rotations by DPP, then
-// the four row maxima through scalar reads.
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_ror(v, 8));
-  v = fmaxf(v, dpp_ror(v, 4));
-  v = fmaxf(v, dpp_ror(v, 2));
-  v = fmaxf(v, dpp_ror(v, 1));
-  const int iv = __builtin_bit_cast(int, v);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
@@ -227,24 +210,17 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Max-shifted exp-space contraction of the row o (lane c holds o[c]):
-// returns M + log(sum_{c'} exp(o[c'] - M) * tr[c'][c]); e = exp(o - M) and M
-// are returned too.  The shift M only needs to be near the maximum (it
-// cancels), so it is a float32 wave reduction; e, the sum and the log are
-// float64-accurate because their rounding would accumulate along the chain.
+// Exp-space contraction: lane c < C holds a[c] = exp(o[c]) / 2^B (at most
+// 1, the largest >= 1/2) and receives sum_{c'} a[c'] * tr[c'][c] in float64.
 // All 64 lanes of wave 0 call.
 template <int CMAX>
 __device__ __forceinline__ double chain_contract(const WSmem &sm, const ChainShape &sh, int lane,
-                                                 double o, double &e_out, double &M_out) {
+                                                 double a) {
   const int C = sh.C;
-  const bool act = lane < C;
-  const float M = wave_max(act ? (float)o : -__builtin_huge_valf());
-  const double Md = (double)M;
-  const double e = act ? exp(o - Md) : 0.0;
-  if (lane < round4(C)) sm.erow[lane] = e;
+  if (lane < round4(C)) sm.erow[lane] = lane < C ? a : 0.0;
   wave_lds_sync();
   double d0 = 0.0, d1 = 0.0, d2 = 0.0, d3 = 0.0;
-  if (act) {
+  if (lane < C) {
 #pragma unroll
     for (int ci = 0; ci < CMAX; ci += 4) {
       if (ci < C) {
@@ -256,31 +232,22 @@ __device__ __forceinline__ double chain_contract(const WSmem &sm, const ChainSha
     }
   }
   wave_lds_sync();
-  e_out = e;
-  M_out = Md;
-  return Md + log((d0 + d1) + (d2 + d3));
+  return (d0 + d1) + (d2 + d3);
 }
 
-// New ring entry for position t of label `lane`, given as d = entry minus
-// the label's log reference R*ln2 (R an exact integer), and the rebase
-// decision.
+// New ring entry for position t of label `lane`: y * 2^s relative to the
+// label's reference 2^R (y > 0 a float64, s an exact integer).  An entry
+// outside [2^-kRebaseExp, 2^kRebaseExp] moves R by its exponent (rebase:
+// the column's older entries are rescaled by the same power of two).
 __device__ __forceinline__ bool chain_insert(const WSmem &sm, const ChainShape &sh, int lane,
-                                             int t, double d, int &R) {
-  int n = 0;
-  if (fabs(d) > kRebaseNatsW) {
-    n = (int)rint(d * kLog2e);
-    R += n;
-    d -= (double)n * kLn2;
-  }
+                                             int t, double y, int s, int &R) {
+  const int ey = exponent_of(y) + s;
+  const int n = (ey > kRebaseExp || ey < -kRebaseExp) ? ey : 0;
+  R += n;
   sm.shiftn[lane] = n;
-  sm.ring[pos_slot(t, sh.K) * sh.C + lane] = exp(d);
+  sm.ring[pos_slot(t, sh.K) * sh.C + lane] = ldexp(y, s - n);
   return n != 0;
 }
-
-// The chain wave's per-step base: label 0's integer reference.  Each step
-// runs relative to base*ln2 so that only small numbers enter the recursion
-// (absolute log values reach ~5e6 at a million positions).
-__device__ __forceinline__ int chain_base(int R) { return __builtin_amdgcn_readlane(R, 0); }
 
 // Wave-vote the rebase decisions of step t into the flag slot t&1 (lane 0).
 __device__ __forceinline__ void chain_flag(const WSmem &sm, int t, bool rb) {
@@ -312,9 +279,165 @@ __device__ __forceinline__ void wload(const double *__restrict__ src, const WSme
   }
 }
 
-__device__ __forceinline__ double ld_or(const double *p, bool ok) { return ok ? *p : 0.0; }
+// Split scores of position t for label c (row / chain lanes; other lanes
+// read label 0), in the order the direction uses them: fx multiplies the
+// K-sum (exp(S) forward, exp(-S) backward), fy the contraction (the other
+// one), n is the exponent (its sign is applied where it is used).  t is
+// clamped into [0, T], so every lane loads from a valid address and no
+// select touches the loaded values: the loads stay in flight until their
+// first use several positions later (a prefetch).
+__device__ __forceinline__ void es_get(const Escaled &es, size_t ob, int t, int T, int C, int c,
+                                       bool fwd, double &fx, double &fy, int &n) {
+  const int tc = t < 0 ? 0 : (t > T ? T : t);
+  const size_t i = ob + (size_t)tc * C + (c < C ? c : 0);
+  fx = (fwd ? es.ep : es.em)[i];
+  fy = (fwd ? es.em : es.ep)[i];
+  n = es.n[i];
+}
+
+// Per-position log rows from a step's staged values (stg: x[C], E[C], d[C],
+// B): row1 = log x + E ln2 (alpha / v), row2 = log d + B ln2 (u / beta).
+// Threads [first, first + nthr) share the 2C logs.
+__device__ __forceinline__ void stage_rows(const double *stg, int C, double *r1, double *r2,
+                                           bool with2, int first, int nthr) {
+  for (int i = (int)threadIdx.x - first; i < 2 * C; i += nthr) {
+    if (i < C)
+      r1[i] = log(stg[i]) + stg[C + i] * kLn2;
+    else if (with2)
+      r2[i - C] = log(stg[C + i]) + stg[3 * C] * kLn2;
+  }
+}
 
 }  // namespace
+
+// Wave roles of the windowed engine.
+enum WinRole { kChainWave = 0, kLoaderWave = 1, kRowWaves = 2 };
+
+// Loader: the split scores of the block of U steps starting at step s0
+// (positions first + sigma*(s0 + i), i < U) for every label -- U*C
+// (position, label) pairs over the 64 lanes, at most kWinPB*32/64 = 4 each.
+template <int U>
+struct BlockLoad {
+  double fx[(U * 32 + 63) / 64], fy[(U * 32 + 63) / 64];
+  int n[(U * 32 + 63) / 64];
+
+  __device__ __forceinline__ void issue(const Escaled &es, size_t ob, int first, int sigma,
+                                        int s0, int T, int C, int lane, bool fwd) {
+#pragma unroll
+    for (int k = 0; k < (U * 32 + 63) / 64; ++k) {
+      const int q = lane + 64 * k;  // pair (i, c) = (q / C, q % C)
+      const int i = q < U * C ? q / C : 0, c = q < U * C ? q % C : 0;
+      es_get(es, ob, first + sigma * (s0 + i), T, C, c, fwd, fx[k], fy[k], n[k]);
+    }
+  }
+
+  __device__ __forceinline__ void put(const WSmem &sm, int buf, int C, int lane) const {
+#pragma unroll
+    for (int k = 0; k < (U * 32 + 63) / 64; ++k) {
+      const int q = lane + 64 * k;
+      if (q < U * C) {
+        const int o = buf * kWinPB * C + q;  // [buf][i][c], q = i*C + c
+        sm.efx[o] = fx[k];
+        sm.efy[o] = fy[k];
+        sm.en[o] = n[k];
+      }
+    }
+  }
+};
+
+// The step loop of one role (see WinRole).  Per step: K-sum share and
+// publish, barrier, role work, barrier (not after the chain's last step),
+// and the rare rebase mini-phase with its own barrier.  The chain wave
+// leaves log Z (tail chunk) or the end-state o / m in lz / o_end / m_end.
+template <int ROLE, int NT, int AMAX, int U, int CMAX>
+__device__ __forceinline__ void sweep_w_loop(const ChainShape &sh, const WSmem &sm,
+                                             Win<AMAX, U> &win, const Escaled &es, size_t ob,
+                                             int first, int nsteps, int sigma, bool fwd,
+                                             bool tail, bool rows, double *row1, double *row2,
+                                             int lane, bool chain, int &R, double &o_end,
+                                             double &m_end, double &lz) {
+  const int C = sh.C, T = sh.T;
+  double nogd[AMAX];
+  BlockLoad<U> bl;
+  bool done = false;
+  for (int s0 = 0; !done; s0 += U) {
+    const int t0 = first + sigma * s0;
+    const int buf = (s0 / U) & 1;
+    win.fill(sm, sh, t0, sigma);
+    if (ROLE == kLoaderWave && s0 + U < nsteps) bl.issue(es, ob, first, sigma, s0 + U, T, C, lane, fwd);
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      if (!done) {
+        const int step = s0 + i;
+        const int t = t0 + sigma * i;
+        // the chain lanes' scores of this step (LDS, staged a block ahead)
+        double fx = 0.0, fy = 0.0;
+        int nq = 0;
+        if (ROLE == kChainWave && chain) {
+          const int o = (buf * kWinPB + i) * C + lane;
+          fx = sm.efx[o];
+          fy = sm.efy[o];
+          nq = sigma * sm.en[o];
+        }
+        const double ks = win.on ? win.template step<false>(i, sm, sh, sigma, nogd, 0.0) : 0.0;
+        win.publish(sm, sh, ks);
+        __syncthreads();
+        const bool last = step == nsteps - 1;
+        const bool lz_step = last && tail;
+        if (ROLE == kChainWave) {
+          // exp(o) = x * 2^E with o = alpha (forward) or v (backward)
+          double x = 0.0;
+          int E = 0;
+          if (chain) {
+            x = chain_sum<NT>(sm, sh, lane) * fx;
+            E = R + nq;
+          }
+          const int Bm = wave_max_i((chain && x > 0.0) ? E + exponent_of(x) : kNoExp);
+          const double a = chain ? ldexp(x, E - Bm) : 0.0;  // exp(o) / 2^Bm
+          double *stg = sm.stg + (step & 1) * (3 * C + 1);
+          if (chain) {
+            stg[lane] = x;
+            stg[C + lane] = (double)E;
+          }
+          if (lz_step) {
+            lz = (double)Bm * kLn2 + log(wave_sum(a));
+          } else {
+            // exp(m) = d * 2^Bm with m = u (forward) or beta (backward)
+            const double d = chain_contract<CMAX>(sm, sh, lane, a);
+            bool rb = false;
+            if (chain) {
+              stg[2 * C + lane] = d;
+              // entry exp(m -+ S) / 2^R = d * fy * 2^(Bm -+ n - R)
+              rb = chain_insert(sm, sh, lane, t, d * fy, Bm - nq - R, R);
+              if (last) {
+                o_end = log(x) + (double)E * kLn2;
+                m_end = log(d) + (double)Bm * kLn2;
+              }
+            }
+            if (lane == 0) stg[3 * C] = (double)Bm;
+            chain_flag(sm, t, rb);
+          }
+        } else if (ROLE == kLoaderWave) {
+          // the next block's scores land in the other buffer before the
+          // barrier that ends this block
+          if (i == U - 1 && s0 + U < nsteps) bl.put(sm, buf ^ 1, C, lane);
+        } else if (rows && step > 0) {
+          const size_t tp = (size_t)(t - sigma) * C;
+          stage_rows(sm.stg + ((step - 1) & 1) * (3 * C + 1), C, row1 + tp, row2 + tp, true, 128,
+                     NT - 128);
+        }
+        if (!lz_step) {
+          __syncthreads();
+          if (sm.flag[t & 1]) {
+            win.rebase(sm, sh, t, sigma);
+            __syncthreads();
+          }
+        }
+        if (last) done = true;
+      }
+    }
+  }
+}
 
 // ------------------------------------------------------------------ sweeps
 // One workgroup per (direction, sequence b, chunk j), chunk = [p0, p1): the
@@ -328,8 +451,7 @@ __device__ __forceinline__ double ld_or(const double *p, bool ok) { return ok ? 
 // chain wave's serial part, barrier; plus the rare rebase mini-phase.
 template <int NT, int AMAX, int U, int CMAX>
 __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__restrict__ trans,
-                                                const float *__restrict__ dur,
-                                                const double *__restrict__ S,
+                                                const float *__restrict__ dur, Escaled es,
                                                 const int32_t *__restrict__ lengths, PitBufs pb,
                                                 int iter) {
   extern __shared__ __align__(16) unsigned char lds[];
@@ -352,14 +474,16 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   Win<AMAX, U> win;
   win.init(sh, dur);
   stage_trans(sm, sh, trans, fwd, NT);
-  const double *Sb = S + (size_t)b * (T + 1) * C;
+  const size_t ob = (size_t)b * (T + 1) * C;
   const size_t cks = ck_stride(C, K);
   double *rec_start = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
   double *rec_end = (fwd ? pb.end_fwd : pb.end_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
   const int sigma = fwd ? 1 : -1;
-  const double sg = (double)sigma;
   const int tstart = fwd ? p0 : p1;
   const bool tail = fwd ? (p1 == L) : (p0 == 0);  // this chunk ends the chain
+  const bool rows = pb.row_a != nullptr;
+  double *row1 = (fwd ? pb.row_a : pb.row_v) + ob;  // alpha / v
+  double *row2 = (fwd ? pb.row_u : pb.row_b) + ob;  // u / beta
 
   int R = 0;  // integer log reference of label `lane` (units of ln2)
   if (iter == 0) {
@@ -367,14 +491,15 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
     __syncthreads();
     const bool exact = fwd ? (jc == 0) : (p1 == L);
     if (exact) {
+      // entry u[0] - S[0] = 0 forward; beta[L] + S[L] = S[L] backward
       if (chain) {
-        double d = 0.0;  // entry minus R*ln2: u[0] - S[0] = 0 forward, beta[L] + S[L] backward
+        double v = 1.0;
         if (!fwd) {
-          const double sl = Sb[(size_t)L * C + lane];
-          R = (int)rint(sl * kLog2e);
-          d = sl - (double)R * kLn2;
+          const size_t i = ob + (size_t)L * C + lane;
+          v = es.ep[i];
+          R = es.n[i];
         }
-        sm.ring[pos_slot(tstart, K) * C + lane] = exp(d);
+        sm.ring[pos_slot(tstart, K) * C + lane] = v;
       }
     } else {
       // neutral start: every entry of the window (positions inside [0, L]) is 1
@@ -388,8 +513,8 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
     // o = NaN marks a neutral start (never accepted by the verification)
     wsave(rec_start, sm, sh, chain, lane, R,
           exact ? -__builtin_huge_val() : __builtin_nan(""), exact ? 0.0 : __builtin_nan(""), NT);
-    if (exact && chain && pb.row_a)  // u[0] = 0 forward, beta[L] = 0 backward
-      (fwd ? pb.row_u : pb.row_b)[((size_t)b * (T + 1) + tstart) * C + lane] = 0.0;
+    if (exact && chain && rows)  // u[0] = 0 forward, beta[L] = 0 backward
+      row2[(size_t)tstart * C + lane] = 0.0;
   } else {
     double o0, m0;
     wload(rec_start, sm, sh, chain, lane, R, o0, m0, NT);
@@ -398,70 +523,42 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
 
   const int first = fwd ? p0 + 1 : p1 - 1;
   const int nsteps = p1 - p0;
-  double Sq[U];
-#pragma unroll
-  for (int i = 0; i < U; ++i) {
-    const int t = first + sigma * i;
-    Sq[i] = chain ? ld_or(Sb + (size_t)t * C + lane, t >= 0 && t <= T) : 0.0;
-  }
-  double nogd[AMAX];
-  bool done = false;
-  for (int s0 = 0; !done; s0 += U) {
-    const int t0 = first + sigma * s0;
-    win.fill(sm, sh, t0, sigma);
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      if (!done) {
-        const int step = s0 + i;
-        const int t = t0 + sigma * i;
-        const double ks = win.on ? win.template step<false>(i, sm, sh, sigma, nogd, 0.0) : 0.0;
-        win.publish(sm, sh, ks);
-        __syncthreads();
-        const bool last = step == nsteps - 1;
-        const bool lz_step = last && tail;
-        double o = 0.0, m = 0.0;  // relative to bl
-        double bl = 0.0;
-        if (wave0) {
-          const double st = Sq[i];
-          const int base = chain_base(R);
-          bl = (double)base * kLn2;
-          o = chain ? sg * st + (double)(R - base) * kLn2 + log(chain_sum<NT>(sm, sh, lane)) : 0.0;
-          if (lz_step) {
-            const float M = wave_max(chain ? (float)o : -__builtin_huge_valf());
-            const double ex = chain ? exp(o - (double)M) : 0.0;
-            const double lz = bl + ((double)M + log(wave_sum(ex)));
-            if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
-          } else {
-            double e, M;
-            m = chain_contract<CMAX>(sm, sh, lane, o, e, M);
-            bool rb = false;
-            if (chain)
-              rb = chain_insert(sm, sh, lane, t, (m - sg * st) + (double)(base - R) * kLn2, R);
-            chain_flag(sm, t, rb);
-          }
-          if (chain && pb.row_a) {  // per-position rows, in this chunk's frame
-            const size_t ri = ((size_t)b * (T + 1) + t) * C + lane;
-            (fwd ? pb.row_a : pb.row_v)[ri] = bl + o;
-            if (!lz_step) (fwd ? pb.row_u : pb.row_b)[ri] = bl + m;
-          }
-          if (chain) {  // prefetch S for the same block offset of the next block
-            const int tp = t + sigma * U;
-            Sq[i] = ld_or(Sb + (size_t)tp * C + lane, tp >= 0 && tp <= T);
-          }
-        }
-        if (!lz_step) {
-          __syncthreads();
-          if (sm.flag[t & 1]) {
-            win.rebase(sm, sh, t, sigma);
-            __syncthreads();
-          }
-        }
-        if (last) {
-          done = true;
-          if (!lz_step) wsave(rec_end, sm, sh, chain, lane, R, bl + o, bl + m, NT);
-        }
-      }
+  double o_end = 0.0, m_end = 0.0, lz = 0.0;
+  {  // the first block's scores (later blocks: the loader wave, a block ahead)
+    const int npair = min(U, nsteps) * C;
+    for (int q = tid; q < npair; q += NT) {
+      double fx, fy;
+      int n;
+      es_get(es, ob, first + sigma * (q / C), T, C, q % C, fwd, fx, fy, n);
+      sm.efx[q] = fx;
+      sm.efy[q] = fy;
+      sm.en[q] = n;
     }
+  }
+  vm_drain();
+  __syncthreads();
+  const int w = tid >> 6;
+  if (w == 0)
+    sweep_w_loop<kChainWave, NT, AMAX, U, CMAX>(sh, sm, win, es, ob, first, nsteps, sigma, fwd,
+                                                tail, rows, row1, row2, lane, chain, R, o_end,
+                                                m_end, lz);
+  else if (w == 1)
+    sweep_w_loop<kLoaderWave, NT, AMAX, U, CMAX>(sh, sm, win, es, ob, first, nsteps, sigma, fwd,
+                                                 tail, rows, row1, row2, lane, chain, R, o_end,
+                                                 m_end, lz);
+  else
+    sweep_w_loop<kRowWaves, NT, AMAX, U, CMAX>(sh, sm, win, es, ob, first, nsteps, sigma, fwd,
+                                               tail, rows, row1, row2, lane, chain, R, o_end,
+                                               m_end, lz);
+  if (tail) {
+    if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
+  } else {
+    wsave(rec_end, sm, sh, chain, lane, R, o_end, m_end, NT);
+  }
+  if (rows) {  // rows of the last step (t = p1 forward, p0 backward)
+    __syncthreads();
+    const size_t tp = (size_t)(fwd ? p1 : p0) * C;
+    stage_rows(sm.stg + ((nsteps - 1) & 1) * (3 * C + 1), C, row1 + tp, row2 + tp, !tail, 0, NT);
   }
 }
 
@@ -485,18 +582,20 @@ struct WinKernels {
     }
   }
   static hipError_t sweep(const ChainShape &sh, const float *trans, const float *dur,
-                          const double *S, const int32_t *lengths, const PitBufs &pb,
+                          const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                           int with_bwd, int iter, hipStream_t st) {
     attrs();
     const size_t lds = win_lds_bytes(sh.C, sh.K, sh.P);
+    if (!lds_fits((const void *)k_sweep_w<NT, AMAX, U, CMAX>, lds))
+      return wreport(hipErrorInvalidConfiguration, "k_sweep_w (LDS)", sh, lds);
     hipLaunchKernelGGL((k_sweep_w<NT, AMAX, U, CMAX>), dim3((with_bwd ? 2 : 1) * sh.B * sh.nchunk),
-                       dim3(NT), lds, st, sh, trans, dur, S, lengths, pb, iter);
+                       dim3(NT), lds, st, sh, trans, dur, es, lengths, pb, iter);
     return wreport(hipGetLastError(), "k_sweep_w", sh, lds);
   }
 };
 
-// Instances: 256 threads; durations per thread AMAX in {8, 16, 32}; unroll /
-// prefetch depth U (sweep) and UC (marginal pass), smaller for the
+// Instances: 256 threads; durations per thread AMAX in {8, 16, 32}; unroll
+// block U (also the score-prefetch block; UC is unused), smaller for the
 // 32-duration windows (register budget); contraction bound CMAX in {8, 32}.
 template <int NT, int AMAX, int U, int UC>
 struct WinByC {
@@ -517,10 +616,10 @@ static hipError_t win_dispatch(const ChainShape &sh, F &&f) {
 }
 
 hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float *dur,
-                          const double *S, const int32_t *lengths, const PitBufs &pb,
+                          const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                           int with_bwd, int iter, hipStream_t st) {
   return win_dispatch(sh, [&](auto k) {
-    return decltype(k)::sweep(sh, trans, dur, S, lengths, pb, with_bwd, iter, st);
+    return decltype(k)::sweep(sh, trans, dur, es, lengths, pb, with_bwd, iter, st);
   });
 }
 

@@ -16,6 +16,7 @@ namespace semicrf {
 
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr double kLn2 = 0.69314718055994530942;
+constexpr double kLn2Lo = 2.3190468138462996e-17;  // ln 2 minus its float64 rounding
 
 // exp(y) for float64 y: 2^floor(y*log2e) * 2^frac.  NaN propagates; 0
 // below the float64 range, +inf above it.
@@ -51,5 +52,56 @@ __device__ __forceinline__ int exponent_of(double x) {
   (void)frexp(x, &e);
   return e;
 }
+
+// exp(s) = ep * 2^n and exp(-s) = em * 2^-n with ep, em in [2^-1/2, 2^1/2]
+// and n = rint(s / ln 2): the reduced argument r = s - n ln 2 is formed with
+// a two-part ln 2 (so it is accurate to a float64 rounding of r, whatever n),
+// then exp(+-r) in float64.  |s| >= 1e9 (no such cumulative score arises
+// from finite float32 emissions at the supported sizes) and NaN give NaN.
+__device__ __forceinline__ void exp_split(double s, double &ep, double &em, int &n) {
+  if (!(fabs(s) < 1e9)) {
+    ep = em = __builtin_nan("");
+    n = 0;
+    return;
+  }
+  const double k = rint(s * kLog2e);
+  const double r = fma(-k, kLn2Lo, fma(-k, kLn2, s));
+  n = static_cast<int>(k);
+  ep = exp(r);
+  em = exp(-r);
+}
+
+// Row rotation (within each row of 16 lanes) by DPP; lanes whose source would
+// be invalid keep their own value, so no register is left undefined.
+__device__ __forceinline__ int dpp_ror_i(int v, int by) {
+  switch (by) {
+    case 8: return __builtin_amdgcn_update_dpp(v, v, 0x128, 0xf, 0xf, false);
+    case 4: return __builtin_amdgcn_update_dpp(v, v, 0x124, 0xf, 0xf, false);
+    case 2: return __builtin_amdgcn_update_dpp(v, v, 0x122, 0xf, 0xf, false);
+    default: return __builtin_amdgcn_update_dpp(v, v, 0x121, 0xf, 0xf, false);
+  }
+}
+
+// Wave-wide maximum of an int (all 64 lanes call): row rotations by DPP,
+// then the four row maxima through scalar reads.
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, dpp_ror_i(v, 8));
+  v = max(v, dpp_ror_i(v, 4));
+  v = max(v, dpp_ror_i(v, 2));
+  v = max(v, dpp_ror_i(v, 1));
+  const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Wait for every outstanding vector-memory access of the wave (loads and
+// stores): s_waitcnt vmcnt(0), other counters untouched.  Placed before a
+// loop whose only vector-memory accesses are prefetch loads, it lets the
+// compiler wait for each of those by count.
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Exponent used for "no value" in the integer maxima below (any real
+// exponent of a float64, plus a label reference, is far above it).
+constexpr int kNoExp = -(1 << 30);
 
 }  // namespace semicrf

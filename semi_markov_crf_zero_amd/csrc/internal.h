@@ -23,14 +23,32 @@ struct ChainShape {
   int Q;       // waves holding row threads = ceil(C / 64) (Viterbi slices)
   int QT;      // contraction slices of the LDS-ring engine
   int CS;      // previous labels per contraction slice = ceil(C / QT)
+  int pf;      // positions per score-prefetch block of the LDS-ring engine (0: none)
+  int nload;   // loader waves of the LDS-ring engine
   int delta;   // checkpoint interval (positions)
   int nchunk;  // ceil(T / delta) chunks per sequence
   int center;  // 1 = subtract the per-label baseline nu
 };
 
 constexpr int kMaxC = 256;
+constexpr int kMaxPairs = 4;  // (position, label) score pairs per loader lane and block
 constexpr int kMaxKC = 16384;
-constexpr size_t kMaxLds = 163840;  // gfx950: 160 KB per workgroup
+constexpr size_t kMaxLds = 163840;  // gfx950: 160 KB per workgroup (static + dynamic)
+// Dynamic-LDS budget of the configurations: the hardware limit less a small
+// reserve (the kernels declare no static LDS; lds_fits checks the sum).
+constexpr size_t kMaxDynLds = kMaxLds - 256;
+
+// True if a launch of kernel f with `dyn` bytes of dynamic LDS fits the
+// per-workgroup LDS together with the kernel's static LDS (queried once per
+// kernel; a dispatch over the limit would be rejected by the queue).
+inline bool lds_fits(const void *f, size_t dyn) {
+  hipFuncAttributes a;
+  if (hipFuncGetAttributes(&a, f) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return a.sharedSizeBytes + dyn <= kMaxLds;
+}
 
 // Scan tiles: NT_SCAN threads as R = NT_SCAN / C rows x C labels, each row
 // thread owning J consecutive positions; a tile covers R*J positions.
@@ -43,17 +61,18 @@ inline int scan_tile(int C) { return scan_rows(C) * kScanJ; }
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Dynamic LDS bytes of one chain workgroup; the carve-up in chain.hip
-// follows the same order.
-__host__ __device__ inline size_t chain_lds_bytes(int C, int K, int P, int QT) {
+// follows the same order.  pf: positions per score-prefetch block.
+__host__ __device__ inline size_t chain_lds_bytes(int C, int K, int P, int QT, int pf) {
   size_t off = 0;
-  off += (size_t)K * C * 8;   // ring
-  off += (size_t)P * C * 8;   // K-sum partials
-  off += (size_t)C * 8;       // o row
-  off += (size_t)C * 8;       // per-label log references
-  off += 8 * 8;               // scalars
-  off += (size_t)C * 8;       // e row
-  off += (size_t)QT * C * 8;  // contraction partials
-  off += (size_t)C * 4;       // rebase shifts
+  off += (size_t)K * C * 8;            // ring
+  off += (size_t)P * C * 8;            // K-sum partials
+  off += (size_t)C * 8;                // e row
+  off += 8 * 8;                        // scalars
+  off += (size_t)QT * C * 8;           // contraction partials
+  off += (size_t)2 * (3 * C + 1) * 8;  // row staging (two steps)
+  off += (size_t)2 * pf * C * 16;      // split scores (two blocks; mantissas)
+  off += (size_t)2 * pf * C * 4;       // split scores (exponents)
+  off += (size_t)C * 4;                // rebase shifts
   return align_up(off, 16);
 }
 
@@ -86,27 +105,29 @@ __host__ __device__ inline size_t viterbi_lds_bytes(int C, int K, int P, int Q) 
 __host__ __device__ inline size_t ck_stride(int C, int K) { return (size_t)(K + 3) * C; }
 
 // LDS bytes of the windowed chain engine (chain_win.hip, same order as its
-// carve-up): ring, K-sum partials, posterior factors, exp(trans)
+// carve-up): ring, K-sum partials, row staging (two steps), exp(trans)
 // (float64) with rows padded to a multiple of 4, e row (float64, padded),
-// rebase shifts, flags.
+// rebase shifts, flags, split scores of two blocks of positions.
 __host__ __device__ inline size_t win_lds_bytes(int C, int K, int P) {
   const size_t C4 = (size_t)((C + 3) & ~3);
   size_t off = 0;
   off += (size_t)K * C * 8;
   off += (size_t)P * C * 8;
-  off += (size_t)C * 8;
+  off += (size_t)2 * (3 * C + 1) * 8;
   off = align_up(off, 16);
   off += C4 * C * 8;
   off = align_up(off, 16);
   off += C4 * 8;
   off += (size_t)C * 4;
   off += 2 * 4;
+  off = align_up(off, 16);
+  off += (size_t)2 * 8 * C * (8 + 8 + 4);  // split scores of two blocks of up to 8 positions
   return align_up(off, 16);
 }
 
 // Workspace layout (byte offsets, 256-aligned).
 struct Layout {
-  size_t S, nu, tile_sum, anchor, logz, logz_bwd;
+  size_t S, es_p, es_m, es_n, nu, tile_sum, anchor, logz, logz_bwd;
   size_t ck_fwd, ck_bwd, end_fwd, end_bwd, redo, corr_i, corr_f, nbad, lz_part, shift;
   size_t row_a, row_u, row_v, row_b;
   size_t cov_part, cov_part2, cov_anchor, cov_mean, tx_part, dur_part;
@@ -133,6 +154,13 @@ struct PostGeom {
   size_t dur_lds;
 };
 
+// The cumulative scores split for the exp-space recursion (scan.hip):
+// exp(S[b,t,c]) = ep * 2^n and exp(-S[b,t,c]) = em * 2^-n, [B][T+1][C].
+struct Escaled {
+  const double *ep, *em;
+  const int32_t *n;
+};
+
 // Buffers of the parallel-in-time sweeps (pit.hip).  Records have the
 // checkpoint layout [K*C ring][C integer refs][C o][C m] (float64).
 struct PitBufs {
@@ -153,25 +181,26 @@ struct PitBufs {
 // ---- launchers (scan.hip, chain.hip, chain_win.hip, pit.hip, post.hip,
 // viterbi.hip) ------------------------------------------------------------
 
+// ep / em / en may be NULL (then only nu and S are written).
 hipError_t launch_scan(const float *x, const int32_t *lengths, int B, int T, int C, int center,
-                       double *nu, double *S, double *tile_sum, double *anchor, int ntile,
-                       hipStream_t st);
+                       double *nu, double *S, double *ep, double *em, int32_t *en,
+                       double *tile_sum, double *anchor, int ntile, hipStream_t st);
 
 // One iteration of the chunk-parallel sweeps (every chunk of every sequence,
 // both directions when with_bwd); iteration 0 builds the start states.
 hipError_t launch_sweep(const ChainShape &sh, const float *trans, const float *dur,
-                        const double *S, const int32_t *lengths, const PitBufs &pb,
+                        const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                         int with_bwd, int iter, hipStream_t st);
 
 // windowed engine for C <= 32 (chain_win.hip); same arguments
 hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float *dur,
-                          const double *S, const int32_t *lengths, const PitBufs &pb,
+                          const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                           int with_bwd, int iter, hipStream_t st);
 
 // The whole parallel-in-time sweep: init, nchunk x (sweep, verify), fix-up
 // of the records, log Z and (when wanted) the per-position rows.
 hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur,
-                      const double *S, const int32_t *lengths, const PitBufs &pb,
+                      const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                       double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
                       hipStream_t st);
 

@@ -231,14 +231,14 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_fixup(ChainShape sh,
 // nchunk iterations always suffice (after n of them the first n chunks of
 // every chain have exact starts); the ones after convergence return at once.
 hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur,
-                      const double *S, const int32_t *lengths, const PitBufs &pb,
+                      const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                       double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
                       hipStream_t st) {
   const int niter = sh.nchunk;
   hipError_t e = launch_pit_init(sh, pb, niter, st);
   if (e != hipSuccess) return e;
   for (int it = 0; it < niter; ++it) {
-    e = launch_sweep(sh, trans, dur, S, lengths, pb, with_bwd, it, st);
+    e = launch_sweep(sh, trans, dur, es, lengths, pb, with_bwd, it, st);
     if (e != hipSuccess) return e;
     e = launch_pit_verify(sh, lengths, pb, it, with_bwd, st);
     if (e != hipSuccess) return e;

@@ -85,19 +85,39 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_partial(ChainShape sh, Post
   }
 }
 
-// Exclusive prefix over tiles per (b, c) and the mean coverage.
-__global__ void k_cov_anchor(ChainShape sh, PostArgs pa, int ntile) {
-  const int b = blockIdx.x;
+// Exclusive prefix over tiles per (b, c) and the mean coverage.  One block
+// per (sequence, label); each thread owns a contiguous range of tiles and
+// the per-thread totals are combined in a fixed order.
+__global__ __launch_bounds__(kCovThreads) void k_cov_anchor(ChainShape sh, PostArgs pa, int ntile) {
+  __shared__ double red[kCovThreads], red2[kCovThreads];
+  const int b = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const int L = pa.lengths[b];
-  for (int c = threadIdx.x; c < sh.C; c += blockDim.x) {
+  const int per = (ntile + kCovThreads - 1) / kCovThreads;
+  const int i0 = tid * per, i1 = min(i0 + per, ntile);
+  const size_t base = (size_t)b * ntile * sh.C + c;
+  double own = 0.0, own2 = 0.0;
+  for (int i = i0; i < i1; ++i) {
+    own += pa.cov_part[base + (size_t)i * sh.C];
+    own2 += pa.cov_part2[base + (size_t)i * sh.C];
+  }
+  red[tid] = own;
+  red2[tid] = own2;
+  __syncthreads();
+  if (tid == 0) {
     double run = 0.0, tot2 = 0.0;
-    for (int i = 0; i < ntile; ++i) {
-      const size_t o = ((size_t)b * ntile + i) * sh.C + c;
-      pa.cov_anchor[o] = run;
-      run += pa.cov_part[o];
-      tot2 += pa.cov_part2[o];
+    for (int q = 0; q < kCovThreads; ++q) {
+      const double v = red[q];
+      red[q] = run;
+      run += v;
+      tot2 += red2[q];
     }
     pa.cov_mean[(size_t)b * sh.C + c] = valid_len(sh, L) ? tot2 / (double)L : 0.0;
+  }
+  __syncthreads();
+  double run = red[tid];
+  for (int i = i0; i < i1; ++i) {
+    pa.cov_anchor[base + (size_t)i * sh.C] = run;
+    run += pa.cov_part[base + (size_t)i * sh.C];
   }
 }
 
@@ -354,7 +374,8 @@ hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream
                      g.cov_ntile);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_cov_anchor, dim3(sh.B), dim3(256), 0, st, sh, pa, g.cov_ntile);
+  hipLaunchKernelGGL(k_cov_anchor, dim3(sh.B, sh.C), dim3(kCovThreads), 0, st, sh, pa,
+                     g.cov_ntile);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_cov_write, dim3(g.cov_ntile, sh.B), dim3(kCovThreads), 0, st, sh, pa,
@@ -377,6 +398,10 @@ hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream
     (void)hipGetLastError();
     attr = true;
   }
+  const void *kd = g.dur_kb == 4 ? (const void *)k_dur_x<4>
+                   : g.dur_kb == 8 ? (const void *)k_dur_x<8>
+                   : g.dur_kb == 16 ? (const void *)k_dur_x<16> : (const void *)k_dur_x<32>;
+  if (!lds_fits(kd, g.dur_lds)) return hipErrorInvalidConfiguration;
   switch (g.dur_kb) {
     case 4: hipLaunchKernelGGL(k_dur_x<4>, gd, dim3(kDurThreads), g.dur_lds, st, sh, pa, g.dur_span, g.dur_nspan, g.dur_npg); break;
     case 8: hipLaunchKernelGGL(k_dur_x<8>, gd, dim3(kDurThreads), g.dur_lds, st, sh, pa, g.dur_span, g.dur_nspan, g.dur_npg); break;

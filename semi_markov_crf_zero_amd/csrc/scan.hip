@@ -9,10 +9,12 @@
 //   S[b,t,c] = sum_{i<t} (x[b,i,c] - nu[b,c]),  t = 0..T  (rows > L_b repeat L_b)
 // in float64, as a three-pass tiled scan over T:
 //   1. per-tile column sums of x (coalesced over C, float64 accumulation);
-//   2. per sequence: nu and the exclusive tile prefix (tile anchors);
-//   3. per tile: anchor + in-tile prefix, written as S.
+//   2. per (sequence, label): nu and the exclusive tile prefix (tile anchors);
+//   3. per tile: anchor + in-tile prefix, written as S and, for the sweeps,
+//      split into exp(+-S) = mantissa * 2^(+-n) (two float64 and an int32).
 // Positions t >= L_b are never read.  HBM traffic per (b,t,c): 4 B (pass 1)
-// + 4 B read + 8 B write (pass 3).
+// + 4 B read + 8 B write (pass 3), + 20 B when the split is written.
+#include "device_math.h"
 #include "internal.h"
 
 namespace semicrf {
@@ -45,32 +47,66 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_partial(
   }
 }
 
-// One block per sequence; threads loop over labels.
+// One block per (sequence, label): each thread owns a contiguous range of
+// tiles; the per-thread totals are combined in a fixed order (deterministic).
 __global__ __launch_bounds__(kScanThreads) void k_scan_anchor(
     const int32_t *__restrict__ lengths, int T, int C, int ntile, int center,
     const double *__restrict__ tile_sum, double *__restrict__ anchor, double *__restrict__ nu) {
-  const int b = blockIdx.x;
+  __shared__ double red[kScanThreads];
+  const int b = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const int L = lengths[b];
   const bool valid_len = L >= 1 && L <= T;
   const int TS = (kScanThreads / C) * kScanJ;
-  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+  const int per = (ntile + kScanThreads - 1) / kScanThreads;
+  const int i0 = tid * per, i1 = min(i0 + per, ntile);
+  const double *ts = tile_sum + (size_t)b * ntile * C + c;
+  double own = 0.0;
+  for (int i = i0; i < i1; ++i) own += ts[(size_t)i * C];
+  red[tid] = own;
+  __syncthreads();
+  if (tid == 0) {
     double total = 0.0;
-    for (int i = 0; i < ntile; ++i) total += tile_sum[((size_t)b * ntile + i) * C + c];
-    const double n = (valid_len && center) ? total / (double)L : 0.0;
-    nu[(size_t)b * C + c] = valid_len ? n : __builtin_nan("");
+    for (int q = 0; q < kScanThreads; ++q) total += red[q];
+    red[0] = total;
+  }
+  __syncthreads();
+  const double n = (valid_len && center) ? red[0] / (double)L : 0.0;
+  if (tid == 0) nu[(size_t)b * C + c] = valid_len ? n : __builtin_nan("");
+  // tile i contributes tile_sum - (valid positions of tile i) * nu
+  double part = 0.0;
+  for (int i = i0; i < i1; ++i) {
+    int nvalid = valid_len ? L - i * TS : 0;
+    nvalid = nvalid < 0 ? 0 : (nvalid > TS ? TS : nvalid);
+    part += ts[(size_t)i * C] - (double)nvalid * n;
+  }
+  __syncthreads();
+  red[tid] = part;
+  __syncthreads();
+  if (tid == 0) {  // exclusive prefix over the threads, in order
     double run = 0.0;
-    for (int i = 0; i < ntile; ++i) {
-      anchor[((size_t)b * ntile + i) * C + c] = run;
-      int nvalid = valid_len ? L - i * TS : 0;
-      nvalid = nvalid < 0 ? 0 : (nvalid > TS ? TS : nvalid);
-      run += tile_sum[((size_t)b * ntile + i) * C + c] - (double)nvalid * n;
+    for (int q = 0; q < kScanThreads; ++q) {
+      const double v = red[q];
+      red[q] = run;
+      run += v;
     }
+  }
+  __syncthreads();
+  double run = red[tid];
+  for (int i = i0; i < i1; ++i) {
+    anchor[((size_t)b * ntile + i) * C + c] = run;
+    int nvalid = valid_len ? L - i * TS : 0;
+    nvalid = nvalid < 0 ? 0 : (nvalid > TS ? TS : nvalid);
+    run += ts[(size_t)i * C] - (double)nvalid * n;
   }
 }
 
+// S is also written split for the exp-space recursion of the sweeps
+// (exp_split: exp(+-S) as a float64 in [2^-1/2, 2^1/2] times 2^(+-n)) when
+// ep is given.
 __global__ __launch_bounds__(kScanThreads) void k_scan_write(
     const float *__restrict__ x, const int32_t *__restrict__ lengths, int T, int C, int ntile,
-    const double *__restrict__ anchor, const double *__restrict__ nu, double *__restrict__ S) {
+    const double *__restrict__ anchor, const double *__restrict__ nu, double *__restrict__ S,
+    double *__restrict__ ep, double *__restrict__ em, int32_t *__restrict__ en) {
   __shared__ double red[kScanThreads];
   const int tile = blockIdx.x, b = blockIdx.y;
   const int R = kScanThreads / C, TS = R * kScanJ;
@@ -78,7 +114,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_write(
   const int L = lengths[b];
   const bool valid_len = L >= 1 && L <= T;
   const float *xb = x + (size_t)b * T * C;
-  double *Sb = S + (size_t)b * (T + 1) * C;
+  const size_t ob = (size_t)b * (T + 1) * C;
   const double n = valid_len ? nu[(size_t)b * C + c] : 0.0;
   const int t0 = tile * TS + r * kScanJ;
   double local = 0.0;
@@ -94,29 +130,41 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_write(
   double run = anchor[((size_t)b * ntile + tile) * C + c];
   for (int rr = 0; rr < r; ++rr) run += red[rr * C + c];
   if (!valid_len) run = __builtin_nan("");
-  if (tile == 0 && r == 0) Sb[c] = valid_len ? 0.0 : run;
+  auto put = [&](int t, double v) {
+    const size_t o = ob + (size_t)t * C + c;
+    S[o] = v;
+    if (ep) {
+      double p, m;
+      int k;
+      exp_split(v, p, m, k);
+      ep[o] = p;
+      em[o] = m;
+      en[o] = k;
+    }
+  };
+  if (tile == 0 && r == 0) put(0, valid_len ? 0.0 : run);
   for (int i = 0; i < kScanJ; ++i) {
     const int t = t0 + i;
     if (t >= T) break;
     if (t < L) run += (double)xb[(size_t)t * C + c] - n;
-    Sb[(size_t)(t + 1) * C + c] = run;
+    put(t + 1, run);
   }
 }
 
 hipError_t launch_scan(const float *x, const int32_t *lengths, int B, int T, int C, int center,
-                       double *nu, double *S, double *tile_sum, double *anchor, int ntile,
-                       hipStream_t st) {
+                       double *nu, double *S, double *ep, double *em, int32_t *en,
+                       double *tile_sum, double *anchor, int ntile, hipStream_t st) {
   dim3 grid(ntile, B);
   hipLaunchKernelGGL(k_scan_partial, grid, dim3(kScanThreads), 0, st, x, lengths, T, C, ntile,
                      tile_sum);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scan_anchor, dim3(B), dim3(kScanThreads), 0, st, lengths, T, C, ntile,
+  hipLaunchKernelGGL(k_scan_anchor, dim3(B, C), dim3(kScanThreads), 0, st, lengths, T, C, ntile,
                      center, tile_sum, anchor, nu);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan_write, grid, dim3(kScanThreads), 0, st, x, lengths, T, C, ntile,
-                     anchor, nu, S);
+                     anchor, nu, S, ep, em, en);
   return hipGetLastError();
 }
 

@@ -242,6 +242,7 @@ static hipError_t viterbi_impl(const ChainShape &sh, const float *trans, const f
     attr = true;
   }
   const size_t lds = viterbi_lds_bytes(sh.C, sh.K, sh.P, sh.Q);
+  if (!lds_fits((const void *)k_viterbi<NT, AMAX, TRMAX>, lds)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((k_viterbi<NT, AMAX, TRMAX>), dim3(sh.B), dim3(NT), lds, st, sh, trans,
                      dur, S, lengths, bp, vbest, vcbest);
   return hipGetLastError();
