@@ -2,9 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload nlp]
 
-A step is one semicrf_fwd_bwd call (cumulative scores, forward and backward
-sweeps with checkpoints, chunk-parallel recompute + posteriors, reductions)
-over one batch of seeded synthetic input already resident in HBM.  The
+A step is one semicrf_fwd_bwd call (cumulative scores, the parallel-in-time
+forward and backward sweeps over every checkpoint interval, data-parallel
+posteriors, reductions) over one batch of seeded synthetic input already
+resident in HBM.  The
 default workload is the NLP-scale configuration (B=32, T=512, C=24, K=32).
 
 Prints ONE JSON line on stdout:
@@ -15,7 +16,7 @@ Prints ONE JSON line on stdout:
                events the library records on the launch stream around the
                sweep phase during the timed steps), against the MI355X
                float64 vector peak (78.6 TFLOP/s); `traffic` is its HBM bytes
-               per step from rocprofv3 counters stored under profiles/ (null
+               per launch from rocprofv3 counters stored under profiles/ (null
                when absent or when the kernel sources changed since)
   cpu_baseline = the float64 oracle timed on this host on the same workload
 Diagnostics go to stderr.  --copy-calibration MB runs one device copy of MB
@@ -146,7 +147,7 @@ def main():
     t = {k: torch.from_numpy(inp[k]).to(dev) for k in ("emissions", "lengths", "trans", "dur")}
     plan = bd.FwdBwdPlan(t["emissions"], t["lengths"], t["trans"], t["dur"],
                          checkpoint_interval=args.checkpoint_interval)
-    ckpt = args.checkpoint_interval or bd.semicrf_default_checkpoint_interval(T, K)
+    ckpt = args.checkpoint_interval or bd.semicrf_checkpoint_interval(B, T, K)
     nph = len(bd.FWD_BWD_PHASES)
     for _ in range(args.warmup):
         plan.run()

@@ -80,6 +80,13 @@ const char *semicrf_status_string(semicrf_status_t status);
  * section 2.C: checkpoints every ~sqrt(TK)). */
 int semicrf_default_checkpoint_interval(int T, int K);
 
+/* The checkpoint interval semicrf_logz_fwd and semicrf_fwd_bwd use when
+ * given 0: the default above, halved while the sweeps (one workgroup per
+ * direction, sequence and interval; every interval is swept concurrently)
+ * would have fewer than 256 workgroups, and never below max(2K, 32).
+ * Returns 0 for B, T or K < 1. */
+int semicrf_checkpoint_interval(int B, int T, int K);
+
 /* Bytes of device workspace `op` needs for these sizes.  checkpoint_interval
  * is the one passed to semicrf_fwd_bwd (0 = default; ignored by other ops).
  * Writes *bytes; returns an error for invalid sizes exactly as the op would. */
@@ -117,7 +124,7 @@ semicrf_status_t semicrf_logz_fwd(const float *emissions, const int32_t *lengths
  *   marginals [B][T][C] or NULL coverage mu[b,t,c] = P(position t lies in a
  *                               segment of label c); sums to 1 over c.
  * checkpoint_interval: positions between stored forward/backward states
- * (0 = semicrf_default_checkpoint_interval).  Results do not depend on it
+ * (0 = semicrf_checkpoint_interval(B, T, K)).  Results do not depend on it
  * beyond rounding. */
 semicrf_status_t semicrf_fwd_bwd(const float *emissions, const int32_t *lengths,
                                  const float *trans, const float *dur,

@@ -29,7 +29,8 @@ STATUS = {
 }
 
 EXPORTS = (
-    "semicrf_status_string", "semicrf_default_checkpoint_interval", "semicrf_workspace_size",
+    "semicrf_status_string", "semicrf_default_checkpoint_interval", "semicrf_checkpoint_interval",
+    "semicrf_workspace_size",
     "semicrf_cumulative_scores", "semicrf_logz_fwd", "semicrf_fwd_bwd", "semicrf_fwd_bwd_timed",
     "semicrf_viterbi",
 )
@@ -58,6 +59,8 @@ def load():
     lib.semicrf_status_string.restype = ctypes.c_char_p
     lib.semicrf_default_checkpoint_interval.argtypes = [I, I]
     lib.semicrf_default_checkpoint_interval.restype = I
+    lib.semicrf_checkpoint_interval.argtypes = [I, I, I]
+    lib.semicrf_checkpoint_interval.restype = I
     lib.semicrf_workspace_size.argtypes = [I, I, I, I, I, U, I, ctypes.POINTER(Z)]
     lib.semicrf_workspace_size.restype = I
     lib.semicrf_cumulative_scores.argtypes = [P, P, I, I, I, U, P, P, P, Z, P]
@@ -81,6 +84,11 @@ def status_string(code: int) -> str:
 
 def semicrf_default_checkpoint_interval(T: int, K: int) -> int:
     return int(load().semicrf_default_checkpoint_interval(int(T), int(K)))
+
+
+def semicrf_checkpoint_interval(B: int, T: int, K: int) -> int:
+    """Interval used by logz / fwd_bwd when given 0 (see semicrf.h)."""
+    return load().semicrf_checkpoint_interval(int(B), int(T), int(K))
 
 
 def semicrf_workspace_size(op: int, B: int, T: int, C: int, K: int, flags: int = 0,

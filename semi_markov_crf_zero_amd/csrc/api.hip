@@ -59,16 +59,15 @@ bool chain_config(int C, int K, ChainShape &sh) {
   return false;
 }
 
-// Windowed engine (C <= 32, 256 threads): each of the P = 256 / C threads
-// of a label owns a register window of up to 32 consecutive durations, so it
-// applies when K <= 32 * P and the LDS fits.  Other shapes run on the
-// LDS-ring engine.
+// Blocked windowed engine (C <= 32, 256 threads): applies when its LDS (ring
+// and exp(dur) table, K*C float64 each, plus block buffers) fits.  Other
+// shapes run on the LDS-ring engine.
 bool win_config(int C, int K, ChainShape &sh) {
   if (C < 1 || C > 32) return false;
   const int NT = 256;
   const int P = NT / C;
   const int A = (K + P - 1) / P;
-  if (A > 32 || win_lds_bytes(C, K, P) > kMaxDynLds) return false;
+  if (win_lds_bytes(C, K, P) > kMaxDynLds) return false;
   sh.NT = NT;
   sh.P = P;
   sh.A = A;
@@ -88,6 +87,21 @@ int default_delta(int T, int K) {
   if (d < 1) d = 1;
   if (d > T) d = T;
   return (int)d;
+}
+
+// Interval used when the caller passes 0: the sqrt(T*K) rule, halved while
+// the sweep (one workgroup per direction and interval) would have fewer than
+// kSweepWorkgroups workgroups -- each interval is a serial chain of its
+// length, so more intervals finish sooner until the chip is full -- and
+// never below max(2K, 32) positions, so each interval spans several
+// segment lengths and forgets its neutral start.
+constexpr long long kSweepWorkgroups = 256;
+
+int effective_delta(int B, int T, int K) {
+  int d = default_delta(T, K);
+  const int dmin = 2 * K > 32 ? 2 * K : 32;
+  while ((d + 1) / 2 >= dmin && 2LL * B * ((T + d - 1) / d) < kSweepWorkgroups) d = (d + 1) / 2;
+  return d;
 }
 
 struct Carver {
@@ -184,7 +198,7 @@ semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int
     ChainShape probe = sh;
     if (!chain_config(C, K, probe)) return SEMICRF_ERR_UNSUPPORTED;
     if (op == SEMICRF_OP_VITERBI || !win_config(C, K, sh)) sh = probe;
-    sh.delta = ckpt > 0 ? (ckpt < T ? ckpt : T) : default_delta(T, K);
+    sh.delta = ckpt > 0 ? (ckpt < T ? ckpt : T) : effective_delta(B, T, K);
     sh.nchunk = (T + sh.delta - 1) / sh.delta;
   }
   if (!make_layout(op, B, T, C, K, &sh, lay)) return SEMICRF_ERR_ARG;
@@ -250,6 +264,11 @@ const char *semicrf_status_string(semicrf_status_t status) {
 int semicrf_default_checkpoint_interval(int T, int K) {
   if (T < 1 || K < 1) return 0;
   return default_delta(T, K);
+}
+
+int semicrf_checkpoint_interval(int B, int T, int K) {
+  if (B < 1 || T < 1 || K < 1) return 0;
+  return effective_delta(B, T, K);
 }
 
 semicrf_status_t semicrf_workspace_size(int op, int B, int T, int C, int K, unsigned flags,

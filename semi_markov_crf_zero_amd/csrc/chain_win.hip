@@ -1,37 +1,37 @@
-// chain_win.hip -- windowed streaming engine for C <= 32 labels.
+// chain_win.hip -- blocked streaming engine for C <= 32 labels.
 //
 // Same recurrences, ring contents, checkpoint records and outputs as
-// chain.hip (see its header for the equations and the method citations);
-// this file only reorganises the work for gfx950 latency:
+// chain.hip (see its header for the equations, the exp-space arithmetic and
+// the method citations); this file reorganises the work so that nothing but
+// the dependent chain itself runs position by position:
 //
-//   * K-sum with register windows.  Thread (g, c) owns the durations
-//     k = a0 .. a0+AMAX-1 (a0 = 1 + g*A) of label c.  The ring values it
-//     needs slide by one position per step, so it keeps them in registers
-//     (W[0 .. AMAX+U-2]) and loads ONE new value from the LDS ring per step;
-//     the loop is unrolled U steps so every register index is a compile-time
-//     constant, and the window is refilled from the ring once per U steps.
-//     LDS traffic per step drops from K*C*8 bytes to about P*C*8*(1+AMAX/U).
-//   * one "chain wave" (wave 0, lane c = label c) does the per-position
-//     serial part -- the K-sum times exp(+-S), an integer maximum of the
-//     float64 exponents, the C x C contraction (exp(trans) staged in LDS), the
-//     new ring entry and the rebase decision -- with wave-local
-//     synchronisation only: two workgroup barriers per step in total.  No
-//     transcendental function sits on this path (see chain.hip: exp(+-S) come
-//     split from the score scan, every rescaling is an exact power of two).
-//   * the waves specialise (each runs its own copy of the step loop, with
-//     the same barriers): wave 1 prefetches the split scores of the next
-//     block of U positions into LDS (its loop issues only loads, so nothing
-//     waits on them before the block ends), waves 2-3 turn the previous
-//     step's staged values into the per-position log rows (their loop issues
-//     only stores), and the chain wave reads its scores from LDS -- no
-//     global-memory access sits on the per-step critical path.
-//   * an exact power-of-two column rebase (rare) runs as its own barrier-
-//     separated mini-phase that rescales the register windows and the LDS
-//     ring together.
+//   * blocks of U positions.  The K-sum of step i of a block (position t)
+//       sum_{k=1..K} D[k][c] * G[t - sigma*k][c]
+//     reads, for k > i, only entries produced before the block began.  So
+//     at a block's start all 256 threads compute these "far" parts for the
+//     U steps at once: thread (g, c) owns the durations k = a0 .. a0+A-1 of
+//     label c, fills a register window with the entries older than the block
+//     (entries inside it read as 0) and accumulates U sums -- U*A fused
+//     multiply-adds with full instruction-level parallelism.  Partials are
+//     reduced inside each wave when C divides 64 and meet in LDS.  One
+//     workgroup barrier.
+//   * then one "chain wave" (wave 0, lane c = label c) runs the block's U
+//     steps alone, with wave-local synchronisation only: the "near" part
+//     sum_{k<=i} D[k][c] * Gb[i-k] over the block's own new entries
+//     (registers), the product with exp(+-S), the integer maximum of the
+//     float64 exponents, the C x C contraction (exp(trans) in LDS), the new
+//     entry and its rebase decision.  A rebase (R += n) rescales the block's
+//     entries in registers and is applied to the precomputed far parts as
+//     they are read (exact ldexp).
+//   * at the block end the chain lanes write the block's entries into the
+//     LDS ring; if a label rebased, all threads rescale its older entries
+//     (rare).  One workgroup barrier.
+//   * meanwhile wave 1 prefetches the split scores of the next block into LDS
+//     (its loop issues only loads) and waves 2-3 turn the previous block's
+//     staged values into the per-position log rows (their loop issues only
+//     stores): no global-memory access and no logarithm on the chain.
 #include <stdio.h>
 #include <stdlib.h>
-
-#include <type_traits>
 
 #include "device_math.h"
 #include "internal.h"
@@ -41,33 +41,40 @@ namespace semicrf {
 namespace {
 
 constexpr int kRebaseExp = 260;  // rebase bound, log2 units
-constexpr int kWinPB = 8;        // largest unroll block (positions); sizes the score buffers
+constexpr int U = kWinU;         // positions per block
 
 struct WSmem {
-  double *ring, *part, *stg, *tr, *erow;
-  double *efx, *efy;  // split scores of two blocks [2][kWinPB][C]
+  double *ring, *dtab, *part, *stg, *erow;
+  double *efx, *efy;  // split scores of two blocks [2][U][C]
   int *shiftn, *flag, *en;
 };
 
-__device__ __forceinline__ int round4(int c) { return (c + 3) & ~3; }
+// Contraction width: C padded to the instance bound 8, 16 or 32.
+__host__ __device__ __forceinline__ int cpad(int c) { return c <= 8 ? 8 : (c <= 16 ? 16 : 32); }
+
+// Partials are pre-reduced inside each wave when C divides 64 (lanes of one
+// label sit C apart); otherwise one partial per duration group.
+__device__ __forceinline__ bool wave_reduced(const ChainShape &sh) { return (64 % sh.C) == 0; }
+__device__ __forceinline__ int part_groups(const ChainShape &sh, int NT) {
+  return wave_reduced(sh) ? NT / 64 : sh.P;
+}
 
 // Carve-up; the byte count is win_lds_bytes() in internal.h.
-__device__ __forceinline__ WSmem wcarve(unsigned char *base, const ChainShape &s) {
+__device__ __forceinline__ WSmem wcarve(unsigned char *base, const ChainShape &s, int NT) {
   WSmem m;
   size_t off = 0;
-  const int C4 = round4(s.C);
+  const int C4 = cpad(s.C);
   m.ring = reinterpret_cast<double *>(base + off); off += (size_t)s.K * s.C * 8;
-  m.part = reinterpret_cast<double *>(base + off); off += (size_t)s.P * s.C * 8;
-  m.stg = reinterpret_cast<double *>(base + off); off += (size_t)2 * (3 * s.C + 1) * 8;
-  off = (off + 15) & ~(size_t)15;
-  m.tr = reinterpret_cast<double *>(base + off); off += (size_t)C4 * s.C * 8;
+  m.dtab = reinterpret_cast<double *>(base + off); off += (size_t)s.K * s.C * 8;
+  m.part = reinterpret_cast<double *>(base + off); off += (size_t)U * part_groups(s, NT) * s.C * 8;
+  m.stg = reinterpret_cast<double *>(base + off); off += (size_t)2 * U * (3 * s.C + 1) * 8;
   off = (off + 15) & ~(size_t)15;
   m.erow = reinterpret_cast<double *>(base + off); off += (size_t)C4 * 8;
   m.shiftn = reinterpret_cast<int *>(base + off); off += (size_t)s.C * 4;
   m.flag = reinterpret_cast<int *>(base + off); off += 2 * 4;
   off = (off + 15) & ~(size_t)15;
-  m.efx = reinterpret_cast<double *>(base + off); off += (size_t)2 * kWinPB * s.C * 8;
-  m.efy = reinterpret_cast<double *>(base + off); off += (size_t)2 * kWinPB * s.C * 8;
+  m.efx = reinterpret_cast<double *>(base + off); off += (size_t)2 * U * s.C * 8;
+  m.efy = reinterpret_cast<double *>(base + off); off += (size_t)2 * U * s.C * 8;
   m.en = reinterpret_cast<int *>(base + off);
   return m;
 }
@@ -77,35 +84,35 @@ __device__ __forceinline__ int pos_slot(int pos, int K) {
   return s < 0 ? s + K : s;
 }
 
-// exp(trans) in float64 (a rounded weight would perturb the parameters, and
+// exp(dur) in float64 (a rounded weight would perturb the parameters, and
 // the parameter gradients move by that times a sensitivity that grows with
-// the sequence length), oriented for the contraction of direction fwd, rows
-// padded to a multiple of 4 with zeros: tr[c_in * C + c_out] = weight of
-// input label c_in for output label c_out.
-__device__ __forceinline__ void stage_trans(const WSmem &sm, const ChainShape &sh,
-                                            const float *__restrict__ trans, bool fwd, int NT) {
-  const int C = sh.C, C4 = round4(C);
-  for (int i = threadIdx.x; i < C4 * C; i += NT) {
-    const int ci = i / C, co = i % C;
-    double w = 0.0;
-    if (ci < C) w = exp((double)(fwd ? trans[(size_t)ci * C + co] : trans[(size_t)co * C + ci]));
-    sm.tr[i] = w;
-  }
+// the sequence length): dtab[(k-1)*C + c] = exp(dur[k-1][c]).
+__device__ __forceinline__ void stage_dur(const WSmem &sm, const ChainShape &sh,
+                                          const float *__restrict__ dur, int NT) {
+  for (int i = threadIdx.x; i < sh.K * sh.C; i += NT) sm.dtab[i] = exp((double)dur[i]);
 }
 
-// Partials are pre-reduced inside each wave when C divides 64 (lanes of one
-// label sit C apart); the chain wave then reads one value per wave.
-__device__ __forceinline__ bool wave_reduced(const ChainShape &sh) { return (64 % sh.C) == 0; }
+// exp(trans) row of a chain lane for the contraction of direction fwd
+// (float64, for the same reason): tr[c_in] = weight of input label c_in for
+// output label c, zero past C.
+template <int CMAX>
+__device__ __forceinline__ void load_tr_row(const ChainShape &sh, const float *__restrict__ trans,
+                                            bool fwd, int c, double (&tr)[CMAX]) {
+  const int C = sh.C;
+#pragma unroll
+  for (int ci = 0; ci < CMAX; ++ci)
+    tr[ci] = (c < C && ci < C)
+                 ? exp((double)(fwd ? trans[(size_t)ci * C + c] : trans[(size_t)c * C + ci]))
+                 : 0.0;
+}
 
-template <int AMAX, int U>
+// Far parts of the K-sums of a block: thread (kg, kc) owns the durations
+// k = a0 + j, j < nage, of label kc.
 struct Win {
-  using DT = typename std::conditional<(AMAX <= 16), double, float>::type;
-  DT D[AMAX];
-  double W[AMAX + U - 1];
-  int kc, kg, a0, nage, yslot;
+  int kc, kg, a0, nage;
   bool on;
 
-  __device__ __forceinline__ void init(const ChainShape &sh, const float *__restrict__ dur) {
+  __device__ __forceinline__ void init(const ChainShape &sh) {
     const int C = sh.C;
     kc = threadIdx.x % C;
     kg = threadIdx.x / C;
@@ -114,90 +121,62 @@ struct Win {
     int n = on ? sh.K - a0 + 1 : 0;
     n = n < 0 ? 0 : (n > sh.A ? sh.A : n);
     nage = n;
-#pragma unroll
-    for (int j = 0; j < AMAX; ++j)
-      D[j] = (j < nage) ? (DT)exp((double)dur[(size_t)(a0 + j - 1) * C + kc]) : (DT)0;
   }
 
-  // Fill W[0 .. AMAX-2] for a block that starts at step t0 (direction sigma)
-  // and point yslot at the value the first step of the block loads.
-  __device__ __forceinline__ void fill(const WSmem &sm, const ChainShape &sh, int t0, int sigma) {
+  // Step i of the block (position t0 + sigma*i) needs, for duration k, the
+  // entry at t0 - sigma*(k - i); positions inside the block (k <= i) and
+  // beyond the window (k - i > K) count 0.  Durations go in chunks of U:
+  // the chunk's U weights and its 2U-1 entries come from LDS, then U*U
+  // fused multiply-adds with compile-time register indices.
+  __device__ __forceinline__ void far(const WSmem &sm, const ChainShape &sh, int t0, int sigma,
+                                      double (&F)[U]) {
+#pragma unroll
+    for (int i = 0; i < U; ++i) F[i] = 0.0;
     if (!on) return;
     const int K = sh.K, C = sh.C;
-    int sl = pos_slot(t0 - sigma * (a0 + AMAX - 1), K);
+    // slot of position t0 - sigma*m for m in [1, K]: base - sigma*m brought
+    // back into [0, K) by one correction
+    const int base = pos_slot(t0, K);
+    for (int jb = 0; jb < nage; jb += U) {
+      double dv[U], wv[2 * U - 1];
 #pragma unroll
-    for (int j = 0; j < AMAX - 1; ++j) {
-      W[j] = sm.ring[sl * C + kc];
-      sl += sigma;
-      sl = sl >= K ? sl - K : (sl < 0 ? sl + K : sl);
-    }
-    yslot = sl;
-  }
-
-  // Load the youngest value of step I of the block (I is a constant once the
-  // block loop is unrolled) and return the K-sum; with GD also accumulate the
-  // segment posteriors gd[j] += q * D[j] * W.
-  template <bool GD>
-  __device__ __forceinline__ double step(int I, const WSmem &sm, const ChainShape &sh, int sigma,
-                                         double (&gd)[AMAX], double q) {
-    W[AMAX - 1 + I] = sm.ring[yslot * sh.C + kc];
-    yslot += sigma;
-    yslot = yslot >= sh.K ? yslot - sh.K : (yslot < 0 ? yslot + sh.K : yslot);
-    double s = 0.0;
+      for (int jj = 0; jj < U; ++jj)
+        dv[jj] = jb + jj < nage ? sm.dtab[(a0 + jb + jj - 1) * C + kc] : 0.0;
 #pragma unroll
-    for (int j = 0; j < AMAX; ++j) {
-      const double w = (double)D[j] * W[AMAX - 1 + I - j];
-      s += w;
-      if (GD) gd[j] += q * w;
-    }
-    return s;
-  }
-
-  // Rebase mini-phase: rescale the register window and the LDS slots of the
-  // durations this thread owns (relative to the next step), except the
-  // newest entry (position t).
-  __device__ __forceinline__ void rebase(const WSmem &sm, const ChainShape &sh, int t, int sigma) {
-    if (!on) return;
-    const int n = sm.shiftn[kc];
-    if (n == 0) return;
+      for (int q = 0; q < 2 * U - 1; ++q) {
+        const int m = a0 + jb + q - (U - 1);  // wv[q]: entry at m = k - i, q = jj - i + U - 1
+        int sl = base - sigma * m;
+        sl += sl < 0 ? K : 0;
+        sl -= sl >= K ? K : 0;
+        wv[q] = (m >= 1 && m <= K) ? sm.ring[sl * C + kc] : 0.0;
+      }
 #pragma unroll
-    for (int j = 0; j < AMAX + U - 1; ++j) W[j] = ldexp(W[j], -n);
-    const int tn = t + sigma;
-    for (int j = 0; j < nage; ++j) {
-      const int k = a0 + j;
-      if (k < 2) continue;
-      const int sl = pos_slot(tn - sigma * k, sh.K);
-      sm.ring[sl * sh.C + kc] = ldexp(sm.ring[sl * sh.C + kc], -n);
+      for (int i = 0; i < U; ++i) {
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj) F[i] = fma(dv[jj], wv[jj - i + U - 1], F[i]);
+      }
     }
   }
 
-  // Publish the K-sum: per thread, or summed over the wave's groups of one
-  // label (all lanes of the workgroup call).
-  __device__ __forceinline__ void publish(const WSmem &sm, const ChainShape &sh, double s) {
+  // Publish the far partials part[i][g][c]: per duration group, or summed
+  // over the wave's groups of one label (all lanes of the workgroup call).
+  __device__ __forceinline__ void publish(const WSmem &sm, const ChainShape &sh, int NT,
+                                          double (&F)[U]) {
+    const int C = sh.C, G = part_groups(sh, NT);
     if (wave_reduced(sh)) {
-      for (int off = sh.C; off < 64; off <<= 1) s += __shfl_xor(s, off);
-      const int lane = threadIdx.x & 63;
-      if (lane < sh.C) sm.part[(threadIdx.x >> 6) * sh.C + lane] = s;
+      const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        double s = F[i];
+        for (int off = C; off < 64; off <<= 1) s += __shfl_xor(s, off);
+        if (lane < C) sm.part[(i * G + w) * C + lane] = s;
+      }
     } else if (on) {
-      sm.part[kg * sh.C + kc] = s;
+#pragma unroll
+      for (int i = 0; i < U; ++i) sm.part[(i * G + kg) * C + kc] = F[i];
     }
   }
 };
-
-// ---------------------------------------------------------------- chain wave
-// Lane c < C of wave 0 reads the K-sum of label c.
-template <int NT>
-__device__ __forceinline__ double chain_sum(const WSmem &sm, const ChainShape &sh, int lane) {
-  double sum = 0.0;
-  if (wave_reduced(sh)) {
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) sum += sm.part[w * sh.C + lane];
-  } else {
-#pragma unroll 4
-    for (int p = 0; p < sh.P; ++p) sum += sm.part[p * sh.C + lane];
-  }
-  return sum;
-}
 
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
@@ -211,48 +190,29 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Exp-space contraction: lane c < C holds a[c] = exp(o[c]) / 2^B (at most
-// 1, the largest >= 1/2) and receives sum_{c'} a[c'] * tr[c'][c] in float64.
-// All 64 lanes of wave 0 call.
+// 1, the largest >= 1/2) and its exp(trans) row, and receives
+// sum_{c'} a[c'] * tr[c'] in float64.  The e row is broadcast through LDS,
+// two values per read, all reads issued before the first multiply.  All 64
+// lanes of wave 0 call.
 template <int CMAX>
 __device__ __forceinline__ double chain_contract(const WSmem &sm, const ChainShape &sh, int lane,
-                                                 double a) {
-  const int C = sh.C;
-  if (lane < round4(C)) sm.erow[lane] = lane < C ? a : 0.0;
+                                                 double a, const double (&tr)[CMAX]) {
+  if (lane < CMAX) sm.erow[lane] = lane < sh.C ? a : 0.0;
   wave_lds_sync();
-  double d0 = 0.0, d1 = 0.0, d2 = 0.0, d3 = 0.0;
-  if (lane < C) {
+  const double2 *e2 = reinterpret_cast<const double2 *>(sm.erow);
+  double2 ev[CMAX / 2];
 #pragma unroll
-    for (int ci = 0; ci < CMAX; ci += 4) {
-      if (ci < C) {
-        d0 = fma(sm.erow[ci + 0], sm.tr[(ci + 0) * C + lane], d0);
-        d1 = fma(sm.erow[ci + 1], sm.tr[(ci + 1) * C + lane], d1);
-        d2 = fma(sm.erow[ci + 2], sm.tr[(ci + 2) * C + lane], d2);
-        d3 = fma(sm.erow[ci + 3], sm.tr[(ci + 3) * C + lane], d3);
-      }
-    }
+  for (int q = 0; q < CMAX / 2; ++q) ev[q] = e2[q];
+  double d0 = 0.0, d1 = 0.0, d2 = 0.0, d3 = 0.0;
+#pragma unroll
+  for (int q = 0; q < CMAX / 2; q += 2) {
+    d0 = fma(ev[q].x, tr[2 * q], d0);
+    d1 = fma(ev[q].y, tr[2 * q + 1], d1);
+    d2 = fma(ev[q + 1].x, tr[2 * q + 2], d2);
+    d3 = fma(ev[q + 1].y, tr[2 * q + 3], d3);
   }
   wave_lds_sync();
   return (d0 + d1) + (d2 + d3);
-}
-
-// New ring entry for position t of label `lane`: y * 2^s relative to the
-// label's reference 2^R (y > 0 a float64, s an exact integer).  An entry
-// outside [2^-kRebaseExp, 2^kRebaseExp] moves R by its exponent (rebase:
-// the column's older entries are rescaled by the same power of two).
-__device__ __forceinline__ bool chain_insert(const WSmem &sm, const ChainShape &sh, int lane,
-                                             int t, double y, int s, int &R) {
-  const int ey = exponent_of(y) + s;
-  const int n = (ey > kRebaseExp || ey < -kRebaseExp) ? ey : 0;
-  R += n;
-  sm.shiftn[lane] = n;
-  sm.ring[pos_slot(t, sh.K) * sh.C + lane] = ldexp(y, s - n);
-  return n != 0;
-}
-
-// Wave-vote the rebase decisions of step t into the flag slot t&1 (lane 0).
-__device__ __forceinline__ void chain_flag(const WSmem &sm, int t, bool rb) {
-  const bool any = __any(rb ? 1 : 0);
-  if ((threadIdx.x & 63) == 0) sm.flag[t & 1] = any ? 1 : 0;
 }
 
 __device__ __forceinline__ void wsave(double *__restrict__ dst, const WSmem &sm,
@@ -279,13 +239,11 @@ __device__ __forceinline__ void wload(const double *__restrict__ src, const WSme
   }
 }
 
-// Split scores of position t for label c (row / chain lanes; other lanes
-// read label 0), in the order the direction uses them: fx multiplies the
-// K-sum (exp(S) forward, exp(-S) backward), fy the contraction (the other
-// one), n is the exponent (its sign is applied where it is used).  t is
-// clamped into [0, T], so every lane loads from a valid address and no
-// select touches the loaded values: the loads stay in flight until their
-// first use several positions later (a prefetch).
+// Split scores of position t for label c (other lanes read label 0), in the
+// order the direction uses them: fx multiplies the K-sum (exp(S) forward,
+// exp(-S) backward), fy the contraction (the other one), n is the exponent
+// (its sign is applied where it is used).  t is clamped into [0, T], so
+// every lane loads from a valid address.
 __device__ __forceinline__ void es_get(const Escaled &es, size_t ob, int t, int T, int C, int c,
                                        bool fwd, double &fx, double &fy, int &n) {
   const int tc = t < 0 ? 0 : (t > T ? T : t);
@@ -295,36 +253,37 @@ __device__ __forceinline__ void es_get(const Escaled &es, size_t ob, int t, int 
   n = es.n[i];
 }
 
-// Per-position log rows from a step's staged values (stg: x[C], E[C], d[C],
-// B): row1 = log x + E ln2 (alpha / v), row2 = log d + B ln2 (u / beta).
-// Threads [first, first + nthr) share the 2C logs.
-__device__ __forceinline__ void stage_rows(const double *stg, int C, double *r1, double *r2,
-                                           bool with2, int first, int nthr) {
-  for (int i = (int)threadIdx.x - first; i < 2 * C; i += nthr) {
-    if (i < C)
-      r1[i] = log(stg[i]) + stg[C + i] * kLn2;
-    else if (with2)
-      r2[i - C] = log(stg[C + i]) + stg[3 * C] * kLn2;
+// Per-position log rows of a block's staged values: stg = [U][x[C], E[C],
+// d[C], B]; step m (position t0 + sigma*m, m < nb) gives row1 = log x + E ln2
+// (alpha / v) and row2 = log d + B ln2 (u / beta; not for the step `no2`).
+// Threads [first, first + nthr) share the nb * 2C logs.
+__device__ __forceinline__ void block_rows(const double *stg, int C, int nb, int t0, int sigma,
+                                           double *row1, double *row2, int no2, int first,
+                                           int nthr) {
+  const int S = 3 * C + 1;
+  for (int q = (int)threadIdx.x - first; q < nb * 2 * C; q += nthr) {
+    const int m = q / (2 * C), r = q % (2 * C);
+    const double *s = stg + m * S;
+    const size_t o = (size_t)(t0 + sigma * m) * C;
+    if (r < C)
+      row1[o + r] = log(s[r]) + s[C + r] * kLn2;
+    else if (m != no2)
+      row2[o + r - C] = log(s[C + r]) + s[3 * C] * kLn2;
   }
 }
 
-}  // namespace
-
-// Wave roles of the windowed engine.
-enum WinRole { kChainWave = 0, kLoaderWave = 1, kRowWaves = 2 };
-
 // Loader: the split scores of the block of U steps starting at step s0
-// (positions first + sigma*(s0 + i), i < U) for every label -- U*C
-// (position, label) pairs over the 64 lanes, at most kWinPB*32/64 = 4 each.
-template <int U>
+// (positions first + sigma*(s0 + i)) for every label -- U*C pairs over the
+// 64 lanes.
 struct BlockLoad {
-  double fx[(U * 32 + 63) / 64], fy[(U * 32 + 63) / 64];
-  int n[(U * 32 + 63) / 64];
+  static constexpr int NP = (U * 32 + 63) / 64;
+  double fx[NP], fy[NP];
+  int n[NP];
 
   __device__ __forceinline__ void issue(const Escaled &es, size_t ob, int first, int sigma,
                                         int s0, int T, int C, int lane, bool fwd) {
 #pragma unroll
-    for (int k = 0; k < (U * 32 + 63) / 64; ++k) {
+    for (int k = 0; k < NP; ++k) {
       const int q = lane + 64 * k;  // pair (i, c) = (q / C, q % C)
       const int i = q < U * C ? q / C : 0, c = q < U * C ? q % C : 0;
       es_get(es, ob, first + sigma * (s0 + i), T, C, c, fwd, fx[k], fy[k], n[k]);
@@ -333,10 +292,10 @@ struct BlockLoad {
 
   __device__ __forceinline__ void put(const WSmem &sm, int buf, int C, int lane) const {
 #pragma unroll
-    for (int k = 0; k < (U * 32 + 63) / 64; ++k) {
+    for (int k = 0; k < NP; ++k) {
       const int q = lane + 64 * k;
       if (q < U * C) {
-        const int o = buf * kWinPB * C + q;  // [buf][i][c], q = i*C + c
+        const int o = buf * U * C + q;  // [buf][i][c], q = i*C + c
         sm.efx[o] = fx[k];
         sm.efy[o] = fy[k];
         sm.en[o] = n[k];
@@ -345,98 +304,103 @@ struct BlockLoad {
   }
 };
 
-// The step loop of one role (see WinRole).  Per step: K-sum share and
-// publish, barrier, role work, barrier (not after the chain's last step),
-// and the rare rebase mini-phase with its own barrier.  The chain wave
-// leaves log Z (tail chunk) or the end-state o / m in lz / o_end / m_end.
-template <int ROLE, int NT, int AMAX, int U, int CMAX>
-__device__ __forceinline__ void sweep_w_loop(const ChainShape &sh, const WSmem &sm,
-                                             Win<AMAX, U> &win, const Escaled &es, size_t ob,
-                                             int first, int nsteps, int sigma, bool fwd,
-                                             bool tail, bool rows, double *row1, double *row2,
-                                             int lane, bool chain, int &R, double &o_end,
-                                             double &m_end, double &lz) {
-  const int C = sh.C, T = sh.T;
-  double nogd[AMAX];
-  BlockLoad<U> bl;
-  bool done = false;
-  for (int s0 = 0; !done; s0 += U) {
-    const int t0 = first + sigma * s0;
-    const int buf = (s0 / U) & 1;
-    win.fill(sm, sh, t0, sigma);
-    if (ROLE == kLoaderWave && s0 + U < nsteps) bl.issue(es, ob, first, sigma, s0 + U, T, C, lane, fwd);
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      if (!done) {
-        const int step = s0 + i;
-        const int t = t0 + sigma * i;
-        // the chain lanes' scores of this step (LDS, staged a block ahead)
-        double fx = 0.0, fy = 0.0;
-        int nq = 0;
-        if (ROLE == kChainWave && chain) {
-          const int o = (buf * kWinPB + i) * C + lane;
-          fx = sm.efx[o];
-          fy = sm.efy[o];
-          nq = sigma * sm.en[o];
-        }
-        const double ks = win.on ? win.template step<false>(i, sm, sh, sigma, nogd, 0.0) : 0.0;
-        win.publish(sm, sh, ks);
-        __syncthreads();
-        const bool last = step == nsteps - 1;
-        const bool lz_step = last && tail;
-        if (ROLE == kChainWave) {
-          // exp(o) = x * 2^E with o = alpha (forward) or v (backward)
-          double x = 0.0;
-          int E = 0;
-          if (chain) {
-            x = chain_sum<NT>(sm, sh, lane) * fx;
-            E = R + nq;
-          }
-          const int Bm = wave_max_i((chain && x > 0.0) ? E + exponent_of(x) : kNoExp);
-          const double a = chain ? ldexp(x, E - Bm) : 0.0;  // exp(o) / 2^Bm
-          double *stg = sm.stg + (step & 1) * (3 * C + 1);
-          if (chain) {
-            stg[lane] = x;
-            stg[C + lane] = (double)E;
-          }
-          if (lz_step) {
-            lz = (double)Bm * kLn2 + log(wave_sum(a));
-          } else {
-            // exp(m) = d * 2^Bm with m = u (forward) or beta (backward)
-            const double d = chain_contract<CMAX>(sm, sh, lane, a);
-            bool rb = false;
-            if (chain) {
-              stg[2 * C + lane] = d;
-              // entry exp(m -+ S) / 2^R = d * fy * 2^(Bm -+ n - R)
-              rb = chain_insert(sm, sh, lane, t, d * fy, Bm - nq - R, R);
-              if (last) {
-                o_end = log(x) + (double)E * kLn2;
-                m_end = log(d) + (double)Bm * kLn2;
-              }
-            }
-            if (lane == 0) stg[3 * C] = (double)Bm;
-            chain_flag(sm, t, rb);
-          }
-        } else if (ROLE == kLoaderWave) {
-          // the next block's scores land in the other buffer before the
-          // barrier that ends this block
-          if (i == U - 1 && s0 + U < nsteps) bl.put(sm, buf ^ 1, C, lane);
-        } else if (rows && step > 0) {
-          const size_t tp = (size_t)(t - sigma) * C;
-          stage_rows(sm.stg + ((step - 1) & 1) * (3 * C + 1), C, row1 + tp, row2 + tp, true, 128,
-                     NT - 128);
-        }
-        if (!lz_step) {
-          __syncthreads();
-          if (sm.flag[t & 1]) {
-            win.rebase(sm, sh, t, sigma);
-            __syncthreads();
-          }
-        }
-        if (last) done = true;
-      }
+}  // namespace
+
+// The chain wave's part of one block (all 64 lanes of wave 0 call; lane c <
+// C = label c): nb serial steps, then the shifts the older ring entries of
+// each label still need.  The far parts are in part[i][g][c]; the block's own
+// entries go straight into the ring (and, for the near part, into the
+// history hist[0] = newest), so a rebase rescales those in place.
+template <int CMAX>
+__device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &sm, int G, int s0,
+                                            int nb, int nsteps, int t0, int sigma, int buf,
+                                            bool tail, int lane, bool chain,
+                                            const double (&Dn)[U], const double (&tr)[CMAX],
+                                            int &R, double &o_end, double &m_end, double &lz) {
+  const int C = sh.C, K = sh.K, S = 3 * C + 1;
+  // reduce the far partials of each step into the g = 0 slot
+  if (chain) {
+    for (int i = 0; i < nb; ++i) {
+      double f = 0.0;
+      for (int g = 0; g < G; ++g) f += sm.part[(i * G + g) * C + lane];
+      sm.part[i * G * C + lane] = f;
     }
   }
+  double hist[U - 1];
+#pragma unroll
+  for (int k = 0; k < U - 1; ++k) hist[k] = 0.0;
+  int shacc = 0;                     // rebase shift of this label since the block began
+  int slot = pos_slot(t0, K);        // ring slot of the step's position
+  double *stg = sm.stg + buf * U * S;
+#pragma unroll 1
+  for (int i = 0; i < nb; ++i) {
+    const int step = s0 + i;
+    const int t = t0 + sigma * i;
+    const bool last = step == nsteps - 1;
+    const bool lz_step = last && tail;
+    double x = 0.0, fy = 0.0;
+    int E = 0, nq = 0;
+    if (chain) {
+      const int o = (buf * U + i) * C + lane;
+      const double fx = sm.efx[o];
+      fy = sm.efy[o];
+      nq = sigma * sm.en[o];
+      double nr = 0.0;  // near part: this block's own entries
+#pragma unroll
+      for (int k = 1; k < U; ++k) nr = fma(Dn[k], hist[k - 1], nr);
+      x = (ldexp(sm.part[i * G * C + lane], -shacc) + nr) * fx;  // exp(o) = x * 2^E
+      E = R + nq;
+    }
+    const int Bm = wave_max_i((chain && x > 0.0) ? E + exponent_of(x) : kNoExp);
+    const double a = chain ? ldexp(x, E - Bm) : 0.0;  // exp(o) / 2^Bm
+    if (chain) {
+      stg[i * S + lane] = x;
+      stg[i * S + C + lane] = (double)E;
+    }
+    if (lz_step) {
+      lz = (double)Bm * kLn2 + log(wave_sum(a));
+    } else {
+      // exp(m) = d * 2^Bm, m = u (forward) or beta (backward)
+      const double d = chain_contract<CMAX>(sm, sh, lane, a, tr);
+      if (chain) {
+        stg[i * S + 2 * C + lane] = d;
+        // entry exp(m -+ S) / 2^R = y * 2^s
+        const double y = d * fy;
+        const int s = Bm - nq - R;
+        const int ey = exponent_of(y) + s;
+        const int n = (ey > kRebaseExp || ey < -kRebaseExp) ? ey : 0;
+        if (n != 0) {  // rebase: this block's earlier entries follow at once
+          R += n;
+          shacc += n;
+#pragma unroll
+          for (int k = 0; k < U - 1; ++k) hist[k] = ldexp(hist[k], -n);
+          int sl = slot;
+          for (int m = 0; m < i; ++m) {
+            sl -= sigma;
+            sl += sl < 0 ? K : 0;
+            sl -= sl >= K ? K : 0;
+            sm.ring[sl * C + lane] = ldexp(sm.ring[sl * C + lane], -n);
+          }
+        }
+        const double g = ldexp(y, s - n);
+        sm.ring[slot * C + lane] = g;
+#pragma unroll
+        for (int k = U - 2; k > 0; --k) hist[k] = hist[k - 1];
+        hist[0] = g;
+        if (last) {
+          o_end = log(x) + (double)E * kLn2;
+          m_end = log(d) + (double)Bm * kLn2;
+        }
+      }
+      if (lane == 0) stg[i * S + 3 * C] = (double)Bm;
+    }
+    slot += sigma;
+    slot += slot < 0 ? K : 0;
+    slot -= slot >= K ? K : 0;
+  }
+  if (chain) sm.shiftn[lane] = shacc;
+  const bool any = __any((chain && shacc != 0) ? 1 : 0);
+  if (lane == 0) sm.flag[0] = any ? 1 : 0;
 }
 
 // ------------------------------------------------------------------ sweeps
@@ -447,9 +411,7 @@ __device__ __forceinline__ void sweep_w_loop(const ChainShape &sh, const WSmem &
 // iteration 0 (exact at the sequence end the chain starts from, neutral
 // elsewhere), re-read afterwards.  The chunk that ends its chain yields log Z
 // in its own frame; every other chunk writes its end state.
-// Per step: K-sum by every thread (one new ring value each), barrier, the
-// chain wave's serial part, barrier; plus the rare rebase mini-phase.
-template <int NT, int AMAX, int U, int CMAX>
+template <int NT, int CMAX>
 __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__restrict__ trans,
                                                 const float *__restrict__ dur, Escaled es,
                                                 const int32_t *__restrict__ lengths, PitBufs pb,
@@ -463,17 +425,24 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   const int tid = threadIdx.x, C = sh.C, K = sh.K, T = sh.T;
   const int lane = tid & 63;
   const bool chain = tid < C;  // lanes of wave 0
-  const bool wave0 = tid < 64;
   if (L < 1 || L > T) return;
   const int p0 = jc * sh.delta;
   if (p0 >= L) return;
   const int p1 = min(p0 + sh.delta, L);
   const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + jc;
   if (iter > 0 && (pb.nbad[iter - 1] == 0 || pb.redo[idx] == 0)) return;
-  const WSmem sm = wcarve(lds, sh);
-  Win<AMAX, U> win;
-  win.init(sh, dur);
-  stage_trans(sm, sh, trans, fwd, NT);
+  const WSmem sm = wcarve(lds, sh, NT);
+  Win win;
+  win.init(sh);
+  stage_dur(sm, sh, dur, NT);
+  double Dn[U];      // near-part weights of the chain lanes
+  double tr[CMAX];   // exp(trans) row of the chain lanes
+  if (tid < 64) {
+#pragma unroll
+    for (int k = 0; k < U; ++k)
+      Dn[k] = (chain && k >= 1 && k <= K) ? exp((double)dur[(size_t)(k - 1) * C + lane]) : 0.0;
+    load_tr_row<CMAX>(sh, trans, fwd, lane, tr);
+  }
   const size_t ob = (size_t)b * (T + 1) * C;
   const size_t cks = ck_stride(C, K);
   double *rec_start = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
@@ -519,11 +488,8 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
     double o0, m0;
     wload(rec_start, sm, sh, chain, lane, R, o0, m0, NT);
   }
-  __syncthreads();
-
   const int first = fwd ? p0 + 1 : p1 - 1;
   const int nsteps = p1 - p0;
-  double o_end = 0.0, m_end = 0.0, lz = 0.0;
   {  // the first block's scores (later blocks: the loader wave, a block ahead)
     const int npair = min(U, nsteps) * C;
     for (int q = tid; q < npair; q += NT) {
@@ -537,28 +503,61 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   }
   vm_drain();
   __syncthreads();
+
+  double o_end = 0.0, m_end = 0.0, lz = 0.0;
+  // wave roles: 0 the chain, 1 the score loader, 2-3 the row writers
   const int w = tid >> 6;
-  if (w == 0)
-    sweep_w_loop<kChainWave, NT, AMAX, U, CMAX>(sh, sm, win, es, ob, first, nsteps, sigma, fwd,
-                                                tail, rows, row1, row2, lane, chain, R, o_end,
-                                                m_end, lz);
-  else if (w == 1)
-    sweep_w_loop<kLoaderWave, NT, AMAX, U, CMAX>(sh, sm, win, es, ob, first, nsteps, sigma, fwd,
-                                                 tail, rows, row1, row2, lane, chain, R, o_end,
-                                                 m_end, lz);
-  else
-    sweep_w_loop<kRowWaves, NT, AMAX, U, CMAX>(sh, sm, win, es, ob, first, nsteps, sigma, fwd,
-                                               tail, rows, row1, row2, lane, chain, R, o_end,
-                                               m_end, lz);
+  const int G = part_groups(sh, NT), S = 3 * C + 1;
+  BlockLoad bl;
+  for (int s0 = 0; s0 < nsteps; s0 += U) {
+    const int nb = min(U, nsteps - s0);  // steps in this block
+    const int t0 = first + sigma * s0;
+    const int buf = (s0 / U) & 1;
+    const bool more = s0 + U < nsteps;
+    if (w == 1 && more) bl.issue(es, ob, first, sigma, s0 + U, T, C, lane, fwd);
+    {
+      double F[U];
+      win.far(sm, sh, t0, sigma, F);
+      win.publish(sm, sh, NT, F);
+    }
+    __syncthreads();
+    if (w == 0) {
+      chain_block<CMAX>(sh, sm, G, s0, nb, nsteps, t0, sigma, buf, tail, lane, chain, Dn, tr, R,
+                        o_end, m_end, lz);
+    } else if (w == 1) {
+      // the next block's scores land in the other buffer before the barrier
+      // that ends this block
+      if (more) bl.put(sm, buf ^ 1, C, lane);
+    } else if (rows && s0 > 0) {
+      // the previous block's rows (a full block of U steps)
+      block_rows(sm.stg + (buf ^ 1) * U * S, C, U, t0 - sigma * U, sigma, row1, row2, -1, 128,
+                 NT - 128);
+    }
+    __syncthreads();
+    if (sm.flag[0]) {
+      // rare: rescale the older entries of the labels that rebased (every
+      // slot but the block's new entries)
+      const int nold = K - nb;
+      for (int q = tid; q < nold * C; q += NT) {
+        const int m = 1 + q / C, c = q % C;
+        const int n = sm.shiftn[c];
+        if (n != 0) {
+          const int sl = pos_slot(t0 - sigma * m, K);
+          sm.ring[sl * C + c] = ldexp(sm.ring[sl * C + c], -n);
+        }
+      }
+      __syncthreads();
+    }
+  }
   if (tail) {
     if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
   } else {
     wsave(rec_end, sm, sh, chain, lane, R, o_end, m_end, NT);
   }
-  if (rows) {  // rows of the last step (t = p1 forward, p0 backward)
-    __syncthreads();
-    const size_t tp = (size_t)(fwd ? p1 : p0) * C;
-    stage_rows(sm.stg + ((nsteps - 1) & 1) * (3 * C + 1), C, row1 + tp, row2 + tp, !tail, 0, NT);
+  if (rows) {  // rows of the last block
+    const int s0 = (nsteps - 1) / U * U;
+    block_rows(sm.stg + ((s0 / U) & 1) * U * (3 * C + 1), C, nsteps - s0, first + sigma * s0,
+               sigma, row1, row2, tail ? nsteps - 1 - s0 : -1, 0, NT);
   }
 }
 
@@ -570,12 +569,12 @@ static hipError_t wreport(hipError_t e, const char *what, const ChainShape &sh, 
   return e;
 }
 
-template <int NT, int AMAX, int U, int UC, int CMAX>
+template <int NT, int CMAX>
 struct WinKernels {
   static void attrs() {
     static bool done = false;
     if (!done) {
-      (void)hipFuncSetAttribute((const void *)k_sweep_w<NT, AMAX, U, CMAX>,
+      (void)hipFuncSetAttribute((const void *)k_sweep_w<NT, CMAX>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
       (void)hipGetLastError();
       done = true;
@@ -586,33 +585,22 @@ struct WinKernels {
                           int with_bwd, int iter, hipStream_t st) {
     attrs();
     const size_t lds = win_lds_bytes(sh.C, sh.K, sh.P);
-    if (!lds_fits((const void *)k_sweep_w<NT, AMAX, U, CMAX>, lds))
+    if (!lds_fits((const void *)k_sweep_w<NT, CMAX>, lds))
       return wreport(hipErrorInvalidConfiguration, "k_sweep_w (LDS)", sh, lds);
-    hipLaunchKernelGGL((k_sweep_w<NT, AMAX, U, CMAX>), dim3((with_bwd ? 2 : 1) * sh.B * sh.nchunk),
+    hipLaunchKernelGGL((k_sweep_w<NT, CMAX>), dim3((with_bwd ? 2 : 1) * sh.B * sh.nchunk),
                        dim3(NT), lds, st, sh, trans, dur, es, lengths, pb, iter);
     return wreport(hipGetLastError(), "k_sweep_w", sh, lds);
   }
 };
 
-// Instances: 256 threads; durations per thread AMAX in {8, 16, 32}; unroll
-// block U (also the score-prefetch block; UC is unused), smaller for the
-// 32-duration windows (register budget); contraction bound CMAX in {8, 32}.
-template <int NT, int AMAX, int U, int UC>
-struct WinByC {
-  template <typename F>
-  static hipError_t run(int C, F &&f) {
-    if (C <= 8) return f(WinKernels<NT, AMAX, U, UC, 8>());
-    return f(WinKernels<NT, AMAX, U, UC, 32>());
-  }
-};
-
+// Instances: 256 threads; contraction width CMAX = cpad(C) in {8, 16, 32}.
 template <typename F>
 static hipError_t win_dispatch(const ChainShape &sh, F &&f) {
   // not a windowed shape: the host configuration never selects these
-  if (sh.NT != 256 || sh.A > 32 || sh.C > 32) return hipErrorInvalidValue;
-  if (sh.A <= 8) return WinByC<256, 8, 8, 8>::run(sh.C, f);
-  if (sh.A <= 16) return WinByC<256, 16, 8, 8>::run(sh.C, f);
-  return WinByC<256, 32, 4, 4>::run(sh.C, f);
+  if (sh.NT != 256 || sh.C > 32) return hipErrorInvalidValue;
+  if (sh.C <= 8) return f(WinKernels<256, 8>());
+  if (sh.C <= 16) return f(WinKernels<256, 16>());
+  return f(WinKernels<256, 32>());
 }
 
 hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float *dur,

@@ -104,24 +104,28 @@ __host__ __device__ inline size_t viterbi_lds_bytes(int C, int K, int P, int Q) 
 // o and m are the chain's row outputs at the checkpoint position.
 __host__ __device__ inline size_t ck_stride(int C, int K) { return (size_t)(K + 3) * C; }
 
-// LDS bytes of the windowed chain engine (chain_win.hip, same order as its
-// carve-up): ring, K-sum partials, row staging (two steps), exp(trans)
-// (float64) with rows padded to a multiple of 4, e row (float64, padded),
-// rebase shifts, flags, split scores of two blocks of positions.
+// Positions per block of the windowed engine (chain_win.hip).
+constexpr int kWinU = 8;
+
+// LDS bytes of the windowed chain engine (chain_win.hip, 256 threads, same
+// order as its carve-up): ring, exp(dur) table, far-part partials
+// [U][groups][C], row staging of two blocks, e row (padded to the
+// contraction width 8, 16 or 32), rebase shifts, flags, split scores of two
+// blocks.
 __host__ __device__ inline size_t win_lds_bytes(int C, int K, int P) {
-  const size_t C4 = (size_t)((C + 3) & ~3);
+  const size_t CP = (size_t)(C <= 8 ? 8 : (C <= 16 ? 16 : 32));  // contraction width
+  const int groups = (64 % C) == 0 ? 256 / 64 : P;
   size_t off = 0;
   off += (size_t)K * C * 8;
-  off += (size_t)P * C * 8;
-  off += (size_t)2 * (3 * C + 1) * 8;
+  off += (size_t)K * C * 8;
+  off += (size_t)kWinU * groups * C * 8;
+  off += (size_t)2 * kWinU * (3 * C + 1) * 8;
   off = align_up(off, 16);
-  off += C4 * C * 8;
-  off = align_up(off, 16);
-  off += C4 * 8;
+  off += CP * 8;
   off += (size_t)C * 4;
   off += 2 * 4;
   off = align_up(off, 16);
-  off += (size_t)2 * 8 * C * (8 + 8 + 4);  // split scores of two blocks of up to 8 positions
+  off += (size_t)2 * kWinU * C * (8 + 8 + 4);
   return align_up(off, 16);
 }
 

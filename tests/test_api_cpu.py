@@ -51,6 +51,21 @@ def test_default_checkpoint_interval(lib):
     assert bd.semicrf_default_checkpoint_interval(3, 100) == 3  # capped at T
 
 
+def test_checkpoint_interval_fills_the_sweep(lib):
+    # halved from ceil(sqrt(T*K)) while 2*B*ceil(T/interval) < 256, not below max(2K, 32)
+    assert bd.semicrf_checkpoint_interval(4, 131072, 512) == 4096    # genome: 256 workgroups
+    assert bd.semicrf_checkpoint_interval(1, 1048576, 256) == 8192   # extreme: 256
+    assert bd.semicrf_checkpoint_interval(16, 4096, 64) == 512       # speech: 256 already
+    assert bd.semicrf_checkpoint_interval(32, 512, 32) == 128        # nlp: 256 already
+    assert bd.semicrf_checkpoint_interval(4, 256, 16) == 32          # tiny: floor 2K = 32
+    assert bd.semicrf_checkpoint_interval(64, 100000, 8) == 895      # already >= 512 workgroups
+    assert bd.semicrf_checkpoint_interval(1, 3, 100) == 3            # capped at T
+    assert bd.semicrf_checkpoint_interval(0, 10, 4) == 0
+    for B, T, K in ((4, 131072, 512), (1, 1048576, 256), (2, 777, 5), (3, 50, 80)):
+        d = bd.semicrf_checkpoint_interval(B, T, K)
+        assert 1 <= d <= bd.semicrf_default_checkpoint_interval(T, K)
+
+
 @pytest.mark.parametrize("args,code", [
     ((bd.OP_FWD_BWD, 0, 10, 4, 4), 2),
     ((bd.OP_FWD_BWD, 1, 0, 4, 4), 2),
