@@ -29,6 +29,7 @@ constexpr int kTxTile = 64;   // output tile of the transition GEMM (64 x 64)
 constexpr int kTxRows = 32;   // positions staged in LDS per batch
 constexpr int kDurThreads = 256;
 constexpr int kDurW = 64;     // positions per duration tile
+constexpr long long kPostWorkgroups = 1024;  // grid size the posterior geometry aims for
 
 __device__ __forceinline__ size_t rix(const ChainShape &sh, int b, int t) {
   return ((size_t)b * (sh.T + 1) + t) * sh.C;
@@ -326,37 +327,62 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
 
 // ------------------------------------------------------------ reductions
 // grad_trans = exp(trans) * sum_b w_b sum_seg X;  grad_dur = sum_b w_b sum_span D.
-__global__ void k_post_reduce(ChainShape sh, PostArgs pa, int nseg, int nspan) {
+// One workgroup per kRedOut consecutive outputs (transition entries first,
+// then durations); thread (o, p) sums slice p of the (sequence, partial)
+// list of output o in order, and the slices meet in LDS in a fixed order.
+constexpr int kRedOut = 16, kRedSlices = 16;
+__global__ __launch_bounds__(kRedOut * kRedSlices) void k_post_reduce(ChainShape sh, PostArgs pa,
+                                                                      int nseg, int nspan) {
+  __shared__ double red[kRedSlices][kRedOut];
   const int C = sh.C, K = sh.K;
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
   const int nx = C * C, ng = K * C;
-  if (e >= nx + ng) return;
+  const int o = threadIdx.x % kRedOut, p = threadIdx.x / kRedOut;
+  const int e = blockIdx.x * kRedOut + o;
+  const bool tx = e < nx;
+  const int np = tx ? nseg : nspan;  // partials per sequence of this output
+  const long long n = (long long)sh.B * np;
+  const long long per = (n + kRedSlices - 1) / kRedSlices;
   double acc = 0.0;
-  for (int b = 0; b < sh.B; ++b) {
-    const int L = pa.lengths[b];
-    if (!valid_len(sh, L)) continue;
-    const double w = pa.grad_logz ? (double)pa.grad_logz[b] : 1.0;
-    double sb = 0.0;
-    if (e < nx) {
-      for (int j = 0; j < nseg; ++j) sb += pa.tx_part[((size_t)b * nseg + j) * nx + e];
-    } else {
-      for (int j = 0; j < nspan; ++j) sb += pa.dur_part[((size_t)b * nspan + j) * ng + (e - nx)];
+  if (e < nx + ng) {
+    for (long long q = p * per; q < n && q < (p + 1) * per; ++q) {
+      const int b = (int)(q / np), j = (int)(q % np);
+      const int L = pa.lengths[b];
+      if (!valid_len(sh, L)) continue;
+      const double w = pa.grad_logz ? (double)pa.grad_logz[b] : 1.0;
+      acc += w * (tx ? pa.tx_part[((size_t)b * nseg + j) * nx + e]
+                     : pa.dur_part[((size_t)b * nspan + j) * ng + (e - nx)]);
     }
-    acc += w * sb;
   }
-  if (e < nx)
-    pa.grad_trans[e] = (float)(acc * exp((double)pa.trans[e]));
-  else
-    pa.grad_dur[e - nx] = (float)acc;
+  red[p][o] = acc;
+  __syncthreads();
+  if (p == 0 && e < nx + ng) {
+    double s = 0.0;
+    for (int q = 0; q < kRedSlices; ++q) s += red[q][o];
+    if (tx)
+      pa.grad_trans[e] = (float)(s * exp((double)pa.trans[e]));
+    else
+      pa.grad_dur[e - nx] = (float)s;
+  }
 }
 
 // ------------------------------------------------------------ launch
 void post_geometry(const ChainShape &sh, PostGeom &g) {
   const int R = kCovThreads / sh.C;
   g.cov_ntile = (sh.T + R * kCovJ - 1) / (R * kCovJ);
-  g.tx_seg = 512;
+  // Position segments of the transition GEMM and spans of the duration
+  // kernel: as long as possible (fewer partials to reduce) while the grid
+  // still has about kPostWorkgroups workgroups.
+  const int ntc = (sh.C + kTxTile - 1) / kTxTile;
+  long long want = (kPostWorkgroups + (long long)ntc * ntc * sh.B - 1) / ((long long)ntc * ntc * sh.B);
+  int seg = (int)((sh.T + want - 1) / want);
+  seg = (seg + kTxRows - 1) / kTxRows * kTxRows;
+  g.tx_seg = seg < kTxRows ? kTxRows : (seg > 512 ? 512 : seg);
   g.tx_nseg = (sh.T + g.tx_seg - 1) / g.tx_seg;
-  g.dur_span = 8;  // tiles of kDurW positions per workgroup
+  const int ncg = (sh.C + 15) / 16, npg = (sh.K + kDurLags - 1) / kDurLags;
+  const int ntile = (sh.T + kDurW - 1) / kDurW;
+  want = (kPostWorkgroups + (long long)ncg * npg * sh.B - 1) / ((long long)ncg * npg * sh.B);
+  int span = (int)((ntile + want - 1) / want);
+  g.dur_span = span < 1 ? 1 : (span > 8 ? 8 : span);  // tiles of kDurW positions per workgroup
   g.dur_nspan = (sh.T + g.dur_span * kDurW - 1) / (g.dur_span * kDurW);
   // lag blocks of KB: the smallest power of two >= 4 with CG x ceil(lags / KB) <= threads
   const int cg = sh.C < 16 ? sh.C : 16;
@@ -415,8 +441,8 @@ hipError_t launch_post_reduce(const ChainShape &sh, const PostArgs &pa, hipStrea
   PostGeom g;
   post_geometry(sh, g);
   const int ne = sh.C * sh.C + sh.K * sh.C;
-  hipLaunchKernelGGL(k_post_reduce, dim3((ne + 255) / 256), dim3(256), 0, st, sh, pa, g.tx_nseg,
-                     g.dur_nspan);
+  hipLaunchKernelGGL(k_post_reduce, dim3((ne + kRedOut - 1) / kRedOut), dim3(kRedOut * kRedSlices),
+                     0, st, sh, pa, g.tx_nseg, g.dur_nspan);
   return hipGetLastError();
 }
 
