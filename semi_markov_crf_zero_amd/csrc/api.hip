@@ -65,7 +65,9 @@ bool chain_config(int C, int K, ChainShape &sh) {
 bool win_config(int C, int K, ChainShape &sh) {
   if (C < 1 || C > 32) return false;
   const int NT = 256;
-  const int P = NT / C;
+  int cp = 1;  // label lanes per duration group: C rounded up to a power of two
+  while (cp < C) cp *= 2;
+  const int P = NT / cp;
   const int A = (K + P - 1) / P;
   if (win_lds_bytes(C, K, P) > kMaxDynLds) return false;
   sh.NT = NT;
@@ -96,6 +98,16 @@ int default_delta(int T, int K) {
 // never below max(2K, 32) positions, so each interval spans several
 // segment lengths and forgets its neutral start.
 constexpr long long kSweepWorkgroups = 256;
+
+// Burn-in of a chunk without an exact start (parallel-in-time iteration 0):
+// for intervals of at least 8K positions a quarter of the interval (at least
+// 2K); shorter intervals sweep twice instead (a burn-in long enough to
+// converge would cost as much as the second sweep).
+int burn_in(int delta, int K) {
+  if ((long long)delta < 8LL * K) return 0;
+  const int w = delta / 4;
+  return w < 2 * K ? 2 * K : w;
+}
 
 int effective_delta(int B, int T, int K) {
   int d = default_delta(T, K);
@@ -200,6 +212,7 @@ semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int
     if (op == SEMICRF_OP_VITERBI || !win_config(C, K, sh)) sh = probe;
     sh.delta = ckpt > 0 ? (ckpt < T ? ckpt : T) : effective_delta(B, T, K);
     sh.nchunk = (T + sh.delta - 1) / sh.delta;
+    sh.burn = burn_in(sh.delta, K);
   }
   if (!make_layout(op, B, T, C, K, &sh, lay)) return SEMICRF_ERR_ARG;
   return SEMICRF_OK;

@@ -13,8 +13,8 @@
 //     label c, fills a register window with the entries older than the block
 //     (entries inside it read as 0) and accumulates U sums -- U*A fused
 //     multiply-adds with full instruction-level parallelism.  Partials are
-//     reduced inside each wave when C divides 64 and meet in LDS.  One
-//     workgroup barrier.
+//     reduced inside each wave (DPP) and meet in LDS.  One workgroup
+//     barrier.
 //   * then one "chain wave" (wave 0, lane c = label c) runs the block's U
 //     steps alone, with wave-local synchronisation only: the "near" part
 //     sum_{k<=i} D[k][c] * Gb[i-k] over the block's own new entries
@@ -52,11 +52,11 @@ struct WSmem {
 // Contraction width: C padded to the instance bound 8, 16 or 32.
 __host__ __device__ __forceinline__ int cpad(int c) { return c <= 8 ? 8 : (c <= 16 ? 16 : 32); }
 
-// Partials are pre-reduced inside each wave when C divides 64 (lanes of one
-// label sit C apart); otherwise one partial per duration group.
-__device__ __forceinline__ bool wave_reduced(const ChainShape &sh) { return (64 % sh.C) == 0; }
+// Far-part partials are pre-reduced inside each wave: one partial per wave
+// and label.
 __device__ __forceinline__ int part_groups(const ChainShape &sh, int NT) {
-  return wave_reduced(sh) ? NT / 64 : sh.P;
+  (void)sh;
+  return NT / 64;
 }
 
 // Carve-up; the byte count is win_lds_bytes() in internal.h.
@@ -106,17 +106,58 @@ __device__ __forceinline__ void load_tr_row(const ChainShape &sh, const float *_
                  : 0.0;
 }
 
+// Sum of a float64 over aligned groups of gw consecutive lanes (gw a power of
+// two, 2 <= gw <= 16) by DPP quad permutes and row mirrors; every lane of a
+// group receives the group sum.
+__device__ __forceinline__ double dpp_f64(double v, int ctrl) {
+  const long long b = __builtin_bit_cast(long long, v);
+  int lo = (int)(b & 0xffffffffLL), hi = (int)(b >> 32);
+  switch (ctrl) {
+    case 0xB1:
+      lo = __builtin_amdgcn_update_dpp(lo, lo, 0xB1, 0xf, 0xf, false);
+      hi = __builtin_amdgcn_update_dpp(hi, hi, 0xB1, 0xf, 0xf, false);
+      break;
+    case 0x4E:
+      lo = __builtin_amdgcn_update_dpp(lo, lo, 0x4E, 0xf, 0xf, false);
+      hi = __builtin_amdgcn_update_dpp(hi, hi, 0x4E, 0xf, 0xf, false);
+      break;
+    case 0x141:
+      lo = __builtin_amdgcn_update_dpp(lo, lo, 0x141, 0xf, 0xf, false);
+      hi = __builtin_amdgcn_update_dpp(hi, hi, 0x141, 0xf, 0xf, false);
+      break;
+    default:
+      lo = __builtin_amdgcn_update_dpp(lo, lo, 0x140, 0xf, 0xf, false);
+      hi = __builtin_amdgcn_update_dpp(hi, hi, 0x140, 0xf, 0xf, false);
+      break;
+  }
+  return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double group_sum(double v, int gw) {
+  v += dpp_f64(v, 0xB1);               // quad_perm [1,0,3,2]: lane ^ 1
+  if (gw >= 4) v += dpp_f64(v, 0x4E);  // quad_perm [2,3,0,1]: lane ^ 2
+  if (gw >= 8) v += dpp_f64(v, 0x141); // row_half_mirror: the other quad of 8
+  if (gw >= 16) v += dpp_f64(v, 0x140);  // row_mirror: the other half of 16
+  return v;
+}
+
 // Far parts of the K-sums of a block: thread (kg, kc) owns the durations
-// k = a0 + j, j < nage, of label kc.
+// k = a0 + j, j < nage, of label kc.  Labels take cp lanes of a wave (C
+// rounded up to a power of two; lanes past C idle), so the gw = 64/cp
+// duration groups of one label in a wave are consecutive lanes and their
+// partials add up by DPP.
 struct Win {
-  int kc, kg, a0, nage;
+  int kc, kg, a0, nage, gw;
   bool on;
 
   __device__ __forceinline__ void init(const ChainShape &sh) {
-    const int C = sh.C;
-    kc = threadIdx.x % C;
-    kg = threadIdx.x / C;
-    on = kg < sh.P;
+    const int C = sh.C, tid = threadIdx.x;
+    int cp = 1;
+    while (cp < C) cp *= 2;
+    gw = 64 / cp;
+    kc = (tid & 63) / gw;
+    kg = (tid >> 6) * gw + (tid & 63) % gw;
+    on = kc < C && kg < sh.P;
     a0 = 1 + kg * sh.A;
     int n = on ? sh.K - a0 + 1 : 0;
     n = n < 0 ? 0 : (n > sh.A ? sh.A : n);
@@ -125,9 +166,10 @@ struct Win {
 
   // Step i of the block (position t0 + sigma*i) needs, for duration k, the
   // entry at t0 - sigma*(k - i); positions inside the block (k <= i) and
-  // beyond the window (k - i > K) count 0.  Durations go in chunks of U:
-  // the chunk's U weights and its 2U-1 entries come from LDS, then U*U
+  // beyond the window (k - i > K) count 0.  Durations go in chunks of DCH:
+  // the chunk's weights and its DCH+U-1 entries come from LDS, then U*DCH
   // fused multiply-adds with compile-time register indices.
+  template <int DCH>
   __device__ __forceinline__ void far(const WSmem &sm, const ChainShape &sh, int t0, int sigma,
                                       double (&F)[U]) {
 #pragma unroll
@@ -137,13 +179,13 @@ struct Win {
     // slot of position t0 - sigma*m for m in [1, K]: base - sigma*m brought
     // back into [0, K) by one correction
     const int base = pos_slot(t0, K);
-    for (int jb = 0; jb < nage; jb += U) {
-      double dv[U], wv[2 * U - 1];
+    for (int jb = 0; jb < nage; jb += DCH) {
+      double dv[DCH], wv[DCH + U - 1];
 #pragma unroll
-      for (int jj = 0; jj < U; ++jj)
+      for (int jj = 0; jj < DCH; ++jj)
         dv[jj] = jb + jj < nage ? sm.dtab[(a0 + jb + jj - 1) * C + kc] : 0.0;
 #pragma unroll
-      for (int q = 0; q < 2 * U - 1; ++q) {
+      for (int q = 0; q < DCH + U - 1; ++q) {
         const int m = a0 + jb + q - (U - 1);  // wv[q]: entry at m = k - i, q = jj - i + U - 1
         int sl = base - sigma * m;
         sl += sl < 0 ? K : 0;
@@ -153,7 +195,7 @@ struct Win {
 #pragma unroll
       for (int i = 0; i < U; ++i) {
 #pragma unroll
-        for (int jj = 0; jj < U; ++jj) F[i] = fma(dv[jj], wv[jj - i + U - 1], F[i]);
+        for (int jj = 0; jj < DCH; ++jj) F[i] = fma(dv[jj], wv[jj - i + U - 1], F[i]);
       }
     }
   }
@@ -163,17 +205,16 @@ struct Win {
   __device__ __forceinline__ void publish(const WSmem &sm, const ChainShape &sh, int NT,
                                           double (&F)[U]) {
     const int C = sh.C, G = part_groups(sh, NT);
-    if (wave_reduced(sh)) {
-      const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-      for (int i = 0; i < U; ++i) {
-        double s = F[i];
-        for (int off = C; off < 64; off <<= 1) s += __shfl_xor(s, off);
-        if (lane < C) sm.part[(i * G + w) * C + lane] = s;
+    for (int i = 0; i < U; ++i) {
+      double s = F[i];  // 0 on idle lanes
+      if (gw <= 16) {
+        s = group_sum(s, gw);
+      } else {  // C <= 2: groups span rows
+        for (int off = 1; off < gw; off <<= 1) s += __shfl_xor(s, off);
       }
-    } else if (on) {
-#pragma unroll
-      for (int i = 0; i < U; ++i) sm.part[(i * G + kg) * C + kc] = F[i];
+      if (lane % gw == 0 && kc < C) sm.part[(i * G + w) * C + kc] = s;
     }
   }
 };
@@ -309,16 +350,29 @@ struct BlockLoad {
 // The chain wave's part of one block (all 64 lanes of wave 0 call; lane c <
 // C = label c): nb serial steps, then the shifts the older ring entries of
 // each label still need.  The far parts are in part[i][g][c]; the block's own
-// entries go straight into the ring (and, for the near part, into the
-// history hist[0] = newest), so a rebase rescales those in place.
+// entries go straight into the ring and into the history hist (hist[0] =
+// the previous step's entry) for the near part, so a rebase rescales those
+// in place.  Per step only Dn[1] * (previous entry) of the near part is on
+// the dependent chain; the rest is summed a step ahead, and the next step's
+// LDS inputs are read a step ahead.  Bm, the step scale 2^Bm of the
+// contraction inputs, carries over from step to step and is recomputed (an
+// exact integer maximum) only when some label's exponent leaves
+// [Bm - kScaleSpan, Bm + kScaleSpan]; every value stays exact either way.
+// o / m of step s_rec (the last burn-in step, see k_sweep_w) go to o_rec /
+// m_rec, those of the chain's last step to o_end / m_end.
+constexpr int kScaleSpan = 256;
+
 template <int CMAX>
 __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &sm, int G, int s0,
                                             int nb, int nsteps, int t0, int sigma, int buf,
                                             bool tail, int lane, bool chain,
                                             const double (&Dn)[U], const double (&tr)[CMAX],
-                                            int &R, double &o_end, double &m_end, double &lz) {
+                                            int s_rec, int &R, int &Bm, double &o_rec,
+                                            double &m_rec, double &o_end, double &m_end,
+                                            double &lz) {
   const int C = sh.C, K = sh.K, S = 3 * C + 1;
-  // reduce the far partials of each step into the g = 0 slot
+  const int cl = chain ? lane : 0;  // label whose LDS values this lane reads
+  // reduce the far partials of each step into the g = 0 slot (own column)
   if (chain) {
     for (int i = 0; i < nb; ++i) {
       double f = 0.0;
@@ -326,32 +380,41 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
       sm.part[i * G * C + lane] = f;
     }
   }
-  double hist[U - 1];
+  double hist[U - 1];  // hist[m] = entry of step i-1-m of this block (0 before the block)
 #pragma unroll
   for (int k = 0; k < U - 1; ++k) hist[k] = 0.0;
-  int shacc = 0;                     // rebase shift of this label since the block began
-  int slot = pos_slot(t0, K);        // ring slot of the step's position
+  double nr = 0.0;      // near part of this step without its newest term
+  int shacc = 0;        // rebase shift of this label since the block began
+  int slot = pos_slot(t0, K);  // ring slot of the step's position
   double *stg = sm.stg + buf * U * S;
+  // inputs of step 0
+  double fxn = sm.efx[buf * U * C + cl], fyn = sm.efy[buf * U * C + cl];
+  int nqn = sm.en[buf * U * C + cl];
+  double fsn = sm.part[cl];
 #pragma unroll 1
   for (int i = 0; i < nb; ++i) {
+    const double fx = fxn, fy = fyn, fs = fsn;
+    const int nq = sigma * nqn;
+    if (i + 1 < nb) {  // the next step's inputs, read a step ahead
+      const int o = (buf * U + i + 1) * C + cl;
+      fxn = sm.efx[o];
+      fyn = sm.efy[o];
+      nqn = sm.en[o];
+      fsn = sm.part[(i + 1) * G * C + cl];
+    }
+    // the near part of the next step without its newest term
+    double nrn = 0.0;
+#pragma unroll
+    for (int k = 2; k < U; ++k) nrn = fma(Dn[k], hist[k - 2], nrn);
     const int step = s0 + i;
     const int t = t0 + sigma * i;
     const bool last = step == nsteps - 1;
     const bool lz_step = last && tail;
-    double x = 0.0, fy = 0.0;
-    int E = 0, nq = 0;
-    if (chain) {
-      const int o = (buf * U + i) * C + lane;
-      const double fx = sm.efx[o];
-      fy = sm.efy[o];
-      nq = sigma * sm.en[o];
-      double nr = 0.0;  // near part: this block's own entries
-#pragma unroll
-      for (int k = 1; k < U; ++k) nr = fma(Dn[k], hist[k - 1], nr);
-      x = (ldexp(sm.part[i * G * C + lane], -shacc) + nr) * fx;  // exp(o) = x * 2^E
-      E = R + nq;
-    }
-    const int Bm = wave_max_i((chain && x > 0.0) ? E + exponent_of(x) : kNoExp);
+    // exp(o) = x * 2^E, o = alpha (forward) or v (backward)
+    const double x = chain ? (ldexp(fs, -shacc) + fma(Dn[1], hist[0], nr)) * fx : 0.0;
+    const int E = R + nq;
+    const int ex = (chain && x > 0.0) ? E + exponent_of(x) : kNoExp;
+    if (__any(ex - Bm > kScaleSpan) || !__any(ex - Bm >= -kScaleSpan)) Bm = wave_max_i(ex);
     const double a = chain ? ldexp(x, E - Bm) : 0.0;  // exp(o) / 2^Bm
     if (chain) {
       stg[i * S + lane] = x;
@@ -374,6 +437,7 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
           shacc += n;
 #pragma unroll
           for (int k = 0; k < U - 1; ++k) hist[k] = ldexp(hist[k], -n);
+          nrn = ldexp(nrn, -n);
           int sl = slot;
           for (int m = 0; m < i; ++m) {
             sl -= sigma;
@@ -387,13 +451,20 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
 #pragma unroll
         for (int k = U - 2; k > 0; --k) hist[k] = hist[k - 1];
         hist[0] = g;
-        if (last) {
-          o_end = log(x) + (double)E * kLn2;
-          m_end = log(d) + (double)Bm * kLn2;
+        if (last || step == s_rec) {
+          const double o = log(x) + (double)E * kLn2, m = log(d) + (double)Bm * kLn2;
+          if (last) {
+            o_end = o;
+            m_end = m;
+          } else {
+            o_rec = o;
+            m_rec = m;
+          }
         }
       }
       if (lane == 0) stg[i * S + 3 * C] = (double)Bm;
     }
+    nr = nrn;
     slot += sigma;
     slot += slot < 0 ? K : 0;
     slot -= slot >= K ? K : 0;
@@ -411,7 +482,7 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
 // iteration 0 (exact at the sequence end the chain starts from, neutral
 // elsewhere), re-read afterwards.  The chunk that ends its chain yields log Z
 // in its own frame; every other chunk writes its end state.
-template <int NT, int CMAX>
+template <int NT, int CMAX, int DCH>
 __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__restrict__ trans,
                                                 const float *__restrict__ dur, Escaled es,
                                                 const int32_t *__restrict__ lengths, PitBufs pb,
@@ -455,10 +526,22 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   double *row2 = (fwd ? pb.row_u : pb.row_b) + ob;  // u / beta
 
   int R = 0;  // integer log reference of label `lane` (units of ln2)
+  // Burn-in: at iteration 0 a chunk without an exact start begins wb
+  // positions early (a whole number of blocks) from the neutral state, sweeps
+  // them without writing rows, and stores the state it reaches at its true
+  // start as its start record.  The recursion forgets where it started, so
+  // that record usually already agrees with the predecessor's end and the
+  // verification accepts it after one iteration.
+  const bool exact = fwd ? (jc == 0) : (p1 == L);
+  int wb = 0;
+  if (iter == 0 && !exact) {
+    wb = min(sh.burn, fwd ? p0 : L - p1);
+    wb = wb / U * U;
+  }
+  const int tbegin = fwd ? p0 - wb : p1 + wb;  // where the sweep starts
   if (iter == 0) {
     for (int i = tid; i < K * C; i += NT) sm.ring[i] = 0.0;
     __syncthreads();
-    const bool exact = fwd ? (jc == 0) : (p1 == L);
     if (exact) {
       // entry u[0] - S[0] = 0 forward; beta[L] + S[L] = S[L] backward
       if (chain) {
@@ -474,22 +557,24 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
       // neutral start: every entry of the window (positions inside [0, L]) is 1
       for (int i = tid; i < K * C; i += NT) {
         const int dq = i / C, c = i % C;
-        const int q = tstart - sigma * dq;
+        const int q = tbegin - sigma * dq;
         if (q >= 0 && q <= L) sm.ring[pos_slot(q, K) * C + c] = 1.0;
       }
     }
     __syncthreads();
-    // o = NaN marks a neutral start (never accepted by the verification)
-    wsave(rec_start, sm, sh, chain, lane, R,
-          exact ? -__builtin_huge_val() : __builtin_nan(""), exact ? 0.0 : __builtin_nan(""), NT);
+    // o = NaN marks a neutral start (never accepted by the verification);
+    // after a burn-in the record is written when the sweep reaches tstart
+    if (wb == 0)
+      wsave(rec_start, sm, sh, chain, lane, R,
+            exact ? -__builtin_huge_val() : __builtin_nan(""), exact ? 0.0 : __builtin_nan(""), NT);
     if (exact && chain && rows)  // u[0] = 0 forward, beta[L] = 0 backward
       row2[(size_t)tstart * C + lane] = 0.0;
   } else {
     double o0, m0;
     wload(rec_start, sm, sh, chain, lane, R, o0, m0, NT);
   }
-  const int first = fwd ? p0 + 1 : p1 - 1;
-  const int nsteps = p1 - p0;
+  const int first = tbegin + sigma;
+  const int nsteps = wb + (p1 - p0);
   {  // the first block's scores (later blocks: the loader wave, a block ahead)
     const int npair = min(U, nsteps) * C;
     for (int q = tid; q < npair; q += NT) {
@@ -504,7 +589,8 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   vm_drain();
   __syncthreads();
 
-  double o_end = 0.0, m_end = 0.0, lz = 0.0;
+  double o_end = 0.0, m_end = 0.0, lz = 0.0, o_rec = 0.0, m_rec = 0.0;
+  int Bm = -(1 << 29);  // step scale of the chain; the first step computes it
   // wave roles: 0 the chain, 1 the score loader, 2-3 the row writers
   const int w = tid >> 6;
   const int G = part_groups(sh, NT), S = 3 * C + 1;
@@ -514,22 +600,24 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
     const int t0 = first + sigma * s0;
     const int buf = (s0 / U) & 1;
     const bool more = s0 + U < nsteps;
+    if (wb > 0 && s0 == wb)  // the burn-in ends: the chunk's start record
+      wsave(rec_start, sm, sh, chain, lane, R, o_rec, m_rec, NT);
     if (w == 1 && more) bl.issue(es, ob, first, sigma, s0 + U, T, C, lane, fwd);
     {
       double F[U];
-      win.far(sm, sh, t0, sigma, F);
+      win.template far<DCH>(sm, sh, t0, sigma, F);
       win.publish(sm, sh, NT, F);
     }
     __syncthreads();
     if (w == 0) {
-      chain_block<CMAX>(sh, sm, G, s0, nb, nsteps, t0, sigma, buf, tail, lane, chain, Dn, tr, R,
-                        o_end, m_end, lz);
+      chain_block<CMAX>(sh, sm, G, s0, nb, nsteps, t0, sigma, buf, tail, lane, chain, Dn, tr,
+                        wb - 1, R, Bm, o_rec, m_rec, o_end, m_end, lz);
     } else if (w == 1) {
       // the next block's scores land in the other buffer before the barrier
       // that ends this block
       if (more) bl.put(sm, buf ^ 1, C, lane);
-    } else if (rows && s0 > 0) {
-      // the previous block's rows (a full block of U steps)
+    } else if (rows && s0 > wb) {
+      // the previous block's rows (a full block of U steps, past the burn-in)
       block_rows(sm.stg + (buf ^ 1) * U * S, C, U, t0 - sigma * U, sigma, row1, row2, -1, 128,
                  NT - 128);
     }
@@ -569,12 +657,12 @@ static hipError_t wreport(hipError_t e, const char *what, const ChainShape &sh, 
   return e;
 }
 
-template <int NT, int CMAX>
+template <int NT, int CMAX, int DCH>
 struct WinKernels {
   static void attrs() {
     static bool done = false;
     if (!done) {
-      (void)hipFuncSetAttribute((const void *)k_sweep_w<NT, CMAX>,
+      (void)hipFuncSetAttribute((const void *)k_sweep_w<NT, CMAX, DCH>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
       (void)hipGetLastError();
       done = true;
@@ -585,22 +673,30 @@ struct WinKernels {
                           int with_bwd, int iter, hipStream_t st) {
     attrs();
     const size_t lds = win_lds_bytes(sh.C, sh.K, sh.P);
-    if (!lds_fits((const void *)k_sweep_w<NT, CMAX>, lds))
+    if (!lds_fits((const void *)k_sweep_w<NT, CMAX, DCH>, lds))
       return wreport(hipErrorInvalidConfiguration, "k_sweep_w (LDS)", sh, lds);
-    hipLaunchKernelGGL((k_sweep_w<NT, CMAX>), dim3((with_bwd ? 2 : 1) * sh.B * sh.nchunk),
+    hipLaunchKernelGGL((k_sweep_w<NT, CMAX, DCH>), dim3((with_bwd ? 2 : 1) * sh.B * sh.nchunk),
                        dim3(NT), lds, st, sh, trans, dur, es, lengths, pb, iter);
     return wreport(hipGetLastError(), "k_sweep_w", sh, lds);
   }
 };
 
-// Instances: 256 threads; contraction width CMAX = cpad(C) in {8, 16, 32}.
+// Instances: 256 threads; contraction width CMAX = cpad(C) in {8, 16, 32};
+// duration chunk DCH in {2, 4, 8} (the smallest covering A, else 8).
+template <int CMAX, typename F>
+static hipError_t win_by_dch(const ChainShape &sh, F &&f) {
+  if (sh.A <= 2) return f(WinKernels<256, CMAX, 2>());
+  if (sh.A <= 4) return f(WinKernels<256, CMAX, 4>());
+  return f(WinKernels<256, CMAX, 8>());
+}
+
 template <typename F>
 static hipError_t win_dispatch(const ChainShape &sh, F &&f) {
   // not a windowed shape: the host configuration never selects these
   if (sh.NT != 256 || sh.C > 32) return hipErrorInvalidValue;
-  if (sh.C <= 8) return f(WinKernels<256, 8>());
-  if (sh.C <= 16) return f(WinKernels<256, 16>());
-  return f(WinKernels<256, 32>());
+  if (sh.C <= 8) return win_by_dch<8>(sh, f);
+  if (sh.C <= 16) return win_by_dch<16>(sh, f);
+  return win_by_dch<32>(sh, f);
 }
 
 hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float *dur,

@@ -25,6 +25,7 @@ struct ChainShape {
   int CS;      // previous labels per contraction slice = ceil(C / QT)
   int pf;      // positions per score-prefetch block of the LDS-ring engine (0: none)
   int nload;   // loader waves of the LDS-ring engine
+  int burn;    // burn-in positions of a chunk without an exact start (iteration 0)
   int delta;   // checkpoint interval (positions)
   int nchunk;  // ceil(T / delta) chunks per sequence
   int center;  // 1 = subtract the per-label baseline nu
@@ -114,7 +115,8 @@ constexpr int kWinU = 8;
 // blocks.
 __host__ __device__ inline size_t win_lds_bytes(int C, int K, int P) {
   const size_t CP = (size_t)(C <= 8 ? 8 : (C <= 16 ? 16 : 32));  // contraction width
-  const int groups = (64 % C) == 0 ? 256 / 64 : P;
+  (void)P;
+  const int groups = 256 / 64;  // far-part partials: one per wave
   size_t off = 0;
   off += (size_t)K * C * 8;
   off += (size_t)K * C * 8;
