@@ -360,22 +360,26 @@ struct PfLoad {
 // barrier, contraction (a barrier when it is split), insertion, barrier
 // (with the rebase vote).  The row threads leave log Z (tail chunk) or the
 // end-state o / m in lz / o_end / m_end.
+// Steps 1..nsteps run at positions tb + sigma*step; the first wb of them are
+// a burn-in (no rows), after which the state is the chunk's start record.
 template <int ROLE, int NT, int AMAX, int TRMAX, typename DT>
 __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
                                            const Regs<AMAX, TRMAX, DT> &r, const Escaled &es,
-                                           size_t ob, int p0, int p1, int tstart, bool fwd,
-                                           bool tail, bool rows, double *row1, double *row2,
-                                           int &R, double &o_end, double &m_end, double &lz) {
+                                           size_t ob, int tb, int nsteps, int wb,
+                                           double *rec_start, bool fwd, bool tail, bool rows,
+                                           double *row1, double *row2, int &R, double &o_end,
+                                           double &m_end, double &lz) {
   const int tid = threadIdx.x, C = sh.C;
   const bool is_row = tid < C;
   const int isig = fwd ? 1 : -1;
   const int pf = sh.pf;
   const int lid = tid - 64 * sh.Q;  // loader lane
   const int wfirst = 64 * (sh.Q + sh.nload), wn = NT - wfirst;  // writer threads
-  const int nsteps = p1 - p0;  // forward t = p0+1..p1, backward t = p1-1..p0
+  const int tstart = tb;
+  double o_rec = 0.0, m_rec = 0.0;
   PfLoad ld;
   for (int step = 1; step <= nsteps; ++step) {
-    const int t = fwd ? p0 + step : p1 - step;
+    const int t = tb + isig * step;
     const int i = pf > 0 ? (step - 1) % pf : 0;  // position in the prefetch block
     const int buf = pf > 0 ? ((step - 1) / pf) & 1 : 0;
     double fx = 0.0, fy = 0.0;
@@ -412,7 +416,8 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
       x = sum * fx;
       E = R + nq;
     }
-    if (ROLE == kWriteRole && rows && step > 1)
+    const bool prev_rows = rows && step - 1 > wb;  // the previous step is past the burn-in
+    if (ROLE == kWriteRole && prev_rows)
       stage_rows(sprev, C, row1 + tprev, row2 + tprev, 0, C, wfirst, wn);
     const int Bm = rows_max_i((is_row && x > 0.0) ? E + exponent_of(x) : kNoExp, sh, sm);
     double *stg = sm.stg + (step & 1) * (3 * C + 1);
@@ -428,12 +433,12 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
         for (int c = 0; c < C; ++c) z += sm.erow[c];
         lz = (double)Bm * kLn2 + log(z);
       }
-      if (ROLE == kWriteRole && rows && step > 1)
+      if (ROLE == kWriteRole && prev_rows)
         stage_rows(sprev, C, row1 + tprev, row2 + tprev, C, 2 * C, wfirst, wn);
       break;  // the chain's last step (uniform)
     }
     const double d = contract(r, sm, sh);  // exp(m) / 2^Bm, m = u or beta
-    if (ROLE == kWriteRole && rows && step > 1)
+    if (ROLE == kWriteRole && prev_rows)
       stage_rows(sprev, C, row1 + tprev, row2 + tprev, C, 2 * C, wfirst, wn);
     int *vote = reinterpret_cast<int *>(sm.scal) + 8;  // rebase votes of two steps
     bool need = false;
@@ -444,9 +449,15 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
       // entry exp(m -+ S) / 2^R = d * fy * 2^(Bm -+ n - R)
       need = insert_entry(sm, sh, t, d * fy, Bm - nq - R, R);
       if (need) vote[step & 1] = 1;
-      if (last) {
-        o_end = log(x) + (double)E * kLn2;
-        m_end = log(d) + (double)Bm * kLn2;
+      if (last || step == wb) {
+        const double o = log(x) + (double)E * kLn2, m = log(d) + (double)Bm * kLn2;
+        if (last) {
+          o_end = o;
+          m_end = m;
+        } else {
+          o_rec = o;
+          m_rec = m;
+        }
       }
     }
     // the next block's scores land in the other buffer before the barrier
@@ -454,6 +465,7 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
     if (ROLE == kLoadRole && i == pf - 1 && next_blk) ld.put(sm, sh, buf ^ 1, lid);
     __syncthreads();
     if (vote[step & 1]) apply_rebase(r, sm, sh, t, fwd);
+    if (step == wb) save_ckpt(rec_start, sm, sh, R, o_rec, m_rec);  // the burn-in ends
   }
 }
 
@@ -492,10 +504,13 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
   double *row2 = (fwd ? pb.row_u : pb.row_b) + ob;  // u / beta
 
   int R = 0;
+  // burn-in of a chunk without an exact start at iteration 0 (see chain_win.hip)
+  const bool exact = fwd ? (jc == 0) : (p1 == L);
+  const int wb = (iter == 0 && !exact) ? min(sh.burn, fwd ? p0 : L - p1) : 0;
+  const int tb = fwd ? p0 - wb : p1 + wb;  // where the sweep starts
   if (iter == 0) {
     for (int i = tid; i < K * C; i += NT) sm.ring[i] = 0.0;
     __syncthreads();
-    const bool exact = fwd ? (jc == 0) : (p1 == L);
     if (exact) {
       // entry u[0] - S[0] = 0 forward; beta[L] + S[L] = S[L] backward
       if (is_row) {
@@ -511,14 +526,16 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
       // neutral start: every entry of the window (positions inside [0, L]) is 1
       for (int i = tid; i < K * C; i += NT) {
         const int dq = i / C, c = i % C;
-        const int q = tstart - isig * dq;
+        const int q = tb - isig * dq;
         if (q >= 0 && q <= L) sm.ring[(q % K) * C + c] = 1.0;
       }
     }
     __syncthreads();
-    // o = NaN marks a neutral start (never accepted by the verification)
-    save_ckpt(rec_start, sm, sh, R, exact ? -__builtin_huge_val() : __builtin_nan(""),
-              exact ? 0.0 : __builtin_nan(""));
+    // o = NaN marks a neutral start (never accepted by the verification);
+    // after a burn-in the record is written when the sweep reaches tstart
+    if (wb == 0)
+      save_ckpt(rec_start, sm, sh, R, exact ? -__builtin_huge_val() : __builtin_nan(""),
+                exact ? 0.0 : __builtin_nan(""));
     if (exact && is_row && rows)  // u[0] = 0 forward, beta[L] = 0 backward
       row2[(size_t)tstart * C + tid] = 0.0;
     __syncthreads();
@@ -526,12 +543,13 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
     double o0, m0;
     load_ckpt(rec_start, sm, sh, R, o0, m0);
   }
+  const int nsteps = wb + (p1 - p0);
   if (sh.pf > 0) {  // the first block's scores (later blocks: the loader waves)
-    const int npair = min(sh.pf, p1 - p0) * C;
+    const int npair = min(sh.pf, nsteps) * C;
     for (int q = tid; q < npair; q += NT) {
       double fx, fy;
       int n;
-      es_get(es, ob, tstart + isig * (1 + q / C), sh.T, C, q % C, fwd, fx, fy, n);
+      es_get(es, ob, tb + isig * (1 + q / C), sh.T, C, q % C, fwd, fx, fy, n);
       sm.efx[q] = fx;
       sm.efy[q] = fy;
       sm.en[q] = n;
@@ -547,14 +565,14 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
   double o_end = 0.0, m_end = 0.0, lz = 0.0;
   const int w = tid >> 6;
   if (w < sh.Q)
-    sweep_loop<kRowRole, NT>(sh, sm, r, es, ob, p0, p1, tstart, fwd, tail, rows, row1, row2, R,
-                             o_end, m_end, lz);
+    sweep_loop<kRowRole, NT>(sh, sm, r, es, ob, tb, nsteps, wb, rec_start, fwd, tail, rows,
+                             row1, row2, R, o_end, m_end, lz);
   else if (w < sh.Q + sh.nload)
-    sweep_loop<kLoadRole, NT>(sh, sm, r, es, ob, p0, p1, tstart, fwd, tail, rows, row1, row2, R,
-                              o_end, m_end, lz);
+    sweep_loop<kLoadRole, NT>(sh, sm, r, es, ob, tb, nsteps, wb, rec_start, fwd, tail, rows,
+                              row1, row2, R, o_end, m_end, lz);
   else
-    sweep_loop<kWriteRole, NT>(sh, sm, r, es, ob, p0, p1, tstart, fwd, tail, rows, row1, row2, R,
-                               o_end, m_end, lz);
+    sweep_loop<kWriteRole, NT>(sh, sm, r, es, ob, tb, nsteps, wb, rec_start, fwd, tail, rows,
+                               row1, row2, R, o_end, m_end, lz);
   if (tail) {
     if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
   } else {
@@ -562,7 +580,6 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
   }
   if (rows) {  // rows of the last step (t = p1 forward, p0 backward)
     __syncthreads();
-    const int nsteps = p1 - p0;
     const size_t tl = (size_t)(fwd ? p1 : p0) * C;
     stage_rows(sm.stg + (nsteps & 1) * (3 * C + 1), C, row1 + tl, row2 + tl, 0,
                tail ? C : 2 * C, 0, NT);
