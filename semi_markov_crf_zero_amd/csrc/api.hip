@@ -32,6 +32,7 @@ bool chain_config(int C, int K, ChainShape &sh) {
     if (A > amax[i]) continue;
     int QT, CS;
     chain_slices(C, NT, QT, CS);
+    if (CS > kTrwRows) continue;  // the widest slice instance
     if (chain_lds_bytes(C, K, P, QT, 0) > kMaxDynLds) continue;
     if (viterbi_lds_bytes(C, K, P, Q) > kMaxDynLds) continue;
     // helper waves: enough row writers for the 2C logs of a step (two per
@@ -162,6 +163,7 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
       lay.nbad = cv.take((size_t)sh->nchunk * 4);
       lay.lz_part = cv.take((size_t)2 * B * 8);
       lay.shift = cv.take(2 * nck * 8);
+      if (!sh->win && sh->NT == 1024) lay.trw = cv.take(trw_floats(C, sh->QT) * 4);
       if (!bwd) break;
       lay.row_a = cv.take(nS * 8);
       lay.row_u = cv.take(nS * 8);
@@ -247,6 +249,7 @@ PitBufs pit_bufs(void *ws, const Layout &lay, bool bwd) {
   pb.row_u = bwd ? at<double>(ws, lay.row_u) : nullptr;
   pb.row_v = bwd ? at<double>(ws, lay.row_v) : nullptr;
   pb.row_b = bwd ? at<double>(ws, lay.row_b) : nullptr;
+  pb.trw = lay.trw ? at<float>(ws, lay.trw) : nullptr;
   return pb;
 }
 

@@ -70,6 +70,7 @@
 namespace semicrf {
 
 constexpr int kRebaseExp = 260;  // rebase bound, log2 units
+constexpr int kErowPad = 64;     // zero tail of the e row: the widest slice reads past C
 
 struct Smem {
   double *ring, *part, *erow, *scal, *dotp, *stg;
@@ -82,7 +83,7 @@ __device__ __forceinline__ Smem carve(unsigned char *base, const ChainShape &s) 
   size_t off = 0;
   m.ring = reinterpret_cast<double *>(base + off); off += (size_t)s.K * s.C * 8;
   m.part = reinterpret_cast<double *>(base + off); off += (size_t)s.P * s.C * 8;
-  m.erow = reinterpret_cast<double *>(base + off); off += (size_t)s.C * 8;
+  m.erow = reinterpret_cast<double *>(base + off); off += (size_t)(s.C + kErowPad) * 8;
   m.scal = reinterpret_cast<double *>(base + off); off += 8 * 8;
   m.dotp = reinterpret_cast<double *>(base + off); off += (size_t)s.QT * s.C * 8;
   m.stg = reinterpret_cast<double *>(base + off); off += (size_t)2 * (3 * s.C + 1) * 8;
@@ -102,8 +103,12 @@ __device__ __forceinline__ Smem carve(unsigned char *base, const ChainShape &s) 
 template <int AMAX, int TRMAX, typename DT>
 struct Regs {
   using WT = typename std::conditional<(TRMAX <= 16), double, float>::type;
-  DT D[AMAX];    // exp(dur[k-1][c]) for the thread's durations
-  WT Tr[TRMAX];  // exp(trans) slice for the contraction role
+  // The 1024-thread instances (float32 weights) read their exp(trans) slice
+  // from the workspace every step: holding it would take 64 of their 128
+  // registers and spill the loop to scratch.
+  static constexpr bool kGlobalW = std::is_same<DT, float>::value;
+  DT D[AMAX];                    // exp(dur[k-1][c]) for the thread's durations
+  WT Tr[kGlobalW ? 1 : TRMAX];   // exp(trans) slice for the contraction role
   int kc, kp, age0, nage;
   int cc, cq, cp0, ncp;
 };
@@ -133,6 +138,7 @@ __device__ __forceinline__ void init_regs(Regs<AMAX, TRMAX, DT> &r, const ChainS
 template <int AMAX, int TRMAX, typename DT>
 __device__ __forceinline__ void load_trans(Regs<AMAX, TRMAX, DT> &r, const ChainShape &sh,
                                            const float *__restrict__ trans, bool fwd) {
+  if (Regs<AMAX, TRMAX, DT>::kGlobalW) return;
   const int C = sh.C;
 #pragma unroll
   for (int j = 0; j < TRMAX; ++j) {
@@ -194,21 +200,50 @@ __device__ __forceinline__ int rows_max_i(int v, const ChainShape &sh, const Sme
 // Requires sm.erow written and a barrier before the call.  All threads call.
 template <int AMAX, int TRMAX, typename DT>
 __device__ __forceinline__ double contract(const Regs<AMAX, TRMAX, DT> &r, const Smem &sm,
-                                           const ChainShape &sh) {
+                                           const ChainShape &sh, const float *__restrict__ trw) {
   using WT = typename Regs<AMAX, TRMAX, DT>::WT;
-  double dp = 0.0;
+  // weights streamed from the workspace ([c_in][c_out] for this direction);
+  // the base is made opaque here so the loads stay in the step loop instead
+  // of being hoisted into 64 long-lived registers
+  const float *base = trw;
+  if (Regs<AMAX, TRMAX, DT>::kGlobalW) asm volatile("" : "+s"(base));
+  const float *wp = base + (size_t)r.cq * kTrwRows * sh.C + r.cc;
+  // the slice's e values two at a time (cp0 is a multiple of the slice
+  // width, so the pairs are aligned), in batches of 8 with a scheduling
+  // barrier between them: hoisting every load of a wide slice would need
+  // two registers per weight on top of the weights themselves.  Weights past
+  // the slice are 0 (in registers and in the padded table alike) and the e
+  // row has a zero tail, so no bound is checked.
+  const double2 *e2 = reinterpret_cast<const double2 *>(sm.erow + r.cp0);
+  double d0 = 0.0, d1 = 0.0;
+  if (r.ncp > 0) {
 #pragma unroll
-  for (int j = 0; j < TRMAX; ++j) {
-    if (j < r.ncp) {
-      WT w = r.Tr[j];
-      if (!std::is_same<WT, double>::value) {
-        // keep a float32 weight live as float32: converting all TRMAX
-        // weights once, outside the time loop, would double their registers
-        asm volatile("" : "+v"(w));
+    for (int j = 0; j < TRMAX; j += 8) {
+      double2 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = e2[j / 2 + q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        WT w0, w1;
+        if (Regs<AMAX, TRMAX, DT>::kGlobalW) {
+          w0 = (WT)wp[(size_t)(j + 2 * q) * sh.C];
+          w1 = (WT)wp[(size_t)(j + 2 * q + 1) * sh.C];
+        } else {
+          w0 = r.Tr[(j + 2 * q) % (Regs<AMAX, TRMAX, DT>::kGlobalW ? 1 : TRMAX)];
+          w1 = r.Tr[(j + 2 * q + 1) % (Regs<AMAX, TRMAX, DT>::kGlobalW ? 1 : TRMAX)];
+        }
+        if (!std::is_same<WT, double>::value && !Regs<AMAX, TRMAX, DT>::kGlobalW) {
+          // keep a float32 weight live as float32: converting all TRMAX
+          // weights once, outside the time loop, would double their registers
+          asm volatile("" : "+v"(w0), "+v"(w1));
+        }
+        d0 = fma(v[q].x, (double)w0, d0);
+        d1 = fma(v[q].y, (double)w1, d1);
       }
-      dp = fma(sm.erow[r.cp0 + j], (double)w, dp);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  double dp = d0 + d1;
   if (sh.QT > 1) {
     if (r.cq < sh.QT) sm.dotp[r.cq * sh.C + r.cc] = dp;
     __syncthreads();
@@ -367,8 +402,8 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
                                            const Regs<AMAX, TRMAX, DT> &r, const Escaled &es,
                                            size_t ob, int tb, int nsteps, int wb,
                                            double *rec_start, bool fwd, bool tail, bool rows,
-                                           double *row1, double *row2, int &R, double &o_end,
-                                           double &m_end, double &lz) {
+                                           double *row1, double *row2, const float *trw,
+                                           int &R, double &o_end, double &m_end, double &lz) {
   const int tid = threadIdx.x, C = sh.C;
   const bool is_row = tid < C;
   const int isig = fwd ? 1 : -1;
@@ -437,7 +472,7 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
         stage_rows(sprev, C, row1 + tprev, row2 + tprev, C, 2 * C, wfirst, wn);
       break;  // the chain's last step (uniform)
     }
-    const double d = contract(r, sm, sh);  // exp(m) / 2^Bm, m = u or beta
+    const double d = contract(r, sm, sh, trw);  // exp(m) / 2^Bm, m = u or beta
     if (ROLE == kWriteRole && prev_rows)
       stage_rows(sprev, C, row1 + tprev, row2 + tprev, C, 2 * C, wfirst, wn);
     int *vote = reinterpret_cast<int *>(sm.scal) + 8;  // rebase votes of two steps
@@ -489,9 +524,11 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
   const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + jc;
   if (iter > 0 && (pb.nbad[iter - 1] == 0 || pb.redo[idx] == 0)) return;
   Smem sm = carve(lds, sh);
+  for (int i = tid; i < kErowPad; i += NT) sm.erow[sh.C + i] = 0.0;
   Regs<AMAX, TRMAX, DT> r;
   init_regs(r, sh, dur);
   load_trans(r, sh, trans, fwd);
+  const float *trw = pb.trw ? pb.trw + (fwd ? 0 : trw_floats(sh.C, sh.QT) / 2) : nullptr;
   const size_t ob = (size_t)b * (sh.T + 1) * C;
   const size_t cks = ck_stride(C, K);
   double *rec_start = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
@@ -566,13 +603,13 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
   const int w = tid >> 6;
   if (w < sh.Q)
     sweep_loop<kRowRole, NT>(sh, sm, r, es, ob, tb, nsteps, wb, rec_start, fwd, tail, rows,
-                             row1, row2, R, o_end, m_end, lz);
+                             row1, row2, trw, R, o_end, m_end, lz);
   else if (w < sh.Q + sh.nload)
     sweep_loop<kLoadRole, NT>(sh, sm, r, es, ob, tb, nsteps, wb, rec_start, fwd, tail, rows,
-                              row1, row2, R, o_end, m_end, lz);
+                              row1, row2, trw, R, o_end, m_end, lz);
   else
     sweep_loop<kWriteRole, NT>(sh, sm, r, es, ob, tb, nsteps, wb, rec_start, fwd, tail, rows,
-                               row1, row2, R, o_end, m_end, lz);
+                               row1, row2, trw, R, o_end, m_end, lz);
   if (tail) {
     if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
   } else {
@@ -584,6 +621,32 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
     stage_rows(sm.stg + (nsteps & 1) * (3 * C + 1), C, row1 + tl, row2 + tl, 0,
                tail ? C : 2 * C, 0, NT);
   }
+}
+
+// exp(trans) in float32 for the instances that stream their weights, one
+// block of kTrwRows rows per contraction slice q (previous labels
+// c_in = q*CS + j, row j < CS; rows past the slice or past C are 0):
+// trw[0][q][j][c_out] = exp(trans[c_in][c_out]) (forward contraction) and
+// trw[1][q][j][c_out] = exp(trans[c_out][c_in]) (backward).
+__global__ void k_trw(int C, int CS, int QT, const float *__restrict__ trans,
+                      float *__restrict__ trw) {
+  const int per = kTrwRows * C, n = QT * per;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < 2 * n; i += gridDim.x * blockDim.x) {
+    const int d = i / n, e = i % n, q = e / per, j = (e % per) / C, co = e % C;
+    const int ci = q * CS + j;
+    float w = 0.0f;
+    if (j < CS && ci < C)
+      w = (float)exp((double)(d == 0 ? trans[(size_t)ci * C + co] : trans[(size_t)co * C + ci]));
+    trw[i] = w;
+  }
+}
+
+hipError_t launch_trw(int C, int CS, int QT, const float *trans, float *trw, hipStream_t st) {
+  const size_t n = trw_floats(C, QT);
+  int grid = (int)((n + 255) / 256);
+  grid = grid > 1024 ? 1024 : grid;
+  hipLaunchKernelGGL(k_trw, dim3(grid), dim3(256), 0, st, C, CS, QT, trans, trw);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------- dispatch

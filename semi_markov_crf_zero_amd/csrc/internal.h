@@ -33,6 +33,10 @@ struct ChainShape {
 
 constexpr int kMaxC = 256;
 constexpr int kMaxPairs = 4;  // (position, label) score pairs per loader lane and block
+// Rows per contraction slice in the streamed exp(trans) table (the widest
+// slice instance); both directions, QT slices of kTrwRows x C float32 each.
+constexpr int kTrwRows = 64;
+__host__ __device__ inline size_t trw_floats(int C, int QT) { return (size_t)2 * QT * kTrwRows * C; }
 constexpr int kMaxKC = 16384;
 constexpr size_t kMaxLds = 163840;  // gfx950: 160 KB per workgroup (static + dynamic)
 // Dynamic-LDS budget of the configurations: the hardware limit less a small
@@ -67,7 +71,7 @@ __host__ __device__ inline size_t chain_lds_bytes(int C, int K, int P, int QT, i
   size_t off = 0;
   off += (size_t)K * C * 8;            // ring
   off += (size_t)P * C * 8;            // K-sum partials
-  off += (size_t)C * 8;                // e row
+  off += (size_t)(C + 64) * 8;         // e row and its zero tail
   off += 8 * 8;                        // scalars
   off += (size_t)QT * C * 8;           // contraction partials
   off += (size_t)2 * (3 * C + 1) * 8;  // row staging (two steps)
@@ -136,7 +140,7 @@ struct Layout {
   size_t S, es_p, es_m, es_n, nu, tile_sum, anchor, logz, logz_bwd;
   size_t ck_fwd, ck_bwd, end_fwd, end_bwd, redo, corr_i, corr_f, nbad, lz_part, shift;
   size_t row_a, row_u, row_v, row_b;
-  size_t cov_part, cov_part2, cov_anchor, cov_mean, tx_part, dur_part;
+  size_t cov_part, cov_part2, cov_anchor, cov_mean, tx_part, dur_part, trw;
   size_t bp, vbest, vcbest;
   size_t total;
   int ntile;
@@ -182,6 +186,9 @@ struct PitBufs {
   // alpha (t = 1..L) and u (t = 0..L-1), backward v (t = 0..L-1) and beta
   // (t = 1..L); written in each chunk's frame, corrected by k_pit_rows.
   double *row_a, *row_u, *row_v, *row_b;
+  // exp(trans) in float32, [2][C][C] (forward, backward orientation), for the
+  // LDS-ring instances that stream their weights (1024 threads); else NULL.
+  float *trw;
 };
 
 // ---- launchers (scan.hip, chain.hip, chain_win.hip, pit.hip, post.hip,
@@ -209,6 +216,9 @@ hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur
                       const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                       double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
                       hipStream_t st);
+
+// exp(trans) for the weight-streaming instances (chain.hip).
+hipError_t launch_trw(int C, int CS, int QT, const float *trans, float *trw, hipStream_t st);
 
 hipError_t launch_pit_init(const ChainShape &sh, const PitBufs &pb, int niter, hipStream_t st);
 hipError_t launch_pit_verify(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,

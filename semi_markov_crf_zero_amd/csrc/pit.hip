@@ -237,6 +237,10 @@ hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur
   const int niter = sh.nchunk;
   hipError_t e = launch_pit_init(sh, pb, niter, st);
   if (e != hipSuccess) return e;
+  if (pb.trw) {
+    e = launch_trw(sh.C, sh.CS, sh.QT, trans, pb.trw, st);
+    if (e != hipSuccess) return e;
+  }
   for (int it = 0; it < niter; ++it) {
     e = launch_sweep(sh, trans, dur, es, lengths, pb, with_bwd, it, st);
     if (e != hipSuccess) return e;
