@@ -19,6 +19,9 @@ Prints ONE JSON line on stdout:
                per launch from rocprofv3 counters stored under profiles/ (null
                when absent or when the kernel sources changed since)
   cpu_baseline = the float64 oracle timed on this host on the same workload
+  rates      = the fwd+bwd rate over valid positions (sum of L_b in place of
+               B*T), and the semicrf_logz_fwd and semicrf_viterbi rates on the
+               same input (timed after the fwd+bwd steps, same repetitions)
 Diagnostics go to stderr.  --copy-calibration MB runs one device copy of MB
 megabytes after the timed steps (outside them), the reference kernel for
 scaling the FETCH_SIZE / WRITE_SIZE counters.
@@ -126,6 +129,8 @@ def main():
                     choices=["tiny", "nlp", "speech", "genome", "extreme"])
     ap.add_argument("--checkpoint-interval", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rates", action="store_true",
+                    help="skip the logz / Viterbi timings (profiler runs of the fwd+bwd kernels)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -179,6 +184,30 @@ def main():
     log("step %.3f ms (wall), %.3e segment-cells/s, workspace %.1f MB"
         % (ms_step, value, plan.ws_bytes / 1e6))
 
+    # the other entry points on the same input, after (and outside) the
+    # timed fwd+bwd steps: log Z alone and Viterbi, the same repetitions
+    def timed(fn, reps):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t1) * 1e3 / reps
+
+    valid = float(np.sum(np.asarray(inp["lengths"], dtype=np.int64))) * K * C
+    rates = {"fwd_bwd_effective": valid / (ms_step * 1e-3),
+             "unit": "segment-cells/s (effective: sum of L_b in place of B*T)"}
+    if not args.no_rates:
+        lz_ms = timed(bd.LogzPlan(t["emissions"], t["lengths"], t["trans"], t["dur"]).run,
+                      args.steps)
+        vt_ms = timed(bd.ViterbiPlan(t["emissions"], t["lengths"], t["trans"], t["dur"]).run,
+                      args.steps)
+        rates.update({"logz_fwd": cells / (lz_ms * 1e-3), "logz_fwd_ms": lz_ms,
+                      "viterbi": cells / (vt_ms * 1e-3), "viterbi_ms": vt_ms})
+        log("logz_fwd %.3f ms, viterbi %.3f ms" % (lz_ms, vt_ms))
+
     if args.copy_calibration > 0:
         n = int(args.copy_calibration * 1e6) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -214,6 +243,7 @@ def main():
                    "checkpoint_interval": ckpt, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "phase_ms": {n: float(m) for n, m in zip(bd.FWD_BWD_PHASES, phase_ms)},
+        "rates": rates,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)

@@ -154,15 +154,7 @@ def semicrf_cumulative_scores(emissions, lengths, center: bool = True):
 
 def semicrf_logz_fwd(emissions, lengths, trans, dur, center: bool = True):
     """log Z [B] float32."""
-    B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
-    flags = 0 if center else NO_CENTER
-    ws, n = _workspace(OP_LOGZ, B, T, C, K, flags, 0, dev)
-    out = torch.empty(B, dtype=torch.float32, device=dev)
-    rc = load().semicrf_logz_fwd(_ptr(emissions), _ptr(lengths), _ptr(trans), _ptr(dur), B, T, C,
-                                 K, flags, _ptr(out), _ptr(ws), n, _stream(dev))
-    if rc:
-        raise SemiCRFError(rc, "semicrf_logz_fwd")
-    return out
+    return LogzPlan(emissions, lengths, trans, dur, center).run()
 
 
 class FwdBwdPlan:
@@ -225,22 +217,60 @@ def semicrf_fwd_bwd(emissions, lengths, trans, dur, center: bool = True, grad_lo
     return plan.run().outputs()
 
 
+class LogzPlan:
+    """Preallocated output + workspace for repeated semicrf_logz_fwd calls."""
+
+    def __init__(self, emissions, lengths, trans, dur, center=True):
+        B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
+        self.args = (emissions, lengths, trans, dur)
+        self.B, self.T, self.C, self.K = B, T, C, K
+        self.flags = 0 if center else NO_CENTER
+        self.dev = dev
+        self.ws, self.ws_bytes = _workspace(OP_LOGZ, B, T, C, K, self.flags, 0, dev)
+        self.logz = torch.empty(B, dtype=torch.float32, device=dev)
+
+    def run(self):
+        e, l, t, d = self.args
+        rc = load().semicrf_logz_fwd(_ptr(e), _ptr(l), _ptr(t), _ptr(d), self.B, self.T, self.C,
+                                     self.K, self.flags, _ptr(self.logz), _ptr(self.ws),
+                                     self.ws_bytes, _stream(self.dev))
+        if rc:
+            raise SemiCRFError(rc, "semicrf_logz_fwd")
+        return self.logz
+
+
+class ViterbiPlan:
+    """Preallocated outputs + workspace for repeated semicrf_viterbi calls."""
+
+    def __init__(self, emissions, lengths, trans, dur, center=True):
+        B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
+        self.args = (emissions, lengths, trans, dur)
+        self.B, self.T, self.C, self.K = B, T, C, K
+        self.flags = 0 if center else NO_CENTER
+        self.dev = dev
+        self.ws, self.ws_bytes = _workspace(OP_VITERBI, B, T, C, K, self.flags, 0, dev)
+        self.best = torch.empty(B, dtype=torch.float32, device=dev)
+        self.seg_start = torch.empty((B, T), dtype=torch.int32, device=dev)
+        self.seg_len = torch.empty((B, T), dtype=torch.int32, device=dev)
+        self.seg_label = torch.empty((B, T), dtype=torch.int32, device=dev)
+        self.num_segs = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def run(self):
+        e, l, t, d = self.args
+        rc = load().semicrf_viterbi(_ptr(e), _ptr(l), _ptr(t), _ptr(d), self.B, self.T, self.C,
+                                    self.K, self.flags, _ptr(self.best), _ptr(self.seg_start),
+                                    _ptr(self.seg_len), _ptr(self.seg_label),
+                                    _ptr(self.num_segs), _ptr(self.ws), self.ws_bytes,
+                                    _stream(self.dev))
+        if rc:
+            raise SemiCRFError(rc, "semicrf_viterbi")
+        return dict(best_score=self.best, seg_start=self.seg_start, seg_len=self.seg_len,
+                    seg_label=self.seg_label, num_segs=self.num_segs)
+
+
 def semicrf_viterbi(emissions, lengths, trans, dur, center: bool = True):
     """Returns dict(best_score [B] f32, seg_start/seg_len/seg_label [B,T] i32, num_segs [B] i32)."""
-    B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
-    flags = 0 if center else NO_CENTER
-    ws, n = _workspace(OP_VITERBI, B, T, C, K, flags, 0, dev)
-    best = torch.empty(B, dtype=torch.float32, device=dev)
-    ss = torch.empty((B, T), dtype=torch.int32, device=dev)
-    sl = torch.empty((B, T), dtype=torch.int32, device=dev)
-    sc = torch.empty((B, T), dtype=torch.int32, device=dev)
-    ns = torch.empty(B, dtype=torch.int32, device=dev)
-    rc = load().semicrf_viterbi(_ptr(emissions), _ptr(lengths), _ptr(trans), _ptr(dur), B, T, C, K,
-                                flags, _ptr(best), _ptr(ss), _ptr(sl), _ptr(sc), _ptr(ns), _ptr(ws),
-                                n, _stream(dev))
-    if rc:
-        raise SemiCRFError(rc, "semicrf_viterbi")
-    return dict(best_score=best, seg_start=ss, seg_len=sl, seg_label=sc, num_segs=ns)
+    return ViterbiPlan(emissions, lengths, trans, dur, center).run()
 
 
 # short aliases

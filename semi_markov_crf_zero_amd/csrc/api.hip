@@ -127,7 +127,8 @@ struct Carver {
 };
 
 // Workspace layout for an op.  Returns false for an invalid op.
-bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layout &lay) {
+bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layout &lay,
+                 const VShape *vs = nullptr) {
   Carver cv;
   lay = Layout{};
   lay.ntile = (T + scan_tile(C) - 1) / scan_tile(C);
@@ -183,6 +184,21 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
       lay.bp = cv.take(nS * 4);
       lay.vbest = cv.take((size_t)B * 8);
       lay.vcbest = cv.take((size_t)B * 4);
+      if (vs) {  // parallel-in-time decoder
+        const size_t nck = (size_t)B * vs->nchunk;
+        lay.vit_pit = 1;
+        lay.v_pred = cv.take(nS * 4);
+        lay.v_rr = cv.take(nck * K * C * 8);
+        lay.v_re = cv.take(nck * K * C * 8);
+        lay.v_corr = cv.take(nck * 8);
+        lay.v_delta = cv.take(nck * 8);
+        lay.v_redo = cv.take(nck * 4);
+        lay.v_nbad = cv.take((size_t)kVitIters * 4);
+        lay.v_lst_t = cv.take((size_t)B * T * 4);
+        lay.v_lst_c = cv.take((size_t)B * T * 4);
+        lay.v_mark = cv.take((size_t)B * (T + 1) * 4);
+        lay.v_sub = cv.take((size_t)B * vs->nsub * kVSubFields * 4);
+      }
       break;
     default:
       return false;
@@ -193,7 +209,7 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
 
 // Validate sizes/flags and fill the shape + layout.  No launches.
 semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int ckpt,
-                         ChainShape &sh, Layout &lay) {
+                         ChainShape &sh, Layout &lay, VShape *vs_out = nullptr) {
   if (op < SEMICRF_OP_SCAN || op > SEMICRF_OP_VITERBI) return SEMICRF_ERR_ARG;
   if (flags & ~(unsigned)SEMICRF_NO_CENTER) return SEMICRF_ERR_ARG;
   if (ckpt < 0) return SEMICRF_ERR_ARG;
@@ -216,7 +232,11 @@ semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int
     sh.nchunk = (T + sh.delta - 1) / sh.delta;
     sh.burn = burn_in(sh.delta, K);
   }
-  if (!make_layout(op, B, T, C, K, &sh, lay)) return SEMICRF_ERR_ARG;
+  VShape vs;
+  const bool pit = op == SEMICRF_OP_VITERBI && vit_config(B, T, C, K, vs);
+  if (pit) vs.center = sh.center;
+  if (!make_layout(op, B, T, C, K, &sh, lay, pit ? &vs : nullptr)) return SEMICRF_ERR_ARG;
+  if (pit && vs_out) *vs_out = vs;
   return SEMICRF_OK;
 }
 
@@ -426,7 +446,8 @@ semicrf_status_t semicrf_viterbi(const float *emissions, const int32_t *lengths,
     return SEMICRF_ERR_NULL;
   ChainShape sh;
   Layout lay;
-  const semicrf_status_t s = prepare(SEMICRF_OP_VITERBI, B, T, C, K, flags, 0, sh, lay);
+  VShape vs;
+  const semicrf_status_t s = prepare(SEMICRF_OP_VITERBI, B, T, C, K, flags, 0, sh, lay, &vs);
   if (s != SEMICRF_OK) return s;
   if (K > 65535 || C > 65535) return SEMICRF_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < lay.total) return SEMICRF_ERR_WORKSPACE;
@@ -438,9 +459,29 @@ semicrf_status_t semicrf_viterbi(const float *emissions, const int32_t *lengths,
                              nullptr, nullptr, nullptr, at<double>(ws, lay.tile_sum),
                              at<double>(ws, lay.anchor), lay.ntile, st);
   if (e != hipSuccess) return hip_status(e);
-  e = launch_viterbi(sh, trans, dur, S, lengths, at<uint32_t>(ws, lay.bp),
-                     at<double>(ws, lay.vbest), at<int32_t>(ws, lay.vcbest), best_score,
-                     seg_start, seg_len, seg_label, num_segs, st);
+  if (lay.vit_pit) {
+    VBufs vb;
+    vb.bp = at<uint32_t>(ws, lay.bp);
+    vb.pred = at<uint32_t>(ws, lay.v_pred);
+    vb.rec_r = at<double>(ws, lay.v_rr);
+    vb.rec_e = at<double>(ws, lay.v_re);
+    vb.corr = at<double>(ws, lay.v_corr);
+    vb.delta = at<double>(ws, lay.v_delta);
+    vb.redo = at<int>(ws, lay.v_redo);
+    vb.nbad = at<int>(ws, lay.v_nbad);
+    vb.vbest = at<double>(ws, lay.vbest);
+    vb.vcbest = at<int32_t>(ws, lay.vcbest);
+    vb.lst_t = at<int32_t>(ws, lay.v_lst_t);
+    vb.lst_c = at<int32_t>(ws, lay.v_lst_c);
+    vb.mark = at<int32_t>(ws, lay.v_mark);
+    vb.sub = at<int32_t>(ws, lay.v_sub);
+    e = launch_vit_pit(vs, trans, dur, S, lengths, vb, best_score, seg_start, seg_len,
+                       seg_label, num_segs, st);
+  } else {
+    e = launch_viterbi(sh, trans, dur, S, lengths, at<uint32_t>(ws, lay.bp),
+                       at<double>(ws, lay.vbest), at<int32_t>(ws, lay.vcbest), best_score,
+                       seg_start, seg_len, seg_label, num_segs, st);
+  }
   return hip_status(e);
 }
 

@@ -107,31 +107,8 @@ __device__ __forceinline__ void load_tr_row(const ChainShape &sh, const float *_
 }
 
 // Sum of a float64 over aligned groups of gw consecutive lanes (gw a power of
-// two, 2 <= gw <= 16) by DPP quad permutes and row mirrors; every lane of a
-// group receives the group sum.
-__device__ __forceinline__ double dpp_f64(double v, int ctrl) {
-  const long long b = __builtin_bit_cast(long long, v);
-  int lo = (int)(b & 0xffffffffLL), hi = (int)(b >> 32);
-  switch (ctrl) {
-    case 0xB1:
-      lo = __builtin_amdgcn_update_dpp(lo, lo, 0xB1, 0xf, 0xf, false);
-      hi = __builtin_amdgcn_update_dpp(hi, hi, 0xB1, 0xf, 0xf, false);
-      break;
-    case 0x4E:
-      lo = __builtin_amdgcn_update_dpp(lo, lo, 0x4E, 0xf, 0xf, false);
-      hi = __builtin_amdgcn_update_dpp(hi, hi, 0x4E, 0xf, 0xf, false);
-      break;
-    case 0x141:
-      lo = __builtin_amdgcn_update_dpp(lo, lo, 0x141, 0xf, 0xf, false);
-      hi = __builtin_amdgcn_update_dpp(hi, hi, 0x141, 0xf, 0xf, false);
-      break;
-    default:
-      lo = __builtin_amdgcn_update_dpp(lo, lo, 0x140, 0xf, 0xf, false);
-      hi = __builtin_amdgcn_update_dpp(hi, hi, 0x140, 0xf, 0xf, false);
-      break;
-  }
-  return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
-}
+// two, 2 <= gw <= 16) by DPP quad permutes and row mirrors (dpp_f64); every
+// lane of a group receives the group sum.
 
 __device__ __forceinline__ double group_sum(double v, int gw) {
   v += dpp_f64(v, 0xB1);               // quad_perm [1,0,3,2]: lane ^ 1

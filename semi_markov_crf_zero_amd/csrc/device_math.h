@@ -94,6 +94,81 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return max(max(r0, r1), max(r2, r3));
 }
 
+// One DPP lane permutation of a float64 (both halves moved alike), for the
+// aligned-group reductions: 0xB1 quad_perm [1,0,3,2] (lane ^ 1), 0x4E
+// quad_perm [2,3,0,1] (lane ^ 2), 0x141 row_half_mirror (the other quad of
+// 8), 0x140 row_mirror (the other half of 16).  Every lane has a source.
+__device__ __forceinline__ double dpp_f64(double v, int ctrl) {
+  const long long b = __builtin_bit_cast(long long, v);
+  int lo = (int)(b & 0xffffffffLL), hi = (int)(b >> 32);
+  switch (ctrl) {
+    case 0xB1:
+      lo = __builtin_amdgcn_update_dpp(lo, lo, 0xB1, 0xf, 0xf, false);
+      hi = __builtin_amdgcn_update_dpp(hi, hi, 0xB1, 0xf, 0xf, false);
+      break;
+    case 0x4E:
+      lo = __builtin_amdgcn_update_dpp(lo, lo, 0x4E, 0xf, 0xf, false);
+      hi = __builtin_amdgcn_update_dpp(hi, hi, 0x4E, 0xf, 0xf, false);
+      break;
+    case 0x141:
+      lo = __builtin_amdgcn_update_dpp(lo, lo, 0x141, 0xf, 0xf, false);
+      hi = __builtin_amdgcn_update_dpp(hi, hi, 0x141, 0xf, 0xf, false);
+      break;
+    default:
+      lo = __builtin_amdgcn_update_dpp(lo, lo, 0x140, 0xf, 0xf, false);
+      hi = __builtin_amdgcn_update_dpp(hi, hi, 0x140, 0xf, 0xf, false);
+      break;
+  }
+  return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ int dpp_i(int v, int ctrl) {
+  switch (ctrl) {
+    case 0xB1: return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xf, 0xf, false);
+    case 0x4E: return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xf, 0xf, false);
+    case 0x141: return __builtin_amdgcn_update_dpp(v, v, 0x141, 0xf, 0xf, false);
+    default: return __builtin_amdgcn_update_dpp(v, v, 0x140, 0xf, 0xf, false);
+  }
+}
+
+// Maximum (float64) and minimum (int) over aligned groups of ng consecutive
+// lanes, ng a power of two up to 64; every lane of a group receives the
+// result.  All 64 lanes of the wave must call with the same ng.
+__device__ __forceinline__ double group_max(double v, int ng) {
+  if (ng >= 2) v = fmax(v, dpp_f64(v, 0xB1));
+  if (ng >= 4) v = fmax(v, dpp_f64(v, 0x4E));
+  if (ng >= 8) v = fmax(v, dpp_f64(v, 0x141));
+  if (ng >= 16) v = fmax(v, dpp_f64(v, 0x140));
+  if (ng >= 32) v = fmax(v, __shfl_xor(v, 16));
+  if (ng >= 64) v = fmax(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ int group_min_i(int v, int ng) {
+  if (ng >= 2) v = min(v, dpp_i(v, 0xB1));
+  if (ng >= 4) v = min(v, dpp_i(v, 0x4E));
+  if (ng >= 8) v = min(v, dpp_i(v, 0x141));
+  if (ng >= 16) v = min(v, dpp_i(v, 0x140));
+  if (ng >= 32) v = min(v, __shfl_xor(v, 16));
+  if (ng >= 64) v = min(v, __shfl_xor(v, 32));
+  return v;
+}
+
+// Workgroup barrier that orders LDS only: vector-memory loads and stores in
+// flight stay in flight across it (a plain __syncthreads waits for them).
+// Global memory written before it is not guaranteed visible after it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Tie tolerance of the Viterbi decisions: a candidate within
+// 1e-11 (|max| + 1) of the maximum ties with it (segmentations that differ
+// only in the order of segment lengths inside a run of one label score the
+// same in real arithmetic and differ by rounding only).
+__device__ __forceinline__ double viterbi_tie_eps(double best) { return 1e-11 * (fabs(best) + 1.0); }
+
 // Wait for every outstanding vector-memory access of the wave (loads and
 // stores): s_waitcnt vmcnt(0), other counters untouched.  Placed before a
 // loop whose only vector-memory accesses are prefetch loads, it lets the

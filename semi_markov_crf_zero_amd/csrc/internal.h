@@ -142,8 +142,10 @@ struct Layout {
   size_t row_a, row_u, row_v, row_b;
   size_t cov_part, cov_part2, cov_anchor, cov_mean, tx_part, dur_part, trw;
   size_t bp, vbest, vcbest;
+  size_t v_pred, v_rr, v_re, v_corr, v_delta, v_redo, v_nbad, v_lst_t, v_lst_c, v_mark, v_sub;
   size_t total;
   int ntile;
+  int vit_pit;  // Viterbi by the parallel-in-time decoder (vpit.hip)
 };
 
 // Arguments of the posterior pass (post.hip).
@@ -242,5 +244,52 @@ hipError_t launch_viterbi(const ChainShape &sh, const float *trans, const float 
                           int32_t *vcbest, float *best_out, int32_t *seg_start,
                           int32_t *seg_len, int32_t *seg_label, int32_t *num_segs,
                           hipStream_t st);
+
+// Parallel-in-time Viterbi (vpit.hip).  Threads of a sweep workgroup form
+// label groups of NG consecutive lanes: group c owns label c, its lanes
+// split the durations (lane g: k = g + 1 + NG*a) and the previous labels
+// (c' = g + NG*i) of that label.
+struct VShape {
+  int B, T, C, K;
+  int NT;      // sweep threads (256 or 1024)
+  int NG;      // lanes per label group (power of two, 4..64)
+  int A;       // durations per lane = ceil(K / NG)
+  int CA;      // previous labels per lane = ceil(C / NG)
+  int U;       // positions per score-staging block (power of two, 2..min(16, NG))
+  int delta;   // positions per sweep chunk
+  int nchunk;  // ceil(T / delta)
+  int burn;    // burn-in positions of a chunk's first sweep
+  int dbt;     // positions per backtrack sub-chunk (>= K)
+  int nsub;    // ceil(T / dbt)
+  int center;
+};
+
+constexpr int kVitIters = 2;     // parallel verification passes before the serial repair
+constexpr int kVSubFields = 10;  // int32 fields per backtrack sub-chunk (vpit.hip)
+
+struct VBufs {
+  uint32_t *bp;        // [B][C][T+1] decisions at (t, c): k | c' << 16
+  uint32_t *pred;      // [B][C][T+1] predecessor of segment end (t, c): k | previous label << 16
+  double *rec_r;       // [B][nchunk][C][K] chunk start states (ring slots by position mod K)
+  double *rec_e;       // [B][nchunk][C][K] chunk end states
+  double *corr;        // [B][nchunk] offset between a chunk's start and its predecessor's end
+  double *delta;       // [B][nchunk] accumulated offset of a chunk's frame
+  int *redo;           // [B][nchunk]
+  int *nbad;           // [kVitIters]
+  double *vbest;       // [B]
+  int32_t *vcbest;     // [B]
+  int32_t *lst_t, *lst_c;  // [B][T] guessed backtrack walks, by sub-chunk
+  int32_t *mark;       // [B][T+1] walk index * 512 + label of the node ending at t, or -1
+  int32_t *sub;        // [B][nsub][kVSubFields]
+};
+
+inline size_t vit_lds_bytes(int C, int K, int U) {
+  return (size_t)C * K * 8 + (size_t)2 * C * 8 + (size_t)2 * U * C * 8 + 256;
+}
+bool vit_config(int B, int T, int C, int K, VShape &vs);
+hipError_t launch_vit_pit(const VShape &vs, const float *trans, const float *dur,
+                          const double *S, const int32_t *lengths, const VBufs &vb,
+                          float *best_out, int32_t *seg_start, int32_t *seg_len,
+                          int32_t *seg_label, int32_t *num_segs, hipStream_t st);
 
 }  // namespace semicrf

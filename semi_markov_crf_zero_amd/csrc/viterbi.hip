@@ -18,11 +18,12 @@
 // the K most recent ghat rows lives in LDS, backpointers (k, c') are packed
 // as two 16-bit fields per (t, c) in the workspace, and a second kernel
 // walks them back (O(number of segments)).
+#include "device_math.h"
 #include "internal.h"
 
 namespace semicrf {
 
-__device__ __forceinline__ double tie_eps(double best) { return 1e-11 * (fabs(best) + 1.0); }
+__device__ __forceinline__ double tie_eps(double best) { return viterbi_tie_eps(best); }
 
 template <int NT, int AMAX, int TRMAX>
 __global__ __launch_bounds__(NT) void k_viterbi(ChainShape sh, const float *__restrict__ trans,

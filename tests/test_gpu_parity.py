@@ -200,6 +200,30 @@ def test_viterbi_shapes(shape):
     assert_viterbi_equal(gpu_viterbi(inp), oracle.viterbi(inp), label=shape[:4])
 
 
+def test_viterbi_serial_decoder_shape():
+    """C = 8, K = 1100: more durations per lane than the parallel-in-time
+    decoder holds, so the one-workgroup-per-sequence decoder runs."""
+    inp = _case(2, 1500, 8, 1100, [1500, 1200], seed=77, tsd=0.3, dsd=0.3)
+    assert_viterbi_equal(gpu_viterbi(inp), oracle.viterbi(inp), label="serial decoder")
+
+
+def test_viterbi_chunks_that_never_forget():
+    """Switching labels costs 50, so the best path never switches and each
+    label's score depends on every earlier position: no chunk's burn-in
+    reaches a start-independent state, every boundary check fails, and only
+    the in-order repair makes the decoding exact."""
+    rng = np.random.default_rng(5)
+    B, T, C, K = 2, 5000, 3, 5
+    x = (0.01 * rng.standard_normal((B, T, C))).astype(np.float32)
+    tr = np.full((C, C), -50.0, np.float32)
+    np.fill_diagonal(tr, 0.0)
+    du = (0.01 * rng.standard_normal((K, C))).astype(np.float32)
+    inp = dict(emissions=x, lengths=np.array([T, 3777], np.int32), trans=tr, dur=du)
+    g, o = gpu_viterbi(inp), oracle.viterbi(inp)
+    assert_viterbi_equal(g, o, label="sticky")
+    assert np.all(g["seg_label"][0, :g["num_segs"][0]] == g["seg_label"][0, 0])
+
+
 def test_viterbi_tie_break_zero_potentials():
     """Every segmentation ties: the rule yields L unit segments of label 0."""
     for (C, K, T) in [(3, 5, 40), (16, 32, 100), (64, 8, 33)]:
