@@ -68,8 +68,10 @@ bool win_config(int C, int K, ChainShape &sh) {
   const int NT = 256;
   int cp = 1;  // label lanes per duration group: C rounded up to a power of two
   while (cp < C) cp *= 2;
-  const int P = NT / cp;
-  const int A = (K + P - 1) / P;
+  // far parts: durations k >= 2U over the three helper waves
+  const int P = (NT - 64) / cp;
+  const int nfar = K - (2 * kWinU - 1);
+  const int A = nfar > 0 ? (nfar + P - 1) / P : 1;
   if (win_lds_bytes(C, K, P) > kMaxDynLds) return false;
   sh.NT = NT;
   sh.P = P;

@@ -7,29 +7,31 @@
 //
 //   * blocks of U positions.  The K-sum of step i of a block (position t)
 //       sum_{k=1..K} D[k][c] * G[t - sigma*k][c]
-//     reads, for k > i, only entries produced before the block began.  So
-//     at a block's start all 256 threads compute these "far" parts for the
-//     U steps at once: thread (g, c) owns the durations k = a0 .. a0+A-1 of
-//     label c, fills a register window with the entries older than the block
-//     (entries inside it read as 0) and accumulates U sums -- U*A fused
-//     multiply-adds with full instruction-level parallelism.  Partials are
-//     reduced inside each wave (DPP) and meet in LDS.  One workgroup
-//     barrier.
-//   * then one "chain wave" (wave 0, lane c = label c) runs the block's U
-//     steps alone, with wave-local synchronisation only: the "near" part
-//     sum_{k<=i} D[k][c] * Gb[i-k] over the block's own new entries
-//     (registers), the product with exp(+-S), the integer maximum of the
-//     float64 exponents, the C x C contraction (exp(trans) in LDS), the new
-//     entry and its rebase decision.  A rebase (R += n) rescales the block's
-//     entries in registers and is applied to the precomputed far parts as
-//     they are read (exact ldexp).
-//   * at the block end the chain lanes write the block's entries into the
-//     LDS ring; if a label rebased, all threads rescale its older entries
-//     (rare).  One workgroup barrier.
-//   * meanwhile wave 1 prefetches the split scores of the next block into LDS
-//     (its loop issues only loads) and waves 2-3 turn the previous block's
-//     staged values into the per-position log rows (their loop issues only
-//     stores): no global-memory access and no logarithm on the chain.
+//     splits at k = 2U: the "near" terms k < 2U are the 2U-1 newest entries,
+//     which the chain wave keeps in a register window that rolls across
+//     blocks; the "far" terms k >= 2U read only entries produced before the
+//     previous block began.  So while the chain runs block n, the helper
+//     waves 1-3 compute the far parts of block n+1 for its U steps at once:
+//     thread (g, c) owns the durations k = a0 .. a0+A-1 (a0 >= 2U) of label
+//     c, fills a register window with the entries and accumulates U sums --
+//     U*A fused multiply-adds with full instruction-level parallelism.
+//     Partials are reduced inside each wave (DPP) and land in the other of
+//     two LDS buffers.  One workgroup barrier per block.
+//   * the "chain wave" (wave 0, lane c = label c) runs the block's U steps
+//     alone, with wave-local synchronisation only: the near part (one fused
+//     multiply-add on the dependent chain, the rest summed a step ahead),
+//     the product with exp(+-S), the integer maximum of the float64
+//     exponents, the C x C contraction (exp(trans) in registers, the e row
+//     through LDS), the new entry straight into the ring and its rebase
+//     decision.  A rebase (R += n) rescales the register window at once and
+//     reaches the far parts -- computed in the reference the labels had when
+//     the previous block began -- as an exact ldexp when they are read.
+//   * at the block end, if a label rebased, all threads rescale its older
+//     ring entries (rare).
+//   * besides the far parts, wave 1 prefetches the split scores of the next
+//     block into LDS (loads issued first, stored last) and waves 2-3 turn
+//     the previous block's staged values into the per-position log rows: no
+//     global-memory access and no logarithm on the chain.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -42,6 +44,7 @@ namespace {
 
 constexpr int kRebaseExp = 260;  // rebase bound, log2 units
 constexpr int U = kWinU;         // positions per block
+constexpr int kNearW = 2 * U - 1;  // near terms k = 1 .. 2U-1 (the chain's register window)
 
 struct WSmem {
   double *ring, *dtab, *part, *stg, *erow;
@@ -52,11 +55,11 @@ struct WSmem {
 // Contraction width: C padded to the instance bound 8, 16 or 32.
 __host__ __device__ __forceinline__ int cpad(int c) { return c <= 8 ? 8 : (c <= 16 ? 16 : 32); }
 
-// Far-part partials are pre-reduced inside each wave: one partial per wave
-// and label.
+// Far-part partials are pre-reduced inside each wave: one partial per helper
+// wave (all but the chain wave) and label.
 __device__ __forceinline__ int part_groups(const ChainShape &sh, int NT) {
   (void)sh;
-  return NT / 64;
+  return NT / 64 - 1;
 }
 
 // Carve-up; the byte count is win_lds_bytes() in internal.h.
@@ -66,7 +69,8 @@ __device__ __forceinline__ WSmem wcarve(unsigned char *base, const ChainShape &s
   const int C4 = cpad(s.C);
   m.ring = reinterpret_cast<double *>(base + off); off += (size_t)s.K * s.C * 8;
   m.dtab = reinterpret_cast<double *>(base + off); off += (size_t)s.K * s.C * 8;
-  m.part = reinterpret_cast<double *>(base + off); off += (size_t)U * part_groups(s, NT) * s.C * 8;
+  m.part = reinterpret_cast<double *>(base + off);
+  off += (size_t)2 * U * part_groups(s, NT) * s.C * 8;  // [2][U][G][C]
   m.stg = reinterpret_cast<double *>(base + off); off += (size_t)2 * U * (3 * s.C + 1) * 8;
   off = (off + 15) & ~(size_t)15;
   m.erow = reinterpret_cast<double *>(base + off); off += (size_t)C4 * 8;
@@ -118,24 +122,24 @@ __device__ __forceinline__ double group_sum(double v, int gw) {
   return v;
 }
 
-// Far parts of the K-sums of a block: thread (kg, kc) owns the durations
-// k = a0 + j, j < nage, of label kc.  Labels take cp lanes of a wave (C
-// rounded up to a power of two; lanes past C idle), so the gw = 64/cp
-// duration groups of one label in a wave are consecutive lanes and their
-// partials add up by DPP.
+// Far parts of the K-sums of a block: helper thread (kg, kc) owns the
+// durations k = a0 + j, j < nage, of label kc, all k >= 2U.  Labels take cp
+// lanes of a wave (C rounded up to a power of two; lanes past C idle), so
+// the gw = 64/cp duration groups of one label in a wave are consecutive
+// lanes and their partials add up by DPP.
 struct Win {
   int kc, kg, a0, nage, gw;
   bool on;
 
   __device__ __forceinline__ void init(const ChainShape &sh) {
-    const int C = sh.C, tid = threadIdx.x;
+    const int C = sh.C, tid = threadIdx.x, w = tid >> 6;
     int cp = 1;
     while (cp < C) cp *= 2;
     gw = 64 / cp;
     kc = (tid & 63) / gw;
-    kg = (tid >> 6) * gw + (tid & 63) % gw;
-    on = kc < C && kg < sh.P;
-    a0 = 1 + kg * sh.A;
+    kg = (w - 1) * gw + (tid & 63) % gw;  // helper waves 1.. only
+    on = w >= 1 && kc < C && kg < sh.P;
+    a0 = kNearW + 1 + kg * sh.A;
     int n = on ? sh.K - a0 + 1 : 0;
     n = n < 0 ? 0 : (n > sh.A ? sh.A : n);
     nage = n;
@@ -177,10 +181,10 @@ struct Win {
     }
   }
 
-  // Publish the far partials part[i][g][c]: per duration group, or summed
-  // over the wave's groups of one label (all lanes of the workgroup call).
+  // Publish the far partials part[buf][i][w-1][c], summed over the wave's
+  // groups of one label (all lanes of the helper waves call).
   __device__ __forceinline__ void publish(const WSmem &sm, const ChainShape &sh, int NT,
-                                          double (&F)[U]) {
+                                          double (&F)[U], int buf) {
     const int C = sh.C, G = part_groups(sh, NT);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -191,7 +195,7 @@ struct Win {
       } else {  // C <= 2: groups span rows
         for (int off = 1; off < gw; off <<= 1) s += __shfl_xor(s, off);
       }
-      if (lane % gw == 0 && kc < C) sm.part[(i * G + w) * C + kc] = s;
+      if (lane % gw == 0 && kc < C) sm.part[((buf * U + i) * G + (w - 1)) * C + kc] = s;
     }
   }
 };
@@ -324,50 +328,52 @@ struct BlockLoad {
 
 }  // namespace
 
+// The chain wave's state carried from block to block: the register window
+// of the near terms and the rebase shift its labels took during the block
+// before (the far parts being read were computed in the reference they had
+// when that block began).
+struct ChainState {
+  double hist[kNearW];  // hist[m] = entry of the step m+1 steps back (0 outside the window)
+  double nr;            // near part of the next step without its newest term
+  int shprev;
+};
+
 // The chain wave's part of one block (all 64 lanes of wave 0 call; lane c <
 // C = label c): nb serial steps, then the shifts the older ring entries of
-// each label still need.  The far parts are in part[i][g][c]; the block's own
-// entries go straight into the ring and into the history hist (hist[0] =
-// the previous step's entry) for the near part, so a rebase rescales those
-// in place.  Per step only Dn[1] * (previous entry) of the near part is on
-// the dependent chain; the rest is summed a step ahead, and the next step's
-// LDS inputs are read a step ahead.  Bm, the step scale 2^Bm of the
-// contraction inputs, carries over from step to step and is recomputed (an
-// exact integer maximum) only when some label's exponent leaves
-// [Bm - kScaleSpan, Bm + kScaleSpan]; every value stays exact either way.
-// o / m of step s_rec (the last burn-in step, see k_sweep_w) go to o_rec /
-// m_rec, those of the chain's last step to o_end / m_end.
+// each label still need.  The far parts are in part[buf][i][g][c]; the new
+// entries go straight into the ring and into the window, so a rebase
+// rescales those in place.  Per step only Dn[1] * (previous entry) of the
+// near part is on the dependent chain; the rest is summed a step ahead, and
+// the next step's LDS inputs are read a step ahead.  Bm, the step scale
+// 2^Bm of the contraction inputs, carries over from step to step and is
+// recomputed (an exact integer maximum) only when some label's exponent
+// leaves [Bm - kScaleSpan, Bm + kScaleSpan]; every value stays exact either
+// way.  o / m of step s_rec (the last burn-in step, see k_sweep_w) go to
+// o_rec / m_rec, those of the chain's last step to o_end / m_end.
 constexpr int kScaleSpan = 256;
-
 template <int CMAX>
 __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &sm, int G, int s0,
                                             int nb, int nsteps, int t0, int sigma, int buf,
                                             bool tail, int lane, bool chain,
-                                            const double (&Dn)[U], const double (&tr)[CMAX],
-                                            int s_rec, int &R, int &Bm, double &o_rec,
-                                            double &m_rec, double &o_end, double &m_end,
-                                            double &lz) {
+                                            const double (&Dn)[kNearW + 1],
+                                            const double (&tr)[CMAX], int s_rec, ChainState &cs,
+                                            int &R, int &Bm, double &o_rec, double &m_rec,
+                                            double &o_end, double &m_end, double &lz) {
   const int C = sh.C, K = sh.K, S = 3 * C + 1;
   const int cl = chain ? lane : 0;  // label whose LDS values this lane reads
-  // reduce the far partials of each step into the g = 0 slot (own column)
-  if (chain) {
-    for (int i = 0; i < nb; ++i) {
-      double f = 0.0;
-      for (int g = 0; g < G; ++g) f += sm.part[(i * G + g) * C + lane];
-      sm.part[i * G * C + lane] = f;
-    }
-  }
-  double hist[U - 1];  // hist[m] = entry of step i-1-m of this block (0 before the block)
-#pragma unroll
-  for (int k = 0; k < U - 1; ++k) hist[k] = 0.0;
-  double nr = 0.0;      // near part of this step without its newest term
-  int shacc = 0;        // rebase shift of this label since the block began
+  const double *part = sm.part + (size_t)buf * U * G * C;
+  auto far_of = [&](int i) {  // the helper waves' partials of step i, in a fixed order
+    double f = 0.0;
+    for (int g = 0; g < G; ++g) f += part[(i * G + g) * C + cl];
+    return f;
+  };
+  int shacc = 0;               // rebase shift of this label since the block began
   int slot = pos_slot(t0, K);  // ring slot of the step's position
   double *stg = sm.stg + buf * U * S;
   // inputs of step 0
   double fxn = sm.efx[buf * U * C + cl], fyn = sm.efy[buf * U * C + cl];
   int nqn = sm.en[buf * U * C + cl];
-  double fsn = sm.part[cl];
+  double fsn = far_of(0);
 #pragma unroll 1
   for (int i = 0; i < nb; ++i) {
     const double fx = fxn, fy = fyn, fs = fsn;
@@ -377,18 +383,19 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
       fxn = sm.efx[o];
       fyn = sm.efy[o];
       nqn = sm.en[o];
-      fsn = sm.part[(i + 1) * G * C + cl];
+      fsn = far_of(i + 1);
     }
     // the near part of the next step without its newest term
     double nrn = 0.0;
 #pragma unroll
-    for (int k = 2; k < U; ++k) nrn = fma(Dn[k], hist[k - 2], nrn);
+    for (int k = 2; k <= kNearW; ++k) nrn = fma(Dn[k], cs.hist[k - 2], nrn);
     const int step = s0 + i;
     const int t = t0 + sigma * i;
     const bool last = step == nsteps - 1;
     const bool lz_step = last && tail;
     // exp(o) = x * 2^E, o = alpha (forward) or v (backward)
-    const double x = chain ? (ldexp(fs, -shacc) + fma(Dn[1], hist[0], nr)) * fx : 0.0;
+    const double x =
+        chain ? (ldexp(fs, -(cs.shprev + shacc)) + fma(Dn[1], cs.hist[0], cs.nr)) * fx : 0.0;
     const int E = R + nq;
     const int ex = (chain && x > 0.0) ? E + exponent_of(x) : kNoExp;
     if (__any(ex - Bm > kScaleSpan) || !__any(ex - Bm >= -kScaleSpan)) Bm = wave_max_i(ex);
@@ -409,11 +416,11 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
         const int s = Bm - nq - R;
         const int ey = exponent_of(y) + s;
         const int n = (ey > kRebaseExp || ey < -kRebaseExp) ? ey : 0;
-        if (n != 0) {  // rebase: this block's earlier entries follow at once
+        if (n != 0) {  // rebase: the window and this block's ring entries follow at once
           R += n;
           shacc += n;
 #pragma unroll
-          for (int k = 0; k < U - 1; ++k) hist[k] = ldexp(hist[k], -n);
+          for (int k = 0; k < kNearW; ++k) cs.hist[k] = ldexp(cs.hist[k], -n);
           nrn = ldexp(nrn, -n);
           int sl = slot;
           for (int m = 0; m < i; ++m) {
@@ -426,8 +433,8 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
         const double g = ldexp(y, s - n);
         sm.ring[slot * C + lane] = g;
 #pragma unroll
-        for (int k = U - 2; k > 0; --k) hist[k] = hist[k - 1];
-        hist[0] = g;
+        for (int k = kNearW - 1; k > 0; --k) cs.hist[k] = cs.hist[k - 1];
+        cs.hist[0] = g;
         if (last || step == s_rec) {
           const double o = log(x) + (double)E * kLn2, m = log(d) + (double)Bm * kLn2;
           if (last) {
@@ -441,11 +448,12 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
       }
       if (lane == 0) stg[i * S + 3 * C] = (double)Bm;
     }
-    nr = nrn;
+    cs.nr = nrn;
     slot += sigma;
     slot += slot < 0 ? K : 0;
     slot -= slot >= K ? K : 0;
   }
+  cs.shprev = shacc;
   if (chain) sm.shiftn[lane] = shacc;
   const bool any = __any((chain && shacc != 0) ? 1 : 0);
   if (lane == 0) sm.flag[0] = any ? 1 : 0;
@@ -483,11 +491,11 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   Win win;
   win.init(sh);
   stage_dur(sm, sh, dur, NT);
-  double Dn[U];      // near-part weights of the chain lanes
-  double tr[CMAX];   // exp(trans) row of the chain lanes
+  double Dn[kNearW + 1];  // near-part weights of the chain lanes (k = 1 .. 2U-1)
+  double tr[CMAX];        // exp(trans) row of the chain lanes
   if (tid < 64) {
 #pragma unroll
-    for (int k = 0; k < U; ++k)
+    for (int k = 0; k <= kNearW; ++k)
       Dn[k] = (chain && k >= 1 && k <= K) ? exp((double)dur[(size_t)(k - 1) * C + lane]) : 0.0;
     load_tr_row<CMAX>(sh, trans, fwd, lane, tr);
   }
@@ -568,35 +576,59 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
 
   double o_end = 0.0, m_end = 0.0, lz = 0.0, o_rec = 0.0, m_rec = 0.0;
   int Bm = -(1 << 29);  // step scale of the chain; the first step computes it
-  // wave roles: 0 the chain, 1 the score loader, 2-3 the row writers
+  // wave roles: 0 the chain; 1-3 the far parts of the next block, besides
+  // which 1 loads the next block's scores and 2-3 write the previous
+  // block's rows
   const int w = tid >> 6;
   const int G = part_groups(sh, NT), S = 3 * C + 1;
+  ChainState cs;
+  if (w == 0) {
+    // the window from the start state: entry m+1 steps back is at position
+    // tbegin - sigma*m (0 beyond the ring)
+#pragma unroll
+    for (int m = 0; m < kNearW; ++m)
+      cs.hist[m] = (chain && m < K) ? sm.ring[pos_slot(tbegin - sigma * m, K) * C + lane] : 0.0;
+    double nr = 0.0;
+#pragma unroll
+    for (int k = 2; k <= kNearW; ++k) nr = fma(Dn[k], cs.hist[k - 1], nr);
+    cs.nr = nr;
+    cs.shprev = 0;
+  } else {
+    double F[U];  // far parts of the first block
+    win.template far<DCH>(sm, sh, first, sigma, F);
+    win.publish(sm, sh, NT, F, 0);
+  }
+  __syncthreads();
   BlockLoad bl;
   for (int s0 = 0; s0 < nsteps; s0 += U) {
     const int nb = min(U, nsteps - s0);  // steps in this block
     const int t0 = first + sigma * s0;
     const int buf = (s0 / U) & 1;
     const bool more = s0 + U < nsteps;
-    if (wb > 0 && s0 == wb)  // the burn-in ends: the chunk's start record
+    if (wb > 0 && s0 == wb) {  // the burn-in ends: the chunk's start record
       wsave(rec_start, sm, sh, chain, lane, R, o_rec, m_rec, NT);
-    if (w == 1 && more) bl.issue(es, ob, first, sigma, s0 + U, T, C, lane, fwd);
-    {
-      double F[U];
-      win.template far<DCH>(sm, sh, t0, sigma, F);
-      win.publish(sm, sh, NT, F);
+      __syncthreads();  // read before the chain overwrites ring slots
     }
-    __syncthreads();
     if (w == 0) {
       chain_block<CMAX>(sh, sm, G, s0, nb, nsteps, t0, sigma, buf, tail, lane, chain, Dn, tr,
-                        wb - 1, R, Bm, o_rec, m_rec, o_end, m_end, lz);
-    } else if (w == 1) {
+                        wb - 1, cs, R, Bm, o_rec, m_rec, o_end, m_end, lz);
+    } else {
+      if (w == 1 && more) bl.issue(es, ob, first, sigma, s0 + U, T, C, lane, fwd);
+      if (w >= 2 && rows && s0 > wb) {
+        // the previous block's rows (a full block of U steps, past the burn-in)
+        block_rows(sm.stg + (buf ^ 1) * U * S, C, U, t0 - sigma * U, sigma, row1, row2, -1, 128,
+                   NT - 128);
+      }
+      if (more) {
+        // far parts of the next block: entries older than this block only,
+        // none of the slots the chain writes meanwhile
+        double F[U];
+        win.template far<DCH>(sm, sh, t0 + sigma * U, sigma, F);
+        win.publish(sm, sh, NT, F, buf ^ 1);
+      }
       // the next block's scores land in the other buffer before the barrier
       // that ends this block
-      if (more) bl.put(sm, buf ^ 1, C, lane);
-    } else if (rows && s0 > wb) {
-      // the previous block's rows (a full block of U steps, past the burn-in)
-      block_rows(sm.stg + (buf ^ 1) * U * S, C, U, t0 - sigma * U, sigma, row1, row2, -1, 128,
-                 NT - 128);
+      if (w == 1 && more) bl.put(sm, buf ^ 1, C, lane);
     }
     __syncthreads();
     if (sm.flag[0]) {

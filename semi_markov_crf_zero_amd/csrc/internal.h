@@ -120,11 +120,11 @@ constexpr int kWinU = 8;
 __host__ __device__ inline size_t win_lds_bytes(int C, int K, int P) {
   const size_t CP = (size_t)(C <= 8 ? 8 : (C <= 16 ? 16 : 32));  // contraction width
   (void)P;
-  const int groups = 256 / 64;  // far-part partials: one per wave
+  const int groups = 256 / 64 - 1;  // far-part partials: one per helper wave
   size_t off = 0;
   off += (size_t)K * C * 8;
   off += (size_t)K * C * 8;
-  off += (size_t)kWinU * groups * C * 8;
+  off += (size_t)2 * kWinU * groups * C * 8;
   off += (size_t)2 * kWinU * (3 * C + 1) * 8;
   off = align_up(off, 16);
   off += CP * 8;
