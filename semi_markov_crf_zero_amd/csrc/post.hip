@@ -244,10 +244,21 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
 // a[s,c] = u[s,c] - S[s,c] and b[e,c] = S[e,c] + beta[e,c] - logZ, for
 // s + k <= L.  One workgroup per (label group of up to 16, lag group of up
 // to kDurLags lags, sequence, span of position tiles); thread (label cl, lag
-// block kb) owns KB consecutive lags and keeps b[s+k0 .. s+k0+KB-1] in a
-// sliding register window, so each position costs one LDS read of a and one
-// of b.  LDS: a for the tile's positions, b for the ends its lags reach.
+// block kb) owns KB consecutive lags.  LDS: a for the tile's positions, b
+// for the ends its lags reach.
+//
+// Each term factors as exp(a[s] - r) * exp(b[s+k] + r) * exp(dur), so per
+// tile and label, with r the tile's largest a, the sum over s is an
+// exp-space correlation: one float64 fused multiply-add per segment cell,
+// in blocks of 8 starts x 8 lags from a register window, and exp(dur)
+// applied once at the end.  Every factor stays within exp(+-(range of a
+// over the tile + |dur|)): a segment starting inside the tile has
+// probability at most 1, and a start and an end at most K + kDurW apart
+// relate through one.  A tile whose range of a exceeds kDurRange nats (only
+// with extreme scores) takes the direct path for that label: one exp per
+// cell.
 constexpr int kDurLags = 512;
+constexpr double kDurRange = 600.0;
 
 template <int KB>
 __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs pa, int span,
@@ -265,10 +276,15 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
   const int L = pa.lengths[b];
   double *sa = reinterpret_cast<double *>(lds);  // [kDurW][16]
   double *sb = sa + (size_t)kDurW * 16;          // [kDurW + kDurLags][16], index e - s0 - klo
-  double acc[KB], dk[KB];
+  double *pmax = sb + (size_t)(kDurW + min(K, kDurLags)) * 16;  // [16][16] partial max / min of a
+  double *pmin = pmax + 256;
+  double *rho = pmin + 256;                      // [16] reference per label
+  int *fast = reinterpret_cast<int *>(rho + 16);  // [16]
+  double accf[KB], accs[KB], dk[KB];
 #pragma unroll
   for (int j = 0; j < KB; ++j) {
-    acc[j] = 0.0;
+    accf[j] = 0.0;
+    accs[j] = 0.0;
     const int k = k0 + j;
     dk[j] = (act && k <= khi) ? (double)pa.dur[(size_t)(k - 1) * C + c] : 0.0;
   }
@@ -294,9 +310,62 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
         sb[ee * 16 + cc] = (Sb[(size_t)e * C + c0 + cc] + pa.row_b[ri]) - logZ;
       }
       __syncthreads();
-      if (act) {
-        // window w[j] = b[s + k0 + j], index (s - s0) + (k0 - klo) + j
-        const int kofs = k0 - klo;
+      {  // per label: the largest a of the tile and its range
+        const int cc = tid & 15, part = tid >> 4;
+        double hi = -__builtin_huge_val(), lo = __builtin_huge_val();
+        if (cc < CG)
+          for (int ss = part; ss < ns; ss += 16) {
+            const double v = sa[ss * 16 + cc];
+            hi = fmax(hi, v);
+            lo = fmin(lo, v);
+          }
+        pmax[part * 16 + cc] = hi;
+        pmin[part * 16 + cc] = lo;
+      }
+      __syncthreads();
+      if (tid < 16) {
+        double hi = -__builtin_huge_val(), lo = __builtin_huge_val();
+        for (int q = 0; q < 16; ++q) {
+          hi = fmax(hi, pmax[q * 16 + tid]);
+          lo = fmin(lo, pmin[q * 16 + tid]);
+        }
+        rho[tid] = hi;
+        fast[tid] = (hi - lo <= kDurRange) ? 1 : 0;  // false for non-finite ranges
+      }
+      __syncthreads();
+      for (int i = tid; i < ns * CG; i += kDurThreads) {
+        const int ss = i / CG, cc = i % CG;
+        if (fast[cc]) sa[ss * 16 + cc] = exp_wide(sa[ss * 16 + cc] - rho[cc]);
+      }
+      for (int i = tid; i < ne * CG; i += kDurThreads) {
+        const int ee = i / CG, cc = i % CG;
+        if (fast[cc]) sb[ee * 16 + cc] = exp_wide(sb[ee * 16 + cc] + rho[cc]);
+      }
+      __syncthreads();
+      if (!act) continue;
+      const int kofs = k0 - klo;  // end index of (s0 + ss, k0 + j): ss + kofs + j
+      if (fast[cl]) {
+        constexpr int JB = KB < 8 ? KB : 8;
+        for (int ss0 = 0; ss0 < ns; ss0 += 8) {
+          double A[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) A[i] = ss0 + i < ns ? sa[(ss0 + i) * 16 + cl] : 0.0;
+#pragma unroll
+          for (int jb = 0; jb < KB; jb += JB) {
+            double W[8 + JB - 1];
+#pragma unroll
+            for (int q = 0; q < 8 + JB - 1; ++q) {
+              const int ee = ss0 + kofs + jb + q;
+              W[q] = ee < ne ? sb[ee * 16 + cl] : 0.0;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+              for (int j = 0; j < JB; ++j) accf[jb + j] = fma(A[i], W[i + j], accf[jb + j]);
+          }
+        }
+      } else {
+        // window w[j] = b[s + k0 + j], index (s - s0) + kofs + j
         double w[KB];
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
@@ -306,7 +375,7 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
         for (int ss = 0; ss < ns; ++ss) {
           const double av = sa[ss * 16 + cl];
 #pragma unroll
-          for (int j = 0; j < KB; ++j) acc[j] += exp_wide(av + w[j] + dk[j]);
+          for (int j = 0; j < KB; ++j) accs[j] += exp_wide(av + w[j] + dk[j]);
 #pragma unroll
           for (int j = 0; j < KB - 1; ++j) w[j] = w[j + 1];
           const int ee = ss + 1 + kofs + KB - 1;
@@ -320,7 +389,7 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       const int k = k0 + j;
-      if (k <= khi) out[(size_t)(k - 1) * C + c] = acc[j];
+      if (k <= khi) out[(size_t)(k - 1) * C + c] = fma(exp(dk[j]), accf[j], accs[j]);
     }
   }
 }
@@ -390,7 +459,8 @@ void post_geometry(const ChainShape &sh, PostGeom &g) {
   g.dur_kb = 4;
   while (g.dur_kb < 32 && cg * ((lags + g.dur_kb - 1) / g.dur_kb) > kDurThreads) g.dur_kb *= 2;
   g.dur_npg = (sh.K + kDurLags - 1) / kDurLags;
-  g.dur_lds = (size_t)(kDurW + kDurW + lags) * 16 * 8;
+  // a, b, partial maxima and minima of a, per-label references and paths
+  g.dur_lds = (size_t)(kDurW + kDurW + lags) * 16 * 8 + 2 * 256 * 8 + 16 * 8 + 16 * 4;
 }
 
 hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream_t st) {
