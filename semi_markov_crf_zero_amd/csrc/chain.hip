@@ -83,6 +83,7 @@ __device__ __forceinline__ Smem carve(unsigned char *base, const ChainShape &s) 
   size_t off = 0;
   m.ring = reinterpret_cast<double *>(base + off); off += (size_t)s.K * s.C * 8;
   m.part = reinterpret_cast<double *>(base + off); off += (size_t)s.P * s.C * 8;
+  off = (off + 15) & ~(size_t)15;  // the e row is read as 16-byte pairs
   m.erow = reinterpret_cast<double *>(base + off); off += (size_t)(s.C + kErowPad) * 8;
   m.scal = reinterpret_cast<double *>(base + off); off += 8 * 8;
   m.dotp = reinterpret_cast<double *>(base + off); off += (size_t)s.QT * s.C * 8;
@@ -208,8 +209,9 @@ __device__ __forceinline__ double contract(const Regs<AMAX, TRMAX, DT> &r, const
   const float *base = trw;
   if (Regs<AMAX, TRMAX, DT>::kGlobalW) asm volatile("" : "+s"(base));
   const float *wp = base + (size_t)r.cq * kTrwRows * sh.C + r.cc;
-  // the slice's e values two at a time (cp0 is a multiple of the slice
-  // width, so the pairs are aligned), in batches of 8 with a scheduling
+  // the slice's e values two at a time (the e row starts on 16 bytes and
+  // cp0 is a multiple of the even slice width, so the pairs are aligned),
+  // in batches of 8 with a scheduling
   // barrier between them: hoisting every load of a wide slice would need
   // two registers per weight on top of the weights themselves.  Weights past
   // the slice are 0 (in registers and in the padded table alike) and the e

@@ -71,6 +71,7 @@ __host__ __device__ inline size_t chain_lds_bytes(int C, int K, int P, int QT, i
   size_t off = 0;
   off += (size_t)K * C * 8;            // ring
   off += (size_t)P * C * 8;            // K-sum partials
+  off = align_up(off, 16);             // the e row is read as 16-byte pairs
   off += (size_t)(C + 64) * 8;         // e row and its zero tail
   off += 8 * 8;                        // scalars
   off += (size_t)QT * C * 8;           // contraction partials
@@ -81,12 +82,14 @@ __host__ __device__ inline size_t chain_lds_bytes(int C, int K, int P, int QT, i
   return align_up(off, 16);
 }
 
-// Contraction split of the LDS-ring engine: as many slices as there are
-// thread rows (NT / C, at most C), each of CS consecutive previous labels.
+// Contraction split of the LDS-ring engine: up to as many slices as there
+// are thread rows (NT / C, at most C), each of CS consecutive previous
+// labels, CS even (a slice starts on a 16-byte pair of the e row).
 __host__ __device__ inline void chain_slices(int C, int NT, int &QT, int &CS) {
   int q = NT / C;
   q = q < 1 ? 1 : (q > C ? C : q);
   CS = (C + q - 1) / q;
+  CS += CS & 1;
   QT = (C + CS - 1) / CS;
 }
 

@@ -31,6 +31,8 @@ SHAPES = [
     (2, 300, 100, 70, [300, 151]),       # 512 threads, 2 contraction slices
     (2, 200, 256, 20, [200, 199]),       # 1024 threads, 4 slices
     (2, 150, 200, 50, [150, 77]),        # 1024 threads, C = 200
+    (2, 400, 40, 8, [400, 251]),         # 256 threads, odd slice width rounded up (7 -> 8)
+    (2, 300, 33, 10, [300, 177]),        # 256 threads, C * (K + P) odd: the e row realigned
     (3, 50, 5, 80, [50, 10, 1]),         # K > T, L = 1
     (2, 64, 1, 8, [64, 63]),             # C = 1
     (2, 90, 6, 1, [90, 40]),             # K = 1 (linear chain)
