@@ -160,9 +160,9 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_verify(ChainShape sh,
 }
 
 // One workgroup per (direction, sequence): prefix sums of the recorded
-// scalars along the direction of the chain, applied to every checkpoint
-// record (integer part to the references, fraction to the ring, both to the
-// absolute o / m rows) and to the chain's log Z.
+// scalars along the direction of the chain, giving each chunk's exact log
+// correction (shift, for the rows; its integer and fractional log2 parts
+// replace the chunk's scalar, for k_pit_records) and the chain's log Z.
 __global__ __launch_bounds__(kPitThreads) void k_pit_fixup(ChainShape sh,
                                                            const int32_t *__restrict__ lengths,
                                                            PitBufs pb, double *logz_ws,
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_fixup(ChainShape sh,
   const int b = fwd ? blockIdx.x : blockIdx.x - sh.B;
   if (!fwd && !with_bwd) return;
   const int L = lengths[b];
-  const int C = sh.C, K = sh.K, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   if (L < 1 || L > sh.T) {
     if (tid == 0) {
       if (fwd) {
@@ -185,36 +185,47 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_fixup(ChainShape sh,
     return;
   }
   const int nvalid = (L + sh.delta - 1) / sh.delta;
-  const size_t cks = ck_stride(C, K);
   const size_t base = (fwd ? 0 : (size_t)sh.B * sh.nchunk) + (size_t)b * sh.nchunk;
-  double *rec0 = (fwd ? pb.ck_fwd : pb.ck_bwd) + (size_t)b * sh.nchunk * cks;
-  long long oi = 0;  // accumulated offset of the current chunk, log2 units
+  __shared__ long long si[kPitThreads];
+  __shared__ double sf[kPitThreads];
+  long long oi = 0;  // accumulated offset of the current chunk, log2 units (thread 0)
   double of = 0.0;
   if (tid == 0) pb.shift[base + (fwd ? 0 : nvalid - 1)] = 0.0;  // the chain's exact chunk
-  for (int s = 1; s < nvalid; ++s) {
-    const int j = fwd ? s : nvalid - 1 - s;
-    oi += pb.corr_i[base + j];
-    of += pb.corr_f[base + j];
-    const double fo = floor(of);
-    oi += (long long)fo;
-    of -= fo;
-    // correction = -(oi + of) = ni + nf, nf in [0, 1)
-    long long ni = -oi;
-    double nf = -of;
-    if (nf < 0.0) {
-      nf += 1.0;
-      ni -= 1;
+  // chunks in the chain's order, kPitThreads at a time: the scalars are read
+  // in parallel, summed in order by one thread, the corrections written back
+  for (int s1 = 1; s1 < nvalid; s1 += kPitThreads) {
+    const int n = min(kPitThreads, nvalid - s1);
+    const int j = fwd ? s1 + tid : nvalid - 1 - (s1 + tid);
+    if (tid < n) {
+      si[tid] = pb.corr_i[base + j];
+      sf[tid] = pb.corr_f[base + j];
     }
-    double *rec = rec0 + (size_t)j * cks;
-    const double scale = exp2(nf);
-    const double shift = ((double)ni + nf) * kLn2;
-    if (tid == 0) pb.shift[base + j] = shift;
-    for (int i = tid; i < K * C; i += kPitThreads) rec[i] *= scale;
-    for (int c = tid; c < C; c += kPitThreads) {
-      rec[(size_t)K * C + c] = (double)((long long)rec[(size_t)K * C + c] + ni);
-      rec[(size_t)K * C + C + c] += shift;
-      rec[(size_t)K * C + 2 * C + c] += shift;
+    __syncthreads();
+    if (tid == 0) {
+      for (int q = 0; q < n; ++q) {
+        oi += si[q];
+        of += sf[q];
+        const double fo = floor(of);
+        oi += (long long)fo;
+        of -= fo;
+        // correction = -(oi + of) = ni + nf, nf in [0, 1)
+        long long ni = -oi;
+        double nf = -of;
+        if (nf < 0.0) {
+          nf += 1.0;
+          ni -= 1;
+        }
+        si[q] = ni;
+        sf[q] = nf;
+      }
     }
+    __syncthreads();
+    if (tid < n) {
+      pb.shift[base + j] = ((double)si[tid] + sf[tid]) * kLn2;
+      pb.corr_i[base + j] = si[tid];  // the scalar is consumed: now the chunk's correction
+      pb.corr_f[base + j] = sf[tid];
+    }
+    __syncthreads();
   }
   if (tid == 0) {
     // the chain's log Z was computed in the frame of its last chunk
@@ -225,6 +236,36 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_fixup(ChainShape sh,
     } else if (logz_bwd_ws) {
       logz_bwd_ws[b] = lz;
     }
+  }
+}
+
+// Every checkpoint record becomes the exact state with its exact log
+// normaliser: the chunk's correction (integer part to the references,
+// fraction to the ring, both to the absolute o / m rows).  One workgroup
+// per (direction, sequence, chunk); the chain's exact chunk has none.
+__global__ __launch_bounds__(kPitThreads) void k_pit_records(ChainShape sh,
+                                                             const int32_t *__restrict__ lengths,
+                                                             PitBufs pb, int with_bwd) {
+  const int nck = sh.B * sh.nchunk;
+  const bool fwd = (int)blockIdx.x < nck;
+  if (!fwd && !with_bwd) return;
+  const int rem = fwd ? blockIdx.x : blockIdx.x - nck;
+  const int b = rem / sh.nchunk, j = rem % sh.nchunk;
+  const int L = lengths[b];
+  if (L < 1 || L > sh.T || j * sh.delta >= L) return;
+  const int nvalid = (L + sh.delta - 1) / sh.delta;
+  if (j == (fwd ? 0 : nvalid - 1)) return;
+  const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + j;
+  const long long ni = pb.corr_i[idx];
+  const double nf = pb.corr_f[idx];
+  const int C = sh.C, K = sh.K;
+  double *rec = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + j) * ck_stride(C, K);
+  const double scale = exp2(nf), shift = pb.shift[idx];
+  for (int i = threadIdx.x; i < K * C; i += kPitThreads) rec[i] *= scale;
+  for (int c = threadIdx.x; c < C; c += kPitThreads) {
+    rec[(size_t)K * C + c] = (double)((long long)rec[(size_t)K * C + c] + ni);
+    rec[(size_t)K * C + C + c] += shift;
+    rec[(size_t)K * C + 2 * C + c] += shift;
   }
 }
 
@@ -248,6 +289,10 @@ hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur
     if (e != hipSuccess) return e;
   }
   e = launch_pit_fixup(sh, lengths, pb, logz_ws, logz_bwd_ws, logz_out, with_bwd, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_pit_records, dim3(2 * sh.B * sh.nchunk), dim3(kPitThreads), 0, st, sh,
+                     lengths, pb, with_bwd);
+  e = hipGetLastError();
   if (e != hipSuccess || !pb.row_a) return e;
   return launch_pit_rows(sh, lengths, pb, st);
 }
