@@ -140,7 +140,9 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
                  const VShape *vs = nullptr) {
   Carver cv;
   lay = Layout{};
-  lay.ntile = (T + scan_tile(C) - 1) / scan_tile(C);
+  lay.scan_j = scan_j(B, T, C);
+  const int tile = scan_rows(C) * lay.scan_j;
+  lay.ntile = (T + tile - 1) / tile;
   const size_t nS = (size_t)B * (T + 1) * C;
   if (op != SEMICRF_OP_SCAN) {
     lay.S = cv.take(nS * 8);
@@ -342,7 +344,7 @@ semicrf_status_t semicrf_cumulative_scores(const float *emissions, const int32_t
   (void)hipGetLastError();
   return hip_status(launch_scan(emissions, lengths, B, T, C, sh.center, nu, S, nullptr,
                                 nullptr, nullptr, at<double>(workspace, lay.tile_sum),
-                                at<double>(workspace, lay.anchor), lay.ntile, st));
+                                at<double>(workspace, lay.anchor), lay.ntile, lay.scan_j, st));
 }
 
 semicrf_status_t semicrf_logz_fwd(const float *emissions, const int32_t *lengths,
@@ -362,7 +364,7 @@ semicrf_status_t semicrf_logz_fwd(const float *emissions, const int32_t *lengths
   hipError_t e = launch_scan(emissions, lengths, B, T, C, sh.center, at<double>(workspace, lay.nu),
                              S, at<double>(workspace, lay.es_p), at<double>(workspace, lay.es_m),
                              at<int32_t>(workspace, lay.es_n), at<double>(workspace, lay.tile_sum),
-                             at<double>(workspace, lay.anchor), lay.ntile, st);
+                             at<double>(workspace, lay.anchor), lay.ntile, lay.scan_j, st);
   if (e != hipSuccess) return hip_status(e);
   e = run_sweeps(sh, trans, dur, es, lengths, pit_bufs(workspace, lay, false),
                  at<double>(workspace, lay.logz), nullptr, logz, 0, st);
@@ -396,7 +398,7 @@ semicrf_status_t semicrf_fwd_bwd_timed(const float *emissions, const int32_t *le
   hipError_t e = launch_scan(emissions, lengths, B, T, C, sh.center, at<double>(ws, lay.nu), S,
                              at<double>(ws, lay.es_p), at<double>(ws, lay.es_m),
                              at<int32_t>(ws, lay.es_n), at<double>(ws, lay.tile_sum),
-                             at<double>(ws, lay.anchor), lay.ntile, st);
+                             at<double>(ws, lay.anchor), lay.ntile, lay.scan_j, st);
   if (e != hipSuccess) return hip_status(e);
   mark(1);
   e = run_sweeps(sh, trans, dur, escaled(ws, lay), lengths, pit_bufs(ws, lay, true),
@@ -466,7 +468,7 @@ semicrf_status_t semicrf_viterbi(const float *emissions, const int32_t *lengths,
   double *S = at<double>(ws, lay.S);
   hipError_t e = launch_scan(emissions, lengths, B, T, C, sh.center, at<double>(ws, lay.nu), S,
                              nullptr, nullptr, nullptr, at<double>(ws, lay.tile_sum),
-                             at<double>(ws, lay.anchor), lay.ntile, st);
+                             at<double>(ws, lay.anchor), lay.ntile, lay.scan_j, st);
   if (e != hipSuccess) return hip_status(e);
   if (lay.vit_pit) {
     VBufs vb;

@@ -216,15 +216,22 @@ __device__ __forceinline__ void wave_lds_sync() {
 // sum_{c'} a[c'] * tr[c'] in float64.  The e row is broadcast through LDS,
 // two values per read, all reads issued before the first multiply.  All 64
 // lanes of wave 0 call.
-template <int CMAX>
+// `meanwhile` runs after the e-row reads are issued and before their
+// results are used: independent work placed there hides in the LDS latency
+// instead of delaying the step (a wave issues in order).
+template <int CMAX, typename F>
 __device__ __forceinline__ double chain_contract(const WSmem &sm, const ChainShape &sh, int lane,
-                                                 double a, const double (&tr)[CMAX]) {
+                                                 double a, const double (&tr)[CMAX],
+                                                 F &&meanwhile) {
   if (lane < CMAX) sm.erow[lane] = lane < sh.C ? a : 0.0;
   wave_lds_sync();
   const double2 *e2 = reinterpret_cast<const double2 *>(sm.erow);
   double2 ev[CMAX / 2];
 #pragma unroll
   for (int q = 0; q < CMAX / 2; ++q) ev[q] = e2[q];
+  __builtin_amdgcn_sched_barrier(0);
+  meanwhile();
+  __builtin_amdgcn_sched_barrier(0);
   double d0 = 0.0, d1 = 0.0, d2 = 0.0, d3 = 0.0;
 #pragma unroll
   for (int q = 0; q < CMAX / 2; q += 2) {
@@ -385,10 +392,18 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
       nqn = sm.en[o];
       fsn = far_of(i + 1);
     }
-    // the near part of the next step without its newest term
+    // the near part of the next step without its newest term (summed while
+    // the contraction's LDS reads are in flight; two chains for latency)
     double nrn = 0.0;
+    auto near_next = [&] {
+      double n0 = 0.0, n1 = 0.0;
 #pragma unroll
-    for (int k = 2; k <= kNearW; ++k) nrn = fma(Dn[k], cs.hist[k - 2], nrn);
+      for (int k = 2; k <= kNearW; k += 2) {
+        n0 = fma(Dn[k], cs.hist[k - 2], n0);
+        if (k + 1 <= kNearW) n1 = fma(Dn[k + 1], cs.hist[k - 1], n1);
+      }
+      nrn = n0 + n1;
+    };
     const int step = s0 + i;
     const int t = t0 + sigma * i;
     const bool last = step == nsteps - 1;
@@ -408,7 +423,7 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
       lz = (double)Bm * kLn2 + log(wave_sum(a));
     } else {
       // exp(m) = d * 2^Bm, m = u (forward) or beta (backward)
-      const double d = chain_contract<CMAX>(sm, sh, lane, a, tr);
+      const double d = chain_contract<CMAX>(sm, sh, lane, a, tr, near_next);
       if (chain) {
         stg[i * S + 2 * C + lane] = d;
         // entry exp(m -+ S) / 2^R = y * 2^s

@@ -56,7 +56,7 @@ __device__ __forceinline__ int exponent_of(double x) {
 // exp(s) = ep * 2^n and exp(-s) = em * 2^-n with ep, em in [2^-1/2, 2^1/2]
 // and n = rint(s / ln 2): the reduced argument r = s - n ln 2 is formed with
 // a two-part ln 2 (so it is accurate to a float64 rounding of r, whatever n),
-// then exp(+-r) in float64.  |s| >= 1e9 (no such cumulative score arises
+// then exp(+-r) in float64 from one shared series.  |s| >= 1e9 (no such cumulative score arises
 // from finite float32 emissions at the supported sizes) and NaN give NaN.
 __device__ __forceinline__ void exp_split(double s, double &ep, double &em, int &n) {
   if (!(fabs(s) < 1e9)) {
@@ -67,8 +67,28 @@ __device__ __forceinline__ void exp_split(double s, double &ep, double &em, int 
   const double k = rint(s * kLog2e);
   const double r = fma(-k, kLn2Lo, fma(-k, kLn2, s));
   n = static_cast<int>(k);
-  ep = exp(r);
-  em = exp(-r);
+  // exp(+-r) = E(r) +- O(r), the even and odd parts of the exponential
+  // series, |r| <= ln2/2: terms through r^14 (the first omitted one is below
+  // 1e-17 of the result), in z = r^2 by Horner's rule
+  const double z = r * r;
+  double e = 1.0 / 87178291200.0;  // 1/14!
+  e = fma(e, z, 1.0 / 479001600.0);  // 1/12!
+  e = fma(e, z, 1.0 / 3628800.0);    // 1/10!
+  e = fma(e, z, 1.0 / 40320.0);      // 1/8!
+  e = fma(e, z, 1.0 / 720.0);        // 1/6!
+  e = fma(e, z, 1.0 / 24.0);         // 1/4!
+  e = fma(e, z, 0.5);                // 1/2!
+  e = fma(e, z, 1.0);
+  double o = 1.0 / 6227020800.0;     // 1/13!
+  o = fma(o, z, 1.0 / 39916800.0);   // 1/11!
+  o = fma(o, z, 1.0 / 362880.0);     // 1/9!
+  o = fma(o, z, 1.0 / 5040.0);       // 1/7!
+  o = fma(o, z, 1.0 / 120.0);        // 1/5!
+  o = fma(o, z, 1.0 / 6.0);          // 1/3!
+  o = fma(o, z, 1.0);
+  o *= r;
+  ep = e + o;
+  em = e - o;
 }
 
 // Row rotation (within each row of 16 lanes) by DPP; lanes whose source would

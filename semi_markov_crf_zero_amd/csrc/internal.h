@@ -56,12 +56,20 @@ inline bool lds_fits(const void *f, size_t dyn) {
 }
 
 // Scan tiles: NT_SCAN threads as R = NT_SCAN / C rows x C labels, each row
-// thread owning J consecutive positions; a tile covers R*J positions.
+// thread owning J consecutive positions; a tile covers R*J positions.  J is
+// 32, halved (down to 8) while the batch would have fewer than
+// kScanWorkgroups tiles: short sequences need the parallelism, long ones
+// fewer tiles for the anchor pass.
 constexpr int kScanThreads = 256;
-constexpr int kScanJ = 32;
+constexpr int kScanWorkgroups = 1024;
 
 inline int scan_rows(int C) { return kScanThreads / C; }
-inline int scan_tile(int C) { return scan_rows(C) * kScanJ; }
+inline int scan_j(int B, int T, int C) {
+  int j = 32;
+  while (j > 8 && (long long)B * ((T + scan_rows(C) * j - 1) / (scan_rows(C) * j)) < kScanWorkgroups)
+    j /= 2;
+  return j;
+}
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -148,6 +156,7 @@ struct Layout {
   size_t v_pred, v_rr, v_re, v_corr, v_delta, v_redo, v_nbad, v_lst_t, v_lst_c, v_mark, v_sub;
   size_t total;
   int ntile;
+  int scan_j;   // positions per scan row thread
   int vit_pit;  // Viterbi by the parallel-in-time decoder (vpit.hip)
 };
 
@@ -202,7 +211,7 @@ struct PitBufs {
 // ep / em / en may be NULL (then only nu and S are written).
 hipError_t launch_scan(const float *x, const int32_t *lengths, int B, int T, int C, int center,
                        double *nu, double *S, double *ep, double *em, int32_t *en,
-                       double *tile_sum, double *anchor, int ntile, hipStream_t st);
+                       double *tile_sum, double *anchor, int ntile, int J, hipStream_t st);
 
 // One iteration of the chunk-parallel sweeps (every chunk of every sequence,
 // both directions when with_bwd); iteration 0 builds the start states.

@@ -21,19 +21,19 @@ namespace semicrf {
 
 // Thread (r, c) of a tile owns positions [tile*TS + r*J, +J) of label c.
 __global__ __launch_bounds__(kScanThreads) void k_scan_partial(
-    const float *__restrict__ x, const int32_t *__restrict__ lengths, int T, int C, int ntile,
+    const float *__restrict__ x, const int32_t *__restrict__ lengths, int T, int C, int ntile, int J,
     double *__restrict__ tile_sum) {
   __shared__ double red[kScanThreads];
   const int tile = blockIdx.x, b = blockIdx.y;
-  const int R = kScanThreads / C, TS = R * kScanJ;
+  const int R = kScanThreads / C, TS = R * J;
   const int tid = threadIdx.x, c = tid % C, r = tid / C;
   const int L = lengths[b];
   const bool valid_len = L >= 1 && L <= T;
   double s = 0.0;
   if (r < R && valid_len) {
-    const int t0 = tile * TS + r * kScanJ;
+    const int t0 = tile * TS + r * J;
     const float *xb = x + (size_t)b * T * C;
-    for (int i = 0; i < kScanJ; ++i) {
+    for (int i = 0; i < J; ++i) {
       const int t = t0 + i;
       if (t < L) s += (double)xb[(size_t)t * C + c];
     }
@@ -50,13 +50,13 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_partial(
 // One block per (sequence, label): each thread owns a contiguous range of
 // tiles; the per-thread totals are combined in a fixed order (deterministic).
 __global__ __launch_bounds__(kScanThreads) void k_scan_anchor(
-    const int32_t *__restrict__ lengths, int T, int C, int ntile, int center,
+    const int32_t *__restrict__ lengths, int T, int C, int ntile, int J, int center,
     const double *__restrict__ tile_sum, double *__restrict__ anchor, double *__restrict__ nu) {
   __shared__ double red[kScanThreads];
   const int b = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const int L = lengths[b];
   const bool valid_len = L >= 1 && L <= T;
-  const int TS = (kScanThreads / C) * kScanJ;
+  const int TS = (kScanThreads / C) * J;
   const int per = (ntile + kScanThreads - 1) / kScanThreads;
   const int i0 = tid * per, i1 = min(i0 + per, ntile);
   const double *ts = tile_sum + (size_t)b * ntile * C + c;
@@ -104,22 +104,22 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_anchor(
 // (exp_split: exp(+-S) as a float64 in [2^-1/2, 2^1/2] times 2^(+-n)) when
 // ep is given.
 __global__ __launch_bounds__(kScanThreads) void k_scan_write(
-    const float *__restrict__ x, const int32_t *__restrict__ lengths, int T, int C, int ntile,
+    const float *__restrict__ x, const int32_t *__restrict__ lengths, int T, int C, int ntile, int J,
     const double *__restrict__ anchor, const double *__restrict__ nu, double *__restrict__ S,
     double *__restrict__ ep, double *__restrict__ em, int32_t *__restrict__ en) {
   __shared__ double red[kScanThreads];
   const int tile = blockIdx.x, b = blockIdx.y;
-  const int R = kScanThreads / C, TS = R * kScanJ;
+  const int R = kScanThreads / C, TS = R * J;
   const int tid = threadIdx.x, c = tid % C, r = tid / C;
   const int L = lengths[b];
   const bool valid_len = L >= 1 && L <= T;
   const float *xb = x + (size_t)b * T * C;
   const size_t ob = (size_t)b * (T + 1) * C;
   const double n = valid_len ? nu[(size_t)b * C + c] : 0.0;
-  const int t0 = tile * TS + r * kScanJ;
+  const int t0 = tile * TS + r * J;
   double local = 0.0;
   if (r < R && valid_len) {
-    for (int i = 0; i < kScanJ; ++i) {
+    for (int i = 0; i < J; ++i) {
       const int t = t0 + i;
       if (t < L) local += (double)xb[(size_t)t * C + c] - n;
     }
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_write(
     }
   };
   if (tile == 0 && r == 0) put(0, valid_len ? 0.0 : run);
-  for (int i = 0; i < kScanJ; ++i) {
+  for (int i = 0; i < J; ++i) {
     const int t = t0 + i;
     if (t >= T) break;
     if (t < L) run += (double)xb[(size_t)t * C + c] - n;
@@ -153,18 +153,18 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_write(
 
 hipError_t launch_scan(const float *x, const int32_t *lengths, int B, int T, int C, int center,
                        double *nu, double *S, double *ep, double *em, int32_t *en,
-                       double *tile_sum, double *anchor, int ntile, hipStream_t st) {
+                       double *tile_sum, double *anchor, int ntile, int J, hipStream_t st) {
   dim3 grid(ntile, B);
   hipLaunchKernelGGL(k_scan_partial, grid, dim3(kScanThreads), 0, st, x, lengths, T, C, ntile,
-                     tile_sum);
+                     J, tile_sum);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan_anchor, dim3(B, C), dim3(kScanThreads), 0, st, lengths, T, C, ntile,
-                     center, tile_sum, anchor, nu);
+                     J, center, tile_sum, anchor, nu);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan_write, grid, dim3(kScanThreads), 0, st, x, lengths, T, C, ntile,
-                     anchor, nu, S, ep, em, en);
+                     J, anchor, nu, S, ep, em, en);
   return hipGetLastError();
 }
 
