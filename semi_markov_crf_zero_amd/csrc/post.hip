@@ -413,13 +413,18 @@ __global__ __launch_bounds__(kRedOut * kRedSlices) void k_post_reduce(ChainShape
   const long long per = (n + kRedSlices - 1) / kRedSlices;
   double acc = 0.0;
   if (e < nx + ng) {
-    for (long long q = p * per; q < n && q < (p + 1) * per; ++q) {
+    // every load is issued unconditionally (the addresses do not depend on
+    // the length), so they pipeline; an invalid sequence's term is dropped
+    // by a select (its partial may hold anything)
+    const double *src = tx ? pa.tx_part + e : pa.dur_part + (e - nx);
+    const size_t stride = tx ? (size_t)nx : (size_t)ng;
+    const long long q1 = min(n, (p + 1) * per);
+    for (long long q = p * per; q < q1; ++q) {
       const int b = (int)(q / np), j = (int)(q % np);
       const int L = pa.lengths[b];
-      if (!valid_len(sh, L)) continue;
       const double w = pa.grad_logz ? (double)pa.grad_logz[b] : 1.0;
-      acc += w * (tx ? pa.tx_part[((size_t)b * nseg + j) * nx + e]
-                     : pa.dur_part[((size_t)b * nspan + j) * ng + (e - nx)]);
+      const double v = src[((size_t)b * np + j) * stride];
+      acc += valid_len(sh, L) ? w * v : 0.0;
     }
   }
   red[p][o] = acc;
