@@ -166,19 +166,21 @@ template <bool WITH_GD, int AMAX, int TRMAX, typename DT, typename GT>
 __device__ __forceinline__ double ksum(const Regs<AMAX, TRMAX, DT> &r, const Smem &sm,
                                        const ChainShape &sh, int t, bool fwd, GT (&gd)[AMAX],
                                        double q) {
-  double s = 0.0;
+  // every term is read without a branch (past the thread's durations the
+  // weight is 0 and the duration is clamped into the ring), so the LDS
+  // reads pipeline; four running sums keep the additions off one chain
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
   const int K = sh.K, C = sh.C;
   const int tm = t % K;
 #pragma unroll
   for (int j = 0; j < AMAX; ++j) {
-    if (j < r.nage) {
-      const int sl = slot_of(tm, r.age0 + j, K, fwd);
-      const double w = (double)r.D[j] * sm.ring[sl * C + r.kc];
-      s += w;
-      if (WITH_GD) gd[j] += (GT)(q * w);
-    }
+    const int k = min(r.age0 + j, K);
+    const int sl = slot_of(tm, k, K, fwd);
+    const double w = (double)r.D[j] * sm.ring[sl * C + r.kc];
+    s[j & 3] += w;
+    if (WITH_GD) gd[j] += (GT)(q * w);
   }
-  return s;
+  return (s[0] + s[1]) + (s[2] + s[3]);
 }
 
 // Maximum over the row threads of an int (others pass kNoExp).  All threads
