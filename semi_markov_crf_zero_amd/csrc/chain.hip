@@ -166,21 +166,52 @@ template <bool WITH_GD, int AMAX, int TRMAX, typename DT, typename GT>
 __device__ __forceinline__ double ksum(const Regs<AMAX, TRMAX, DT> &r, const Smem &sm,
                                        const ChainShape &sh, int t, bool fwd, GT (&gd)[AMAX],
                                        double q) {
-  // every term is read without a branch (past the thread's durations the
-  // weight is 0 and the duration is clamped into the ring), so the LDS
-  // reads pipeline; four running sums keep the additions off one chain
+  // The ring offset of duration age0 + j moves by one row per duration
+  // (wrapping once), so no multiply per term; past the thread's durations
+  // the weight is 0 and the offset merely stays inside the ring.  Reads go
+  // in batches of 8 into separate registers, so they pipeline, and four
+  // running sums keep the additions off one chain.
+  const int K = sh.K, C = sh.C, KC = K * C;
+  const int dC = fwd ? -C : C;
+  int off = slot_of(t % K, min(r.age0, K), K, fwd) * C + r.kc;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
-  const int K = sh.K, C = sh.C;
-  const int tm = t % K;
 #pragma unroll
-  for (int j = 0; j < AMAX; ++j) {
-    const int k = min(r.age0 + j, K);
-    const int sl = slot_of(tm, k, K, fwd);
-    const double w = (double)r.D[j] * sm.ring[sl * C + r.kc];
-    s[j & 3] += w;
-    if (WITH_GD) gd[j] += (GT)(q * w);
+  for (int jb = 0; jb < AMAX; jb += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8 && jb + u < AMAX; ++u) {
+      v[u] = sm.ring[off];
+      off += dC;
+      off += off < 0 ? KC : 0;
+      off -= off >= KC ? KC : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8 && jb + u < AMAX; ++u) {
+      const double w = (double)r.D[jb + u] * v[u];
+      s[u & 3] += w;
+      if (WITH_GD) gd[jb + u] += (GT)(q * w);
+    }
   }
   return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
+// Sum of n values at stride `stride` (in a fixed order): reads in batches of
+// 8 into separate registers so they pipeline.
+__device__ __forceinline__ double sum_strided(const double *p, int n, int stride) {
+  double s0 = 0.0, s1 = 0.0;
+  int q = 0;
+  for (; q + 8 <= n; q += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(q + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      s0 += v[u];
+      s1 += v[u + 1];
+    }
+  }
+  for (; q < n; ++q) s0 += p[q * stride];
+  return s0 + s1;
 }
 
 // Maximum over the row threads of an int (others pass kNoExp).  All threads
@@ -251,10 +282,7 @@ __device__ __forceinline__ double contract(const Regs<AMAX, TRMAX, DT> &r, const
   if (sh.QT > 1) {
     if (r.cq < sh.QT) sm.dotp[r.cq * sh.C + r.cc] = dp;
     __syncthreads();
-    if ((int)threadIdx.x < sh.C) {
-      dp = 0.0;
-      for (int q = 0; q < sh.QT; ++q) dp += sm.dotp[q * sh.C + threadIdx.x];
-    }
+    if ((int)threadIdx.x < sh.C) dp = sum_strided(sm.dotp + threadIdx.x, sh.QT, sh.C);
   }
   return dp;
 }
@@ -450,9 +478,7 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
     double x = 0.0;
     int E = 0;
     if (ROLE == kRowRole && is_row) {
-      double sum = 0.0;
-      for (int p = 0; p < sh.P; ++p) sum += sm.part[p * C + tid];
-      x = sum * fx;
+      x = sum_strided(sm.part + tid, sh.P, C) * fx;
       E = R + nq;
     }
     const bool prev_rows = rows && step - 1 > wb;  // the previous step is past the burn-in
