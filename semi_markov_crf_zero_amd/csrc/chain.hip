@@ -69,7 +69,7 @@
 
 namespace semicrf {
 
-constexpr int kRebaseExp = 260;  // rebase bound, log2 units
+constexpr int kRebaseExp = 512;  // rebase bound, log2 units (see insert_entry)
 constexpr int kErowPad = 64;     // zero tail of the e row: the widest slice reads past C
 
 struct Smem {
@@ -291,7 +291,11 @@ __device__ __forceinline__ double contract(const Regs<AMAX, TRMAX, DT> &r, const
 // reference 2^R (y > 0, s an exact integer), and decides an exact
 // power-of-two rebase of its column: an entry outside
 // [2^-kRebaseExp, 2^kRebaseExp] moves R by its exponent.  Returns true if
-// the column must be rescaled by 2^-n (n in sm.shiftn[c]).
+// the column must be rescaled by 2^-n (n in sm.shiftn[c]).  The bound
+// leaves headroom for the K-sum, at most 2^kRebaseExp * K * max exp(dur),
+// below float64's 2^1023 for K <= 16384 and dur below ~270 nats; older
+// entries that fall below the float64 range are smaller than the newest by
+// more than 2^kRebaseExp and weigh nothing.
 __device__ __forceinline__ bool insert_entry(const Smem &sm, const ChainShape &sh, int t,
                                              double y, int s, int &R) {
   const int c = threadIdx.x;
@@ -309,16 +313,32 @@ __device__ __forceinline__ bool insert_entry(const Smem &sm, const ChainShape &s
 template <int AMAX, int TRMAX, typename DT>
 __device__ __forceinline__ void apply_rebase(const Regs<AMAX, TRMAX, DT> &r, const Smem &sm,
                                              const ChainShape &sh, int t, bool fwd) {
-  if (r.nage > 0) {
-    const int n = sm.shiftn[r.kc];
-    if (n != 0) {
-      const int tn = fwd ? t + 1 : t - 1;
-      const int tm = tn % sh.K;
-      for (int j = 0; j < r.nage; ++j) {
-        const int k = r.age0 + j;
-        if (k < 2) continue;
-        const int sl = slot_of(tm, k, sh.K, fwd);
-        sm.ring[sl * sh.C + r.kc] = ldexp(sm.ring[sl * sh.C + r.kc], -n);
+  // the thread's own slots only (another thread owns every other slot, so
+  // nothing past them is written); reads in batches of 8 without a branch so
+  // they pipeline, stores predicated
+  const int n = r.nage > 0 ? sm.shiftn[r.kc] : 0;
+  if (n != 0) {
+    const int K = sh.K, C = sh.C, KC = K * C;
+    const int dC = fwd ? -C : C;
+    const int tn = fwd ? t + 1 : t - 1;
+    int off = slot_of(tn % K, min(r.age0, K), K, fwd) * C + r.kc;
+#pragma unroll
+    for (int jb = 0; jb < AMAX; jb += 8) {
+      double v[8];
+      int o[8];
+#pragma unroll
+      for (int u = 0; u < 8 && jb + u < AMAX; ++u) {
+        o[u] = off;
+        v[u] = sm.ring[off];
+        off += dC;
+        off += off < 0 ? KC : 0;
+        off -= off >= KC ? KC : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8 && jb + u < AMAX; ++u) {
+        const int j = jb + u;
+        // duration 1 is the entry just inserted in the new reference
+        if (j < r.nage && r.age0 + j >= 2) sm.ring[o[u]] = ldexp(v[u], -n);
       }
     }
   }

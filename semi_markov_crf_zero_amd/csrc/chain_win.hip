@@ -42,7 +42,7 @@ namespace semicrf {
 
 namespace {
 
-constexpr int kRebaseExp = 260;  // rebase bound, log2 units
+constexpr int kRebaseExp = 512;  // rebase bound, log2 units (see chain.hip)
 constexpr int U = kWinU;         // positions per block
 constexpr int kNearW = 2 * U - 1;  // near terms k = 1 .. 2U-1 (the chain's register window)
 
