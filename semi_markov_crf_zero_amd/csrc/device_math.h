@@ -153,14 +153,27 @@ __device__ __forceinline__ int dpp_i(int v, int ctrl) {
 
 // Maximum (float64) and minimum (int) over aligned groups of ng consecutive
 // lanes, ng a power of two up to 64; every lane of a group receives the
-// result.  All 64 lanes of the wave must call with the same ng.
+// result.  All 64 lanes of the wave must call with the same ng.  Within rows
+// of 16 by DPP; across rows (ng = 32, 64) through the four row results read
+// into scalars (v_readlane), not an LDS permute.
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const long long b = __builtin_bit_cast(long long, v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffLL), lane);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+
 __device__ __forceinline__ double group_max(double v, int ng) {
   if (ng >= 2) v = fmax(v, dpp_f64(v, 0xB1));
   if (ng >= 4) v = fmax(v, dpp_f64(v, 0x4E));
   if (ng >= 8) v = fmax(v, dpp_f64(v, 0x141));
   if (ng >= 16) v = fmax(v, dpp_f64(v, 0x140));
-  if (ng >= 32) v = fmax(v, __shfl_xor(v, 16));
-  if (ng >= 64) v = fmax(v, __shfl_xor(v, 32));
+  if (ng >= 32) {
+    const double r0 = readlane_f64(v, 0), r1 = readlane_f64(v, 16);
+    const double r2 = readlane_f64(v, 32), r3 = readlane_f64(v, 48);
+    const double lo = fmax(r0, r1), hi = fmax(r2, r3);
+    v = ng >= 64 ? fmax(lo, hi) : ((threadIdx.x & 32) ? hi : lo);
+  }
   return v;
 }
 
@@ -169,8 +182,12 @@ __device__ __forceinline__ int group_min_i(int v, int ng) {
   if (ng >= 4) v = min(v, dpp_i(v, 0x4E));
   if (ng >= 8) v = min(v, dpp_i(v, 0x141));
   if (ng >= 16) v = min(v, dpp_i(v, 0x140));
-  if (ng >= 32) v = min(v, __shfl_xor(v, 16));
-  if (ng >= 64) v = min(v, __shfl_xor(v, 32));
+  if (ng >= 32) {
+    const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    const int lo = min(r0, r1), hi = min(r2, r3);
+    v = ng >= 64 ? min(lo, hi) : ((threadIdx.x & 32) ? hi : lo);
+  }
   return v;
 }
 

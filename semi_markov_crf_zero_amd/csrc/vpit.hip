@@ -179,33 +179,66 @@ __device__ __forceinline__ void vsweep(const VShape &vs, const VRegs<AMAX, CAMAX
       const int row = min(q + 1 + (blk + 1) * U + tid / C, T);
       sreg = Sb[(size_t)row * C + tid % C];
     }
-    // durations: max over k and the smallest tied k
+    // durations: max over k and the smallest tied k.  Every candidate is
+    // read without a branch (the slot clamped into the ring; invalid ones
+    // masked afterwards), in batches of 8, so the reads pipeline.
     const int kmax = min(K, t);
+    const double *rc = sm.ring + c * K;
+    // (the wide instances, short of registers, keep one guarded read per
+    // candidate and read again for the smallest tied k)
+    constexpr bool kFlat = CAMAX <= 4;
+    double cand[kFlat ? AMAX : 1];
     double m = ninf;
+    if constexpr (kFlat) {
 #pragma unroll
-    for (int a = 0; a < AMAX; ++a) {
-      const int k = g + 1 + NG * a;
-      if (r.on && a < vs.A && k <= kmax) {
-        int sl = kslot - NG * a;
+    for (int ab = 0; ab < AMAX; ab += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8 && ab + u < AMAX; ++u) {
+        int sl = kslot - NG * (ab + u);
         sl += sl < 0 ? K : 0;
-        m = fmax(m, wide<kWide>(r.dr[a]) + sm.ring[c * K + sl]);
+        sl = sl < 0 ? 0 : sl;
+        v[u] = rc[sl];
+      }
+#pragma unroll
+      for (int u = 0; u < 8 && ab + u < AMAX; ++u) {
+        const int a = ab + u, k = g + 1 + NG * a;
+        const bool ok = r.on && a < vs.A && k <= kmax;
+        cand[a] = ok ? wide<kWide>(r.dr[a]) + v[u] : ninf;
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < AMAX; ++a) m = fmax(m, cand[a]);
+    } else {
+#pragma unroll
+      for (int a = 0; a < AMAX; ++a) {
+        const int k = g + 1 + NG * a;
+        if (r.on && a < vs.A && k <= kmax) {
+          int sl = kslot - NG * a;
+          sl += sl < 0 ? K : 0;
+          m = fmax(m, wide<kWide>(r.dr[a]) + rc[sl]);
+        }
       }
     }
     const double M = group_max(m, NG);
-    // wide lanes read their candidates again rather than hold them across
-    // the reduction (a compiler-only memory barrier stops the reuse)
-    if (AMAX > 4) asm volatile("" ::: "memory");
     const double st = sm.sst[((blk & 1) * U + w) * C + c];
     const double ah = st + M;
     const double thr = M - viterbi_tie_eps(ah);
     int kb = kNoArg;
+    if constexpr (kFlat) {
 #pragma unroll
-    for (int a = AMAX - 1; a >= 0; --a) {
-      const int k = g + 1 + NG * a;
-      if (r.on && a < vs.A && k <= kmax) {
-        int sl = kslot - NG * a;
-        sl += sl < 0 ? K : 0;
-        if (wide<kWide>(r.dr[a]) + sm.ring[c * K + sl] >= thr) kb = k;
+      for (int a = AMAX - 1; a >= 0; --a)
+        if (cand[a] >= thr) kb = g + 1 + NG * a;  // invalid candidates are -inf
+    } else {
+      if (AMAX > 4) asm volatile("" ::: "memory");  // read again rather than hold
+#pragma unroll
+      for (int a = AMAX - 1; a >= 0; --a) {
+        const int k = g + 1 + NG * a;
+        if (r.on && a < vs.A && k <= kmax) {
+          int sl = kslot - NG * a;
+          sl += sl < 0 ? K : 0;
+          if (wide<kWide>(r.dr[a]) + rc[sl] >= thr) kb = k;
+        }
       }
     }
     kb = group_min_i(kb, NG);
@@ -221,7 +254,13 @@ __device__ __forceinline__ void vsweep(const VShape &vs, const VRegs<AMAX, CAMAX
 #pragma unroll
       for (int i = 0; i < CAMAX; ++i) {
         const int cp = g + NG * i;
-        if (r.on && i < vs.CA && cp < C) m2 = fmax(m2, ar[cp] + wide<kWide>(r.tr[i]));
+        const bool ok = r.on && i < vs.CA && cp < C;
+        if constexpr (CAMAX <= 4) {
+          const double v = ar[ok ? cp : 0] + wide<kWide>(r.tr[i]);  // read without a branch
+          m2 = fmax(m2, ok ? v : ninf);
+        } else if (ok) {
+          m2 = fmax(m2, ar[cp] + wide<kWide>(r.tr[i]));
+        }
         // batches of 8 loads: hoisting all of them would take two registers each
         if (CAMAX > 8 && (i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
       }
@@ -232,7 +271,13 @@ __device__ __forceinline__ void vsweep(const VShape &vs, const VRegs<AMAX, CAMAX
 #pragma unroll
       for (int i = CAMAX - 1; i >= 0; --i) {
         const int cp = g + NG * i;
-        if (r.on && i < vs.CA && cp < C && ar[cp] + wide<kWide>(r.tr[i]) >= thr2) cl = cp;
+        const bool ok = r.on && i < vs.CA && cp < C;
+        if constexpr (CAMAX <= 4) {
+          const double v = ar[ok ? cp : 0] + wide<kWide>(r.tr[i]);
+          if (ok && v >= thr2) cl = cp;
+        } else if (ok && ar[cp] + wide<kWide>(r.tr[i]) >= thr2) {
+          cl = cp;
+        }
         if (CAMAX > 8 && (i & 7) == 0) __builtin_amdgcn_sched_barrier(0);
       }
       cb = group_min_i(cl, NG) & 0xffff;
