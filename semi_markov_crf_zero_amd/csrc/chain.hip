@@ -70,6 +70,7 @@
 namespace semicrf {
 
 constexpr int kRebaseExp = 512;  // rebase bound, log2 units (see insert_entry)
+constexpr int kScaleSpan = 256;  // step-scale span, log2 units (see sweep_loop)
 constexpr int kErowPad = 64;     // zero tail of the e row: the widest slice reads past C
 
 struct Smem {
@@ -172,18 +173,25 @@ __device__ __forceinline__ double ksum(const Regs<AMAX, TRMAX, DT> &r, const Sme
   // in batches of 8 into separate registers, so they pipeline, and four
   // running sums keep the additions off one chain.
   const int K = sh.K, C = sh.C, KC = K * C;
-  const int dC = fwd ? -C : C;
   int off = slot_of(t % K, min(r.age0, K), K, fwd) * C + r.kc;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int jb = 0; jb < AMAX; jb += 8) {
     double v[8];
+    if (fwd) {  // older positions at lower slots: one wrap check per term
 #pragma unroll
-    for (int u = 0; u < 8 && jb + u < AMAX; ++u) {
-      v[u] = sm.ring[off];
-      off += dC;
-      off += off < 0 ? KC : 0;
-      off -= off >= KC ? KC : 0;
+      for (int u = 0; u < 8 && jb + u < AMAX; ++u) {
+        v[u] = sm.ring[off];
+        off -= C;
+        off += off < 0 ? KC : 0;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8 && jb + u < AMAX; ++u) {
+        v[u] = sm.ring[off];
+        off += C;
+        off -= off >= KC ? KC : 0;
+      }
     }
 #pragma unroll
     for (int u = 0; u < 8 && jb + u < AMAX; ++u) {
@@ -464,6 +472,7 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
   const int wfirst = 64 * (sh.Q + sh.nload), wn = NT - wfirst;  // writer threads
   const int tstart = tb;
   double o_rec = 0.0, m_rec = 0.0;
+  int Bm = -(1 << 29);  // step scale of the rows; the first step computes it
   PfLoad ld;
   for (int step = 1; step <= nsteps; ++step) {
     const int t = tb + isig * step;
@@ -504,7 +513,16 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
     const bool prev_rows = rows && step - 1 > wb;  // the previous step is past the burn-in
     if (ROLE == kWriteRole && prev_rows)
       stage_rows(sprev, C, row1 + tprev, row2 + tprev, 0, C, wfirst, wn);
-    const int Bm = rows_max_i((is_row && x > 0.0) ? E + exponent_of(x) : kNoExp, sh, sm);
+    // the step scale: with the rows in one wave it carries over from step to
+    // step and is recomputed (an exact integer maximum) only when some
+    // label's exponent leaves [Bm - kScaleSpan, Bm + kScaleSpan], as in
+    // chain_win.hip; every value stays exact either way
+    const int ex = (is_row && x > 0.0) ? E + exponent_of(x) : kNoExp;
+    if (sh.Q == 1) {
+      if (__any(ex - Bm > kScaleSpan) || !__any(ex - Bm >= -kScaleSpan)) Bm = wave_max_i(ex);
+    } else {
+      Bm = rows_max_i(ex, sh, sm);
+    }
     double *stg = sm.stg + (step & 1) * (3 * C + 1);
     if (ROLE == kRowRole && is_row) {
       stg[tid] = x;
