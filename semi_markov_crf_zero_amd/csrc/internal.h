@@ -174,7 +174,7 @@ struct PostArgs {
 
 // Launch geometry of the posterior pass (also sizes its workspace).
 struct PostGeom {
-  int cov_ntile, tx_seg, tx_nseg, dur_span, dur_nspan, dur_kb, dur_npg;
+  int cov_j, cov_ntile, tx_seg, tx_nseg, dur_span, dur_nspan, dur_kb, dur_npg;
   size_t dur_lds;
 };
 

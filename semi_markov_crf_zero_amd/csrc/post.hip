@@ -23,7 +23,9 @@ namespace semicrf {
 namespace {
 
 constexpr int kCovThreads = 256;
-constexpr int kCovJ = 16;  // consecutive positions per coverage thread
+// consecutive positions per coverage thread: 16, halved (down to 4) while a
+// batch has fewer than kCovTiles tiles (short sequences need the parallelism)
+constexpr int kCovJ = 16, kCovJMin = 4, kCovTiles = 1024;
 constexpr int kTxThreads = 256;
 constexpr int kTxTile = 64;   // output tile of the transition GEMM (64 x 64)
 constexpr int kTxRows = 32;   // positions staged in LDS per batch
@@ -53,7 +55,7 @@ __device__ __forceinline__ double cov_delta(const PostArgs &pa, const ChainShape
 }
 
 __global__ __launch_bounds__(kCovThreads) void k_cov_partial(ChainShape sh, PostArgs pa,
-                                                             int ntile) {
+                                                             int ntile, int J) {
   __shared__ double red1[kCovThreads], red2[kCovThreads];
   const int tile = blockIdx.x, b = blockIdx.y;
   const int C = sh.C, R = kCovThreads / C, tid = threadIdx.x;
@@ -62,8 +64,8 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_partial(ChainShape sh, Post
   double s1 = 0.0, s2 = 0.0;
   if (r < R && valid_len(sh, L)) {
     const double logZ = pa.logz[b];
-    const int t0 = tile * R * kCovJ + r * kCovJ;
-    for (int j = 0; j < kCovJ; ++j) {
+    const int t0 = tile * R * J + r * J;
+    for (int j = 0; j < J; ++j) {
       const int t = t0 + j;
       if (t >= L) break;
       const double d = cov_delta(pa, sh, b, t, c, logZ);
@@ -122,7 +124,8 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_anchor(ChainShape sh, PostA
   }
 }
 
-__global__ __launch_bounds__(kCovThreads) void k_cov_write(ChainShape sh, PostArgs pa, int ntile) {
+__global__ __launch_bounds__(kCovThreads) void k_cov_write(ChainShape sh, PostArgs pa, int ntile,
+                                                           int J) {
   __shared__ double runs[kCovThreads];
   const int tile = blockIdx.x, b = blockIdx.y;
   const int C = sh.C, R = kCovThreads / C, tid = threadIdx.x;
@@ -130,10 +133,10 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_write(ChainShape sh, PostAr
   const int L = pa.lengths[b];
   const bool ok = valid_len(sh, L);
   const double logZ = ok ? pa.logz[b] : 0.0;
-  const int t0 = tile * R * kCovJ + r * kCovJ;
+  const int t0 = tile * R * J + r * J;
   double own = 0.0;
   if (r < R && ok) {
-    for (int j = 0; j < kCovJ; ++j) {
+    for (int j = 0; j < J; ++j) {
       const int t = t0 + j;
       if (t >= L) break;
       own += cov_delta(pa, sh, b, t, c, logZ);
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_write(ChainShape sh, PostAr
     mean = sh.center ? pa.cov_mean[(size_t)b * C + c] : 0.0;
     w = pa.grad_logz ? (double)pa.grad_logz[b] : 1.0;
   }
-  for (int j = 0; j < kCovJ; ++j) {
+  for (int j = 0; j < J; ++j) {
     const int t = t0 + j;
     if (t >= sh.T) break;
     float m_out = 0.f, g_out = 0.f;
@@ -399,7 +402,7 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
 // One workgroup per kRedOut consecutive outputs (transition entries first,
 // then durations); thread (o, p) sums slice p of the (sequence, partial)
 // list of output o in order, and the slices meet in LDS in a fixed order.
-constexpr int kRedOut = 16, kRedSlices = 16;
+constexpr int kRedOut = 8, kRedSlices = 32;
 __global__ __launch_bounds__(kRedOut * kRedSlices) void k_post_reduce(ChainShape sh, PostArgs pa,
                                                                       int nseg, int nspan) {
   __shared__ double red[kRedSlices][kRedOut];
@@ -442,7 +445,10 @@ __global__ __launch_bounds__(kRedOut * kRedSlices) void k_post_reduce(ChainShape
 // ------------------------------------------------------------ launch
 void post_geometry(const ChainShape &sh, PostGeom &g) {
   const int R = kCovThreads / sh.C;
-  g.cov_ntile = (sh.T + R * kCovJ - 1) / (R * kCovJ);
+  g.cov_j = kCovJ;
+  while (g.cov_j > kCovJMin && (long long)sh.B * ((sh.T + R * g.cov_j - 1) / (R * g.cov_j)) < kCovTiles)
+    g.cov_j /= 2;
+  g.cov_ntile = (sh.T + R * g.cov_j - 1) / (R * g.cov_j);
   // Position segments of the transition GEMM and spans of the duration
   // kernel: as long as possible (fewer partials to reduce) while the grid
   // still has about kPostWorkgroups workgroups.
@@ -472,7 +478,7 @@ hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream
   PostGeom g;
   post_geometry(sh, g);
   hipLaunchKernelGGL(k_cov_partial, dim3(g.cov_ntile, sh.B), dim3(kCovThreads), 0, st, sh, pa,
-                     g.cov_ntile);
+                     g.cov_ntile, g.cov_j);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_cov_anchor, dim3(sh.B, sh.C), dim3(kCovThreads), 0, st, sh, pa,
@@ -480,7 +486,7 @@ hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_cov_write, dim3(g.cov_ntile, sh.B), dim3(kCovThreads), 0, st, sh, pa,
-                     g.cov_ntile);
+                     g.cov_ntile, g.cov_j);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ntc = (sh.C + kTxTile - 1) / kTxTile;
