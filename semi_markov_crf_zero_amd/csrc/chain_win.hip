@@ -96,18 +96,32 @@ __device__ __forceinline__ void stage_dur(const WSmem &sm, const ChainShape &sh,
   for (int i = threadIdx.x; i < sh.K * sh.C; i += NT) sm.dtab[i] = exp((double)dur[i]);
 }
 
-// exp(trans) row of a chain lane for the contraction of direction fwd
-// (float64, for the same reason): tr[c_in] = weight of input label c_in for
-// output label c, zero past C.
+// The contraction of a label is split over kSplit lanes of wave 0: lane l
+// takes label c = l % CMAX and the previous labels c' of part
+// h = (l / CMAX) % kSplit, c' = h*CMAX/kSplit + j; lane_swap_add joins the
+// parts (lanes CMAX, 2*CMAX apart).  Fewer multiply-adds, LDS reads and
+// weight registers per lane on the dependent chain, for two or three
+// cross-lane adds.
+template <int CMAX>
+constexpr int kSplit = CMAX >= 32 ? 2 : 4;
+static_assert(32 * kSplit<32> <= 64 && 16 * kSplit<16> <= 64, "parts fit one wave");
+
+// exp(trans) weights of lane `lane` of wave 0 for the contraction of
+// direction fwd (float64, for the same reason): tr[j] = weight of input
+// label c' = h*CMAX/kSplit + j for output label c, zero past C.
 template <int CMAX>
 __device__ __forceinline__ void load_tr_row(const ChainShape &sh, const float *__restrict__ trans,
-                                            bool fwd, int c, double (&tr)[CMAX]) {
-  const int C = sh.C;
+                                            bool fwd, int lane,
+                                            double (&tr)[CMAX / kSplit<CMAX>]) {
+  constexpr int NJ = CMAX / kSplit<CMAX>;
+  const int C = sh.C, c = lane % CMAX, h = (lane / CMAX) % kSplit<CMAX>;
 #pragma unroll
-  for (int ci = 0; ci < CMAX; ++ci)
-    tr[ci] = (c < C && ci < C)
-                 ? exp((double)(fwd ? trans[(size_t)ci * C + c] : trans[(size_t)c * C + ci]))
-                 : 0.0;
+  for (int j = 0; j < NJ; ++j) {
+    const int ci = h * NJ + j;
+    tr[j] = (c < C && ci < C)
+                ? exp((double)(fwd ? trans[(size_t)ci * C + c] : trans[(size_t)c * C + ci]))
+                : 0.0;
+  }
 }
 
 // Sum of a float64 over aligned groups of gw consecutive lanes (gw a power of
@@ -212,36 +226,47 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Exp-space contraction: lane c < C holds a[c] = exp(o[c]) / 2^B (at most
-// 1, the largest >= 1/2) and its exp(trans) row, and receives
-// sum_{c'} a[c'] * tr[c'] in float64.  The e row is broadcast through LDS,
-// two values per read, all reads issued before the first multiply.  All 64
-// lanes of wave 0 call.
-// `meanwhile` runs after the e-row reads are issued and before their
+// 1, the largest >= 1/2) and receives sum_{c'} a[c'] * tr[c'] in float64.
+// The e row is broadcast through LDS, two values per read, all reads issued
+// before the first multiply; every lane sums its part of the previous labels
+// (load_tr_row) and the parts meet by lane swaps.  All 64 lanes of wave 0
+// call.  `meanwhile` runs after the e-row reads are issued and before their
 // results are used: independent work placed there hides in the LDS latency
 // instead of delaying the step (a wave issues in order).
 template <int CMAX, typename F>
 __device__ __forceinline__ double chain_contract(const WSmem &sm, const ChainShape &sh, int lane,
-                                                 double a, const double (&tr)[CMAX],
+                                                 double a, const double (&tr)[CMAX / kSplit<CMAX>],
                                                  F &&meanwhile) {
+  constexpr int SP = kSplit<CMAX>, NJ = CMAX / SP;
+  static_assert(NJ % 2 == 0, "pairs of previous labels per read");
   if (lane < CMAX) sm.erow[lane] = lane < sh.C ? a : 0.0;
   wave_lds_sync();
-  const double2 *e2 = reinterpret_cast<const double2 *>(sm.erow);
-  double2 ev[CMAX / 2];
+  const int h = (lane / CMAX) % SP;
+  const double2 *e2 = reinterpret_cast<const double2 *>(sm.erow + h * NJ);
+  double2 ev[NJ / 2];
 #pragma unroll
-  for (int q = 0; q < CMAX / 2; ++q) ev[q] = e2[q];
+  for (int q = 0; q < NJ / 2; ++q) ev[q] = e2[q];
   __builtin_amdgcn_sched_barrier(0);
   meanwhile();
   __builtin_amdgcn_sched_barrier(0);
-  double d0 = 0.0, d1 = 0.0, d2 = 0.0, d3 = 0.0;
+  double d;
+  if constexpr (NJ >= 4) {
+    double d0 = 0.0, d1 = 0.0, d2 = 0.0, d3 = 0.0;
 #pragma unroll
-  for (int q = 0; q < CMAX / 2; q += 2) {
-    d0 = fma(ev[q].x, tr[2 * q], d0);
-    d1 = fma(ev[q].y, tr[2 * q + 1], d1);
-    d2 = fma(ev[q + 1].x, tr[2 * q + 2], d2);
-    d3 = fma(ev[q + 1].y, tr[2 * q + 3], d3);
+    for (int q = 0; q < NJ / 2; q += 2) {
+      d0 = fma(ev[q].x, tr[2 * q], d0);
+      d1 = fma(ev[q].y, tr[2 * q + 1], d1);
+      d2 = fma(ev[q + 1].x, tr[2 * q + 2], d2);
+      d3 = fma(ev[q + 1].y, tr[2 * q + 3], d3);
+    }
+    d = (d0 + d1) + (d2 + d3);
+  } else {
+    d = fma(ev[0].y, tr[1], ev[0].x * tr[0]);
   }
+  d = lane_swap_add<CMAX>(d);
+  if constexpr (SP >= 4) d = lane_swap_add<2 * CMAX>(d);
   wave_lds_sync();
-  return (d0 + d1) + (d2 + d3);
+  return d;
 }
 
 __device__ __forceinline__ void wsave(double *__restrict__ dst, const WSmem &sm,
@@ -357,15 +382,19 @@ struct ChainState {
 // leaves [Bm - kScaleSpan, Bm + kScaleSpan]; every value stays exact either
 // way.  o / m of step s_rec (the last burn-in step, see k_sweep_w) go to
 // o_rec / m_rec, those of the chain's last step to o_end / m_end.
+// The U steps are unrolled so the window never moves between registers:
+// wv[U - i + m] is the entry m+1 steps before step i, and step i writes its
+// entry to wv[U - 1 - i]; the window rolls once per block.
 constexpr int kScaleSpan = 256;
 template <int CMAX>
 __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &sm, int G, int s0,
                                             int nb, int nsteps, int t0, int sigma, int buf,
                                             bool tail, int lane, bool chain,
                                             const double (&Dn)[kNearW + 1],
-                                            const double (&tr)[CMAX], int s_rec, ChainState &cs,
-                                            int &R, int &Bm, double &o_rec, double &m_rec,
-                                            double &o_end, double &m_end, double &lz) {
+                                            const double (&tr)[CMAX / kSplit<CMAX>], int s_rec,
+                                            ChainState &cs, int &R, int &Bm, double &o_rec,
+                                            double &m_rec, double &o_end, double &m_end,
+                                            double &lz) {
   const int C = sh.C, K = sh.K, S = 3 * C + 1;
   const int cl = chain ? lane : 0;  // label whose LDS values this lane reads
   const double *part = sm.part + (size_t)buf * U * G * C;
@@ -374,6 +403,11 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
     for (int g = 0; g < G; ++g) f += part[(i * G + g) * C + cl];
     return f;
   };
+  double wv[U + kNearW];
+#pragma unroll
+  for (int m = 0; m < kNearW; ++m) wv[U + m] = cs.hist[m];
+#pragma unroll
+  for (int i = 0; i < U; ++i) wv[i] = 0.0;
   int shacc = 0;               // rebase shift of this label since the block began
   int slot = pos_slot(t0, K);  // ring slot of the step's position
   double *stg = sm.stg + buf * U * S;
@@ -381,8 +415,10 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
   double fxn = sm.efx[buf * U * C + cl], fyn = sm.efy[buf * U * C + cl];
   int nqn = sm.en[buf * U * C + cl];
   double fsn = far_of(0);
-#pragma unroll 1
-  for (int i = 0; i < nb; ++i) {
+  double nr = cs.nr;
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    if (i >= nb) break;
     const double fx = fxn, fy = fyn, fs = fsn;
     const int nq = sigma * nqn;
     if (i + 1 < nb) {  // the next step's inputs, read a step ahead
@@ -399,18 +435,19 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
       double n0 = 0.0, n1 = 0.0;
 #pragma unroll
       for (int k = 2; k <= kNearW; k += 2) {
-        n0 = fma(Dn[k], cs.hist[k - 2], n0);
-        if (k + 1 <= kNearW) n1 = fma(Dn[k + 1], cs.hist[k - 1], n1);
+        n0 = fma(Dn[k], wv[U - i + k - 2], n0);
+        if (k + 1 <= kNearW) n1 = fma(Dn[k + 1], wv[U - i + k - 1], n1);
       }
       nrn = n0 + n1;
+      // keep the sum here, inside the LDS latency, rather than sunk to its use
+      __asm__ volatile("" : "+v"(nrn));
     };
     const int step = s0 + i;
-    const int t = t0 + sigma * i;
     const bool last = step == nsteps - 1;
     const bool lz_step = last && tail;
     // exp(o) = x * 2^E, o = alpha (forward) or v (backward)
     const double x =
-        chain ? (ldexp(fs, -(cs.shprev + shacc)) + fma(Dn[1], cs.hist[0], cs.nr)) * fx : 0.0;
+        chain ? (ldexp(fs, -(cs.shprev + shacc)) + fma(Dn[1], wv[U - i], nr)) * fx : 0.0;
     const int E = R + nq;
     const int ex = (chain && x > 0.0) ? E + exponent_of(x) : kNoExp;
     if (__any(ex - Bm > kScaleSpan) || !__any(ex - Bm >= -kScaleSpan)) Bm = wave_max_i(ex);
@@ -422,22 +459,25 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
     if (lz_step) {
       lz = (double)Bm * kLn2 + log(wave_sum(a));
     } else {
-      // exp(m) = d * 2^Bm, m = u (forward) or beta (backward)
+      // exp(m) = d * 2^Bm, m = u (forward) or beta (backward).  Every lane
+      // runs the rest of the step (lanes past C on harmless values, n = 0,
+      // no stores), so the window's registers see no divergent branch.
       const double d = chain_contract<CMAX>(sm, sh, lane, a, tr, near_next);
-      if (chain) {
-        stg[i * S + 2 * C + lane] = d;
-        // entry exp(m -+ S) / 2^R = y * 2^s
-        const double y = d * fy;
-        const int s = Bm - nq - R;
-        const int ey = exponent_of(y) + s;
-        const int n = (ey > kRebaseExp || ey < -kRebaseExp) ? ey : 0;
-        if (n != 0) {  // rebase: the window and this block's ring entries follow at once
-          R += n;
-          shacc += n;
+      // entry exp(m -+ S) / 2^R = y * 2^s
+      const double y = d * fy;
+      const int s = Bm - nq - R;
+      const int ey = exponent_of(y) + s;
+      const int n = (chain && (ey > kRebaseExp || ey < -kRebaseExp)) ? ey : 0;
+      if (chain) stg[i * S + 2 * C + lane] = d;
+      if (__any(n != 0)) {  // rebase: the window and this block's ring entries follow at once
+        R += n;
+        shacc += n;
 #pragma unroll
-          for (int k = 0; k < kNearW; ++k) cs.hist[k] = ldexp(cs.hist[k], -n);
-          nrn = ldexp(nrn, -n);
+        for (int m = 0; m < kNearW; ++m) wv[U - i + m] = ldexp(wv[U - i + m], -n);
+        nrn = ldexp(nrn, -n);
+        if (chain && n != 0) {
           int sl = slot;
+#pragma unroll
           for (int m = 0; m < i; ++m) {
             sl -= sigma;
             sl += sl < 0 ? K : 0;
@@ -445,29 +485,32 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
             sm.ring[sl * C + lane] = ldexp(sm.ring[sl * C + lane], -n);
           }
         }
-        const double g = ldexp(y, s - n);
-        sm.ring[slot * C + lane] = g;
-#pragma unroll
-        for (int k = kNearW - 1; k > 0; --k) cs.hist[k] = cs.hist[k - 1];
-        cs.hist[0] = g;
-        if (last || step == s_rec) {
-          const double o = log(x) + (double)E * kLn2, m = log(d) + (double)Bm * kLn2;
-          if (last) {
-            o_end = o;
-            m_end = m;
-          } else {
-            o_rec = o;
-            m_rec = m;
-          }
+      }
+      const double g = ldexp(y, s - n);
+      if (chain) sm.ring[slot * C + lane] = g;
+      wv[U - 1 - i] = g;
+      if (last || step == s_rec) {
+        const double o = log(x) + (double)E * kLn2, m = log(d) + (double)Bm * kLn2;
+        if (last) {
+          o_end = o;
+          m_end = m;
+        } else {
+          o_rec = o;
+          m_rec = m;
         }
       }
       if (lane == 0) stg[i * S + 3 * C] = (double)Bm;
     }
-    cs.nr = nrn;
+    nr = nrn;
     slot += sigma;
     slot += slot < 0 ? K : 0;
     slot -= slot >= K ? K : 0;
   }
+  // roll the window by the block (a block of fewer than U steps ends the
+  // chunk, so its window is not used again)
+#pragma unroll
+  for (int m = 0; m < kNearW; ++m) cs.hist[m] = wv[m];
+  cs.nr = nr;
   cs.shprev = shacc;
   if (chain) sm.shiftn[lane] = shacc;
   const bool any = __any((chain && shacc != 0) ? 1 : 0);
@@ -507,7 +550,7 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   win.init(sh);
   stage_dur(sm, sh, dur, NT);
   double Dn[kNearW + 1];  // near-part weights of the chain lanes (k = 1 .. 2U-1)
-  double tr[CMAX];        // exp(trans) row of the chain lanes
+  double tr[CMAX / kSplit<CMAX>];  // this lane's part of the exp(trans) weights
   if (tid < 64) {
 #pragma unroll
     for (int k = 0; k <= kNearW; ++k)

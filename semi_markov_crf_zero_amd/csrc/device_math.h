@@ -142,6 +142,40 @@ __device__ __forceinline__ double dpp_f64(double v, int ctrl) {
   return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
 }
 
+// v(l) + v(l ^ S) in every lane l, for S = 8, 16 or 32: a row rotation by 8
+// (DPP) within each row of 16, or gfx950's lane swaps between the two rows of
+// each row pair (S = 16) or the two halves of the wave (S = 32).  Both lanes
+// of a pair add the same two values, so both hold the same sum.
+template <int S>
+__device__ __forceinline__ double lane_swap_add(double v) {
+  static_assert(S == 8 || S == 16 || S == 32, "lane distance 8, 16 or 32");
+  const long long b = __builtin_bit_cast(long long, v);
+  const unsigned lo = (unsigned)(b & 0xffffffffLL), hi = (unsigned)((unsigned long long)b >> 32);
+  unsigned plo, phi;  // the partner lane's halves
+  if constexpr (S == 8) {
+    plo = (unsigned)__builtin_amdgcn_update_dpp((int)lo, (int)lo, 0x128, 0xf, 0xf, false);
+    phi = (unsigned)__builtin_amdgcn_update_dpp((int)hi, (int)hi, 0x128, 0xf, 0xf, false);
+    return v + __builtin_bit_cast(double, ((unsigned long long)phi << 32) | plo);
+  } else {
+    // swap(x, x): the first result holds the lane's own value in the lower
+    // row (half) of each pair and the partner's in the upper one, the second
+    // the other way round
+    if constexpr (S == 16) {
+      const auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+      const auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+      const double u = __builtin_bit_cast(double, ((unsigned long long)rh[0] << 32) | rl[0]);
+      const double w = __builtin_bit_cast(double, ((unsigned long long)rh[1] << 32) | rl[1]);
+      return u + w;
+    } else {
+      const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+      const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+      const double u = __builtin_bit_cast(double, ((unsigned long long)rh[0] << 32) | rl[0]);
+      const double w = __builtin_bit_cast(double, ((unsigned long long)rh[1] << 32) | rl[1]);
+      return u + w;
+    }
+  }
+}
+
 __device__ __forceinline__ int dpp_i(int v, int ctrl) {
   switch (ctrl) {
     case 0xB1: return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xf, 0xf, false);
