@@ -71,7 +71,11 @@ bool win_config(int C, int K, ChainShape &sh) {
   // far parts: durations k >= 2U over the three helper waves
   const int P = (NT - 64) / cp;
   const int nfar = K - (2 * kWinU - 1);
-  const int A = nfar > 0 ? (nfar + P - 1) / P : 1;
+  int A = nfar > 0 ? (nfar + P - 1) / P : 1;
+  // a whole number of the far loop's duration chunks (2, 4 or 8) per group,
+  // so no chunk reaches into the next group's durations
+  const int dch = A <= 2 ? 2 : (A <= 4 ? 4 : 8);
+  A = (A + dch - 1) / dch * dch;
   if (win_lds_bytes(C, K, P) > kMaxDynLds) return false;
   sh.NT = NT;
   sh.P = P;

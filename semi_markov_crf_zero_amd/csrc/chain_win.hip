@@ -67,8 +67,8 @@ __device__ __forceinline__ WSmem wcarve(unsigned char *base, const ChainShape &s
   WSmem m;
   size_t off = 0;
   const int C4 = cpad(s.C);
-  m.ring = reinterpret_cast<double *>(base + off); off += (size_t)s.K * s.C * 8;
-  m.dtab = reinterpret_cast<double *>(base + off); off += (size_t)s.K * s.C * 8;
+  m.ring = reinterpret_cast<double *>(base + off); off += (size_t)(s.K + kWinMirror) * s.C * 8;
+  m.dtab = reinterpret_cast<double *>(base + off); off += (size_t)(s.K + kWinDurPad) * s.C * 8;
   m.part = reinterpret_cast<double *>(base + off);
   off += (size_t)2 * U * part_groups(s, NT) * s.C * 8;  // [2][U][G][C]
   m.stg = reinterpret_cast<double *>(base + off); off += (size_t)2 * U * (3 * s.C + 1) * 8;
@@ -88,12 +88,21 @@ __device__ __forceinline__ int pos_slot(int pos, int K) {
   return s < 0 ? s + K : s;
 }
 
+// Store ring slot `slot` of label c, and its mirror copy at slot + K for
+// the slots below kWinMirror (read by the far loop across the wrap).
+__device__ __forceinline__ void ring_put(const WSmem &sm, int K, int C, int slot, int c,
+                                         double v) {
+  sm.ring[slot * C + c] = v;
+  if (slot < kWinMirror) sm.ring[(slot + K) * C + c] = v;
+}
+
 // exp(dur) in float64 (a rounded weight would perturb the parameters, and
 // the parameter gradients move by that times a sensitivity that grows with
 // the sequence length): dtab[(k-1)*C + c] = exp(dur[k-1][c]).
 __device__ __forceinline__ void stage_dur(const WSmem &sm, const ChainShape &sh,
                                           const float *__restrict__ dur, int NT) {
   for (int i = threadIdx.x; i < sh.K * sh.C; i += NT) sm.dtab[i] = exp((double)dur[i]);
+  for (int i = threadIdx.x; i < kWinDurPad * sh.C; i += NT) sm.dtab[sh.K * sh.C + i] = 0.0;
 }
 
 // The contraction of a label is split over kSplit lanes of wave 0: lane l
@@ -160,33 +169,37 @@ struct Win {
   }
 
   // Step i of the block (position t0 + sigma*i) needs, for duration k, the
-  // entry at t0 - sigma*(k - i); positions inside the block (k <= i) and
-  // beyond the window (k - i > K) count 0.  Durations go in chunks of DCH:
-  // the chunk's weights and its DCH+U-1 entries come from LDS, then U*DCH
-  // fused multiply-adds with compile-time register indices.
+  // entry at t0 - sigma*(k - i); here k >= 2U > i and k <= K, so k - i lies
+  // in [1, K].  Durations go in chunks of DCH (A is a multiple of DCH, so a
+  // chunk holds this group's durations or rows past K, which are zero): the
+  // chunk's weights and its DCH+U-1 entries (consecutive positions, read
+  // from a start slot that needs no wrap thanks to the ring's mirror) come
+  // from LDS with no branch, then U*DCH fused multiply-adds with
+  // compile-time register indices.
   template <int DCH>
   __device__ __forceinline__ void far(const WSmem &sm, const ChainShape &sh, int t0, int sigma,
                                       double (&F)[U]) {
+    constexpr int NR = DCH + U - 1;  // entries per chunk
+    static_assert(NR - 1 <= kWinMirror && DCH <= kWinDurPad, "mirror and padding cover a chunk");
 #pragma unroll
     for (int i = 0; i < U; ++i) F[i] = 0.0;
     if (!on) return;
     const int K = sh.K, C = sh.C;
-    // slot of position t0 - sigma*m for m in [1, K]: base - sigma*m brought
-    // back into [0, K) by one correction
     const int base = pos_slot(t0, K);
+    const int rstep = -sigma * C;  // ring index step to the next older position
+    const double *dp = sm.dtab + (size_t)(a0 - 1) * C + kc;
     for (int jb = 0; jb < nage; jb += DCH) {
-      double dv[DCH], wv[DCH + U - 1];
+      double dv[DCH], wv[NR];
 #pragma unroll
-      for (int jj = 0; jj < DCH; ++jj)
-        dv[jj] = jb + jj < nage ? sm.dtab[(a0 + jb + jj - 1) * C + kc] : 0.0;
+      for (int jj = 0; jj < DCH; ++jj) dv[jj] = dp[(jb + jj) * C];
+      // wv[q]: entry at m = k - i = m0 + q, q = jj - i + U - 1; forward the
+      // slots fall with q, so a start near 0 moves to its mirror copy
+      const int m0 = a0 + jb - (U - 1);
+      int s0 = pos_slot(base - sigma * m0, K);
+      if (sigma > 0 && s0 < NR - 1) s0 += K;
+      const double *rp = sm.ring + (size_t)s0 * C + kc;
 #pragma unroll
-      for (int q = 0; q < DCH + U - 1; ++q) {
-        const int m = a0 + jb + q - (U - 1);  // wv[q]: entry at m = k - i, q = jj - i + U - 1
-        int sl = base - sigma * m;
-        sl += sl < 0 ? K : 0;
-        sl -= sl >= K ? K : 0;
-        wv[q] = (m >= 1 && m <= K) ? sm.ring[sl * C + kc] : 0.0;
-      }
+      for (int q = 0; q < NR; ++q) wv[q] = rp[q * rstep];
 #pragma unroll
       for (int i = 0; i < U; ++i) {
 #pragma unroll
@@ -286,6 +299,9 @@ __device__ __forceinline__ void wload(const double *__restrict__ src, const WSme
                                       double &o, double &m, int NT) {
   const int n = sh.K * sh.C;
   for (int i = threadIdx.x; i < n; i += NT) sm.ring[i] = src[i];
+  // the mirror of slots [0, kWinMirror) (those below K)
+  const int nm = (sh.K < kWinMirror ? sh.K : kWinMirror) * sh.C;
+  for (int i = threadIdx.x; i < nm; i += NT) sm.ring[n + i] = src[i];
   if (chain) {
     R = (int)src[n + lane];
     o = src[n + sh.C + lane];
@@ -482,12 +498,12 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
             sl -= sigma;
             sl += sl < 0 ? K : 0;
             sl -= sl >= K ? K : 0;
-            sm.ring[sl * C + lane] = ldexp(sm.ring[sl * C + lane], -n);
+            ring_put(sm, K, C, sl, lane, ldexp(sm.ring[sl * C + lane], -n));
           }
         }
       }
       const double g = ldexp(y, s - n);
-      if (chain) sm.ring[slot * C + lane] = g;
+      if (chain) ring_put(sm, K, C, slot, lane, g);
       wv[U - 1 - i] = g;
       if (last || step == s_rec) {
         const double o = log(x) + (double)E * kLn2, m = log(d) + (double)Bm * kLn2;
@@ -583,7 +599,7 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   }
   const int tbegin = fwd ? p0 - wb : p1 + wb;  // where the sweep starts
   if (iter == 0) {
-    for (int i = tid; i < K * C; i += NT) sm.ring[i] = 0.0;
+    for (int i = tid; i < (K + kWinMirror) * C; i += NT) sm.ring[i] = 0.0;
     __syncthreads();
     if (exact) {
       // entry u[0] - S[0] = 0 forward; beta[L] + S[L] = S[L] backward
@@ -594,14 +610,14 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
           v = es.ep[i];
           R = es.n[i];
         }
-        sm.ring[pos_slot(tstart, K) * C + lane] = v;
+        ring_put(sm, K, C, pos_slot(tstart, K), lane, v);
       }
     } else {
       // neutral start: every entry of the window (positions inside [0, L]) is 1
       for (int i = tid; i < K * C; i += NT) {
         const int dq = i / C, c = i % C;
         const int q = tbegin - sigma * dq;
-        if (q >= 0 && q <= L) sm.ring[pos_slot(q, K) * C + c] = 1.0;
+        if (q >= 0 && q <= L) ring_put(sm, K, C, pos_slot(q, K), c, 1.0);
       }
     }
     __syncthreads();
@@ -691,14 +707,19 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
     __syncthreads();
     if (sm.flag[0]) {
       // rare: rescale the older entries of the labels that rebased (every
-      // slot but the block's new entries)
-      const int nold = K - nb;
-      for (int q = tid; q < nold * C; q += NT) {
-        const int m = 1 + q / C, c = q % C;
-        const int n = sm.shiftn[c];
-        if (n != 0) {
-          const int sl = pos_slot(t0 - sigma * m, K);
-          sm.ring[sl * C + c] = ldexp(sm.ring[sl * C + c], -n);
+      // slot but the block's new entries), label by label over all threads
+      const int nl = lane < C ? sm.shiftn[lane] : 0;
+      unsigned long long rb = __ballot(nl != 0);
+      const int slot0 = pos_slot(t0, K);
+      while (rb) {
+        const int c = __builtin_ctzll(rb);
+        rb &= rb - 1;
+        const int n = __builtin_amdgcn_readlane(nl, c);
+        for (int m = 1 + tid; m <= K - nb; m += NT) {
+          int sl = slot0 - sigma * m;
+          sl += sl < 0 ? K : 0;
+          sl -= sl >= K ? K : 0;
+          ring_put(sm, K, C, sl, c, ldexp(sm.ring[sl * C + c], -n));
         }
       }
       __syncthreads();
