@@ -260,7 +260,8 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
 // relate through one.  A tile whose range of a exceeds kDurRange nats (only
 // with extreme scores) takes the direct path for that label: one exp per
 // cell.
-constexpr int kDurLags = 512;
+constexpr int kDurLags = 256;
+static_assert(kDurW % 8 == 0, "duration tiles hold whole blocks of 8 starts");
 constexpr double kDurRange = 600.0;
 
 template <int KB>
@@ -278,8 +279,11 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
   const int c = c0 + cl;
   const int L = pa.lengths[b];
   double *sa = reinterpret_cast<double *>(lds);  // [kDurW][16]
-  double *sb = sa + (size_t)kDurW * 16;          // [kDurW + kDurLags][16], index e - s0 - klo
-  double *pmax = sb + (size_t)(kDurW + min(K, kDurLags)) * 16;  // [16][16] partial max / min of a
+  // [kDurW + lags + KB][16], index e - s0 - klo; the rows past the tile's
+  // last end are zero on the fast path, so its reads need no bound check
+  const int sbrows = kDurW + min(K, kDurLags) + KB;
+  double *sb = sa + (size_t)kDurW * 16;
+  double *pmax = sb + (size_t)sbrows * 16;  // [16][16] partial max / min of a
   double *pmin = pmax + 256;
   double *rho = pmin + 256;                      // [16] reference per label
   int *fast = reinterpret_cast<int *>(rho + 16);  // [16]
@@ -336,13 +340,14 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
         fast[tid] = (hi - lo <= kDurRange) ? 1 : 0;  // false for non-finite ranges
       }
       __syncthreads();
-      for (int i = tid; i < ns * CG; i += kDurThreads) {
+      // fast labels: the factors, zero past the tile's starts and ends
+      for (int i = tid; i < kDurW * CG; i += kDurThreads) {
         const int ss = i / CG, cc = i % CG;
-        if (fast[cc]) sa[ss * 16 + cc] = exp_wide(sa[ss * 16 + cc] - rho[cc]);
+        if (fast[cc]) sa[ss * 16 + cc] = ss < ns ? exp_wide(sa[ss * 16 + cc] - rho[cc]) : 0.0;
       }
-      for (int i = tid; i < ne * CG; i += kDurThreads) {
+      for (int i = tid; i < sbrows * CG; i += kDurThreads) {
         const int ee = i / CG, cc = i % CG;
-        if (fast[cc]) sb[ee * 16 + cc] = exp_wide(sb[ee * 16 + cc] + rho[cc]);
+        if (fast[cc]) sb[ee * 16 + cc] = ee < ne ? exp_wide(sb[ee * 16 + cc] + rho[cc]) : 0.0;
       }
       __syncthreads();
       if (!act) continue;
@@ -352,15 +357,12 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
         for (int ss0 = 0; ss0 < ns; ss0 += 8) {
           double A[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) A[i] = ss0 + i < ns ? sa[(ss0 + i) * 16 + cl] : 0.0;
+          for (int i = 0; i < 8; ++i) A[i] = sa[(ss0 + i) * 16 + cl];
 #pragma unroll
           for (int jb = 0; jb < KB; jb += JB) {
             double W[8 + JB - 1];
 #pragma unroll
-            for (int q = 0; q < 8 + JB - 1; ++q) {
-              const int ee = ss0 + kofs + jb + q;
-              W[q] = ee < ne ? sb[ee * 16 + cl] : 0.0;
-            }
+            for (int q = 0; q < 8 + JB - 1; ++q) W[q] = sb[(ss0 + kofs + jb + q) * 16 + cl];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -471,7 +473,7 @@ void post_geometry(const ChainShape &sh, PostGeom &g) {
   while (g.dur_kb < 32 && cg * ((lags + g.dur_kb - 1) / g.dur_kb) > kDurThreads) g.dur_kb *= 2;
   g.dur_npg = (sh.K + kDurLags - 1) / kDurLags;
   // a, b, partial maxima and minima of a, per-label references and paths
-  g.dur_lds = (size_t)(kDurW + kDurW + lags) * 16 * 8 + 2 * 256 * 8 + 16 * 8 + 16 * 4;
+  g.dur_lds = (size_t)(kDurW + kDurW + lags + g.dur_kb) * 16 * 8 + 2 * 256 * 8 + 16 * 8 + 16 * 4;
 }
 
 hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream_t st) {
