@@ -25,7 +25,7 @@ namespace {
 constexpr int kCovThreads = 256;
 // consecutive positions per coverage thread: 16, halved (down to 4) while a
 // batch has fewer than kCovTiles tiles (short sequences need the parallelism)
-constexpr int kCovJ = 16, kCovJMin = 4, kCovTiles = 1024;
+constexpr int kCovJ = 16, kCovJMin = 4, kCovTiles = 1024;  // J: a kernel instance each
 constexpr int kTxThreads = 256;
 constexpr int kTxTile = 64;   // output tile of the transition GEMM (64 x 64)
 constexpr int kTxRows = 32;   // positions staged in LDS per batch
@@ -46,31 +46,49 @@ __device__ __forceinline__ bool valid_len(const ChainShape &sh, int L) { return 
 // (r, c) owns J consecutive positions of label c), as in the score scan.
 // delta[t,c] = E_start[t,c] - E_end[t,c] (E_end[0] = 0), float64-accurate:
 // the coverage is their running sum over the whole sequence.
-__device__ __forceinline__ double cov_delta(const PostArgs &pa, const ChainShape &sh, int b,
-                                            int t, int c, double logZ) {
-  const size_t i = rix(sh, b, t) + c;
-  double d = exp(pa.row_u[i] + pa.row_v[i] - logZ);
-  if (t >= 1) d -= exp(pa.row_a[i] + pa.row_b[i] - logZ);
-  return d;
+// The deltas of positions t0 .. t0+J-1 of label c (0 at t >= L).  Every
+// load is issued before the first exponential (indices clamped into the
+// sequence), so a thread waits for memory once rather than once per
+// position.
+template <int J>
+__device__ __forceinline__ void cov_deltas(const PostArgs &pa, const ChainShape &sh, int b,
+                                           int t0, int c, int L, double logZ, double (&d)[J]) {
+  double u[J], v[J], a[J], w[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int t = t0 + j < L ? t0 + j : L - 1;
+    const size_t i = rix(sh, b, t) + c;
+    u[j] = pa.row_u[i];
+    v[j] = pa.row_v[i];
+    a[j] = pa.row_a[i];
+    w[j] = pa.row_b[i];
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int t = t0 + j;
+    double dd = exp(u[j] + v[j] - logZ);
+    if (t >= 1) dd -= exp(a[j] + w[j] - logZ);
+    d[j] = t < L ? dd : 0.0;
+  }
 }
 
+template <int J>
 __global__ __launch_bounds__(kCovThreads) void k_cov_partial(ChainShape sh, PostArgs pa,
-                                                             int ntile, int J) {
+                                                             int ntile) {
   __shared__ double red1[kCovThreads], red2[kCovThreads];
   const int tile = blockIdx.x, b = blockIdx.y;
   const int C = sh.C, R = kCovThreads / C, tid = threadIdx.x;
   const int c = tid % C, r = tid / C;
   const int L = pa.lengths[b];
   double s1 = 0.0, s2 = 0.0;
-  if (r < R && valid_len(sh, L)) {
-    const double logZ = pa.logz[b];
-    const int t0 = tile * R * J + r * J;
+  const int t0 = tile * R * J + r * J;
+  if (r < R && valid_len(sh, L) && t0 < L) {
+    double d[J];
+    cov_deltas<J>(pa, sh, b, t0, c, L, pa.logz[b], d);
+#pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int t = t0 + j;
-      if (t >= L) break;
-      const double d = cov_delta(pa, sh, b, t, c, logZ);
-      s1 += d;
-      s2 += d * (double)(L - t);  // sum_{i<L} mu[i] = sum_t delta[t] (L - t)
+      s1 += d[j];
+      s2 += d[j] * (double)(L - (t0 + j));  // sum_{i<L} mu[i] = sum_t delta[t] (L - t)
     }
   }
   red1[tid] = s1;
@@ -124,8 +142,8 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_anchor(ChainShape sh, PostA
   }
 }
 
-__global__ __launch_bounds__(kCovThreads) void k_cov_write(ChainShape sh, PostArgs pa, int ntile,
-                                                           int J) {
+template <int J>
+__global__ __launch_bounds__(kCovThreads) void k_cov_write(ChainShape sh, PostArgs pa, int ntile) {
   __shared__ double runs[kCovThreads];
   const int tile = blockIdx.x, b = blockIdx.y;
   const int C = sh.C, R = kCovThreads / C, tid = threadIdx.x;
@@ -134,14 +152,13 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_write(ChainShape sh, PostAr
   const bool ok = valid_len(sh, L);
   const double logZ = ok ? pa.logz[b] : 0.0;
   const int t0 = tile * R * J + r * J;
+  double d[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) d[j] = 0.0;
+  if (r < R && ok && t0 < L) cov_deltas<J>(pa, sh, b, t0, c, L, logZ, d);
   double own = 0.0;
-  if (r < R && ok) {
-    for (int j = 0; j < J; ++j) {
-      const int t = t0 + j;
-      if (t >= L) break;
-      own += cov_delta(pa, sh, b, t, c, logZ);
-    }
-  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) own += d[j];
   runs[tid] = own;
   __syncthreads();
   if (r >= R) return;
@@ -152,18 +169,20 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_write(ChainShape sh, PostAr
     mean = sh.center ? pa.cov_mean[(size_t)b * C + c] : 0.0;
     w = pa.grad_logz ? (double)pa.grad_logz[b] : 1.0;
   }
+#pragma unroll
   for (int j = 0; j < J; ++j) {
     const int t = t0 + j;
-    if (t >= sh.T) break;
-    float m_out = 0.f, g_out = 0.f;
-    if (ok && t < L) {
-      mu += cov_delta(pa, sh, b, t, c, logZ);
-      m_out = (float)mu;
-      g_out = (float)(w * (mu - mean));
+    if (t < sh.T) {
+      float m_out = 0.f, g_out = 0.f;
+      if (ok && t < L) {
+        mu += d[j];
+        m_out = (float)mu;
+        g_out = (float)(w * (mu - mean));
+      }
+      const size_t o = ((size_t)b * sh.T + t) * C + c;
+      pa.grad_emissions[o] = g_out;
+      if (pa.marginals) pa.marginals[o] = m_out;
     }
-    const size_t o = ((size_t)b * sh.T + t) * C + c;
-    pa.grad_emissions[o] = g_out;
-    if (pa.marginals) pa.marginals[o] = m_out;
   }
 }
 
@@ -479,16 +498,23 @@ void post_geometry(const ChainShape &sh, PostGeom &g) {
 hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream_t st) {
   PostGeom g;
   post_geometry(sh, g);
-  hipLaunchKernelGGL(k_cov_partial, dim3(g.cov_ntile, sh.B), dim3(kCovThreads), 0, st, sh, pa,
-                     g.cov_ntile, g.cov_j);
+  const dim3 gc(g.cov_ntile, sh.B);
+  switch (g.cov_j) {
+    case 4: hipLaunchKernelGGL(k_cov_partial<4>, gc, dim3(kCovThreads), 0, st, sh, pa, g.cov_ntile); break;
+    case 8: hipLaunchKernelGGL(k_cov_partial<8>, gc, dim3(kCovThreads), 0, st, sh, pa, g.cov_ntile); break;
+    default: hipLaunchKernelGGL(k_cov_partial<16>, gc, dim3(kCovThreads), 0, st, sh, pa, g.cov_ntile); break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_cov_anchor, dim3(sh.B, sh.C), dim3(kCovThreads), 0, st, sh, pa,
                      g.cov_ntile);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_cov_write, dim3(g.cov_ntile, sh.B), dim3(kCovThreads), 0, st, sh, pa,
-                     g.cov_ntile, g.cov_j);
+  switch (g.cov_j) {
+    case 4: hipLaunchKernelGGL(k_cov_write<4>, gc, dim3(kCovThreads), 0, st, sh, pa, g.cov_ntile); break;
+    case 8: hipLaunchKernelGGL(k_cov_write<8>, gc, dim3(kCovThreads), 0, st, sh, pa, g.cov_ntile); break;
+    default: hipLaunchKernelGGL(k_cov_write<16>, gc, dim3(kCovThreads), 0, st, sh, pa, g.cov_ntile); break;
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ntc = (sh.C + kTxTile - 1) / kTxTile;

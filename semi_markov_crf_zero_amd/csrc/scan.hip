@@ -20,8 +20,21 @@
 namespace semicrf {
 
 // Thread (r, c) of a tile owns positions [tile*TS + r*J, +J) of label c.
+// Its J scores are loaded together, before the first use (positions past
+// the sequence read a valid position and count 0).
+template <int J>
+__device__ __forceinline__ void load_scores(const float *__restrict__ xb, int t0, int L, int C,
+                                            int c, float (&v)[J]) {
+#pragma unroll
+  for (int i = 0; i < J; ++i) {
+    const int t = t0 + i < L ? t0 + i : L - 1;
+    v[i] = xb[(size_t)t * C + c];
+  }
+}
+
+template <int J>
 __global__ __launch_bounds__(kScanThreads) void k_scan_partial(
-    const float *__restrict__ x, const int32_t *__restrict__ lengths, int T, int C, int ntile, int J,
+    const float *__restrict__ x, const int32_t *__restrict__ lengths, int T, int C, int ntile,
     double *__restrict__ tile_sum) {
   __shared__ double red[kScanThreads];
   const int tile = blockIdx.x, b = blockIdx.y;
@@ -30,13 +43,12 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_partial(
   const int L = lengths[b];
   const bool valid_len = L >= 1 && L <= T;
   double s = 0.0;
-  if (r < R && valid_len) {
-    const int t0 = tile * TS + r * J;
-    const float *xb = x + (size_t)b * T * C;
-    for (int i = 0; i < J; ++i) {
-      const int t = t0 + i;
-      if (t < L) s += (double)xb[(size_t)t * C + c];
-    }
+  const int t0 = tile * TS + r * J;
+  if (r < R && valid_len && t0 < L) {
+    float v[J];
+    load_scores<J>(x + (size_t)b * T * C, t0, L, C, c, v);
+#pragma unroll
+    for (int i = 0; i < J; ++i) s += t0 + i < L ? (double)v[i] : 0.0;
   }
   red[tid] = s;
   __syncthreads();
@@ -103,8 +115,9 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_anchor(
 // S is also written split for the exp-space recursion of the sweeps
 // (exp_split: exp(+-S) as a float64 in [2^-1/2, 2^1/2] times 2^(+-n)) when
 // ep is given.
+template <int J>
 __global__ __launch_bounds__(kScanThreads) void k_scan_write(
-    const float *__restrict__ x, const int32_t *__restrict__ lengths, int T, int C, int ntile, int J,
+    const float *__restrict__ x, const int32_t *__restrict__ lengths, int T, int C, int ntile,
     const double *__restrict__ anchor, const double *__restrict__ nu, double *__restrict__ S,
     double *__restrict__ ep, double *__restrict__ em, int32_t *__restrict__ en) {
   __shared__ double red[kScanThreads];
@@ -113,17 +126,21 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_write(
   const int tid = threadIdx.x, c = tid % C, r = tid / C;
   const int L = lengths[b];
   const bool valid_len = L >= 1 && L <= T;
-  const float *xb = x + (size_t)b * T * C;
   const size_t ob = (size_t)b * (T + 1) * C;
   const double n = valid_len ? nu[(size_t)b * C + c] : 0.0;
   const int t0 = tile * TS + r * J;
-  double local = 0.0;
-  if (r < R && valid_len) {
-    for (int i = 0; i < J; ++i) {
-      const int t = t0 + i;
-      if (t < L) local += (double)xb[(size_t)t * C + c] - n;
-    }
+  double xs[J];  // x - nu of the thread's positions, 0 past the sequence
+#pragma unroll
+  for (int i = 0; i < J; ++i) xs[i] = 0.0;
+  if (r < R && valid_len && t0 < L) {
+    float v[J];
+    load_scores<J>(x + (size_t)b * T * C, t0, L, C, c, v);
+#pragma unroll
+    for (int i = 0; i < J; ++i) xs[i] = t0 + i < L ? (double)v[i] - n : 0.0;
   }
+  double local = 0.0;
+#pragma unroll
+  for (int i = 0; i < J; ++i) local += xs[i];
   red[tid] = local;
   __syncthreads();
   if (r >= R) return;
@@ -143,11 +160,13 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_write(
     }
   };
   if (tile == 0 && r == 0) put(0, valid_len ? 0.0 : run);
+#pragma unroll
   for (int i = 0; i < J; ++i) {
     const int t = t0 + i;
-    if (t >= T) break;
-    if (t < L) run += (double)xb[(size_t)t * C + c] - n;
-    put(t + 1, run);
+    if (t < T) {
+      run += xs[i];
+      put(t + 1, run);
+    }
   }
 }
 
@@ -155,16 +174,23 @@ hipError_t launch_scan(const float *x, const int32_t *lengths, int B, int T, int
                        double *nu, double *S, double *ep, double *em, int32_t *en,
                        double *tile_sum, double *anchor, int ntile, int J, hipStream_t st) {
   dim3 grid(ntile, B);
-  hipLaunchKernelGGL(k_scan_partial, grid, dim3(kScanThreads), 0, st, x, lengths, T, C, ntile,
-                     J, tile_sum);
+  switch (J) {
+    case 8: hipLaunchKernelGGL(k_scan_partial<8>, grid, dim3(kScanThreads), 0, st, x, lengths, T, C, ntile, tile_sum); break;
+    case 16: hipLaunchKernelGGL(k_scan_partial<16>, grid, dim3(kScanThreads), 0, st, x, lengths, T, C, ntile, tile_sum); break;
+    case 32: hipLaunchKernelGGL(k_scan_partial<32>, grid, dim3(kScanThreads), 0, st, x, lengths, T, C, ntile, tile_sum); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan_anchor, dim3(B, C), dim3(kScanThreads), 0, st, lengths, T, C, ntile,
                      J, center, tile_sum, anchor, nu);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scan_write, grid, dim3(kScanThreads), 0, st, x, lengths, T, C, ntile,
-                     J, anchor, nu, S, ep, em, en);
+  switch (J) {
+    case 8: hipLaunchKernelGGL(k_scan_write<8>, grid, dim3(kScanThreads), 0, st, x, lengths, T, C, ntile, anchor, nu, S, ep, em, en); break;
+    case 16: hipLaunchKernelGGL(k_scan_write<16>, grid, dim3(kScanThreads), 0, st, x, lengths, T, C, ntile, anchor, nu, S, ep, em, en); break;
+    default: hipLaunchKernelGGL(k_scan_write<32>, grid, dim3(kScanThreads), 0, st, x, lengths, T, C, ntile, anchor, nu, S, ep, em, en); break;
+  }
   return hipGetLastError();
 }
 
