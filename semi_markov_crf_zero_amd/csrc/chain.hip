@@ -160,13 +160,14 @@ __device__ __forceinline__ int slot_of(int tm, int k, int K, bool fwd) {
   return s;
 }
 
-// K-sum over the thread's durations: sum_k D[k] * ring[slot(t,k)].  With
-// WITH_GD (backward marginal pass) also accumulates the segment posteriors
+// K-sum over the thread's durations: sum_k D[k] * ring[slot(t,k)], its
+// first term (duration age0) returned apart in `first`.  With WITH_GD
+// (backward marginal pass) also accumulates the segment posteriors
 // gd[j] += q * D[k] * ring[slot].
 template <bool WITH_GD, int AMAX, int TRMAX, typename DT, typename GT>
 __device__ __forceinline__ double ksum(const Regs<AMAX, TRMAX, DT> &r, const Smem &sm,
                                        const ChainShape &sh, int t, bool fwd, GT (&gd)[AMAX],
-                                       double q) {
+                                       double q, double &first) {
   // The ring offset of duration age0 + j moves by one row per duration
   // (wrapping once), so no multiply per term; past the thread's durations
   // the weight is 0 and the offset merely stays inside the ring.  Reads go
@@ -196,7 +197,10 @@ __device__ __forceinline__ double ksum(const Regs<AMAX, TRMAX, DT> &r, const Sme
 #pragma unroll
     for (int u = 0; u < 8 && jb + u < AMAX; ++u) {
       const double w = (double)r.D[jb + u] * v[u];
-      s[u & 3] += w;
+      if (jb + u == 0)
+        first = w;
+      else
+        s[u & 3] += w;
       if (WITH_GD) gd[jb + u] += (GT)(q * w);
     }
   }
@@ -298,26 +302,33 @@ __device__ __forceinline__ double contract(const Regs<AMAX, TRMAX, DT> &r, const
 // Row thread c inserts the entry for position t, y * 2^s relative to its
 // reference 2^R (y > 0, s an exact integer), and decides an exact
 // power-of-two rebase of its column: an entry outside
-// [2^-kRebaseExp, 2^kRebaseExp] moves R by its exponent.  Returns true if
-// the column must be rescaled by 2^-n (n in sm.shiftn[c]).  The bound
+// [2^-kRebaseExp, 2^kRebaseExp] moves R by its exponent.  Returns that
+// shift n (0: none); the column's older slots must be rescaled by 2^-n (n
+// also in sm.shiftn[c]).  The bound
 // leaves headroom for the K-sum, at most 2^kRebaseExp * K * max exp(dur),
 // below float64's 2^1023 for K <= 16384 and dur below ~270 nats; older
 // entries that fall below the float64 range are smaller than the newest by
 // more than 2^kRebaseExp and weigh nothing.
-__device__ __forceinline__ bool insert_entry(const Smem &sm, const ChainShape &sh, int t,
-                                             double y, int s, int &R) {
+__device__ __forceinline__ int insert_entry(const Smem &sm, const ChainShape &sh, int t,
+                                            double y, int s, int &R) {
   const int c = threadIdx.x;
   const int ey = exponent_of(y) + s;
   const int n = (ey > kRebaseExp || ey < -kRebaseExp) ? ey : 0;
   R += n;
   sm.shiftn[c] = n;
   sm.ring[(t % sh.K) * sh.C + c] = ldexp(y, s - n);
-  return n != 0;
+  return n;
+}
+
+// Rebase votes of two consecutive steps (by step parity), in the scalar area.
+__device__ __forceinline__ int *vote_of(const Smem &sm) {
+  return reinterpret_cast<int *>(sm.scal) + 8;
 }
 
 // Apply pending column rescales: every ring slot except the newest (position
 // t) is multiplied by 2^-shiftn[c].  Slots are owned through the durations
-// of the next step, so each is touched by exactly one thread.
+// of the next step, so each is touched by exactly one thread; no barrier
+// here (the caller orders the rescale against the slots' other readers).
 template <int AMAX, int TRMAX, typename DT>
 __device__ __forceinline__ void apply_rebase(const Regs<AMAX, TRMAX, DT> &r, const Smem &sm,
                                              const ChainShape &sh, int t, bool fwd) {
@@ -350,7 +361,6 @@ __device__ __forceinline__ void apply_rebase(const Regs<AMAX, TRMAX, DT> &r, con
       }
     }
   }
-  __syncthreads();
 }
 
 
@@ -473,6 +483,13 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
   const int tstart = tb;
   double o_rec = 0.0, m_rec = 0.0;
   int Bm = -(1 << 29);  // step scale of the rows; the first step computes it
+  // A rebase decided at one step reaches the ring's older slots during the
+  // next one, after its first barrier (uniform `lazy`, the vote of the step
+  // before); that step's K-sum still reads them in the old reference, so
+  // the row thread scales all but the newest term by 2^-npend, its label's
+  // shift.  The steps that store a record apply their rebases at once.
+  int npend = 0;
+  bool lazy = false;
   PfLoad ld;
   for (int step = 1; step <= nsteps; ++step) {
     const int t = tb + isig * step;
@@ -480,25 +497,28 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
     const int buf = pf > 0 ? ((step - 1) / pf) & 1 : 0;
     double fx = 0.0, fy = 0.0;
     int nq = 0;
-    if (ROLE == kRowRole && is_row) {
-      if (pf > 0) {
-        const int o = (buf * pf + i) * C + tid;
-        fx = sm.efx[o];
-        fy = sm.efy[o];
-        nq = isig * sm.en[o];
-      } else {
-        int n;
-        es_get(es, ob, t, sh.T, C, tid, fwd, fx, fy, n);
-        nq = isig * n;
-      }
+    if (ROLE == kRowRole && is_row && pf == 0) {  // (prefetched scores: after the first barrier)
+      int n;
+      es_get(es, ob, t, sh.T, C, tid, fwd, fx, fy, n);
+      nq = isig * n;
     }
     const bool next_blk = pf > 0 && step - 1 - i + pf < nsteps;  // a block follows this one
     if (ROLE == kLoadRole && i == 0 && next_blk)
       ld.issue(es, ob, sh, tstart, isig, step + pf, lid, fwd);
     double nogd[AMAX];
-    const double s = r.kp < sh.P ? ksum<false>(r, sm, sh, t, fwd, nogd, 0.0) : 0.0;
-    if (r.kp < sh.P) sm.part[r.kp * C + r.kc] = s;
+    double first = 0.0;  // the thread's first term (the row threads': duration 1, the newest entry)
+    const double s = r.kp < sh.P ? ksum<false>(r, sm, sh, t, fwd, nogd, 0.0, first) : 0.0;
+    if (r.kp < sh.P) sm.part[r.kp * C + r.kc] = r.kp == 0 ? s : s + first;
     __syncthreads();
+    // the previous step's rebases (every thread rescales the slots it has
+    // just read; the next readers are past the barriers below)
+    if (lazy && vote_of(sm)[(step - 1) & 1]) apply_rebase(r, sm, sh, t - isig, fwd);
+    if (ROLE == kRowRole && is_row && pf > 0) {
+      const int o = (buf * pf + i) * C + tid;
+      fx = sm.efx[o];
+      fy = sm.efy[o];
+      nq = isig * sm.en[o];
+    }
     const bool last = step == nsteps;
     const bool lz_step = last && tail;
     const double *sprev = sm.stg + ((step - 1) & 1) * (3 * C + 1);
@@ -507,7 +527,7 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
     double x = 0.0;
     int E = 0;
     if (ROLE == kRowRole && is_row) {
-      x = sum_strided(sm.part + tid, sh.P, C) * fx;
+      x = (ldexp(sum_strided(sm.part + tid, sh.P, C), -npend) + first) * fx;
       E = R + nq;
     }
     const bool prev_rows = rows && step - 1 > wb;  // the previous step is past the burn-in
@@ -543,15 +563,14 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
     const double d = contract(r, sm, sh, trw);  // exp(m) / 2^Bm, m = u or beta
     if (ROLE == kWriteRole && prev_rows)
       stage_rows(sprev, C, row1 + tprev, row2 + tprev, C, 2 * C, wfirst, wn);
-    int *vote = reinterpret_cast<int *>(sm.scal) + 8;  // rebase votes of two steps
-    bool need = false;
+    int *vote = vote_of(sm);  // rebase votes of two steps
     if (ROLE == kRowRole && is_row) {
       if (tid == 0) vote[(step + 1) & 1] = 0;  // every thread has read it (last step)
       stg[2 * C + tid] = d;
       if (tid == 0) stg[3 * C] = (double)Bm;
       // entry exp(m -+ S) / 2^R = d * fy * 2^(Bm -+ n - R)
-      need = insert_entry(sm, sh, t, d * fy, Bm - nq - R, R);
-      if (need) vote[step & 1] = 1;
+      npend = insert_entry(sm, sh, t, d * fy, Bm - nq - R, R);
+      if (npend != 0) vote[step & 1] = 1;
       if (last || step == wb) {
         const double o = log(x) + (double)E * kLn2, m = log(d) + (double)Bm * kLn2;
         if (last) {
@@ -566,9 +585,18 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
     // the next block's scores land in the other buffer before the barrier
     // that ends this block
     if (ROLE == kLoadRole && i == pf - 1 && next_blk) ld.put(sm, sh, buf ^ 1, lid);
-    __syncthreads();
-    if (vote[step & 1]) apply_rebase(r, sm, sh, t, fwd);
-    if (step == wb) save_ckpt(rec_start, sm, sh, R, o_rec, m_rec);  // the burn-in ends
+    if (last || step == wb) {  // a record follows: the ring made whole now
+      __syncthreads();
+      if (vote[step & 1]) {
+        apply_rebase(r, sm, sh, t, fwd);
+        __syncthreads();
+      }
+      npend = 0;
+      lazy = false;
+      if (step == wb) save_ckpt(rec_start, sm, sh, R, o_rec, m_rec);  // the burn-in ends
+    } else {
+      lazy = true;
+    }
   }
 }
 
