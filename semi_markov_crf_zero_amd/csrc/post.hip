@@ -124,9 +124,10 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_anchor(ChainShape sh, PostA
   red[tid] = own;
   red2[tid] = own2;
   __syncthreads();
+  const int nq = min(kCovThreads, (ntile + per - 1) / per);  // threads that own tiles
   if (tid == 0) {
     double run = 0.0, tot2 = 0.0;
-    for (int q = 0; q < kCovThreads; ++q) {
+    for (int q = 0; q < nq; ++q) {
       const double v = red[q];
       red[q] = run;
       run += v;
@@ -443,12 +444,20 @@ __global__ __launch_bounds__(kRedOut * kRedSlices) void k_post_reduce(ChainShape
     const double *src = tx ? pa.tx_part + e : pa.dur_part + (e - nx);
     const size_t stride = tx ? (size_t)nx : (size_t)ng;
     const long long q1 = min(n, (p + 1) * per);
-    for (long long q = p * per; q < q1; ++q) {
-      const int b = (int)(q / np), j = (int)(q % np);
-      const int L = pa.lengths[b];
-      const double w = pa.grad_logz ? (double)pa.grad_logz[b] : 1.0;
-      const double v = src[((size_t)b * np + j) * stride];
-      acc += valid_len(sh, L) ? w * v : 0.0;
+    for (long long q0 = p * per; q0 < q1; q0 += 4) {  // 4 partials' loads at a time
+      double v[4], w[4];
+      int L[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const long long q = q0 + u < q1 ? q0 + u : q1 - 1;  // clamped: a valid partial
+        const int b = (int)(q / np), j = (int)(q % np);
+        L[u] = pa.lengths[b];
+        w[u] = pa.grad_logz ? (double)pa.grad_logz[b] : 1.0;
+        v[u] = src[((size_t)b * np + j) * stride];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (q0 + u < q1) acc += valid_len(sh, L[u]) ? w[u] * v[u] : 0.0;
     }
   }
   red[p][o] = acc;

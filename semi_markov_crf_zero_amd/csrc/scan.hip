@@ -76,9 +76,11 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_anchor(
   for (int i = i0; i < i1; ++i) own += ts[(size_t)i * C];
   red[tid] = own;
   __syncthreads();
+  // threads past nq own no tile (ranges of `per` tiles from the start)
+  const int nq = min(kScanThreads, (ntile + per - 1) / per);
   if (tid == 0) {
     double total = 0.0;
-    for (int q = 0; q < kScanThreads; ++q) total += red[q];
+    for (int q = 0; q < nq; ++q) total += red[q];
     red[0] = total;
   }
   __syncthreads();
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_anchor(
   __syncthreads();
   if (tid == 0) {  // exclusive prefix over the threads, in order
     double run = 0.0;
-    for (int q = 0; q < kScanThreads; ++q) {
+    for (int q = 0; q < nq; ++q) {
       const double v = red[q];
       red[q] = run;
       run += v;
