@@ -610,6 +610,16 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
   const bool fwd = (int)blockIdx.x < nck;
   const int rem = fwd ? blockIdx.x : blockIdx.x - nck;
   const int b = rem / sh.nchunk, jc = rem % sh.nchunk;
+  const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + jc;
+  if (iter == 0) {  // the parallel-in-time state, before any verification reads it
+    if (threadIdx.x == 0) {
+      pb.redo[idx] = 1;
+      pb.corr_i[idx] = 0;
+      pb.corr_f[idx] = 0.0;
+    }
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i < sh.nchunk; i += NT) pb.nbad[i] = 0;
+  }
   const int L = lengths[b];
   const int tid = threadIdx.x, C = sh.C, K = sh.K;
   const bool is_row = tid < C;
@@ -617,7 +627,6 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
   const int p0 = jc * sh.delta;
   if (p0 >= L) return;
   const int p1 = min(p0 + sh.delta, L);
-  const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + jc;
   if (iter > 0 && (pb.nbad[iter - 1] == 0 || pb.redo[idx] == 0)) return;
   Smem sm = carve(lds, sh);
   for (int i = tid; i < kErowPad; i += NT) sm.erow[sh.C + i] = 0.0;

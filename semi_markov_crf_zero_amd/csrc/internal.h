@@ -239,7 +239,6 @@ hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur
 // exp(trans) for the weight-streaming instances (chain.hip).
 hipError_t launch_trw(int C, int CS, int QT, const float *trans, float *trw, hipStream_t st);
 
-hipError_t launch_pit_init(const ChainShape &sh, const PitBufs &pb, int niter, hipStream_t st);
 hipError_t launch_pit_verify(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
                              int iter, int with_bwd, hipStream_t st);
 hipError_t launch_pit_fixup(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,

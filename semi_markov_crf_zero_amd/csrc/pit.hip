@@ -48,17 +48,6 @@ __device__ __forceinline__ MaxArg max_arg(MaxArg a, MaxArg b) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kPitThreads) void k_pit_init(ChainShape sh, PitBufs pb, int niter) {
-  const int n = 2 * sh.B * sh.nchunk;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
-    pb.redo[i] = 1;
-    pb.corr_i[i] = 0;
-    pb.corr_f[i] = 0.0;
-  }
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < niter; i += gridDim.x * blockDim.x)
-    pb.nbad[i] = 0;
-}
-
 // One workgroup per (direction, sequence, chunk).  Forward chunk j >= 1
 // compares its start (state at p0_j) with the end of forward chunk j-1;
 // backward chunk j compares its start (state at p1_j) with the end of
@@ -275,9 +264,10 @@ hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur
                       const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                       double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
                       hipStream_t st) {
+  // iteration 0 of the sweep also sets every chunk's redo flag and scalar
+  // and clears the per-iteration mismatch counts
   const int niter = sh.nchunk;
-  hipError_t e = launch_pit_init(sh, pb, niter, st);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   if (pb.trw) {
     e = launch_trw(sh.C, sh.CS, sh.QT, trans, pb.trw, st);
     if (e != hipSuccess) return e;
@@ -333,14 +323,6 @@ hipError_t launch_pit_rows(const ChainShape &sh, const int32_t *lengths, const P
   gx = gx < 1 ? 1 : (gx > 64 ? 64 : gx);
   hipLaunchKernelGGL(k_pit_rows, dim3(gx, 2 * sh.B * sh.nchunk), dim3(kPitThreads), 0, st, sh,
                      lengths, pb);
-  return hipGetLastError();
-}
-
-hipError_t launch_pit_init(const ChainShape &sh, const PitBufs &pb, int niter, hipStream_t st) {
-  const int n = 2 * sh.B * sh.nchunk;
-  const int grid = (n + kPitThreads - 1) / kPitThreads;
-  hipLaunchKernelGGL(k_pit_init, dim3(grid > 0 ? grid : 1), dim3(kPitThreads), 0, st, sh, pb,
-                     niter);
   return hipGetLastError();
 }
 
