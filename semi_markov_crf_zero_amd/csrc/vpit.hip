@@ -762,8 +762,11 @@ bool vit_config(int B, int T, int C, int K, VShape &vs) {
   int ng = 64;
   while (ng > 4 && ng * C > 1024) ng >>= 1;
   if (ng * C > 1024) return false;
+  // half the group width (512 threads, half the waves at every barrier)
+  // when a lane then still holds at most 16 durations and 4 previous labels
+  if (ng * C > 512 && ng > 4 && (K + ng / 2 - 1) / (ng / 2) <= 16 && C <= 4 * (ng / 2)) ng >>= 1;
   vs.NG = ng;
-  vs.NT = ng * C <= 256 ? 256 : 1024;
+  vs.NT = ng * C <= 256 ? 256 : (ng * C <= 512 && C <= 4 * ng ? 512 : 1024);
   vs.A = (K + ng - 1) / ng;
   vs.CA = (C + ng - 1) / ng;
   if (vs.A > 16 || vs.CA > 64) return false;
@@ -797,6 +800,9 @@ hipError_t launch_vit_pit(const VShape &vs, const float *trans, const float *dur
   if (vs.NT == 256)  // C <= 4: one previous label per lane
     e = a4 ? vsweeps<256, 4, 4, 0>(vs, trans, dur, S, lengths, vb, st)
            : vsweeps<256, 16, 4, 0>(vs, trans, dur, S, lengths, vb, st);
+  else if (vs.NT == 512)  // at most 4 previous labels per lane
+    e = a4 ? vsweeps<512, 4, 4, 0>(vs, trans, dur, S, lengths, vb, st)
+           : vsweeps<512, 16, 4, 0>(vs, trans, dur, S, lengths, vb, st);
   else if (vs.CA <= 4)
     e = a4 ? vsweeps<1024, 4, 4, 0>(vs, trans, dur, S, lengths, vb, st)
            : vsweeps<1024, 16, 4, 0>(vs, trans, dur, S, lengths, vb, st);
