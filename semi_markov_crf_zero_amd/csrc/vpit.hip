@@ -762,9 +762,9 @@ bool vit_config(int B, int T, int C, int K, VShape &vs) {
   int ng = 64;
   while (ng > 4 && ng * C > 1024) ng >>= 1;
   if (ng * C > 1024) return false;
-  // half the group width (512 threads, half the waves at every barrier)
-  // when a lane then still holds at most 16 durations and 4 previous labels
-  if (ng * C > 512 && ng > 4 && (K + ng / 2 - 1) / (ng / 2) <= 16 && C <= 4 * (ng / 2)) ng >>= 1;
+  // narrower groups (fewer threads, fewer waves at every barrier) while a
+  // lane then still holds at most 16 durations and 4 previous labels
+  while (ng * C > 256 && ng > 4 && (K + ng / 2 - 1) / (ng / 2) <= 16 && C <= 4 * (ng / 2)) ng >>= 1;
   vs.NG = ng;
   vs.NT = ng * C <= 256 ? 256 : (ng * C <= 512 && C <= 4 * ng ? 512 : 1024);
   vs.A = (K + ng - 1) / ng;
