@@ -19,16 +19,16 @@ constexpr double kLn2 = 0.69314718055994530942;
 constexpr double kLn2Lo = 2.3190468138462996e-17;  // ln 2 minus its float64 rounding
 
 // exp(y) for float64 y: 2^floor(y*log2e) * 2^frac.  NaN propagates; 0
-// below the float64 range, +inf above it.
+// below the float64 range, +inf above it (the exponent is clamped to
+// [-1100, 1100] and ldexp saturates).  No branch: selects only.
 __device__ __forceinline__ double exp_wide(double y) {
   const double z = y * kLog2e;
-  if (z != z) return z;
-  if (z <= -1075.0) return 0.0;
-  if (z >= 1024.0) return __builtin_huge_val();
-  const double n = floor(z);
-  const float f = static_cast<float>(z - n);  // in [0, 1]
-  const float m = __builtin_amdgcn_exp2f(f);  // 2^f in [1, 2]
-  return ldexp(static_cast<double>(m), static_cast<int>(n));
+  const double zc = fmin(fmax(z, -1100.0), 1100.0);  // (a NaN z becomes -1100 here)
+  const double n = floor(zc);
+  const float f = static_cast<float>(zc - n);  // in [0, 1]
+  const float m = __builtin_amdgcn_exp2f(f);   // 2^f in [1, 2]
+  const double r = ldexp(static_cast<double>(m), static_cast<int>(n));
+  return z != z ? z : r;
 }
 
 // log(x) for float64 x >= 0: exponent exactly, mantissa via v_log_f32.

@@ -198,7 +198,6 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
                                                         int nseg) {
   __shared__ double ta[kTxRows][kTxTile];
   __shared__ double tg[kTxRows][kTxTile];
-  __shared__ double tm[kTxRows];
   const int ntc = (sh.C + kTxTile - 1) / kTxTile;
   const int ti = blockIdx.x / ntc, tj = blockIdx.x % ntc;  // rows c' / columns c
   const int b = blockIdx.y / nseg, seg = blockIdx.y % nseg;
@@ -215,28 +214,32 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
   if (!valid_len(sh, L)) tend = tbeg;
   if (tend > L) tend = L;  // transitions at 1 <= t < L
   const double logZ = valid_len(sh, L) ? pa.logz[b] : 0.0;
+  // staging: wave w holds rows 4u + w of the batch (u < kTxPer), lane =
+  // column, so each row's maximum is a wave reduction; every load of a batch
+  // is issued before the first use (indices clamped, invalid entries masked)
+  constexpr int kTxPer = kTxRows * kTxTile / kTxThreads;
+  static_assert(kTxTile == 64 && kTxThreads == 256, "a staged row is one wave, four waves");
+  const int lane = tid & 63, w = tid >> 6;
+  const int ca = min(ci0 + lane, C - 1), cg = min(cj0 + lane, C - 1);
   for (int r0 = tbeg; r0 < tend; r0 += kTxRows) {
     const int nr = min(kTxRows, tend - r0);
-    __syncthreads();
-    for (int i = tid; i < kTxRows * kTxTile; i += kTxThreads) {
-      const int rr = i / kTxTile, cc = i % kTxTile;
-      const bool in = rr < nr && ci0 + cc < C;
-      ta[rr][cc] = in ? pa.row_a[rix(sh, b, r0 + rr) + ci0 + cc] : -__builtin_huge_val();
+    double va[kTxPer], vg[kTxPer];
+#pragma unroll
+    for (int u = 0; u < kTxPer; ++u) {
+      const int rr = 4 * u + w;
+      const size_t ri = rix(sh, b, r0 + min(rr, nr - 1));
+      va[u] = pa.row_a[ri + ca];
+      vg[u] = pa.row_v[ri + cg];
     }
-    __syncthreads();
-    if (tid < kTxRows) {
-      double m = -__builtin_huge_val();
-      for (int cc = 0; cc < kTxTile; ++cc) m = fmax(m, ta[tid][cc]);
-      tm[tid] = m;
-    }
-    __syncthreads();
-    for (int i = tid; i < kTxRows * kTxTile; i += kTxThreads) {
-      const int rr = i / kTxTile, cc = i % kTxTile;
-      const bool ina = rr < nr && ci0 + cc < C;
-      const bool ing = rr < nr && cj0 + cc < C;
-      const double m = tm[rr];
-      ta[rr][cc] = ina ? exp_wide(ta[rr][cc] - m) : 0.0;
-      tg[rr][cc] = ing ? exp_wide(pa.row_v[rix(sh, b, r0 + rr) + cj0 + cc] + m - logZ) : 0.0;
+    __syncthreads();  // the previous batch's products are done with ta / tg
+#pragma unroll
+    for (int u = 0; u < kTxPer; ++u) {
+      const int rr = 4 * u + w;
+      const bool ina = rr < nr && ci0 + lane < C;
+      const bool ing = rr < nr && cj0 + lane < C;
+      const double m = group_max(ina ? va[u] : -__builtin_huge_val(), 64);
+      ta[rr][lane] = ina ? exp_wide(va[u] - m) : 0.0;
+      tg[rr][lane] = ing ? exp_wide(vg[u] + m - logZ) : 0.0;
     }
     __syncthreads();
     for (int rr = 0; rr < nr; ++rr) {
