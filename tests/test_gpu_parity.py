@@ -163,6 +163,16 @@ def test_large_emission_scales(sigma):
     assert_viterbi_equal(gpu_viterbi(inp), oracle.viterbi(inp), label=sigma)
 
 
+@pytest.mark.parametrize("sigma", [10.0, 100.0])
+def test_large_emission_scales_lds_ring(sigma):
+    """C = 48 runs the LDS-ring engine: frequent rebases, applied a step
+    late (and at once on the steps that store a checkpoint record)."""
+    inp = _case(2, 400, 48, 30, [400, 263], seed=17, sigma=sigma, tsd=1.0, dsd=1.0)
+    o = oracle.fwd_bwd(inp)
+    assert_fwd_bwd_close(gpu_fwd_bwd(inp), o, label=sigma)
+    assert_fwd_bwd_close(gpu_fwd_bwd(inp, ckpt=64), o, label=(sigma, 64))
+
+
 def test_deterministic_bitwise():
     inp = _case(3, 500, 16, 40, [500, 300, 77], seed=17)
     a = gpu_fwd_bwd(inp)
@@ -199,6 +209,22 @@ def test_cumulative_scores(C, T):
 def test_viterbi_shapes(shape):
     B, T, C, K, lengths = shape
     inp = _case(B, T, C, K, lengths, seed=2 * T + C, tsd=0.3, dsd=0.3)
+    assert_viterbi_equal(gpu_viterbi(inp), oracle.viterbi(inp), label=shape[:4])
+
+
+# Shapes whose label groups stop narrowing at 512 threads (a lane would
+# otherwise hold more than 16 durations): the 512-thread decoder instances.
+VIT_512_SHAPES = [
+    (2, 700, 16, 300, [700, 433]),       # 32-lane groups, 10 durations per lane
+    (2, 900, 8, 600, [900, 610]),        # 64-lane groups, 10 durations per lane
+    (2, 500, 20, 200, [500, 321]),       # 16-lane groups, 13 durations, 2 labels per lane
+]
+
+
+@pytest.mark.parametrize("shape", VIT_512_SHAPES, ids=lambda s: "B%dT%dC%dK%d" % s[:4])
+def test_viterbi_512_thread_groups(shape):
+    B, T, C, K, lengths = shape
+    inp = _case(B, T, C, K, lengths, seed=3 * T + C, tsd=0.3, dsd=0.3)
     assert_viterbi_equal(gpu_viterbi(inp), oracle.viterbi(inp), label=shape[:4])
 
 
