@@ -185,6 +185,7 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
       lay.row_u = cv.take(nS * 8);
       lay.row_v = cv.take(nS * 8);
       lay.row_b = cv.take(nS * 8);
+      lay.pos_shift = cv.take((size_t)2 * B * (T + 1) * 8);
       PostGeom g;
       post_geometry(*sh, g);
       lay.cov_part = cv.take((size_t)B * g.cov_ntile * C * 8);
@@ -284,6 +285,7 @@ PitBufs pit_bufs(void *ws, const Layout &lay, bool bwd) {
   pb.row_u = bwd ? at<double>(ws, lay.row_u) : nullptr;
   pb.row_v = bwd ? at<double>(ws, lay.row_v) : nullptr;
   pb.row_b = bwd ? at<double>(ws, lay.row_b) : nullptr;
+  pb.pos_shift = bwd ? at<double>(ws, lay.pos_shift) : nullptr;
   pb.trw = lay.trw ? at<float>(ws, lay.trw) : nullptr;
   return pb;
 }
@@ -421,6 +423,7 @@ semicrf_status_t semicrf_fwd_bwd_timed(const float *emissions, const int32_t *le
   pa.row_u = at<double>(ws, lay.row_u);
   pa.row_v = at<double>(ws, lay.row_v);
   pa.row_b = at<double>(ws, lay.row_b);
+  pa.pos_shift = at<double>(ws, lay.pos_shift);
   pa.cov_part = at<double>(ws, lay.cov_part);
   pa.cov_part2 = at<double>(ws, lay.cov_part2);
   pa.cov_anchor = at<double>(ws, lay.cov_anchor);

@@ -154,7 +154,7 @@ __host__ __device__ inline size_t win_lds_bytes(int C, int K, int P) {
 // Workspace layout (byte offsets, 256-aligned).
 struct Layout {
   size_t S, es_p, es_m, es_n, nu, tile_sum, anchor, logz, logz_bwd;
-  size_t ck_fwd, ck_bwd, end_fwd, end_bwd, redo, corr_i, corr_f, nbad, lz_part, shift;
+  size_t ck_fwd, ck_bwd, end_fwd, end_bwd, redo, corr_i, corr_f, nbad, lz_part, shift, pos_shift;
   size_t row_a, row_u, row_v, row_b;
   size_t cov_part, cov_part2, cov_anchor, cov_mean, tx_part, dur_part, trw;
   size_t bp, vbest, vcbest;
@@ -171,6 +171,7 @@ struct PostArgs {
   const float *trans, *dur, *grad_logz;
   const double *S, *logz;
   const double *row_a, *row_u, *row_v, *row_b;
+  const double *pos_shift;  // [2][B][T+1]: add to forward / backward rows at t
   double *cov_part, *cov_part2, *cov_anchor, *cov_mean;  // [B][ntile][C], [B][C]
   double *tx_part;                                       // [B][tx_nseg][C][C]
   double *dur_part;                                      // [B][dur_nspan][K][C]
@@ -203,8 +204,11 @@ struct PitBufs {
   double *shift;              // [2][B][nchunk]: log correction of each chunk (fix-up)
   // Per-position rows [B][T+1][C] (float64, NULL when not wanted): forward
   // alpha (t = 1..L) and u (t = 0..L-1), backward v (t = 0..L-1) and beta
-  // (t = 1..L); written in each chunk's frame, corrected by k_pit_rows.
+  // (t = 1..L); written in each chunk's frame.  Their readers add
+  // pos_shift[0][b][t] (forward rows) and pos_shift[1][b][t] (backward rows),
+  // the correction of the chunk that wrote position t (k_pit_pos_shift).
   double *row_a, *row_u, *row_v, *row_b;
+  double *pos_shift;          // [2][B][T+1]
   // exp(trans) in float32, [2][C][C] (forward, backward orientation), for the
   // LDS-ring instances that stream their weights (1024 threads); else NULL.
   float *trw;
@@ -244,9 +248,6 @@ hipError_t launch_pit_verify(const ChainShape &sh, const int32_t *lengths, const
 hipError_t launch_pit_fixup(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
                             double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
                             hipStream_t st);
-hipError_t launch_pit_rows(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
-                           hipStream_t st);
-
 void post_geometry(const ChainShape &sh, PostGeom &g);
 
 // Coverage, emission gradients and marginals; transition and duration

@@ -260,6 +260,33 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_records(ChainShape sh,
 
 // nchunk iterations always suffice (after n of them the first n chunks of
 // every chain have exact starts); the ones after convergence return at once.
+// Each position's row correction: the log correction of the chunk that
+// wrote it (forward chunk j writes alpha and u at t in (p0, p1], t = 0
+// belonging to chunk 0; backward chunk j writes v and beta at t in
+// [p0, p1), t = L belonging to the last chunk).  pos_shift[0][b][t] and
+// pos_shift[1][b][t], t = 0..T (0 past L and for invalid lengths).  A
+// table of B*(T+1) pairs instead of a pass over the four [B][T+1][C] rows.
+__global__ __launch_bounds__(kPitThreads) void k_pit_pos_shift(ChainShape sh,
+                                                               const int32_t *__restrict__ lengths,
+                                                               PitBufs pb) {
+  const int b = blockIdx.y;
+  const int L = lengths[b];
+  const bool ok = L >= 1 && L <= sh.T;
+  const int nvalid = ok ? (L + sh.delta - 1) / sh.delta : 1;
+  const size_t nck = (size_t)sh.B * sh.nchunk;
+  const double *sf = pb.shift + (size_t)b * sh.nchunk, *sb = pb.shift + nck + (size_t)b * sh.nchunk;
+  double *of = pb.pos_shift + (size_t)b * (sh.T + 1), *ob = of + (size_t)sh.B * (sh.T + 1);
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t <= sh.T; t += gridDim.x * blockDim.x) {
+    double f = 0.0, g = 0.0;
+    if (ok && t <= L) {
+      f = sf[min(t >= 1 ? (t - 1) / sh.delta : 0, nvalid - 1)];
+      g = sb[min(t / sh.delta, nvalid - 1)];
+    }
+    of[t] = f;
+    ob[t] = g;
+  }
+}
+
 hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur,
                       const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                       double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
@@ -284,47 +311,13 @@ hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur
                      lengths, pb, with_bwd);
   e = hipGetLastError();
   if (e != hipSuccess || !pb.row_a) return e;
-  return launch_pit_rows(sh, lengths, pb, st);
-}
-
-// Add each chunk's log correction to the rows it wrote: forward chunk j
-// owns alpha and u at t in (p0, p1]; backward chunk j owns v and beta at t
-// in [p0, p1).  Grid: (direction, sequence, chunk) x row blocks.
-__global__ __launch_bounds__(kPitThreads) void k_pit_rows(ChainShape sh,
-                                                          const int32_t *__restrict__ lengths,
-                                                          PitBufs pb) {
-  const int nck = sh.B * sh.nchunk;
-  const bool fwd = (int)blockIdx.y < nck;
-  const int rem = fwd ? blockIdx.y : blockIdx.y - nck;
-  const int b = rem / sh.nchunk, j = rem % sh.nchunk;
-  const int L = lengths[b];
-  if (L < 1 || L > sh.T) return;
-  const int p0 = j * sh.delta;
-  if (p0 >= L) return;
-  const int p1 = min(p0 + sh.delta, L);
-  const double sh_j = pb.shift[(fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + j];
-  if (sh_j == 0.0) return;
-  const int C = sh.C;
-  const int t0 = fwd ? p0 + 1 : p0;  // rows [t0, t0 + p1 - p0)
-  const size_t n = (size_t)(p1 - p0) * C;
-  double *r1 = (fwd ? pb.row_a : pb.row_v) + ((size_t)b * (sh.T + 1) + t0) * C;
-  double *r2 = (fwd ? pb.row_u : pb.row_b) + ((size_t)b * (sh.T + 1) + t0) * C;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x) {
-    r1[i] += sh_j;
-    r2[i] += sh_j;
-  }
-}
-
-hipError_t launch_pit_rows(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
-                           hipStream_t st) {
-  const size_t per = (size_t)sh.delta * sh.C;
-  int gx = (int)((per + kPitThreads - 1) / kPitThreads);
-  gx = gx < 1 ? 1 : (gx > 64 ? 64 : gx);
-  hipLaunchKernelGGL(k_pit_rows, dim3(gx, 2 * sh.B * sh.nchunk), dim3(kPitThreads), 0, st, sh,
-                     lengths, pb);
+  int gx = (sh.T + 1 + kPitThreads - 1) / kPitThreads;
+  gx = gx > 64 ? 64 : gx;
+  hipLaunchKernelGGL(k_pit_pos_shift, dim3(gx, sh.B), dim3(kPitThreads), 0, st, sh, lengths, pb);
   return hipGetLastError();
 }
+
+
 
 hipError_t launch_pit_verify(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
                              int iter, int with_bwd, hipStream_t st) {

@@ -53,7 +53,9 @@ __device__ __forceinline__ bool valid_len(const ChainShape &sh, int L) { return 
 template <int J>
 __device__ __forceinline__ void cov_deltas(const PostArgs &pa, const ChainShape &sh, int b,
                                            int t0, int c, int L, double logZ, double (&d)[J]) {
-  double u[J], v[J], a[J], w[J];
+  double u[J], v[J], a[J], w[J], z[J];
+  const double *pf = pa.pos_shift + (size_t)b * (sh.T + 1);
+  const double *pg = pf + (size_t)sh.B * (sh.T + 1);
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int t = t0 + j < L ? t0 + j : L - 1;
@@ -62,12 +64,13 @@ __device__ __forceinline__ void cov_deltas(const PostArgs &pa, const ChainShape 
     v[j] = pa.row_v[i];
     a[j] = pa.row_a[i];
     w[j] = pa.row_b[i];
+    z[j] = pf[t] + pg[t] - logZ;  // the rows' chunk corrections, less log Z
   }
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int t = t0 + j;
-    double dd = exp(u[j] + v[j] - logZ);
-    if (t >= 1) dd -= exp(a[j] + w[j] - logZ);
+    double dd = exp(u[j] + v[j] + z[j]);
+    if (t >= 1) dd -= exp(a[j] + w[j] + z[j]);
     d[j] = t < L ? dd : 0.0;
   }
 }
@@ -223,13 +226,16 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
   const int ca = min(ci0 + lane, C - 1), cg = min(cj0 + lane, C - 1);
   for (int r0 = tbeg; r0 < tend; r0 += kTxRows) {
     const int nr = min(kTxRows, tend - r0);
-    double va[kTxPer], vg[kTxPer];
+    double va[kTxPer], vg[kTxPer], vz[kTxPer];
 #pragma unroll
     for (int u = 0; u < kTxPer; ++u) {
-      const int rr = 4 * u + w;
-      const size_t ri = rix(sh, b, r0 + min(rr, nr - 1));
+      const int rr = 4 * u + w, t = r0 + min(rr, nr - 1);
+      const size_t ri = rix(sh, b, t);
       va[u] = pa.row_a[ri + ca];
       vg[u] = pa.row_v[ri + cg];
+      // the rows' chunk corrections (alpha forward, v backward), less log Z
+      vz[u] = pa.pos_shift[(size_t)b * (sh.T + 1) + t] +
+              pa.pos_shift[((size_t)sh.B + b) * (sh.T + 1) + t] - logZ;
     }
     __syncthreads();  // the previous batch's products are done with ta / tg
 #pragma unroll
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
       const bool ing = rr < nr && cj0 + lane < C;
       const double m = group_max(ina ? va[u] : -__builtin_huge_val(), 64);
       ta[rr][lane] = ina ? exp_wide(va[u] - m) : 0.0;
-      tg[rr][lane] = ing ? exp_wide(vg[u] + m - logZ) : 0.0;
+      tg[rr][lane] = ing ? exp_wide(vg[u] + m + vz[u]) : 0.0;
     }
     __syncthreads();
     for (int rr = 0; rr < nr; ++rr) {
@@ -331,13 +337,16 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
       for (int i = tid; i < ns * CG; i += kDurThreads) {
         const int ss = i / CG, cc = i % CG;
         const size_t ri = rix(sh, b, s0 + ss) + c0 + cc;
-        sa[ss * 16 + cc] = pa.row_u[ri] - Sb[(size_t)(s0 + ss) * C + c0 + cc];
+        sa[ss * 16 + cc] = (pa.row_u[ri] + pa.pos_shift[(size_t)b * (sh.T + 1) + s0 + ss]) -
+                           Sb[(size_t)(s0 + ss) * C + c0 + cc];
       }
       for (int i = tid; i < ne * CG; i += kDurThreads) {
         const int ee = i / CG, cc = i % CG;
         const int e = s0 + klo + ee;
         const size_t ri = rix(sh, b, e) + c0 + cc;
-        sb[ee * 16 + cc] = (Sb[(size_t)e * C + c0 + cc] + pa.row_b[ri]) - logZ;
+        sb[ee * 16 + cc] = (Sb[(size_t)e * C + c0 + cc] +
+                            (pa.row_b[ri] + pa.pos_shift[((size_t)sh.B + b) * (sh.T + 1) + e])) -
+                           logZ;
       }
       __syncthreads();
       {  // per label: the largest a of the tile and its range
