@@ -19,8 +19,9 @@
 //     again in the next iteration;
 //   the iterations stop once one verification finds no difference.  After
 //     n iterations the first n chunks have exact starts, so nchunk
-//     iterations always suffice; every kernel of an iteration after
-//     convergence returns at once;
+//     iterations always suffice, and the last one (which can only sweep the
+//     chain's last chunk) needs no verification; every kernel of an
+//     iteration after convergence returns at once;
 //   k_pit_fixup adds the prefix sums of the recorded scalars to the
 //     checkpoint records and to log Z, which makes every record the exact
 //     state with its exact log normaliser -- the checkpoint-boundary
@@ -140,8 +141,11 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_verify(ChainShape sh,
       pb.redo[idx] = 0;
     }
   } else {
+    // the start becomes the predecessor's end exactly: scalar 0 between them
     for (size_t i = tid; i < cks; i += kPitThreads) A[i] = E[i];
     if (tid == 0) {
+      pb.corr_i[idx] = 0;
+      pb.corr_f[idx] = 0.0;
       pb.redo[idx] = 1;
       atomicAdd(&pb.nbad[iter], 1);
     }
@@ -299,9 +303,14 @@ hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur
     e = launch_trw(sh.C, sh.CS, sh.QT, trans, pb.trw, st);
     if (e != hipSuccess) return e;
   }
+  // After iteration it the first it+1 chunks of the chain are exact, so the
+  // last iteration can only sweep the chain's last chunk, which has no
+  // successor to verify: no verification follows it (a chunk whose start
+  // was replaced carries scalar 0, set with the copy).
   for (int it = 0; it < niter; ++it) {
     e = launch_sweep(sh, trans, dur, es, lengths, pb, with_bwd, it, st);
     if (e != hipSuccess) return e;
+    if (it + 1 == niter) break;
     e = launch_pit_verify(sh, lengths, pb, it, with_bwd, st);
     if (e != hipSuccess) return e;
   }
