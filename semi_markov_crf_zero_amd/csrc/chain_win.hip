@@ -101,7 +101,15 @@ __device__ __forceinline__ void ring_put(const WSmem &sm, int K, int C, int slot
 // the sequence length): dtab[(k-1)*C + c] = exp(dur[k-1][c]).
 __device__ __forceinline__ void stage_dur(const WSmem &sm, const ChainShape &sh,
                                           const float *__restrict__ dur, int NT) {
-  for (int i = threadIdx.x; i < sh.K * sh.C; i += NT) sm.dtab[i] = exp((double)dur[i]);
+  const int n = sh.K * sh.C;
+  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {  // 4 loads in flight per thread
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = dur[min(i0 + u * NT, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * NT < n) sm.dtab[i0 + u * NT] = exp((double)v[u]);
+  }
   for (int i = threadIdx.x; i < kWinDurPad * sh.C; i += NT) sm.dtab[sh.K * sh.C + i] = 0.0;
 }
 
@@ -298,7 +306,14 @@ __device__ __forceinline__ void wload(const double *__restrict__ src, const WSme
                                       const ChainShape &sh, bool chain, int lane, int &R,
                                       double &o, double &m, int NT) {
   const int n = sh.K * sh.C;
-  for (int i = threadIdx.x; i < n; i += NT) sm.ring[i] = src[i];
+  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {  // 4 loads in flight per thread
+    double v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = src[min(i0 + u * NT, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * NT < n) sm.ring[i0 + u * NT] = v[u];
+  }
   // the mirror of slots [0, kWinMirror) (those below K)
   const int nm = (sh.K < kWinMirror ? sh.K : kWinMirror) * sh.C;
   for (int i = threadIdx.x; i < nm; i += NT) sm.ring[n + i] = src[i];
@@ -565,11 +580,13 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   const int tid = threadIdx.x, C = sh.C, K = sh.K, T = sh.T;
   const int lane = tid & 63;
   const bool chain = tid < C;  // lanes of wave 0
+  // (the iteration flags are loaded with the length: one memory wait)
+  const int nbad = iter > 0 ? pb.nbad[iter - 1] : 1, redo = iter > 0 ? pb.redo[idx] : 1;
   if (L < 1 || L > T) return;
   const int p0 = jc * sh.delta;
   if (p0 >= L) return;
   const int p1 = min(p0 + sh.delta, L);
-  if (iter > 0 && (pb.nbad[iter - 1] == 0 || pb.redo[idx] == 0)) return;
+  if (nbad == 0 || redo == 0) return;
   const WSmem sm = wcarve(lds, sh, NT);
   Win win;
   win.init(sh);
