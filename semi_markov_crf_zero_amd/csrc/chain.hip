@@ -460,11 +460,13 @@ struct PfLoad {
   }
 };
 
-// The step loop of one role.  Per step: K-sum share, barrier, row phase
-// (label maximum, with a barrier when the rows span several waves),
-// barrier, contraction (a barrier when it is split), insertion, barrier
-// (with the rebase vote).  The row threads leave log Z (tail chunk) or the
-// end-state o / m in lz / o_end / m_end.
+// The step loop of one role.  Per step: K-sum share, barrier (then the
+// previous step's rebases reach the ring), row phase (label maximum, with a
+// barrier when the rows span several waves), barrier, contraction (a
+// barrier when it is split), insertion with the rebase vote; a step that
+// stores a record adds a barrier and applies its own rebase at once.  The
+// row threads leave log Z (tail chunk) or the end-state o / m in lz /
+// o_end / m_end.
 // Steps 1..nsteps run at positions tb + sigma*step; the first wb of them are
 // a burn-in (no rows), after which the state is the chunk's start record.
 template <int ROLE, int NT, int AMAX, int TRMAX, typename DT>
@@ -582,8 +584,8 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
         }
       }
     }
-    // the next block's scores land in the other buffer before the barrier
-    // that ends this block
+    // the next block's scores land in the other buffer before the next
+    // step's first barrier, after which the row threads read them
     if (ROLE == kLoadRole && i == pf - 1 && next_blk) ld.put(sm, sh, buf ^ 1, lid);
     if (last || step == wb) {  // a record follows: the ring made whole now
       __syncthreads();

@@ -13,21 +13,24 @@
 //     previous block began.  So while the chain runs block n, the helper
 //     waves 1-3 compute the far parts of block n+1 for its U steps at once:
 //     thread (g, c) owns the durations k = a0 .. a0+A-1 (a0 >= 2U) of label
-//     c, fills a register window with the entries and accumulates U sums --
-//     U*A fused multiply-adds with full instruction-level parallelism.
+//     c, fills a register window with the entries (consecutive positions,
+//     read across the ring's wrap from its mirror copy of the first slots)
+//     and accumulates U sums -- U*A fused multiply-adds with full
+//     instruction-level parallelism.
 //     Partials are reduced inside each wave (DPP) and land in the other of
 //     two LDS buffers.  One workgroup barrier per block.
 //   * the "chain wave" (wave 0, lane c = label c) runs the block's U steps
 //     alone, with wave-local synchronisation only: the near part (one fused
 //     multiply-add on the dependent chain, the rest summed a step ahead),
 //     the product with exp(+-S), the integer maximum of the float64
-//     exponents, the C x C contraction (exp(trans) in registers, the e row
-//     through LDS), the new entry straight into the ring and its rebase
-//     decision.  A rebase (R += n) rescales the register window at once and
+//     exponents, the C x C contraction (each label's sum shared by two or
+//     four lanes, exp(trans) in registers, the e row through LDS), the new
+//     entry straight into the ring and its rebase decision; the block's U
+//     steps are unrolled.  A rebase (R += n) rescales the register window at once and
 //     reaches the far parts -- computed in the reference the labels had when
 //     the previous block began -- as an exact ldexp when they are read.
 //   * at the block end, if a label rebased, all threads rescale its older
-//     ring entries (rare).
+//     ring entries (rare; label by label).
 //   * besides the far parts, wave 1 prefetches the split scores of the next
 //     block into LDS (loads issued first, stored last) and waves 2-3 turn
 //     the previous block's staged values into the per-position log rows: no
