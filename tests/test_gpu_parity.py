@@ -173,6 +173,17 @@ def test_large_emission_scales_lds_ring(sigma):
     assert_fwd_bwd_close(gpu_fwd_bwd(inp, ckpt=64), o, label=(sigma, 64))
 
 
+@pytest.mark.parametrize("C", [24, 40])
+def test_large_emissions_with_burn_in(C):
+    """Intervals of at least 8K positions start with a burn-in whose last
+    step stores the chunk's start record; with emission scale 30 labels
+    rebase often, also on that step (windowed engine at C = 24, LDS-ring at
+    C = 40)."""
+    inp = _case(2, 800, C, 12, [800, 555], seed=23, sigma=30.0, tsd=1.0, dsd=1.0)
+    o = oracle.fwd_bwd(inp)
+    assert_fwd_bwd_close(gpu_fwd_bwd(inp, ckpt=128), o, label=(C, 128))
+
+
 def test_deterministic_bitwise():
     inp = _case(3, 500, 16, 40, [500, 300, 77], seed=17)
     a = gpu_fwd_bwd(inp)
