@@ -65,7 +65,8 @@ enum {
     SEMICRF_OP_SCAN = 0,    /* semicrf_cumulative_scores */
     SEMICRF_OP_LOGZ = 1,    /* semicrf_logz_fwd */
     SEMICRF_OP_FWD_BWD = 2, /* semicrf_fwd_bwd */
-    SEMICRF_OP_VITERBI = 3  /* semicrf_viterbi */
+    SEMICRF_OP_VITERBI = 3, /* semicrf_viterbi */
+    SEMICRF_OP_PATH_SCORE = 4 /* semicrf_path_score */
 };
 
 /* flags */
@@ -114,7 +115,8 @@ semicrf_status_t semicrf_logz_fwd(const float *emissions, const int32_t *lengths
 
 /* Forward-backward (abstract: streaming forward-backward with
  * checkpoint-boundary normalisation, exact gradients; technical summary
- * 2.B-2.C).  With F = sum_b w_b log Z_b (w = grad_logz, NULL = all ones):
+ * 2.B-2.C).  With F = sum_b w_b log Z_b (w = grad_logz [B] float32,
+ * contiguous; NULL = all ones):
  *   logz [B] float32            log Z_b
  *   grad_emissions [B][T][C]    dF/dx; with centring this is the exact
  *                               derivative through nu:
@@ -134,30 +136,71 @@ semicrf_status_t semicrf_fwd_bwd(const float *emissions, const int32_t *lengths,
                                  float *grad_dur, float *marginals,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
-/* semicrf_fwd_bwd with phase timing: `phase_events` (may be NULL) points to
- * SEMICRF_FWD_BWD_PHASES + 1 hipEvent_t handles created by the caller; event
- * i is recorded on `stream` when phase i is enqueued and the last one after
- * the final phase.  Phases: 0 cumulative scores (3 kernels); 1 the
- * parallel-in-time forward and backward sweeps (one sweep launch per
- * iteration, at most one iteration per checkpoint interval, with their
- * verification, normaliser fix-up and row correction); 2 the posteriors
- * (coverage scan, transition and duration sums: 5 kernels); 3 the
- * parameter-gradient reduction (1 kernel).  Everything else is identical to
- * semicrf_fwd_bwd. */
-enum { SEMICRF_FWD_BWD_PHASES = 4 };
-semicrf_status_t semicrf_fwd_bwd_timed(const float *emissions, const int32_t *lengths,
-                                       const float *trans, const float *dur,
-                                       int B, int T, int C, int K, unsigned flags,
-                                       int checkpoint_interval, const float *grad_logz,
-                                       float *logz, float *grad_emissions, float *grad_trans,
-                                       float *grad_dur, float *marginals,
-                                       void *workspace, size_t workspace_bytes, void *stream,
-                                       void *const *phase_events);
+/* semicrf_fwd_bwd with two optional extras.
+ *   boundary [B][T] float32 or NULL: P(a segment starts at position t)
+ *     = sum_c P(a segment of label c starts at t) -- the uncertainty of the
+ *     segment boundaries (abstract: "uncertainty estimates at their
+ *     boundaries").  1 at t = 0, 0 at t >= L_b; P(a segment ends at t) is
+ *     boundary[b, t] for 0 < t < L_b.
+ *   phase_events (may be NULL): SEMICRF_FWD_BWD_PHASES + 1 hipEvent_t handles
+ *     created by the caller; event i is recorded on `stream` where phase i
+ *     begins and the last one after the final phase.  Phases: 0 cumulative
+ *     scores (3 kernels); 1 the first parallel-in-time sweep launch (every
+ *     checkpoint interval of both directions); 2 the rest of the sweeps
+ *     (verification, further iterations -- no-ops once converged --,
+ *     normaliser fix-up, record and row corrections); 3 the posteriors
+ *     (coverage scan, boundaries, transition and duration sums); 4 the
+ *     parameter-gradient reduction.
+ * Everything else is identical to semicrf_fwd_bwd. */
+enum { SEMICRF_FWD_BWD_PHASES = 5 };
+semicrf_status_t semicrf_fwd_bwd_ex(const float *emissions, const int32_t *lengths,
+                                    const float *trans, const float *dur,
+                                    int B, int T, int C, int K, unsigned flags,
+                                    int checkpoint_interval, const float *grad_logz,
+                                    float *logz, float *grad_emissions, float *grad_trans,
+                                    float *grad_dur, float *marginals, float *boundary,
+                                    void *workspace, size_t workspace_bytes, void *stream,
+                                    void *const *phase_events);
+
+/* Score of a given labelled segmentation under the same model, and its
+ * gradients: the second term of the training loss log Z - score(gold)
+ * (technical summary, section 3: training on labelled segmentations).
+ *   score_b = sum_j (S[b, s_j + k_j, c_j] - S[b, s_j, c_j] + dur[k_j - 1, c_j])
+ *           + sum_{j >= 1} trans[c_{j-1}, c_j]
+ * Segments in the Viterbi output layout: seg_start / seg_len / seg_label
+ * [B][T] int32, segment j of sequence b at index b*T + j for j < num_segs[b]
+ * (entries past num_segs[b] are not read).  A segmentation is valid when
+ * 1 <= num_segs[b] <= L_b, s_0 = 0, each segment starts where the previous
+ * one ends, 1 <= k_j <= K, 0 <= c_j < C and the last one ends at L_b; an
+ * invalid one (or a length outside [1, T]) gives score NaN, zero gradient
+ * rows, and no share of grad_trans / grad_dur.
+ * Gradients of F = sum_b w_b score_b (weights [B] or NULL = all ones), each
+ * output optional (NULL skips it):
+ *   grad_emissions [B][T][C]: w_b (1[position t has label c] - n_bc / L_b)
+ *     with centring (n_bc = positions of label c), the indicator without;
+ *     0 at t >= L_b;
+ *   grad_trans [C][C]: sum_b w_b #(consecutive segments c' -> c);
+ *   grad_dur [K][C]: sum_b w_b #(segments of length k and label c).
+ * score [B] float32 (required).  The workspace is
+ * semicrf_workspace_size(SEMICRF_OP_PATH_SCORE, ...). */
+semicrf_status_t semicrf_path_score(const float *emissions, const int32_t *lengths,
+                                    const float *trans, const float *dur,
+                                    int B, int T, int C, int K, unsigned flags,
+                                    const int32_t *seg_start, const int32_t *seg_len,
+                                    const int32_t *seg_label, const int32_t *num_segs,
+                                    const float *weights, float *score,
+                                    float *grad_emissions, float *grad_trans, float *grad_dur,
+                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* Viterbi: the same model in the (max,+) semiring.  The pages give no
  * decoder; this is the maximising segmentation of the scores above.
- * Ties: smallest duration k, then smallest previous label c'; at the end the
- * smallest final label c.
+ * Ties: segmentations that only reorder segment lengths inside a run of one
+ * label score the same in exact arithmetic, so the recursion compares in
+ * float64 with a tolerance: a candidate within 1e-11 * (|max| + 1) of the
+ * maximum at a decision ties with it (at |max| ~ 5e6 candidates up to ~5e-5
+ * apart tie).  Among tied candidates the smallest duration k wins, then the
+ * smallest previous label c'; at the end the smallest final label c among
+ * the tied final scores.
  *   best_score [B] float32; seg_start/seg_len/seg_label [B][T] int32: segment
  *   j of sequence b at index b*T + j for j < num_segs[b], in increasing
  *   start order, remaining slots -1; num_segs [B] int32. */

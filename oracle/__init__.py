@@ -10,5 +10,8 @@ Contents
   oracle.bruteforce  explicit enumeration of every segmentation (tiny inputs)
   oracle.linear_chain  an independent textbook linear-chain CRF (the K=1 case)
   oracle.closed_form   log Z for zero potentials at any length
+  oracle.path        score of a given segmentation and its gradients (the
+                     gold-path term of the training loss)
 """
 from .core import build, prefix, fwd_bwd, logz, viterbi  # noqa: F401
+from .path import path_score  # noqa: F401

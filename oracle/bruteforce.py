@@ -69,7 +69,8 @@ def brute_force(inp, center=True, grad_logz=None):
     segmentation by enumeration.  Returns a dict like oracle.fwd_bwd plus
     'viterbi' = list of (best_score, segments) per sequence, where among
     maximisers the first in enumeration order is kept; 'viterbi_ties' lists
-    every segmentation within rounding (1e-9 relative) of the maximum."""
+    every segmentation within rounding (1e-9 relative) of the maximum;
+    'boundary' [B,T] is the probability that a segment starts at t."""
     x = np.asarray(inp["emissions"], dtype=np.float64)
     lengths = np.asarray(inp["lengths"])
     trans = np.asarray(inp["trans"], dtype=np.float64)
@@ -82,6 +83,7 @@ def brute_force(inp, center=True, grad_logz=None):
     gx = np.zeros((B, T, C))
     gt = np.zeros((C, C))
     gd = np.zeros((K, C))
+    bnd = np.zeros((B, T))
     vit = []
     ties = []
     for b in range(B):
@@ -95,6 +97,7 @@ def brute_force(inp, center=True, grad_logz=None):
             prev = None
             for (s, k, c) in segs:
                 mu[b, s:s + k, c] += p
+                bnd[b, s] += p
                 gd[k - 1, c] += w[b] * p
                 if prev is not None:
                     gt[prev, c] += w[b] * p
@@ -110,7 +113,7 @@ def brute_force(inp, center=True, grad_logz=None):
         vit.append((float(best), items[idx[0]][0]))
         ties.append([items[i][0] for i in idx])
     return dict(logz=logz, marginals=mu, grad_emissions=gx, grad_trans=gt, grad_dur=gd,
-                viterbi=vit, viterbi_ties=ties)
+                boundary=bnd, viterbi=vit, viterbi_ties=ties)
 
 
 def path_score(x, L, trans, dur, segs, center=True):

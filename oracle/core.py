@@ -38,7 +38,7 @@ def _load():
         P = ctypes.c_void_p
         I = ctypes.c_int
         lib.oracle_prefix.argtypes = [I, I, I, P, P, I, P, P]
-        lib.oracle_fwd_bwd.argtypes = [I, I, I, I, P, P, P, P, I, P, P, P, P, P, P, P, I]
+        lib.oracle_fwd_bwd.argtypes = [I, I, I, I, P, P, P, P, I, P, P, P, P, P, P, P, P, I]
         lib.oracle_viterbi.argtypes = [I, I, I, I, P, P, P, P, I, P, P, P, P, P, P, I]
         for f in (lib.oracle_prefix, lib.oracle_fwd_bwd, lib.oracle_viterbi):
             f.restype = I
@@ -75,7 +75,8 @@ def prefix(inp, center=True):
 def fwd_bwd(inp, center=True, grad_logz=None, nthreads=0, want_grads=True):
     """Full forward-backward.  Returns a dict of float64 arrays:
     logz [B], logz_bwd [B], grad_emissions [B,T,C], grad_trans [C,C],
-    grad_dur [K,C], marginals [B,T,C]."""
+    grad_dur [K,C], marginals [B,T,C], boundary [B,T] (probability that a
+    segment starts at t)."""
     x, lengths, trans, dur, B, T, C, K = _inputs(inp)
     logz = np.zeros(B)
     logz_bwd = np.zeros(B)
@@ -85,16 +86,17 @@ def fwd_bwd(inp, center=True, grad_logz=None, nthreads=0, want_grads=True):
         gt = np.zeros((C, C))
         gd = np.zeros((K, C))
         mu = np.zeros((B, T, C))
+        bnd = np.zeros((B, T))
     else:
-        gx = gt = gd = mu = None
+        gx = gt = gd = mu = bnd = None
     rc = _load().oracle_fwd_bwd(B, T, C, K, _p(x), _p(lengths), _p(trans), _p(dur),
                                 int(center), _p(w), _p(logz), _p(logz_bwd), _p(gx),
-                                _p(gt), _p(gd), _p(mu), int(nthreads))
+                                _p(gt), _p(gd), _p(mu), _p(bnd), int(nthreads))
     if rc:
         raise RuntimeError("oracle_fwd_bwd failed with code %d" % rc)
     out = dict(logz=logz, logz_bwd=logz_bwd)
     if want_grads:
-        out.update(grad_emissions=gx, grad_trans=gt, grad_dur=gd, marginals=mu)
+        out.update(grad_emissions=gx, grad_trans=gt, grad_dur=gd, marginals=mu, boundary=bnd)
     return out
 
 
@@ -104,7 +106,7 @@ def logz(inp, center=True, nthreads=0):
     out = np.zeros(B)
     rc = _load().oracle_fwd_bwd(B, T, C, K, _p(x), _p(lengths), _p(trans), _p(dur),
                                 int(center), None, _p(out), None, None, None, None, None,
-                                int(nthreads))
+                                None, int(nthreads))
     if rc:
         raise RuntimeError("oracle_fwd_bwd failed with code %d" % rc)
     return out

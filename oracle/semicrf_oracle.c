@@ -47,6 +47,9 @@
  *   P(transition c'->c at boundary t) = exp(alpha[t,c'] + trans[c',c] + v[t,c] - log Z)
  *   coverage mu[i,c] = sum of P(segment) over the segments of label c that
  *                      contain position i (accumulated with a difference array)
+ *   boundary   P(a segment starts at s) = sum over every segment (s, k, c)
+ *              that starts at s of P(segment)  (the boundary uncertainty of
+ *              the abstract)
  * and the gradients of F = sum_b w_b log Z_b are
  *   dF/d dur[k-1,c]    = sum_b w_b sum_s P(s,k,c)
  *   dF/d trans[c',c]   = sum_b w_b sum_t P(t,c'->c)
@@ -261,10 +264,11 @@ static void posteriors_one(int T, int L, int C, int K, int center, double w, dou
                            const double *alpha, const double *u, const double *v,
                            const double *beta, const double *zf, const double *zb,
                            double *gtrans, double *gdur, double *mu_out, double *gx_out,
-                           int nth)
+                           double *bnd_out, int nth)
 {
     double *diff = calloc((size_t)(T + 1) * C, sizeof(double));
     double *mu = calloc((size_t)T * C, sizeof(double));
+    double *start = bnd_out ? calloc((size_t)T * C, sizeof(double)) : NULL;
 #pragma omp parallel for num_threads(nth) if (nth > 1) schedule(static)
     for (int c = 0; c < C; ++c) {
         /* every segment (s, k, c) */
@@ -278,6 +282,7 @@ static void posteriors_one(int T, int L, int C, int K, int center, double w, dou
                           + ((zf[s] + zb[s + k] - zf[L]) - lzs);
                 double p = exp(lp);
                 if (gdur) gdur[(size_t)(k - 1) * C + c] += w * p;
+                if (start) start[(size_t)s * C + c] += p;
                 diff[(size_t)s * C + c] += p;
                 diff[(size_t)(s + k) * C + c] -= p;
             }
@@ -307,8 +312,17 @@ static void posteriors_one(int T, int L, int C, int K, int center, double w, dou
             if (gx_out) gx_out[(size_t)i * C + c] = i < L ? w * (m - mean) : 0.0;
         }
     }
+    if (bnd_out) {
+        for (int s = 0; s < T; ++s) {
+            double b = 0.0;
+            if (s < L)
+                for (int c = 0; c < C; ++c) b += start[(size_t)s * C + c];
+            bnd_out[s] = b;
+        }
+    }
     free(diff);
     free(mu);
+    free(start);
 }
 
 /* --------------------------------------------------------------- public API */
@@ -327,11 +341,12 @@ int oracle_prefix(int B, int T, int C, const float *x, const int32_t *lengths, i
 }
 
 /* Full forward-backward.  Output pointers other than logz may be NULL.
- * logz_bwd (optional) receives the right-to-left log Z for consistency checks. */
+ * logz_bwd (optional) receives the right-to-left log Z for consistency checks;
+ * boundary (optional, [B][T]) the probability that a segment starts at t. */
 int oracle_fwd_bwd(int B, int T, int C, int K, const float *x, const int32_t *lengths,
                    const float *trans, const float *dur, int center, const double *w,
                    double *logz, double *logz_bwd, double *grad_x, double *grad_trans,
-                   double *grad_dur, double *marginals, int nthreads)
+                   double *grad_dur, double *marginals, double *boundary, int nthreads)
 {
     if (B < 1 || T < 1 || C < 1 || K < 1) return 2;
     int nth = pick_threads(nthreads);
@@ -339,7 +354,7 @@ int oracle_fwd_bwd(int B, int T, int C, int K, const float *x, const int32_t *le
     double *du = malloc((size_t)K * C * sizeof(double));
     for (size_t i = 0; i < (size_t)C * C; ++i) tr[i] = trans[i];
     for (size_t i = 0; i < (size_t)K * C; ++i) du[i] = dur[i];
-    int want_post = grad_x || grad_trans || grad_dur || marginals;
+    int want_post = grad_x || grad_trans || grad_dur || marginals || boundary;
     /* per-sequence parameter-gradient buffers, summed in sequence order */
     double *gt_all = want_post ? calloc((size_t)B * C * C, sizeof(double)) : NULL;
     double *gd_all = want_post ? calloc((size_t)B * K * C, sizeof(double)) : NULL;
@@ -359,6 +374,8 @@ int oracle_fwd_bwd(int B, int T, int C, int K, const float *x, const int32_t *le
                 if (grad_x) grad_x[(size_t)b * T * C + i] = 0.0;
                 if (marginals) marginals[(size_t)b * T * C + i] = 0.0;
             }
+            if (boundary)
+                for (int i = 0; i < T; ++i) boundary[(size_t)b * T + i] = 0.0;
             continue;
         }
         tables_t tb;
@@ -379,7 +396,8 @@ int oracle_fwd_bwd(int B, int T, int C, int K, const float *x, const int32_t *le
                            tb.beta, tb.zf, tb.zb, gt_all + (size_t)b * C * C,
                            gd_all + (size_t)b * K * C,
                            marginals ? marginals + (size_t)b * T * C : NULL,
-                           grad_x ? grad_x + (size_t)b * T * C : NULL, inner);
+                           grad_x ? grad_x + (size_t)b * T * C : NULL,
+                           boundary ? boundary + (size_t)b * T : NULL, inner);
         free(nu);
         tables_free(&tb);
     }

@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsemicrf.so")
 
-OP_SCAN, OP_LOGZ, OP_FWD_BWD, OP_VITERBI = 0, 1, 2, 3
+OP_SCAN, OP_LOGZ, OP_FWD_BWD, OP_VITERBI, OP_PATH_SCORE = 0, 1, 2, 3, 4
 NO_CENTER = 1
 
 STATUS = {
@@ -31,10 +31,10 @@ STATUS = {
 EXPORTS = (
     "semicrf_status_string", "semicrf_default_checkpoint_interval", "semicrf_checkpoint_interval",
     "semicrf_workspace_size",
-    "semicrf_cumulative_scores", "semicrf_logz_fwd", "semicrf_fwd_bwd", "semicrf_fwd_bwd_timed",
-    "semicrf_viterbi",
+    "semicrf_cumulative_scores", "semicrf_logz_fwd", "semicrf_fwd_bwd", "semicrf_fwd_bwd_ex",
+    "semicrf_viterbi", "semicrf_path_score",
 )
-FWD_BWD_PHASES = ("cumulative_scores", "sweeps", "posteriors", "reductions")
+FWD_BWD_PHASES = ("cumulative_scores", "sweep_first", "sweep_rest", "posteriors", "reductions")
 
 
 class SemiCRFError(RuntimeError):
@@ -69,9 +69,12 @@ def load():
     lib.semicrf_logz_fwd.restype = I
     lib.semicrf_fwd_bwd.argtypes = [P, P, P, P, I, I, I, I, U, I, P, P, P, P, P, P, P, Z, P]
     lib.semicrf_fwd_bwd.restype = I
-    lib.semicrf_fwd_bwd_timed.argtypes = [P, P, P, P, I, I, I, I, U, I, P, P, P, P, P, P, P, Z, P,
-                                          P]
-    lib.semicrf_fwd_bwd_timed.restype = I
+    lib.semicrf_fwd_bwd_ex.argtypes = [P, P, P, P, I, I, I, I, U, I, P, P, P, P, P, P, P, P, Z,
+                                       P, P]
+    lib.semicrf_fwd_bwd_ex.restype = I
+    lib.semicrf_path_score.argtypes = [P, P, P, P, I, I, I, I, U, P, P, P, P, P, P, P, P, P, P, Z,
+                                       P]
+    lib.semicrf_path_score.restype = I
     lib.semicrf_viterbi.argtypes = [P, P, P, P, I, I, I, I, U, P, P, P, P, P, P, Z, P]
     lib.semicrf_viterbi.restype = I
     _lib = lib
@@ -133,6 +136,16 @@ def _check_inputs(emissions, lengths, trans=None, dur=None):
     return B, T, C, K, dev
 
 
+def _check_weights(name, w, B, dev):
+    """A per-sequence weight vector: None, or a contiguous float32 [B] tensor
+    on `dev` (the kernels read w[b] as contiguous memory)."""
+    if w is None:
+        return
+    if (w.shape != (B,) or w.dtype != torch.float32 or w.device != dev
+            or not w.is_contiguous()):
+        raise ValueError("%s must be a contiguous float32 [%d] tensor on %s" % (name, B, dev))
+
+
 def _workspace(op, B, T, C, K, flags, ckpt, dev):
     n = semicrf_workspace_size(op, B, T, C, K, flags, ckpt)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=dev), n
@@ -162,11 +175,9 @@ class FwdBwdPlan:
     one shape (the benchmark times `run()` alone)."""
 
     def __init__(self, emissions, lengths, trans, dur, center=True, grad_logz=None,
-                 checkpoint_interval=0, want_marginals=False):
+                 checkpoint_interval=0, want_marginals=False, want_boundary=False):
         B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
-        if grad_logz is not None and (grad_logz.shape != (B,) or grad_logz.dtype != torch.float32
-                                      or grad_logz.device != dev):
-            raise ValueError("grad_logz must be a float32 [B] tensor on %s" % dev)
+        _check_weights("grad_logz", grad_logz, B, dev)
         self.args = (emissions, lengths, trans, dur)
         self.B, self.T, self.C, self.K = B, T, C, K
         self.flags = 0 if center else NO_CENTER
@@ -180,6 +191,8 @@ class FwdBwdPlan:
         self.grad_dur = torch.empty((K, C), dtype=torch.float32, device=dev)
         self.marginals = (torch.empty((B, T, C), dtype=torch.float32, device=dev)
                           if want_marginals else None)
+        self.boundary = (torch.empty((B, T), dtype=torch.float32, device=dev)
+                         if want_boundary else None)
 
     def run(self, stream=None, phase_events=None):
         """Enqueue one fwd+bwd.  phase_events: optional list of
@@ -192,11 +205,11 @@ class FwdBwdPlan:
             if len(phase_events) != len(FWD_BWD_PHASES) + 1:
                 raise ValueError("need %d events" % (len(FWD_BWD_PHASES) + 1))
             evs = (ctypes.c_void_p * len(phase_events))(*[ev.cuda_event for ev in phase_events])
-        rc = load().semicrf_fwd_bwd_timed(
+        rc = load().semicrf_fwd_bwd_ex(
             _ptr(e), _ptr(l), _ptr(t), _ptr(d), self.B, self.T, self.C, self.K, self.flags,
             self.ckpt, _ptr(self.grad_logz), _ptr(self.logz), _ptr(self.grad_emissions),
-            _ptr(self.grad_trans), _ptr(self.grad_dur), _ptr(self.marginals), _ptr(self.ws),
-            self.ws_bytes, st, evs)
+            _ptr(self.grad_trans), _ptr(self.grad_dur), _ptr(self.marginals),
+            _ptr(self.boundary), _ptr(self.ws), self.ws_bytes, st, evs)
         if rc:
             raise SemiCRFError(rc, "semicrf_fwd_bwd")
         return self
@@ -206,15 +219,56 @@ class FwdBwdPlan:
                    grad_trans=self.grad_trans, grad_dur=self.grad_dur)
         if self.marginals is not None:
             out["marginals"] = self.marginals
+        if self.boundary is not None:
+            out["boundary"] = self.boundary
         return out
 
 
 def semicrf_fwd_bwd(emissions, lengths, trans, dur, center: bool = True, grad_logz=None,
-                    checkpoint_interval: int = 0, want_marginals: bool = False):
-    """Returns dict(logz, grad_emissions, grad_trans, grad_dur[, marginals])."""
+                    checkpoint_interval: int = 0, want_marginals: bool = False,
+                    want_boundary: bool = False):
+    """Returns dict(logz, grad_emissions, grad_trans, grad_dur[, marginals][, boundary])."""
     plan = FwdBwdPlan(emissions, lengths, trans, dur, center, grad_logz, checkpoint_interval,
-                      want_marginals)
+                      want_marginals, want_boundary)
     return plan.run().outputs()
+
+
+def _check_segments(segments, B, T, dev):
+    names = ("seg_start", "seg_len", "seg_label", "num_segs")
+    shapes = ((B, T), (B, T), (B, T), (B,))
+    for n, shp in zip(names, shapes):
+        t = segments[n]
+        if t.device != dev or t.dtype != torch.int32 or not t.is_contiguous() or t.shape != shp:
+            raise ValueError("%s must be a contiguous int32 %s tensor on %s" % (n, shp, dev))
+    return [segments[n] for n in names]
+
+
+def semicrf_path_score(emissions, lengths, trans, dur, segments, center: bool = True,
+                       weights=None, want_grads: bool = False):
+    """Score of the segmentations `segments` (dict of seg_start, seg_len,
+    seg_label [B,T] and num_segs [B] int32, the Viterbi output layout).
+    Returns dict(score [B] f32[, grad_emissions, grad_trans, grad_dur]): the
+    gradients of sum_b weights_b score_b (weights [B] float32 or None = 1)."""
+    B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
+    ss, sl, sc, ns = _check_segments(segments, B, T, dev)
+    _check_weights("weights", weights, B, dev)
+    flags = 0 if center else NO_CENTER
+    ws, n = _workspace(OP_PATH_SCORE, B, T, C, K, flags, 0, dev)
+    score = torch.empty(B, dtype=torch.float32, device=dev)
+    out = dict(score=score)
+    gx = gt = gd = None
+    if want_grads:
+        gx = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+        gt = torch.empty((C, C), dtype=torch.float32, device=dev)
+        gd = torch.empty((K, C), dtype=torch.float32, device=dev)
+        out.update(grad_emissions=gx, grad_trans=gt, grad_dur=gd)
+    rc = load().semicrf_path_score(_ptr(emissions), _ptr(lengths), _ptr(trans), _ptr(dur), B, T,
+                                   C, K, flags, _ptr(ss), _ptr(sl), _ptr(sc), _ptr(ns),
+                                   _ptr(weights), _ptr(score), _ptr(gx), _ptr(gt), _ptr(gd),
+                                   _ptr(ws), n, _stream(dev))
+    if rc:
+        raise SemiCRFError(rc, "semicrf_path_score")
+    return out
 
 
 class LogzPlan:
@@ -278,4 +332,5 @@ cumulative_scores = semicrf_cumulative_scores
 logz = semicrf_logz_fwd
 fwd_bwd = semicrf_fwd_bwd
 viterbi = semicrf_viterbi
+path_score = semicrf_path_score
 workspace_size = semicrf_workspace_size

@@ -3,7 +3,9 @@
     python -m semi_markov_crf_zero_amd.build [--asm]
 
 Every .hip file under csrc/ is compiled to an object in _build/ (in
-parallel) and linked into semi_markov_crf_zero_amd/libsemicrf.so.
+parallel) and linked into semi_markov_crf_zero_amd/libsemicrf.so; the
+peak microbenchmarks under probe/ (used by the benchmark only) become
+semi_markov_crf_zero_amd/libsemicrf_peaks.so.
 Packed FP32 instructions are disabled for all device code.  --asm also keeps
 the gfx950 assembly (_build/*.s) for inspection.
 """
@@ -20,6 +22,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsemicrf.so")
+PROBE = os.path.join(PKG, "probe")
+PEAKS_LIB = os.path.join(PKG, "libsemicrf_peaks.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -32,7 +36,8 @@ COMMON = [
 
 
 def _compile(src: str, asm: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    obj = os.path.join(BUILD, os.path.basename(os.path.dirname(src)) + "_" +
+                       os.path.basename(src) + ".o")
     cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
     if asm:
         cmd += ["--save-temps"]
@@ -43,15 +48,21 @@ def _compile(src: str, asm: bool) -> str:
     return obj
 
 
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    subprocess.check_call(cmd)
+    os.replace(tmp, lib)
+
+
 def build(asm: bool = False, jobs: int = 4) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probes = sorted(glob.glob(os.path.join(PROBE, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, asm), srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
-    subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+        objs = list(ex.map(lambda s: _compile(s, asm), srcs + probes))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PEAKS_LIB)
     return LIB
 
 

@@ -196,6 +196,12 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
       lay.dur_part = cv.take((size_t)B * g.dur_nspan * K * C * 8);
       break;
     }
+    case SEMICRF_OP_PATH_SCORE:
+      lay.p_score = cv.take((size_t)B * 8);
+      lay.p_valid = cv.take((size_t)B * 4);
+      lay.p_cnt = cv.take((size_t)B * ((size_t)C * C + (size_t)K * C + C) * 4);
+      lay.p_lab = cv.take((size_t)B * T * 4);
+      break;
     case SEMICRF_OP_VITERBI:
       lay.bp = cv.take(nS * 4);
       lay.vbest = cv.take((size_t)B * 8);
@@ -226,7 +232,7 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
 // Validate sizes/flags and fill the shape + layout.  No launches.
 semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int ckpt,
                          ChainShape &sh, Layout &lay, VShape *vs_out = nullptr) {
-  if (op < SEMICRF_OP_SCAN || op > SEMICRF_OP_VITERBI) return SEMICRF_ERR_ARG;
+  if (op < SEMICRF_OP_SCAN || op > SEMICRF_OP_PATH_SCORE) return SEMICRF_ERR_ARG;
   if (flags & ~(unsigned)SEMICRF_NO_CENTER) return SEMICRF_ERR_ARG;
   if (ckpt < 0) return SEMICRF_ERR_ARG;
   const semicrf_status_t s = check_sizes(B, T, C, op == SEMICRF_OP_SCAN ? 1 : K);
@@ -238,7 +244,7 @@ semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int
   sh.C = C;
   sh.K = K;
   sh.center = (flags & SEMICRF_NO_CENTER) ? 0 : 1;
-  if (op != SEMICRF_OP_SCAN) {
+  if (op != SEMICRF_OP_SCAN && op != SEMICRF_OP_PATH_SCORE) {
     // Viterbi always uses the LDS-ring layout; the sweeps use the windowed
     // engine when it applies.  Both must exist for a supported (C, K).
     ChainShape probe = sh;
@@ -377,13 +383,13 @@ semicrf_status_t semicrf_logz_fwd(const float *emissions, const int32_t *lengths
   return hip_status(e);
 }
 
-semicrf_status_t semicrf_fwd_bwd_timed(const float *emissions, const int32_t *lengths,
-                                       const float *trans, const float *dur, int B, int T, int C,
-                                       int K, unsigned flags, int checkpoint_interval,
-                                       const float *grad_logz, float *logz,
-                                       float *grad_emissions, float *grad_trans, float *grad_dur,
-                                       float *marginals, void *workspace, size_t workspace_bytes,
-                                       void *stream, void *const *phase_events) {
+semicrf_status_t semicrf_fwd_bwd_ex(const float *emissions, const int32_t *lengths,
+                                    const float *trans, const float *dur, int B, int T, int C,
+                                    int K, unsigned flags, int checkpoint_interval,
+                                    const float *grad_logz, float *logz, float *grad_emissions,
+                                    float *grad_trans, float *grad_dur, float *marginals,
+                                    float *boundary, void *workspace, size_t workspace_bytes,
+                                    void *stream, void *const *phase_events) {
   if (!emissions || !lengths || !trans || !dur || !logz || !grad_emissions || !grad_trans ||
       !grad_dur)
     return SEMICRF_ERR_NULL;
@@ -408,10 +414,10 @@ semicrf_status_t semicrf_fwd_bwd_timed(const float *emissions, const int32_t *le
   if (e != hipSuccess) return hip_status(e);
   mark(1);
   e = run_sweeps(sh, trans, dur, escaled(ws, lay), lengths, pit_bufs(ws, lay, true),
-                 at<double>(ws, lay.logz),
-                 at<double>(ws, lay.logz_bwd), logz, 1, st);
+                 at<double>(ws, lay.logz), at<double>(ws, lay.logz_bwd), logz, 1, st,
+                 phase_events ? static_cast<hipEvent_t>(phase_events[2]) : nullptr);
   if (e != hipSuccess) return hip_status(e);
-  mark(2);
+  mark(3);
   PostArgs pa;
   pa.lengths = lengths;
   pa.trans = trans;
@@ -434,9 +440,10 @@ semicrf_status_t semicrf_fwd_bwd_timed(const float *emissions, const int32_t *le
   pa.marginals = marginals;
   pa.grad_trans = grad_trans;
   pa.grad_dur = grad_dur;
+  pa.boundary = boundary;
   e = launch_posteriors(sh, pa, st);
   if (e != hipSuccess) return hip_status(e);
-  mark(3);
+  mark(4);
   e = launch_post_reduce(sh, pa, st);
   if (e != hipSuccess) return hip_status(e);
   mark(SEMICRF_FWD_BWD_PHASES);
@@ -449,9 +456,54 @@ semicrf_status_t semicrf_fwd_bwd(const float *emissions, const int32_t *lengths,
                                  float *logz, float *grad_emissions, float *grad_trans,
                                  float *grad_dur, float *marginals, void *workspace,
                                  size_t workspace_bytes, void *stream) {
-  return semicrf_fwd_bwd_timed(emissions, lengths, trans, dur, B, T, C, K, flags,
-                               checkpoint_interval, grad_logz, logz, grad_emissions, grad_trans,
-                               grad_dur, marginals, workspace, workspace_bytes, stream, nullptr);
+  return semicrf_fwd_bwd_ex(emissions, lengths, trans, dur, B, T, C, K, flags,
+                            checkpoint_interval, grad_logz, logz, grad_emissions, grad_trans,
+                            grad_dur, marginals, nullptr, workspace, workspace_bytes, stream,
+                            nullptr);
+}
+
+semicrf_status_t semicrf_path_score(const float *emissions, const int32_t *lengths,
+                                    const float *trans, const float *dur, int B, int T, int C,
+                                    int K, unsigned flags, const int32_t *seg_start,
+                                    const int32_t *seg_len, const int32_t *seg_label,
+                                    const int32_t *num_segs, const float *weights, float *score,
+                                    float *grad_emissions, float *grad_trans, float *grad_dur,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  if (!emissions || !lengths || !trans || !dur || !seg_start || !seg_len || !seg_label ||
+      !num_segs || !score)
+    return SEMICRF_ERR_NULL;
+  ChainShape sh;
+  Layout lay;
+  const semicrf_status_t s = prepare(SEMICRF_OP_PATH_SCORE, B, T, C, K, flags, 0, sh, lay);
+  if (s != SEMICRF_OK) return s;
+  if (!workspace || workspace_bytes < lay.total) return SEMICRF_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  void *ws = workspace;
+  double *S = at<double>(ws, lay.S);
+  hipError_t e = launch_scan(emissions, lengths, B, T, C, sh.center, at<double>(ws, lay.nu), S,
+                             nullptr, nullptr, nullptr, at<double>(ws, lay.tile_sum),
+                             at<double>(ws, lay.anchor), lay.ntile, lay.scan_j, st);
+  if (e != hipSuccess) return hip_status(e);
+  PathArgs pa;
+  pa.lengths = lengths;
+  pa.trans = trans;
+  pa.dur = dur;
+  pa.w = weights;
+  pa.S = S;
+  pa.seg_start = seg_start;
+  pa.seg_len = seg_len;
+  pa.seg_label = seg_label;
+  pa.num_segs = num_segs;
+  pa.score = score;
+  pa.grad_x = grad_emissions;
+  pa.grad_trans = grad_trans;
+  pa.grad_dur = grad_dur;
+  pa.score_ws = at<double>(ws, lay.p_score);
+  pa.valid = at<int>(ws, lay.p_valid);
+  pa.cnt = at<int>(ws, lay.p_cnt);
+  pa.lab = at<int32_t>(ws, lay.p_lab);
+  return hip_status(launch_path_score(sh, pa, st));
 }
 
 semicrf_status_t semicrf_viterbi(const float *emissions, const int32_t *lengths,

@@ -158,12 +158,29 @@ struct Layout {
   size_t row_a, row_u, row_v, row_b;
   size_t cov_part, cov_part2, cov_anchor, cov_mean, tx_part, dur_part, trw;
   size_t bp, vbest, vcbest;
+  size_t p_score, p_valid, p_cnt, p_lab;
   size_t v_pred, v_rr, v_re, v_corr, v_delta, v_redo, v_nbad, v_lst_t, v_lst_c, v_mark, v_sub;
   size_t total;
   int ntile;
   int scan_j;   // positions per scan row thread
   int vit_pit;  // Viterbi by the parallel-in-time decoder (vpit.hip)
 };
+
+// Arguments of the path score (path.hip).
+struct PathArgs {
+  const int32_t *lengths;
+  const float *trans, *dur, *w;  // w: [B] weights of the gradients (NULL = ones)
+  const double *S;
+  const int32_t *seg_start, *seg_len, *seg_label, *num_segs;
+  float *score;                                 // [B]
+  float *grad_x, *grad_trans, *grad_dur;        // each may be NULL
+  double *score_ws;                             // [B]
+  int *valid;                                   // [B]
+  int *cnt;  // [B][C][C] transitions, [B][K][C] durations, [B][C] positions per label
+  int32_t *lab;                                 // [B][T] label of each position
+};
+
+hipError_t launch_path_score(const ChainShape &sh, const PathArgs &pa, hipStream_t st);
 
 // Arguments of the posterior pass (post.hip).
 struct PostArgs {
@@ -176,6 +193,7 @@ struct PostArgs {
   double *tx_part;                                       // [B][tx_nseg][C][C]
   double *dur_part;                                      // [B][dur_nspan][K][C]
   float *grad_emissions, *marginals, *grad_trans, *grad_dur;
+  float *boundary;  // [B][T] P(a segment starts at t), or NULL
 };
 
 // Launch geometry of the posterior pass (also sizes its workspace).
@@ -235,10 +253,12 @@ hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float 
 
 // The whole parallel-in-time sweep: init, nchunk x (sweep, verify), fix-up
 // of the records, log Z and (when wanted) the per-position rows.
+// after_first (may be NULL) is recorded on st right after the first sweep
+// launch (iteration 0, which sweeps every chunk).
 hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur,
                       const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                       double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
-                      hipStream_t st);
+                      hipStream_t st, hipEvent_t after_first = nullptr);
 
 // exp(trans) for the weight-streaming instances (chain.hip).
 hipError_t launch_trw(int C, int CS, int QT, const float *trans, float *trw, hipStream_t st);

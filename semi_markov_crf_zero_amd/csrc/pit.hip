@@ -66,14 +66,14 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_verify(ChainShape sh,
   const int L = lengths[b];
   if (L < 1 || L > sh.T) return;
   const int nvalid = (L + sh.delta - 1) / sh.delta;
-  int jp;  // chunk whose end must equal this chunk's start
-  if (fwd) {
-    if (j == 0 || j >= nvalid) return;
-    jp = j - 1;
-  } else {
-    if (j + 1 >= nvalid) return;
-    jp = j + 1;
+  if (j >= nvalid) return;  // past the sequence: never swept
+  if (fwd ? j == 0 : j + 1 == nvalid) {
+    // the chain's exact chunk: its start is exact from iteration 0, so it is
+    // never swept again
+    if (threadIdx.x == 0) pb.redo[(fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + j] = 0;
+    return;
   }
+  const int jp = fwd ? j - 1 : j + 1;  // chunk whose end must equal this chunk's start
   const int C = sh.C, K = sh.K;
   const size_t cks = ck_stride(C, K);
   double *A = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + j) * cks;
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_pos_shift(ChainShape sh,
 hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur,
                       const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                       double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
-                      hipStream_t st) {
+                      hipStream_t st, hipEvent_t after_first) {
   // iteration 0 of the sweep also sets every chunk's redo flag and scalar
   // and clears the per-iteration mismatch counts
   const int niter = sh.nchunk;
@@ -310,6 +310,7 @@ hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur
   for (int it = 0; it < niter; ++it) {
     e = launch_sweep(sh, trans, dur, es, lengths, pb, with_bwd, it, st);
     if (e != hipSuccess) return e;
+    if (it == 0 && after_first) (void)hipEventRecord(after_first, st);
     if (it + 1 == niter) break;
     e = launch_pit_verify(sh, lengths, pb, it, with_bwd, st);
     if (e != hipSuccess) return e;

@@ -431,6 +431,34 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
   }
 }
 
+// ------------------------------------------------------------ boundaries
+// boundary[b,t] = sum_c E_start[t,c] = P(a segment starts at position t)
+// for t < L (1 at t = 0), 0 for t >= L: the boundary uncertainty of the
+// abstract of "Streaming Structured Inference with Flash-SemiCRF".  One wave
+// per position at a time (grid-stride), lanes over labels; the lanes' sums
+// meet by a fixed butterfly, so the result is deterministic.
+constexpr int kBndThreads = 256;
+__global__ __launch_bounds__(kBndThreads) void k_boundary(ChainShape sh, PostArgs pa) {
+  const int lane = threadIdx.x & 63;
+  constexpr int wpb = kBndThreads / 64;
+  const long long npos = (long long)sh.B * sh.T;
+  const long long nw = (long long)gridDim.x * wpb;
+  for (long long q = (long long)blockIdx.x * wpb + (threadIdx.x >> 6); q < npos; q += nw) {
+    const int b = (int)(q / sh.T), t = (int)(q % sh.T);
+    const int L = pa.lengths[b];
+    double s = 0.0;
+    if (valid_len(sh, L) && t < L) {  // uniform over the wave
+      const double z = pa.pos_shift[(size_t)b * (sh.T + 1) + t] +
+                       pa.pos_shift[((size_t)sh.B + b) * (sh.T + 1) + t] - pa.logz[b];
+      const size_t i = rix(sh, b, t);
+      for (int c = lane; c < sh.C; c += 64) s += exp(pa.row_u[i + c] + pa.row_v[i + c] + z);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) pa.boundary[q] = (float)s;
+  }
+}
+
 // ------------------------------------------------------------ reductions
 // grad_trans = exp(trans) * sum_b w_b sum_seg X;  grad_dur = sum_b w_b sum_span D.
 // One workgroup per kRedOut consecutive outputs (transition entries first,
@@ -558,6 +586,13 @@ hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream
                    : g.dur_kb == 8 ? (const void *)k_dur_x<8>
                    : g.dur_kb == 16 ? (const void *)k_dur_x<16> : (const void *)k_dur_x<32>;
   if (!lds_fits(kd, g.dur_lds)) return hipErrorInvalidConfiguration;
+  if (pa.boundary) {
+    long long nb = ((long long)sh.B * sh.T + (kBndThreads / 64) - 1) / (kBndThreads / 64);
+    nb = nb > 2048 ? 2048 : nb;
+    hipLaunchKernelGGL(k_boundary, dim3((int)nb), dim3(kBndThreads), 0, st, sh, pa);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   switch (g.dur_kb) {
     case 4: hipLaunchKernelGGL(k_dur_x<4>, gd, dim3(kDurThreads), g.dur_lds, st, sh, pa, g.dur_span, g.dur_nspan, g.dur_npg); break;
     case 8: hipLaunchKernelGGL(k_dur_x<8>, gd, dim3(kDurThreads), g.dur_lds, st, sh, pa, g.dur_span, g.dur_nspan, g.dur_npg); break;

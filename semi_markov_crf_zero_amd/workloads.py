@@ -78,6 +78,30 @@ def _path(rng, T, K, C, kind):
     return lens.astype(np.int64), labels.astype(np.int64)
 
 
+def segment_arrays(paths, lengths, T):
+    """Segment lists in the layout of the library's segmentation arguments:
+    seg_start / seg_len / seg_label [B,T] int32 (-1 past num_segs) and
+    num_segs [B], each path cut at its sequence's length."""
+    B = len(paths)
+    out = {k: np.full((B, T), -1, dtype=np.int32) for k in ("seg_start", "seg_len", "seg_label")}
+    out["num_segs"] = np.zeros(B, dtype=np.int32)
+    for b, (lens, labels) in enumerate(paths):
+        L = int(lengths[b])
+        pos = 0
+        j = 0
+        for k, c in zip(lens, labels):
+            if pos >= L:
+                break
+            k = min(int(k), L - pos)
+            out["seg_start"][b, j] = pos
+            out["seg_len"][b, j] = k
+            out["seg_label"][b, j] = int(c)
+            pos += k
+            j += 1
+        out["num_segs"][b] = j
+    return out
+
+
 def _paint(x_b, lens, labels, amount):
     pos = 0
     for L, c in zip(lens, labels):
@@ -87,7 +111,10 @@ def _paint(x_b, lens, labels, amount):
 
 def make_inputs(name: str, seed: int = 0):
     """Return a dict with emissions [B,T,C] f32, lengths [B] i32,
-    trans [C,C] f32, dur [K,C] f32 and the shape ints for a named workload."""
+    trans [C,C] f32, dur [K,C] f32, the shape ints for a named workload and
+    `gold`, the path the emissions were raised on (segment arrays of
+    segment_arrays(), cut at each length; for tiny, whose emissions have no
+    path, one drawn afterwards from a separate generator)."""
     w = WORKLOADS[name]
     B, T, C, K = w.B, w.T, w.C, w.K
     rng = np.random.default_rng(seed)
@@ -110,8 +137,12 @@ def make_inputs(name: str, seed: int = 0):
     dur = rng.normal(0.0, 0.1, size=(K, C))
     if name == "speech":
         dur = dur - 0.05 * np.arange(1, K + 1)[:, None]
+    if name == "tiny":
+        rng2 = np.random.default_rng(seed + 1)
+        paths = [_path(rng2, T, K, C, "uniform1K") for _ in range(B)]
     return dict(
         B=B, T=T, C=C, K=K,
+        gold=segment_arrays(paths, lengths, T),
         emissions=np.ascontiguousarray(x, dtype=np.float32),
         lengths=np.ascontiguousarray(lengths, dtype=np.int32),
         trans=np.ascontiguousarray(trans, dtype=np.float32),

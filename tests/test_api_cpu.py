@@ -148,3 +148,47 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 4, 2)
     with pytest.raises(ValueError):
         bd.semicrf_logz_fwd(x, torch.ones(1, dtype=torch.int32), torch.zeros(2, 2), torch.zeros(3, 2))
+
+
+def test_weight_vectors_must_be_contiguous():
+    """grad_logz / weights are read as contiguous [B] float32 memory: a
+    strided view (w[::2]) would silently weight the wrong sequences."""
+    import torch
+    dev = torch.device("cpu")
+    bd._check_weights("grad_logz", None, 3, dev)
+    bd._check_weights("grad_logz", torch.ones(3), 3, dev)
+    with pytest.raises(ValueError):
+        bd._check_weights("grad_logz", torch.ones(6)[::2], 3, dev)
+    with pytest.raises(ValueError):
+        bd._check_weights("grad_logz", torch.ones(3, dtype=torch.float64), 3, dev)
+    with pytest.raises(ValueError):
+        bd._check_weights("weights", torch.ones(4), 3, dev)
+
+
+def test_fwd_bwd_ex_and_path_score_validate_before_launch(lib):
+    P = FAKE
+    need = bd.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 10, 4, 4)
+    # fwd_bwd_ex: boundary and phase events optional; the rest as fwd_bwd
+    assert lib.semicrf_fwd_bwd_ex(P, P, P, P, 2, 10, 4, 4, 0, 0, None, P, P, P, None, None, None,
+                                  P, need, None, None) == 1
+    assert lib.semicrf_fwd_bwd_ex(P, P, P, P, 2, 10, 4, 4, 0, 0, None, P, P, P, P, None, None,
+                                  P, need - 1, None, None) == 4
+    assert lib.semicrf_fwd_bwd_ex(P, P, P, P, 2, 10, 300, 4, 0, 0, None, P, P, P, P, None, P,
+                                  P, need, None, None) == 3
+    # path score: inputs, segments and score required; gradients optional
+    need = bd.semicrf_workspace_size(bd.OP_PATH_SCORE, 2, 10, 4, 4)
+    assert need > 0
+    base = [P, P, P, P, 2, 10, 4, 4, 0, P, P, P, P, None, P, None, None, None, P, need, None]
+    for idx in (0, 1, 2, 3, 9, 10, 11, 12, 14):
+        args = list(base)
+        args[idx] = None
+        assert lib.semicrf_path_score(*args) == 1
+    args = list(base)
+    args[19] = need - 1
+    assert lib.semicrf_path_score(*args) == 4
+    args = list(base)
+    args[8] = 4  # unknown flag
+    assert lib.semicrf_path_score(*args) == 6
+    args = list(base)
+    args[4] = 0
+    assert lib.semicrf_path_score(*args) == 2

@@ -283,3 +283,23 @@ def test_viterbi_enumeration_grid(C, K):
     for center in (True, False):
         inp = _case(3, T, C, K, [T, 4, 1], seed=100 + C * 10 + K, tsd=0.5, dsd=0.5)
         assert_viterbi_equal(gpu_viterbi(inp, center), oracle.viterbi(inp, center), label=(C, K))
+
+
+@pytest.mark.parametrize("ckpt", [64, 0])
+def test_fwd_bwd_sticky_transitions_redo(ckpt):
+    """Off-diagonal transitions of -50: the chain stays in one label for long
+    runs, so the direction of each interval's state depends on the far past
+    and a neutral start does not match its predecessor's end: the
+    parallel-in-time sweeps go through their verification failures, redo
+    sweeps (up to one per interval) and the in-order correction of the
+    interval normalisers.  Every element against the oracle."""
+    C = 4
+    inp = _case(2, 2048, C, 16, [2048, 1501], seed=11, tsd=0.0, dsd=0.3)
+    trans = np.full((C, C), -50.0, np.float32)
+    np.fill_diagonal(trans, 0.0)
+    inp["trans"] = trans
+    o = oracle.fwd_bwd(inp)
+    g = gpu_fwd_bwd(inp, ckpt=ckpt)
+    errs = assert_fwd_bwd_close(g, o, label=("sticky", ckpt))
+    print("sticky", ckpt, errs)
+    assert_viterbi_equal(gpu_viterbi(inp), oracle.viterbi(inp), label="sticky")

@@ -1,13 +1,18 @@
 """GPU parity on the five named workloads, in the launch configuration that
-bench.py times (default checkpoint interval, library-chosen workgroups).
+bench.py times (default checkpoint interval, library-chosen workgroups),
+element by element against the float64 oracle run in the test on the host
+cores:
 
-tiny and NLP: element-by-element against the oracle run in the test.
-speech, genome, extreme: against tests/golden/<name>.npz, written by
-tests/golden/make_golden.py from the oracle alone (log Z, parameter
-gradients, sampled rows of marginals / emission gradients / cumulative
-scores, the complete Viterbi segmentation), plus properties checked over
-every position: marginals in [0, 1] summing to 1 over labels, and (with
-centring) emission gradients summing to 0 over time for every label.
+  fwd+bwd     log Z (relative 1e-5), every element of grad_emissions,
+              marginals and boundary posteriors (absolute 1e-4), every
+              element of grad_trans and grad_dur (1e-4 or one float32 ulp);
+  scan        every element of nu and of the cumulative scores S;
+  Viterbi     the complete segmentation of every sequence, bit-exact;
+  path score  the gold path's score and every element of its gradients.
+
+tests/golden/<name>.npz (written by tests/golden/make_golden.py from the
+oracle alone) is kept as a drift check: the digest of the regenerated inputs
+and the stored log Z must still match.
 """
 import os
 
@@ -19,22 +24,23 @@ import oracle
 from semi_markov_crf_zero_amd import binding as bd
 from semi_markov_crf_zero_amd.workloads import make_inputs
 from tests.golden.make_golden import input_digest
-from tests.gpu_util import (TOL_GRAD, assert_fwd_bwd_close, assert_viterbi_equal, gpu_fwd_bwd,
-                            gpu_scan, gpu_viterbi, logz_rel_err, param_excess, to_dev)
+from tests.gpu_util import (DEV, TOL_GRAD, assert_fwd_bwd_close, assert_viterbi_equal,
+                            gpu_fwd_bwd, gpu_scan, gpu_viterbi, logz_rel_err, param_excess,
+                            to_dev)
 
 pytestmark = pytest.mark.gpu
 
-GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+GOLDEN = os.path.dirname(os.path.abspath(__file__)) + "/golden"
+NAMES = ["tiny", "nlp", "speech", "genome", "extreme"]
 
 
-@pytest.mark.parametrize("name", ["tiny", "nlp"])
-def test_small_workloads_full(name):
-    inp = make_inputs(name)
-    o = oracle.fwd_bwd(inp)
-    g = gpu_fwd_bwd(inp)
-    errs = assert_fwd_bwd_close(g, o, label=name)
-    print(name, errs)
-    assert_viterbi_equal(gpu_viterbi(inp), oracle.viterbi(inp), label=name)
+def _drift_check(name, inp, o):
+    path = os.path.join(GOLDEN, name + ".npz")
+    if not os.path.exists(path):
+        return
+    gold = np.load(path, allow_pickle=False)
+    assert input_digest(inp) == str(gold["input_sha256"]), "input generator drifted"
+    np.testing.assert_allclose(o["logz"], gold["logz"], rtol=1e-12)
 
 
 def _properties(inp, out):
@@ -45,53 +51,59 @@ def _properties(inp, out):
         s = mu[b, :L[b]].sum(axis=1)
         assert np.abs(s - 1).max() <= TOL_GRAD, (b, np.abs(s - 1).max())
         assert np.all(mu[b, L[b]:] == 0)
-        col = out["grad_emissions"][b, :L[b]].sum(axis=0)
-        assert np.abs(col).max() <= 2e-3 * max(1.0, L[b] / 1000.0)
 
 
-@pytest.mark.parametrize("name", ["speech", "genome", "extreme"])
-def test_large_workloads_golden(name):
-    path = os.path.join(GOLDEN, name + ".npz")
-    gold = np.load(path, allow_pickle=False)
+@pytest.mark.parametrize("name", NAMES)
+def test_workload_fwd_bwd(name):
     inp = make_inputs(name)
-    assert input_digest(inp) == str(gold["input_sha256"]), "input generator drifted"
+    print("workload", name, flush=True)
+    g = gpu_fwd_bwd(inp)
+    o = oracle.fwd_bwd(inp)
+    _drift_check(name, inp, o)
+    errs = assert_fwd_bwd_close(g, o, label=name)
+    print(name, "logz rel %.2e" % logz_rel_err(g["logz"], o["logz"]).max(), errs,
+          "param excess trans %.3f dur %.3f" % (param_excess(g["grad_trans"], o["grad_trans"]),
+                                                param_excess(g["grad_dur"], o["grad_dur"])))
+    _properties(inp, g)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_workload_scan(name):
+    inp = make_inputs(name)
+    nu, S = gpu_scan(inp)
+    onu, oS = oracle.prefix(inp)
+    np.testing.assert_allclose(nu, onu, rtol=1e-12, atol=1e-12)
+    # float64 running sums of T terms: each addition rounds by at most
+    # u * |partial sum|, so two summation orders agree within 2u T max|S|
+    tol = 2.0 ** -52 * inp["T"] * max(1.0, float(np.abs(oS).max()))
+    err = float(np.abs(S - oS).max())
+    print(name, "S err %.2e (bar %.2e)" % (err, tol))
+    assert err <= tol
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_workload_viterbi(name):
+    inp = make_inputs(name)
+    v = gpu_viterbi(inp)
+    o = oracle.viterbi(inp)
+    assert_viterbi_equal(v, o, label=name)
+    print(name, "segments", v["num_segs"][:4], "min margin", o["min_margin"].min())
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_workload_path_score(name):
+    inp = make_inputs(name)
     t = to_dev(inp)
-    out = bd.semicrf_fwd_bwd(t["emissions"], t["lengths"], t["trans"], t["dur"],
-                             want_marginals=True)
+    gold = {k: torch.from_numpy(v).to(DEV) for k, v in inp["gold"].items()}
+    w = np.linspace(0.5, 1.5, inp["B"]).astype(np.float32)
+    out = bd.semicrf_path_score(t["emissions"], t["lengths"], t["trans"], t["dur"], gold,
+                                weights=torch.from_numpy(w).to(DEV), want_grads=True)
     torch.cuda.synchronize()
     g = {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
-    rel = logz_rel_err(g["logz"], gold["logz"])
-    assert rel.max() <= 1e-5, rel
-    e_tr = np.abs(g["grad_trans"] - gold["grad_trans"]).max()
-    e_du = np.abs(g["grad_dur"] - gold["grad_dur"]).max()
-    x_tr = param_excess(g["grad_trans"], gold["grad_trans"])
-    x_du = param_excess(g["grad_dur"], gold["grad_dur"])
-    rows = gold["rows"]
-    bidx = np.arange(inp["B"])[:, None]
-    e_mu = np.abs(g["marginals"][bidx, rows] - gold["marginals_rows"]).max()
-    e_gx = np.abs(g["grad_emissions"][bidx, rows] - gold["grad_rows"]).max()
-    print(name, "logz rel %.2e trans %.2e dur %.2e mu %.2e gx %.2e" % (rel.max(), e_tr, e_du, e_mu, e_gx))
-    assert x_tr <= 1.0 and x_du <= 1.0, (e_tr, x_tr, e_du, x_du)
-    assert e_mu <= TOL_GRAD and e_gx <= TOL_GRAD
-    np.testing.assert_allclose(g["marginals"].sum(axis=1), gold["colsum_marginals"],
-                               atol=TOL_GRAD * inp["T"] / 100)
-    _properties(inp, g)
-    del g, out
-    # cumulative scores at sampled rows
-    nu, S = gpu_scan(inp)
-    np.testing.assert_allclose(nu, gold["nu"], rtol=1e-12, atol=1e-12)
-    # float64 running sums of T terms: each addition rounds by at most u*|partial sum|,
-    # so the two summation orders agree within 2u*T*max|S| (u = 2^-53)
-    s_tol = 2.0 ** -52 * inp["T"] * max(1.0, float(np.abs(gold["S_rows"]).max()))
-    np.testing.assert_allclose(S[bidx, rows[:, ::4]], gold["S_rows"], rtol=0, atol=s_tol)
-    np.testing.assert_allclose(S[np.arange(inp["B"]), inp["lengths"]], gold["S_last"], atol=s_tol)
-    del S
-    # Viterbi: the complete segmentation
-    v = gpu_viterbi(inp)
-    n = gold["vit_num"]
-    assert np.array_equal(v["num_segs"], n), (v["num_segs"], n, gold["vit_margin"])
-    for b in range(inp["B"]):
-        for k, gk in (("seg_start", "vit_start"), ("seg_len", "vit_len"), ("seg_label", "vit_label")):
-            assert np.array_equal(v[k][b, :n[b]], gold[gk][b, :n[b]]), (b, k, gold["vit_margin"][b])
-        assert np.all(v["seg_start"][b, n[b]:] == -1)
-    np.testing.assert_allclose(v["best_score"], gold["vit_score"], rtol=1e-6)
+    o = oracle.path_score(inp, inp["gold"], weights=w)
+    rel = np.abs(g["score"] - o["score"]) / np.maximum(1.0, np.abs(o["score"]))
+    assert rel.max() <= 1e-6, rel
+    assert np.abs(g["grad_emissions"] - o["grad_emissions"]).max() <= 1e-6
+    # counts times float32 weights, summed in float64 and rounded once
+    for k in ("grad_trans", "grad_dur"):
+        assert param_excess(g[k], o[k], 1e-6) <= 1.0, k

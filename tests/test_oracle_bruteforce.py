@@ -31,7 +31,7 @@ def test_oracle_matches_enumeration(oracle_mod, C, K, seed, center):
     orc = oracle_mod.fwd_bwd(inp, center=center, grad_logz=w)
     np.testing.assert_allclose(orc["logz"], bf["logz"], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(orc["logz_bwd"], bf["logz"], rtol=1e-12, atol=1e-12)
-    for key in ("marginals", "grad_emissions", "grad_trans", "grad_dur"):
+    for key in ("marginals", "grad_emissions", "grad_trans", "grad_dur", "boundary"):
         np.testing.assert_allclose(orc[key], bf[key], rtol=0, atol=1e-11, err_msg=key)
     vit = oracle_mod.viterbi(inp, center=center)
     for b in range(3):
