@@ -326,7 +326,10 @@ __device__ __forceinline__ void vsweep(const VShape &vs, const VRegs<AMAX, CAMAX
 // R_j - E_{j-1} must be one constant over the ring entries of positions
 // (p0 - K, p0] that exist.  Records the constant, or makes E_{j-1} the start
 // of chunk j and marks it for another sweep.  Returns true if consistent.
-__device__ bool vverify(const VShape &vs, int b, int j, const VBufs &vb, int *flag, int iter) {
+// With `force` the test is skipped and E_{j-1} becomes the start: for a
+// chunk already marked, whose E_j does not follow from R_j yet.
+__device__ bool vverify(const VShape &vs, int b, int j, const VBufs &vb, int *flag, int iter,
+                        bool force = false) {
   const int C = vs.C, K = vs.K, tid = threadIdx.x, nt = blockDim.x;
   const int p0 = j * vs.delta;
   double *R = vb.rec_r + rec_base(vs, b, j);
@@ -347,7 +350,7 @@ __device__ bool vverify(const VShape &vs, int b, int j, const VBufs &vb, int *fl
   bad = __any(bad);
   if ((tid & 63) == 0) flag[tid >> 6] = bad;
   __syncthreads();
-  bad = 0;
+  bad = force ? 1 : 0;
   for (int w = 0; w < nt / 64; ++w) bad |= flag[w];
   const size_t idx = (size_t)b * vs.nchunk + j;
   __syncthreads();  // every read of R precedes the copy below
@@ -395,7 +398,12 @@ __global__ __launch_bounds__(NT) void k_vsweep(VShape vs, int mode, int iter,
 
 // Serial repair, one workgroup per sequence: chunks still marked after the
 // parallel passes are swept in order, each followed by the check of its
-// successor, so every chunk ends consistent with its predecessor.
+// successor, so every chunk ends consistent with its predecessor.  A
+// successor that is itself still marked was given a new start by the last
+// parallel check but not swept from it, so its end state belongs to an
+// older start: it is not checked against its predecessor (a passing check
+// would keep that stale end) but takes the predecessor's new end as its
+// start and is swept in turn.
 template <int NT, int AMAX, int CAMAX, int NGT>
 __global__ __launch_bounds__(NT) void k_vrepair(VShape vs, const float *__restrict__ trans,
                                                 const float *__restrict__ dur,
@@ -413,7 +421,8 @@ __global__ __launch_bounds__(NT) void k_vrepair(VShape vs, const float *__restri
     __syncthreads();
     if (!vb.redo[(size_t)b * vs.nchunk + j]) continue;
     vsweep<NT, AMAX, CAMAX, NGT>(vs, r, sm, kRedo, b, j, L, S, vb);
-    if (j + 1 < nvalid) vverify(vs, b, j + 1, vb, sm.flag, -1);
+    if (j + 1 < nvalid)
+      vverify(vs, b, j + 1, vb, sm.flag, -1, vb.redo[(size_t)b * vs.nchunk + j + 1] != 0);
   }
 }
 
