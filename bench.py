@@ -38,7 +38,7 @@ Prints ONE JSON line on stdout:
                inputs, outputs, workspace -- the library allocates nothing)
                and the size the materialised edge tensor would have.
   cpu_baseline the float64 oracle timed on this host on a bounded sample of
-               the headline workload (the first 2^19 positions for extreme).
+               the headline workload (the first 2^17 positions for extreme).
   rates        fwd+bwd over valid positions, semicrf_logz_fwd and
                semicrf_viterbi on the same input (after the timed steps).
 Diagnostics go to stderr.  --copy-calibration MB runs one device copy of MB
@@ -282,7 +282,7 @@ def run_workload(name, steps, warmup, ckpt, peaks, dev, want_rates, want_memory=
     return rec, inp
 
 
-def cpu_baseline(inp, name, max_positions=1 << 19, budget_s=12.0):
+def cpu_baseline(inp, name, max_positions=1 << 17, budget_s=12.0):
     import numpy as np
 
     import oracle

@@ -45,6 +45,9 @@ __global__ __launch_bounds__(kThreads) void k_exp(float *out, int iters, float s
   out[blockIdx.x * (size_t)kThreads + threadIdx.x] = s;
 }
 
+__device__ __forceinline__ double fma_t(double x, double a, double b) { return __builtin_fma(x, a, b); }
+__device__ __forceinline__ float fma_t(float x, float a, float b) { return __builtin_fmaf(x, a, b); }
+
 template <typename F>
 __global__ __launch_bounds__(kThreads) void k_fma(F *out, int iters, F a, F b) {
   F x[kChains];
@@ -52,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void k_fma(F *out, int iters, F a, F b) {
   for (int j = 0; j < kChains; ++j) x[j] = (F)(threadIdx.x + j);
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
-    for (int j = 0; j < kChains; ++j) x[j] = __builtin_fma(x[j], a, b);
+    for (int j = 0; j < kChains; ++j) x[j] = fma_t(x[j], a, b);
   }
   F s = 0;
 #pragma unroll
