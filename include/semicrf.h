@@ -57,7 +57,8 @@ typedef enum {
     SEMICRF_ERR_UNSUPPORTED = 3, /* C or K outside the supported sizes above */
     SEMICRF_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
     SEMICRF_ERR_HIP = 5,         /* a kernel launch failed */
-    SEMICRF_ERR_ARG = 6          /* unknown op or flag, negative checkpoint interval */
+    SEMICRF_ERR_ARG = 6,         /* unknown op or flag, negative checkpoint interval */
+    SEMICRF_ERR_SCRATCH = 7      /* semicrf_fwd_bwd_static: sizes beyond its scratch */
 } semicrf_status_t;
 
 /* operations, for semicrf_workspace_size */
@@ -161,6 +162,29 @@ semicrf_status_t semicrf_fwd_bwd_ex(const float *emissions, const int32_t *lengt
                                     float *grad_dur, float *marginals, float *boundary,
                                     void *workspace, size_t workspace_bytes, void *stream,
                                     void *const *phase_events);
+
+/* semicrf_fwd_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The workspace is a static
+ * device array of 64 MiB inside the library (SEMICRF_STATIC_SCRATCH_BYTES),
+ * which every GPU the library runs on holds until the process ends; its
+ * address is looked up once per device on the first call with that device
+ * current.  Sizes whose workspace (semicrf_workspace_size with op
+ * SEMICRF_OP_FWD_BWD) exceeds it return SEMICRF_ERR_SCRATCH before
+ * anything is launched (e.g. the NLP shape B=32 T=512 C=24 K=32 fits,
+ * T = 4096 with C = 256 does not).  The call allocates nothing: no
+ * hipMalloc, no hipFree, no allocating library routine.
+ * All calls on one GPU share its array and it keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap on
+ * one GPU -- concurrent streams or threads -- race and must be serialised
+ * by the caller.  Everything else is identical to semicrf_fwd_bwd. */
+enum { SEMICRF_STATIC_SCRATCH_BYTES = 64 << 20 };
+semicrf_status_t semicrf_fwd_bwd_static(const float *emissions, const int32_t *lengths,
+                                        const float *trans, const float *dur,
+                                        int B, int T, int C, int K, unsigned flags,
+                                        int checkpoint_interval, const float *grad_logz,
+                                        float *logz, float *grad_emissions, float *grad_trans,
+                                        float *grad_dur, float *marginals, void *stream);
 
 /* Score of a given labelled segmentation under the same model, and its
  * gradients: the second term of the training loss log Z - score(gold)

@@ -25,14 +25,15 @@ NO_CENTER = 1
 STATUS = {
     0: "SEMICRF_OK", 1: "SEMICRF_ERR_NULL", 2: "SEMICRF_ERR_SHAPE",
     3: "SEMICRF_ERR_UNSUPPORTED", 4: "SEMICRF_ERR_WORKSPACE", 5: "SEMICRF_ERR_HIP",
-    6: "SEMICRF_ERR_ARG",
+    6: "SEMICRF_ERR_ARG", 7: "SEMICRF_ERR_SCRATCH",
 }
+STATIC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = (
     "semicrf_status_string", "semicrf_default_checkpoint_interval", "semicrf_checkpoint_interval",
     "semicrf_workspace_size",
     "semicrf_cumulative_scores", "semicrf_logz_fwd", "semicrf_fwd_bwd", "semicrf_fwd_bwd_ex",
-    "semicrf_viterbi", "semicrf_path_score",
+    "semicrf_viterbi", "semicrf_path_score", "semicrf_fwd_bwd_static",
 )
 FWD_BWD_PHASES = ("cumulative_scores", "sweep_first", "sweep_rest", "posteriors", "reductions")
 
@@ -75,6 +76,8 @@ def load():
     lib.semicrf_path_score.argtypes = [P, P, P, P, I, I, I, I, U, P, P, P, P, P, P, P, P, P, P, Z,
                                        P]
     lib.semicrf_path_score.restype = I
+    lib.semicrf_fwd_bwd_static.argtypes = [P, P, P, P, I, I, I, I, U, I, P, P, P, P, P, P, P]
+    lib.semicrf_fwd_bwd_static.restype = I
     lib.semicrf_viterbi.argtypes = [P, P, P, P, I, I, I, I, U, P, P, P, P, P, P, Z, P]
     lib.semicrf_viterbi.restype = I
     _lib = lib
@@ -231,6 +234,32 @@ def semicrf_fwd_bwd(emissions, lengths, trans, dur, center: bool = True, grad_lo
     plan = FwdBwdPlan(emissions, lengths, trans, dur, center, grad_logz, checkpoint_interval,
                       want_marginals, want_boundary)
     return plan.run().outputs()
+
+
+def semicrf_fwd_bwd_static(emissions, lengths, trans, dur, center: bool = True, grad_logz=None,
+                           checkpoint_interval: int = 0, want_marginals: bool = False, out=None):
+    """semicrf_fwd_bwd on the library's static device scratch (no workspace
+    argument; see semicrf.h).  `out` may hold preallocated outputs (a dict as
+    returned), so that repeated calls allocate nothing on the torch side
+    either.  Returns dict(logz, grad_emissions, grad_trans, grad_dur[,
+    marginals])."""
+    B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
+    _check_weights("grad_logz", grad_logz, B, dev)
+    if out is None:
+        out = dict(logz=torch.empty(B, dtype=torch.float32, device=dev),
+                   grad_emissions=torch.empty((B, T, C), dtype=torch.float32, device=dev),
+                   grad_trans=torch.empty((C, C), dtype=torch.float32, device=dev),
+                   grad_dur=torch.empty((K, C), dtype=torch.float32, device=dev))
+        if want_marginals:
+            out["marginals"] = torch.empty((B, T, C), dtype=torch.float32, device=dev)
+    flags = 0 if center else NO_CENTER
+    rc = load().semicrf_fwd_bwd_static(
+        _ptr(emissions), _ptr(lengths), _ptr(trans), _ptr(dur), B, T, C, K, flags,
+        int(checkpoint_interval), _ptr(grad_logz), _ptr(out["logz"]), _ptr(out["grad_emissions"]),
+        _ptr(out["grad_trans"]), _ptr(out["grad_dur"]), _ptr(out.get("marginals")), _stream(dev))
+    if rc:
+        raise SemiCRFError(rc, "semicrf_fwd_bwd_static")
+    return out
 
 
 def _check_segments(segments, B, T, dev):

@@ -7,10 +7,19 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "../../include/semicrf.h"
 #include "internal.h"
 
 using namespace semicrf;
+
+// Device scratch of semicrf_fwd_bwd_static (for callers that cannot
+// allocate): a file-scope array each GPU holds once the library runs on it.
+// Host code never uses this name as an address (it is a host-side stand-in);
+// static_scratch() looks the device address up per device.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -296,6 +305,30 @@ PitBufs pit_bufs(void *ws, const Layout &lay, bool bwd) {
   return pb;
 }
 
+// The device address of `scratch` on the current device: looked up with
+// hipGetSymbolAddress on the first call with that device current, then
+// reused (each GPU holds its own copy of the array at its own address).
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+hipError_t static_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 // With SEMICRF_DEBUG set in the environment, name the HIP error on stderr.
 semicrf_status_t hip_status(hipError_t e) {
   if (e == hipSuccess) return SEMICRF_OK;
@@ -316,6 +349,9 @@ const char *semicrf_status_string(semicrf_status_t status) {
     case SEMICRF_ERR_WORKSPACE: return "workspace NULL or smaller than semicrf_workspace_size";
     case SEMICRF_ERR_HIP: return "HIP launch failed";
     case SEMICRF_ERR_ARG: return "invalid op, flags or checkpoint interval";
+    case SEMICRF_ERR_SCRATCH:
+      return "these sizes need more workspace than the 64 MiB static scratch of "
+             "semicrf_fwd_bwd_static";
   }
   return "unknown status";
 }
@@ -459,6 +495,32 @@ semicrf_status_t semicrf_fwd_bwd(const float *emissions, const int32_t *lengths,
   return semicrf_fwd_bwd_ex(emissions, lengths, trans, dur, B, T, C, K, flags,
                             checkpoint_interval, grad_logz, logz, grad_emissions, grad_trans,
                             grad_dur, marginals, nullptr, workspace, workspace_bytes, stream,
+                            nullptr);
+}
+
+semicrf_status_t semicrf_fwd_bwd_static(const float *emissions, const int32_t *lengths,
+                                        const float *trans, const float *dur, int B, int T,
+                                        int C, int K, unsigned flags, int checkpoint_interval,
+                                        const float *grad_logz, float *logz,
+                                        float *grad_emissions, float *grad_trans,
+                                        float *grad_dur, float *marginals, void *stream) {
+  if (!emissions || !lengths || !trans || !dur || !logz || !grad_emissions || !grad_trans ||
+      !grad_dur)
+    return SEMICRF_ERR_NULL;
+  ChainShape sh;
+  Layout lay;
+  const semicrf_status_t s =
+      prepare(SEMICRF_OP_FWD_BWD, B, T, C, K, flags, checkpoint_interval, sh, lay);
+  if (s != SEMICRF_OK) return s;
+  if (lay.total > kStaticScratchBytes) return SEMICRF_ERR_SCRATCH;
+  void *ws = nullptr;
+  const hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  // every kernel of the call writes the workspace before it reads it, so
+  // what an earlier call left there is never used
+  return semicrf_fwd_bwd_ex(emissions, lengths, trans, dur, B, T, C, K, flags,
+                            checkpoint_interval, grad_logz, logz, grad_emissions, grad_trans,
+                            grad_dur, marginals, nullptr, ws, kStaticScratchBytes, stream,
                             nullptr);
 }
 

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         assert len(bd.status_string(code)) >= 2
     assert bd.status_string(99) == "unknown status"
 
