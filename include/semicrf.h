@@ -72,7 +72,20 @@ enum {
 
 /* flags */
 enum {
-    SEMICRF_NO_CENTER = 1u << 0 /* nu = 0: the textbook, uncentred semi-CRF */
+    SEMICRF_NO_CENTER = 1u << 0,  /* nu = 0: the textbook, uncentred semi-CRF */
+    /* semicrf_fwd_bwd / _ex: working memory sublinear in T beyond the
+     * cumulative scores (abstract: checkpoint-boundary normalisation keeps
+     * working memory sublinear in sequence length; technical summary 2.C:
+     * forward messages recomputed between checkpoints).  The sweeps keep only
+     * the checkpoint records (default interval ceil(sqrt(T*K)), raised to K
+     * when smaller); the posterior pass then replays the intervals window by
+     * window from their exact records -- ceil(sqrt(#intervals)) intervals
+     * forward, one more backward (the durations reach past the window) --
+     * and consumes each window's messages before the next, so they take
+     * O(sqrt(T/interval) * interval * C) memory.  Slower (the windows run
+     * one after another); same results up to rounding.  Ignored by the other
+     * operations. */
+    SEMICRF_LOW_MEMORY = 1u << 1
 };
 
 /* Human-readable name of a status code (static string, never NULL). */

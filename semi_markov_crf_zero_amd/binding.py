@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libsemicrf.so")
 
 OP_SCAN, OP_LOGZ, OP_FWD_BWD, OP_VITERBI, OP_PATH_SCORE = 0, 1, 2, 3, 4
 NO_CENTER = 1
+LOW_MEMORY = 2  # fwd_bwd: checkpoint records only, posteriors replayed in windows
 
 STATUS = {
     0: "SEMICRF_OK", 1: "SEMICRF_ERR_NULL", 2: "SEMICRF_ERR_SHAPE",
@@ -178,12 +179,13 @@ class FwdBwdPlan:
     one shape (the benchmark times `run()` alone)."""
 
     def __init__(self, emissions, lengths, trans, dur, center=True, grad_logz=None,
-                 checkpoint_interval=0, want_marginals=False, want_boundary=False):
+                 checkpoint_interval=0, want_marginals=False, want_boundary=False,
+                 low_memory=False):
         B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
         _check_weights("grad_logz", grad_logz, B, dev)
         self.args = (emissions, lengths, trans, dur)
         self.B, self.T, self.C, self.K = B, T, C, K
-        self.flags = 0 if center else NO_CENTER
+        self.flags = (0 if center else NO_CENTER) | (LOW_MEMORY if low_memory else 0)
         self.ckpt = int(checkpoint_interval)
         self.grad_logz = grad_logz
         self.dev = dev
@@ -229,10 +231,12 @@ class FwdBwdPlan:
 
 def semicrf_fwd_bwd(emissions, lengths, trans, dur, center: bool = True, grad_logz=None,
                     checkpoint_interval: int = 0, want_marginals: bool = False,
-                    want_boundary: bool = False):
-    """Returns dict(logz, grad_emissions, grad_trans, grad_dur[, marginals][, boundary])."""
+                    want_boundary: bool = False, low_memory: bool = False):
+    """Returns dict(logz, grad_emissions, grad_trans, grad_dur[, marginals][, boundary]).
+    low_memory: keep only the checkpoint records and replay the intervals in
+    windows for the posteriors (SEMICRF_LOW_MEMORY)."""
     plan = FwdBwdPlan(emissions, lengths, trans, dur, center, grad_logz, checkpoint_interval,
-                      want_marginals, want_boundary)
+                      want_marginals, want_boundary, low_memory)
     return plan.run().outputs()
 
 

@@ -148,6 +148,16 @@ struct Carver {
   }
 };
 
+// Low-memory posterior windows: ceil(sqrt(nchunk)) forward chunks per
+// window, so the rows of a window (about sqrt(nchunk) * delta positions)
+// grow like T^(3/4) K^(1/4) with the default interval: sublinear in T, as the
+// records (nchunk rings of K x C) are.
+int lowmem_window(int nchunk) {
+  int w = 1;
+  while (w * w < nchunk) ++w;
+  return w;
+}
+
 // Workspace layout for an op.  Returns false for an invalid op.
 bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layout &lay,
                  const VShape *vs = nullptr) {
@@ -160,11 +170,6 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
   if (op != SEMICRF_OP_SCAN) {
     lay.S = cv.take(nS * 8);
     lay.nu = cv.take((size_t)B * C * 8);
-  }
-  if (op == SEMICRF_OP_LOGZ || op == SEMICRF_OP_FWD_BWD) {
-    lay.es_p = cv.take(nS * 8);
-    lay.es_m = cv.take(nS * 8);
-    lay.es_n = cv.take(nS * 4);
   }
   lay.tile_sum = cv.take((size_t)B * lay.ntile * C * 8);
   lay.anchor = cv.take((size_t)B * lay.ntile * C * 8);
@@ -190,17 +195,22 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
       lay.shift = cv.take(2 * nck * 8);
       if (!sh->win && sh->NT == 1024) lay.trw = cv.take(trw_floats(C, sh->QT) * 4);
       if (!bwd) break;
-      lay.row_a = cv.take(nS * 8);
-      lay.row_u = cv.take(nS * 8);
-      lay.row_v = cv.take(nS * 8);
-      lay.row_b = cv.take(nS * 8);
-      lay.pos_shift = cv.take((size_t)2 * B * (T + 1) * 8);
+      // rows of every position, or (low memory) of one window of chunks
+      const int rs = sh->lm_w ? (sh->lm_w + sh->lm_h) * sh->delta + 1 : T + 1;
+      const size_t nR = (size_t)B * rs * C;
+      lay.row_stride = rs;
+      lay.row_a = cv.take(nR * 8);
+      lay.row_u = cv.take(nR * 8);
+      lay.row_v = cv.take(nR * 8);
+      lay.row_b = cv.take(nR * 8);
+      if (!sh->lm_w) lay.pos_shift = cv.take((size_t)2 * B * (T + 1) * 8);
       PostGeom g;
-      post_geometry(*sh, g);
+      post_geometry(*sh, g, sh->lm_w ? sh->lm_w * sh->delta : T);
       lay.cov_part = cv.take((size_t)B * g.cov_ntile * C * 8);
       lay.cov_part2 = cv.take((size_t)B * g.cov_ntile * C * 8);
       lay.cov_anchor = cv.take((size_t)B * g.cov_ntile * C * 8);
       lay.cov_mean = cv.take((size_t)B * C * 8);
+      if (sh->lm_w) lay.cov_carry = cv.take((size_t)B * C * 8);
       lay.tx_part = cv.take((size_t)B * g.tx_nseg * C * C * 8);
       lay.dur_part = cv.take((size_t)B * g.dur_nspan * K * C * 8);
       break;
@@ -242,7 +252,7 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
 semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int ckpt,
                          ChainShape &sh, Layout &lay, VShape *vs_out = nullptr) {
   if (op < SEMICRF_OP_SCAN || op > SEMICRF_OP_PATH_SCORE) return SEMICRF_ERR_ARG;
-  if (flags & ~(unsigned)SEMICRF_NO_CENTER) return SEMICRF_ERR_ARG;
+  if (flags & ~(unsigned)(SEMICRF_NO_CENTER | SEMICRF_LOW_MEMORY)) return SEMICRF_ERR_ARG;
   if (ckpt < 0) return SEMICRF_ERR_ARG;
   const semicrf_status_t s = check_sizes(B, T, C, op == SEMICRF_OP_SCAN ? 1 : K);
   if (s != SEMICRF_OK) return s;
@@ -259,9 +269,23 @@ semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int
     ChainShape probe = sh;
     if (!chain_config(C, K, probe)) return SEMICRF_ERR_UNSUPPORTED;
     if (op == SEMICRF_OP_VITERBI || !win_config(C, K, sh)) sh = probe;
-    sh.delta = ckpt > 0 ? (ckpt < T ? ckpt : T) : effective_delta(B, T, K);
+    const bool lowmem = op == SEMICRF_OP_FWD_BWD && (flags & SEMICRF_LOW_MEMORY);
+    if (lowmem) {
+      // the pages' interval (no splitting for parallelism: the records are
+      // the working memory), at least K so one more backward chunk covers
+      // the durations that reach past a window
+      int d = ckpt > 0 ? ckpt : default_delta(T, K);
+      if (d < K) d = K;
+      sh.delta = d < T ? d : T;
+    } else {
+      sh.delta = ckpt > 0 ? (ckpt < T ? ckpt : T) : effective_delta(B, T, K);
+    }
     sh.nchunk = (T + sh.delta - 1) / sh.delta;
     sh.burn = burn_in(sh.delta, K);
+    if (lowmem) {
+      sh.lm_w = lowmem_window(sh.nchunk);
+      sh.lm_h = sh.nchunk > sh.lm_w ? 1 : 0;  // delta >= K: one chunk past the window
+    }
   }
   VShape vs;
   const bool pit = op == SEMICRF_OP_VITERBI && vit_config(B, T, C, K, vs);
@@ -278,9 +302,7 @@ P *at(void *ws, size_t off) {
 
 Escaled escaled(void *ws, const Layout &lay) {
   Escaled es;
-  es.ep = at<double>(ws, lay.es_p);
-  es.em = at<double>(ws, lay.es_m);
-  es.n = at<int32_t>(ws, lay.es_n);
+  es.S = at<double>(ws, lay.S);
   return es;
 }
 
@@ -300,7 +322,9 @@ PitBufs pit_bufs(void *ws, const Layout &lay, bool bwd) {
   pb.row_u = bwd ? at<double>(ws, lay.row_u) : nullptr;
   pb.row_v = bwd ? at<double>(ws, lay.row_v) : nullptr;
   pb.row_b = bwd ? at<double>(ws, lay.row_b) : nullptr;
-  pb.pos_shift = bwd ? at<double>(ws, lay.pos_shift) : nullptr;
+  pb.pos_shift = bwd && lay.pos_shift ? at<double>(ws, lay.pos_shift) : nullptr;
+  pb.row_t0 = 0;
+  pb.row_stride = lay.row_stride;
   pb.trw = lay.trw ? at<float>(ws, lay.trw) : nullptr;
   return pb;
 }
@@ -410,8 +434,7 @@ semicrf_status_t semicrf_logz_fwd(const float *emissions, const int32_t *lengths
   double *S = at<double>(workspace, lay.S);
   const Escaled es = escaled(workspace, lay);
   hipError_t e = launch_scan(emissions, lengths, B, T, C, sh.center, at<double>(workspace, lay.nu),
-                             S, at<double>(workspace, lay.es_p), at<double>(workspace, lay.es_m),
-                             at<int32_t>(workspace, lay.es_n), at<double>(workspace, lay.tile_sum),
+                             S, nullptr, nullptr, nullptr, at<double>(workspace, lay.tile_sum),
                              at<double>(workspace, lay.anchor), lay.ntile, lay.scan_j, st);
   if (e != hipSuccess) return hip_status(e);
   e = run_sweeps(sh, trans, dur, es, lengths, pit_bufs(workspace, lay, false),
@@ -444,13 +467,17 @@ semicrf_status_t semicrf_fwd_bwd_ex(const float *emissions, const int32_t *lengt
   double *S = at<double>(ws, lay.S);
   mark(0);
   hipError_t e = launch_scan(emissions, lengths, B, T, C, sh.center, at<double>(ws, lay.nu), S,
-                             at<double>(ws, lay.es_p), at<double>(ws, lay.es_m),
-                             at<int32_t>(ws, lay.es_n), at<double>(ws, lay.tile_sum),
+                             nullptr, nullptr, nullptr, at<double>(ws, lay.tile_sum),
                              at<double>(ws, lay.anchor), lay.ntile, lay.scan_j, st);
   if (e != hipSuccess) return hip_status(e);
   mark(1);
-  e = run_sweeps(sh, trans, dur, escaled(ws, lay), lengths, pit_bufs(ws, lay, true),
-                 at<double>(ws, lay.logz), at<double>(ws, lay.logz_bwd), logz, 1, st,
+  const bool lowmem = sh.lm_w > 0;
+  PitBufs pb = pit_bufs(ws, lay, true);
+  if (lowmem) {  // the sweeps keep the checkpoint records only
+    pb.row_a = pb.row_u = pb.row_v = pb.row_b = nullptr;
+  }
+  e = run_sweeps(sh, trans, dur, escaled(ws, lay), lengths, pb, at<double>(ws, lay.logz),
+                 at<double>(ws, lay.logz_bwd), logz, 1, st,
                  phase_events ? static_cast<hipEvent_t>(phase_events[2]) : nullptr);
   if (e != hipSuccess) return hip_status(e);
   mark(3);
@@ -465,7 +492,15 @@ semicrf_status_t semicrf_fwd_bwd_ex(const float *emissions, const int32_t *lengt
   pa.row_u = at<double>(ws, lay.row_u);
   pa.row_v = at<double>(ws, lay.row_v);
   pa.row_b = at<double>(ws, lay.row_b);
-  pa.pos_shift = at<double>(ws, lay.pos_shift);
+  pa.pos_shift = lay.pos_shift ? at<double>(ws, lay.pos_shift) : nullptr;
+  pa.t_lo = 0;
+  pa.t_hi = T;
+  pa.row_t0 = 0;
+  pa.row_stride = lay.row_stride;
+  pa.geom_T = lowmem ? sh.lm_w * sh.delta : T;
+  pa.accumulate = 0;
+  pa.defer_mean = 0;
+  pa.cov_carry = lay.cov_carry ? at<double>(ws, lay.cov_carry) : nullptr;
   pa.cov_part = at<double>(ws, lay.cov_part);
   pa.cov_part2 = at<double>(ws, lay.cov_part2);
   pa.cov_anchor = at<double>(ws, lay.cov_anchor);
@@ -477,8 +512,35 @@ semicrf_status_t semicrf_fwd_bwd_ex(const float *emissions, const int32_t *lengt
   pa.grad_trans = grad_trans;
   pa.grad_dur = grad_dur;
   pa.boundary = boundary;
-  e = launch_posteriors(sh, pa, st);
-  if (e != hipSuccess) return hip_status(e);
+  if (!lowmem) {
+    e = launch_posteriors(sh, pa, st);
+    if (e != hipSuccess) return hip_status(e);
+  } else {
+    // windows of lm_w checkpoint intervals, in order: replay the window's
+    // intervals (and lm_h more backward ones) from their exact records into
+    // the row buffers, then the window's posteriors, which continue the
+    // coverage sum and add to the partials of the windows before
+    const Escaled es = escaled(ws, lay);
+    PitBufs rb = pit_bufs(ws, lay, true);
+    pa.defer_mean = 1;
+    for (int j0 = 0, w = 0; j0 < sh.nchunk; j0 += sh.lm_w, ++w) {
+      ChainShape rs = sh;
+      rs.rj0 = j0;
+      rs.rnf = sh.lm_w < sh.nchunk - j0 ? sh.lm_w : sh.nchunk - j0;
+      rs.rnb = sh.lm_w + sh.lm_h < sh.nchunk - j0 ? sh.lm_w + sh.lm_h : sh.nchunk - j0;
+      rb.row_t0 = j0 * sh.delta;
+      e = launch_sweep(rs, trans, dur, es, lengths, rb, 1, -1, st);
+      if (e != hipSuccess) return hip_status(e);
+      pa.t_lo = j0 * sh.delta;
+      pa.t_hi = (j0 + rs.rnf) * sh.delta < T ? (j0 + rs.rnf) * sh.delta : T;
+      pa.row_t0 = pa.t_lo;
+      pa.accumulate = w > 0;
+      e = launch_posteriors(sh, pa, st);
+      if (e != hipSuccess) return hip_status(e);
+    }
+    e = launch_mean_fix(sh, pa, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
   mark(4);
   e = launch_post_reduce(sh, pa, st);
   if (e != hipSuccess) return hip_status(e);

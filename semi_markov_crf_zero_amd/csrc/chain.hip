@@ -387,20 +387,28 @@ __device__ __forceinline__ void load_ckpt(const double *__restrict__ src, const 
   __syncthreads();
 }
 
-// Split scores of position t for label c (row / chain lanes; other lanes
-// read label 0), in the order the direction uses them: fx multiplies the
-// K-sum (exp(S) forward, exp(-S) backward), fy the contraction (the other
-// one), n is the exponent (its sign is applied where it is used).  t is
-// clamped into [0, T], so every lane loads from a valid address and no
-// select touches the loaded values: the loads stay in flight until their
-// first use several positions later (a prefetch).
+// Cumulative score of position t for label c (row / chain lanes; other
+// lanes read label 0).  t is clamped into [0, T], so every lane loads from a
+// valid address and no select touches the loaded value: the load stays in
+// flight until its first use (a prefetch).
+__device__ __forceinline__ double es_raw(const Escaled &es, size_t ob, int t, int T, int C, int c) {
+  const int tc = t < 0 ? 0 : (t > T ? T : t);
+  return es.S[ob + (size_t)tc * C + (c < C ? c : 0)];
+}
+
+// The split of a score in the order the direction uses it: fx multiplies
+// the K-sum (exp(S) forward, exp(-S) backward), fy the contraction (the
+// other one), n is the exponent (its sign is applied where it is used).
+__device__ __forceinline__ void es_split(double s, bool fwd, double &fx, double &fy, int &n) {
+  double ep, em;
+  exp_split(s, ep, em, n);
+  fx = fwd ? ep : em;
+  fy = fwd ? em : ep;
+}
+
 __device__ __forceinline__ void es_get(const Escaled &es, size_t ob, int t, int T, int C, int c,
                                        bool fwd, double &fx, double &fy, int &n) {
-  const int tc = t < 0 ? 0 : (t > T ? T : t);
-  const size_t i = ob + (size_t)tc * C + (c < C ? c : 0);
-  fx = (fwd ? es.ep : es.em)[i];
-  fy = (fwd ? es.em : es.ep)[i];
-  n = es.n[i];
+  es_split(es_raw(es, ob, t, T, C, c), fwd, fx, fy, n);
 }
 
 // Log rows from a step's staged values (stg: x[C], E[C], d[C], B), rows
@@ -430,31 +438,35 @@ enum ChainRole { kRowRole = 0, kLoadRole = 1, kWriteRole = 2 };
 
 // Loader: the split scores of the prefetch block starting at step s (steps
 // s .. s+pf-1, positions tstart + isig*step) for every label, pf*C pairs
-// over the loader lanes, at most kMaxPairs each.
+// over the loader lanes, at most kMaxPairs each.  issue() only loads the
+// scores; put() -- a block later -- splits and stores them.
 struct PfLoad {
-  double fx[kMaxPairs], fy[kMaxPairs];
-  int n[kMaxPairs];
+  double sv[kMaxPairs];
 
   __device__ __forceinline__ void issue(const Escaled &es, size_t ob, const ChainShape &sh,
-                                        int tstart, int isig, int s, int lid, bool fwd) {
+                                        int tstart, int isig, int s, int lid) {
 #pragma unroll
     for (int k = 0; k < kMaxPairs; ++k) {
       const int q = lid + 64 * sh.nload * k;  // pair (i, c) = (q / C, q % C)
       const bool in = q < sh.pf * sh.C;
       const int i = in ? q / sh.C : 0, c = in ? q % sh.C : 0;
-      es_get(es, ob, tstart + isig * (s + i), sh.T, sh.C, c, fwd, fx[k], fy[k], n[k]);
+      sv[k] = es_raw(es, ob, tstart + isig * (s + i), sh.T, sh.C, c);
     }
   }
 
-  __device__ __forceinline__ void put(const Smem &sm, const ChainShape &sh, int buf, int lid) const {
+  __device__ __forceinline__ void put(const Smem &sm, const ChainShape &sh, int buf, int lid,
+                                      bool fwd) const {
 #pragma unroll
     for (int k = 0; k < kMaxPairs; ++k) {
       const int q = lid + 64 * sh.nload * k;
       if (q < sh.pf * sh.C) {
         const int o = buf * sh.pf * sh.C + q;  // [buf][i][c], q = i*C + c
-        sm.efx[o] = fx[k];
-        sm.efy[o] = fy[k];
-        sm.en[o] = n[k];
+        double fx, fy;
+        int n;
+        es_split(sv[k], fwd, fx, fy, n);
+        sm.efx[o] = fx;
+        sm.efy[o] = fy;
+        sm.en[o] = n;
       }
     }
   }
@@ -474,7 +486,7 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
                                            const Regs<AMAX, TRMAX, DT> &r, const Escaled &es,
                                            size_t ob, int tb, int nsteps, int wb,
                                            double *rec_start, bool fwd, bool tail, bool rows,
-                                           double *row1, double *row2, const float *trw,
+                                           double *row1, double *row2, int rt0, const float *trw,
                                            int &R, double &o_end, double &m_end, double &lz) {
   const int tid = threadIdx.x, C = sh.C;
   const bool is_row = tid < C;
@@ -506,7 +518,7 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
     }
     const bool next_blk = pf > 0 && step - 1 - i + pf < nsteps;  // a block follows this one
     if (ROLE == kLoadRole && i == 0 && next_blk)
-      ld.issue(es, ob, sh, tstart, isig, step + pf, lid, fwd);
+      ld.issue(es, ob, sh, tstart, isig, step + pf, lid);
     double nogd[AMAX];
     double first = 0.0;  // the thread's first term (the row threads': duration 1, the newest entry)
     const double s = r.kp < sh.P ? ksum<false>(r, sm, sh, t, fwd, nogd, 0.0, first) : 0.0;
@@ -524,7 +536,7 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
     const bool last = step == nsteps;
     const bool lz_step = last && tail;
     const double *sprev = sm.stg + ((step - 1) & 1) * (3 * C + 1);
-    const size_t tprev = (size_t)(t - isig) * C;
+    const size_t tprev = (size_t)(t - isig - rt0) * C;  // rows are window-relative
     // exp(o) = x * 2^E, o = alpha (forward) or v (backward)
     double x = 0.0;
     int E = 0;
@@ -586,7 +598,7 @@ __device__ __forceinline__ void sweep_loop(const ChainShape &sh, const Smem &sm,
     }
     // the next block's scores land in the other buffer before the next
     // step's first barrier, after which the row threads read them
-    if (ROLE == kLoadRole && i == pf - 1 && next_blk) ld.put(sm, sh, buf ^ 1, lid);
+    if (ROLE == kLoadRole && i == pf - 1 && next_blk) ld.put(sm, sh, buf ^ 1, lid, fwd);
     if (last || step == wb) {  // a record follows: the ring made whole now
       __syncthreads();
       if (vote[step & 1]) {
@@ -609,9 +621,22 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
                                               int iter) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int nck = sh.B * sh.nchunk;
-  const bool fwd = (int)blockIdx.x < nck;
-  const int rem = fwd ? blockIdx.x : blockIdx.x - nck;
-  const int b = rem / sh.nchunk, jc = rem % sh.nchunk;
+  const bool replay = iter < 0;  // a window of chunks swept again from exact records
+  bool fwd;
+  int b, jc;
+  if (replay) {
+    const int nf = sh.B * sh.rnf;
+    fwd = (int)blockIdx.x < nf;
+    const int nj = fwd ? sh.rnf : sh.rnb;
+    const int rem = fwd ? blockIdx.x : blockIdx.x - nf;
+    b = rem / nj;
+    jc = sh.rj0 + rem % nj;
+  } else {
+    fwd = (int)blockIdx.x < nck;
+    const int rem = fwd ? blockIdx.x : blockIdx.x - nck;
+    b = rem / sh.nchunk;
+    jc = rem % sh.nchunk;
+  }
   const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + jc;
   if (iter == 0) {  // the parallel-in-time state, before any verification reads it
     if (threadIdx.x == 0) {
@@ -625,11 +650,12 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
   const int L = lengths[b];
   const int tid = threadIdx.x, C = sh.C, K = sh.K;
   const bool is_row = tid < C;
-  if (L < 1 || L > sh.T) return;
+  if (L < 1 || L > sh.T || jc >= sh.nchunk) return;
   const int p0 = jc * sh.delta;
   if (p0 >= L) return;
   const int p1 = min(p0 + sh.delta, L);
   if (iter > 0 && (pb.nbad[iter - 1] == 0 || pb.redo[idx] == 0)) return;
+  const int rt0 = pb.row_t0;
   Smem sm = carve(lds, sh);
   for (int i = tid; i < kErowPad; i += NT) sm.erow[sh.C + i] = 0.0;
   Regs<AMAX, TRMAX, DT> r;
@@ -644,8 +670,9 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
   const int tstart = fwd ? p0 : p1;
   const bool tail = fwd ? (p1 == L) : (p0 == 0);  // this chunk ends the chain
   const bool rows = pb.row_a != nullptr;
-  double *row1 = (fwd ? pb.row_a : pb.row_v) + ob;  // alpha / v
-  double *row2 = (fwd ? pb.row_u : pb.row_b) + ob;  // u / beta
+  const size_t orow = (size_t)b * pb.row_stride * C;
+  double *row1 = rows ? (fwd ? pb.row_a : pb.row_v) + orow : nullptr;  // alpha / v
+  double *row2 = rows ? (fwd ? pb.row_u : pb.row_b) + orow : nullptr;  // u / beta
 
   int R = 0;
   // burn-in of a chunk without an exact start at iteration 0 (see chain_win.hip)
@@ -659,10 +686,9 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
       // entry u[0] - S[0] = 0 forward; beta[L] + S[L] = S[L] backward
       if (is_row) {
         double v = 1.0;
-        if (!fwd) {
-          const size_t i = ob + (size_t)L * C + tid;
-          v = es.ep[i];
-          R = es.n[i];
+        if (!fwd) {  // exp(S[L]) = ep * 2^n
+          double em;
+          exp_split(es.S[ob + (size_t)L * C + tid], v, em, R);
         }
         sm.ring[(tstart % K) * C + tid] = v;
       }
@@ -681,11 +707,18 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
       save_ckpt(rec_start, sm, sh, R, exact ? -__builtin_huge_val() : __builtin_nan(""),
                 exact ? 0.0 : __builtin_nan(""));
     if (exact && is_row && rows)  // u[0] = 0 forward, beta[L] = 0 backward
-      row2[(size_t)tstart * C + tid] = 0.0;
+      row2[(size_t)(tstart - rt0) * C + tid] = 0.0;
     __syncthreads();
   } else {
     double o0, m0;
     load_ckpt(rec_start, sm, sh, R, o0, m0);
+    // a replay window's first row (its chunk before is not swept again): the
+    // record's exact outputs at the start position
+    if (replay && rows && is_row &&
+        (fwd ? jc == sh.rj0 : (jc == sh.rj0 + sh.rnb - 1 || p1 == L))) {
+      row1[(size_t)(tstart - rt0) * C + tid] = o0;
+      row2[(size_t)(tstart - rt0) * C + tid] = m0;
+    }
   }
   const int nsteps = wb + (p1 - p0);
   if (sh.pf > 0) {  // the first block's scores (later blocks: the loader waves)
@@ -710,21 +743,23 @@ __global__ __launch_bounds__(NT) void k_sweep(ChainShape sh, const float *__rest
   const int w = tid >> 6;
   if (w < sh.Q)
     sweep_loop<kRowRole, NT>(sh, sm, r, es, ob, tb, nsteps, wb, rec_start, fwd, tail, rows,
-                             row1, row2, trw, R, o_end, m_end, lz);
+                             row1, row2, rt0, trw, R, o_end, m_end, lz);
   else if (w < sh.Q + sh.nload)
     sweep_loop<kLoadRole, NT>(sh, sm, r, es, ob, tb, nsteps, wb, rec_start, fwd, tail, rows,
-                              row1, row2, trw, R, o_end, m_end, lz);
+                              row1, row2, rt0, trw, R, o_end, m_end, lz);
   else
     sweep_loop<kWriteRole, NT>(sh, sm, r, es, ob, tb, nsteps, wb, rec_start, fwd, tail, rows,
-                               row1, row2, trw, R, o_end, m_end, lz);
-  if (tail) {
-    if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
-  } else {
-    save_ckpt(rec_end, sm, sh, R, o_end, m_end);
+                               row1, row2, rt0, trw, R, o_end, m_end, lz);
+  if (!replay) {
+    if (tail) {
+      if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
+    } else {
+      save_ckpt(rec_end, sm, sh, R, o_end, m_end);
+    }
   }
   if (rows) {  // rows of the last step (t = p1 forward, p0 backward)
     __syncthreads();
-    const size_t tl = (size_t)(fwd ? p1 : p0) * C;
+    const size_t tl = (size_t)((fwd ? p1 : p0) - rt0) * C;
     stage_rows(sm.stg + (nsteps & 1) * (3 * C + 1), C, row1 + tl, row2 + tl, 0,
                tail ? C : 2 * C, 0, NT);
   }
@@ -785,8 +820,9 @@ struct ChainKernels {
     set_attrs();
     if (!lds_fits((const void *)k_sweep<NT, AMAX, TRMAX, DT>, lds))
       return report(hipErrorInvalidConfiguration, "k_sweep (LDS)", sh, lds);
-    hipLaunchKernelGGL((k_sweep<NT, AMAX, TRMAX, DT>), dim3((with_bwd ? 2 : 1) * sh.B * sh.nchunk),
-                       dim3(NT), lds, st, sh, trans, dur, es, lengths, pb, iter);
+    const int grid = iter < 0 ? sh.B * (sh.rnf + sh.rnb) : (with_bwd ? 2 : 1) * sh.B * sh.nchunk;
+    hipLaunchKernelGGL((k_sweep<NT, AMAX, TRMAX, DT>), dim3(grid), dim3(NT), lds, st, sh, trans,
+                       dur, es, lengths, pb, iter);
     return report(hipGetLastError(), "k_sweep", sh, lds);
   }
 };

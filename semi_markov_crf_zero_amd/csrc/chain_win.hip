@@ -327,18 +327,26 @@ __device__ __forceinline__ void wload(const double *__restrict__ src, const WSme
   }
 }
 
-// Split scores of position t for label c (other lanes read label 0), in the
-// order the direction uses them: fx multiplies the K-sum (exp(S) forward,
-// exp(-S) backward), fy the contraction (the other one), n is the exponent
-// (its sign is applied where it is used).  t is clamped into [0, T], so
-// every lane loads from a valid address.
+// Cumulative score of position t for label c (other lanes read label 0);
+// t is clamped into [0, T], so every lane loads from a valid address.
+__device__ __forceinline__ double es_raw(const Escaled &es, size_t ob, int t, int T, int C, int c) {
+  const int tc = t < 0 ? 0 : (t > T ? T : t);
+  return es.S[ob + (size_t)tc * C + (c < C ? c : 0)];
+}
+
+// Its split in the order the direction uses it: fx multiplies the K-sum
+// (exp(S) forward, exp(-S) backward), fy the contraction (the other one), n
+// is the exponent (its sign is applied where it is used).
+__device__ __forceinline__ void es_split(double s, bool fwd, double &fx, double &fy, int &n) {
+  double ep, em;
+  exp_split(s, ep, em, n);
+  fx = fwd ? ep : em;
+  fy = fwd ? em : ep;
+}
+
 __device__ __forceinline__ void es_get(const Escaled &es, size_t ob, int t, int T, int C, int c,
                                        bool fwd, double &fx, double &fy, int &n) {
-  const int tc = t < 0 ? 0 : (t > T ? T : t);
-  const size_t i = ob + (size_t)tc * C + (c < C ? c : 0);
-  fx = (fwd ? es.ep : es.em)[i];
-  fy = (fwd ? es.em : es.ep)[i];
-  n = es.n[i];
+  es_split(es_raw(es, ob, t, T, C, c), fwd, fx, fy, n);
 }
 
 // Per-position log rows of a block's staged values: stg = [U][x[C], E[C],
@@ -365,28 +373,31 @@ __device__ __forceinline__ void block_rows(const double *stg, int C, int nb, int
 // 64 lanes.
 struct BlockLoad {
   static constexpr int NP = (U * 32 + 63) / 64;
-  double fx[NP], fy[NP];
-  int n[NP];
+  double sv[NP];
 
+  // the scores only; put() splits and stores them a block later
   __device__ __forceinline__ void issue(const Escaled &es, size_t ob, int first, int sigma,
-                                        int s0, int T, int C, int lane, bool fwd) {
+                                        int s0, int T, int C, int lane) {
 #pragma unroll
     for (int k = 0; k < NP; ++k) {
       const int q = lane + 64 * k;  // pair (i, c) = (q / C, q % C)
       const int i = q < U * C ? q / C : 0, c = q < U * C ? q % C : 0;
-      es_get(es, ob, first + sigma * (s0 + i), T, C, c, fwd, fx[k], fy[k], n[k]);
+      sv[k] = es_raw(es, ob, first + sigma * (s0 + i), T, C, c);
     }
   }
 
-  __device__ __forceinline__ void put(const WSmem &sm, int buf, int C, int lane) const {
+  __device__ __forceinline__ void put(const WSmem &sm, int buf, int C, int lane, bool fwd) const {
 #pragma unroll
     for (int k = 0; k < NP; ++k) {
       const int q = lane + 64 * k;
       if (q < U * C) {
         const int o = buf * U * C + q;  // [buf][i][c], q = i*C + c
-        sm.efx[o] = fx[k];
-        sm.efy[o] = fy[k];
-        sm.en[o] = n[k];
+        double fx, fy;
+        int n;
+        es_split(sv[k], fwd, fx, fy, n);
+        sm.efx[o] = fx;
+        sm.efy[o] = fy;
+        sm.en[o] = n;
       }
     }
   }
@@ -566,9 +577,22 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
                                                 int iter) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int nck = sh.B * sh.nchunk;
-  const bool fwd = (int)blockIdx.x < nck;
-  const int rem = fwd ? blockIdx.x : blockIdx.x - nck;
-  const int b = rem / sh.nchunk, jc = rem % sh.nchunk;
+  const bool replay = iter < 0;  // a window of chunks swept again from exact records
+  bool fwd;
+  int b, jc;
+  if (replay) {
+    const int nf = sh.B * sh.rnf;
+    fwd = (int)blockIdx.x < nf;
+    const int nj = fwd ? sh.rnf : sh.rnb;
+    const int rem = fwd ? blockIdx.x : blockIdx.x - nf;
+    b = rem / nj;
+    jc = sh.rj0 + rem % nj;
+  } else {
+    fwd = (int)blockIdx.x < nck;
+    const int rem = fwd ? blockIdx.x : blockIdx.x - nck;
+    b = rem / sh.nchunk;
+    jc = rem % sh.nchunk;
+  }
   const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + jc;
   if (iter == 0) {  // the parallel-in-time state, before any verification reads it
     if (threadIdx.x == 0) {
@@ -585,7 +609,7 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   const bool chain = tid < C;  // lanes of wave 0
   // (the iteration flags are loaded with the length: one memory wait)
   const int nbad = iter > 0 ? pb.nbad[iter - 1] : 1, redo = iter > 0 ? pb.redo[idx] : 1;
-  if (L < 1 || L > T) return;
+  if (L < 1 || L > T || jc >= sh.nchunk) return;
   const int p0 = jc * sh.delta;
   if (p0 >= L) return;
   const int p1 = min(p0 + sh.delta, L);
@@ -610,8 +634,10 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   const int tstart = fwd ? p0 : p1;
   const bool tail = fwd ? (p1 == L) : (p0 == 0);  // this chunk ends the chain
   const bool rows = pb.row_a != nullptr;
-  double *row1 = (fwd ? pb.row_a : pb.row_v) + ob;  // alpha / v
-  double *row2 = (fwd ? pb.row_u : pb.row_b) + ob;  // u / beta
+  const int rt0 = pb.row_t0;  // rows are written relative to the window start
+  const size_t orow = (size_t)b * pb.row_stride * C;
+  double *row1 = rows ? (fwd ? pb.row_a : pb.row_v) + orow : nullptr;  // alpha / v
+  double *row2 = rows ? (fwd ? pb.row_u : pb.row_b) + orow : nullptr;  // u / beta
 
   int R = 0;  // integer log reference of label `lane` (units of ln2)
   // Burn-in: at iteration 0 a chunk without an exact start begins wb
@@ -634,10 +660,9 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
       // entry u[0] - S[0] = 0 forward; beta[L] + S[L] = S[L] backward
       if (chain) {
         double v = 1.0;
-        if (!fwd) {
-          const size_t i = ob + (size_t)L * C + lane;
-          v = es.ep[i];
-          R = es.n[i];
+        if (!fwd) {  // exp(S[L]) = ep * 2^n
+          double em;
+          exp_split(es.S[ob + (size_t)L * C + lane], v, em, R);
         }
         ring_put(sm, K, C, pos_slot(tstart, K), lane, v);
       }
@@ -656,10 +681,17 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
       wsave(rec_start, sm, sh, chain, lane, R,
             exact ? -__builtin_huge_val() : __builtin_nan(""), exact ? 0.0 : __builtin_nan(""), NT);
     if (exact && chain && rows)  // u[0] = 0 forward, beta[L] = 0 backward
-      row2[(size_t)tstart * C + lane] = 0.0;
+      row2[(size_t)(tstart - rt0) * C + lane] = 0.0;
   } else {
     double o0, m0;
     wload(rec_start, sm, sh, chain, lane, R, o0, m0, NT);
+    // a replay window's first row (its chunk before is not swept again): the
+    // record's exact outputs at the start position
+    if (replay && rows && chain &&
+        (fwd ? jc == sh.rj0 : (jc == sh.rj0 + sh.rnb - 1 || p1 == L))) {
+      row1[(size_t)(tstart - rt0) * C + lane] = o0;
+      row2[(size_t)(tstart - rt0) * C + lane] = m0;
+    }
   }
   const int first = tbegin + sigma;
   const int nsteps = wb + (p1 - p0);
@@ -716,10 +748,10 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
       chain_block<CMAX>(sh, sm, G, s0, nb, nsteps, t0, sigma, buf, tail, lane, chain, Dn, tr,
                         wb - 1, cs, R, Bm, o_rec, m_rec, o_end, m_end, lz);
     } else {
-      if (w == 1 && more) bl.issue(es, ob, first, sigma, s0 + U, T, C, lane, fwd);
+      if (w == 1 && more) bl.issue(es, ob, first, sigma, s0 + U, T, C, lane);
       if (w >= 2 && rows && s0 > wb) {
         // the previous block's rows (a full block of U steps, past the burn-in)
-        block_rows(sm.stg + (buf ^ 1) * U * S, C, U, t0 - sigma * U, sigma, row1, row2, -1, 128,
+        block_rows(sm.stg + (buf ^ 1) * U * S, C, U, t0 - sigma * U - rt0, sigma, row1, row2, -1, 128,
                    NT - 128);
       }
       if (more) {
@@ -731,7 +763,7 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
       }
       // the next block's scores land in the other buffer before the barrier
       // that ends this block
-      if (w == 1 && more) bl.put(sm, buf ^ 1, C, lane);
+      if (w == 1 && more) bl.put(sm, buf ^ 1, C, lane, fwd);
     }
     __syncthreads();
     if (sm.flag[0]) {
@@ -754,15 +786,17 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
       __syncthreads();
     }
   }
-  if (tail) {
-    if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
-  } else {
-    wsave(rec_end, sm, sh, chain, lane, R, o_end, m_end, NT);
+  if (!replay) {
+    if (tail) {
+      if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
+    } else {
+      wsave(rec_end, sm, sh, chain, lane, R, o_end, m_end, NT);
+    }
   }
   if (rows) {  // rows of the last block
     const int s0 = (nsteps - 1) / U * U;
-    block_rows(sm.stg + ((s0 / U) & 1) * U * (3 * C + 1), C, nsteps - s0, first + sigma * s0,
-               sigma, row1, row2, tail ? nsteps - 1 - s0 : -1, 0, NT);
+    block_rows(sm.stg + ((s0 / U) & 1) * U * (3 * C + 1), C, nsteps - s0,
+               first + sigma * s0 - rt0, sigma, row1, row2, tail ? nsteps - 1 - s0 : -1, 0, NT);
   }
 }
 
@@ -792,8 +826,9 @@ struct WinKernels {
     const size_t lds = win_lds_bytes(sh.C, sh.K, sh.P);
     if (!lds_fits((const void *)k_sweep_w<NT, CMAX, DCH>, lds))
       return wreport(hipErrorInvalidConfiguration, "k_sweep_w (LDS)", sh, lds);
-    hipLaunchKernelGGL((k_sweep_w<NT, CMAX, DCH>), dim3((with_bwd ? 2 : 1) * sh.B * sh.nchunk),
-                       dim3(NT), lds, st, sh, trans, dur, es, lengths, pb, iter);
+    const int grid = iter < 0 ? sh.B * (sh.rnf + sh.rnb) : (with_bwd ? 2 : 1) * sh.B * sh.nchunk;
+    hipLaunchKernelGGL((k_sweep_w<NT, CMAX, DCH>), dim3(grid), dim3(NT), lds, st, sh, trans,
+                       dur, es, lengths, pb, iter);
     return wreport(hipGetLastError(), "k_sweep_w", sh, lds);
   }
 };

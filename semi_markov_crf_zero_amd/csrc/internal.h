@@ -29,6 +29,14 @@ struct ChainShape {
   int delta;   // checkpoint interval (positions)
   int nchunk;  // ceil(T / delta) chunks per sequence
   int center;  // 1 = subtract the per-label baseline nu
+  // Replay (sweep launches with iteration -1): chunks rj0 .. rj0+rnf-1
+  // forward and rj0 .. rj0+rnb-1 backward of every sequence, each swept once
+  // from its exact checkpoint record, writing rows only (no records).
+  int rj0, rnf, rnb;
+  // Low-memory fwd+bwd: the posterior pass works in windows of lm_w chunks,
+  // each replayed with lm_h more backward chunks (the segments that start in
+  // the window end up to K positions past it); 0 when the rows are kept.
+  int lm_w, lm_h;
 };
 
 constexpr int kMaxC = 256;
@@ -153,10 +161,11 @@ __host__ __device__ inline size_t win_lds_bytes(int C, int K, int P) {
 
 // Workspace layout (byte offsets, 256-aligned).
 struct Layout {
-  size_t S, es_p, es_m, es_n, nu, tile_sum, anchor, logz, logz_bwd;
+  size_t S, nu, tile_sum, anchor, logz, logz_bwd;
   size_t ck_fwd, ck_bwd, end_fwd, end_bwd, redo, corr_i, corr_f, nbad, lz_part, shift, pos_shift;
   size_t row_a, row_u, row_v, row_b;
-  size_t cov_part, cov_part2, cov_anchor, cov_mean, tx_part, dur_part, trw;
+  size_t cov_part, cov_part2, cov_anchor, cov_mean, cov_carry, tx_part, dur_part, trw;
+  int row_stride;  // rows per sequence in the row buffers
   size_t bp, vbest, vcbest;
   size_t p_score, p_valid, p_cnt, p_lab;
   size_t v_pred, v_rr, v_re, v_corr, v_delta, v_redo, v_nbad, v_lst_t, v_lst_c, v_mark, v_sub;
@@ -194,7 +203,24 @@ struct PostArgs {
   double *dur_part;                                      // [B][dur_nspan][K][C]
   float *grad_emissions, *marginals, *grad_trans, *grad_dur;
   float *boundary;  // [B][T] P(a segment starts at t), or NULL
+  // The positions of this pass, [t_lo, t_hi) (0, T: all), and the row
+  // geometry (as PitBufs: row t at ((b * row_stride) + t - row_t0) * C).
+  // pos_shift NULL: the rows are exact (replayed from exact records).
+  int t_lo, t_hi, row_t0, row_stride;
+  int geom_T;  // positions the launch geometry and partial slots are sized for
+  // Windowed passes (positions in several consecutive windows): the
+  // partials of every window after the first add to the earlier ones
+  // (accumulate), the coverage continues from cov_carry [B][C] (the running
+  // sum of all earlier windows, updated in place), cov_mean accumulates, and
+  // the emission gradients are written as w * mu with the centring term
+  // subtracted after the last window (defer_mean).
+  int accumulate, defer_mean;
+  double *cov_carry;
 };
+
+// Emission gradients minus w_b * mean (the centring term) at t < L_b, after
+// the last window of a windowed posterior pass.
+hipError_t launch_mean_fix(const ChainShape &sh, const PostArgs &pa, hipStream_t st);
 
 // Launch geometry of the posterior pass (also sizes its workspace).
 struct PostGeom {
@@ -202,11 +228,12 @@ struct PostGeom {
   size_t dur_lds;
 };
 
-// The cumulative scores split for the exp-space recursion (scan.hip):
-// exp(S[b,t,c]) = ep * 2^n and exp(-S[b,t,c]) = em * 2^-n, [B][T+1][C].
+// The cumulative scores [B][T+1][C] the sweeps read (scan.hip).  The sweeps
+// form the exp-space split exp(S) = ep * 2^n, exp(-S) = em * 2^-n
+// (device_math.h: exp_split) themselves, in the waves that prefetch the
+// scores, so no split copy of S is stored.
 struct Escaled {
-  const double *ep, *em;
-  const int32_t *n;
+  const double *S;
 };
 
 // Buffers of the parallel-in-time sweeps (pit.hip).  Records have the
@@ -226,6 +253,10 @@ struct PitBufs {
   // pos_shift[0][b][t] (forward rows) and pos_shift[1][b][t] (backward rows),
   // the correction of the chunk that wrote position t (k_pit_pos_shift).
   double *row_a, *row_u, *row_v, *row_b;
+  // Row geometry: row t of sequence b is at ((b * row_stride) + t - row_t0) * C
+  // (row_t0 = 0, row_stride = T + 1 when the rows cover every position; a
+  // replay writes a window of positions starting at row_t0).
+  int row_t0, row_stride;
   double *pos_shift;          // [2][B][T+1]
   // exp(trans) in float32, [2][C][C] (forward, backward orientation), for the
   // LDS-ring instances that stream their weights (1024 threads); else NULL.
@@ -268,7 +299,8 @@ hipError_t launch_pit_verify(const ChainShape &sh, const int32_t *lengths, const
 hipError_t launch_pit_fixup(const ChainShape &sh, const int32_t *lengths, const PitBufs &pb,
                             double *logz_ws, double *logz_bwd_ws, float *logz_out, int with_bwd,
                             hipStream_t st);
-void post_geometry(const ChainShape &sh, PostGeom &g);
+// Tw: positions the posterior pass covers at once (T, or a window's length).
+void post_geometry(const ChainShape &sh, PostGeom &g, int Tw);
 
 // Coverage, emission gradients and marginals; transition and duration
 // posterior sums (per-block partials) ...

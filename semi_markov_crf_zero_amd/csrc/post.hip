@@ -33,8 +33,17 @@ constexpr int kDurThreads = 256;
 constexpr int kDurW = 64;     // positions per duration tile
 constexpr long long kPostWorkgroups = 1024;  // grid size the posterior geometry aims for
 
-__device__ __forceinline__ size_t rix(const ChainShape &sh, int b, int t) {
-  return ((size_t)b * (sh.T + 1) + t) * sh.C;
+// Row t of sequence b in the row buffers (which may cover a window only).
+__device__ __forceinline__ size_t rix(const ChainShape &sh, const PostArgs &pa, int b, int t) {
+  return ((size_t)b * pa.row_stride + (t - pa.row_t0)) * sh.C;
+}
+
+// The rows' chunk corrections at t (forward, backward): 0 for exact rows.
+__device__ __forceinline__ double shift_f(const ChainShape &sh, const PostArgs &pa, int b, int t) {
+  return pa.pos_shift ? pa.pos_shift[(size_t)b * (sh.T + 1) + t] : 0.0;
+}
+__device__ __forceinline__ double shift_b(const ChainShape &sh, const PostArgs &pa, int b, int t) {
+  return pa.pos_shift ? pa.pos_shift[((size_t)sh.B + b) * (sh.T + 1) + t] : 0.0;
 }
 
 __device__ __forceinline__ bool valid_len(const ChainShape &sh, int L) { return L >= 1 && L <= sh.T; }
@@ -46,32 +55,31 @@ __device__ __forceinline__ bool valid_len(const ChainShape &sh, int L) { return 
 // (r, c) owns J consecutive positions of label c), as in the score scan.
 // delta[t,c] = E_start[t,c] - E_end[t,c] (E_end[0] = 0), float64-accurate:
 // the coverage is their running sum over the whole sequence.
-// The deltas of positions t0 .. t0+J-1 of label c (0 at t >= L).  Every
-// load is issued before the first exponential (indices clamped into the
-// sequence), so a thread waits for memory once rather than once per
-// position.
+// The deltas of positions t0 .. t0+J-1 of label c (0 at t >= lim, lim the
+// end of the sequence or of the window).  Every load is issued before the
+// first exponential (indices clamped into [t0, lim)), so a thread waits for
+// memory once rather than once per position.
 template <int J>
 __device__ __forceinline__ void cov_deltas(const PostArgs &pa, const ChainShape &sh, int b,
-                                           int t0, int c, int L, double logZ, double (&d)[J]) {
+                                           int t0, int c, int lim, double logZ, double (&d)[J]) {
   double u[J], v[J], a[J], w[J], z[J];
-  const double *pf = pa.pos_shift + (size_t)b * (sh.T + 1);
-  const double *pg = pf + (size_t)sh.B * (sh.T + 1);
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int t = t0 + j < L ? t0 + j : L - 1;
-    const size_t i = rix(sh, b, t) + c;
+    const int t = t0 + j < lim ? t0 + j : lim - 1;
+    const size_t i = rix(sh, pa, b, t) + c;
     u[j] = pa.row_u[i];
     v[j] = pa.row_v[i];
     a[j] = pa.row_a[i];
     w[j] = pa.row_b[i];
-    z[j] = pf[t] + pg[t] - logZ;  // the rows' chunk corrections, less log Z
+    // the rows' chunk corrections, less log Z
+    z[j] = shift_f(sh, pa, b, t) + shift_b(sh, pa, b, t) - logZ;
   }
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int t = t0 + j;
     double dd = exp(u[j] + v[j] + z[j]);
     if (t >= 1) dd -= exp(a[j] + w[j] + z[j]);
-    d[j] = t < L ? dd : 0.0;
+    d[j] = t < lim ? dd : 0.0;
   }
 }
 
@@ -83,11 +91,12 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_partial(ChainShape sh, Post
   const int C = sh.C, R = kCovThreads / C, tid = threadIdx.x;
   const int c = tid % C, r = tid / C;
   const int L = pa.lengths[b];
+  const int lim = min(L, pa.t_hi);
   double s1 = 0.0, s2 = 0.0;
-  const int t0 = tile * R * J + r * J;
-  if (r < R && valid_len(sh, L) && t0 < L) {
+  const int t0 = pa.t_lo + tile * R * J + r * J;
+  if (r < R && valid_len(sh, L) && t0 < lim) {
     double d[J];
-    cov_deltas<J>(pa, sh, b, t0, c, L, pa.logz[b], d);
+    cov_deltas<J>(pa, sh, b, t0, c, lim, pa.logz[b], d);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       s1 += d[j];
@@ -129,14 +138,18 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_anchor(ChainShape sh, PostA
   __syncthreads();
   const int nq = min(kCovThreads, (ntile + per - 1) / per);  // threads that own tiles
   if (tid == 0) {
-    double run = 0.0, tot2 = 0.0;
+    // a windowed pass continues from the earlier windows' running sum
+    const size_t bc = (size_t)b * sh.C + c;
+    double run = pa.accumulate ? pa.cov_carry[bc] : 0.0, tot2 = 0.0;
     for (int q = 0; q < nq; ++q) {
       const double v = red[q];
       red[q] = run;
       run += v;
       tot2 += red2[q];
     }
-    pa.cov_mean[(size_t)b * sh.C + c] = valid_len(sh, L) ? tot2 / (double)L : 0.0;
+    const double m = valid_len(sh, L) ? tot2 / (double)L : 0.0;
+    pa.cov_mean[bc] = pa.accumulate ? pa.cov_mean[bc] + m : m;
+    if (pa.cov_carry) pa.cov_carry[bc] = run;
   }
   __syncthreads();
   double run = red[tid];
@@ -155,11 +168,12 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_write(ChainShape sh, PostAr
   const int L = pa.lengths[b];
   const bool ok = valid_len(sh, L);
   const double logZ = ok ? pa.logz[b] : 0.0;
-  const int t0 = tile * R * J + r * J;
+  const int lim = min(L, pa.t_hi);
+  const int t0 = pa.t_lo + tile * R * J + r * J;
   double d[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) d[j] = 0.0;
-  if (r < R && ok && t0 < L) cov_deltas<J>(pa, sh, b, t0, c, L, logZ, d);
+  if (r < R && ok && t0 < lim) cov_deltas<J>(pa, sh, b, t0, c, lim, logZ, d);
   double own = 0.0;
 #pragma unroll
   for (int j = 0; j < J; ++j) own += d[j];
@@ -170,13 +184,13 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_write(ChainShape sh, PostAr
   if (ok) {
     mu = pa.cov_anchor[((size_t)b * ntile + tile) * C + c];
     for (int q = 0; q < r; ++q) mu += runs[q * C + c];
-    mean = sh.center ? pa.cov_mean[(size_t)b * C + c] : 0.0;
+    mean = (sh.center && !pa.defer_mean) ? pa.cov_mean[(size_t)b * C + c] : 0.0;
     w = pa.grad_logz ? (double)pa.grad_logz[b] : 1.0;
   }
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int t = t0 + j;
-    if (t < sh.T) {
+    if (t < pa.t_hi) {
       float m_out = 0.f, g_out = 0.f;
       if (ok && t < L) {
         mu += d[j];
@@ -213,9 +227,10 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
   for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
-  int tbeg = 1 + seg * tseg, tend = tbeg + tseg;
+  int tbeg = max(1, pa.t_lo) + seg * tseg, tend = tbeg + tseg;
   if (!valid_len(sh, L)) tend = tbeg;
   if (tend > L) tend = L;  // transitions at 1 <= t < L
+  if (tend > pa.t_hi) tend = pa.t_hi;
   const double logZ = valid_len(sh, L) ? pa.logz[b] : 0.0;
   // staging: wave w holds rows 4u + w of the batch (u < kTxPer), lane =
   // column, so each row's maximum is a wave reduction; every load of a batch
@@ -230,12 +245,11 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
 #pragma unroll
     for (int u = 0; u < kTxPer; ++u) {
       const int rr = 4 * u + w, t = r0 + min(rr, nr - 1);
-      const size_t ri = rix(sh, b, t);
+      const size_t ri = rix(sh, pa, b, t);
       va[u] = pa.row_a[ri + ca];
       vg[u] = pa.row_v[ri + cg];
       // the rows' chunk corrections (alpha forward, v backward), less log Z
-      vz[u] = pa.pos_shift[(size_t)b * (sh.T + 1) + t] +
-              pa.pos_shift[((size_t)sh.B + b) * (sh.T + 1) + t] - logZ;
+      vz[u] = shift_f(sh, pa, b, t) + shift_b(sh, pa, b, t) - logZ;
     }
     __syncthreads();  // the previous batch's products are done with ta / tg
 #pragma unroll
@@ -267,7 +281,10 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
       const int cp = ci0 + 4 * bi + x, c = cj0 + 4 * bj + y;
-      if (cp < C && c < C) out[(size_t)cp * C + c] = acc[x][y];
+      if (cp < C && c < C) {
+        const size_t o = (size_t)cp * C + c;
+        out[o] = pa.accumulate ? out[o] + acc[x][y] : acc[x][y];
+      }
     }
 }
 
@@ -327,8 +344,8 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
   if (valid_len(sh, L)) {
     const double logZ = pa.logz[b];
     const double *Sb = pa.S + (size_t)b * (sh.T + 1) * C;
-    const int sbeg = sp * span * kDurW;
-    const int send = min(sbeg + span * kDurW, L);  // segment starts s < L
+    const int sbeg = pa.t_lo + sp * span * kDurW;
+    const int send = min(min(sbeg + span * kDurW, L), pa.t_hi);  // segment starts s < L
     for (int s0 = sbeg; s0 < send; s0 += kDurW) {
       const int ns = min(kDurW, send - s0);
       // ends e in [s0 + klo, min(s0 + ns - 1 + khi, L)]
@@ -336,16 +353,15 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
       __syncthreads();
       for (int i = tid; i < ns * CG; i += kDurThreads) {
         const int ss = i / CG, cc = i % CG;
-        const size_t ri = rix(sh, b, s0 + ss) + c0 + cc;
-        sa[ss * 16 + cc] = (pa.row_u[ri] + pa.pos_shift[(size_t)b * (sh.T + 1) + s0 + ss]) -
+        const size_t ri = rix(sh, pa, b, s0 + ss) + c0 + cc;
+        sa[ss * 16 + cc] = (pa.row_u[ri] + shift_f(sh, pa, b, s0 + ss)) -
                            Sb[(size_t)(s0 + ss) * C + c0 + cc];
       }
       for (int i = tid; i < ne * CG; i += kDurThreads) {
         const int ee = i / CG, cc = i % CG;
         const int e = s0 + klo + ee;
-        const size_t ri = rix(sh, b, e) + c0 + cc;
-        sb[ee * 16 + cc] = (Sb[(size_t)e * C + c0 + cc] +
-                            (pa.row_b[ri] + pa.pos_shift[((size_t)sh.B + b) * (sh.T + 1) + e])) -
+        const size_t ri = rix(sh, pa, b, e) + c0 + cc;
+        sb[ee * 16 + cc] = (Sb[(size_t)e * C + c0 + cc] + (pa.row_b[ri] + shift_b(sh, pa, b, e))) -
                            logZ;
       }
       __syncthreads();
@@ -426,7 +442,11 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       const int k = k0 + j;
-      if (k <= khi) out[(size_t)(k - 1) * C + c] = fma(exp(dk[j]), accf[j], accs[j]);
+      if (k <= khi) {
+        const size_t o = (size_t)(k - 1) * C + c;
+        const double v = fma(exp(dk[j]), accf[j], accs[j]);
+        out[o] = pa.accumulate ? out[o] + v : v;
+      }
     }
   }
 }
@@ -441,22 +461,51 @@ constexpr int kBndThreads = 256;
 __global__ __launch_bounds__(kBndThreads) void k_boundary(ChainShape sh, PostArgs pa) {
   const int lane = threadIdx.x & 63;
   constexpr int wpb = kBndThreads / 64;
-  const long long npos = (long long)sh.B * sh.T;
+  const int Tw = pa.t_hi - pa.t_lo;  // this pass's positions
+  const long long npos = (long long)sh.B * Tw;
   const long long nw = (long long)gridDim.x * wpb;
   for (long long q = (long long)blockIdx.x * wpb + (threadIdx.x >> 6); q < npos; q += nw) {
-    const int b = (int)(q / sh.T), t = (int)(q % sh.T);
+    const int b = (int)(q / Tw), t = pa.t_lo + (int)(q % Tw);
     const int L = pa.lengths[b];
     double s = 0.0;
     if (valid_len(sh, L) && t < L) {  // uniform over the wave
-      const double z = pa.pos_shift[(size_t)b * (sh.T + 1) + t] +
-                       pa.pos_shift[((size_t)sh.B + b) * (sh.T + 1) + t] - pa.logz[b];
-      const size_t i = rix(sh, b, t);
+      const double z = shift_f(sh, pa, b, t) + shift_b(sh, pa, b, t) - pa.logz[b];
+      const size_t i = rix(sh, pa, b, t);
       for (int c = lane; c < sh.C; c += 64) s += exp(pa.row_u[i + c] + pa.row_v[i + c] + z);
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) pa.boundary[q] = (float)s;
+    if (lane == 0) pa.boundary[(size_t)b * sh.T + t] = (float)s;
   }
+}
+
+// ---------------------------------------------------------- centring term
+// After the last window of a windowed pass: grad_x[b,t,c] -= w_b mean[b,c]
+// for t < L_b (mean = cov_mean, summed over the windows).
+__global__ __launch_bounds__(256) void k_mean_fix(ChainShape sh, PostArgs pa) {
+  const size_t n = (size_t)sh.B * sh.T * sh.C;
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int c = (int)(i % sh.C);
+    const size_t bt = i / sh.C;
+    const int t = (int)(bt % sh.T), b = (int)(bt / sh.T);
+    const int L = pa.lengths[b];
+    if (valid_len(sh, L) && t < L) {
+      const double w = pa.grad_logz ? (double)pa.grad_logz[b] : 1.0;
+      // the window wrote (float)(w * mu); mu is re-formed from it exactly
+      // enough (one float32 rounding) for the 1e-4 absolute bar
+      pa.grad_emissions[i] =
+          (float)((double)pa.grad_emissions[i] - w * pa.cov_mean[(size_t)b * sh.C + c]);
+    }
+  }
+}
+
+hipError_t launch_mean_fix(const ChainShape &sh, const PostArgs &pa, hipStream_t st) {
+  if (!sh.center) return hipSuccess;
+  const size_t n = (size_t)sh.B * sh.T * sh.C;
+  size_t grid = (n + 255) / 256;
+  grid = grid > 8192 ? 8192 : grid;
+  hipLaunchKernelGGL(k_mean_fix, dim3((int)grid), dim3(256), 0, st, sh, pa);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ reductions
@@ -513,27 +562,27 @@ __global__ __launch_bounds__(kRedOut * kRedSlices) void k_post_reduce(ChainShape
 }
 
 // ------------------------------------------------------------ launch
-void post_geometry(const ChainShape &sh, PostGeom &g) {
+void post_geometry(const ChainShape &sh, PostGeom &g, int Tw) {
   const int R = kCovThreads / sh.C;
   g.cov_j = kCovJ;
-  while (g.cov_j > kCovJMin && (long long)sh.B * ((sh.T + R * g.cov_j - 1) / (R * g.cov_j)) < kCovTiles)
+  while (g.cov_j > kCovJMin && (long long)sh.B * ((Tw + R * g.cov_j - 1) / (R * g.cov_j)) < kCovTiles)
     g.cov_j /= 2;
-  g.cov_ntile = (sh.T + R * g.cov_j - 1) / (R * g.cov_j);
+  g.cov_ntile = (Tw + R * g.cov_j - 1) / (R * g.cov_j);
   // Position segments of the transition GEMM and spans of the duration
   // kernel: as long as possible (fewer partials to reduce) while the grid
   // still has about kPostWorkgroups workgroups.
   const int ntc = (sh.C + kTxTile - 1) / kTxTile;
   long long want = (kPostWorkgroups + (long long)ntc * ntc * sh.B - 1) / ((long long)ntc * ntc * sh.B);
-  int seg = (int)((sh.T + want - 1) / want);
+  int seg = (int)((Tw + want - 1) / want);
   seg = (seg + kTxRows - 1) / kTxRows * kTxRows;
   g.tx_seg = seg < kTxRows ? kTxRows : (seg > 512 ? 512 : seg);
-  g.tx_nseg = (sh.T + g.tx_seg - 1) / g.tx_seg;
+  g.tx_nseg = (Tw + g.tx_seg - 1) / g.tx_seg;
   const int ncg = (sh.C + 15) / 16, npg = (sh.K + kDurLags - 1) / kDurLags;
-  const int ntile = (sh.T + kDurW - 1) / kDurW;
+  const int ntile = (Tw + kDurW - 1) / kDurW;
   want = (kPostWorkgroups + (long long)ncg * npg * sh.B - 1) / ((long long)ncg * npg * sh.B);
   int span = (int)((ntile + want - 1) / want);
   g.dur_span = span < 1 ? 1 : (span > 8 ? 8 : span);  // tiles of kDurW positions per workgroup
-  g.dur_nspan = (sh.T + g.dur_span * kDurW - 1) / (g.dur_span * kDurW);
+  g.dur_nspan = (Tw + g.dur_span * kDurW - 1) / (g.dur_span * kDurW);
   // lag blocks of KB: the smallest power of two >= 4 with CG x ceil(lags / KB) <= threads
   const int cg = sh.C < 16 ? sh.C : 16;
   const int lags = sh.K < kDurLags ? sh.K : kDurLags;
@@ -546,7 +595,7 @@ void post_geometry(const ChainShape &sh, PostGeom &g) {
 
 hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream_t st) {
   PostGeom g;
-  post_geometry(sh, g);
+  post_geometry(sh, g, pa.geom_T);
   const dim3 gc(g.cov_ntile, sh.B);
   switch (g.cov_j) {
     case 4: hipLaunchKernelGGL(k_cov_partial<4>, gc, dim3(kCovThreads), 0, st, sh, pa, g.cov_ntile); break;
@@ -587,7 +636,7 @@ hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream
                    : g.dur_kb == 16 ? (const void *)k_dur_x<16> : (const void *)k_dur_x<32>;
   if (!lds_fits(kd, g.dur_lds)) return hipErrorInvalidConfiguration;
   if (pa.boundary) {
-    long long nb = ((long long)sh.B * sh.T + (kBndThreads / 64) - 1) / (kBndThreads / 64);
+    long long nb = ((long long)sh.B * (pa.t_hi - pa.t_lo) + (kBndThreads / 64) - 1) / (kBndThreads / 64);
     nb = nb > 2048 ? 2048 : nb;
     hipLaunchKernelGGL(k_boundary, dim3((int)nb), dim3(kBndThreads), 0, st, sh, pa);
     e = hipGetLastError();
@@ -604,7 +653,7 @@ hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream
 
 hipError_t launch_post_reduce(const ChainShape &sh, const PostArgs &pa, hipStream_t st) {
   PostGeom g;
-  post_geometry(sh, g);
+  post_geometry(sh, g, pa.geom_T);
   const int ne = sh.C * sh.C + sh.K * sh.C;
   hipLaunchKernelGGL(k_post_reduce, dim3((ne + kRedOut - 1) / kRedOut), dim3(kRedOut * kRedSlices),
                      0, st, sh, pa, g.tx_nseg, g.dur_nspan);

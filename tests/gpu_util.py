@@ -37,12 +37,12 @@ def to_dev(inp):
             for k in ("emissions", "lengths", "trans", "dur")}
 
 
-def gpu_fwd_bwd(inp, center=True, w=None, ckpt=0):
+def gpu_fwd_bwd(inp, center=True, w=None, ckpt=0, low_memory=False):
     t = to_dev(inp)
     gl = None if w is None else torch.tensor(np.asarray(w), dtype=torch.float32, device=DEV)
     out = bd.semicrf_fwd_bwd(t["emissions"], t["lengths"], t["trans"], t["dur"], center=center,
                              grad_logz=gl, checkpoint_interval=ckpt, want_marginals=True,
-                             want_boundary=True)
+                             want_boundary=True, low_memory=low_memory)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
 

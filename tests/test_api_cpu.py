@@ -85,7 +85,7 @@ def test_workspace_size_errors(lib, args, code):
 
 def test_workspace_size_flags_and_interval(lib):
     n = ctypes.c_size_t(0)
-    assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 2, 0, ctypes.byref(n)) == 6
+    assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 4, 0, ctypes.byref(n)) == 6
     assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 0, -1, ctypes.byref(n)) == 6
     assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 0, 0, None) == 1
     assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 1, 7, ctypes.byref(n)) == 0
@@ -192,3 +192,26 @@ def test_fwd_bwd_ex_and_path_score_validate_before_launch(lib):
     args = list(base)
     args[4] = 0
     assert lib.semicrf_path_score(*args) == 2
+
+
+def test_low_memory_workspace_is_sublinear(lib):
+    """SEMICRF_LOW_MEMORY keeps checkpoint records and one window of rows:
+    beyond the cumulative scores (8 bytes per position and label) its
+    workspace grows more slowly than T, while the default keeps per-position
+    rows."""
+    C, K = 64, 256
+
+    def beyond_scores(T, flags):
+        n = bd.semicrf_workspace_size(bd.OP_FWD_BWD, 1, T, C, K, flags)
+        return n - (T + 1) * C * 8
+
+    for T in (1 << 16, 1 << 18, 1 << 20):
+        assert beyond_scores(T, bd.LOW_MEMORY) < beyond_scores(T, 0) / 2
+    assert beyond_scores(1 << 20, bd.LOW_MEMORY) < beyond_scores(1 << 20, 0) / 6
+    # 16x the positions: ~T^(3/4) (8x) for the windows, ~T for the rows
+    g_low = beyond_scores(1 << 20, bd.LOW_MEMORY) / beyond_scores(1 << 16, bd.LOW_MEMORY)
+    g_all = beyond_scores(1 << 20, 0) / beyond_scores(1 << 16, 0)
+    assert g_all > 8 and g_low < 6, (g_all, g_low)
+    n = ctypes.c_size_t(0)
+    assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 3, 0, ctypes.byref(n)) == 0
+    assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 4, 0, ctypes.byref(n)) == 6
