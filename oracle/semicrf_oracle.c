@@ -258,7 +258,10 @@ static double backward_one(int L, int C, int K, const double *S, const double *t
 
 /* Posteriors of one sequence.  Adds w * (its contribution) into gtrans/gdur
  * (local per-sequence buffers supplied by the caller) and writes mu / grad_x
- * rows [0,T) (zeros at t >= L). */
+ * rows [0,T) (zeros at t >= L).  Each label's sums are taken in arrays of
+ * that label alone (one thread per label) and stored once at the end, so no
+ * two threads write the same cache line while they add; every sum adds the
+ * same terms in the same order as the formulas state. */
 static void posteriors_one(int T, int L, int C, int K, int center, double w, double lzs,
                            const double *S, const double *tr, const double *du,
                            const double *alpha, const double *u, const double *v,
@@ -266,11 +269,14 @@ static void posteriors_one(int T, int L, int C, int K, int center, double w, dou
                            double *gtrans, double *gdur, double *mu_out, double *gx_out,
                            double *bnd_out, int nth)
 {
-    double *diff = calloc((size_t)(T + 1) * C, sizeof(double));
-    double *mu = calloc((size_t)T * C, sizeof(double));
     double *start = bnd_out ? calloc((size_t)T * C, sizeof(double)) : NULL;
 #pragma omp parallel for num_threads(nth) if (nth > 1) schedule(static)
     for (int c = 0; c < C; ++c) {
+        double *diff = calloc((size_t)T + 1, sizeof(double)); /* difference array of mu[., c] */
+        double *mu = calloc((size_t)T, sizeof(double));
+        double *st = start ? calloc((size_t)T, sizeof(double)) : NULL;
+        double *gd = calloc((size_t)K, sizeof(double));
+        double *gt = calloc((size_t)C, sizeof(double));
         /* every segment (s, k, c) */
         for (int s = 0; s < L; ++s) {
             int kmax = (L - s) < K ? (L - s) : K;
@@ -281,36 +287,44 @@ static void posteriors_one(int T, int L, int C, int K, int center, double w, dou
                           + beta[(size_t)(s + k) * C + c]
                           + ((zf[s] + zb[s + k] - zf[L]) - lzs);
                 double p = exp(lp);
-                if (gdur) gdur[(size_t)(k - 1) * C + c] += w * p;
-                if (start) start[(size_t)s * C + c] += p;
-                diff[(size_t)s * C + c] += p;
-                diff[(size_t)(s + k) * C + c] -= p;
+                gd[k - 1] += w * p;
+                if (st) st[s] += p;
+                diff[s] += p;
+                diff[s + k] -= p;
             }
         }
         double run = 0.0;
         for (int i = 0; i < L; ++i) {
-            run += diff[(size_t)i * C + c];
-            mu[(size_t)i * C + c] = run;
+            run += diff[i];
+            mu[i] = run;
         }
         /* every transition c' -> c at an interior boundary t */
-        if (gtrans) {
-            for (int t = 1; t < L; ++t)
-                for (int cp = 0; cp < C; ++cp) {
-                    double lp = alpha[(size_t)t * C + cp] + tr[(size_t)cp * C + c]
-                              + v[(size_t)t * C + c] + ((zf[t] + zb[t] - zf[L]) - lzs);
-                    gtrans[(size_t)cp * C + c] += w * exp(lp);
-                }
-        }
+        for (int t = 1; t < L; ++t)
+            for (int cp = 0; cp < C; ++cp) {
+                double lp = alpha[(size_t)t * C + cp] + tr[(size_t)cp * C + c]
+                          + v[(size_t)t * C + c] + ((zf[t] + zb[t] - zf[L]) - lzs);
+                gt[cp] += w * exp(lp);
+            }
         double mean = 0.0;
         if (center) {
-            for (int i = 0; i < L; ++i) mean += mu[(size_t)i * C + c];
+            for (int i = 0; i < L; ++i) mean += mu[i];
             mean /= (double)L;
         }
         for (int i = 0; i < T; ++i) {
-            double m = i < L ? mu[(size_t)i * C + c] : 0.0;
+            double m = i < L ? mu[i] : 0.0;
             if (mu_out) mu_out[(size_t)i * C + c] = m;
             if (gx_out) gx_out[(size_t)i * C + c] = i < L ? w * (m - mean) : 0.0;
+            if (st) start[(size_t)i * C + c] = st[i];
         }
+        if (gdur)
+            for (int k = 0; k < K; ++k) gdur[(size_t)k * C + c] += gd[k];
+        if (gtrans)
+            for (int cp = 0; cp < C; ++cp) gtrans[(size_t)cp * C + c] += gt[cp];
+        free(diff);
+        free(mu);
+        free(st);
+        free(gd);
+        free(gt);
     }
     if (bnd_out) {
         for (int s = 0; s < T; ++s) {
@@ -320,8 +334,6 @@ static void posteriors_one(int T, int L, int C, int K, int center, double w, dou
             bnd_out[s] = b;
         }
     }
-    free(diff);
-    free(mu);
     free(start);
 }
 
