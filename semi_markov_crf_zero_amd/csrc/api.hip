@@ -269,6 +269,8 @@ semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int
     ChainShape probe = sh;
     if (!chain_config(C, K, probe)) return SEMICRF_ERR_UNSUPPORTED;
     if (op == SEMICRF_OP_VITERBI || !win_config(C, K, sh)) sh = probe;
+    // 32 < C <= 64 with K <= 256: the register-ring engine (chain64.hip)
+    if (op != SEMICRF_OP_VITERBI && !sh.win && sweep64_applies(C, K)) sh.e64 = 1;
     const bool lowmem = op == SEMICRF_OP_FWD_BWD && (flags & SEMICRF_LOW_MEMORY);
     if (lowmem) {
       // the pages' interval (no splitting for parallelism: the records are

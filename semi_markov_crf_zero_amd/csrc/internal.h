@@ -18,6 +18,7 @@ struct ChainShape {
   int B, T, C, K;
   int NT;      // threads per workgroup (256, 512 or 1024)
   int win;     // 1: windowed engine (C <= 32), 0: LDS-ring engine
+  int e64;     // 1: the engine of chain64.hip (32 < C <= 64, K <= 256)
   int P;       // K-sum threads per label = NT / C
   int A;       // durations per K-sum thread = ceil(K / P)
   int Q;       // waves holding row threads = ceil(C / 64) (Viterbi slices)
@@ -276,6 +277,12 @@ hipError_t launch_scan(const float *x, const int32_t *lengths, int B, int T, int
 hipError_t launch_sweep(const ChainShape &sh, const float *trans, const float *dur,
                         const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                         int with_bwd, int iter, hipStream_t st);
+
+// engine for 32 < C <= 64, K <= 256 (chain64.hip); same arguments
+bool sweep64_applies(int C, int K);
+hipError_t launch_sweep_64(const ChainShape &sh, const float *trans, const float *dur,
+                           const Escaled &es, const int32_t *lengths, const PitBufs &pb,
+                           int with_bwd, int iter, hipStream_t st);
 
 // windowed engine for C <= 32 (chain_win.hip); same arguments
 hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float *dur,
