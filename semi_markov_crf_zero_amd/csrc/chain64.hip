@@ -28,11 +28,12 @@
 //     compile-time constants; the steps are predicated, so a block's control
 //     flow is a plain sequence.
 //   * one barrier per step, the only exchange between waves: each label's x
-//     and E (the row, exp(o) = x 2^E) and each wave's largest exponent go to
-//     LDS; after the barrier every wave takes the same step scale B (the
-//     largest exponent over all labels, carried while it stays within a
-//     span) and every lane reads the x, E of its 8 input labels (broadcast
-//     reads) for a = x 2^(E-B) and its share of the contraction.  The new
+//     and E (the row, exp(o) = x 2^E) go to LDS; after the barrier every
+//     lane reads the x, E of its 8 input labels (broadcast reads), the 8
+//     lanes of a label together hold all 64, so a max over them gives every
+//     wave the same step scale B (the largest exponent over all labels,
+//     carried while it stays within a span), then a = x 2^(E-B) and the
+//     lane's share of the contraction.  The new
 //     entry, its rebase (R[c] += n, the label's registers rescaled by 2^-n
 //     exactly) and the next K-sum stay within the label's 8 lanes.
 //   * rows: lane q keeps the raw values (x, E, d, B) of the steps s with
@@ -103,13 +104,12 @@ struct S64 {
   int *pfn;           // [2][kPf][64]
   int *re;            // [kPf][64]: E of the last kPf steps
   int *rb;            // [kPf]: their step scales
-  int *mx;            // [2][kW]: each wave's largest exponent
 };
 
 constexpr size_t kLdsBytes = (size_t)2 * kG * kXS * 8 + (size_t)2 * 2 * kPf * kLab * 8 +
                              (size_t)kTabN * 8 + (size_t)2 * kPf * kLab * 8 +
                              (size_t)2 * kG * kES * 4 + (size_t)2 * kPf * kLab * 4 +
-                             (size_t)kPf * kLab * 4 + (size_t)kPf * 4 + (size_t)2 * kW * 4;
+                             (size_t)kPf * kLab * 4 + (size_t)kPf * 4;
 
 __device__ __forceinline__ S64 carve64(unsigned char *base) {
   S64 m;
@@ -123,8 +123,7 @@ __device__ __forceinline__ S64 carve64(unsigned char *base) {
   m.er = reinterpret_cast<int *>(base + off); off += (size_t)2 * kG * kES * 4;
   m.pfn = reinterpret_cast<int *>(base + off); off += (size_t)2 * kPf * kLab * 4;
   m.re = reinterpret_cast<int *>(base + off); off += (size_t)kPf * kLab * 4;
-  m.rb = reinterpret_cast<int *>(base + off); off += (size_t)kPf * 4;
-  m.mx = reinterpret_cast<int *>(base + off);
+  m.rb = reinterpret_cast<int *>(base + off);
   return m;
 }
 
@@ -218,6 +217,14 @@ __device__ __forceinline__ double gsum8(double v) {
   return v;
 }
 
+// Largest value over the 8 lanes of a label (every lane gets it).
+__device__ __forceinline__ int gmax8_i(int v) {
+  v = max(v, dpp_i(v, 0xB1));
+  v = max(v, dpp_i(v, 0x4E));
+  v = max(v, dpp_i(v, 0x141));
+  return v;
+}
+
 // The value of the lane before (row_shr:1; the first lane of each row of 16
 // keeps its own, which the caller replaces).
 __device__ __forceinline__ double shr1_f64(double v) {
@@ -228,11 +235,11 @@ __device__ __forceinline__ double shr1_f64(double v) {
   return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
 }
 
-// r[i] *= 2^-n[lane] for 8 ring registers, in place, on the lanes of `mask`
-// (none: skipped).  Written as one asm statement so that the rare rebase
-// is no branch in the compiler's view: a branch there makes it merge the
-// ring's two versions with a copy of every register.
-__device__ __forceinline__ void rescale8(double *r, int negn, unsigned long long mask) {
+// r[i] *= 2^-n[lane] for 16 ring registers, in place, on the lanes of
+// `mask` (none: skipped).  Written as one asm statement so that the rare
+// rebase is no branch in the compiler's view: a branch there makes it merge
+// the ring's two versions with a copy of every register.
+__device__ __forceinline__ void rescale16(double *r, int negn, unsigned long long mask) {
   unsigned long long save;
   asm volatile(
       "s_and_saveexec_b64 %[sv], %[m]\n\t"
@@ -244,11 +251,21 @@ __device__ __forceinline__ void rescale8(double *r, int negn, unsigned long long
       "v_ldexp_f64 %[a4], %[a4], %[n]\n\t"
       "v_ldexp_f64 %[a5], %[a5], %[n]\n\t"
       "v_ldexp_f64 %[a6], %[a6], %[n]\n\t"
-      "v_ldexp_f64 %[a7], %[a7], %[n]\n"
+      "v_ldexp_f64 %[a7], %[a7], %[n]\n\t"
+      "v_ldexp_f64 %[a8], %[a8], %[n]\n\t"
+      "v_ldexp_f64 %[a9], %[a9], %[n]\n\t"
+      "v_ldexp_f64 %[a10], %[a10], %[n]\n\t"
+      "v_ldexp_f64 %[a11], %[a11], %[n]\n\t"
+      "v_ldexp_f64 %[a12], %[a12], %[n]\n\t"
+      "v_ldexp_f64 %[a13], %[a13], %[n]\n\t"
+      "v_ldexp_f64 %[a14], %[a14], %[n]\n\t"
+      "v_ldexp_f64 %[a15], %[a15], %[n]\n"
       ".Lrescale%=:\n\t"
       "s_mov_b64 exec, %[sv]"
       : [a0] "+v"(r[0]), [a1] "+v"(r[1]), [a2] "+v"(r[2]), [a3] "+v"(r[3]), [a4] "+v"(r[4]),
-        [a5] "+v"(r[5]), [a6] "+v"(r[6]), [a7] "+v"(r[7]), [sv] "=&s"(save)
+        [a5] "+v"(r[5]), [a6] "+v"(r[6]), [a7] "+v"(r[7]), [a8] "+v"(r[8]), [a9] "+v"(r[9]),
+        [a10] "+v"(r[10]), [a11] "+v"(r[11]), [a12] "+v"(r[12]), [a13] "+v"(r[13]),
+        [a14] "+v"(r[14]), [a15] "+v"(r[15]), [sv] "=&s"(save)
       : [n] "v"(negn), [m] "s"(mask)
       : "scc");
 }
@@ -317,27 +334,31 @@ __device__ __forceinline__ void step64(Sweep64 &c, int base) {
 #pragma unroll
   for (int j = 0; j < kA; ++j) sa[j & 3] = fma(c.Dr[j], c.r[(H + j) % kA], sa[j & 3]);
   const double ks = gsum8((sa[0] + sa[1]) + (sa[2] + sa[3]));
-  // 2. the row: exp(o) = x 2^E, published with this wave's largest exponent
+  // 2. the row: exp(o) = x 2^E, published
   const double x = c.label ? ks * fx : 0.0;
   const int E = c.R + nq;
-  const int ex = (c.label && x > 0.0) ? E + exponent_of(x) : kNoExp;
-  const int wmx = wave_max_i(ex);
   if (c.q == 0) {
     c.sm.xr[(par * kG + (c.cl >> 3)) * kXS + (c.cl & 7)] = x;
     c.sm.er[(par * kG + (c.cl >> 3)) * kES + (c.cl & 7)] = E;
   }
-  if (c.lane == 0) c.sm.mx[par * kW + c.w] = wmx;
   __syncthreads();
-  // 3. the step scale (the same in every wave) and a = x 2^(E-B) of this
-  // lane's 8 input labels
-  int gmx = c.sm.mx[par * kW];
+  // 3. x, E of this lane's 8 input labels (block q); the step scale B: the
+  // largest exponent over all labels -- over the 8 blocks the label's 8
+  // lanes hold, the same in every lane and every wave -- kept while it stays
+  // within the span; a = x 2^(E-B)
+  double xv[kG];
+  int ev[kG], mxl = kNoExp;
 #pragma unroll
-  for (int v = 1; v < kW; ++v) gmx = max(gmx, c.sm.mx[par * kW + v]);
+  for (int i = 0; i < kG; ++i) {
+    xv[i] = c.sm.xr[(par * kG + c.q) * kXS + i];
+    ev[i] = c.sm.er[(par * kG + c.q) * kES + i];
+    mxl = max(mxl, xv[i] > 0.0 ? ev[i] + exponent_of(xv[i]) : kNoExp);
+  }
+  const int gmx = __builtin_amdgcn_readfirstlane(gmax8_i(mxl));
   if (gmx - c.Bm > kSpan || gmx - c.Bm < -kSpan) c.Bm = gmx;
   double a[kG];
 #pragma unroll
-  for (int i = 0; i < kG; ++i)
-    a[i] = ldexp(c.sm.xr[(par * kG + c.q) * kXS + i], c.sm.er[(par * kG + c.q) * kES + i] - c.Bm);
+  for (int i = 0; i < kG; ++i) a[i] = ldexp(xv[i], ev[i] - c.Bm);
   if (PRED && step == c.nrun && c.lz_tail) {
     // log Z of the chain, in this chunk's frame: the sum of a over all labels
     // (only in the last block: an exit that the whole blocks cannot take would
@@ -374,8 +395,8 @@ __device__ __forceinline__ void step64(Sweep64 &c, int base) {
   const double e = c.label ? ldexp(y, sh - n) : 0.0;
   {  // the label's registers into the new reference (lanes that rebase)
     const unsigned long long m = __ballot(n != 0);
-#pragma unroll
-    for (int j = 0; j < kA; j += 8) rescale8(c.r + j, -n, m);
+    rescale16(c.r, -n, m);
+    rescale16(c.r + 16, -n, m);
   }
   // 6. the ring of the next step: the oldest entry of each lane (register
   // H1) moves to the next lane of its label; lane 0 takes the new entry
