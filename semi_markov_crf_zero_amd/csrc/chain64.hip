@@ -27,13 +27,14 @@
 //     the block (a template), so the head and every ring register index are
 //     compile-time constants; the steps are predicated, so a block's control
 //     flow is a plain sequence.
-//   * one barrier per step, the only exchange between waves: each label's x
-//     and E (the row, exp(o) = x 2^E) go to LDS; after the barrier every
-//     lane reads the x, E of its 8 input labels (broadcast reads), the 8
-//     lanes of a label together hold all 64, so a max over them gives every
-//     wave the same step scale B (the largest exponent over all labels,
-//     carried while it stays within a span), then a = x 2^(E-B) and the
-//     lane's share of the contraction.  The new
+//   * one barrier per step, the only exchange between waves: each label's
+//     row (exp(o) = x 2^E), its exponent and a = x 2^(E-B) with the carried
+//     step scale B go to LDS; after the barrier every lane reads those of its
+//     8 input labels (broadcast reads).  The 8 lanes of a label together
+//     hold all 64, so a max over them gives every wave the same new step
+//     scale (the largest exponent over all labels, carried while it stays
+//     within a span; when it moves, a is formed anew from x and E).  Then
+//     the lane's share of the contraction.  The new
 //     entry, its rebase (R[c] += n, the label's registers rescaled by 2^-n
 //     exactly) and the next K-sum stay within the label's 8 lanes.
 //   * rows: lane q keeps the raw values (x, E, d, B) of the steps s with
@@ -97,30 +98,34 @@ __constant__ double kTab64[kTabN] = {
 
 struct S64 {
   double *xr;         // [2][8][kXS]: x of each label (block, index), by step parity
+  double *ar;         // [2][8][kXS]: a = x 2^(E-B) with the carried step scale B
   double *pfx, *pfy;  // [2][kPf][64]: split scores
   double *tab;        // [kTabN]
   double *rx, *rd;    // [kPf][64]: x and d of the last kPf steps (rows, end record)
   int *er;            // [2][8][kES]: E of each label
+  int *xe;            // [2][8][kES]: exponent of x 2^E of each label
   int *pfn;           // [2][kPf][64]
   int *re;            // [kPf][64]: E of the last kPf steps
   int *rb;            // [kPf]: their step scales
 };
 
-constexpr size_t kLdsBytes = (size_t)2 * kG * kXS * 8 + (size_t)2 * 2 * kPf * kLab * 8 +
+constexpr size_t kLdsBytes = (size_t)2 * 2 * kG * kXS * 8 + (size_t)2 * 2 * kPf * kLab * 8 +
                              (size_t)kTabN * 8 + (size_t)2 * kPf * kLab * 8 +
-                             (size_t)2 * kG * kES * 4 + (size_t)2 * kPf * kLab * 4 +
+                             (size_t)2 * 2 * kG * kES * 4 + (size_t)2 * kPf * kLab * 4 +
                              (size_t)kPf * kLab * 4 + (size_t)kPf * 4;
 
 __device__ __forceinline__ S64 carve64(unsigned char *base) {
   S64 m;
   size_t off = 0;
   m.xr = reinterpret_cast<double *>(base + off); off += (size_t)2 * kG * kXS * 8;
+  m.ar = reinterpret_cast<double *>(base + off); off += (size_t)2 * kG * kXS * 8;
   m.pfx = reinterpret_cast<double *>(base + off); off += (size_t)2 * kPf * kLab * 8;
   m.pfy = reinterpret_cast<double *>(base + off); off += (size_t)2 * kPf * kLab * 8;
   m.tab = reinterpret_cast<double *>(base + off); off += (size_t)kTabN * 8;
   m.rx = reinterpret_cast<double *>(base + off); off += (size_t)kPf * kLab * 8;
   m.rd = reinterpret_cast<double *>(base + off); off += (size_t)kPf * kLab * 8;
   m.er = reinterpret_cast<int *>(base + off); off += (size_t)2 * kG * kES * 4;
+  m.xe = reinterpret_cast<int *>(base + off); off += (size_t)2 * kG * kES * 4;
   m.pfn = reinterpret_cast<int *>(base + off); off += (size_t)2 * kPf * kLab * 4;
   m.re = reinterpret_cast<int *>(base + off); off += (size_t)kPf * kLab * 4;
   m.rb = reinterpret_cast<int *>(base + off);
@@ -207,33 +212,37 @@ __device__ __forceinline__ void split64(double s, bool fwd, double &fx, double &
   fy = fwd ? em : ep;
 }
 
-// Sum over the 8 lanes of a label (aligned groups of 8): a butterfly whose
-// every step adds the same two values in every lane, so all 8 lanes end
-// with the same bits.
+// A DPP lane permutation of a float64 without an "old" operand (every lane
+// has a source, or is overwritten by the caller), so no copy is made.
+template <int CTRL>
+__device__ __forceinline__ double dpp_mov_f64(double v) {
+  const long long b = __builtin_bit_cast(long long, v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(b & 0xffffffffLL), CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(b >> 32), CTRL, 0xf, 0xf, true);
+  return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Sum over the 8 lanes of a label (aligned groups of 8: lane ^ 1, lane ^ 2,
+// the other quad): a butterfly whose every step adds the same two values in
+// every lane, so all 8 lanes end with the same bits.
 __device__ __forceinline__ double gsum8(double v) {
-  v += dpp_f64(v, 0xB1);
-  v += dpp_f64(v, 0x4E);
-  v += dpp_f64(v, 0x141);
+  v += dpp_mov_f64<0xB1>(v);
+  v += dpp_mov_f64<0x4E>(v);
+  v += dpp_mov_f64<0x141>(v);
   return v;
 }
 
 // Largest value over the 8 lanes of a label (every lane gets it).
 __device__ __forceinline__ int gmax8_i(int v) {
-  v = max(v, dpp_i(v, 0xB1));
-  v = max(v, dpp_i(v, 0x4E));
-  v = max(v, dpp_i(v, 0x141));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xf, 0xf, true));
   return v;
 }
 
-// The value of the lane before (row_shr:1; the first lane of each row of 16
-// keeps its own, which the caller replaces).
-__device__ __forceinline__ double shr1_f64(double v) {
-  const long long b = __builtin_bit_cast(long long, v);
-  int lo = (int)(b & 0xffffffffLL), hi = (int)(b >> 32);
-  lo = __builtin_amdgcn_update_dpp(lo, lo, 0x111, 0xf, 0xf, false);
-  hi = __builtin_amdgcn_update_dpp(hi, hi, 0x111, 0xf, 0xf, false);
-  return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
-}
+// The value of the lane before (row_shr:1; the first lane of each row of 16,
+// a lane 0 of a label, gets 0 and is overwritten by the caller).
+__device__ __forceinline__ double shr1_f64(double v) { return dpp_mov_f64<0x111>(v); }
 
 // r[i] *= 2^-n[lane] for 16 ring registers, in place, on the lanes of
 // `mask` (none: skipped).  Written as one asm statement so that the rare
@@ -279,11 +288,13 @@ struct Sweep64 {
   double *row1, *row2;
   int T, C, K, w, lane, cl, q, isig, t0, nrun, rt0;
   bool fwd, label, rows, lz_tail;
-  double Dr[kA], Wt[kG];
+  double Dr[kA], Wt[kG], D1;
   // ring: register (h + j) mod kA = entry of duration 32q + 1 + j of the
   // coming step, h = -(steps done) mod kA
   double r[kA];
   int R, Bm;
+  double x;  // the coming step's row exp(o) = x 2^E
+  int E;
   double pf_s;
   double z_end;
   int done;     // steps done (the last one may be the chain's last, log Z)
@@ -318,47 +329,63 @@ __device__ __forceinline__ void step64(Sweep64 &c, int base) {
   const int step = base + I + 1;
   if (PRED && (step > c.nrun || c.ended)) return;
   constexpr int ipf = I % kPf, buf = (I / kPf) & 1;
+  constexpr int ipf1 = (I + 1) % kPf, buf1 = ((I + 1) / kPf) & 1;  // the next step's slot
   constexpr int par = I & 1;             // LDS parity of this step
   constexpr int H = (kA - I) % kA;       // head of this step's ring
   constexpr int H1 = (H + kA - 1) % kA;  // head of the next step's
-  const int t = c.t0 + c.isig * step;
   const bool next_blk = step - 1 - ipf + kPf < c.nrun;
   if (ipf == 0 && next_blk)  // lane q: label cl at step + kPf + q
     c.pf_s = c.S[(size_t)min(max(c.t0 + c.isig * (step + kPf + c.q), 0), c.T) * c.C +
                  (c.label ? c.cl : 0)];
-  const int o = (buf * kPf + ipf) * kLab + c.cl;
-  const double fx = c.sm.pfx[o], fy = c.sm.pfy[o];
-  const int nq = c.isig * c.sm.pfn[o];
-  // 1. this step's K-sum: 32 durations per lane, then over the label's lanes
-  double sa[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-  for (int j = 0; j < kA; ++j) sa[j & 3] = fma(c.Dr[j], c.r[(H + j) % kA], sa[j & 3]);
-  const double ks = gsum8((sa[0] + sa[1]) + (sa[2] + sa[3]));
-  // 2. the row: exp(o) = x 2^E, published
-  const double x = c.label ? ks * fx : 0.0;
-  const int E = c.R + nq;
+  // 1. this step's row exp(o) = x 2^E (formed in the step before), its
+  // exponent and a = x 2^(E-B) with the carried scale B, published; the row
+  // values kept for the row outputs
   if (c.q == 0) {
-    c.sm.xr[(par * kG + (c.cl >> 3)) * kXS + (c.cl & 7)] = x;
-    c.sm.er[(par * kG + (c.cl >> 3)) * kES + (c.cl & 7)] = E;
+    const int lb = c.cl >> 3, li = c.cl & 7;
+    c.sm.xr[(par * kG + lb) * kXS + li] = c.x;
+    c.sm.ar[(par * kG + lb) * kXS + li] = ldexp(c.x, c.E - c.Bm);
+    c.sm.er[(par * kG + lb) * kES + li] = c.E;
+    c.sm.xe[(par * kG + lb) * kES + li] = c.x > 0.0 ? c.E + exponent_of(c.x) : kNoExp;
+    c.sm.rx[ipf * kLab + c.cl] = c.x;
+    c.sm.re[ipf * kLab + c.cl] = c.E;
   }
   __syncthreads();
-  // 3. x, E of this lane's 8 input labels (block q); the step scale B: the
-  // largest exponent over all labels -- over the 8 blocks the label's 8
-  // lanes hold, the same in every lane and every wave -- kept while it stays
-  // within the span; a = x 2^(E-B)
-  double xv[kG];
-  int ev[kG], mxl = kNoExp;
+  // the reads of this lane's 8 input labels (block q) first: their latency
+  // hides behind the K-sum below
+  double a[kG];
+  int xev[kG];
 #pragma unroll
   for (int i = 0; i < kG; ++i) {
-    xv[i] = c.sm.xr[(par * kG + c.q) * kXS + i];
-    ev[i] = c.sm.er[(par * kG + c.q) * kES + i];
-    mxl = max(mxl, xv[i] > 0.0 ? ev[i] + exponent_of(xv[i]) : kNoExp);
+    a[i] = c.sm.ar[(par * kG + c.q) * kXS + i];
+    xev[i] = c.sm.xe[(par * kG + c.q) * kES + i];
   }
-  const int gmx = __builtin_amdgcn_readfirstlane(gmax8_i(mxl));
-  if (gmx - c.Bm > kSpan || gmx - c.Bm < -kSpan) c.Bm = gmx;
-  double a[kG];
+  __builtin_amdgcn_sched_barrier(0);
+  // 2. the ring of the next step but its newest entry: the oldest entry of
+  // each lane (register H1) moves to the next lane of the label, lane 0's
+  // register H1 waits for this step's entry; the K-sum over it.  Nothing
+  // here depends on this step's entry, so these multiply-adds run beside
+  // the chain below.
+  c.r[H1] = c.q == 0 ? 0.0 : shr1_f64(c.r[H1]);
+  double sa[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int i = 0; i < kG; ++i) a[i] = ldexp(xv[i], ev[i] - c.Bm);
+  for (int j = 0; j < kA; ++j) sa[j & 3] = fma(c.Dr[j], c.r[(H1 + j) % kA], sa[j & 3]);
+  const double gk = gsum8((sa[0] + sa[1]) + (sa[2] + sa[3]));
+  // 3. the step scale B: the largest exponent over all labels -- over the 8
+  // blocks the label's 8 lanes hold, the same in every lane and every wave
+  // -- kept while it stays within the span (then the published a hold);
+  // when it moves, a = x 2^(E-B) anew from the raw values (the same bits
+  // the publisher would have formed)
+  int mxl = kNoExp;
+#pragma unroll
+  for (int i = 0; i < kG; ++i) mxl = max(mxl, xev[i]);
+  const int gmx = __builtin_amdgcn_readfirstlane(gmax8_i(mxl));
+  if (gmx - c.Bm > kSpan || gmx - c.Bm < -kSpan) {
+    c.Bm = gmx;
+#pragma unroll
+    for (int i = 0; i < kG; ++i)
+      a[i] = ldexp(c.sm.xr[(par * kG + c.q) * kXS + i],
+                   c.sm.er[(par * kG + c.q) * kES + i] - c.Bm);
+  }
   if (PRED && step == c.nrun && c.lz_tail) {
     // log Z of the chain, in this chunk's frame: the sum of a over all labels
     // (only in the last block: an exit that the whole blocks cannot take would
@@ -367,10 +394,6 @@ __device__ __forceinline__ void step64(Sweep64 &c, int base) {
 #pragma unroll
     for (int i = 0; i < kG; ++i) z += a[i];
     c.z_end = gsum8(z);
-    if (c.q == 0) {  // alpha / v of the last position
-      c.sm.rx[ipf * kLab + c.cl] = x;
-      c.sm.re[ipf * kLab + c.cl] = E;
-    }
     c.done = step;
     c.ended = true;
     return;
@@ -384,6 +407,9 @@ __device__ __forceinline__ void step64(Sweep64 &c, int base) {
   }
   const double d = gsum8(dp0 + dp1);
   // 5. the new entry exp(m -+ S) / 2^R = d fy 2^(B -+ n - R), its rebase
+  const int o = (buf * kPf + ipf) * kLab + c.cl;
+  const double fy = c.sm.pfy[o];
+  const int nq = c.isig * c.sm.pfn[o];
   const double y = d * fy;
   const int sh = c.Bm - nq - c.R;
   int n = 0;
@@ -398,17 +424,8 @@ __device__ __forceinline__ void step64(Sweep64 &c, int base) {
     rescale16(c.r, -n, m);
     rescale16(c.r + 16, -n, m);
   }
-  // 6. the ring of the next step: the oldest entry of each lane (register
-  // H1) moves to the next lane of its label; lane 0 takes the new entry
-  {
-    const double in = shr1_f64(c.r[H1]);
-    c.r[H1] = c.q == 0 ? e : in;
-  }
-  if (c.q == 0) {  // the step's values, for its rows and the end record
-    c.sm.rx[ipf * kLab + c.cl] = x;
-    c.sm.re[ipf * kLab + c.cl] = E;
-    c.sm.rd[ipf * kLab + c.cl] = d;
-  }
+  c.r[H1] = c.q == 0 ? e : c.r[H1];  // the new entry: duration 1 of the next step
+  if (c.q == 0) c.sm.rd[ipf * kLab + c.cl] = d;
   if (c.lane == 0) c.sm.rb[ipf] = c.Bm;
   c.done = step;
   if (ipf == kPf - 1 && next_blk) {  // the next block's scores, split
@@ -419,6 +436,13 @@ __device__ __forceinline__ void step64(Sweep64 &c, int base) {
     c.sm.pfx[po] = px;
     c.sm.pfy[po] = py;
     c.sm.pfn[po] = pn;
+  }
+  // 6. the next step's row: its K-sum (taken before the rebase: exact
+  // power-of-two correction) plus the new entry's term, times exp(+-S)
+  {
+    const int o1 = (buf1 * kPf + ipf1) * kLab + c.cl;
+    c.x = c.label ? (ldexp(gk, -n) + c.D1 * e) * c.sm.pfx[o1] : 0.0;
+    c.E = c.R + c.isig * c.sm.pfn[o1];
   }
   if (ipf == kPf - 1 && c.rows) flush_rows(c);  // (the wave's own labels: no barrier)
 }
@@ -510,6 +534,7 @@ __global__ __launch_bounds__(kNT) void k_sweep64(ChainShape sh, const float *__r
     const int k = kA * q + 1 + j;
     c.Dr[j] = (label && k <= K) ? exp((double)dur[(size_t)(k - 1) * C + cl]) : 0.0;
   }
+  c.D1 = label ? exp((double)dur[cl]) : 0.0;
 #pragma unroll
   for (int i = 0; i < kG; ++i) {
     const int cp = kG * q + i;
@@ -620,6 +645,15 @@ __global__ __launch_bounds__(kNT) void k_sweep64(ChainShape sh, const float *__r
     }
     vm_drain();
     __syncthreads();
+    {  // the first step's row: K-sum over the whole start ring (its newest
+       // entry included), times exp(+-S) of position 1
+      double sa[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int j = 0; j < kA; ++j) sa[j & 3] = fma(c.Dr[j], c.r[j], sa[j & 3]);
+      const double g1 = gsum8((sa[0] + sa[1]) + (sa[2] + sa[3]));
+      c.x = label ? g1 * c.sm.pfx[cl] : 0.0;
+      c.E = c.R + isig * c.sm.pfn[cl];
+    }
     // ---- the steps, in blocks of kA (the logs of the rows every kPf steps,
     // those of the record and log Z values after the loop)
     c.Bm = -(1 << 29);
