@@ -238,7 +238,8 @@ def run_workload(name, steps, warmup, ckpt, peaks, dev, want_rates, want_memory=
     rec = {"workload": name, "B": B, "T": T, "C": C, "K": K, "checkpoint_interval": interval,
            "ms_per_step": ms_step, "segment_cells_per_s": cells_bt / (ms_step * 1e-3),
            "phase_ms": {n: float(m) for n, m in zip(bd.FWD_BWD_PHASES, phase_ms)}}
-    dom = "k_sweep_w" if C <= 32 else "k_sweep"
+    # the sweep kernel the library runs at this shape
+    dom = "k_sweep_w" if C <= 32 else ("k_sweep64" if C <= 64 and K <= 256 else "k_sweep")
     roof = sweep_roofline(cells, npos, C, float(phase_ms[1]), peaks)
     roof["kernel"] = dom
     roof["traffic"] = stored_traffic(dom, name)
