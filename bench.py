@@ -28,6 +28,9 @@ Prints ONE JSON line on stdout:
                `traffic` is the kernel's HBM bytes per launch from rocprofv3
                counters stored under profiles/ (null when absent or when the
                kernel sources changed since).
+  scan_roofline  the score scan (the call's first phase) against the HBM peak:
+               12 bytes per position and label (x read once, S written in
+               float64) over the phase time.
   call_roofline  the same for the whole call (2 transcendentals and 12 VALU
                operations per cell, 6 C^2 flops per position, 20 bytes of
                HBM per position and label) against ms_per_step.
@@ -245,6 +248,13 @@ def run_workload(name, steps, warmup, ckpt, peaks, dev, want_rates, want_memory=
     roof["traffic"] = stored_traffic(dom, name)
     rec["roofline"] = roof
     rec["call_roofline"] = call_roofline(cells, npos, B, T, C, ms_step, peaks)
+    # the score scan (phase 0) is HBM-bound: x read once (4 B) and S written in
+    # float64 (8 B) per position and label, against the HBM peak
+    hbm_peak, hbm_src = pick(peaks, "hbm_GBs")
+    scan_gbs = 12.0 * B * T * C / (float(phase_ms[0]) * 1e-3) / 1e9
+    rec["scan_roofline"] = {"bound": "hbm", "achieved": scan_gbs, "peak": hbm_peak, "unit": "GB/s",
+                            "frac": scan_gbs / hbm_peak, "peak_source": hbm_src,
+                            "bytes": 12.0 * B * T * C, "ms": float(phase_ms[0])}
     rec["effective_cells_per_s"] = float(np.sum(inp["lengths"], dtype=np.int64)) * K * C / (ms_step * 1e-3)
     log("%-8s step %8.3f ms  %.3e cells/s  sweep %.3f ms  roof frac %.3f (call %.3f)  phases %s"
         % (name, ms_step, rec["segment_cells_per_s"], phase_ms[1], roof["frac"],
@@ -369,6 +379,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": head["roofline"],
         "call_roofline": head["call_roofline"],
+        "scan_roofline": head["scan_roofline"],
         "phase_ms": head["phase_ms"],
         "memory": head["memory"],
         "rates": dict(head.get("rates", {}), fwd_bwd_effective=head["effective_cells_per_s"]),
