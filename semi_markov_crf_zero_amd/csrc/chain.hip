@@ -6,9 +6,12 @@
 //     (scan.hip); no edge tensor exists anywhere;
 //   * the forward and backward messages stream through a ring buffer of the
 //     K most recent rows (section 2.B);
-//   * the forward state is stored every `delta` ~ sqrt(T*K) positions
-//     together with its running log normaliser, and the backward pass
-//     recomputes the forward messages between those checkpoints (2.C).
+//   * the state (ring and integer log references) is stored every `delta`
+//     positions (the pages' interval ~ sqrt(T*K), section 2.C).  Every
+//     interval is swept concurrently from its record (pit.hip); by default
+//     the sweeps also keep the per-position rows for the posterior pass,
+//     and in the low-memory mode the posterior pass recomputes them between
+//     the checkpoints instead, window by window, from the records (api.hip).
 //
 // Recurrences (0-based, per sequence of length L; sigma = +1 forward, -1
 // backward; "entry" is what a position contributes to the ring):
@@ -28,7 +31,7 @@
 //     log-sum-exp becomes a K-term float64 dot product with
 //     D[k][c] = exp(dur[k-1][c]) (no transcendental per segment cell).
 //   * the whole step stays in exp space, so no transcendental function sits
-//     on the serial path at all.  The score scan supplies exp(+-S[t,c]) split
+//     on the serial path at all.  The loader waves split exp(+-S[t,c]) (from S)
 //     as a float64 mantissa in [2^-1/2, 2^1/2] times 2^(+-n[t,c]); with the
 //     K-sum ks[c] (relative to 2^R[c])
 //       exp(o[t,c]) = x[c] * 2^E[c],  x = ks * exp(+-S) mantissa, E = R +- n
