@@ -327,7 +327,8 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
   double *sa = reinterpret_cast<double *>(lds);  // [kDurW][16]
   // [kDurW + lags + KB][16], index e - s0 - klo; the rows past the tile's
   // last end are zero on the fast path, so its reads need no bound check
-  const int sbrows = kDurW + min(K, kDurLags) + KB;
+  // (+8: the end-row window of the fast path slides once past the tile)
+  const int sbrows = kDurW + min(K, kDurLags) + KB + 8;
   double *sb = sa + (size_t)kDurW * 16;
   double *pmax = sb + (size_t)sbrows * 16;  // [16][16] partial max / min of a
   double *pmin = pmax + 256;
@@ -351,22 +352,25 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
       // ends e in [s0 + klo, min(s0 + ns - 1 + khi, L)]
       const int ne = min(ns - 1 + khi - klo + 1, L - s0 - klo + 1);
       __syncthreads();
-      for (int i = tid; i < ns * CG; i += kDurThreads) {
-        const int ss = i / CG, cc = i % CG;
-        const size_t ri = rix(sh, pa, b, s0 + ss) + c0 + cc;
-        sa[ss * 16 + cc] = (pa.row_u[ri] + shift_f(sh, pa, b, s0 + ss)) -
-                           Sb[(size_t)(s0 + ss) * C + c0 + cc];
-      }
-      for (int i = tid; i < ne * CG; i += kDurThreads) {
-        const int ee = i / CG, cc = i % CG;
-        const int e = s0 + klo + ee;
-        const size_t ri = rix(sh, pa, b, e) + c0 + cc;
-        sb[ee * 16 + cc] = (Sb[(size_t)e * C + c0 + cc] + (pa.row_b[ri] + shift_b(sh, pa, b, e))) -
-                           logZ;
+      // staging: thread (row r0 + 16 i, label column cc); the row's index
+      // and correction once per row, no division
+      const int cc = tid & 15, r0 = tid >> 4;
+      if (cc < CG) {
+        for (int ss = r0; ss < ns; ss += kDurThreads / 16) {
+          const size_t ri = rix(sh, pa, b, s0 + ss) + c0 + cc;
+          sa[ss * 16 + cc] = (pa.row_u[ri] + shift_f(sh, pa, b, s0 + ss)) -
+                             Sb[(size_t)(s0 + ss) * C + c0 + cc];
+        }
+        for (int ee = r0; ee < ne; ee += kDurThreads / 16) {
+          const int e = s0 + klo + ee;
+          const size_t ri = rix(sh, pa, b, e) + c0 + cc;
+          sb[ee * 16 + cc] =
+              (Sb[(size_t)e * C + c0 + cc] + (pa.row_b[ri] + shift_b(sh, pa, b, e))) - logZ;
+        }
       }
       __syncthreads();
       {  // per label: the largest a of the tile and its range
-        const int cc = tid & 15, part = tid >> 4;
+        const int part = r0;
         double hi = -__builtin_huge_val(), lo = __builtin_huge_val();
         if (cc < CG)
           for (int ss = part; ss < ns; ss += 16) {
@@ -389,33 +393,36 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
       }
       __syncthreads();
       // fast labels: the factors, zero past the tile's starts and ends
-      for (int i = tid; i < kDurW * CG; i += kDurThreads) {
-        const int ss = i / CG, cc = i % CG;
-        if (fast[cc]) sa[ss * 16 + cc] = ss < ns ? exp_wide(sa[ss * 16 + cc] - rho[cc]) : 0.0;
-      }
-      for (int i = tid; i < sbrows * CG; i += kDurThreads) {
-        const int ee = i / CG, cc = i % CG;
-        if (fast[cc]) sb[ee * 16 + cc] = ee < ne ? exp_wide(sb[ee * 16 + cc] + rho[cc]) : 0.0;
+      if (cc < CG && fast[cc]) {
+        const double rc = rho[cc];
+        for (int ss = r0; ss < kDurW; ss += kDurThreads / 16)
+          sa[ss * 16 + cc] = ss < ns ? exp_wide(sa[ss * 16 + cc] - rc) : 0.0;
+        for (int ee = r0; ee < sbrows; ee += kDurThreads / 16)
+          sb[ee * 16 + cc] = ee < ne ? exp_wide(sb[ee * 16 + cc] + rc) : 0.0;
       }
       __syncthreads();
       if (!act) continue;
       const int kofs = k0 - klo;  // end index of (s0 + ss, k0 + j): ss + kofs + j
       if (fast[cl]) {
-        constexpr int JB = KB < 8 ? KB : 8;
+        // blocks of 8 starts x KB lags; the end factors they need, rows
+        // ss0 + kofs .. ss0 + kofs + KB + 6, stay in a register window that
+        // slides by 8 rows from block to block (8 new reads per block)
+        constexpr int NW = KB + 7;
+        double W[NW];
+#pragma unroll
+        for (int q = 0; q < NW; ++q) W[q] = sb[(kofs + q) * 16 + cl];
         for (int ss0 = 0; ss0 < ns; ss0 += 8) {
           double A[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) A[i] = sa[(ss0 + i) * 16 + cl];
 #pragma unroll
-          for (int jb = 0; jb < KB; jb += JB) {
-            double W[8 + JB - 1];
+          for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int q = 0; q < 8 + JB - 1; ++q) W[q] = sb[(ss0 + kofs + jb + q) * 16 + cl];
+            for (int j = 0; j < KB; ++j) accf[j] = fma(A[i], W[i + j], accf[j]);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+          for (int q = 0; q < NW - 8; ++q) W[q] = W[q + 8];
 #pragma unroll
-              for (int j = 0; j < JB; ++j) accf[jb + j] = fma(A[i], W[i + j], accf[jb + j]);
-          }
+          for (int q = NW - 8; q < NW; ++q) W[q] = sb[(ss0 + 8 + kofs + q) * 16 + cl];
         }
       } else {
         // window w[j] = b[s + k0 + j], index (s - s0) + kofs + j
@@ -590,7 +597,7 @@ void post_geometry(const ChainShape &sh, PostGeom &g, int Tw) {
   while (g.dur_kb < 32 && cg * ((lags + g.dur_kb - 1) / g.dur_kb) > kDurThreads) g.dur_kb *= 2;
   g.dur_npg = (sh.K + kDurLags - 1) / kDurLags;
   // a, b, partial maxima and minima of a, per-label references and paths
-  g.dur_lds = (size_t)(kDurW + kDurW + lags + g.dur_kb) * 16 * 8 + 2 * 256 * 8 + 16 * 8 + 16 * 4;
+  g.dur_lds = (size_t)(kDurW + kDurW + lags + g.dur_kb + 8) * 16 * 8 + 2 * 256 * 8 + 16 * 8 + 16 * 4;
 }
 
 hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream_t st) {
