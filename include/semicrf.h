@@ -85,7 +85,17 @@ enum {
      * O(sqrt(T/interval) * interval * C) memory.  Slower (the windows run
      * one after another); same results up to rounding.  Ignored by the other
      * operations. */
-    SEMICRF_LOW_MEMORY = 1u << 1
+    SEMICRF_LOW_MEMORY = 1u << 1,
+    /* semicrf_logz_fwd / semicrf_fwd_bwd: every sweep in float64.  Without
+     * it, shapes with 64 < C <= 256 and K <= 64 run a sweep whose ring
+     * entries, K-sums and transition contraction are float32 (integer
+     * references, scales, the combination of partial sums and every output
+     * stay float64): a relative rounding of about 1e-7 per position, and
+     * the parameters must keep 2 |dur| + |trans| below about 60 nats (a
+     * larger spread overflows the float32 ring).  The pages fix no
+     * precision; this flag selects the float64 engine for those shapes
+     * (slower).  Ignored by the other operations. */
+    SEMICRF_FLOAT64 = 1u << 2
 };
 
 /* Human-readable name of a status code (static string, never NULL). */

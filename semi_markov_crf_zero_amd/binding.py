@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libsemicrf.so")
 OP_SCAN, OP_LOGZ, OP_FWD_BWD, OP_VITERBI, OP_PATH_SCORE = 0, 1, 2, 3, 4
 NO_CENTER = 1
 LOW_MEMORY = 2  # fwd_bwd: checkpoint records only, posteriors replayed in windows
+FLOAT64 = 4  # logz_fwd / fwd_bwd: float64 sweeps for 64 < C <= 256, K <= 64 as well
 
 STATUS = {
     0: "SEMICRF_OK", 1: "SEMICRF_ERR_NULL", 2: "SEMICRF_ERR_SHAPE",
@@ -169,9 +170,9 @@ def semicrf_cumulative_scores(emissions, lengths, center: bool = True):
     return nu, S
 
 
-def semicrf_logz_fwd(emissions, lengths, trans, dur, center: bool = True):
-    """log Z [B] float32."""
-    return LogzPlan(emissions, lengths, trans, dur, center).run()
+def semicrf_logz_fwd(emissions, lengths, trans, dur, center: bool = True, float64: bool = False):
+    """log Z [B] float32.  float64: float64 sweeps for every shape (SEMICRF_FLOAT64)."""
+    return LogzPlan(emissions, lengths, trans, dur, center, float64).run()
 
 
 class FwdBwdPlan:
@@ -180,12 +181,13 @@ class FwdBwdPlan:
 
     def __init__(self, emissions, lengths, trans, dur, center=True, grad_logz=None,
                  checkpoint_interval=0, want_marginals=False, want_boundary=False,
-                 low_memory=False):
+                 low_memory=False, float64=False):
         B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
         _check_weights("grad_logz", grad_logz, B, dev)
         self.args = (emissions, lengths, trans, dur)
         self.B, self.T, self.C, self.K = B, T, C, K
-        self.flags = (0 if center else NO_CENTER) | (LOW_MEMORY if low_memory else 0)
+        self.flags = ((0 if center else NO_CENTER) | (LOW_MEMORY if low_memory else 0)
+                      | (FLOAT64 if float64 else 0))
         self.ckpt = int(checkpoint_interval)
         self.grad_logz = grad_logz
         self.dev = dev
@@ -231,12 +233,14 @@ class FwdBwdPlan:
 
 def semicrf_fwd_bwd(emissions, lengths, trans, dur, center: bool = True, grad_logz=None,
                     checkpoint_interval: int = 0, want_marginals: bool = False,
-                    want_boundary: bool = False, low_memory: bool = False):
+                    want_boundary: bool = False, low_memory: bool = False,
+                    float64: bool = False):
     """Returns dict(logz, grad_emissions, grad_trans, grad_dur[, marginals][, boundary]).
     low_memory: keep only the checkpoint records and replay the intervals in
-    windows for the posteriors (SEMICRF_LOW_MEMORY)."""
+    windows for the posteriors (SEMICRF_LOW_MEMORY).  float64: float64 sweeps
+    for every shape (SEMICRF_FLOAT64)."""
     plan = FwdBwdPlan(emissions, lengths, trans, dur, center, grad_logz, checkpoint_interval,
-                      want_marginals, want_boundary, low_memory)
+                      want_marginals, want_boundary, low_memory, float64)
     return plan.run().outputs()
 
 
@@ -307,11 +311,11 @@ def semicrf_path_score(emissions, lengths, trans, dur, segments, center: bool = 
 class LogzPlan:
     """Preallocated output + workspace for repeated semicrf_logz_fwd calls."""
 
-    def __init__(self, emissions, lengths, trans, dur, center=True):
+    def __init__(self, emissions, lengths, trans, dur, center=True, float64=False):
         B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
         self.args = (emissions, lengths, trans, dur)
         self.B, self.T, self.C, self.K = B, T, C, K
-        self.flags = 0 if center else NO_CENTER
+        self.flags = (0 if center else NO_CENTER) | (FLOAT64 if float64 else 0)
         self.dev = dev
         self.ws, self.ws_bytes = _workspace(OP_LOGZ, B, T, C, K, self.flags, 0, dev)
         self.logz = torch.empty(B, dtype=torch.float32, device=dev)

@@ -193,7 +193,7 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
       lay.nbad = cv.take((size_t)sh->nchunk * 4);
       lay.lz_part = cv.take((size_t)2 * B * 8);
       lay.shift = cv.take(2 * nck * 8);
-      if (!sh->win && sh->NT == 1024) lay.trw = cv.take(trw_floats(C, sh->QT) * 4);
+      if (!sh->win && !sh->e64 && !sh->e256 && sh->NT == 1024) lay.trw = cv.take(trw_floats(C, sh->QT) * 4);
       if (!bwd) break;
       // rows of every position, or (low memory) of one window of chunks
       const int rs = sh->lm_w ? (sh->lm_w + sh->lm_h) * sh->delta + 1 : T + 1;
@@ -252,7 +252,8 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
 semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int ckpt,
                          ChainShape &sh, Layout &lay, VShape *vs_out = nullptr) {
   if (op < SEMICRF_OP_SCAN || op > SEMICRF_OP_PATH_SCORE) return SEMICRF_ERR_ARG;
-  if (flags & ~(unsigned)(SEMICRF_NO_CENTER | SEMICRF_LOW_MEMORY)) return SEMICRF_ERR_ARG;
+  if (flags & ~(unsigned)(SEMICRF_NO_CENTER | SEMICRF_LOW_MEMORY | SEMICRF_FLOAT64))
+    return SEMICRF_ERR_ARG;
   if (ckpt < 0) return SEMICRF_ERR_ARG;
   const semicrf_status_t s = check_sizes(B, T, C, op == SEMICRF_OP_SCAN ? 1 : K);
   if (s != SEMICRF_OK) return s;
@@ -271,6 +272,11 @@ semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int
     if (op == SEMICRF_OP_VITERBI || !win_config(C, K, sh)) sh = probe;
     // 32 < C <= 64 with K <= 256: the register-ring engine (chain64.hip)
     if (op != SEMICRF_OP_VITERBI && !sh.win && sweep64_applies(C, K)) sh.e64 = 1;
+    // 64 < C <= 256 with K <= 64: the float32 wave-sliced contraction engine
+    // (chain256.hip), unless the caller asks for float64 sweeps
+    if (op != SEMICRF_OP_VITERBI && !sh.win && !sh.e64 && !(flags & SEMICRF_FLOAT64) &&
+        sweep256_applies(C, K))
+      sh.e256 = 1;
     const bool lowmem = op == SEMICRF_OP_FWD_BWD && (flags & SEMICRF_LOW_MEMORY);
     if (lowmem) {
       // the pages' interval (no splitting for parallelism: the records are

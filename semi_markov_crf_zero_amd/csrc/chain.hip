@@ -859,6 +859,7 @@ hipError_t launch_sweep(const ChainShape &sh, const float *trans, const float *d
                         int with_bwd, int iter, hipStream_t st) {
   if (sh.win) return launch_sweep_w(sh, trans, dur, es, lengths, pb, with_bwd, iter, st);
   if (sh.e64) return launch_sweep_64(sh, trans, dur, es, lengths, pb, with_bwd, iter, st);
+  if (sh.e256) return launch_sweep_256(sh, trans, dur, es, lengths, pb, with_bwd, iter, st);
   SEMICRF_CHAIN_DISPATCH(sh, sweep(sh, trans, dur, es, lengths, pb, with_bwd, iter, st));
 }
 

@@ -19,6 +19,7 @@ struct ChainShape {
   int NT;      // threads per workgroup (256, 512 or 1024)
   int win;     // 1: windowed engine (C <= 32), 0: LDS-ring engine
   int e64;     // 1: the engine of chain64.hip (32 < C <= 64, K <= 256)
+  int e256;    // 1: the engine of chain256.hip (64 < C <= 256, K <= 64)
   int P;       // K-sum threads per label = NT / C
   int A;       // durations per K-sum thread = ceil(K / P)
   int Q;       // waves holding row threads = ceil(C / 64) (Viterbi slices)
@@ -283,6 +284,12 @@ bool sweep64_applies(int C, int K);
 hipError_t launch_sweep_64(const ChainShape &sh, const float *trans, const float *dur,
                            const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                            int with_bwd, int iter, hipStream_t st);
+
+// engine for 64 < C <= 256, K <= 64 (chain256.hip); same arguments
+bool sweep256_applies(int C, int K);
+hipError_t launch_sweep_256(const ChainShape &sh, const float *trans, const float *dur,
+                            const Escaled &es, const int32_t *lengths, const PitBufs &pb,
+                            int with_bwd, int iter, hipStream_t st);
 
 // windowed engine for C <= 32 (chain_win.hip); same arguments
 hipError_t launch_sweep_w(const ChainShape &sh, const float *trans, const float *dur,

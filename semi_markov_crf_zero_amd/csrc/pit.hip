@@ -36,6 +36,10 @@ namespace {
 
 constexpr int kPitThreads = 256;
 constexpr double kPitTol = 1e-12;  // direction mismatch accepted, relative to the largest entry
+// The same for the engine whose ring and sums are float32 (chain256.hip): two
+// chains that reach one state along different paths agree to float32
+// rounding there, so a float64-level bar would reject every converged chunk.
+constexpr double kPitTolF32 = 1e-5;
 
 struct MaxArg {
   double v;
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_verify(ChainShape sh,
     __syncthreads();
     mism = redd[0];
     for (int q = 1; q < kPitThreads / 64; ++q) mism = fmax(mism, redd[q]);
-    ok = mism <= kPitTol;
+    ok = mism <= (sh.e256 ? kPitTolF32 : kPitTol);
   }
   const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + j;
   __syncthreads();  // every read of A above precedes the copy below

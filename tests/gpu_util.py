@@ -37,19 +37,20 @@ def to_dev(inp):
             for k in ("emissions", "lengths", "trans", "dur")}
 
 
-def gpu_fwd_bwd(inp, center=True, w=None, ckpt=0, low_memory=False):
+def gpu_fwd_bwd(inp, center=True, w=None, ckpt=0, low_memory=False, float64=False):
     t = to_dev(inp)
     gl = None if w is None else torch.tensor(np.asarray(w), dtype=torch.float32, device=DEV)
     out = bd.semicrf_fwd_bwd(t["emissions"], t["lengths"], t["trans"], t["dur"], center=center,
                              grad_logz=gl, checkpoint_interval=ckpt, want_marginals=True,
-                             want_boundary=True, low_memory=low_memory)
+                             want_boundary=True, low_memory=low_memory, float64=float64)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
 
 
-def gpu_logz(inp, center=True):
+def gpu_logz(inp, center=True, float64=False):
     t = to_dev(inp)
-    out = bd.semicrf_logz_fwd(t["emissions"], t["lengths"], t["trans"], t["dur"], center=center)
+    out = bd.semicrf_logz_fwd(t["emissions"], t["lengths"], t["trans"], t["dur"], center=center,
+                              float64=float64)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64)
 

@@ -85,13 +85,29 @@ def test_workspace_size_errors(lib, args, code):
 
 def test_workspace_size_flags_and_interval(lib):
     n = ctypes.c_size_t(0)
-    assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 4, 0, ctypes.byref(n)) == 6
+    assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 8, 0, ctypes.byref(n)) == 6
     assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 0, -1, ctypes.byref(n)) == 6
     assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 0, 0, None) == 1
     assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 1, 7, ctypes.byref(n)) == 0
     small = n.value
     assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 1, 50, ctypes.byref(n)) == 0
     assert n.value != small  # the checkpoint count and chunk scratch depend on the interval
+
+
+def test_float64_flag_selects_the_float64_sweep(lib):
+    # 64 < C <= 256, K <= 64 runs the float32-ring sweep by default; the flag
+    # moves it to the float64 LDS-ring sweep, whose 1024-thread instance
+    # streams a float32 exp(trans) table from the workspace (larger workspace)
+    n32, n64, m = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    for op in (bd.OP_LOGZ, bd.OP_FWD_BWD):
+        assert lib.semicrf_workspace_size(op, 2, 300, 256, 64, 0, 0, ctypes.byref(n32)) == 0
+        assert lib.semicrf_workspace_size(op, 2, 300, 256, 64, bd.FLOAT64, 0,
+                                          ctypes.byref(n64)) == 0
+        assert n64.value > n32.value
+        # shapes outside the float32 sweep: the flag changes nothing
+        assert lib.semicrf_workspace_size(op, 2, 300, 64, 64, 0, 0, ctypes.byref(n32)) == 0
+        assert lib.semicrf_workspace_size(op, 2, 300, 64, 64, bd.FLOAT64, 0, ctypes.byref(m)) == 0
+        assert m.value == n32.value
 
 
 def test_supported_workloads_have_a_configuration(lib):
@@ -136,7 +152,7 @@ def test_bad_sizes_rejected_before_launch(lib):
     P = FAKE
     assert lib.semicrf_fwd_bwd(P, P, P, P, 2, 10, 300, 4, 0, 0, None, P, P, P, P, None, P,
                                1 << 30, None) == 3
-    assert lib.semicrf_fwd_bwd(P, P, P, P, 2, 10, 4, 4, 4, 0, None, P, P, P, P, None, P,
+    assert lib.semicrf_fwd_bwd(P, P, P, P, 2, 10, 4, 4, 8, 0, None, P, P, P, P, None, P,
                                1 << 30, None) == 6
     assert lib.semicrf_fwd_bwd(P, P, P, P, 2, 10, 4, 4, 0, -3, None, P, P, P, P, None, P,
                                1 << 30, None) == 6
@@ -187,7 +203,7 @@ def test_fwd_bwd_ex_and_path_score_validate_before_launch(lib):
     args[19] = need - 1
     assert lib.semicrf_path_score(*args) == 4
     args = list(base)
-    args[8] = 4  # unknown flag
+    args[8] = 8  # unknown flag
     assert lib.semicrf_path_score(*args) == 6
     args = list(base)
     args[4] = 0
@@ -214,4 +230,4 @@ def test_low_memory_workspace_is_sublinear(lib):
     assert g_all > 8 and g_low < 6, (g_all, g_low)
     n = ctypes.c_size_t(0)
     assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 3, 0, ctypes.byref(n)) == 0
-    assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 4, 0, ctypes.byref(n)) == 6
+    assert lib.semicrf_workspace_size(bd.OP_FWD_BWD, 2, 100, 4, 8, 8, 0, ctypes.byref(n)) == 6
