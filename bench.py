@@ -14,8 +14,10 @@ genome claims are about), each timed the same way in the same run.
 Prints ONE JSON line on stdout:
   value        B*T*K*C segment cells per second (whole job, 1 GPU)
   roofline     the dominant kernel -- the parallel-in-time sweep (k_sweep_w
-               for C <= 32, k_sweep otherwise) -- timed with HIP events the
-               library records on the launch stream around its first launch
+               for C <= 32, k_sweep64 for C <= 64 and K <= 256, k_sweep256
+               for C <= 256 and K <= 64, k_sweep otherwise) -- timed with
+               HIP events the library records on the launch stream around
+               its first launch
                (every checkpoint interval of both directions; once the
                verification passes, the later launches return at once and
                are timed with the rest of the phase).  Its algorithmic work
@@ -242,7 +244,8 @@ def run_workload(name, steps, warmup, ckpt, peaks, dev, want_rates, want_memory=
            "ms_per_step": ms_step, "segment_cells_per_s": cells_bt / (ms_step * 1e-3),
            "phase_ms": {n: float(m) for n, m in zip(bd.FWD_BWD_PHASES, phase_ms)}}
     # the sweep kernel the library runs at this shape
-    dom = "k_sweep_w" if C <= 32 else ("k_sweep64" if C <= 64 and K <= 256 else "k_sweep")
+    dom = ("k_sweep_w" if C <= 32 else "k_sweep64" if C <= 64 and K <= 256
+           else "k_sweep256" if C <= 256 and K <= 64 else "k_sweep")
     roof = sweep_roofline(cells, npos, C, float(phase_ms[1]), peaks)
     roof["kernel"] = dom
     roof["traffic"] = stored_traffic(dom, name)

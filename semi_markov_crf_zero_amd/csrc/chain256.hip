@@ -240,14 +240,51 @@ __device__ __forceinline__ float shr1_f32(float v) {
       float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x111, 0xf, 0xf, true));
 }
 
-// r[i] = min(r[i] 2^-n[lane], 2^120) for 16 ring registers, in place, on the
-// lanes of `mask` (none: skipped).  One asm statement, so that the rebase
-// is no branch in the compiler's view (a branch makes it merge the ring's
-// two versions with a copy of every register).  The bound only ever touches
-// registers past the label's K durations (weight 0, no longer bounded by the
-// newest entry, and scaled up by every downward rebase until they leave the
-// ring): capped, they stay finite, so 0 times them stays 0.
-__device__ __forceinline__ void rescale16(float *r, int negn, unsigned long long mask) {
+// r[i] *= 2^-n[lane] for 16 ring registers, in place, on the lanes of
+// `mask` (none: skipped); with CL also capped at 2^120.  One asm statement,
+// so that the rebase is no branch in the compiler's view (a branch makes it
+// merge the ring's two versions with a copy of every register).  The cap
+// (K < 64 only) touches registers past the label's K durations: weight 0,
+// no longer bounded by the newest entry, and scaled up by every downward
+// rebase until they leave the ring; capped, they stay finite, so 0 times
+// them stays 0.  With K = 64 every register holds a live duration.
+template <bool CL>
+__device__ __forceinline__ void rescale16(float *r, int negn, unsigned long long mask);
+
+template <>
+__device__ __forceinline__ void rescale16<false>(float *r, int negn, unsigned long long mask) {
+  unsigned long long save;
+  asm volatile(
+      "s_and_saveexec_b64 %[sv], %[m]\n\t"
+      "s_cbranch_execz .Lrescale%=\n\t"
+      "v_ldexp_f32 %[a0], %[a0], %[n]\n\t"
+      "v_ldexp_f32 %[a1], %[a1], %[n]\n\t"
+      "v_ldexp_f32 %[a2], %[a2], %[n]\n\t"
+      "v_ldexp_f32 %[a3], %[a3], %[n]\n\t"
+      "v_ldexp_f32 %[a4], %[a4], %[n]\n\t"
+      "v_ldexp_f32 %[a5], %[a5], %[n]\n\t"
+      "v_ldexp_f32 %[a6], %[a6], %[n]\n\t"
+      "v_ldexp_f32 %[a7], %[a7], %[n]\n\t"
+      "v_ldexp_f32 %[a8], %[a8], %[n]\n\t"
+      "v_ldexp_f32 %[a9], %[a9], %[n]\n\t"
+      "v_ldexp_f32 %[a10], %[a10], %[n]\n\t"
+      "v_ldexp_f32 %[a11], %[a11], %[n]\n\t"
+      "v_ldexp_f32 %[a12], %[a12], %[n]\n\t"
+      "v_ldexp_f32 %[a13], %[a13], %[n]\n\t"
+      "v_ldexp_f32 %[a14], %[a14], %[n]\n\t"
+      "v_ldexp_f32 %[a15], %[a15], %[n]\n"
+      ".Lrescale%=:\n\t"
+      "s_mov_b64 exec, %[sv]"
+      : [a0] "+v"(r[0]), [a1] "+v"(r[1]), [a2] "+v"(r[2]), [a3] "+v"(r[3]), [a4] "+v"(r[4]),
+        [a5] "+v"(r[5]), [a6] "+v"(r[6]), [a7] "+v"(r[7]), [a8] "+v"(r[8]), [a9] "+v"(r[9]),
+        [a10] "+v"(r[10]), [a11] "+v"(r[11]), [a12] "+v"(r[12]), [a13] "+v"(r[13]),
+        [a14] "+v"(r[14]), [a15] "+v"(r[15]), [sv] "=&s"(save)
+      : [n] "v"(negn), [m] "s"(mask)
+      : "scc");
+}
+
+template <>
+__device__ __forceinline__ void rescale16<true>(float *r, int negn, unsigned long long mask) {
   unsigned long long save;
   asm volatile(
       "s_and_saveexec_b64 %[sv], %[m]\n\t"
@@ -330,7 +367,7 @@ __device__ __forceinline__ double score_at(const Sweep256 &c, int step) {
 // are compile-time constants.  Whole blocks that end before the segment's
 // last step run unpredicated (PRED false); the last, partial block skips
 // the steps past the end (PRED true).
-template <int I, bool PRED>
+template <int I, bool PRED, bool CL>
 __device__ __forceinline__ void step256(Sweep256 &c, int base) {
   const int step = base + I + 1;
   if (PRED && (step > c.nrun || c.ended)) return;
@@ -411,9 +448,12 @@ __device__ __forceinline__ void step256(Sweep256 &c, int base) {
     if (c.lane == 0) c.sm.bw[par * kW + c.w] = bw;
   }
   __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
   // 3. the ring of the next step but its newest entry: lane 2i's oldest
   // entry (register H1) moves to lane 2i+1, lane 2i's register H1 waits for
-  // this step's entry; the K-sum over it (independent of this step's entry)
+  // this step's entry; the K-sum over it.  Independent of this step's entry,
+  // so it fills the latency of the dependent chain below (partials ->
+  // entry -> next row) instead of delaying the barrier.
   c.r[H1] = c.q == 0 ? 0.0f : shr1_f32(c.r[H1]);
   float sa0 = 0.0f, sa1 = 0.0f;
 #pragma unroll
@@ -422,7 +462,6 @@ __device__ __forceinline__ void step256(Sweep256 &c, int base) {
     sa1 = fmaf(c.drl[(j + 1) * kLab], c.r[(H1 + j + 1) % kA], sa1);
   }
   const double gk = gsum2((double)sa0 + (double)sa1);
-  __syncthreads();
   // 4. this label's contraction: the 8 waves' partials at the step scale B
   int bws[kW];
   {
@@ -454,8 +493,8 @@ __device__ __forceinline__ void step256(Sweep256 &c, int base) {
   const float e = c.label ? (float)ldexp(y, sh - n) : 0.0f;
   {  // the label's registers into the new reference (lanes that rebase)
     const unsigned long long m = __ballot(n != 0);
-    rescale16(c.r, -n, m);
-    rescale16(c.r + 16, -n, m);
+    rescale16<CL>(c.r, -n, m);
+    rescale16<CL>(c.r + 16, -n, m);
   }
   c.r[H1] = c.q == 0 ? e : c.r[H1];  // the new entry: duration 1 of the next step
   // 6. the rows of this step: lane 0 of the pair o = log(x 2^E), lane 1
@@ -481,10 +520,10 @@ __device__ __forceinline__ void step256(Sweep256 &c, int base) {
   c.done = step;
 }
 
-template <bool PRED, int... Is>
+template <bool PRED, bool CL, int... Is>
 __device__ __forceinline__ void block256(Sweep256 &c, int base,
                                          std::integer_sequence<int, Is...>) {
-  (step256<Is, PRED>(c, base), ...);
+  (step256<Is, PRED, CL>(c, base), ...);
 }
 
 }  // namespace
@@ -492,6 +531,8 @@ __device__ __forceinline__ void block256(Sweep256 &c, int base,
 // One workgroup per (direction, sequence, chunk), as k_sweep (chain.hip):
 // the same launch grid, start states, records ([K][C] ring by slot, then R,
 // o, m), verification hand-off, log Z of the tail chunk and replay windows.
+// CL: K < 64 (ring registers past K exist; see rescale16).
+template <bool CL>
 __global__ __launch_bounds__(kNT) void k_sweep256(ChainShape sh, const float *__restrict__ trans,
                                                   const float *__restrict__ dur, Escaled es,
                                                   const int32_t *__restrict__ lengths,
@@ -715,8 +756,8 @@ __global__ __launch_bounds__(kNT) void k_sweep256(ChainShape sh, const float *__
     c.o_end = c.m_end = 0.0;
     const int nfull = (c.nrun - 1) / kA;  // whole blocks before the last step's
     for (int blk = 0; blk < nfull; ++blk)
-      block256<false>(c, blk * kA, std::make_integer_sequence<int, kA>{});
-    block256<true>(c, nfull * kA, std::make_integer_sequence<int, kA>{});
+      block256<false, CL>(c, blk * kA, std::make_integer_sequence<int, kA>{});
+    block256<true, CL>(c, nfull * kA, std::make_integer_sequence<int, kA>{});
     if (c.ended) {
       if (!replay && tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = log_t(c.z_end, c.zB, c.sm.tab);
     } else {
@@ -749,11 +790,16 @@ hipError_t launch_sweep_256(const ChainShape &sh, const float *trans, const floa
                             const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                             int with_bwd, int iter, hipStream_t st) {
   const size_t lds = sweep256_lds_bytes(sh.K);
-  if (!sweep256_applies(sh.C, sh.K) || !lds_fits((const void *)k_sweep256, lds))
-    return hipErrorInvalidConfiguration;
+  const bool cl = sh.K < kDmax;
+  const void *f = cl ? (const void *)k_sweep256<true> : (const void *)k_sweep256<false>;
+  if (!sweep256_applies(sh.C, sh.K) || !lds_fits(f, lds)) return hipErrorInvalidConfiguration;
   const int grid = iter < 0 ? sh.B * (sh.rnf + sh.rnb) : (with_bwd ? 2 : 1) * sh.B * sh.nchunk;
-  hipLaunchKernelGGL(k_sweep256, dim3(grid), dim3(kNT), lds, st, sh, trans, dur, es, lengths, pb,
-                     iter);
+  if (cl)
+    hipLaunchKernelGGL(k_sweep256<true>, dim3(grid), dim3(kNT), lds, st, sh, trans, dur, es,
+                       lengths, pb, iter);
+  else
+    hipLaunchKernelGGL(k_sweep256<false>, dim3(grid), dim3(kNT), lds, st, sh, trans, dur, es,
+                       lengths, pb, iter);
   return hipGetLastError();
 }
 
