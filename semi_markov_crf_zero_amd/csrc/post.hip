@@ -20,6 +20,8 @@
 
 namespace semicrf {
 
+typedef double v4d __attribute__((ext_vector_type(4)));  // an MFMA float64 accumulator
+
 namespace {
 
 constexpr int kCovThreads = 256;
@@ -209,8 +211,14 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_write(ChainShape sh, PostAr
 // GEMM over positions: a[t,c'] = exp(alpha[t,c'] - m_t) and
 // g[t,c] = exp(v[t,c] + m_t - logZ), m_t the largest alpha of the block's
 // rows (a <= 1, and g <= exp(-min trans): no overflow).  One workgroup per
-// (64 x 64 output tile, sequence, position segment); each thread owns a
-// 4 x 4 block of the tile.
+// (64 x 64 output tile, sequence, position segment), four waves; the
+// products run on the matrix cores in float64: wave (wi, wj) owns the
+// 32 x 32 block at rows 32 wi, columns 32 wj of the tile as 2 x 2 blocks of
+// 16 x 16, and every 4 staged positions add one v_mfma_f64_16x16x4 per
+// block (A = a^T: lane l holds a[position 4k' + l / 16][row l % 16], B = g:
+// lane l holds g[position 4k' + l / 16][column l % 16]; element r of the
+// accumulator of lane l is row l / 16 + 4 r, column l % 16 -- the float64
+// instruction's layout, checked on the device).
 __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs pa, int tseg,
                                                         int nseg) {
   __shared__ double ta[kTxRows][kTxTile];
@@ -221,12 +229,11 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
   const int C = sh.C, tid = threadIdx.x;
   const int L = pa.lengths[b];
   const int ci0 = ti * kTxTile, cj0 = tj * kTxTile;
-  const int bi = tid / (kTxTile / 4), bj = tid % (kTxTile / 4);  // 16 x 16 thread grid
-  double acc[4][4];
+  v4d acc[2][2];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+    for (int y = 0; y < 2; ++y) acc[x][y] = v4d{0.0, 0.0, 0.0, 0.0};
   int tbeg = max(1, pa.t_lo) + seg * tseg, tend = tbeg + tseg;
   if (!valid_len(sh, L)) tend = tbeg;
   if (tend > L) tend = L;  // transitions at 1 <= t < L
@@ -262,30 +269,32 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
       tg[rr][lane] = ing ? exp_wide(vg[u] + m + vz[u]) : 0.0;
     }
     __syncthreads();
-    for (int rr = 0; rr < nr; ++rr) {
-      double a[4], g[4];
+    // rows past nr were staged as zeros, so whole groups of 4 run
+    const int kq = lane >> 4, li = lane & 15, wi = w >> 1, wj = w & 1;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        a[x] = ta[rr][4 * bi + x];
-        g[x] = tg[rr][4 * bj + x];
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], g[y], acc[x][y]);
+    for (int kk = 0; kk < kTxRows; kk += 4) {
+      const double a0 = ta[kk + kq][32 * wi + li], a1 = ta[kk + kq][32 * wi + 16 + li];
+      const double g0 = tg[kk + kq][32 * wj + li], g1 = tg[kk + kq][32 * wj + 16 + li];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, g0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, g1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, g0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, g1, acc[1][1], 0, 0, 0);
     }
   }
   double *out = pa.tx_part + ((size_t)b * nseg + seg) * C * C;
+  const int kq = lane >> 4, li = lane & 15, wi = w >> 1, wj = w & 1;
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int cp = ci0 + 4 * bi + x, c = cj0 + 4 * bj + y;
-      if (cp < C && c < C) {
-        const size_t o = (size_t)cp * C + c;
-        out[o] = pa.accumulate ? out[o] + acc[x][y] : acc[x][y];
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int cp = ci0 + 32 * wi + 16 * x + kq + 4 * r, c = cj0 + 32 * wj + 16 * y + li;
+        if (cp < C && c < C) {
+          const size_t o = (size_t)cp * C + c;
+          out[o] = pa.accumulate ? out[o] + acc[x][y][r] : acc[x][y][r];
+        }
       }
-    }
 }
 
 // ------------------------------------------------------------ durations
