@@ -83,8 +83,18 @@ enum {
      * forward, one more backward (the durations reach past the window) --
      * and consumes each window's messages before the next, so they take
      * O(sqrt(T/interval) * interval * C) memory.  Slower (the windows run
-     * one after another); same results up to rounding.  Ignored by the other
-     * operations. */
+     * one after another); same results up to rounding.
+     * semicrf_viterbi: the decisions are not kept for every position.  The
+     * parallel sweeps keep only each chunk's start state; then, window by
+     * window from the end (ceil(sqrt(#chunks)) chunks a window), the
+     * decisions of the window and of the chunk before it are recomputed
+     * from those states and the optimal path is followed back through the
+     * window, one thread per sequence.  Decision memory
+     * O(sqrt(T/chunk) * chunk * C) instead of O(T * C); the same
+     * segmentation as without the flag.  Slower (the windows run one after
+     * another; the walk is serial per sequence).  Shapes the parallel
+     * decoder does not take (see semicrf_viterbi) ignore the flag.
+     * Ignored by the other operations. */
     SEMICRF_LOW_MEMORY = 1u << 1,
     /* semicrf_logz_fwd / semicrf_fwd_bwd: every sweep in float64.  Without
      * it, shapes with 64 < C <= 256 and K <= 64 run a sweep whose ring

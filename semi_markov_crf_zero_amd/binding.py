@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libsemicrf.so")
 
 OP_SCAN, OP_LOGZ, OP_FWD_BWD, OP_VITERBI, OP_PATH_SCORE = 0, 1, 2, 3, 4
 NO_CENTER = 1
-LOW_MEMORY = 2  # fwd_bwd: checkpoint records only, posteriors replayed in windows
+LOW_MEMORY = 2  # fwd_bwd / viterbi: checkpoint records only, replayed in windows
 FLOAT64 = 4  # logz_fwd / fwd_bwd: float64 sweeps for 64 < C <= 256, K <= 64 as well
 
 STATUS = {
@@ -333,11 +333,11 @@ class LogzPlan:
 class ViterbiPlan:
     """Preallocated outputs + workspace for repeated semicrf_viterbi calls."""
 
-    def __init__(self, emissions, lengths, trans, dur, center=True):
+    def __init__(self, emissions, lengths, trans, dur, center=True, low_memory=False):
         B, T, C, K, dev = _check_inputs(emissions, lengths, trans, dur)
         self.args = (emissions, lengths, trans, dur)
         self.B, self.T, self.C, self.K = B, T, C, K
-        self.flags = 0 if center else NO_CENTER
+        self.flags = (0 if center else NO_CENTER) | (LOW_MEMORY if low_memory else 0)
         self.dev = dev
         self.ws, self.ws_bytes = _workspace(OP_VITERBI, B, T, C, K, self.flags, 0, dev)
         self.best = torch.empty(B, dtype=torch.float32, device=dev)
@@ -359,9 +359,11 @@ class ViterbiPlan:
                     seg_label=self.seg_label, num_segs=self.num_segs)
 
 
-def semicrf_viterbi(emissions, lengths, trans, dur, center: bool = True):
-    """Returns dict(best_score [B] f32, seg_start/seg_len/seg_label [B,T] i32, num_segs [B] i32)."""
-    return ViterbiPlan(emissions, lengths, trans, dur, center).run()
+def semicrf_viterbi(emissions, lengths, trans, dur, center: bool = True,
+                    low_memory: bool = False):
+    """Returns dict(best_score [B] f32, seg_start/seg_len/seg_label [B,T] i32, num_segs [B] i32).
+    low_memory: recompute the decisions window by window (SEMICRF_LOW_MEMORY)."""
+    return ViterbiPlan(emissions, lengths, trans, dur, center, low_memory).run()
 
 
 # short aliases

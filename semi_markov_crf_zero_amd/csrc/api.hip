@@ -222,23 +222,38 @@ bool make_layout(int op, int B, int T, int C, int K, const ChainShape *sh, Layou
       lay.p_lab = cv.take((size_t)B * T * 4);
       break;
     case SEMICRF_OP_VITERBI:
-      lay.bp = cv.take(nS * 4);
+      // decisions of every position, or (low memory) of one window of chunks
+      // and the chunk before it
+      lay.bp = cv.take(vs && vs->lm_w ? (size_t)B * C * ((size_t)(vs->lm_w + 1) * vs->delta + 1) * 4
+                                      : nS * 4);
       lay.vbest = cv.take((size_t)B * 8);
       lay.vcbest = cv.take((size_t)B * 4);
       if (vs) {  // parallel-in-time decoder
         const size_t nck = (size_t)B * vs->nchunk;
         lay.vit_pit = 1;
-        lay.v_pred = cv.take(nS * 4);
         lay.v_rr = cv.take(nck * K * C * 8);
         lay.v_re = cv.take(nck * K * C * 8);
         lay.v_corr = cv.take(nck * 8);
         lay.v_delta = cv.take(nck * 8);
         lay.v_redo = cv.take(nck * 4);
         lay.v_nbad = cv.take((size_t)kVitIters * 4);
-        lay.v_lst_t = cv.take((size_t)B * T * 4);
-        lay.v_lst_c = cv.take((size_t)B * T * 4);
-        lay.v_mark = cv.take((size_t)B * (T + 1) * 4);
-        lay.v_sub = cv.take((size_t)B * vs->nsub * kVSubFields * 4);
+        if (vs->lm_w) {  // the parallel backtrack over one window at a time
+          const size_t wpos = (size_t)vs->lm_w * vs->delta;  // positions of a window
+          const size_t wst = wpos + vs->delta + 1;           // with the chunk before it
+          const size_t wsub = (wpos + vs->dbt - 1) / vs->dbt;
+          lay.v_pred = cv.take((size_t)B * C * wst * 4);
+          lay.v_lst_t = cv.take((size_t)B * wpos * 4);
+          lay.v_lst_c = cv.take((size_t)B * wpos * 4);
+          lay.v_mark = cv.take((size_t)B * wst * 4);
+          lay.v_sub = cv.take((size_t)B * wsub * kVSubFields * 4);
+          lay.v_node = cv.take((size_t)B * 3 * 4);
+        } else {  // the parallel backtrack over the whole sequence
+          lay.v_pred = cv.take(nS * 4);
+          lay.v_lst_t = cv.take((size_t)B * T * 4);
+          lay.v_lst_c = cv.take((size_t)B * T * 4);
+          lay.v_mark = cv.take((size_t)B * (T + 1) * 4);
+          lay.v_sub = cv.take((size_t)B * vs->nsub * kVSubFields * 4);
+        }
       }
       break;
     default:
@@ -298,6 +313,9 @@ semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int
   VShape vs;
   const bool pit = op == SEMICRF_OP_VITERBI && vit_config(B, T, C, K, vs);
   if (pit) vs.center = sh.center;
+  // low-memory decoding: decisions recomputed window by window from the
+  // chunk start states (ceil(sqrt(#chunks)) chunks a window)
+  if (pit && (flags & SEMICRF_LOW_MEMORY) && vs.nchunk > 1) vs.lm_w = lowmem_window(vs.nchunk);
   if (!make_layout(op, B, T, C, K, &sh, lay, pit ? &vs : nullptr)) return SEMICRF_ERR_ARG;
   if (pit && vs_out) *vs_out = vs;
   return SEMICRF_OK;
@@ -663,8 +681,9 @@ semicrf_status_t semicrf_viterbi(const float *emissions, const int32_t *lengths,
   if (e != hipSuccess) return hip_status(e);
   if (lay.vit_pit) {
     VBufs vb;
+    auto opt = [&](size_t off) { return off ? at<int32_t>(ws, off) : nullptr; };
     vb.bp = at<uint32_t>(ws, lay.bp);
-    vb.pred = at<uint32_t>(ws, lay.v_pred);
+    vb.pred = lay.v_pred ? at<uint32_t>(ws, lay.v_pred) : nullptr;
     vb.rec_r = at<double>(ws, lay.v_rr);
     vb.rec_e = at<double>(ws, lay.v_re);
     vb.corr = at<double>(ws, lay.v_corr);
@@ -673,10 +692,11 @@ semicrf_status_t semicrf_viterbi(const float *emissions, const int32_t *lengths,
     vb.nbad = at<int>(ws, lay.v_nbad);
     vb.vbest = at<double>(ws, lay.vbest);
     vb.vcbest = at<int32_t>(ws, lay.vcbest);
-    vb.lst_t = at<int32_t>(ws, lay.v_lst_t);
-    vb.lst_c = at<int32_t>(ws, lay.v_lst_c);
-    vb.mark = at<int32_t>(ws, lay.v_mark);
-    vb.sub = at<int32_t>(ws, lay.v_sub);
+    vb.lst_t = opt(lay.v_lst_t);
+    vb.lst_c = opt(lay.v_lst_c);
+    vb.mark = opt(lay.v_mark);
+    vb.sub = opt(lay.v_sub);
+    vb.node = opt(lay.v_node);
     e = launch_vit_pit(vs, trans, dur, S, lengths, vb, best_score, seg_start, seg_len,
                        seg_label, num_segs, st);
   } else {

@@ -171,6 +171,7 @@ struct Layout {
   size_t bp, vbest, vcbest;
   size_t p_score, p_valid, p_cnt, p_lab;
   size_t v_pred, v_rr, v_re, v_corr, v_delta, v_redo, v_nbad, v_lst_t, v_lst_c, v_mark, v_sub;
+  size_t v_node;
   size_t total;
   int ntile;
   int scan_j;   // positions per scan row thread
@@ -345,6 +346,17 @@ struct VShape {
   int dbt;     // positions per backtrack sub-chunk (>= K)
   int nsub;    // ceil(T / dbt)
   int center;
+  // Decisions of the absolute sweep (kAbs): chunks aj0 .. aj0+anj-1 of every
+  // sequence; the decision of (t, c) at bp[(b*C + c)*bp_stride + t - bp_t0].
+  // The whole sequence: aj0 = 0, anj = nchunk, bp_t0 = 0, bp_stride = T+1;
+  // the low-memory decoder sweeps one window of chunks at a time.
+  int aj0, anj, bp_t0, bp_stride;
+  int lm_w;    // low-memory decoder: chunks per window (0: decisions kept whole)
+  // Backtrack range: positions (wp0, wp1] in wsub sub-chunks of dbt, their
+  // predecessor words and marks at (t - bp_t0) with stride bp_stride as the
+  // decisions, walk lists at (t - wp0) with stride lst_stride.  The whole
+  // sequence: wp0 = 0, wp1 = T, wsub = nsub, lst_stride = T.
+  int wp0, wp1, wsub, lst_stride;
 };
 
 constexpr int kVitIters = 2;     // parallel verification passes before the serial repair
@@ -364,6 +376,8 @@ struct VBufs {
   int32_t *lst_t, *lst_c;  // [B][T] guessed backtrack walks, by sub-chunk
   int32_t *mark;       // [B][T+1] walk index * 512 + label of the node ending at t, or -1
   int32_t *sub;        // [B][nsub][kVSubFields]
+  int32_t *node;       // low-memory decoder: [B][3] entry node (t, label) of the next
+                       // window's walk (t = -1: not started), segments found so far
 };
 
 inline size_t vit_lds_bytes(int C, int K, int U) {

@@ -164,7 +164,9 @@ __device__ __forceinline__ void vsweep(const VShape &vs, const VRegs<AMAX, CAMAX
 
   const int c = r.on ? r.c : 0, g = r.g;
   const double ninf = -__builtin_huge_val();
-  uint32_t *bpc = vb.bp + ((size_t)b * C + c) * (T + 1);
+  // decisions of (t, c) at bpc[t - bp_t0] (kAbs only)
+  uint32_t *bpc = vb.bp + ((size_t)b * C + c) * vs.bp_stride;
+  const int bt0 = vs.bp_t0;
   int kslot = (((q - g) % K) + K) % K;  // slot of position t - 1 - g at t = q + 1
   int tslot = (q + 1) % K;              // slot of position t
   double sreg = 0.0;  // this thread's staged score of the next block (U*C <= NT)
@@ -286,7 +288,7 @@ __device__ __forceinline__ void vsweep(const VShape &vs, const VRegs<AMAX, CAMAX
     if (mode == kAbs) {
       if (g == w) dec = (uint32_t)(kb & 0xffff) | ((uint32_t)cb << 16);
       if (w == U - 1 || s + 1 == nsteps) {
-        if (r.on && g <= w) bpc[t - w + g] = dec;
+        if (r.on && g <= w) bpc[t - w + g - bt0] = dec;
       }
     }
     kslot = kslot + 1 == K ? 0 : kslot + 1;
@@ -378,7 +380,9 @@ __global__ __launch_bounds__(NT) void k_vsweep(VShape vs, int mode, int iter,
                                                const double *__restrict__ S,
                                                const int32_t *__restrict__ lengths, VBufs vb) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const int b = blockIdx.x / vs.nchunk, j = blockIdx.x % vs.nchunk;
+  // kAbs: the chunks aj0 .. aj0+anj-1 (all of them, or one low-memory window)
+  const int nj = mode == kAbs ? vs.anj : vs.nchunk, j0 = mode == kAbs ? vs.aj0 : 0;
+  const int b = blockIdx.x / nj, j = j0 + blockIdx.x % nj;
   const int L = lengths[b];
   if (L < 1 || L > vs.T) {
     if (mode == kAbs && j == 0 && threadIdx.x == 0) {
@@ -465,32 +469,49 @@ __global__ __launch_bounds__(64) void k_vfix(VShape vs, const int32_t *__restric
 // ------------------------------------------------------------ backtrack
 
 // pred[t, c] = k | (label of the segment before) << 16 for the segment of
-// label c ending at t, from the decisions (0xffff: no segment before).
+// label c ending at t, from the decisions (0xffff: no segment before), for
+// t in (wp0, wp1] (its start t - k > wp0 - K lies inside the decisions).
 __global__ __launch_bounds__(kVHelp) void k_vpred(VShape vs, const int32_t *__restrict__ lengths,
                                                   VBufs vb) {
-  const int T1 = vs.T + 1, C = vs.C;
-  const size_t n = (size_t)vs.B * C * T1;
+  const int C = vs.C, nw = vs.wp1 - vs.wp0;
+  const size_t n = (size_t)vs.B * C * nw;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
-    const int t = (int)(i % T1);
-    const size_t bc = i / T1;
+    const int t = vs.wp0 + 1 + (int)(i % nw);
+    const size_t bc = i / nw;
     const int b = (int)(bc / C);
     const int L = lengths[b];
-    if (t < 1 || L < 1 || L > vs.T || t > L) continue;
-    int k = (int)(vb.bp[i] & 0xffffu);
+    if (L < 1 || L > vs.T || t > L) continue;
+    const size_t o = bc * vs.bp_stride + (t - vs.bp_t0);
+    int k = (int)(vb.bp[o] & 0xffffu);
     if (k < 1 || k > t) k = t;  // only reachable with non-finite scores
     const int s = t - k;
     uint32_t prev = 0xffffu;
     if (s > 0) {
-      prev = vb.bp[i - k] >> 16;
+      prev = vb.bp[o - k] >> 16;
       if (prev >= (uint32_t)C) prev = 0;  // only reachable with non-finite scores
     }
-    vb.pred[i] = (uint32_t)k | (prev << 16);
+    vb.pred[o] = (uint32_t)k | (prev << 16);
   }
 }
 
 __device__ __forceinline__ int32_t *sub_of(const VShape &vs, const VBufs &vb, int b, int j) {
-  return vb.sub + ((size_t)b * vs.nsub + j) * kVSubFields;
+  return vb.sub + ((size_t)b * vs.wsub + j) * kVSubFields;
+}
+
+// The entry node of the range's last sub-chunk: the path's end (L, best
+// final label) when it lies in the range, else the exit of the walk through
+// the range after it (low-memory windows).
+__device__ __forceinline__ void range_entry(const VShape &vs, const VBufs &vb, int b, int L,
+                                            int &t, int &c) {
+  if (L <= vs.wp1) {
+    t = L;
+    c = vb.vcbest[b];
+    if (c < 0 || c >= vs.C) c = 0;  // only reachable with non-finite scores
+  } else {
+    t = vb.node[3 * (size_t)b];
+    c = vb.node[3 * (size_t)b + 1];
+  }
 }
 
 // One thread per (sequence, sub-chunk): walk back from a guessed entry node
@@ -499,28 +520,26 @@ __device__ __forceinline__ int32_t *sub_of(const VShape &vs, const VBufs &vb, in
 __global__ __launch_bounds__(kVHelp) void k_vwalk(VShape vs, const int32_t *__restrict__ lengths,
                                                   VBufs vb) {
   const int id = blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= vs.B * vs.nsub) return;
-  const int b = id / vs.nsub, j = id % vs.nsub;
+  if (id >= vs.B * vs.wsub) return;
+  const int b = id / vs.wsub, j = id % vs.wsub;
   const int L = lengths[b];
   if (L < 1 || L > vs.T) return;
-  const int lo = j * vs.dbt;
-  if (lo >= L) return;
-  const int hi = min(lo + vs.dbt, L), C = vs.C, T1 = vs.T + 1;
-  int32_t *mk = vb.mark + (size_t)b * T1;
-  for (int t = lo + 1; t <= hi; ++t) mk[t] = -1;
+  const int lo = vs.wp0 + j * vs.dbt, top = min(vs.wp1, L);
+  if (lo >= top) return;
+  const int hi = min(lo + vs.dbt, top), C = vs.C, T1 = vs.bp_stride, t0 = vs.bp_t0;
+  int32_t *mk = vb.mark + (size_t)b * T1;  // position t at mk[t - t0]
+  for (int t = lo + 1; t <= hi; ++t) mk[t - t0] = -1;
   int t = hi, c = 0;
-  if (hi == L) {
-    c = vb.vcbest[b];
-    if (c < 0 || c >= C) c = 0;
-  }
+  if (hi == top) range_entry(vs, vb, b, L, t, c);
   const uint32_t *pr = vb.pred + (size_t)b * C * T1;
-  int32_t *lt = vb.lst_t + (size_t)b * vs.T + lo, *lc = vb.lst_c + (size_t)b * vs.T + lo;
+  int32_t *lt = vb.lst_t + (size_t)b * vs.lst_stride + (lo - vs.wp0);
+  int32_t *lc = vb.lst_c + (size_t)b * vs.lst_stride + (lo - vs.wp0);
   int n = 0;
   while (t > lo) {
-    const uint32_t w = pr[(size_t)c * T1 + t];
+    const uint32_t w = pr[(size_t)c * T1 + (t - t0)];
     lt[n] = t;
     lc[n] = c;
-    mk[t] = n * 512 + c;
+    mk[t - t0] = n * 512 + c;
     ++n;
     t -= (int)(w & 0xffffu);
     c = (int)(w >> 16);
@@ -535,7 +554,7 @@ __global__ __launch_bounds__(kVHelp) void k_vwalk(VShape vs, const int32_t *__re
 // node of the sub-chunk's guessed walk; record the head length, the merge
 // index and the exit of the true path.
 __device__ void vmerge_one(const VShape &vs, const VBufs &vb, int b, int j, int t, int c) {
-  const int lo = j * vs.dbt, C = vs.C, T1 = vs.T + 1;
+  const int lo = vs.wp0 + j * vs.dbt, C = vs.C, T1 = vs.bp_stride, t0 = vs.bp_t0;
   const int32_t *mk = vb.mark + (size_t)b * T1;
   const uint32_t *pr = vb.pred + (size_t)b * C * T1;
   int32_t *f = sub_of(vs, vb, b, j);
@@ -543,12 +562,12 @@ __device__ void vmerge_one(const VShape &vs, const VBufs &vb, int b, int j, int 
   f[kSubEnC] = c;
   int h = 0, mi = -1;
   while (t > lo) {
-    const int m = mk[t];
+    const int m = mk[t - t0];
     if (m >= 0 && (m & 511) == c) {
       mi = m >> 9;
       break;
     }
-    const uint32_t w = pr[(size_t)c * T1 + t];
+    const uint32_t w = pr[(size_t)c * T1 + (t - t0)];
     ++h;
     t -= (int)(w & 0xffffu);
     c = (int)(w >> 16);
@@ -568,18 +587,16 @@ __device__ void vmerge_one(const VShape &vs, const VBufs &vb, int b, int j, int 
 __global__ __launch_bounds__(kVHelp) void k_vmerge(VShape vs, const int32_t *__restrict__ lengths,
                                                    VBufs vb) {
   const int id = blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= vs.B * vs.nsub) return;
-  const int b = id / vs.nsub, j = id % vs.nsub;
+  if (id >= vs.B * vs.wsub) return;
+  const int b = id / vs.wsub, j = id % vs.wsub;
   const int L = lengths[b];
   if (L < 1 || L > vs.T) return;
-  const int lo = j * vs.dbt;
-  if (lo >= L) return;
-  const int hi = min(lo + vs.dbt, L);
+  const int lo = vs.wp0 + j * vs.dbt, top = min(vs.wp1, L);
+  if (lo >= top) return;
+  const int hi = min(lo + vs.dbt, top);
   int t, c;
-  if (hi == L) {
-    t = L;
-    c = vb.vcbest[b];
-    if (c < 0 || c >= vs.C) c = 0;
+  if (hi == top) {
+    range_entry(vs, vb, b, L, t, c);
   } else {
     const int32_t *fn = sub_of(vs, vb, b, j + 1);
     t = fn[kSubExT];
@@ -597,14 +614,16 @@ __global__ __launch_bounds__(kVHelp) void k_vfinish(VShape vs, const int32_t *__
   __shared__ int red[kVHelp];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int L = lengths[b];
+  const bool win = vs.lm_w > 0;  // one window of a low-memory decode
   if (L < 1 || L > vs.T) {
-    if (tid == 0) {
+    if (tid == 0 && !win) {
       num_segs[b] = 0;
       best_out[b] = __builtin_nanf("");
     }
     return;
   }
-  const int nv = (L + vs.dbt - 1) / vs.dbt;
+  if (L <= vs.wp0) return;  // the path ends before this window
+  const int nv = (min(vs.wp1, L) - vs.wp0 + vs.dbt - 1) / vs.dbt;
   auto mismatch = [&](int j) {
     const int32_t *f = sub_of(vs, vb, b, j), *fn = sub_of(vs, vb, b, j + 1);
     return f[kSubEnT] != fn[kSubTxT] || f[kSubEnC] != fn[kSubTxC];
@@ -646,8 +665,21 @@ __global__ __launch_bounds__(kVHelp) void k_vfinish(VShape vs, const int32_t *__
       red[q] = run;
       run += v;
     }
-    num_segs[b] = run;
-    best_out[b] = (float)vb.vbest[b];
+    if (win) {
+      // the window's segments go to row slots [T - after - run, T - after)
+      // (after: the segments of the windows behind it); the exit of the
+      // first sub-chunk's true path is the next window's entry
+      int32_t *nd = vb.node + 3 * (size_t)b;
+      const int after = nd[2], base = vs.T - after - run;
+      for (int q = 0; q < kVHelp; ++q) red[q] += base;
+      const int32_t *f0 = sub_of(vs, vb, b, 0);
+      nd[0] = f0[kSubTxT];
+      nd[1] = f0[kSubTxC];
+      nd[2] = after + run;
+    } else {
+      num_segs[b] = run;
+      best_out[b] = (float)vb.vbest[b];
+    }
   }
   __syncthreads();
   int run = red[tid];
@@ -665,13 +697,13 @@ __global__ __launch_bounds__(kVHelp) void k_vwrite(VShape vs, const int32_t *__r
                                                    int32_t *__restrict__ seg_len,
                                                    int32_t *__restrict__ seg_label) {
   const int id = blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= vs.B * vs.nsub) return;
-  const int b = id / vs.nsub, j = id % vs.nsub;
+  if (id >= vs.B * vs.wsub) return;
+  const int b = id / vs.wsub, j = id % vs.wsub;
   const int L = lengths[b];
   if (L < 1 || L > vs.T) return;
-  const int lo = j * vs.dbt;
-  if (lo >= L) return;
-  const int C = vs.C, T1 = vs.T + 1;
+  const int lo = vs.wp0 + j * vs.dbt;
+  if (lo >= min(vs.wp1, L)) return;
+  const int C = vs.C, T1 = vs.bp_stride, t0 = vs.bp_t0;
   const int32_t *f = sub_of(vs, vb, b, j);
   const int h = f[kSubH], n = f[kSubN], mi = f[kSubMi];
   const int cnt = h + n - mi, off = f[kSubOff];
@@ -680,7 +712,7 @@ __global__ __launch_bounds__(kVHelp) void k_vwrite(VShape vs, const int32_t *__r
           *sc = seg_label + (size_t)b * vs.T;
   int t = f[kSubEnT], c = f[kSubEnC];
   for (int w = 0; w < h; ++w) {
-    const uint32_t p = pr[(size_t)c * T1 + t];
+    const uint32_t p = pr[(size_t)c * T1 + (t - t0)];
     const int k = (int)(p & 0xffffu), o = off + cnt - 1 - w;
     ss[o] = t - k;
     sl[o] = k;
@@ -688,10 +720,11 @@ __global__ __launch_bounds__(kVHelp) void k_vwrite(VShape vs, const int32_t *__r
     t -= k;
     c = (int)(p >> 16);
   }
-  const int32_t *lt = vb.lst_t + (size_t)b * vs.T + lo, *lc = vb.lst_c + (size_t)b * vs.T + lo;
+  const int32_t *lt = vb.lst_t + (size_t)b * vs.lst_stride + (lo - vs.wp0);
+  const int32_t *lc = vb.lst_c + (size_t)b * vs.lst_stride + (lo - vs.wp0);
   for (int i = mi; i < n; ++i) {
     const int tt = lt[i], cc = lc[i];
-    const int k = (int)(pr[(size_t)cc * T1 + tt] & 0xffffu);
+    const int k = (int)(pr[(size_t)cc * T1 + (tt - t0)] & 0xffffu);
     const int o = off + cnt - 1 - (h + i - mi);
     ss[o] = tt - k;
     sl[o] = k;
@@ -715,9 +748,76 @@ __global__ __launch_bounds__(kVHelp) void k_vpad(int B, int T, const int32_t *__
   }
 }
 
+// ------------------------------------------------- low-memory backtrack
+
+// node[b] = {t, c, n}: the entry node of the next window's walk (the
+// segment of label c that ends at t; t = -1 before the path's last window)
+// and the number of segments found so far.
+__global__ __launch_bounds__(64) void k_vlm_init(VShape vs, VBufs vb) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= vs.B) return;
+  vb.node[3 * (size_t)b] = -1;
+  vb.node[3 * (size_t)b + 1] = 0;
+  vb.node[3 * (size_t)b + 2] = 0;
+}
+
+// One workgroup per sequence: its n segments sit at row slots [T - n, T) in
+// start order; move them to [0, n), blocks in increasing order, each block
+// read before any of it is written (a destination block never reaches a
+// later block's source: T - n >= 0); then the count and the best score.
+__global__ __launch_bounds__(kVHelp) void k_vlm_finish(VShape vs,
+                                                       const int32_t *__restrict__ lengths,
+                                                       VBufs vb, float *__restrict__ best_out,
+                                                       int32_t *seg_start, int32_t *seg_len,
+                                                       int32_t *seg_label,
+                                                       int32_t *__restrict__ num_segs) {
+  const int b = blockIdx.x, T = vs.T;
+  const int L = lengths[b];
+  const bool ok = L >= 1 && L <= T;
+  const int n = ok ? vb.node[3 * (size_t)b + 2] : 0;
+  const size_t base = (size_t)b * T;
+  for (int i0 = 0; i0 < n; i0 += kVHelp) {
+    const int i = i0 + threadIdx.x;
+    int32_t st = 0, ln = 0, lb = 0;
+    if (i < n) {
+      st = seg_start[base + T - n + i];
+      ln = seg_len[base + T - n + i];
+      lb = seg_label[base + T - n + i];
+    }
+    __syncthreads();
+    if (i < n) {
+      seg_start[base + i] = st;
+      seg_len[base + i] = ln;
+      seg_label[base + i] = lb;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    num_segs[b] = n;
+    best_out[b] = ok ? (float)vb.vbest[b] : __builtin_nanf("");
+  }
+}
+
+int grid_for(size_t n);
+hipError_t vit_backtrack(const VShape &vs, const int32_t *lengths, const VBufs &vb,
+                         float *best_out, int32_t *seg_start, int32_t *seg_len,
+                         int32_t *seg_label, int32_t *num_segs, hipStream_t st, bool pad);
+
+template <int NT, int AMAX, int CAMAX, int NGT>
+hipError_t vsweep_abs(const VShape &vs, const float *trans, const float *dur, const double *S,
+                      const int32_t *lengths, const VBufs &vb, hipStream_t st) {
+  const size_t lds = vit_lds_bytes(vs.C, vs.K, vs.U);
+  hipLaunchKernelGGL((k_vsweep<NT, AMAX, CAMAX, NGT>), dim3(vs.B * vs.anj), dim3(NT), lds, st, vs,
+                     (int)kAbs, 0, trans, dur, S, lengths, vb);
+  return hipGetLastError();
+}
+
+// The parallel-in-time passes: relative sweeps, verification, repair and
+// frame offsets; then (abs) the absolute sweep of vs.aj0 .. that stores the
+// decisions.
 template <int NT, int AMAX, int CAMAX, int NGT>
 hipError_t vsweeps(const VShape &vs, const float *trans, const float *dur, const double *S,
-                   const int32_t *lengths, const VBufs &vb, hipStream_t st) {
+                   const int32_t *lengths, const VBufs &vb, bool abs, hipStream_t st) {
   const size_t lds = vit_lds_bytes(vs.C, vs.K, vs.U);
   static bool attr = false;
   if (!attr) {
@@ -747,9 +847,69 @@ hipError_t vsweeps(const VShape &vs, const float *trans, const float *dur, const
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_vfix, dim3((vs.B + 63) / 64), dim3(64), 0, st, vs, lengths, vb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_vsweep<NT, AMAX, CAMAX, NGT>), dim3(nck), dim3(NT), lds, st, vs, (int)kAbs, 0,
-                     trans, dur, S, lengths, vb);
+  return abs ? vsweep_abs<NT, AMAX, CAMAX, NGT>(vs, trans, dur, S, lengths, vb, st) : hipSuccess;
+}
+
+// Low-memory decoding (working memory sublinear in T beyond the cumulative
+// scores; the pages' recompute-between-checkpoints, technical summary 2.C,
+// in the max semiring): the parallel passes keep only the chunk start
+// states; then, window by window from the end of the sequences, the
+// absolute sweep recomputes the decisions of the window's chunks -- and of
+// the chunk before, whose last K positions hold the previous labels of the
+// segments that start in the window -- into buffers of one window, and the
+// parallel backtrack (sub-chunk walks, merge, count, write) runs on the
+// window, entered where the window after it left the path.  Segments are
+// found window by window from the end and written from the end of the
+// output rows (k_vfinish places them); k_vlm_finish moves them to the front.
+// The decisions are the whole-sequence sweep's (same start states, same
+// arithmetic), so the segmentation is the same.
+template <int NT, int AMAX, int CAMAX, int NGT>
+hipError_t vit_lowmem(const VShape &vs, const float *trans, const float *dur, const double *S,
+                      const int32_t *lengths, const VBufs &vb, float *best_out,
+                      int32_t *seg_start, int32_t *seg_len, int32_t *seg_label,
+                      int32_t *num_segs, hipStream_t st) {
+  hipError_t e = vsweeps<NT, AMAX, CAMAX, NGT>(vs, trans, dur, S, lengths, vb, false, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_vlm_init, dim3((vs.B + 63) / 64), dim3(64), 0, st, vs, vb);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int W = vs.lm_w, nwin = (vs.nchunk + W - 1) / W;
+  for (int w = nwin - 1; w >= 0; --w) {
+    const int j0 = w * W, j1 = min(j0 + W, vs.nchunk);
+    VShape ws = vs;
+    ws.aj0 = j0 > 0 ? j0 - 1 : 0;
+    ws.anj = j1 - ws.aj0;
+    ws.bp_t0 = ws.aj0 * vs.delta;
+    ws.wp0 = j0 * vs.delta;
+    ws.wp1 = min(j1 * vs.delta, vs.T);
+    ws.bp_stride = ws.wp1 - ws.bp_t0 + 1;
+    ws.wsub = (ws.wp1 - ws.wp0 + vs.dbt - 1) / vs.dbt;
+    ws.lst_stride = W * vs.delta;
+    e = vsweep_abs<NT, AMAX, CAMAX, NGT>(ws, trans, dur, S, lengths, vb, st);
+    if (e != hipSuccess) return e;
+    e = vit_backtrack(ws, lengths, vb, best_out, seg_start, seg_len, seg_label, num_segs, st,
+                      false);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_vlm_finish, dim3(vs.B), dim3(kVHelp), 0, st, vs, lengths, vb, best_out,
+                     seg_start, seg_len, seg_label, num_segs);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_vpad, dim3(grid_for((size_t)vs.B * vs.T)), dim3(kVHelp), 0, st, vs.B,
+                     vs.T, num_segs, seg_start, seg_len, seg_label);
   return hipGetLastError();
+}
+
+// The whole decoder for one kernel instance.
+template <int NT, int AMAX, int CAMAX, int NGT>
+hipError_t vit_run(const VShape &vs, const float *trans, const float *dur, const double *S,
+                   const int32_t *lengths, const VBufs &vb, float *best_out, int32_t *seg_start,
+                   int32_t *seg_len, int32_t *seg_label, int32_t *num_segs, hipStream_t st) {
+  if (vs.lm_w > 0)
+    return vit_lowmem<NT, AMAX, CAMAX, NGT>(vs, trans, dur, S, lengths, vb, best_out, seg_start,
+                                            seg_len, seg_label, num_segs, st);
+  hipError_t e = vsweeps<NT, AMAX, CAMAX, NGT>(vs, trans, dur, S, lengths, vb, true, st);
+  if (e != hipSuccess) return e;
+  return vit_backtrack(vs, lengths, vb, best_out, seg_start, seg_len, seg_label, num_segs, st,
+                       true);
 }
 
 int grid_for(size_t n) {
@@ -795,6 +955,15 @@ bool vit_config(int B, int T, int C, int K, VShape &vs) {
   vs.burn = 2 * K > vs.delta / 4 ? 2 * K : vs.delta / 4;
   vs.dbt = K > 128 ? K : 128;
   vs.nsub = (T + vs.dbt - 1) / vs.dbt;
+  vs.aj0 = 0;
+  vs.anj = vs.nchunk;
+  vs.bp_t0 = 0;
+  vs.bp_stride = T + 1;
+  vs.lm_w = 0;
+  vs.wp0 = 0;
+  vs.wp1 = T;
+  vs.wsub = vs.nsub;
+  vs.lst_stride = T;
   return true;
 }
 
@@ -802,30 +971,35 @@ hipError_t launch_vit_pit(const VShape &vs, const float *trans, const float *dur
                           const double *S, const int32_t *lengths, const VBufs &vb,
                           float *best_out, int32_t *seg_start, int32_t *seg_len,
                           int32_t *seg_label, int32_t *num_segs, hipStream_t st) {
-  hipError_t e;
   // instances: durations per lane (<= 4, <= 16) x previous labels per lane
   // (<= 4 at any group width; <= 16 at width 8, C <= 128; <= 64 at width 4)
   const bool a4 = vs.A <= 4;
+#define SEMICRF_VIT_RUN(...) \
+  vit_run<__VA_ARGS__>(vs, trans, dur, S, lengths, vb, best_out, seg_start, seg_len, seg_label, \
+                       num_segs, st)
   if (vs.NT == 256)  // C <= 4: one previous label per lane
-    e = a4 ? vsweeps<256, 4, 4, 0>(vs, trans, dur, S, lengths, vb, st)
-           : vsweeps<256, 16, 4, 0>(vs, trans, dur, S, lengths, vb, st);
-  else if (vs.NT == 512)  // at most 4 previous labels per lane
-    e = a4 ? vsweeps<512, 4, 4, 0>(vs, trans, dur, S, lengths, vb, st)
-           : vsweeps<512, 16, 4, 0>(vs, trans, dur, S, lengths, vb, st);
-  else if (vs.CA <= 4)
-    e = a4 ? vsweeps<1024, 4, 4, 0>(vs, trans, dur, S, lengths, vb, st)
-           : vsweeps<1024, 16, 4, 0>(vs, trans, dur, S, lengths, vb, st);
-  else if (vs.NG == 8)
-    e = a4 ? vsweeps<1024, 4, 16, 8>(vs, trans, dur, S, lengths, vb, st)
-           : vsweeps<1024, 16, 16, 8>(vs, trans, dur, S, lengths, vb, st);
-  else
-    e = a4 ? vsweeps<1024, 4, 64, 4>(vs, trans, dur, S, lengths, vb, st)
-           : vsweeps<1024, 16, 64, 4>(vs, trans, dur, S, lengths, vb, st);
-  if (e != hipSuccess) return e;
-  const size_t npred = (size_t)vs.B * vs.C * (vs.T + 1);
+    return a4 ? SEMICRF_VIT_RUN(256, 4, 4, 0) : SEMICRF_VIT_RUN(256, 16, 4, 0);
+  if (vs.NT == 512)  // at most 4 previous labels per lane
+    return a4 ? SEMICRF_VIT_RUN(512, 4, 4, 0) : SEMICRF_VIT_RUN(512, 16, 4, 0);
+  if (vs.CA <= 4) return a4 ? SEMICRF_VIT_RUN(1024, 4, 4, 0) : SEMICRF_VIT_RUN(1024, 16, 4, 0);
+  if (vs.NG == 8) return a4 ? SEMICRF_VIT_RUN(1024, 4, 16, 8) : SEMICRF_VIT_RUN(1024, 16, 16, 8);
+  return a4 ? SEMICRF_VIT_RUN(1024, 4, 64, 4) : SEMICRF_VIT_RUN(1024, 16, 64, 4);
+#undef SEMICRF_VIT_RUN
+}
+
+namespace {
+
+// The parallel backtrack over the decisions of positions (wp0, wp1]: the
+// whole sequence, or one low-memory window (then no padding: the segments
+// are moved into place at the end).
+hipError_t vit_backtrack(const VShape &vs, const int32_t *lengths, const VBufs &vb,
+                         float *best_out, int32_t *seg_start, int32_t *seg_len,
+                         int32_t *seg_label, int32_t *num_segs, hipStream_t st, bool pad) {
+  hipError_t e;
+  const size_t npred = (size_t)vs.B * vs.C * (vs.wp1 - vs.wp0);
   hipLaunchKernelGGL(k_vpred, dim3(grid_for(npred)), dim3(kVHelp), 0, st, vs, lengths, vb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int nsub = vs.B * vs.nsub;
+  const int nsub = vs.B * vs.wsub;
   const int gs = (nsub + kVHelp - 1) / kVHelp;
   hipLaunchKernelGGL(k_vwalk, dim3(gs), dim3(kVHelp), 0, st, vs, lengths, vb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -837,9 +1011,12 @@ hipError_t launch_vit_pit(const VShape &vs, const float *trans, const float *dur
   hipLaunchKernelGGL(k_vwrite, dim3(gs), dim3(kVHelp), 0, st, vs, lengths, vb, seg_start,
                      seg_len, seg_label);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!pad) return hipSuccess;
   hipLaunchKernelGGL(k_vpad, dim3(grid_for((size_t)vs.B * vs.T)), dim3(kVHelp), 0, st, vs.B,
                      vs.T, num_segs, seg_start, seg_len, seg_label);
   return hipGetLastError();
 }
+
+}  // namespace
 
 }  // namespace semicrf

@@ -55,9 +55,10 @@ def gpu_logz(inp, center=True, float64=False):
     return out.cpu().numpy().astype(np.float64)
 
 
-def gpu_viterbi(inp, center=True):
+def gpu_viterbi(inp, center=True, low_memory=False):
     t = to_dev(inp)
-    out = bd.semicrf_viterbi(t["emissions"], t["lengths"], t["trans"], t["dur"], center=center)
+    out = bd.semicrf_viterbi(t["emissions"], t["lengths"], t["trans"], t["dur"], center=center,
+                             low_memory=low_memory)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 

@@ -110,6 +110,19 @@ def test_float64_flag_selects_the_float64_sweep(lib):
         assert m.value == n32.value
 
 
+def test_low_memory_viterbi_workspace(lib):
+    # the whole decoder keeps decisions and predecessor words for every
+    # position (8 bytes per position and label); the low-memory decoder keeps
+    # one window of chunks.  extreme: B=1, T=2^20, C=64, K=256
+    full, low = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    args = (bd.OP_VITERBI, 1, 1 << 20, 64, 256)
+    assert lib.semicrf_workspace_size(*args, 0, 0, ctypes.byref(full)) == 0
+    assert lib.semicrf_workspace_size(*args, bd.LOW_MEMORY, 0, ctypes.byref(low)) == 0
+    S = 8 * ((1 << 20) + 1) * 64
+    assert full.value - S > 8 * (1 << 20) * 64  # beyond the scores: decisions of every position
+    assert low.value - S < 0.15 * (full.value - S)
+
+
 def test_supported_workloads_have_a_configuration(lib):
     from semi_markov_crf_zero_amd.workloads import WORKLOADS
     for w in WORKLOADS.values():
