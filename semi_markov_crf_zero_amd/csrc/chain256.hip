@@ -56,6 +56,7 @@
 
 #include "device_math.h"
 #include "internal.h"
+#include "pitcheck.h"
 
 namespace semicrf {
 
@@ -532,17 +533,21 @@ __device__ __forceinline__ void block256(Sweep256 &c, int base,
 // the same launch grid, start states, records ([K][C] ring by slot, then R,
 // o, m), verification hand-off, log Z of the tail chunk and replay windows.
 // CL: K < 64 (ring registers past K exist; see rescale16).
-template <bool CL>
+template <bool CL, bool REP>
 __global__ __launch_bounds__(kNT) void k_sweep256(ChainShape sh, const float *__restrict__ trans,
                                                   const float *__restrict__ dur, Escaled es,
                                                   const int32_t *__restrict__ lengths,
                                                   PitBufs pb, int iter) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int nck = sh.B * sh.nchunk;
-  const bool replay = iter < 0;
+  const bool replay = iter == -1;
   bool fwd;
   int b, jc;
-  if (replay) {
+  if (REP) {  // the in-order repair: one workgroup per (direction, sequence)
+    fwd = (int)blockIdx.x < sh.B;
+    b = fwd ? blockIdx.x : blockIdx.x - sh.B;
+    jc = 0;
+  } else if (replay) {
     const int nf = sh.B * sh.rnf;
     fwd = (int)blockIdx.x < nf;
     const int nj = fwd ? sh.rnf : sh.rnb;
@@ -555,8 +560,9 @@ __global__ __launch_bounds__(kNT) void k_sweep256(ChainShape sh, const float *__
     b = rem / sh.nchunk;
     jc = rem % sh.nchunk;
   }
-  const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + jc;
-  if (iter == 0) {  // the parallel-in-time state, before any verification reads it
+  const size_t base = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk;  // this chain's flags
+  const size_t idx = base + jc;
+  if (!REP && iter == 0) {  // the parallel-in-time state, before any verification reads it
     if (threadIdx.x == 0) {
       pb.redo[idx] = 1;
       pb.corr_i[idx] = 0;
@@ -568,18 +574,24 @@ __global__ __launch_bounds__(kNT) void k_sweep256(ChainShape sh, const float *__
   const int L = lengths[b];
   const int tid = threadIdx.x, C = sh.C, K = sh.K, T = sh.T;
   if (L < 1 || L > T || jc >= sh.nchunk) return;
-  const int p0 = jc * sh.delta;
-  if (p0 >= L) return;
-  const int p1 = min(p0 + sh.delta, L);
-  if (iter > 0 && (pb.nbad[iter - 1] == 0 || pb.redo[idx] == 0)) return;
+  if (jc * sh.delta >= L) return;
+  const int nvalid = (L + sh.delta - 1) / sh.delta;
+  __shared__ PitMaxArg red[kNT / 64];  // scratch of the repair's checks
+  __shared__ double redd[kNT / 64];
+  if constexpr (REP) {
+    // nothing to repair unless the last parallel check found a chunk of
+    // this chain inconsistent
+    if (pb.nbad[kPitParallelIters - 1] == 0) return;
+    int marked = 0;
+    for (int j = tid; j < nvalid; j += kNT) marked |= pb.redo[base + j];
+    if (!pit_any<kNT>(marked != 0, red)) return;
+  } else {
+    if (iter > 0 && (pb.nbad[iter - 1] == 0 || pb.redo[idx] == 0)) return;
+  }
   const size_t ob = (size_t)b * (T + 1) * C;
   const size_t cks = ck_stride(C, K);
   const size_t kc = (size_t)K * C;
-  double *rec_start = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
-  double *rec_end = (fwd ? pb.end_fwd : pb.end_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
   const int isig = fwd ? 1 : -1;
-  const int tstart = fwd ? p0 : p1;
-  const bool tail = fwd ? (p1 == L) : (p0 == 0);
   const bool rows = pb.row_a != nullptr;
   const size_t orow = (size_t)b * pb.row_stride * C;
 
@@ -607,8 +619,6 @@ __global__ __launch_bounds__(kNT) void k_sweep256(ChainShape sh, const float *__
   c.drl = c.sm.dr + (size_t)kA * c.q * kLab + c.cl;
   const int cl = c.cl, q = c.q;
   const bool label = c.label;
-  // exp(trans) of the contraction role: input 32w + i, output 4 lane + r
-  // (forward: previous label -> label; backward: label -> next label)
   // exp(trans) of the contraction role: input 32w + i, output 4 lane + r
   // (forward: previous label -> label; backward: label -> next label),
   // formed by loops (one copy of the exponential's code) through LDS and
@@ -671,109 +681,138 @@ __global__ __launch_bounds__(kNT) void k_sweep256(ChainShape sh, const float *__
     }
   };
 
-  const bool exact = fwd ? (jc == 0) : (p1 == L);
-  const int wb = (iter == 0 && !exact) ? min(sh.burn, fwd ? p0 : L - p1) : 0;
-  const int tb = fwd ? p0 - wb : p1 + wb;  // where the sweep starts
-  for (int seg = wb > 0 ? 0 : 1; seg < 2; ++seg) {
-    const bool main = seg == 1;
-    c.t0 = main ? tstart : tb;
-    c.nrun = main ? p1 - p0 : wb;
-    c.rows = rows && main;
-    c.lz_tail = main && tail;
-    // ---- the start state, head 0
-    c.R = 0;
-    if (iter == 0 && (!main || wb == 0)) {
-      if (exact) {
-        // entry u[0] - S[0] = 0 forward; beta[L] + S[L] = S[L] backward
-        double v = 1.0;
-        if (!fwd) {
-          double em;
-          exp_split_t(c.S[(size_t)L * C + (label ? cl : 0)], v, em, c.R, c.sm.tab);
+  // one chunk, p0 .. p1, from its start record (or, at iteration 0, from
+  // its exact or neutral start after the burn-in)
+  auto sweep_chunk = [&](const int jc) __attribute__((always_inline)) {
+    const int p0 = jc * sh.delta;
+    const int p1 = min(p0 + sh.delta, L);
+    double *rec_start = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
+    double *rec_end = (fwd ? pb.end_fwd : pb.end_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
+    const int tstart = fwd ? p0 : p1;
+    const bool tail = fwd ? (p1 == L) : (p0 == 0);
+    const bool exact = fwd ? (jc == 0) : (p1 == L);
+    const int wb = (iter == 0 && !exact) ? min(sh.burn, fwd ? p0 : L - p1) : 0;
+    const int tb = fwd ? p0 - wb : p1 + wb;  // where the sweep starts
+    for (int seg = wb > 0 ? 0 : 1; seg < 2; ++seg) {
+      const bool main = seg == 1;
+      c.t0 = main ? tstart : tb;
+      c.nrun = main ? p1 - p0 : wb;
+      c.rows = rows && main;
+      c.lz_tail = main && tail;
+      // ---- the start state, head 0
+      c.R = 0;
+      if (iter == 0 && (!main || wb == 0)) {
+        if (exact) {
+          // entry u[0] - S[0] = 0 forward; beta[L] + S[L] = S[L] backward
+          double v = 1.0;
+          if (!fwd) {
+            double em;
+            exp_split_t(c.S[(size_t)L * C + (label ? cl : 0)], v, em, c.R, c.sm.tab);
+          }
+          if (!label) {
+            c.R = 0;
+            v = 0.0;
+          }
+  #pragma unroll
+          for (int j = 0; j < kA; ++j) c.r[j] = (q == 0 && j == 0) ? (float)v : 0.0f;
+        } else {
+          // neutral start: every entry of the window (positions inside [0, L]) is 1
+  #pragma unroll
+          for (int j = 0; j < kA; ++j) {
+            const int pos = c.t0 - isig * (kA * q + j);
+            c.r[j] = (label && kA * q + 1 + j <= K && pos >= 0 && pos <= L) ? 1.0f : 0.0f;
+          }
         }
-        if (!label) {
-          c.R = 0;
-          v = 0.0;
+        if (main) {
+          save_ring(rec_start, c.t0, 0, exact ? -__builtin_huge_val() : __builtin_nan(""),
+                    exact ? 0.0 : __builtin_nan(""));
+          if (exact && q == 0 && label && rows)  // u[0] = 0 forward, beta[L] = 0 backward
+            c.row2[(size_t)(tstart - c.rt0) * C + cl] = 0.0;
         }
-#pragma unroll
-        for (int j = 0; j < kA; ++j) c.r[j] = (q == 0 && j == 0) ? (float)v : 0.0f;
       } else {
-        // neutral start: every entry of the window (positions inside [0, L]) is 1
-#pragma unroll
+        // the chunk's start record (written by the burn-in segment just now, or
+        // by an earlier sweep); each lane reads back the slots it wrote itself
+        if (wb > 0) {
+          __threadfence_block();
+          __syncthreads();
+        }
+  #pragma unroll
         for (int j = 0; j < kA; ++j) {
-          const int pos = c.t0 - isig * (kA * q + j);
-          c.r[j] = (label && kA * q + 1 + j <= K && pos >= 0 && pos <= L) ? 1.0f : 0.0f;
+          const int k = kA * q + 1 + j;
+          c.r[j] = (label && k <= K)
+                       ? (float)rec_start[(size_t)pslot(c.t0 - isig * (k - 1), K) * C + cl]
+                       : 0.0f;
+        }
+        c.R = label ? (int)rec_start[kc + cl] : 0;
+        if (replay && rows && q == 0 && label &&
+            (fwd ? jc == sh.rj0 : (jc == sh.rj0 + sh.rnb - 1 || p1 == L))) {
+          c.row1[(size_t)(tstart - c.rt0) * C + cl] = rec_start[kc + C + cl];
+          c.row2[(size_t)(tstart - c.rt0) * C + cl] = rec_start[kc + 2 * C + cl];
         }
       }
-      if (main) {
-        save_ring(rec_start, c.t0, 0, exact ? -__builtin_huge_val() : __builtin_nan(""),
-                  exact ? 0.0 : __builtin_nan(""));
-        if (exact && q == 0 && label && rows)  // u[0] = 0 forward, beta[L] = 0 backward
-          c.row2[(size_t)(tstart - c.rt0) * C + cl] = 0.0;
+      // the scores of the first steps: position 1 split now, 2 .. kPq + 1 queued
+  #pragma unroll
+      for (int j = 0; j < kPq; ++j) c.sq[j] = score_at(c, 2 + j);
+      {  // the first step's row: K-sum over the whole start ring (its newest
+         // entry included), times exp(+-S) of position 1
+        float sa0 = 0.0f, sa1 = 0.0f;
+  #pragma unroll
+        for (int j = 0; j < kA; j += 2) {
+          sa0 = fmaf(c.drl[j * kLab], c.r[j], sa0);
+          sa1 = fmaf(c.drl[(j + 1) * kLab], c.r[j + 1], sa1);
+        }
+        const double g1 = gsum2((double)sa0 + (double)sa1);
+        double fx;
+        split256(score_at(c, 1), fwd, fx, c.fy, c.fn, c.sm.tab);
+        c.x = label ? g1 * fx : 0.0;
+        c.E = c.R + isig * c.fn;
       }
-    } else {
-      // the chunk's start record (written by the burn-in segment just now, or
-      // by an earlier sweep); each lane reads back the slots it wrote itself
-      if (wb > 0) {
-        __threadfence_block();
+      // ---- the steps, in blocks of kA
+      c.z_end = 0.0;
+      c.zB = 0;
+      c.done = 0;
+      c.ended = false;
+      c.o_end = c.m_end = 0.0;
+      const int nfull = (c.nrun - 1) / kA;  // whole blocks before the last step's
+      for (int blk = 0; blk < nfull; ++blk)
+        block256<false, CL>(c, blk * kA, std::make_integer_sequence<int, kA>{});
+      block256<true, CL>(c, nfull * kA, std::make_integer_sequence<int, kA>{});
+      if (c.ended) {
+        if (!replay && tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = log_t(c.z_end, c.zB, c.sm.tab);
+      } else {
+        // the ring after the segment: its record (with the last step's o, m);
+        // the position and head pass through an empty asm statement so that
+        // the record's addresses are formed here, not before the step loop
+        // (where they would stay live through it)
+        int h = (kA - c.nrun % kA) % kA, tref = c.t0 + isig * c.nrun;
+        asm volatile("" : "+v"(h), "+v"(tref));
+        if (!main)
+          save_ring(rec_start, tref, h, c.o_end, c.m_end);
+        else if (!replay)
+          save_ring(rec_end, tref, h, c.o_end, c.m_end);
+      }
+      // (the next segment reuses the LDS step buffers: wait for all)
+      __syncthreads();
+    }
+  };
+  if constexpr (REP) {
+    // the chain's chunks in order, past its exact one: a marked chunk is
+    // swept from its replaced start, then its successor is checked against
+    // the new end (forced to take it if the successor is marked too: its own
+    // end belongs to an older start)
+    for (int s = 1; s < nvalid; ++s) {
+      const int j = fwd ? s : nvalid - 1 - s;
+      if (pb.redo[base + j] == 0) continue;
+      sweep_chunk(j);
+      if (s + 1 < nvalid) {
+        const int jn = fwd ? j + 1 : j - 1;
+        __threadfence_block();  // the end record, for every thread of the check
         __syncthreads();
-      }
-#pragma unroll
-      for (int j = 0; j < kA; ++j) {
-        const int k = kA * q + 1 + j;
-        c.r[j] = (label && k <= K)
-                     ? (float)rec_start[(size_t)pslot(c.t0 - isig * (k - 1), K) * C + cl]
-                     : 0.0f;
-      }
-      c.R = label ? (int)rec_start[kc + cl] : 0;
-      if (replay && rows && q == 0 && label &&
-          (fwd ? jc == sh.rj0 : (jc == sh.rj0 + sh.rnb - 1 || p1 == L))) {
-        c.row1[(size_t)(tstart - c.rt0) * C + cl] = rec_start[kc + C + cl];
-        c.row2[(size_t)(tstart - c.rt0) * C + cl] = rec_start[kc + 2 * C + cl];
+        pit_check<kNT>(sh, pb, fwd, b, jn, -1, pb.redo[base + jn] != 0, red, redd);
       }
     }
-    // the scores of the first steps: position 1 split now, 2 .. kPq + 1 queued
-#pragma unroll
-    for (int j = 0; j < kPq; ++j) c.sq[j] = score_at(c, 2 + j);
-    {  // the first step's row: K-sum over the whole start ring (its newest
-       // entry included), times exp(+-S) of position 1
-      float sa0 = 0.0f, sa1 = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kA; j += 2) {
-        sa0 = fmaf(c.drl[j * kLab], c.r[j], sa0);
-        sa1 = fmaf(c.drl[(j + 1) * kLab], c.r[j + 1], sa1);
-      }
-      const double g1 = gsum2((double)sa0 + (double)sa1);
-      double fx;
-      split256(score_at(c, 1), fwd, fx, c.fy, c.fn, c.sm.tab);
-      c.x = label ? g1 * fx : 0.0;
-      c.E = c.R + isig * c.fn;
-    }
-    // ---- the steps, in blocks of kA
-    c.z_end = 0.0;
-    c.zB = 0;
-    c.done = 0;
-    c.ended = false;
-    c.o_end = c.m_end = 0.0;
-    const int nfull = (c.nrun - 1) / kA;  // whole blocks before the last step's
-    for (int blk = 0; blk < nfull; ++blk)
-      block256<false, CL>(c, blk * kA, std::make_integer_sequence<int, kA>{});
-    block256<true, CL>(c, nfull * kA, std::make_integer_sequence<int, kA>{});
-    if (c.ended) {
-      if (!replay && tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = log_t(c.z_end, c.zB, c.sm.tab);
-    } else {
-      // the ring after the segment: its record (with the last step's o, m);
-      // the position and head pass through an empty asm statement so that
-      // the record's addresses are formed here, not before the step loop
-      // (where they would stay live through it)
-      int h = (kA - c.nrun % kA) % kA, tref = c.t0 + isig * c.nrun;
-      asm volatile("" : "+v"(h), "+v"(tref));
-      if (!main)
-        save_ring(rec_start, tref, h, c.o_end, c.m_end);
-      else if (!replay)
-        save_ring(rec_end, tref, h, c.o_end, c.m_end);
-    }
-    // (the next segment reuses the LDS step buffers: wait for all)
-    __syncthreads();
+  } else {
+    sweep_chunk(jc);
   }
 }
 
@@ -790,16 +829,29 @@ hipError_t launch_sweep_256(const ChainShape &sh, const float *trans, const floa
                             const Escaled &es, const int32_t *lengths, const PitBufs &pb,
                             int with_bwd, int iter, hipStream_t st) {
   const size_t lds = sweep256_lds_bytes(sh.K);
-  const bool cl = sh.K < kDmax;
-  const void *f = cl ? (const void *)k_sweep256<true> : (const void *)k_sweep256<false>;
+  const bool cl = sh.K < kDmax, rep = iter == kPitRepair;
+  const void *f = cl ? (rep ? (const void *)k_sweep256<true, true>
+                            : (const void *)k_sweep256<true, false>)
+                     : (rep ? (const void *)k_sweep256<false, true>
+                            : (const void *)k_sweep256<false, false>);
   if (!sweep256_applies(sh.C, sh.K) || !lds_fits(f, lds)) return hipErrorInvalidConfiguration;
-  const int grid = iter < 0 ? sh.B * (sh.rnf + sh.rnb) : (with_bwd ? 2 : 1) * sh.B * sh.nchunk;
-  if (cl)
-    hipLaunchKernelGGL(k_sweep256<true>, dim3(grid), dim3(kNT), lds, st, sh, trans, dur, es,
-                       lengths, pb, iter);
-  else
-    hipLaunchKernelGGL(k_sweep256<false>, dim3(grid), dim3(kNT), lds, st, sh, trans, dur, es,
-                       lengths, pb, iter);
+  const int nd = with_bwd ? 2 : 1;
+  const int grid = rep ? nd * sh.B : iter < 0 ? sh.B * (sh.rnf + sh.rnb) : nd * sh.B * sh.nchunk;
+#define SEMICRF_SWEEP256(CLV, REPV)                                                             \
+  hipLaunchKernelGGL((k_sweep256<CLV, REPV>), dim3(grid), dim3(kNT), lds, st, sh, trans, dur, es, \
+                     lengths, pb, iter)
+  if (cl) {
+    if (rep)
+      SEMICRF_SWEEP256(true, true);
+    else
+      SEMICRF_SWEEP256(true, false);
+  } else {
+    if (rep)
+      SEMICRF_SWEEP256(false, true);
+    else
+      SEMICRF_SWEEP256(false, false);
+  }
+#undef SEMICRF_SWEEP256
   return hipGetLastError();
 }
 

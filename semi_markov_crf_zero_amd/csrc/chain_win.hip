@@ -40,6 +40,7 @@
 
 #include "device_math.h"
 #include "internal.h"
+#include "pitcheck.h"
 
 namespace semicrf {
 
@@ -570,17 +571,21 @@ __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &s
 // iteration 0 (exact at the sequence end the chain starts from, neutral
 // elsewhere), re-read afterwards.  The chunk that ends its chain yields log Z
 // in its own frame; every other chunk writes its end state.
-template <int NT, int CMAX, int DCH>
+template <int NT, int CMAX, int DCH, bool REP>
 __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__restrict__ trans,
                                                 const float *__restrict__ dur, Escaled es,
                                                 const int32_t *__restrict__ lengths, PitBufs pb,
                                                 int iter) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int nck = sh.B * sh.nchunk;
-  const bool replay = iter < 0;  // a window of chunks swept again from exact records
+  const bool replay = iter == -1;  // a window of chunks swept again from exact records
   bool fwd;
   int b, jc;
-  if (replay) {
+  if (REP) {  // the in-order repair: one workgroup per (direction, sequence)
+    fwd = (int)blockIdx.x < sh.B;
+    b = fwd ? blockIdx.x : blockIdx.x - sh.B;
+    jc = 0;
+  } else if (replay) {
     const int nf = sh.B * sh.rnf;
     fwd = (int)blockIdx.x < nf;
     const int nj = fwd ? sh.rnf : sh.rnb;
@@ -593,8 +598,9 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
     b = rem / sh.nchunk;
     jc = rem % sh.nchunk;
   }
-  const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + jc;
-  if (iter == 0) {  // the parallel-in-time state, before any verification reads it
+  const size_t base = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk;  // this chain's flags
+  const size_t idx = base + jc;
+  if (!REP && iter == 0) {  // the parallel-in-time state, before any verification reads it
     if (threadIdx.x == 0) {
       pb.redo[idx] = 1;
       pb.corr_i[idx] = 0;
@@ -608,12 +614,21 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   const int lane = tid & 63;
   const bool chain = tid < C;  // lanes of wave 0
   // (the iteration flags are loaded with the length: one memory wait)
-  const int nbad = iter > 0 ? pb.nbad[iter - 1] : 1, redo = iter > 0 ? pb.redo[idx] : 1;
+  const int nbad = REP ? pb.nbad[kPitParallelIters - 1] : iter > 0 ? pb.nbad[iter - 1] : 1,
+            redo = !REP && iter > 0 ? pb.redo[idx] : 1;
   if (L < 1 || L > T || jc >= sh.nchunk) return;
-  const int p0 = jc * sh.delta;
-  if (p0 >= L) return;
-  const int p1 = min(p0 + sh.delta, L);
+  if (jc * sh.delta >= L) return;
   if (nbad == 0 || redo == 0) return;
+  const int nvalid = (L + sh.delta - 1) / sh.delta;
+  __shared__ PitMaxArg red[NT / 64];  // scratch of the repair's checks
+  __shared__ double redd[NT / 64];
+  if constexpr (REP) {
+    // nothing to repair unless the last parallel check found a chunk of
+    // this chain inconsistent
+    int marked = 0;
+    for (int j = tid; j < nvalid; j += NT) marked |= pb.redo[base + j];
+    if (!pit_any<NT>(marked != 0, red)) return;
+  }
   const WSmem sm = wcarve(lds, sh, NT);
   Win win;
   win.init(sh);
@@ -628,175 +643,201 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
   }
   const size_t ob = (size_t)b * (T + 1) * C;
   const size_t cks = ck_stride(C, K);
-  double *rec_start = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
-  double *rec_end = (fwd ? pb.end_fwd : pb.end_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
   const int sigma = fwd ? 1 : -1;
-  const int tstart = fwd ? p0 : p1;
-  const bool tail = fwd ? (p1 == L) : (p0 == 0);  // this chunk ends the chain
   const bool rows = pb.row_a != nullptr;
   const int rt0 = pb.row_t0;  // rows are written relative to the window start
   const size_t orow = (size_t)b * pb.row_stride * C;
   double *row1 = rows ? (fwd ? pb.row_a : pb.row_v) + orow : nullptr;  // alpha / v
   double *row2 = rows ? (fwd ? pb.row_u : pb.row_b) + orow : nullptr;  // u / beta
 
-  int R = 0;  // integer log reference of label `lane` (units of ln2)
-  // Burn-in: at iteration 0 a chunk without an exact start begins wb
-  // positions early (a whole number of blocks) from the neutral state, sweeps
-  // them without writing rows, and stores the state it reaches at its true
-  // start as its start record.  The recursion forgets where it started, so
-  // that record usually already agrees with the predecessor's end and the
-  // verification accepts it after one iteration.
-  const bool exact = fwd ? (jc == 0) : (p1 == L);
-  int wb = 0;
-  if (iter == 0 && !exact) {
-    wb = min(sh.burn, fwd ? p0 : L - p1);
-    wb = wb / U * U;
-  }
-  const int tbegin = fwd ? p0 - wb : p1 + wb;  // where the sweep starts
-  if (iter == 0) {
-    for (int i = tid; i < (K + kWinMirror) * C; i += NT) sm.ring[i] = 0.0;
-    __syncthreads();
-    if (exact) {
-      // entry u[0] - S[0] = 0 forward; beta[L] + S[L] = S[L] backward
-      if (chain) {
-        double v = 1.0;
-        if (!fwd) {  // exp(S[L]) = ep * 2^n
-          double em;
-          exp_split(es.S[ob + (size_t)L * C + lane], v, em, R);
+  // one chunk, p0 .. p1, from its start record (or, at iteration 0, from
+  // its exact or neutral start after the burn-in)
+  auto sweep_chunk = [&](const int jc) __attribute__((always_inline)) {
+    const int p0 = jc * sh.delta;
+    const int p1 = min(p0 + sh.delta, L);
+    double *rec_start = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
+    double *rec_end = (fwd ? pb.end_fwd : pb.end_bwd) + ((size_t)b * sh.nchunk + jc) * cks;
+    const int tstart = fwd ? p0 : p1;
+    const bool tail = fwd ? (p1 == L) : (p0 == 0);  // this chunk ends the chain
+    int R = 0;  // integer log reference of label `lane` (units of ln2)
+    // Burn-in: at iteration 0 a chunk without an exact start begins wb
+    // positions early (a whole number of blocks) from the neutral state, sweeps
+    // them without writing rows, and stores the state it reaches at its true
+    // start as its start record.  The recursion forgets where it started, so
+    // that record usually already agrees with the predecessor's end and the
+    // verification accepts it after one iteration.
+    const bool exact = fwd ? (jc == 0) : (p1 == L);
+    int wb = 0;
+    if (iter == 0 && !exact) {
+      wb = min(sh.burn, fwd ? p0 : L - p1);
+      wb = wb / U * U;
+    }
+    const int tbegin = fwd ? p0 - wb : p1 + wb;  // where the sweep starts
+    if (iter == 0) {
+      for (int i = tid; i < (K + kWinMirror) * C; i += NT) sm.ring[i] = 0.0;
+      __syncthreads();
+      if (exact) {
+        // entry u[0] - S[0] = 0 forward; beta[L] + S[L] = S[L] backward
+        if (chain) {
+          double v = 1.0;
+          if (!fwd) {  // exp(S[L]) = ep * 2^n
+            double em;
+            exp_split(es.S[ob + (size_t)L * C + lane], v, em, R);
+          }
+          ring_put(sm, K, C, pos_slot(tstart, K), lane, v);
         }
-        ring_put(sm, K, C, pos_slot(tstart, K), lane, v);
-      }
-    } else {
-      // neutral start: every entry of the window (positions inside [0, L]) is 1
-      for (int i = tid; i < K * C; i += NT) {
-        const int dq = i / C, c = i % C;
-        const int q = tbegin - sigma * dq;
-        if (q >= 0 && q <= L) ring_put(sm, K, C, pos_slot(q, K), c, 1.0);
-      }
-    }
-    __syncthreads();
-    // o = NaN marks a neutral start (never accepted by the verification);
-    // after a burn-in the record is written when the sweep reaches tstart
-    if (wb == 0)
-      wsave(rec_start, sm, sh, chain, lane, R,
-            exact ? -__builtin_huge_val() : __builtin_nan(""), exact ? 0.0 : __builtin_nan(""), NT);
-    if (exact && chain && rows)  // u[0] = 0 forward, beta[L] = 0 backward
-      row2[(size_t)(tstart - rt0) * C + lane] = 0.0;
-  } else {
-    double o0, m0;
-    wload(rec_start, sm, sh, chain, lane, R, o0, m0, NT);
-    // a replay window's first row (its chunk before is not swept again): the
-    // record's exact outputs at the start position
-    if (replay && rows && chain &&
-        (fwd ? jc == sh.rj0 : (jc == sh.rj0 + sh.rnb - 1 || p1 == L))) {
-      row1[(size_t)(tstart - rt0) * C + lane] = o0;
-      row2[(size_t)(tstart - rt0) * C + lane] = m0;
-    }
-  }
-  const int first = tbegin + sigma;
-  const int nsteps = wb + (p1 - p0);
-  {  // the first block's scores (later blocks: the loader wave, a block ahead)
-    const int npair = min(U, nsteps) * C;
-    for (int q = tid; q < npair; q += NT) {
-      double fx, fy;
-      int n;
-      es_get(es, ob, first + sigma * (q / C), T, C, q % C, fwd, fx, fy, n);
-      sm.efx[q] = fx;
-      sm.efy[q] = fy;
-      sm.en[q] = n;
-    }
-  }
-  vm_drain();
-  __syncthreads();
-
-  double o_end = 0.0, m_end = 0.0, lz = 0.0, o_rec = 0.0, m_rec = 0.0;
-  int Bm = -(1 << 29);  // step scale of the chain; the first step computes it
-  // wave roles: 0 the chain; 1-3 the far parts of the next block, besides
-  // which 1 loads the next block's scores and 2-3 write the previous
-  // block's rows
-  const int w = tid >> 6;
-  const int G = part_groups(sh, NT), S = 3 * C + 1;
-  ChainState cs;
-  if (w == 0) {
-    // the window from the start state: entry m+1 steps back is at position
-    // tbegin - sigma*m (0 beyond the ring)
-#pragma unroll
-    for (int m = 0; m < kNearW; ++m)
-      cs.hist[m] = (chain && m < K) ? sm.ring[pos_slot(tbegin - sigma * m, K) * C + lane] : 0.0;
-    double nr = 0.0;
-#pragma unroll
-    for (int k = 2; k <= kNearW; ++k) nr = fma(Dn[k], cs.hist[k - 1], nr);
-    cs.nr = nr;
-    cs.shprev = 0;
-  } else {
-    double F[U];  // far parts of the first block
-    win.template far<DCH>(sm, sh, first, sigma, F);
-    win.publish(sm, sh, NT, F, 0);
-  }
-  __syncthreads();
-  BlockLoad bl;
-  for (int s0 = 0; s0 < nsteps; s0 += U) {
-    const int nb = min(U, nsteps - s0);  // steps in this block
-    const int t0 = first + sigma * s0;
-    const int buf = (s0 / U) & 1;
-    const bool more = s0 + U < nsteps;
-    if (wb > 0 && s0 == wb) {  // the burn-in ends: the chunk's start record
-      wsave(rec_start, sm, sh, chain, lane, R, o_rec, m_rec, NT);
-      __syncthreads();  // read before the chain overwrites ring slots
-    }
-    if (w == 0) {
-      chain_block<CMAX>(sh, sm, G, s0, nb, nsteps, t0, sigma, buf, tail, lane, chain, Dn, tr,
-                        wb - 1, cs, R, Bm, o_rec, m_rec, o_end, m_end, lz);
-    } else {
-      if (w == 1 && more) bl.issue(es, ob, first, sigma, s0 + U, T, C, lane);
-      if (w >= 2 && rows && s0 > wb) {
-        // the previous block's rows (a full block of U steps, past the burn-in)
-        block_rows(sm.stg + (buf ^ 1) * U * S, C, U, t0 - sigma * U - rt0, sigma, row1, row2, -1, 128,
-                   NT - 128);
-      }
-      if (more) {
-        // far parts of the next block: entries older than this block only,
-        // none of the slots the chain writes meanwhile
-        double F[U];
-        win.template far<DCH>(sm, sh, t0 + sigma * U, sigma, F);
-        win.publish(sm, sh, NT, F, buf ^ 1);
-      }
-      // the next block's scores land in the other buffer before the barrier
-      // that ends this block
-      if (w == 1 && more) bl.put(sm, buf ^ 1, C, lane, fwd);
-    }
-    __syncthreads();
-    if (sm.flag[0]) {
-      // rare: rescale the older entries of the labels that rebased (every
-      // slot but the block's new entries), label by label over all threads
-      const int nl = lane < C ? sm.shiftn[lane] : 0;
-      unsigned long long rb = __ballot(nl != 0);
-      const int slot0 = pos_slot(t0, K);
-      while (rb) {
-        const int c = __builtin_ctzll(rb);
-        rb &= rb - 1;
-        const int n = __builtin_amdgcn_readlane(nl, c);
-        for (int m = 1 + tid; m <= K - nb; m += NT) {
-          int sl = slot0 - sigma * m;
-          sl += sl < 0 ? K : 0;
-          sl -= sl >= K ? K : 0;
-          ring_put(sm, K, C, sl, c, ldexp(sm.ring[sl * C + c], -n));
+      } else {
+        // neutral start: every entry of the window (positions inside [0, L]) is 1
+        for (int i = tid; i < K * C; i += NT) {
+          const int dq = i / C, c = i % C;
+          const int q = tbegin - sigma * dq;
+          if (q >= 0 && q <= L) ring_put(sm, K, C, pos_slot(q, K), c, 1.0);
         }
       }
       __syncthreads();
-    }
-  }
-  if (!replay) {
-    if (tail) {
-      if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
+      // o = NaN marks a neutral start (never accepted by the verification);
+      // after a burn-in the record is written when the sweep reaches tstart
+      if (wb == 0)
+        wsave(rec_start, sm, sh, chain, lane, R,
+              exact ? -__builtin_huge_val() : __builtin_nan(""), exact ? 0.0 : __builtin_nan(""), NT);
+      if (exact && chain && rows)  // u[0] = 0 forward, beta[L] = 0 backward
+        row2[(size_t)(tstart - rt0) * C + lane] = 0.0;
     } else {
-      wsave(rec_end, sm, sh, chain, lane, R, o_end, m_end, NT);
+      double o0, m0;
+      wload(rec_start, sm, sh, chain, lane, R, o0, m0, NT);
+      // a replay window's first row (its chunk before is not swept again): the
+      // record's exact outputs at the start position
+      if (replay && rows && chain &&
+          (fwd ? jc == sh.rj0 : (jc == sh.rj0 + sh.rnb - 1 || p1 == L))) {
+        row1[(size_t)(tstart - rt0) * C + lane] = o0;
+        row2[(size_t)(tstart - rt0) * C + lane] = m0;
+      }
     }
-  }
-  if (rows) {  // rows of the last block
-    const int s0 = (nsteps - 1) / U * U;
-    block_rows(sm.stg + ((s0 / U) & 1) * U * (3 * C + 1), C, nsteps - s0,
-               first + sigma * s0 - rt0, sigma, row1, row2, tail ? nsteps - 1 - s0 : -1, 0, NT);
+    const int first = tbegin + sigma;
+    const int nsteps = wb + (p1 - p0);
+    {  // the first block's scores (later blocks: the loader wave, a block ahead)
+      const int npair = min(U, nsteps) * C;
+      for (int q = tid; q < npair; q += NT) {
+        double fx, fy;
+        int n;
+        es_get(es, ob, first + sigma * (q / C), T, C, q % C, fwd, fx, fy, n);
+        sm.efx[q] = fx;
+        sm.efy[q] = fy;
+        sm.en[q] = n;
+      }
+    }
+    vm_drain();
+    __syncthreads();
+
+    double o_end = 0.0, m_end = 0.0, lz = 0.0, o_rec = 0.0, m_rec = 0.0;
+    int Bm = -(1 << 29);  // step scale of the chain; the first step computes it
+    // wave roles: 0 the chain; 1-3 the far parts of the next block, besides
+    // which 1 loads the next block's scores and 2-3 write the previous
+    // block's rows
+    const int w = tid >> 6;
+    const int G = part_groups(sh, NT), S = 3 * C + 1;
+    ChainState cs;
+    if (w == 0) {
+      // the window from the start state: entry m+1 steps back is at position
+      // tbegin - sigma*m (0 beyond the ring)
+  #pragma unroll
+      for (int m = 0; m < kNearW; ++m)
+        cs.hist[m] = (chain && m < K) ? sm.ring[pos_slot(tbegin - sigma * m, K) * C + lane] : 0.0;
+      double nr = 0.0;
+  #pragma unroll
+      for (int k = 2; k <= kNearW; ++k) nr = fma(Dn[k], cs.hist[k - 1], nr);
+      cs.nr = nr;
+      cs.shprev = 0;
+    } else {
+      double F[U];  // far parts of the first block
+      win.template far<DCH>(sm, sh, first, sigma, F);
+      win.publish(sm, sh, NT, F, 0);
+    }
+    __syncthreads();
+    BlockLoad bl;
+    for (int s0 = 0; s0 < nsteps; s0 += U) {
+      const int nb = min(U, nsteps - s0);  // steps in this block
+      const int t0 = first + sigma * s0;
+      const int buf = (s0 / U) & 1;
+      const bool more = s0 + U < nsteps;
+      if (wb > 0 && s0 == wb) {  // the burn-in ends: the chunk's start record
+        wsave(rec_start, sm, sh, chain, lane, R, o_rec, m_rec, NT);
+        __syncthreads();  // read before the chain overwrites ring slots
+      }
+      if (w == 0) {
+        chain_block<CMAX>(sh, sm, G, s0, nb, nsteps, t0, sigma, buf, tail, lane, chain, Dn, tr,
+                          wb - 1, cs, R, Bm, o_rec, m_rec, o_end, m_end, lz);
+      } else {
+        if (w == 1 && more) bl.issue(es, ob, first, sigma, s0 + U, T, C, lane);
+        if (w >= 2 && rows && s0 > wb) {
+          // the previous block's rows (a full block of U steps, past the burn-in)
+          block_rows(sm.stg + (buf ^ 1) * U * S, C, U, t0 - sigma * U - rt0, sigma, row1, row2, -1, 128,
+                     NT - 128);
+        }
+        if (more) {
+          // far parts of the next block: entries older than this block only,
+          // none of the slots the chain writes meanwhile
+          double F[U];
+          win.template far<DCH>(sm, sh, t0 + sigma * U, sigma, F);
+          win.publish(sm, sh, NT, F, buf ^ 1);
+        }
+        // the next block's scores land in the other buffer before the barrier
+        // that ends this block
+        if (w == 1 && more) bl.put(sm, buf ^ 1, C, lane, fwd);
+      }
+      __syncthreads();
+      if (sm.flag[0]) {
+        // rare: rescale the older entries of the labels that rebased (every
+        // slot but the block's new entries), label by label over all threads
+        const int nl = lane < C ? sm.shiftn[lane] : 0;
+        unsigned long long rb = __ballot(nl != 0);
+        const int slot0 = pos_slot(t0, K);
+        while (rb) {
+          const int c = __builtin_ctzll(rb);
+          rb &= rb - 1;
+          const int n = __builtin_amdgcn_readlane(nl, c);
+          for (int m = 1 + tid; m <= K - nb; m += NT) {
+            int sl = slot0 - sigma * m;
+            sl += sl < 0 ? K : 0;
+            sl -= sl >= K ? K : 0;
+            ring_put(sm, K, C, sl, c, ldexp(sm.ring[sl * C + c], -n));
+          }
+        }
+        __syncthreads();
+      }
+    }
+    if (!replay) {
+      if (tail) {
+        if (tid == 0) pb.lz_part[(fwd ? 0 : sh.B) + b] = lz;
+      } else {
+        wsave(rec_end, sm, sh, chain, lane, R, o_end, m_end, NT);
+      }
+    }
+    if (rows) {  // rows of the last block
+      const int s0 = (nsteps - 1) / U * U;
+      block_rows(sm.stg + ((s0 / U) & 1) * U * (3 * C + 1), C, nsteps - s0,
+                 first + sigma * s0 - rt0, sigma, row1, row2, tail ? nsteps - 1 - s0 : -1, 0, NT);
+    }
+  };
+  if constexpr (REP) {
+    // the chain's chunks in order, past its exact one: a marked chunk is
+    // swept from its replaced start, then its successor is checked against
+    // the new end (forced to take it if the successor is marked too: its own
+    // end belongs to an older start)
+    for (int s = 1; s < nvalid; ++s) {
+      const int j = fwd ? s : nvalid - 1 - s;
+      __syncthreads();  // the previous chunk's LDS and rows
+      if (pb.redo[base + j] == 0) continue;
+      sweep_chunk(j);
+      if (s + 1 < nvalid) {
+        const int jn = fwd ? j + 1 : j - 1;
+        __threadfence_block();  // the end record, for every thread of the check
+        __syncthreads();
+        pit_check<NT>(sh, pb, fwd, b, jn, -1, pb.redo[base + jn] != 0, red, redd);
+      }
+    }
+  } else {
+    sweep_chunk(jc);
   }
 }
 
@@ -813,7 +854,9 @@ struct WinKernels {
   static void attrs() {
     static bool done = false;
     if (!done) {
-      (void)hipFuncSetAttribute((const void *)k_sweep_w<NT, CMAX, DCH>,
+      (void)hipFuncSetAttribute((const void *)k_sweep_w<NT, CMAX, DCH, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+      (void)hipFuncSetAttribute((const void *)k_sweep_w<NT, CMAX, DCH, true>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
       (void)hipGetLastError();
       done = true;
@@ -824,11 +867,19 @@ struct WinKernels {
                           int with_bwd, int iter, hipStream_t st) {
     attrs();
     const size_t lds = win_lds_bytes(sh.C, sh.K, sh.P);
-    if (!lds_fits((const void *)k_sweep_w<NT, CMAX, DCH>, lds))
-      return wreport(hipErrorInvalidConfiguration, "k_sweep_w (LDS)", sh, lds);
-    const int grid = iter < 0 ? sh.B * (sh.rnf + sh.rnb) : (with_bwd ? 2 : 1) * sh.B * sh.nchunk;
-    hipLaunchKernelGGL((k_sweep_w<NT, CMAX, DCH>), dim3(grid), dim3(NT), lds, st, sh, trans,
-                       dur, es, lengths, pb, iter);
+    const bool rep = iter == kPitRepair;
+    const void *f = rep ? (const void *)k_sweep_w<NT, CMAX, DCH, true>
+                        : (const void *)k_sweep_w<NT, CMAX, DCH, false>;
+    if (!lds_fits(f, lds)) return wreport(hipErrorInvalidConfiguration, "k_sweep_w (LDS)", sh, lds);
+    const int nd = with_bwd ? 2 : 1;
+    if (rep) {
+      hipLaunchKernelGGL((k_sweep_w<NT, CMAX, DCH, true>), dim3(nd * sh.B), dim3(NT), lds, st, sh,
+                         trans, dur, es, lengths, pb, iter);
+    } else {
+      const int grid = iter < 0 ? sh.B * (sh.rnf + sh.rnb) : nd * sh.B * sh.nchunk;
+      hipLaunchKernelGGL((k_sweep_w<NT, CMAX, DCH, false>), dim3(grid), dim3(NT), lds, st, sh,
+                         trans, dur, es, lengths, pb, iter);
+    }
     return wreport(hipGetLastError(), "k_sweep_w", sh, lds);
   }
 };

@@ -50,7 +50,8 @@ __host__ __device__ inline size_t trw_floats(int C, int QT) { return (size_t)2 *
 constexpr int kMaxKC = 16384;
 constexpr size_t kMaxLds = 163840;  // gfx950: 160 KB per workgroup (static + dynamic)
 // Dynamic-LDS budget of the configurations: the hardware limit less a small
-// reserve (the kernels declare no static LDS; lds_fits checks the sum).
+// reserve for static LDS (at most 192 bytes, in the sweep engines' repair
+// instantiations; lds_fits checks the sum).
 constexpr size_t kMaxDynLds = kMaxLds - 256;
 
 // True if a launch of kernel f with `dyn` bytes of dynamic LDS fits the

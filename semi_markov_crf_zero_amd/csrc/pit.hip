@@ -22,6 +22,13 @@
 //     iterations always suffice, and the last one (which can only sweep the
 //     chain's last chunk) needs no verification; every kernel of an
 //     iteration after convergence returns at once;
+//   the register-ring engines (chain64.hip, chain256.hip, chain_win.hip) stop
+//     after kPitParallelIters parallel iterations: one more launch of the
+//     engine, one workgroup per (direction, sequence), walks the chain in
+//     order, sweeping each chunk still marked and checking its successor
+//     against the new end (pitcheck.h).  Nothing is marked after a
+//     converged check, so that launch returns at once in the usual case and
+//     the loop above costs two iterations instead of nchunk;
 //   k_pit_fixup adds the prefix sums of the recorded scalars to the
 //     checkpoint records and to log Z, which makes every record the exact
 //     state with its exact log normaliser -- the checkpoint-boundary
@@ -29,27 +36,13 @@
 //     (abstract; technical summary, section 2.C) computed chunk-parallel.
 #include "device_math.h"
 #include "internal.h"
+#include "pitcheck.h"
 
 namespace semicrf {
 
 namespace {
 
 constexpr int kPitThreads = 256;
-constexpr double kPitTol = 1e-12;  // direction mismatch accepted, relative to the largest entry
-// The same for the engine whose ring and sums are float32 (chain256.hip): two
-// chains that reach one state along different paths agree to float32
-// rounding there, so a float64-level bar would reject every converged chunk.
-constexpr double kPitTolF32 = 1e-5;
-
-struct MaxArg {
-  double v;
-  int i;
-};
-
-__device__ __forceinline__ MaxArg max_arg(MaxArg a, MaxArg b) {
-  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
-  return a;
-}
 
 }  // namespace
 
@@ -61,7 +54,7 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_verify(ChainShape sh,
                                                             const int32_t *__restrict__ lengths,
                                                             PitBufs pb, int iter) {
   if (iter > 0 && pb.nbad[iter - 1] == 0) return;
-  __shared__ MaxArg red[kPitThreads / 64];
+  __shared__ PitMaxArg red[kPitThreads / 64];
   __shared__ double redd[kPitThreads / 64];
   const int nck = sh.B * sh.nchunk;
   const bool fwd = (int)blockIdx.x < nck;
@@ -77,83 +70,7 @@ __global__ __launch_bounds__(kPitThreads) void k_pit_verify(ChainShape sh,
     if (threadIdx.x == 0) pb.redo[(fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + j] = 0;
     return;
   }
-  const int jp = fwd ? j - 1 : j + 1;  // chunk whose end must equal this chunk's start
-  const int C = sh.C, K = sh.K;
-  const size_t cks = ck_stride(C, K);
-  double *A = (fwd ? pb.ck_fwd : pb.ck_bwd) + ((size_t)b * sh.nchunk + j) * cks;
-  const double *E = (fwd ? pb.end_fwd : pb.end_bwd) + ((size_t)b * sh.nchunk + jp) * cks;
-  const double *RA = A + (size_t)K * C, *RE = E + (size_t)K * C;
-  const int n = K * C;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const long long re0 = (long long)RE[0];
-
-  // largest entry of E in log2, relative to E's label-0 reference
-  MaxArg best = {-__builtin_huge_val(), 0x7fffffff};
-  for (int i = tid; i < n; i += kPitThreads) {
-    const double e = E[i];
-    if (e > 0.0) {
-      const double le = (double)((long long)RE[i % C] - re0) + log2(e);
-      best = max_arg(best, MaxArg{le, i});
-    }
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    MaxArg o;
-    o.v = __shfl_xor(best.v, off);
-    o.i = __shfl_xor(best.i, off);
-    best = max_arg(best, o);
-  }
-  if (lane == 0) red[w] = best;
-  __syncthreads();
-  best = red[0];
-  for (int q = 1; q < kPitThreads / 64; ++q) best = max_arg(best, red[q]);
-  const bool neutral = A[(size_t)K * C + C] != A[(size_t)K * C + C];  // o is NaN on a neutral start
-  bool ok = best.i != 0x7fffffff && !neutral && A[best.i] > 0.0;
-  long long di = 0;
-  double df = 0.0;
-  double mism = 0.0;
-  if (ok) {
-    // scalar between the states: A ~ 2^delta E, delta = di + df
-    const int cs = best.i % C;
-    const double l = log2(A[best.i]) - log2(E[best.i]);
-    const double fl = floor(l);
-    di = (long long)RA[cs] - (long long)RE[cs] + (long long)fl;
-    df = l - fl;
-    for (int i = tid; i < n; i += kPitThreads) {
-      const double a = A[i], e = E[i];
-      if (a == 0.0 && e == 0.0) continue;
-      const int c = i % C;
-      const double we =
-          e > 0.0 ? exp2((double)((long long)RE[c] - re0) + log2(e) - best.v) : 0.0;
-      const double wa =
-          a > 0.0 ? exp2((double)((long long)RA[c] - re0 - di) + (log2(a) - df) - best.v) : 0.0;
-      mism = fmax(mism, fabs(wa - we));
-    }
-    for (int off = 32; off > 0; off >>= 1) mism = fmax(mism, __shfl_xor(mism, off));
-    __syncthreads();
-    if (lane == 0) redd[w] = mism;
-    __syncthreads();
-    mism = redd[0];
-    for (int q = 1; q < kPitThreads / 64; ++q) mism = fmax(mism, redd[q]);
-    ok = mism <= (sh.e256 ? kPitTolF32 : kPitTol);
-  }
-  const size_t idx = (fwd ? 0 : (size_t)nck) + (size_t)b * sh.nchunk + j;
-  __syncthreads();  // every read of A above precedes the copy below
-  if (ok) {
-    if (tid == 0) {
-      pb.corr_i[idx] = di;
-      pb.corr_f[idx] = df;
-      pb.redo[idx] = 0;
-    }
-  } else {
-    // the start becomes the predecessor's end exactly: scalar 0 between them
-    for (size_t i = tid; i < cks; i += kPitThreads) A[i] = E[i];
-    if (tid == 0) {
-      pb.corr_i[idx] = 0;
-      pb.corr_f[idx] = 0.0;
-      pb.redo[idx] = 1;
-      atomicAdd(&pb.nbad[iter], 1);
-    }
-  }
+  pit_check<kPitThreads>(sh, pb, fwd, b, j, iter, false, red, redd);
 }
 
 // One workgroup per (direction, sequence): prefix sums of the recorded
@@ -310,13 +227,20 @@ hipError_t run_sweeps(const ChainShape &sh, const float *trans, const float *dur
   // After iteration it the first it+1 chunks of the chain are exact, so the
   // last iteration can only sweep the chain's last chunk, which has no
   // successor to verify: no verification follows it (a chunk whose start
-  // was replaced carries scalar 0, set with the copy).
-  for (int it = 0; it < niter; ++it) {
+  // was replaced carries scalar 0, set with the copy).  Engines with an
+  // in-order repair run kPitParallelIters iterations, then the repair.
+  const bool repair = sh.win || sh.e64 || sh.e256;
+  const int npar = repair && niter > kPitParallelIters ? kPitParallelIters : niter;
+  for (int it = 0; it < npar; ++it) {
     e = launch_sweep(sh, trans, dur, es, lengths, pb, with_bwd, it, st);
     if (e != hipSuccess) return e;
     if (it == 0 && after_first) (void)hipEventRecord(after_first, st);
     if (it + 1 == niter) break;
     e = launch_pit_verify(sh, lengths, pb, it, with_bwd, st);
+    if (e != hipSuccess) return e;
+  }
+  if (npar < niter) {
+    e = launch_sweep(sh, trans, dur, es, lengths, pb, with_bwd, kPitRepair, st);
     if (e != hipSuccess) return e;
   }
   e = launch_pit_fixup(sh, lengths, pb, logz_ws, logz_bwd_ws, logz_out, with_bwd, st);

@@ -75,7 +75,9 @@ def logz_rel_err(g, o):
     return np.abs(g[ok] - o[ok]) / np.maximum(1.0, np.abs(o[ok]))
 
 
-def assert_fwd_bwd_close(g, o, tol_logz=TOL_LOGZ, tol=TOL_GRAD, label=""):
+def assert_fwd_bwd_close(g, o, tol_logz=TOL_LOGZ, tol=TOL_GRAD, label="", param_rel=0.0):
+    """param_rel > 0 widens the parameter-gradient bar to param_rel * |oracle|
+    where that is larger (the float32-ring engine on slowly mixing chains)."""
     assert np.array_equal(np.isnan(g["logz"]), np.isnan(o["logz"])), label
     rel = logz_rel_err(g["logz"], o["logz"])
     assert rel.size == 0 or rel.max() <= tol_logz, (label, "logz", rel.max())
@@ -89,6 +91,9 @@ def assert_fwd_bwd_close(g, o, tol_logz=TOL_LOGZ, tol=TOL_GRAD, label=""):
         if k in g and k in o:
             errs[k] = float(np.abs(g[k] - o[k]).max()) if g[k].size else 0.0
             x = param_excess(g[k], o[k], tol)
+            if param_rel > 0.0:
+                bar = np.maximum(param_tol(o[k], tol), param_rel * np.abs(o[k]))
+                x = float((np.abs(g[k] - o[k]) / bar).max()) if g[k].size else 0.0
             assert x <= 1.0, (label, k, errs[k], "bar exceeded by", x)
     return errs
 
