@@ -163,6 +163,17 @@ def test_large_emission_scales(sigma):
     assert_viterbi_equal(gpu_viterbi(inp), oracle.viterbi(inp), label=sigma)
 
 
+@pytest.mark.parametrize("sigma", [1.0, 100.0])
+def test_duration_posteriors_many_lags(sigma):
+    """K = 200 with 16 labels a group: the duration kernel's lag blocks of 16.
+    At emission scale 100 the scores swing by hundreds of nats within a
+    64-start tile, so labels take the direct path (an exponential per
+    cell); at scale 1 the factorised path."""
+    inp = _case(2, 700, 20, 200, [700, 433], seed=29, sigma=sigma, tsd=1.0, dsd=1.0)
+    o = oracle.fwd_bwd(inp)
+    assert_fwd_bwd_close(gpu_fwd_bwd(inp), o, label=sigma)
+
+
 @pytest.mark.parametrize("sigma", [10.0, 100.0])
 def test_large_emission_scales_lds_ring(sigma):
     """C = 48 runs the LDS-ring engine: frequent rebases, applied a step
