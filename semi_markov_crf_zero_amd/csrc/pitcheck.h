@@ -33,8 +33,9 @@ __device__ __forceinline__ PitMaxArg pit_max_arg(PitMaxArg a, PitMaxArg b) {
 
 // Chunk j of direction `fwd` of sequence b (not the chain's exact chunk):
 // compare its start record A with the end record E of the chunk before it
-// in the chain (forward j - 1, backward j + 1).  Consistent -- the two agree
-// in direction within the tolerance, A ~ 2^(di + df) E -- and not `force`d:
+// in the chain (forward j - 1, backward j + 1), entry by entry relative to
+// (about) E's largest entry.  Consistent -- the two agree in direction
+// within the tolerance, A ~ 2^(di + df) E -- and not `force`d:
 // records the scalar and clears the chunk's redo flag.  Otherwise E becomes
 // the start exactly (scalar 0), redo is set and, for iter >= 0, counted in
 // nbad[iter].  Returns whether it was consistent.  All NT threads of the
@@ -55,15 +56,22 @@ __device__ bool pit_check(const ChainShape &sh, const PitBufs &pb, bool fwd, int
   const int n = K * C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const long long re0 = (long long)RE[0];
+  const int cstep = NT % C;  // label of entry i + NT from that of entry i
 
-  // largest entry of E in log2, relative to E's label-0 reference
+  // an entry of E within a factor 2^0.09 of its largest, in log2 relative to
+  // E's label-0 reference (exponent plus the mantissa's chord: log2 of
+  // 2m in [1, 2) taken as 2m - 1)
   PitMaxArg best = {-__builtin_huge_val(), 0x7fffffff};
-  for (int i = tid; i < n; i += NT) {
+  for (int i = tid, c = tid % C; i < n; i += NT) {
     const double e = E[i];
     if (e > 0.0) {
-      const double le = (double)((long long)RE[i % C] - re0) + log2(e);
+      int ex;
+      const double m = frexp(e, &ex);
+      const double le = (double)((long long)RE[c] - re0 + ex) + (2.0 * m - 2.0);
       best = pit_max_arg(best, PitMaxArg{le, i});
     }
+    c += cstep;
+    c -= c >= C ? C : 0;
   }
   for (int off = 32; off > 0; off >>= 1) {
     PitMaxArg o;
@@ -87,15 +95,24 @@ __device__ bool pit_check(const ChainShape &sh, const PitBufs &pb, bool fwd, int
     const double fl = floor(l);
     di = (long long)RA[cs] - (long long)RE[cs] + (long long)fl;
     df = l - fl;
-    for (int i = tid; i < n; i += NT) {
+    // entries relative to 2^best.v: E as e 2^(RE - re0 - bv), A as
+    // a 2^(RA - re0 - di - df - bv); integer parts by ldexp (exact),
+    // fractional parts by two factors formed once
+    const double bi = floor(best.v);
+    const long long bvi = (long long)bi;
+    const double fe = exp2(bi - best.v), fa = exp2(bi - best.v - df);
+    auto pow2 = [](double x, long long k) {
+      return ldexp(x, (int)(k < -4000 ? -4000 : (k > 4000 ? 4000 : k)));
+    };
+    for (int i = tid, c = tid % C; i < n; i += NT) {
       const double a = A[i], e = E[i];
-      if (a == 0.0 && e == 0.0) continue;
-      const int c = i % C;
-      const double we =
-          e > 0.0 ? exp2((double)((long long)RE[c] - re0) + log2(e) - best.v) : 0.0;
-      const double wa =
-          a > 0.0 ? exp2((double)((long long)RA[c] - re0 - di) + (log2(a) - df) - best.v) : 0.0;
-      mism = fmax(mism, fabs(wa - we));
+      if (a != 0.0 || e != 0.0) {
+        const double we = e > 0.0 ? pow2(e * fe, (long long)RE[c] - re0 - bvi) : 0.0;
+        const double wa = a > 0.0 ? pow2(a * fa, (long long)RA[c] - re0 - di - bvi) : 0.0;
+        mism = fmax(mism, fabs(wa - we));
+      }
+      c += cstep;
+      c -= c >= C ? C : 0;
     }
     for (int off = 32; off > 0; off >>= 1) mism = fmax(mism, __shfl_xor(mism, off));
     __syncthreads();
