@@ -217,7 +217,7 @@ def run_workload(name, steps, warmup, ckpt, peaks, dev, want_rates, want_memory=
     t = {k: torch.from_numpy(inp[k]).to(dev) for k in ("emissions", "lengths", "trans", "dur")}
     plan = bd.FwdBwdPlan(t["emissions"], t["lengths"], t["trans"], t["dur"],
                          checkpoint_interval=ckpt)
-    interval = ckpt or bd.semicrf_checkpoint_interval(B, T, K)
+    interval = ckpt or bd.semicrf_checkpoint_interval(B, T, C, K)
     nph = len(bd.FWD_BWD_PHASES)
     for _ in range(warmup):
         plan.run()

@@ -118,9 +118,11 @@ int semicrf_default_checkpoint_interval(int T, int K);
 /* The checkpoint interval semicrf_logz_fwd and semicrf_fwd_bwd use when
  * given 0: the default above, halved while the sweeps (one workgroup per
  * direction, sequence and interval; every interval is swept concurrently)
- * would have fewer than 256 workgroups, and never below max(2K, 32).
- * Returns 0 for B, T or K < 1. */
-int semicrf_checkpoint_interval(int B, int T, int K);
+ * would have fewer workgroups than the GPU runs at once -- 256, or 512 for
+ * the C <= 16 engine while two of its workgroups fit one compute unit's LDS
+ * (C = 16 up to K of about 550) -- and never below max(2K, 32).  Depends on C
+ * through the engine.  Returns 0 for B, T, C or K < 1. */
+int semicrf_checkpoint_interval(int B, int T, int C, int K);
 
 /* Bytes of device workspace `op` needs for these sizes.  checkpoint_interval
  * is the one passed to semicrf_fwd_bwd (0 = default; ignored by other ops).
@@ -160,7 +162,7 @@ semicrf_status_t semicrf_logz_fwd(const float *emissions, const int32_t *lengths
  *   marginals [B][T][C] or NULL coverage mu[b,t,c] = P(position t lies in a
  *                               segment of label c); sums to 1 over c.
  * checkpoint_interval: positions between stored forward/backward states
- * (0 = semicrf_checkpoint_interval(B, T, K)).  Results do not depend on it
+ * (0 = semicrf_checkpoint_interval(B, T, C, K)).  Results do not depend on it
  * beyond rounding. */
 semicrf_status_t semicrf_fwd_bwd(const float *emissions, const int32_t *lengths,
                                  const float *trans, const float *dur,

@@ -62,7 +62,7 @@ def load():
     lib.semicrf_status_string.restype = ctypes.c_char_p
     lib.semicrf_default_checkpoint_interval.argtypes = [I, I]
     lib.semicrf_default_checkpoint_interval.restype = I
-    lib.semicrf_checkpoint_interval.argtypes = [I, I, I]
+    lib.semicrf_checkpoint_interval.argtypes = [I, I, I, I]
     lib.semicrf_checkpoint_interval.restype = I
     lib.semicrf_workspace_size.argtypes = [I, I, I, I, I, U, I, ctypes.POINTER(Z)]
     lib.semicrf_workspace_size.restype = I
@@ -94,9 +94,9 @@ def semicrf_default_checkpoint_interval(T: int, K: int) -> int:
     return int(load().semicrf_default_checkpoint_interval(int(T), int(K)))
 
 
-def semicrf_checkpoint_interval(B: int, T: int, K: int) -> int:
+def semicrf_checkpoint_interval(B: int, T: int, C: int, K: int) -> int:
     """Interval used by logz / fwd_bwd when given 0 (see semicrf.h)."""
-    return load().semicrf_checkpoint_interval(int(B), int(T), int(K))
+    return load().semicrf_checkpoint_interval(int(B), int(T), int(C), int(K))
 
 
 def semicrf_workspace_size(op: int, B: int, T: int, C: int, K: int, flags: int = 0,

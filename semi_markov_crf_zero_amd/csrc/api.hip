@@ -69,9 +69,10 @@ bool chain_config(int C, int K, ChainShape &sh) {
   return false;
 }
 
-// Blocked windowed engine (C <= 32, 256 threads): applies when its LDS (ring
-// and exp(dur) table, K*C float64 each, plus block buffers) fits.  Other
-// shapes run on the LDS-ring engine.
+// Blocked windowed engine (C <= 32, 256 threads): applies when its LDS (the
+// ring, K*C float64, plus block buffers) fits and each helper thread's far
+// durations fit its registers (at most 8 * kWinFarChunks).  Other shapes run
+// on the LDS-ring engine.
 bool win_config(int C, int K, ChainShape &sh) {
   if (C < 1 || C > 32) return false;
   const int NT = 256;
@@ -85,6 +86,7 @@ bool win_config(int C, int K, ChainShape &sh) {
   // so no chunk reaches into the next group's durations
   const int dch = A <= 2 ? 2 : (A <= 4 ? 4 : 8);
   A = (A + dch - 1) / dch * dch;
+  if (A > dch * (dch == 8 ? kWinFarChunks : 1)) return false;
   if (win_lds_bytes(C, K, P) > kMaxDynLds) return false;
   sh.NT = NT;
   sh.P = P;
@@ -108,15 +110,34 @@ int default_delta(int T, int K) {
 }
 
 // Interval used when the caller passes 0: the sqrt(T*K) rule, halved while
-// the sweep (one workgroup per direction and interval) would have fewer than
-// kSweepWorkgroups workgroups -- each interval is a serial chain of its
-// length, so more intervals finish sooner until the chip is full -- and
-// never below max(2K, 32) positions, so each interval spans several
-// segment lengths and forgets its neutral start.
+// the sweep (one workgroup per direction and interval) would have fewer
+// workgroups than the chip holds at once -- each interval is a serial chain
+// of its length, so more intervals finish sooner until the chip is full --
+// and never below max(2K, 32) positions, so each interval spans several
+// segment lengths and forgets its neutral start.  The chip holds one
+// workgroup per compute unit of every engine, and two of the windowed
+// engine while two of its LDS footprints fit one compute unit: one chain's
+// step is a latency-bound dependent chain, and a second chain on the same
+// unit hides most of it (measured at C = 16: 638 ns per step alone, 764 ns
+// with two per unit).
 constexpr long long kSweepWorkgroups = 256;
 
+// Two windowed workgroups per compute unit need two LDS footprints and two
+// waves' registers per SIMD (at most 256 VGPRs + AGPRs a wave): the
+// instances for C <= 16 take 250, those for 16 < C <= 32 with far chunks of
+// 8 durations 263 (one per unit), with chunks of 2 or 4 durations 209.
+long long sweep_workgroups(int C, int K) {
+  ChainShape w{};
+  if (win_config(C, K, w) && (C <= 16 || w.A <= 4) &&
+      2 * (win_lds_bytes(C, K, w.P) + 256) <= kMaxLds)
+    return 2 * kSweepWorkgroups;
+  return kSweepWorkgroups;
+}
+
 // Burn-in of a chunk without an exact start (parallel-in-time iteration 0),
-// for intervals of at least 8K positions: kBurnIn positions.  The ring's
+// for intervals of at least 8K positions, or of at least 4K and 1024
+// positions (the burn-in then costs at most 1/32 of the interval):
+// kBurnIn positions.  The ring's
 // entries are exp-space values relative to the newest ones, and the scores
 // grow by several nats per position, so entries a few dozen positions old
 // weigh nothing at the verification's 1e-12; what has to settle is the
@@ -129,13 +150,15 @@ constexpr long long kSweepWorkgroups = 256;
 constexpr int kBurnIn = 32;
 
 int burn_in(int delta, int K) {
-  return (long long)delta < 8LL * K ? 0 : kBurnIn;
+  const long long d = delta;
+  return (d >= 8LL * K || (d >= 4LL * K && d >= 32 * kBurnIn)) ? kBurnIn : 0;
 }
 
-int effective_delta(int B, int T, int K) {
+int effective_delta(int B, int T, int C, int K) {
   int d = default_delta(T, K);
   const int dmin = 2 * K > 32 ? 2 * K : 32;
-  while ((d + 1) / 2 >= dmin && 2LL * B * ((T + d - 1) / d) < kSweepWorkgroups) d = (d + 1) / 2;
+  const long long target = sweep_workgroups(C, K);
+  while ((d + 1) / 2 >= dmin && 2LL * B * ((T + d - 1) / d) < target) d = (d + 1) / 2;
   return d;
 }
 
@@ -301,7 +324,7 @@ semicrf_status_t prepare(int op, int B, int T, int C, int K, unsigned flags, int
       if (d < K) d = K;
       sh.delta = d < T ? d : T;
     } else {
-      sh.delta = ckpt > 0 ? (ckpt < T ? ckpt : T) : effective_delta(B, T, K);
+      sh.delta = ckpt > 0 ? (ckpt < T ? ckpt : T) : effective_delta(B, T, C, K);
     }
     sh.nchunk = (T + sh.delta - 1) / sh.delta;
     sh.burn = burn_in(sh.delta, K);
@@ -411,9 +434,9 @@ int semicrf_default_checkpoint_interval(int T, int K) {
   return default_delta(T, K);
 }
 
-int semicrf_checkpoint_interval(int B, int T, int K) {
-  if (B < 1 || T < 1 || K < 1) return 0;
-  return effective_delta(B, T, K);
+int semicrf_checkpoint_interval(int B, int T, int C, int K) {
+  if (B < 1 || T < 1 || C < 1 || K < 1) return 0;
+  return effective_delta(B, T, C, K);
 }
 
 semicrf_status_t semicrf_workspace_size(int op, int B, int T, int C, int K, unsigned flags,

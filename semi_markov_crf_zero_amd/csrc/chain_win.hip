@@ -13,10 +13,13 @@
 //     previous block began.  So while the chain runs block n, the helper
 //     waves 1-3 compute the far parts of block n+1 for its U steps at once:
 //     thread (g, c) owns the durations k = a0 .. a0+A-1 (a0 >= 2U) of label
-//     c, fills a register window with the entries (consecutive positions,
-//     read across the ring's wrap from its mirror copy of the first slots)
-//     and accumulates U sums -- U*A fused multiply-adds with full
-//     instruction-level parallelism.
+//     c, holds their weights exp(dur) in registers for the whole sweep, fills
+//     a register window with the entries (consecutive positions, read across
+//     the ring's wrap from its mirror copy of the first slots) and
+//     accumulates U sums -- U*A fused multiply-adds with full
+//     instruction-level parallelism.  Only the ring and small block buffers
+//     live in LDS, so two workgroups share a compute unit up to K*C of about
+//     8800 (C = 16 with K = 512) and hide each other's step latency.
 //     Partials are reduced inside each wave (DPP) and land in the other of
 //     two LDS buffers.  One workgroup barrier per block.
 //   * the "chain wave" (wave 0, lane c = label c) runs the block's U steps
@@ -51,7 +54,7 @@ constexpr int U = kWinU;         // positions per block
 constexpr int kNearW = 2 * U - 1;  // near terms k = 1 .. 2U-1 (the chain's register window)
 
 struct WSmem {
-  double *ring, *dtab, *part, *stg, *erow;
+  double *ring, *part, *stg, *erow;
   double *efx, *efy;  // split scores of two blocks [2][U][C]
   int *shiftn, *flag, *en;
 };
@@ -72,7 +75,6 @@ __device__ __forceinline__ WSmem wcarve(unsigned char *base, const ChainShape &s
   size_t off = 0;
   const int C4 = cpad(s.C);
   m.ring = reinterpret_cast<double *>(base + off); off += (size_t)(s.K + kWinMirror) * s.C * 8;
-  m.dtab = reinterpret_cast<double *>(base + off); off += (size_t)(s.K + kWinDurPad) * s.C * 8;
   m.part = reinterpret_cast<double *>(base + off);
   off += (size_t)2 * U * part_groups(s, NT) * s.C * 8;  // [2][U][G][C]
   m.stg = reinterpret_cast<double *>(base + off); off += (size_t)2 * U * (3 * s.C + 1) * 8;
@@ -100,23 +102,6 @@ __device__ __forceinline__ void ring_put(const WSmem &sm, int K, int C, int slot
   if (slot < kWinMirror) sm.ring[(slot + K) * C + c] = v;
 }
 
-// exp(dur) in float64 (a rounded weight would perturb the parameters, and
-// the parameter gradients move by that times a sensitivity that grows with
-// the sequence length): dtab[(k-1)*C + c] = exp(dur[k-1][c]).
-__device__ __forceinline__ void stage_dur(const WSmem &sm, const ChainShape &sh,
-                                          const float *__restrict__ dur, int NT) {
-  const int n = sh.K * sh.C;
-  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * NT) {  // 4 loads in flight per thread
-    float v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = dur[min(i0 + u * NT, n - 1)];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (i0 + u * NT < n) sm.dtab[i0 + u * NT] = exp((double)v[u]);
-  }
-  for (int i = threadIdx.x; i < kWinDurPad * sh.C; i += NT) sm.dtab[sh.K * sh.C + i] = 0.0;
-}
-
 // The contraction of a label is split over kSplit lanes of wave 0: lane l
 // takes label c = l % CMAX and the previous labels c' of part
 // h = (l / CMAX) % kSplit, c' = h*CMAX/kSplit + j; lane_swap_add joins the
@@ -132,8 +117,7 @@ static_assert(32 * kSplit<32> <= 64 && 16 * kSplit<16> <= 64, "parts fit one wav
 // label c' = h*CMAX/kSplit + j for output label c, zero past C.
 template <int CMAX>
 __device__ __forceinline__ void load_tr_row(const ChainShape &sh, const float *__restrict__ trans,
-                                            bool fwd, int lane,
-                                            double (&tr)[CMAX / kSplit<CMAX>]) {
+                                            bool fwd, int lane, double *tr) {
   constexpr int NJ = CMAX / kSplit<CMAX>;
   const int C = sh.C, c = lane % CMAX, h = (lane / CMAX) % kSplit<CMAX>;
 #pragma unroll
@@ -162,11 +146,26 @@ __device__ __forceinline__ double group_sum(double v, int gw) {
 // lanes of a wave (C rounded up to a power of two; lanes past C idle), so
 // the gw = 64/cp duration groups of one label in a wave are consecutive
 // lanes and their partials add up by DPP.
+template <int DCH, int CMAX>
 struct Win {
+  // duration chunks a helper thread holds: A <= DCH * NCH (win_config)
+  static constexpr int NCH = DCH == 8 ? kWinFarChunks : 1;
+  // the chain wave's weights in the same registers: exp(dur) of the near
+  // durations (Dn[k], k = 0 .. 2U-1) and its lane's exp(trans) part
+  static constexpr int NCHAIN = kNearW + 1 + CMAX / kSplit<CMAX>;
+  static constexpr int NW = DCH * NCH > NCHAIN ? DCH * NCH : NCHAIN;
   int kc, kg, a0, nage, gw;
   bool on;
+  // helper waves: exp(dur) of this thread's durations a0 .. a0 + nage - 1, 0
+  // past them, in float64 (a rounded weight would perturb the parameters,
+  // and the parameter gradients move by that times a sensitivity that grows
+  // with the sequence length); held for the whole sweep.  Wave 0 keeps its
+  // own weights here instead (the two roles never share a wave, and one
+  // array keeps the register count of both within two workgroups per
+  // compute unit).
+  double wd[NW];
 
-  __device__ __forceinline__ void init(const ChainShape &sh) {
+  __device__ __forceinline__ void init(const ChainShape &sh, const float *__restrict__ dur) {
     const int C = sh.C, tid = threadIdx.x, w = tid >> 6;
     int cp = 1;
     while (cp < C) cp *= 2;
@@ -178,32 +177,36 @@ struct Win {
     int n = on ? sh.K - a0 + 1 : 0;
     n = n < 0 ? 0 : (n > sh.A ? sh.A : n);
     nage = n;
+    float v[NW];  // all loads in flight before the first exponential
+#pragma unroll
+    for (int j = 0; j < NW; ++j) v[j] = j < nage ? dur[(size_t)(a0 + j - 1) * C + kc] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) wd[j] = j < nage ? exp((double)v[j]) : 0.0;
   }
 
   // Step i of the block (position t0 + sigma*i) needs, for duration k, the
   // entry at t0 - sigma*(k - i); here k >= 2U > i and k <= K, so k - i lies
   // in [1, K].  Durations go in chunks of DCH (A is a multiple of DCH, so a
-  // chunk holds this group's durations or rows past K, which are zero): the
-  // chunk's weights and its DCH+U-1 entries (consecutive positions, read
-  // from a start slot that needs no wrap thanks to the ring's mirror) come
-  // from LDS with no branch, then U*DCH fused multiply-adds with
-  // compile-time register indices.
-  template <int DCH>
+  // chunk holds this group's durations or weights past K, which are zero):
+  // the chunk's DCH+U-1 entries (consecutive positions, read from a start
+  // slot that needs no wrap thanks to the ring's mirror) come from LDS with
+  // no branch, then U*DCH fused multiply-adds with compile-time register
+  // indices.
   __device__ __forceinline__ void far(const WSmem &sm, const ChainShape &sh, int t0, int sigma,
                                       double (&F)[U]) {
     constexpr int NR = DCH + U - 1;  // entries per chunk
-    static_assert(NR - 1 <= kWinMirror && DCH <= kWinDurPad, "mirror and padding cover a chunk");
+    static_assert(NR - 1 <= kWinMirror, "the mirror covers a chunk");
 #pragma unroll
     for (int i = 0; i < U; ++i) F[i] = 0.0;
     if (!on) return;
     const int K = sh.K, C = sh.C;
     const int base = pos_slot(t0, K);
     const int rstep = -sigma * C;  // ring index step to the next older position
-    const double *dp = sm.dtab + (size_t)(a0 - 1) * C + kc;
-    for (int jb = 0; jb < nage; jb += DCH) {
-      double dv[DCH], wv[NR];
 #pragma unroll
-      for (int jj = 0; jj < DCH; ++jj) dv[jj] = dp[(jb + jj) * C];
+    for (int cb = 0; cb < NCH; ++cb) {
+      const int jb = cb * DCH;
+      if (jb >= nage) break;
+      double wv[NR];
       // wv[q]: entry at m = k - i = m0 + q, q = jj - i + U - 1; forward the
       // slots fall with q, so a start near 0 moves to its mirror copy
       const int m0 = a0 + jb - (U - 1);
@@ -215,7 +218,7 @@ struct Win {
 #pragma unroll
       for (int i = 0; i < U; ++i) {
 #pragma unroll
-        for (int jj = 0; jj < DCH; ++jj) F[i] = fma(dv[jj], wv[jj - i + U - 1], F[i]);
+        for (int jj = 0; jj < DCH; ++jj) F[i] = fma(wd[jb + jj], wv[jj - i + U - 1], F[i]);
       }
     }
   }
@@ -260,7 +263,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // instead of delaying the step (a wave issues in order).
 template <int CMAX, typename F>
 __device__ __forceinline__ double chain_contract(const WSmem &sm, const ChainShape &sh, int lane,
-                                                 double a, const double (&tr)[CMAX / kSplit<CMAX>],
+                                                 double a, const double *tr,
                                                  F &&meanwhile) {
   constexpr int SP = kSplit<CMAX>, NJ = CMAX / SP;
   static_assert(NJ % 2 == 0, "pairs of previous labels per read");
@@ -436,8 +439,7 @@ template <int CMAX>
 __device__ __forceinline__ void chain_block(const ChainShape &sh, const WSmem &sm, int G, int s0,
                                             int nb, int nsteps, int t0, int sigma, int buf,
                                             bool tail, int lane, bool chain,
-                                            const double (&Dn)[kNearW + 1],
-                                            const double (&tr)[CMAX / kSplit<CMAX>], int s_rec,
+                                            const double *Dn, const double *tr, int s_rec,
                                             ChainState &cs, int &R, int &Bm, double &o_rec,
                                             double &m_rec, double &o_end, double &m_end,
                                             double &lz) {
@@ -630,11 +632,10 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
     if (!pit_any<NT>(marked != 0, red)) return;
   }
   const WSmem sm = wcarve(lds, sh, NT);
-  Win win;
-  win.init(sh);
-  stage_dur(sm, sh, dur, NT);
-  double Dn[kNearW + 1];  // near-part weights of the chain lanes (k = 1 .. 2U-1)
-  double tr[CMAX / kSplit<CMAX>];  // this lane's part of the exp(trans) weights
+  Win<DCH, CMAX> win;
+  win.init(sh, dur);
+  double *const Dn = win.wd;  // near-part weights of the chain lanes (k = 1 .. 2U-1)
+  double *const tr = win.wd + kNearW + 1;  // this lane's part of the exp(trans) weights
   if (tid < 64) {
 #pragma unroll
     for (int k = 0; k <= kNearW; ++k)
@@ -750,7 +751,7 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
       cs.shprev = 0;
     } else {
       double F[U];  // far parts of the first block
-      win.template far<DCH>(sm, sh, first, sigma, F);
+      win.far(sm, sh, first, sigma, F);
       win.publish(sm, sh, NT, F, 0);
     }
     __syncthreads();
@@ -778,7 +779,7 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
           // far parts of the next block: entries older than this block only,
           // none of the slots the chain writes meanwhile
           double F[U];
-          win.template far<DCH>(sm, sh, t0 + sigma * U, sigma, F);
+          win.far(sm, sh, t0 + sigma * U, sigma, F);
           win.publish(sm, sh, NT, F, buf ^ 1);
         }
         // the next block's scores land in the other buffer before the barrier

@@ -132,15 +132,16 @@ __host__ __device__ inline size_t viterbi_lds_bytes(int C, int K, int P, int Q) 
 __host__ __device__ inline size_t ck_stride(int C, int K) { return (size_t)(K + 3) * C; }
 
 // Positions per block of the windowed engine (chain_win.hip).
-constexpr int kWinU = 8;
+constexpr int kWinU = 4;
 // Its ring keeps a second copy of slots [0, kWinMirror) after slot K-1, so
 // the far loop reads up to 8 + kWinU - 1 consecutive positions without a
-// wrap; its exp(dur) table has kWinDurPad zero rows past K.
+// wrap.
 constexpr int kWinMirror = 16;
-constexpr int kWinDurPad = 8;
+// Far-part duration chunks (of 8) a helper thread holds in registers.
+constexpr int kWinFarChunks = 6;
 
 // LDS bytes of the windowed chain engine (chain_win.hip, 256 threads, same
-// order as its carve-up): ring (with its mirror), exp(dur) table (padded), far-part partials
+// order as its carve-up): ring (with its mirror), far-part partials
 // [U][groups][C], row staging of two blocks, e row (padded to the
 // contraction width 8, 16 or 32), rebase shifts, flags, split scores of two
 // blocks.
@@ -150,7 +151,6 @@ __host__ __device__ inline size_t win_lds_bytes(int C, int K, int P) {
   const int groups = 256 / 64 - 1;  // far-part partials: one per helper wave
   size_t off = 0;
   off += (size_t)(K + kWinMirror) * C * 8;
-  off += (size_t)(K + kWinDurPad) * C * 8;
   off += (size_t)2 * kWinU * groups * C * 8;
   off += (size_t)2 * kWinU * (3 * C + 1) * 8;
   off = align_up(off, 16);

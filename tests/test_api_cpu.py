@@ -52,17 +52,25 @@ def test_default_checkpoint_interval(lib):
 
 
 def test_checkpoint_interval_fills_the_sweep(lib):
-    # halved from ceil(sqrt(T*K)) while 2*B*ceil(T/interval) < 256, not below max(2K, 32)
-    assert bd.semicrf_checkpoint_interval(4, 131072, 512) == 4096    # genome: 256 workgroups
-    assert bd.semicrf_checkpoint_interval(1, 1048576, 256) == 8192   # extreme: 256
-    assert bd.semicrf_checkpoint_interval(16, 4096, 64) == 512       # speech: 256 already
-    assert bd.semicrf_checkpoint_interval(32, 512, 32) == 128        # nlp: 256 already
-    assert bd.semicrf_checkpoint_interval(4, 256, 16) == 32          # tiny: floor 2K = 32
-    assert bd.semicrf_checkpoint_interval(64, 100000, 8) == 895      # already >= 512 workgroups
-    assert bd.semicrf_checkpoint_interval(1, 3, 100) == 3            # capped at T
-    assert bd.semicrf_checkpoint_interval(0, 10, 4) == 0
-    for B, T, K in ((4, 131072, 512), (1, 1048576, 256), (2, 777, 5), (3, 50, 80)):
-        d = bd.semicrf_checkpoint_interval(B, T, K)
+    # halved from ceil(sqrt(T*K)) while 2*B*ceil(T/interval) is below the
+    # workgroups the GPU runs at once (512 for the C <= 32 engine while two of
+    # its workgroups fit a compute unit's LDS and registers, else 256), not
+    # below max(2K, 32)
+    ci = bd.semicrf_checkpoint_interval
+    assert ci(4, 131072, 16, 512) == 2048     # genome: 512 windowed workgroups
+    assert ci(4, 131072, 16, 1024) == 2897    # LDS-ring engine: 256 workgroups
+    assert ci(1, 1048576, 64, 256) == 8192    # extreme: 256
+    assert ci(16, 4096, 256, 64) == 512       # speech: 256 already
+    assert ci(32, 512, 24, 32) == 128         # nlp: 256 already (C > 16: one per unit)
+    assert ci(32, 512, 16, 32) == 64          # C <= 16: 512 windowed workgroups
+    assert ci(4, 256, 8, 16) == 32            # tiny: floor 2K = 32
+    assert ci(64, 100000, 8, 8) == 895        # already >= 512 workgroups
+    assert ci(1, 3, 4, 100) == 3              # capped at T
+    assert ci(0, 10, 4, 4) == 0
+    assert ci(1, 10, 0, 4) == 0
+    for B, T, C, K in ((4, 131072, 16, 512), (1, 1048576, 64, 256), (2, 777, 3, 5),
+                       (3, 50, 40, 80)):
+        d = ci(B, T, C, K)
         assert 1 <= d <= bd.semicrf_default_checkpoint_interval(T, K)
 
 
