@@ -344,12 +344,14 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
   double *rho = pmin + 256;                      // [16] reference per label
   int *fast = reinterpret_cast<int *>(rho + 16);  // [16]
   double accf[KB], accs[KB], dk[KB];
+  float dv[KB];  // every load issued first (lags clamped into the group)
+#pragma unroll
+  for (int j = 0; j < KB; ++j) dv[j] = pa.dur[(size_t)(min(k0 + j, khi) - 1) * C + c];
 #pragma unroll
   for (int j = 0; j < KB; ++j) {
     accf[j] = 0.0;
     accs[j] = 0.0;
-    const int k = k0 + j;
-    dk[j] = (act && k <= khi) ? (double)pa.dur[(size_t)(k - 1) * C + c] : 0.0;
+    dk[j] = (act && k0 + j <= khi) ? (double)dv[j] : 0.0;
   }
   if (valid_len(sh, L)) {
     const double logZ = pa.logz[b];
@@ -362,19 +364,39 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
       const int ne = min(ns - 1 + khi - klo + 1, L - s0 - klo + 1);
       __syncthreads();
       // staging: thread (row r0 + 16 i, label column cc); the row's index
-      // and correction once per row, no division
+      // and correction once per row, no division; the loads of a batch of
+      // rows are all issued before the first use (row indices clamped into
+      // the tile, stores masked)
       const int cc = tid & 15, r0 = tid >> 4;
+      constexpr int RS = kDurThreads / 16;  // row stride
       if (cc < CG) {
-        for (int ss = r0; ss < ns; ss += kDurThreads / 16) {
-          const size_t ri = rix(sh, pa, b, s0 + ss) + c0 + cc;
-          sa[ss * 16 + cc] = (pa.row_u[ri] + shift_f(sh, pa, b, s0 + ss)) -
-                             Sb[(size_t)(s0 + ss) * C + c0 + cc];
+        {
+          constexpr int NA = kDurW / RS;  // start rows per thread
+          double u[NA], f[NA], sv[NA];
+#pragma unroll
+          for (int i = 0; i < NA; ++i) {
+            const int t = s0 + min(r0 + RS * i, ns - 1);
+            u[i] = pa.row_u[rix(sh, pa, b, t) + c0 + cc];
+            f[i] = shift_f(sh, pa, b, t);
+            sv[i] = Sb[(size_t)t * C + c0 + cc];
+          }
+#pragma unroll
+          for (int i = 0; i < NA; ++i)
+            if (r0 + RS * i < ns) sa[(r0 + RS * i) * 16 + cc] = (u[i] + f[i]) - sv[i];
         }
-        for (int ee = r0; ee < ne; ee += kDurThreads / 16) {
-          const int e = s0 + klo + ee;
-          const size_t ri = rix(sh, pa, b, e) + c0 + cc;
-          sb[ee * 16 + cc] =
-              (Sb[(size_t)e * C + c0 + cc] + (pa.row_b[ri] + shift_b(sh, pa, b, e))) - logZ;
+        constexpr int NE = 8;  // end rows per batch
+        for (int e0 = r0; e0 < ne; e0 += NE * RS) {
+          double sv[NE], bv[NE], fv[NE];
+#pragma unroll
+          for (int i = 0; i < NE; ++i) {
+            const int e = s0 + klo + min(e0 + RS * i, ne - 1);
+            sv[i] = Sb[(size_t)e * C + c0 + cc];
+            bv[i] = pa.row_b[rix(sh, pa, b, e) + c0 + cc];
+            fv[i] = shift_b(sh, pa, b, e);
+          }
+#pragma unroll
+          for (int i = 0; i < NE; ++i)
+            if (e0 + RS * i < ne) sb[(e0 + RS * i) * 16 + cc] = (sv[i] + (bv[i] + fv[i])) - logZ;
         }
       }
       __syncthreads();
@@ -402,12 +424,27 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
       }
       __syncthreads();
       // fast labels: the factors, zero past the tile's starts and ends
+      // (a batch of rows read before the first exponential)
       if (cc < CG && fast[cc]) {
         const double rc = rho[cc];
-        for (int ss = r0; ss < kDurW; ss += kDurThreads / 16)
-          sa[ss * 16 + cc] = ss < ns ? exp_wide(sa[ss * 16 + cc] - rc) : 0.0;
-        for (int ee = r0; ee < sbrows; ee += kDurThreads / 16)
-          sb[ee * 16 + cc] = ee < ne ? exp_wide(sb[ee * 16 + cc] + rc) : 0.0;
+        {
+          constexpr int NA = kDurW / RS;
+          double v[NA];
+#pragma unroll
+          for (int i = 0; i < NA; ++i) v[i] = sa[(r0 + RS * i) * 16 + cc];
+#pragma unroll
+          for (int i = 0; i < NA; ++i)
+            sa[(r0 + RS * i) * 16 + cc] = r0 + RS * i < ns ? exp_wide(v[i] - rc) : 0.0;
+        }
+        constexpr int NE = 8;
+        for (int e0 = r0; e0 < sbrows; e0 += NE * RS) {
+          double v[NE];
+#pragma unroll
+          for (int i = 0; i < NE; ++i) v[i] = sb[min(e0 + RS * i, sbrows - 1) * 16 + cc];
+#pragma unroll
+          for (int i = 0; i < NE; ++i)
+            if (e0 + RS * i < sbrows) sb[(e0 + RS * i) * 16 + cc] = e0 + RS * i < ne ? exp_wide(v[i] + rc) : 0.0;
+        }
       }
       __syncthreads();
       if (!act) continue;
