@@ -202,15 +202,23 @@ struct Win {
     const int K = sh.K, C = sh.C;
     const int base = pos_slot(t0, K);
     const int rstep = -sigma * C;  // ring index step to the next older position
+    // slot of the first chunk's first entry, m = a0 - (U - 1) in [U + 1, K]
+    // positions back: base - sigma*m lies in (-K, 2K), so one wrap, no division
+    int sf = base - sigma * (a0 - (U - 1));
+    sf += sf < 0 ? K : 0;
+    sf -= sf >= K ? K : 0;
 #pragma unroll
     for (int cb = 0; cb < NCH; ++cb) {
       const int jb = cb * DCH;
       if (jb >= nage) break;
       double wv[NR];
-      // wv[q]: entry at m = k - i = m0 + q, q = jj - i + U - 1; forward the
-      // slots fall with q, so a start near 0 moves to its mirror copy
-      const int m0 = a0 + jb - (U - 1);
-      int s0 = pos_slot(base - sigma * m0, K);
+      // wv[q]: entry at m = k - i = m0 + q, m0 = a0 + jb - (U - 1),
+      // q = jj - i + U - 1 (jb < nage <= K - a0 + 1, so one wrap again);
+      // forward the slots fall with q, so a start near 0 moves to its mirror
+      // copy
+      int s0 = sf - sigma * jb;
+      s0 += s0 < 0 ? K : 0;
+      s0 -= s0 >= K ? K : 0;
       if (sigma > 0 && s0 < NR - 1) s0 += K;
       const double *rp = sm.ring + (size_t)s0 * C + kc;
 #pragma unroll
@@ -366,9 +374,9 @@ __device__ __forceinline__ void block_rows(const double *stg, int C, int nb, int
     const double *s = stg + m * S;
     const size_t o = (size_t)(t0 + sigma * m) * C;
     if (r < C)
-      row1[o + r] = log(s[r]) + s[C + r] * kLn2;
+      row1[o + r] = log_plus(s[r], s[C + r]);
     else if (m != no2)
-      row2[o + r - C] = log(s[C + r]) + s[3 * C] * kLn2;
+      row2[o + r - C] = log_plus(s[C + r], s[3 * C]);
   }
 }
 

@@ -40,6 +40,35 @@ __device__ __forceinline__ double log_wide(double x) {
   return (static_cast<double>(e) + static_cast<double>(l2)) * kLn2;
 }
 
+// log(x) + q ln 2 for float64 x > 0 and an integer-valued q (0 gives -inf,
+// +inf and NaN pass through): x = m 2^e with m in [2^-1/2, 2^1/2);
+// log m = 2 atanh(s), s = (m - 1) / (m + 1), |s| <= 0.172, by its series
+// sum_k s^(2k+1) / (2k+1) through k = 11 (the next term is below 1e-18 of
+// the sum); (e + q) ln 2 with a two-part ln 2, so a large q costs no
+// accuracy.  About a third of the instructions of the library logarithm.
+// The coefficients come from constant memory through scalar registers
+// (as literals the compiler would hold them in vector registers).
+__constant__ double kAtanhSeries[12] = {1.0,        1.0 / 3.0,  1.0 / 5.0,  1.0 / 7.0,
+                                        1.0 / 9.0,  1.0 / 11.0, 1.0 / 13.0, 1.0 / 15.0,
+                                        1.0 / 17.0, 1.0 / 19.0, 1.0 / 21.0, 1.0 / 23.0};
+__device__ __forceinline__ double log_plus(double x, double q) {
+  if (!(x > 0.0 && x < __builtin_huge_val())) return x == 0.0 ? -__builtin_huge_val() : x + x;
+  int ex;
+  double m = frexp(x, &ex);  // [1/2, 1)
+  if (m < 0.70710678118654752440) {
+    m *= 2.0;
+    ex -= 1;
+  }
+  const double f = m - 1.0;  // exact
+  const double s = f / (2.0 + f);
+  const double z = s * s;
+  double p = kAtanhSeries[11];
+#pragma unroll
+  for (int k = 10; k >= 0; --k) p = fma(p, z, kAtanhSeries[k]);
+  const double qe = (double)ex + q;
+  return fma(qe, kLn2, fma(qe, kLn2Lo, 2.0 * s * p));
+}
+
 // exp(y) in float32 for y <= ~88 (probabilities and bounded ratios).
 __device__ __forceinline__ float exp_f32(double y) {
   return __builtin_amdgcn_exp2f(static_cast<float>(y * kLog2e));
