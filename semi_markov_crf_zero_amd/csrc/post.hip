@@ -339,20 +339,15 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
   // (+8: the end-row window of the fast path slides once past the tile)
   const int sbrows = kDurW + min(K, kDurLags) + KB + 8;
   double *sb = sa + (size_t)kDurW * 16;
-  double *pmax = sb + (size_t)sbrows * 16;  // [16][16] partial max / min of a
-  double *pmin = pmax + 256;
-  double *rho = pmin + 256;                      // [16] reference per label
+  double *pmax = sb + (size_t)sbrows * 16;  // [4][16] per-wave max / min of a
+  double *pmin = pmax + 64;
+  double *rho = pmin + 64;                       // [16] reference per label
   int *fast = reinterpret_cast<int *>(rho + 16);  // [16]
-  double accf[KB], accs[KB], dk[KB];
-  float dv[KB];  // every load issued first (lags clamped into the group)
+  // sum over the starts of exp(a[s] + b[s+k]) per lag; exp(dur) is applied
+  // once at the end, so the duration biases need no registers meanwhile
+  double acc[KB];
 #pragma unroll
-  for (int j = 0; j < KB; ++j) dv[j] = pa.dur[(size_t)(min(k0 + j, khi) - 1) * C + c];
-#pragma unroll
-  for (int j = 0; j < KB; ++j) {
-    accf[j] = 0.0;
-    accs[j] = 0.0;
-    dk[j] = (act && k0 + j <= khi) ? (double)dv[j] : 0.0;
-  }
+  for (int j = 0; j < KB; ++j) acc[j] = 0.0;
   if (valid_len(sh, L)) {
     const double logZ = pa.logz[b];
     const double *Sb = pa.S + (size_t)b * (sh.T + 1) * C;
@@ -400,22 +395,29 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
         }
       }
       __syncthreads();
-      {  // per label: the largest a of the tile and its range
-        const int part = r0;
+      {  // per label: the largest a of the tile and its range (rows r0 + 16 i,
+         // then the wave's four row groups of the label: lanes 16 and 32 apart)
         double hi = -__builtin_huge_val(), lo = __builtin_huge_val();
         if (cc < CG)
-          for (int ss = part; ss < ns; ss += 16) {
+          for (int ss = r0; ss < ns; ss += 16) {
             const double v = sa[ss * 16 + cc];
             hi = fmax(hi, v);
             lo = fmin(lo, v);
           }
-        pmax[part * 16 + cc] = hi;
-        pmin[part * 16 + cc] = lo;
+#pragma unroll
+        for (int off = 16; off < 64; off <<= 1) {
+          hi = fmax(hi, __shfl_xor(hi, off));
+          lo = fmin(lo, __shfl_xor(lo, off));
+        }
+        if ((tid & 63) < 16) {
+          pmax[(tid >> 6) * 16 + cc] = hi;
+          pmin[(tid >> 6) * 16 + cc] = lo;
+        }
       }
       __syncthreads();
       if (tid < 16) {
         double hi = -__builtin_huge_val(), lo = __builtin_huge_val();
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < kDurThreads / 64; ++q) {
           hi = fmax(hi, pmax[q * 16 + tid]);
           lo = fmin(lo, pmin[q * 16 + tid]);
         }
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
 #pragma unroll
           for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < KB; ++j) accf[j] = fma(A[i], W[i + j], accf[j]);
+            for (int j = 0; j < KB; ++j) acc[j] = fma(A[i], W[i + j], acc[j]);
 #pragma unroll
           for (int q = 0; q < NW - 8; ++q) W[q] = W[q + 8];
 #pragma unroll
@@ -481,7 +483,7 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
         for (int ss = 0; ss < ns; ++ss) {
           const double av = sa[ss * 16 + cl];
 #pragma unroll
-          for (int j = 0; j < KB; ++j) accs[j] += exp_wide(av + w[j] + dk[j]);
+          for (int j = 0; j < KB; ++j) acc[j] += exp_wide(av + w[j]);
 #pragma unroll
           for (int j = 0; j < KB - 1; ++j) w[j] = w[j + 1];
           const int ee = ss + 1 + kofs + KB - 1;
@@ -497,7 +499,7 @@ __global__ __launch_bounds__(kDurThreads) void k_dur_x(ChainShape sh, PostArgs p
       const int k = k0 + j;
       if (k <= khi) {
         const size_t o = (size_t)(k - 1) * C + c;
-        const double v = fma(exp(dk[j]), accf[j], accs[j]);
+        const double v = exp((double)pa.dur[o]) * acc[j];
         out[o] = pa.accumulate ? out[o] + v : v;
       }
     }
@@ -643,7 +645,7 @@ void post_geometry(const ChainShape &sh, PostGeom &g, int Tw) {
   while (g.dur_kb < 32 && cg * ((lags + g.dur_kb - 1) / g.dur_kb) > kDurThreads) g.dur_kb *= 2;
   g.dur_npg = (sh.K + kDurLags - 1) / kDurLags;
   // a, b, partial maxima and minima of a, per-label references and paths
-  g.dur_lds = (size_t)(kDurW + kDurW + lags + g.dur_kb + 8) * 16 * 8 + 2 * 256 * 8 + 16 * 8 + 16 * 4;
+  g.dur_lds = (size_t)(kDurW + kDurW + lags + g.dur_kb + 8) * 16 * 8 + 2 * 64 * 8 + 16 * 8 + 16 * 4;
 }
 
 hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream_t st) {
