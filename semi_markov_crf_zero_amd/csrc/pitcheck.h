@@ -20,6 +20,7 @@ constexpr double kPitTol = 1e-12;  // direction mismatch accepted, relative to t
 // chains that reach one state along different paths agree to float32
 // rounding there, so a float64-level bar would reject every converged chunk.
 constexpr double kPitTolF32 = 1e-5;
+constexpr int kPitBatch = 8;  // record entries per thread and batch of loads
 
 struct PitMaxArg {
   double v;
@@ -61,17 +62,28 @@ __device__ bool pit_check(const ChainShape &sh, const PitBufs &pb, bool fwd, int
   // an entry of E within a factor 2^0.09 of its largest, in log2 relative to
   // E's label-0 reference (exponent plus the mantissa's chord: log2 of
   // 2m in [1, 2) taken as 2m - 1)
+  // (entries in batches of kPitBatch per thread, every load of a batch
+  // issued before the first use; the maximum does not depend on the order)
   PitMaxArg best = {-__builtin_huge_val(), 0x7fffffff};
-  for (int i = tid, c = tid % C; i < n; i += NT) {
-    const double e = E[i];
-    if (e > 0.0) {
-      int ex;
-      const double m = frexp(e, &ex);
-      const double le = (double)((long long)RE[c] - re0 + ex) + (2.0 * m - 2.0);
-      best = pit_max_arg(best, PitMaxArg{le, i});
+  for (int i0 = tid, c = tid % C; i0 < n; i0 += kPitBatch * NT) {
+    double ev[kPitBatch], rv[kPitBatch];
+#pragma unroll
+    for (int u = 0; u < kPitBatch; ++u) {
+      const int i = i0 + u * NT;
+      ev[u] = i < n ? E[i] : 0.0;
+      rv[u] = RE[c];
+      c += cstep;
+      c -= c >= C ? C : 0;
     }
-    c += cstep;
-    c -= c >= C ? C : 0;
+#pragma unroll
+    for (int u = 0; u < kPitBatch; ++u) {
+      if (ev[u] > 0.0) {
+        int ex;
+        const double m = frexp(ev[u], &ex);
+        const double le = (double)((long long)rv[u] - re0 + ex) + (2.0 * m - 2.0);
+        best = pit_max_arg(best, PitMaxArg{le, i0 + u * NT});
+      }
+    }
   }
   for (int off = 32; off > 0; off >>= 1) {
     PitMaxArg o;
@@ -104,15 +116,27 @@ __device__ bool pit_check(const ChainShape &sh, const PitBufs &pb, bool fwd, int
     auto pow2 = [](double x, long long k) {
       return ldexp(x, (int)(k < -4000 ? -4000 : (k > 4000 ? 4000 : k)));
     };
-    for (int i = tid, c = tid % C; i < n; i += NT) {
-      const double a = A[i], e = E[i];
-      if (a != 0.0 || e != 0.0) {
-        const double we = e > 0.0 ? pow2(e * fe, (long long)RE[c] - re0 - bvi) : 0.0;
-        const double wa = a > 0.0 ? pow2(a * fa, (long long)RA[c] - re0 - di - bvi) : 0.0;
-        mism = fmax(mism, fabs(wa - we));
+    for (int i0 = tid, c = tid % C; i0 < n; i0 += kPitBatch * NT) {
+      double av[kPitBatch], ev[kPitBatch], ra[kPitBatch], re[kPitBatch];
+#pragma unroll
+      for (int u = 0; u < kPitBatch; ++u) {
+        const int i = i0 + u * NT;
+        av[u] = i < n ? A[i] : 0.0;
+        ev[u] = i < n ? E[i] : 0.0;
+        ra[u] = RA[c];
+        re[u] = RE[c];
+        c += cstep;
+        c -= c >= C ? C : 0;
       }
-      c += cstep;
-      c -= c >= C ? C : 0;
+#pragma unroll
+      for (int u = 0; u < kPitBatch; ++u) {
+        const double a = av[u], e = ev[u];
+        if (a != 0.0 || e != 0.0) {
+          const double we = e > 0.0 ? pow2(e * fe, (long long)re[u] - re0 - bvi) : 0.0;
+          const double wa = a > 0.0 ? pow2(a * fa, (long long)ra[u] - re0 - di - bvi) : 0.0;
+          mism = fmax(mism, fabs(wa - we));
+        }
+      }
     }
     for (int off = 32; off > 0; off >>= 1) mism = fmax(mism, __shfl_xor(mism, off));
     __syncthreads();
