@@ -485,12 +485,15 @@ __device__ __forceinline__ void step256(Sweep256 &c, int base) {
   // 5. the entry exp(m -+ S) / 2^R = d fy 2^(B -+ n - R), its rebase
   const double y = d * c.fy;
   const int sh = B - c.isig * c.fn - c.R;
+  // When a label of the wave leaves the bound, every label of the wave
+  // rebases at once by its own exponent (an exact power of two either way):
+  // the labels drift alike, so they reach the bound again together and the
+  // wave runs the rescale about once every few steps instead of whenever any
+  // one of its 32 labels crosses.
   int n = 0;
-  if (c.label) {
-    const int ey = exponent_of(y) + sh;
-    n = (ey > kRebase || ey < -kRebase) ? ey : 0;
-    c.R += n;
-  }
+  const int ey = c.label ? exponent_of(y) + sh : 0;
+  if (__any(ey > kRebase || ey < -kRebase)) n = ey;
+  c.R += n;
   const float e = c.label ? (float)ldexp(y, sh - n) : 0.0f;
   {  // the label's registers into the new reference (lanes that rebase)
     const unsigned long long m = __ballot(n != 0);
