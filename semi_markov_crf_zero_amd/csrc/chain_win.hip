@@ -201,28 +201,42 @@ struct Win {
     if (!on) return;
     const int K = sh.K, C = sh.C;
     const int base = pos_slot(t0, K);
-    const int rstep = -sigma * C;  // ring index step to the next older position
+    // byte step to the next older position, held in a vector register: as a
+    // uniform value the compiler keeps one multiple of it per read in scalar
+    // registers, which spill (a v_readlane per read); here each read's
+    // address is one add
+    int rstep = -sigma * C * 8;
+    __asm__("" : "+v"(rstep));
     // slot of the first chunk's first entry, m = a0 - (U - 1) in [U + 1, K]
     // positions back: base - sigma*m lies in (-K, 2K), so one wrap, no division
-    int sf = base - sigma * (a0 - (U - 1));
-    sf += sf < 0 ? K : 0;
-    sf -= sf >= K ? K : 0;
+    int s0 = base - sigma * (a0 - (U - 1));
+    s0 += s0 < 0 ? K : 0;
+    s0 -= s0 >= K ? K : 0;
+    // forward the slots fall with q, so a chunk whose reads would pass slot 0
+    // starts in the mirror copy instead
+    if (sigma > 0 && s0 < NR - 1) s0 += K;
+    const unsigned c8 = (unsigned)C * 8u;
 #pragma unroll
     for (int cb = 0; cb < NCH; ++cb) {
       const int jb = cb * DCH;
       if (jb >= nage) break;
       double wv[NR];
       // wv[q]: entry at m = k - i = m0 + q, m0 = a0 + jb - (U - 1),
-      // q = jj - i + U - 1 (jb < nage <= K - a0 + 1, so one wrap again);
-      // forward the slots fall with q, so a start near 0 moves to its mirror
-      // copy
-      int s0 = sf - sigma * jb;
-      s0 += s0 < 0 ? K : 0;
-      s0 -= s0 >= K ? K : 0;
-      if (sigma > 0 && s0 < NR - 1) s0 += K;
-      const double *rp = sm.ring + (size_t)s0 * C + kc;
+      // q = jj - i + U - 1.  The next chunk starts DCH slots further back: one
+      // wrap in the direction of travel (jb < nage <= K - a0 + 1, and a
+      // forward start in the mirror rows reads copies of slots 0..15)
+      if (cb > 0) {
+        s0 -= sigma * DCH;
+        if (sigma > 0 && s0 < NR - 1) s0 += K;
+        if (sigma < 0 && s0 >= K) s0 -= K;
+      }
+      const char *rp = reinterpret_cast<const char *>(sm.ring) + __umul24((unsigned)s0, c8) +
+                       (unsigned)kc * 8u;
 #pragma unroll
-      for (int q = 0; q < NR; ++q) wv[q] = rp[q * rstep];
+      for (int q = 0; q < NR; ++q) {
+        wv[q] = *reinterpret_cast<const double *>(rp);
+        rp += rstep;
+      }
 #pragma unroll
       for (int i = 0; i < U; ++i) {
 #pragma unroll
