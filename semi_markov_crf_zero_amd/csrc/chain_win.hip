@@ -394,6 +394,39 @@ __device__ __forceinline__ void block_rows(const double *stg, int C, int nb, int
   }
 }
 
+// The same for full blocks of U steps on the row waves, with each thread's
+// first item split into (step, entry) once per chunk (RowIdx) instead of by a
+// division per block.
+struct RowIdx {
+  int m0, r0, ms, rs;  // first item's step and entry; the stride's quotient and remainder
+  __device__ __forceinline__ void init(int q0, int C, int nthr) {
+    const int w = 2 * C;
+    m0 = q0 / w;
+    r0 = q0 % w;
+    ms = nthr / w;
+    rs = nthr % w;
+  }
+};
+
+__device__ __forceinline__ void block_rows_full(const double *stg, int C, int t0, int sigma,
+                                                double *row1, double *row2, const RowIdx &ix) {
+  const int S = 3 * C, w = 2 * C;
+  for (int m = ix.m0, r = ix.r0; m < U;) {
+    const double *s = stg + m * (S + 1);
+    const size_t o = (size_t)(t0 + sigma * m) * C;
+    if (r < C)
+      row1[o + r] = log_plus(s[r], s[C + r]);
+    else
+      row2[o + r - C] = log_plus(s[C + r], s[S]);
+    m += ix.ms;
+    r += ix.rs;
+    if (r >= w) {
+      r -= w;
+      ++m;
+    }
+  }
+}
+
 // Loader: the split scores of the block of U steps starting at step s0
 // (positions first + sigma*(s0 + i)) for every label -- U*C pairs over the
 // 64 lanes.
@@ -778,6 +811,8 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
     }
     __syncthreads();
     BlockLoad bl;
+    RowIdx rix;  // the row waves' items (threads 128 .. NT-1)
+    rix.init(tid - 128, C, NT - 128);
     for (int s0 = 0; s0 < nsteps; s0 += U) {
       const int nb = min(U, nsteps - s0);  // steps in this block
       const int t0 = first + sigma * s0;
@@ -794,8 +829,8 @@ __global__ __launch_bounds__(NT) void k_sweep_w(ChainShape sh, const float *__re
         if (w == 1 && more) bl.issue(es, ob, first, sigma, s0 + U, T, C, lane);
         if (w >= 2 && rows && s0 > wb) {
           // the previous block's rows (a full block of U steps, past the burn-in)
-          block_rows(sm.stg + (buf ^ 1) * U * S, C, U, t0 - sigma * U - rt0, sigma, row1, row2, -1, 128,
-                     NT - 128);
+          block_rows_full(sm.stg + (buf ^ 1) * U * S, C, t0 - sigma * U - rt0, sigma, row1, row2,
+                          rix);
         }
         if (more) {
           // far parts of the next block: entries older than this block only,
