@@ -10,9 +10,12 @@ run in the test on the host cores:
   Viterbi     the complete segmentation of every sequence, bit-exact;
   path score  the gold path's score and every element of its gradients.
 
-extreme (T = 2^20): the oracle's fwd+bwd and Viterbi take minutes on the
-host, so they come from tests/golden/extreme.npz, written by
-tests/golden/make_golden.py from the oracle alone: log Z and every element
+extreme (T = 2^20): the oracle's fwd+bwd runs in the test too (about a
+minute on 16 host cores) and is compared with the GPU element by element
+like the others (test_extreme_fwd_bwd_oracle).  The golden file
+tests/golden/extreme.npz, written by tests/golden/make_golden.py from the
+oracle alone, is a drift check besides it and the reference of the
+Viterbi test (the oracle's decoder takes minutes there): log Z and every element
 of grad_trans / grad_dur; marginals, emission gradients and boundary
 posteriors at every multiple of 4096 positions (the boundaries of the
 4096-, 8192- and 16384-position checkpoint intervals), their neighbours and
@@ -126,6 +129,20 @@ def test_extreme_fwd_bwd_golden():
     assert max(e.values()) <= TOL_GRAD
     assert max(sums.values()) <= TOL_GRAD * blk
     _properties(inp, g)
+
+
+def test_extreme_fwd_bwd_oracle():
+    """Every element of every fwd+bwd output at T = 2^20 against the oracle
+    run here (log Z, grad_emissions, marginals, boundary posteriors,
+    grad_trans, grad_dur)."""
+    inp = make_inputs("extreme")
+    g = gpu_fwd_bwd(inp)
+    print("extreme: oracle fwd+bwd on the host ...", flush=True)
+    o = oracle.fwd_bwd(inp)
+    errs = assert_fwd_bwd_close(g, o, label="extreme")
+    print("extreme logz rel %.2e" % logz_rel_err(g["logz"], o["logz"]).max(), errs,
+          "param excess trans %.3f dur %.3f" % (param_excess(g["grad_trans"], o["grad_trans"]),
+                                                param_excess(g["grad_dur"], o["grad_dur"])))
 
 
 def test_extreme_viterbi_golden():
