@@ -10,12 +10,11 @@ run in the test on the host cores:
   Viterbi     the complete segmentation of every sequence, bit-exact;
   path score  the gold path's score and every element of its gradients.
 
-extreme (T = 2^20): the oracle's fwd+bwd runs in the test too (about a
-minute on 16 host cores) and is compared with the GPU element by element
-like the others (test_extreme_fwd_bwd_oracle).  The golden file
+extreme (T = 2^20): the oracle's fwd+bwd and Viterbi run in the test too
+(about a minute and half a minute on 16 host cores) and are compared with
+the GPU like the others (test_extreme_*_oracle).  The golden file
 tests/golden/extreme.npz, written by tests/golden/make_golden.py from the
-oracle alone, is a drift check besides it and the reference of the
-Viterbi test (the oracle's decoder takes minutes there): log Z and every element
+oracle alone, is a drift check beside them: log Z and every element
 of grad_trans / grad_dur; marginals, emission gradients and boundary
 posteriors at every multiple of 4096 positions (the boundaries of the
 4096-, 8192- and 16384-position checkpoint intervals), their neighbours and
@@ -143,6 +142,17 @@ def test_extreme_fwd_bwd_oracle():
     print("extreme logz rel %.2e" % logz_rel_err(g["logz"], o["logz"]).max(), errs,
           "param excess trans %.3f dur %.3f" % (param_excess(g["grad_trans"], o["grad_trans"]),
                                                 param_excess(g["grad_dur"], o["grad_dur"])))
+
+
+def test_extreme_viterbi_oracle():
+    """The complete segmentation at T = 2^20 against the oracle's decoder run
+    here."""
+    inp = make_inputs("extreme")
+    v = gpu_viterbi(inp)
+    print("extreme: oracle Viterbi on the host ...", flush=True)
+    o = oracle.viterbi(inp)
+    assert_viterbi_equal(v, o, label="extreme")
+    print("extreme segments", v["num_segs"], "min margin", o["min_margin"].min())
 
 
 def test_extreme_viterbi_golden():
