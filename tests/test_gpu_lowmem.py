@@ -7,7 +7,8 @@ working memory sublinear in sequence length; technical summary, section
 windows on both sweep engines (windowed C <= 32, LDS-ring C > 32 at 256, 512
 and 1024 threads), ragged lengths, an interval below K (raised to K), K > T,
 invalid lengths, weights, centring off, and the named workloads; extreme
-against its golden file."""
+against its golden file here, and element by element against the oracle in
+test_gpu_workloads.py."""
 import os
 
 import numpy as np

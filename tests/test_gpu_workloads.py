@@ -133,26 +133,29 @@ def test_extreme_fwd_bwd_golden():
 def test_extreme_fwd_bwd_oracle():
     """Every element of every fwd+bwd output at T = 2^20 against the oracle
     run here (log Z, grad_emissions, marginals, boundary posteriors,
-    grad_trans, grad_dur)."""
+    grad_trans, grad_dur), in the default mode and in the low-memory mode
+    (records only, recomputation between checkpoints)."""
     inp = make_inputs("extreme")
-    g = gpu_fwd_bwd(inp)
+    runs = {"default": gpu_fwd_bwd(inp), "low-memory": gpu_fwd_bwd(inp, low_memory=True)}
     print("extreme: oracle fwd+bwd on the host ...", flush=True)
     o = oracle.fwd_bwd(inp)
-    errs = assert_fwd_bwd_close(g, o, label="extreme")
-    print("extreme logz rel %.2e" % logz_rel_err(g["logz"], o["logz"]).max(), errs,
-          "param excess trans %.3f dur %.3f" % (param_excess(g["grad_trans"], o["grad_trans"]),
-                                                param_excess(g["grad_dur"], o["grad_dur"])))
+    for mode, g in runs.items():
+        errs = assert_fwd_bwd_close(g, o, label="extreme " + mode)
+        print("extreme", mode, "logz rel %.2e" % logz_rel_err(g["logz"], o["logz"]).max(), errs,
+              "param excess trans %.3f dur %.3f" % (param_excess(g["grad_trans"], o["grad_trans"]),
+                                                    param_excess(g["grad_dur"], o["grad_dur"])))
 
 
 def test_extreme_viterbi_oracle():
     """The complete segmentation at T = 2^20 against the oracle's decoder run
-    here."""
+    here, from the whole-sequence decoder and the low-memory one."""
     inp = make_inputs("extreme")
-    v = gpu_viterbi(inp)
+    runs = {"whole": gpu_viterbi(inp), "low-memory": gpu_viterbi(inp, low_memory=True)}
     print("extreme: oracle Viterbi on the host ...", flush=True)
     o = oracle.viterbi(inp)
-    assert_viterbi_equal(v, o, label="extreme")
-    print("extreme segments", v["num_segs"], "min margin", o["min_margin"].min())
+    for mode, v in runs.items():
+        assert_viterbi_equal(v, o, label="extreme " + mode)
+    print("extreme segments", runs["whole"]["num_segs"], "min margin", o["min_margin"].min())
 
 
 def test_extreme_viterbi_golden():
