@@ -39,20 +39,26 @@ SHAPES = [
 ]
 
 
-# one per instance of the windowed engine (C <= 32, 256 threads): durations
-# per thread A in {<=8, <=16, <=32} x label bound C in {<=8, <=32}; the C > 32
-# entries run on the LDS-ring engine.
+# one per instance of the windowed engine (C <= 32, 256 threads): far
+# durations per helper thread A (a multiple of the chunk 2, 4 or 8, at most 48
+# in registers) x label bound C in {<=8, <=16, <=32}, the largest A on both
+# sides of that bound (C = 16 past it runs on the LDS-ring engine) and the
+# two-workgroups-per-compute-unit configuration (C <= 16 with its LDS below
+# half the unit's); the C > 32 entries run on the LDS-ring engine.
 _WIN64_SKIP = pytest.mark.skip(
     reason="faulted the GPU while C > 32 shapes ran on the windowed engine (cause not "
            "found on the CPU emulation); that engine is now limited to C <= 32 and these "
            "shapes stay off the GPU until the fault is explained")
 WINDOW_SHAPES = [
     (2, 300, 8, 40, [300, 177]),         # A = 2,  C <= 8
-    (2, 800, 8, 500, [800, 555]),        # A = 16, C <= 8
-    (2, 1200, 8, 1000, [1200, 1001]),    # A = 32, C <= 8
-    (2, 400, 32, 60, [400, 261]),        # A = 8,  C <= 32
-    (2, 900, 32, 120, [900, 611]),       # A = 15, C <= 32
-    (2, 1100, 16, 500, [1100, 777]),     # A = 32, C <= 32 (genome-like)
+    (2, 800, 8, 500, [800, 555]),        # A = 24, C <= 8
+    (2, 1200, 8, 1000, [1200, 1001]),    # A = 48, C <= 8
+    (2, 2600, 8, 1150, [2600, 1777]),    # A = 48, C <= 8, K at the register bound; 2 per unit
+    (2, 400, 32, 60, [400, 261]),        # A = 16, C <= 32
+    (2, 900, 32, 120, [900, 611]),       # A = 24, C <= 32
+    (2, 1100, 16, 500, [1100, 777]),     # A = 48, C <= 16 (genome-like), 2 per unit
+    (2, 2000, 16, 576, [2000, 1333]),    # A = 48, C <= 16, K at the register bound
+    (2, 2000, 16, 600, [2000, 1500]),    # A would be 56: the LDS-ring engine
     pytest.param((2, 400, 64, 32, [400, 271]), marks=_WIN64_SKIP),
     pytest.param((2, 700, 64, 60, [700, 513]), marks=_WIN64_SKIP),
     pytest.param((2, 600, 48, 160, [600, 389]), marks=_WIN64_SKIP),
