@@ -88,9 +88,17 @@ bool win_config(int C, int K, ChainShape &sh) {
   A = (A + dch - 1) / dch * dch;
   if (A > dch * (dch == 8 ? kWinFarChunks : 1)) return false;
   if (win_lds_bytes(C, K, P) > kMaxDynLds) return false;
+  // wave 1's groups take A durations each; waves 2-3, which also write the
+  // rows (a logarithm per lane and block, more than wave 1's score loads),
+  // share what is left: at most A, a whole number of chunks
+  const int gw = 64 / cp;  // duration groups per helper wave
+  const int rem = nfar - gw * A;
+  int A2 = rem > 0 ? (rem + 2 * gw - 1) / (2 * gw) : 0;
+  A2 = (A2 + dch - 1) / dch * dch;
   sh.NT = NT;
   sh.P = P;
   sh.A = A;
+  sh.A2 = A2;
   sh.Q = 1;
   sh.win = 1;
   return true;

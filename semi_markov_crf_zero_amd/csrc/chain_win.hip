@@ -142,7 +142,8 @@ __device__ __forceinline__ double group_sum(double v, int gw) {
 }
 
 // Far parts of the K-sums of a block: helper thread (kg, kc) owns the
-// durations k = a0 + j, j < nage, of label kc, all k >= 2U.  Labels take cp
+// durations k = a0 + j, j < nage, of label kc, all k >= 2U (A of them per
+// group of wave 1, A2 per group of the row-writing waves 2..).  Labels take cp
 // lanes of a wave (C rounded up to a power of two; lanes past C idle), so
 // the gw = 64/cp duration groups of one label in a wave are consecutive
 // lanes and their partials add up by DPP.
@@ -173,9 +174,11 @@ struct Win {
     kc = (tid & 63) / gw;
     kg = (w - 1) * gw + (tid & 63) % gw;  // helper waves 1.. only
     on = w >= 1 && kc < C && kg < sh.P;
-    a0 = kNearW + 1 + kg * sh.A;
+    // wave 1's groups hold A durations each, those of waves 2.. A2
+    const int cap = kg < gw ? sh.A : sh.A2;
+    a0 = kNearW + 1 + (kg < gw ? kg * sh.A : gw * sh.A + (kg - gw) * sh.A2);
     int n = on ? sh.K - a0 + 1 : 0;
-    n = n < 0 ? 0 : (n > sh.A ? sh.A : n);
+    n = n < 0 ? 0 : (n > cap ? cap : n);
     nage = n;
     float v[NW];  // all loads in flight before the first exponential
 #pragma unroll

@@ -22,6 +22,7 @@ struct ChainShape {
   int e256;    // 1: the engine of chain256.hip (64 < C <= 256, K <= 64)
   int P;       // K-sum threads per label = NT / C
   int A;       // durations per K-sum thread = ceil(K / P)
+  int A2;      // windowed engine: far durations per group of helper waves 2.. (A: wave 1)
   int Q;       // waves holding row threads = ceil(C / 64) (Viterbi slices)
   int QT;      // contraction slices of the LDS-ring engine
   int CS;      // previous labels per contraction slice = ceil(C / QT)
