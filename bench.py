@@ -344,9 +344,10 @@ def main():
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the batch would shard across GPUs with one all-reduce of the parameter "
-              "gradients; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the "
+              "batch, or for a single sequence its checkpoint intervals, would shard across "
+              "GPUs with one all-reduce of the parameter gradients). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
