@@ -297,6 +297,75 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
       }
 }
 
+// The same for C <= 16, where a 64 x 64 tile would leave 15 of its 16
+// matrix blocks empty: a staged 64-lane row holds 4 positions x 16 labels
+// (lane 16p + c), each wave multiplies its own quarter of a 64-position
+// batch into the one 16 x 16 block (every matrix instruction fully used,
+// every staged lane live), and the four waves' blocks are added in a fixed
+// order at the end.
+constexpr int kTx16Rows = 64;  // positions staged per batch (C <= 16)
+__global__ __launch_bounds__(kTxThreads) void k_trans_x16(ChainShape sh, PostArgs pa, int tseg,
+                                                          int nseg) {
+  __shared__ double ta[kTx16Rows][16];
+  __shared__ double tg[kTx16Rows][16];
+  __shared__ double red[kTxThreads / 64][16][17];
+  const int b = blockIdx.y / nseg, seg = blockIdx.y % nseg;
+  const int C = sh.C, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int L = pa.lengths[b];
+  const int p = lane >> 4, c = lane & 15, cc = min(c, C - 1);
+  v4d acc = v4d{0.0, 0.0, 0.0, 0.0};
+  int tbeg = max(1, pa.t_lo) + seg * tseg, tend = tbeg + tseg;
+  if (!valid_len(sh, L)) tend = tbeg;
+  if (tend > L) tend = L;  // transitions at 1 <= t < L
+  if (tend > pa.t_hi) tend = pa.t_hi;
+  const double logZ = valid_len(sh, L) ? pa.logz[b] : 0.0;
+  // staging: thread (wave w, lane 16p + c) holds label c of the positions
+  // 16u + 4w + p of the batch; every load of a batch is issued before the
+  // first use (indices clamped, invalid entries masked)
+  constexpr int kPer = kTx16Rows * 16 / kTxThreads;
+  static_assert(kTxThreads == 256 && kPer * kTxThreads == kTx16Rows * 16, "four waves");
+  for (int r0 = tbeg; r0 < tend; r0 += kTx16Rows) {
+    const int nr = min(kTx16Rows, tend - r0);
+    double va[kPer], vg[kPer], vz[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int rr = 16 * u + 4 * w + p, t = r0 + min(rr, nr - 1);
+      const size_t ri = rix(sh, pa, b, t);
+      va[u] = pa.row_a[ri + cc];
+      vg[u] = pa.row_v[ri + cc];
+      vz[u] = shift_f(sh, pa, b, t) + shift_b(sh, pa, b, t) - logZ;
+    }
+    __syncthreads();  // the previous batch's products are done with ta / tg
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int rr = 16 * u + 4 * w + p;
+      const bool in = rr < nr && c < C;
+      const double m = group_max(in ? va[u] : -__builtin_huge_val(), 16);  // the row's maximum
+      ta[rr][c] = in ? exp_wide(va[u] - m) : 0.0;
+      tg[rr][c] = in ? exp_wide(vg[u] + m + vz[u]) : 0.0;
+    }
+    __syncthreads();
+    // wave w: positions 16w .. 16w+15 of the batch, 4 per instruction
+    // (rows past nr were staged as zeros)
+#pragma unroll
+    for (int kk = 0; kk < 16; kk += 4) {
+      const double a = ta[16 * w + kk + p][c], g = tg[16 * w + kk + p][c];
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, g, acc, 0, 0, 0);
+    }
+  }
+  // element r of lane 16p + c is entry (p + 4r, c) of the wave's block
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[w][p + 4 * r][c] = acc[r];
+  __syncthreads();
+  const int cp = tid >> 4, cq = tid & 15;
+  const double v = ((red[0][cp][cq] + red[1][cp][cq]) + red[2][cp][cq]) + red[3][cp][cq];
+  if (cp < C && cq < C) {
+    double *out = pa.tx_part + ((size_t)b * nseg + seg) * C * C;
+    const size_t o = (size_t)cp * C + cq;
+    out[o] = pa.accumulate ? out[o] + v : v;
+  }
+}
+
 // ------------------------------------------------------------ durations
 // D[k,c] = sum_s exp(a[s,c] + b[s+k,c] + dur[k-1,c]) with
 // a[s,c] = u[s,c] - S[s,c] and b[e,c] = S[e,c] + beta[e,c] - logZ, for
@@ -671,8 +740,12 @@ hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ntc = (sh.C + kTxTile - 1) / kTxTile;
-  hipLaunchKernelGGL(k_trans_x, dim3(ntc * ntc, sh.B * g.tx_nseg), dim3(kTxThreads), 0, st, sh,
-                     pa, g.tx_seg, g.tx_nseg);
+  if (sh.C <= 16)
+    hipLaunchKernelGGL(k_trans_x16, dim3(1, sh.B * g.tx_nseg), dim3(kTxThreads), 0, st, sh, pa,
+                       g.tx_seg, g.tx_nseg);
+  else
+    hipLaunchKernelGGL(k_trans_x, dim3(ntc * ntc, sh.B * g.tx_nseg), dim3(kTxThreads), 0, st, sh,
+                       pa, g.tx_seg, g.tx_nseg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ncg = (sh.C + 15) / 16;
