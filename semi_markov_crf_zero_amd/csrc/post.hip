@@ -297,6 +297,99 @@ __global__ __launch_bounds__(kTxThreads) void k_trans_x(ChainShape sh, PostArgs 
       }
 }
 
+// The same for C > 64 with 128 x 128 output tiles: each row element is
+// staged and exponentiated by half as many tiles, and a row's maximum is one
+// wave reduction over two elements per lane.  Batches of 16 positions (the
+// two staged tiles take 32 KB); wave (wi, wj) accumulates the 64 x 64 block
+// (64 wi, 64 wj) as 4 x 4 blocks of 16 x 16.
+constexpr int kTx128 = 128, kTx128Rows = 16;
+__global__ __launch_bounds__(kTxThreads, 2) void k_trans_x128(ChainShape sh, PostArgs pa, int tseg,
+                                                           int nseg) {
+  __shared__ double ta[kTx128Rows][kTx128];
+  __shared__ double tg[kTx128Rows][kTx128];
+  const int ntc = (sh.C + kTx128 - 1) / kTx128;
+  const int ti = blockIdx.x / ntc, tj = blockIdx.x % ntc;  // rows c' / columns c
+  const int b = blockIdx.y / nseg, seg = blockIdx.y % nseg;
+  const int C = sh.C, tid = threadIdx.x;
+  const int L = pa.lengths[b];
+  const int ci0 = ti * kTx128, cj0 = tj * kTx128;
+  v4d acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = v4d{0.0, 0.0, 0.0, 0.0};
+  int tbeg = max(1, pa.t_lo) + seg * tseg, tend = tbeg + tseg;
+  if (!valid_len(sh, L)) tend = tbeg;
+  if (tend > L) tend = L;  // transitions at 1 <= t < L
+  if (tend > pa.t_hi) tend = pa.t_hi;
+  const double logZ = valid_len(sh, L) ? pa.logz[b] : 0.0;
+  // staging: wave w holds rows 4u + w of the batch (u < kPer), lane l the
+  // columns l and 64 + l; every load of a batch is issued before the first
+  // use (indices clamped, invalid entries masked)
+  constexpr int kPer = kTx128Rows / (kTxThreads / 64);
+  const int lane = tid & 63, w = tid >> 6;
+  const int ca0 = min(ci0 + lane, C - 1), ca1 = min(ci0 + 64 + lane, C - 1);
+  const int cg0 = min(cj0 + lane, C - 1), cg1 = min(cj0 + 64 + lane, C - 1);
+  for (int r0 = tbeg; r0 < tend; r0 += kTx128Rows) {
+    const int nr = min(kTx128Rows, tend - r0);
+    double va0[kPer], va1[kPer], vg0[kPer], vg1[kPer], vz[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int rr = 4 * u + w, t = r0 + min(rr, nr - 1);
+      const size_t ri = rix(sh, pa, b, t);
+      va0[u] = pa.row_a[ri + ca0];
+      va1[u] = pa.row_a[ri + ca1];
+      vg0[u] = pa.row_v[ri + cg0];
+      vg1[u] = pa.row_v[ri + cg1];
+      vz[u] = shift_f(sh, pa, b, t) + shift_b(sh, pa, b, t) - logZ;
+    }
+    __syncthreads();  // the previous batch's products are done with ta / tg
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int rr = 4 * u + w;
+      const bool ia0 = rr < nr && ci0 + lane < C, ia1 = rr < nr && ci0 + 64 + lane < C;
+      const bool ig0 = rr < nr && cj0 + lane < C, ig1 = rr < nr && cj0 + 64 + lane < C;
+      const double m = group_max(fmax(ia0 ? va0[u] : -__builtin_huge_val(),
+                                      ia1 ? va1[u] : -__builtin_huge_val()), 64);
+      ta[rr][lane] = ia0 ? exp_wide(va0[u] - m) : 0.0;
+      ta[rr][64 + lane] = ia1 ? exp_wide(va1[u] - m) : 0.0;
+      tg[rr][lane] = ig0 ? exp_wide(vg0[u] + m + vz[u]) : 0.0;
+      tg[rr][64 + lane] = ig1 ? exp_wide(vg1[u] + m + vz[u]) : 0.0;
+    }
+    __syncthreads();
+    // rows past nr were staged as zeros, so whole groups of 4 run
+    const int kq = lane >> 4, li = lane & 15, wi = w >> 1, wj = w & 1;
+#pragma unroll
+    for (int kk = 0; kk < kTx128Rows; kk += 4) {
+      double a[4], g[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        a[x] = ta[kk + kq][64 * wi + 16 * x + li];
+        g[x] = tg[kk + kq][64 * wj + 16 * x + li];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], g[y], acc[x][y], 0, 0, 0);
+    }
+  }
+  double *out = pa.tx_part + ((size_t)b * nseg + seg) * C * C;
+  const int kq = lane >> 4, li = lane & 15, wi = w >> 1, wj = w & 1;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int cp = ci0 + 64 * wi + 16 * x + kq + 4 * r, c = cj0 + 64 * wj + 16 * y + li;
+        if (cp < C && c < C) {
+          const size_t o = (size_t)cp * C + c;
+          out[o] = pa.accumulate ? out[o] + acc[x][y][r] : acc[x][y][r];
+        }
+      }
+}
+
 // The same for C <= 16, where a 64 x 64 tile would leave 15 of its 16
 // matrix blocks empty: a staged 64-lane row holds 4 positions x 16 labels
 // (lane 16p + c), each wave multiplies its own quarter of a 64-position
@@ -740,10 +833,14 @@ hipError_t launch_posteriors(const ChainShape &sh, const PostArgs &pa, hipStream
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ntc = (sh.C + kTxTile - 1) / kTxTile;
-  if (sh.C <= 16)
+  if (sh.C <= 16) {
     hipLaunchKernelGGL(k_trans_x16, dim3(1, sh.B * g.tx_nseg), dim3(kTxThreads), 0, st, sh, pa,
                        g.tx_seg, g.tx_nseg);
-  else
+  } else if (sh.C > kTxTile) {
+    const int n128 = (sh.C + kTx128 - 1) / kTx128;
+    hipLaunchKernelGGL(k_trans_x128, dim3(n128 * n128, sh.B * g.tx_nseg), dim3(kTxThreads), 0, st,
+                       sh, pa, g.tx_seg, g.tx_nseg);
+  } else
     hipLaunchKernelGGL(k_trans_x, dim3(ntc * ntc, sh.B * g.tx_nseg), dim3(kTxThreads), 0, st, sh,
                        pa, g.tx_seg, g.tx_nseg);
   e = hipGetLastError();
